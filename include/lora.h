@@ -1,0 +1,164 @@
+/*
+ * lora.h -- C ABI of liblora_mi355x.so: the multi-LoRA batched linear on MI355X (gfx950).
+ *
+ * Source pages, cited by title and section:
+ *   [P1] "Multi-LoRA Serving: Why 100 Adapters Fit on One GPU" (dev.to)
+ *   [P2] "Serving Many LoRA Adapters From One Base Model" (ai-tldr.dev)
+ *   [P3] "Multi-LoRA Serving: Sharing One GPU Across Adapters" (cloudai.pt)
+ *
+ * The layer ([P1], "Why can't you just merge LoRA weights into the base model?", the
+ * layer equation):
+ *
+ *     y[m, :] = x[m, :] W  +  (x[m, :] A_i) B_i * (alpha_i / r_i),   i = ids[m]
+ *
+ * for a mixed batch in which every row names its own adapter, and id -1 means the bare
+ * base model ([P2], "A worked example: the memory math", the adapter=None request).
+ * The shared term is one GEMM over the whole batch; the delta is computed for all adapters
+ * in one pass over the full batch, an index vector mapping rows to adapter ids, and a
+ * stacked adapter tensor ([P1], "How does one batch run 30 different adapters at once?"),
+ * in two steps, shrink (x A_i, down to the rank) and expand (times B_i, back to d_out)
+ * ([P3], "MoE Models Raise the Bar").
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Pointers.  All array arguments are DEVICE pointers (hipMalloc'd or torch CUDA tensors),
+ *    row-major and contiguous.  x, W, A, B, y and t must be 16-byte aligned; the workspace
+ *    256-byte aligned.  Scalars are passed by value.
+ *  - Types.  x, W, A, B hold bfloat16 bit patterns (uint16).  y is bfloat16 or float32
+ *    (lora_dtype_t).  t is float32.  scale is float32, ranks and ids are int32.
+ *  - Shapes.  x[M, d_in], W[d_in, d_out], A[n_adapters, d_in, r_max],
+ *    B[n_adapters, r_max, d_out], y[M, d_out], t[M, r_max].  A_i is stored d_in x r_max and
+ *    B_i r_max x d_out: the transposes of [P1]'s "A: r x d_in, B: d_out x r" in "How much
+ *    memory does one LoRA adapter actually cost?", same r * (d_in + d_out) parameters.
+ *  - Limits.  0 <= M <= LORA_MAX_ROWS (M = 0 is a no-op that returns LORA_OK);
+ *    d_in, d_out positive multiples of 8; r_max one of 8, 16, 32, 64;
+ *    1 <= n_adapters <= LORA_MAX_ADAPTERS.
+ *  - Pool contents (caller's contract).  Every adapter is padded to r_max ([P1], "What
+ *    does a working multi-LoRA config look like?" and "Where does multi-LoRA serving
+ *    actually break?", rank padding): ranks[i] in [1, r_max], and the entries of A_i beyond
+ *    column ranks[i] and of B_i beyond row ranks[i] are zero.  scale[i] = alpha_i / ranks[i]
+ *    is computed by the caller.  ranks may be NULL, meaning every adapter has rank r_max.
+ *    Registering an adapter is a plain device copy into slot i of A and B plus ranks[i] and
+ *    scale[i] ([P2], "How it works", "Loading and swapping adapters"); no call is needed.
+ *  - ids.  ids[m] in [-1, n_adapters).  An id outside that range is counted in meta[2] on
+ *    the device and its row is treated as base-only; nothing faults.
+ *  - Streams.  `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *    enqueues work on it and returns; none synchronises.  The library keeps no state
+ *    between calls and allocates nothing: the caller owns every buffer, including the
+ *    workspace.  Calls that share a workspace or segment buffers must not overlap in time.
+ *  - Errors.  Arguments are validated on the host before anything is enqueued; on a
+ *    validation error nothing is enqueued and the call returns the status.  LORA_ERR_HIP
+ *    reports a failed launch; lora_last_hip_error() names the HIP error.
+ */
+#ifndef LORA_MI355X_H
+#define LORA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LORA_TILE_ROWS 16        /* rows per work tile of a segment */
+#define LORA_MAX_ADAPTERS 16384  /* pool slots one call can address */
+#define LORA_MAX_ROWS (1 << 22)  /* rows per call */
+
+typedef enum {
+    LORA_OK = 0,
+    LORA_ERR_NULL = 1,      /* a required pointer is NULL */
+    LORA_ERR_SHAPE = 2,     /* M, d_in, d_out or n_adapters out of range */
+    LORA_ERR_RANK = 3,      /* r_max not one of 8, 16, 32, 64 */
+    LORA_ERR_ALIGN = 4,     /* a pointer is not aligned as required */
+    LORA_ERR_WORKSPACE = 5, /* ws_bytes smaller than lora_workspace_bytes() */
+    LORA_ERR_DTYPE = 6,     /* unknown lora_dtype_t */
+    LORA_ERR_HIP = 7,       /* a kernel launch failed */
+    LORA_ERR_BAD_ID = 8,    /* reserved: invalid ids are counted on the device in meta[2] */
+    LORA_ERR_MODE = 9       /* unknown lora_mode_t */
+} lora_status_t;
+
+typedef enum { LORA_BF16 = 0, LORA_F32 = 1 } lora_dtype_t;
+
+/* DECODE: y = x W on a decode-shaped GEMM, then y += delta (two roundings of a bf16 y).
+ * PREFILL: x W with the delta added in the GEMM epilogue before the only store.
+ * AUTO: PREFILL when M >= LORA_PREFILL_MIN_ROWS, else DECODE. */
+typedef enum { LORA_MODE_AUTO = 0, LORA_MODE_DECODE = 1, LORA_MODE_PREFILL = 2 } lora_mode_t;
+#define LORA_PREFILL_MIN_ROWS 1024
+
+/* Rows grouped by adapter, as built by lora_build_segments.  All device buffers, owned by
+ * the caller, sized for the M and n_adapters of the batch:
+ *   perm        int32[M]                  rows of adapter 0 in ascending row order, then
+ *                                         adapter 1, ..., then base-only rows (id -1 or
+ *                                         invalid) in ascending row order
+ *   offsets     int32[n_adapters + 1]     offsets[i] = first position of adapter i in perm;
+ *                                         offsets[n_adapters] = number of LoRA rows
+ *   seg_adapter int32[max(1, min(M, n))]  adapters with at least one row, ascending
+ *   tiles       int32[2 * lora_max_tiles(M, n)]
+ *                                         every segment cut into runs of LORA_TILE_ROWS
+ *                                         positions of perm: {first position, adapter}
+ *   meta        int32[4]                  {segments, LoRA rows, invalid ids, tiles} */
+typedef struct {
+    int32_t *perm;
+    int32_t *offsets;
+    int32_t *seg_adapter;
+    int32_t *tiles;
+    int32_t *meta;
+} lora_segments_t;
+
+/* Upper bound on the number of tiles: min(M, n_adapters) + M / LORA_TILE_ROWS. */
+int32_t lora_max_tiles(int32_t M, int32_t n_adapters);
+
+/* Workspace bytes needed by lora_linear and lora_shrink for these sizes (0 when M = 0).
+ * Returns 0 for arguments that the calls would reject. */
+size_t lora_workspace_bytes(int32_t M, int32_t d_in, int32_t d_out, int32_t r_max,
+                            int32_t n_adapters);
+
+/* Group the rows of a batch by adapter: a histogram of ids, a prefix sum into offsets,
+ * and a stable scatter into perm, all on the device in one launch.  The grouping is what
+ * lets one pass serve every adapter of the batch ([P1], "How does one batch run 30
+ * different adapters at once?"; [P2], "Going deeper", grouping by adapter).
+ * ids: int32[M] (device).  Output: seg (see lora_segments_t).  Deterministic. */
+lora_status_t lora_build_segments(const int32_t *ids, int32_t M, int32_t n_adapters,
+                                  lora_segments_t seg, void *stream);
+
+/* Shrink: t[m, j] = sum_k x[m, k] A[ids[m], k, j] for rows with an adapter (j < r_max,
+ * columns beyond the adapter's rank are 0), t[m, :] = 0 for base-only rows.  seg must have
+ * been built for the same ids, M and n_adapters.  ws: at least
+ * lora_workspace_bytes(M, d_in, 8, r_max, n_adapters) bytes (split-K partial sums).  The
+ * partial sums are added in a fixed order: the result is deterministic. */
+lora_status_t lora_shrink(const void *x, const void *A, const int32_t *ranks, int32_t M,
+                          int32_t d_in, int32_t r_max, int32_t n_adapters,
+                          lora_segments_t seg, float *t, void *ws, size_t ws_bytes,
+                          void *stream);
+
+/* Expand: y[m, :] += scale[i] * sum_{j < ranks[i]} t[m, j] B[i, j, :] for every row m with
+ * adapter i = ids[m] >= 0; base-only rows of y are not read or written.  One rounding per
+ * element of y.  seg as for lora_shrink. */
+lora_status_t lora_expand(const float *t, const void *B, const float *scale,
+                          const int32_t *ranks, int32_t M, int32_t d_out, int32_t r_max,
+                          int32_t n_adapters, lora_segments_t seg, void *y,
+                          lora_dtype_t y_dtype, void *stream);
+
+/* The whole layer: y = x W + (x A_i) B_i scale_i, overwriting y[M, d_out].
+ * segs: NULL to build the segments inside the workspace from ids, or segments already
+ * built for these ids (lets several projections of one batch share one build).
+ * ws: at least lora_workspace_bytes(M, d_in, d_out, r_max, n_adapters) bytes. */
+lora_status_t lora_linear(const void *x, const void *W, const void *A, const void *B,
+                          const float *scale, const int32_t *ranks, const int32_t *ids,
+                          int32_t M, int32_t d_in, int32_t d_out, int32_t r_max,
+                          int32_t n_adapters, const lora_segments_t *segs, void *y,
+                          lora_dtype_t y_dtype, lora_mode_t mode, void *ws,
+                          size_t ws_bytes, void *stream);
+
+/* Human-readable name of a status. */
+const char *lora_status_string(lora_status_t status);
+
+/* The HIP error string of the last call on this host thread that returned LORA_ERR_HIP
+ * ("no error" otherwise).  Each call clears errors that were pending before it. */
+const char *lora_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LORA_MI355X_H */

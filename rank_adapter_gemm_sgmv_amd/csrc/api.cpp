@@ -1,0 +1,230 @@
+// api.cpp -- the C ABI of liblora_mi355x.so (include/lora.h): host-side validation,
+// workspace layout and the launch sequence of each call.  No call allocates, synchronises
+// or keeps state.
+#include <stdint.h>
+#include <string.h>
+
+#include "common.h"
+
+using namespace lora;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxDim = 1 << 20;
+
+size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool rank_ok(int32_t r_max) { return r_max == 8 || r_max == 16 || r_max == 32 || r_max == 64; }
+
+bool dim_ok(int32_t d) { return d > 0 && d <= kMaxDim && d % 8 == 0; }
+
+lora_status_t check_common(int32_t M, int32_t r_max, int32_t n_adapters) {
+    if (M < 0 || M > LORA_MAX_ROWS) return LORA_ERR_SHAPE;
+    if (n_adapters < 1 || n_adapters > LORA_MAX_ADAPTERS) return LORA_ERR_SHAPE;
+    if (!rank_ok(r_max)) return LORA_ERR_RANK;
+    return LORA_OK;
+}
+
+lora_status_t check_seg(const lora_segments_t &s) {
+    if (!s.perm || !s.offsets || !s.seg_adapter || !s.tiles || !s.meta) return LORA_ERR_NULL;
+    if (!aligned(s.perm, 4) || !aligned(s.offsets, 4) || !aligned(s.seg_adapter, 4) ||
+        !aligned(s.tiles, 8) || !aligned(s.meta, 4))
+        return LORA_ERR_ALIGN;
+    return LORA_OK;
+}
+
+size_t segments_bytes(int32_t M, int32_t n) {
+    const int32_t segs = M < n ? M : n;
+    return round_up((size_t)M * 4) + round_up((size_t)(n + 1) * 4) +
+           round_up((size_t)(segs > 1 ? segs : 1) * 4) +
+           round_up((size_t)2 * lora_max_tiles(M, n) * 4) + round_up(4 * 4);
+}
+
+lora_segments_t carve_segments(char *&p, int32_t M, int32_t n) {
+    lora_segments_t s;
+    const int32_t segs = M < n ? M : n;
+    s.perm = reinterpret_cast<int32_t *>(p); p += round_up((size_t)M * 4);
+    s.offsets = reinterpret_cast<int32_t *>(p); p += round_up((size_t)(n + 1) * 4);
+    s.seg_adapter = reinterpret_cast<int32_t *>(p); p += round_up((size_t)(segs > 1 ? segs : 1) * 4);
+    s.tiles = reinterpret_cast<int32_t *>(p); p += round_up((size_t)2 * lora_max_tiles(M, n) * 4);
+    s.meta = reinterpret_cast<int32_t *>(p); p += round_up(4 * 4);
+    return s;
+}
+
+size_t shrink_partial_bytes(int32_t M, int32_t d_in, int32_t r_max) {
+    int kc, ksplit;
+    shrink_plan(d_in, &kc, &ksplit);
+    return round_up((size_t)ksplit * M * r_max * sizeof(float));
+}
+
+size_t t_bytes(int32_t M, int32_t r_max) { return round_up((size_t)M * r_max * sizeof(float)); }
+
+size_t gemm_bytes(int32_t M, int32_t d_in, int32_t d_out) {
+    return round_up(gemm_partial_floats(M, d_in, d_out) * sizeof(float));
+}
+
+thread_local hipError_t g_last_hip_error = hipSuccess;
+
+lora_status_t hip_status(hipError_t e) {
+    g_last_hip_error = e;
+    return e == hipSuccess ? LORA_OK : LORA_ERR_HIP;
+}
+
+// Launch errors are read with hipGetLastError after each launch; clear anything pending
+// from before this call so it is not reported as ours.
+void clear_stale_error() { (void)hipGetLastError(); }
+
+}  // namespace
+
+extern "C" {
+
+int32_t lora_max_tiles(int32_t M, int32_t n_adapters) {
+    if (M <= 0 || n_adapters <= 0) return 0;
+    const int32_t segs = M < n_adapters ? M : n_adapters;
+    return segs + M / LORA_TILE_ROWS;
+}
+
+size_t lora_workspace_bytes(int32_t M, int32_t d_in, int32_t d_out, int32_t r_max,
+                            int32_t n_adapters) {
+    if (check_common(M, r_max, n_adapters) != LORA_OK || !dim_ok(d_in) || !dim_ok(d_out)) return 0;
+    if (M == 0) return 0;
+    return segments_bytes(M, n_adapters) + t_bytes(M, r_max) + shrink_partial_bytes(M, d_in, r_max) +
+           gemm_bytes(M, d_in, d_out);
+}
+
+lora_status_t lora_build_segments(const int32_t *ids, int32_t M, int32_t n_adapters,
+                                  lora_segments_t seg, void *stream) {
+    if (M < 0 || M > LORA_MAX_ROWS || n_adapters < 1 || n_adapters > LORA_MAX_ADAPTERS)
+        return LORA_ERR_SHAPE;
+    if (M == 0) return LORA_OK;
+    if (!ids) return LORA_ERR_NULL;
+    lora_status_t st = check_seg(seg);
+    if (st != LORA_OK) return st;
+    if (!aligned(ids, 4)) return LORA_ERR_ALIGN;
+    clear_stale_error();
+    return hip_status(launch_build_segments(ids, M, n_adapters, to_seg(seg), (hipStream_t)stream));
+}
+
+lora_status_t lora_shrink(const void *x, const void *A, const int32_t *ranks, int32_t M,
+                          int32_t d_in, int32_t r_max, int32_t n_adapters, lora_segments_t seg,
+                          float *t, void *ws, size_t ws_bytes, void *stream) {
+    lora_status_t st = check_common(M, r_max, n_adapters);
+    if (st != LORA_OK) return st;
+    if (!dim_ok(d_in)) return LORA_ERR_SHAPE;
+    if (M == 0) return LORA_OK;
+    if (!x || !A || !t || !ws) return LORA_ERR_NULL;
+    if ((st = check_seg(seg)) != LORA_OK) return st;
+    if (!aligned(x, 16) || !aligned(A, 16) || !aligned(t, 16) || !aligned(ws, kAlign) ||
+        (ranks && !aligned(ranks, 4)))
+        return LORA_ERR_ALIGN;
+    if (ws_bytes < shrink_partial_bytes(M, d_in, r_max)) return LORA_ERR_WORKSPACE;
+    int kc, ksplit;
+    shrink_plan(d_in, &kc, &ksplit);
+    clear_stale_error();
+    hipStream_t s = (hipStream_t)stream;
+    float *partial = static_cast<float *>(ws);
+    const Seg sg = to_seg(seg);
+    hipError_t e = launch_shrink(static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(A),
+                                 ranks, M, d_in, r_max, n_adapters, sg, partial, kc, ksplit, s);
+    if (e == hipSuccess) e = launch_shrink_finalize(partial, M, r_max, ksplit, sg, t, s);
+    return hip_status(e);
+}
+
+lora_status_t lora_expand(const float *t, const void *B, const float *scale, const int32_t *ranks,
+                          int32_t M, int32_t d_out, int32_t r_max, int32_t n_adapters,
+                          lora_segments_t seg, void *y, lora_dtype_t y_dtype, void *stream) {
+    lora_status_t st = check_common(M, r_max, n_adapters);
+    if (st != LORA_OK) return st;
+    if (!dim_ok(d_out)) return LORA_ERR_SHAPE;
+    if (y_dtype != LORA_BF16 && y_dtype != LORA_F32) return LORA_ERR_DTYPE;
+    if (M == 0) return LORA_OK;
+    if (!t || !B || !scale || !y) return LORA_ERR_NULL;
+    if ((st = check_seg(seg)) != LORA_OK) return st;
+    if (!aligned(t, 16) || !aligned(B, 16) || !aligned(y, 16) || !aligned(scale, 4) ||
+        (ranks && !aligned(ranks, 4)))
+        return LORA_ERR_ALIGN;
+    clear_stale_error();
+    return hip_status(launch_expand(t, static_cast<const uint16_t *>(B), scale, ranks, M, d_out,
+                                    r_max, n_adapters, to_seg(seg), y, y_dtype == LORA_F32,
+                                    (hipStream_t)stream));
+}
+
+lora_status_t lora_linear(const void *x, const void *W, const void *A, const void *B,
+                          const float *scale, const int32_t *ranks, const int32_t *ids, int32_t M,
+                          int32_t d_in, int32_t d_out, int32_t r_max, int32_t n_adapters,
+                          const lora_segments_t *segs, void *y, lora_dtype_t y_dtype,
+                          lora_mode_t mode, void *ws, size_t ws_bytes, void *stream) {
+    lora_status_t st = check_common(M, r_max, n_adapters);
+    if (st != LORA_OK) return st;
+    if (!dim_ok(d_in) || !dim_ok(d_out)) return LORA_ERR_SHAPE;
+    if (y_dtype != LORA_BF16 && y_dtype != LORA_F32) return LORA_ERR_DTYPE;
+    if (mode != LORA_MODE_AUTO && mode != LORA_MODE_DECODE && mode != LORA_MODE_PREFILL)
+        return LORA_ERR_MODE;
+    if (M == 0) return LORA_OK;
+    if (!x || !W || !A || !B || !scale || !ids || !y || !ws) return LORA_ERR_NULL;
+    if (segs && (st = check_seg(*segs)) != LORA_OK) return st;
+    if (!aligned(x, 16) || !aligned(W, 16) || !aligned(A, 16) || !aligned(B, 16) ||
+        !aligned(y, 16) || !aligned(ws, kAlign) || !aligned(scale, 4) || !aligned(ids, 4) ||
+        (ranks && !aligned(ranks, 4)))
+        return LORA_ERR_ALIGN;
+    if (ws_bytes < lora_workspace_bytes(M, d_in, d_out, r_max, n_adapters)) return LORA_ERR_WORKSPACE;
+
+    const bool prefill = mode == LORA_MODE_PREFILL || (mode == LORA_MODE_AUTO && M >= LORA_PREFILL_MIN_ROWS);
+    hipStream_t s = (hipStream_t)stream;
+    char *p = static_cast<char *>(ws);
+    lora_segments_t own = carve_segments(p, M, n_adapters);
+    float *t = reinterpret_cast<float *>(p); p += t_bytes(M, r_max);
+    float *spart = reinterpret_cast<float *>(p); p += shrink_partial_bytes(M, d_in, r_max);
+    float *gpart = reinterpret_cast<float *>(p);
+    const size_t gpart_floats = gemm_partial_floats(M, d_in, d_out);
+
+    const lora_segments_t use = segs ? *segs : own;
+    const Seg sg = to_seg(use);
+    const uint16_t *xb = static_cast<const uint16_t *>(x);
+    clear_stale_error();
+    hipError_t e = hipSuccess;
+    if (!segs) e = launch_build_segments(ids, M, n_adapters, sg, s);
+    int kc, ksplit;
+    shrink_plan(d_in, &kc, &ksplit);
+    if (e == hipSuccess)
+        e = launch_shrink(xb, static_cast<const uint16_t *>(A), ranks, M, d_in, r_max, n_adapters, sg,
+                          spart, kc, ksplit, s);
+    if (e == hipSuccess) e = launch_shrink_finalize(spart, M, r_max, ksplit, sg, t, s);
+    if (e != hipSuccess) return hip_status(e);
+
+    const uint16_t *Wb = static_cast<const uint16_t *>(W);
+    const uint16_t *Bb = static_cast<const uint16_t *>(B);
+    const bool yf = y_dtype == LORA_F32;
+    if (prefill) {
+        LoraEpilogue ep{t, Bb, scale, ids, r_max, n_adapters};
+        e = launch_gemm(xb, Wb, M, d_in, d_out, y, yf, true, sg, &ep, nullptr, 0, s);
+    } else {
+        e = launch_gemm(xb, Wb, M, d_in, d_out, y, yf, false, sg, nullptr, gpart, gpart_floats, s);
+        if (e == hipSuccess)
+            e = launch_expand(t, Bb, scale, ranks, M, d_out, r_max, n_adapters, sg, y, yf, s);
+    }
+    return hip_status(e);
+}
+
+const char *lora_status_string(lora_status_t status) {
+    switch (status) {
+        case LORA_OK: return "LORA_OK";
+        case LORA_ERR_NULL: return "LORA_ERR_NULL: a required pointer is NULL";
+        case LORA_ERR_SHAPE: return "LORA_ERR_SHAPE: M, d_in, d_out or n_adapters out of range";
+        case LORA_ERR_RANK: return "LORA_ERR_RANK: r_max must be 8, 16, 32 or 64";
+        case LORA_ERR_ALIGN: return "LORA_ERR_ALIGN: a pointer is not aligned as required";
+        case LORA_ERR_WORKSPACE: return "LORA_ERR_WORKSPACE: workspace smaller than lora_workspace_bytes()";
+        case LORA_ERR_DTYPE: return "LORA_ERR_DTYPE: unknown output dtype";
+        case LORA_ERR_HIP: return "LORA_ERR_HIP: a kernel launch failed";
+        case LORA_ERR_BAD_ID: return "LORA_ERR_BAD_ID: adapter id out of range";
+        case LORA_ERR_MODE: return "LORA_ERR_MODE: unknown mode";
+    }
+    return "unknown lora_status_t";
+}
+
+const char *lora_last_hip_error(void) { return hipGetErrorString(g_last_hip_error); }
+
+}  // extern "C"

@@ -1,0 +1,93 @@
+// common.h -- device helpers and launch interfaces shared by the gfx950 kernels of
+// liblora_mi355x.so.  Internal: the public interface is include/lora.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lora.h"
+
+namespace lora {
+
+constexpr int kTileRows = LORA_TILE_ROWS;
+
+// Segment buffers as seen by the kernels.
+struct Seg {
+    int32_t *perm;
+    int32_t *offsets;
+    int32_t *seg_adapter;
+    int32_t *tiles;
+    int32_t *meta;
+};
+
+inline Seg to_seg(const lora_segments_t &s) {
+    return Seg{s.perm, s.offsets, s.seg_adapter, s.tiles, s.meta};
+}
+
+// ---- bfloat16 <-> float32 --------------------------------------------------------------
+// bf16 is the high half of a float32 word: widening is a shift, exact.
+__device__ __forceinline__ float bf16_lo(uint32_t packed) { return __uint_as_float(packed << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t packed) { return __uint_as_float(packed & 0xFFFF0000u); }
+
+// Round to nearest even; a NaN stays a (quiet) NaN.  Branch-free (a select).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    const uint32_t u = __float_as_uint(f);
+    const uint32_t rounded = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+    const uint32_t quiet_nan = (u >> 16) | 0x40u;
+    return (f != f) ? quiet_nan : rounded;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+// 8 bf16 (one 16-byte vector) -> 8 floats
+__device__ __forceinline__ void unpack8(const uint4 v, float f[8]) {
+    f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
+    f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+    f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z);
+    f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+}
+
+__device__ __forceinline__ uint4 ld16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
+__device__ __forceinline__ void st16(void *p, uint4 v) { *reinterpret_cast<uint4 *>(p) = v; }
+
+// ---- launchers (one per kernel family) -------------------------------------------------
+
+hipError_t launch_build_segments(const int32_t *ids, int M, int n_adapters, Seg seg,
+                                 hipStream_t s);
+
+// Split-K shrink: partial[ks][m][j] for rows of every tile; ks = 0..ksplit-1, chunks of
+// kc columns of x.  Followed by launch_shrink_finalize to sum the partials into t.
+hipError_t launch_shrink(const uint16_t *x, const uint16_t *A, const int32_t *ranks, int M,
+                         int d_in, int r_max, int n_adapters, Seg seg, float *partial, int kc,
+                         int ksplit, hipStream_t s);
+hipError_t launch_shrink_finalize(const float *partial, int M, int r_max, int ksplit, Seg seg,
+                                  float *t, hipStream_t s);
+
+hipError_t launch_expand(const float *t, const uint16_t *B, const float *scale,
+                         const int32_t *ranks, int M, int d_out, int r_max, int n_adapters,
+                         Seg seg, void *y, bool y_f32, hipStream_t s);
+
+// LoRA epilogue arguments of the prefill GEMM (rows are taken in segment order).
+struct LoraEpilogue {
+    const float *t;        // [M][r_max]
+    const uint16_t *B;     // [n][r_max][d_out]
+    const float *scale;    // [n]
+    const int32_t *ids;    // [M]
+    int r_max;
+    int n_adapters;
+};
+
+// y = x W (+ LoRA epilogue when lora != nullptr).  `prefill` selects the 256x256 tiling
+// and segment-ordered rows; otherwise a decode tiling with split-K partials in `ws`.
+hipError_t launch_gemm(const uint16_t *x, const uint16_t *W, int M, int K, int N, void *y,
+                       bool y_f32, bool prefill, Seg seg, const LoraEpilogue *lora,
+                       float *ws_partial, size_t ws_partial_floats, hipStream_t s);
+
+// Workspace floats the decode GEMM needs for split-K partials at these sizes.
+size_t gemm_partial_floats(int M, int K, int N);
+
+// Split-K plan of the shrink for d_in.
+void shrink_plan(int d_in, int *kc, int *ksplit);
+
+}  // namespace lora

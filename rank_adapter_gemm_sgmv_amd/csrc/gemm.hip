@@ -1,0 +1,384 @@
+// gemm.hip -- the shared base term y = x W on bf16 MFMA (gfx950), with the LoRA delta
+// fused into the epilogue for prefill.
+//
+// Source: "Multi-LoRA Serving: Why 100 Adapters Fit on One GPU" (dev.to), "Why can't you
+// just merge LoRA weights into the base model?": the x W term is one big GEMM across the
+// whole batch; "How does one batch run 30 different adapters at once?": prefill is
+// compute-bound and the delta is small next to x W.
+//
+// Operands: x[M][K] (K contiguous) and W[K][N] (N contiguous), bf16.  The gfx950 MFMA
+// v_mfma_f32_32x32x16_bf16 takes, per lane, 8 consecutive-k values of one row of the left
+// operand and 8 consecutive-k values of one column of the right operand.  x tiles go to LDS
+// as they are ([row][k]).  W tiles are loaded as 8x8 blocks (8 k rows x 16 bytes), transposed
+// in registers with byte permutes and stored to LDS as [n][k], so both operands are read
+// from LDS with one 16-byte read per lane per MFMA.  LDS rows are padded by 16 bytes.
+//
+// Pipeline: LDS double buffer, one barrier per 64-deep k step; the global loads of step
+// k+1 are in flight while step k's MFMAs run.
+//
+// Tilings: prefill 256 x 256 (4 waves of 128 x 128, 16 accumulators of 32 x 32 each);
+// decode 64 x 64, 128 x 64 or 128 x 128 with split-K partial sums reduced by a second
+// kernel in split order.  Prefill tiles are mapped XCD-aware: workgroup b runs on XCD b % 8,
+// so each XCD is handed a compact 4 x 8 block of tiles and its L2 serves the x and W panels
+// those tiles share.
+//
+// Prefill epilogue (segment-ordered rows): the tile's rows are positions of perm, so each
+// tile holds a few long runs of one adapter.  For every run, T = scale_a * t[rows, :] (bf16)
+// and B_a[:, tile columns] (transposed in registers as above) are staged in LDS and added to
+// the accumulators by r_max / 16 more MFMA steps -- the K-extension [x | T] [W ; B_a] -- before
+// the only store of y.  Rows with id -1 get no delta.
+#include "common.h"
+
+namespace lora {
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int kBK = 64;
+constexpr int kLDK = kBK + 8;  // LDS row length in bf16 (16-byte pad)
+
+// 8x8 bf16 transpose: in[kk] = 8 consecutive n at row kk (4 dwords, low half = even n);
+// out[nn] = 8 consecutive k at column nn.
+__device__ __forceinline__ void transpose8x8(const uint4 in[8], uint4 out[8]) {
+    const uint32_t *r = reinterpret_cast<const uint32_t *>(in);
+    uint32_t *o = reinterpret_cast<uint32_t *>(out);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {      // dword p of a row holds columns 2p, 2p+1
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {  // dword q of a column holds rows 2q, 2q+1
+            const uint32_t lo = r[(2 * q) * 4 + p], hi = r[(2 * q + 1) * 4 + p];
+            o[(2 * p) * 4 + q] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);      // even column
+            o[(2 * p + 1) * 4 + q] = __builtin_amdgcn_perm(hi, lo, 0x07060302u);  // odd column
+        }
+    }
+}
+
+template <int BM_, int BN_, int WM_, int WN_>
+struct Cfg {
+    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+    static constexpr int NT = 64 * WM * WN;
+    static constexpr int WTM = BM / WM, WTN = BN / WN;
+    static constexpr int TM = WTM / 32, TN = WTN / 32;
+    static constexpr int XCH = BM * (kBK / 8) / NT;           // x 16-byte chunks per thread
+    static constexpr int WBL = (kBK / 8) * (BN / 8);          // 8x8 W blocks per tile
+    static constexpr int WB = (WBL + NT - 1) / NT;            // W blocks per thread
+    static_assert(TM >= 1 && TN >= 1 && XCH >= 1, "tile shape");
+    static_assert(BM * (kBK / 8) % NT == 0, "x chunks must divide evenly");
+};
+
+// Prefill tile order: XCD-major, then groups of 4 tile rows, column-major inside a group.
+__device__ __forceinline__ void tile_coords(int b, int n_tm, int n_tn, bool xcd_remap, int &tm,
+                                            int &tn) {
+    const int T = n_tm * n_tn;
+    int lin = b;
+    if (xcd_remap && (T % 8) == 0) lin = (b % 8) * (T / 8) + b / 8;
+    constexpr int G = 4;
+    const int group = lin / (G * n_tn);
+    const int first = group * G;
+    const int gsz = min(n_tm - first, G);
+    const int in = lin % (G * n_tn);
+    tm = first + in % gsz;
+    tn = in / gsz;
+}
+
+// One 16-deep MFMA step of a wave's TM x TN block of 32x32 accumulators; operands from LDS.
+template <class C>
+__device__ __forceinline__ void mfma_step(f32x16_t (&acc)[C::TM][C::TN], const uint16_t *as,
+                                          const uint16_t *bs, int wm0, int wn0, int lane, int kk) {
+    const int koff = kk * 16 + (lane >> 5) * 8;
+    bf16x8_t af[C::TM], bf[C::TN];
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+        af[i] = *reinterpret_cast<const bf16x8_t *>(&as[(wm0 + i * 32 + (lane & 31)) * kLDK + koff]);
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j)
+        bf[j] = *reinterpret_cast<const bf16x8_t *>(&bs[(wn0 + j * 32 + (lane & 31)) * kLDK + koff]);
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+}
+
+// Global loads of one 64-deep k step: x chunks (16 bytes) and 8x8 W blocks.
+template <class C>
+__device__ __forceinline__ void load_tile(uint4 (&xr)[C::XCH], uint4 (&wr)[C::WB][8],
+                                          const uint16_t *__restrict__ x,
+                                          const uint16_t *__restrict__ W, const int (&xrow)[C::XCH],
+                                          int tid, int k0, int kz1, int K, int N, int n0) {
+#pragma unroll
+    for (int i = 0; i < C::XCH; ++i) {
+        const int kc = ((tid + i * C::NT) % (kBK / 8)) * 8;
+        xr[i] = (xrow[i] >= 0 && k0 + kc < kz1) ? ld16(x + (size_t)xrow[i] * K + k0 + kc)
+                                                 : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < C::WB; ++j) {
+        const int b = tid + j * C::NT;
+        const int kb = b % 8, nb = b / 8;
+        const int n = n0 + nb * 8;
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+            const int k = k0 + kb * 8 + kk;
+            wr[j][kk] = (b < C::WBL && n < N && k < kz1) ? ld16(W + (size_t)k * N + n)
+                                                         : make_uint4(0, 0, 0, 0);
+        }
+    }
+}
+
+template <class C>
+__device__ __forceinline__ void store_tile(const uint4 (&xr)[C::XCH], const uint4 (&wr)[C::WB][8],
+                                           uint16_t *as, uint16_t *bs, int tid) {
+#pragma unroll
+    for (int i = 0; i < C::XCH; ++i) {
+        const int c = tid + i * C::NT;
+        st16(&as[(c / (kBK / 8)) * kLDK + (c % (kBK / 8)) * 8], xr[i]);
+    }
+#pragma unroll
+    for (int j = 0; j < C::WB; ++j) {
+        const int b = tid + j * C::NT;
+        if (b < C::WBL) {
+            const int kb = b % 8, nb = b / 8;
+            uint4 t8[8];
+            transpose8x8(wr[j], t8);
+#pragma unroll
+            for (int nn = 0; nn < 8; ++nn) st16(&bs[(nb * 8 + nn) * kLDK + kb * 8], t8[nn]);
+        }
+    }
+}
+
+template <class C, bool PREFILL, bool YF32>
+__global__ __launch_bounds__(C::NT) void gemm_kernel(const uint16_t *__restrict__ x,
+                                                     const uint16_t *__restrict__ W, int M, int K,
+                                                     int N, void *__restrict__ y,
+                                                     float *__restrict__ partial, int k_per_split,
+                                                     int n_tm, int n_tn, Seg seg, LoraEpilogue ep) {
+    constexpr int BM = C::BM, BN = C::BN, NT = C::NT;
+    __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * kLDK];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * kLDK];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm0 = (wave / C::WN) * C::WTM, wn0 = (wave % C::WN) * C::WTN;
+
+    int tmi, tni;
+    tile_coords(blockIdx.x, n_tm, n_tn, PREFILL, tmi, tni);
+    const int row0 = tmi * BM, n0 = tni * BN;
+    const int split = blockIdx.y;
+    const int kz0 = split * k_per_split;
+    const int kz1 = min(K, kz0 + k_per_split);
+
+    // rows of x this thread loads (fixed over the k loop); -1 = beyond M
+    int xrow[C::XCH];
+#pragma unroll
+    for (int i = 0; i < C::XCH; ++i) {
+        const int rr = row0 + (tid + i * NT) / (kBK / 8);
+        int m = -1;
+        if (rr < M) m = PREFILL ? seg.perm[rr] : rr;
+        xrow[i] = m;
+    }
+
+    uint4 xr[C::XCH];
+    uint4 wr[C::WB][8];
+    f32x16_t acc[C::TM][C::TN];
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+    const int nk = (kz1 - kz0 + kBK - 1) / kBK;
+    if (nk > 0) {
+        load_tile<C>(xr, wr, x, W, xrow, tid, kz0, kz1, K, N, n0);
+        store_tile<C>(xr, wr, As[0], Bs[0], tid);
+    }
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const int cur = kt & 1;
+        if (kt + 1 < nk) load_tile<C>(xr, wr, x, W, xrow, tid, kz0 + (kt + 1) * kBK, kz1, K, N, n0);
+#pragma unroll
+        for (int kk = 0; kk < kBK / 16; ++kk) mfma_step<C>(acc, As[cur], Bs[cur], wm0, wn0, lane, kk);
+        if (kt + 1 < nk) store_tile<C>(xr, wr, As[cur ^ 1], Bs[cur ^ 1], tid);
+        __syncthreads();
+    }
+
+    if constexpr (PREFILL) {
+        // LoRA delta for the runs of one adapter inside this tile's rows (positions of perm).
+        const int n_lora = seg.meta[1];
+        const int RM = ep.r_max;
+        const int KE = RM < 16 ? 16 : RM;  // k extent of the extension, multiple of 16
+        int p = row0;
+        const int p_end = min(row0 + BM, n_lora);
+        while (p < p_end) {
+            const int a = ep.ids[seg.perm[p]];
+            if (a < 0 || a >= ep.n_adapters) break;  // segments not built for these ids
+            const int q_end = min(seg.offsets[a + 1], p_end);
+            if (q_end <= p) break;
+            const float s = ep.scale[a];
+            // T rows: scale_a * t for rows of this run, zero elsewhere
+            for (int c = tid; c < BM * (KE / 8); c += NT) {
+                const int rr = c / (KE / 8), jc = (c % (KE / 8)) * 8;
+                const int pos = row0 + rr;
+                uint4 v = make_uint4(0, 0, 0, 0);
+                if (pos >= p && pos < q_end && jc < RM) {
+                    const float *tp = ep.t + (size_t)seg.perm[pos] * RM + jc;
+                    const float4 t0 = *reinterpret_cast<const float4 *>(tp);
+                    const float4 t1 = *reinterpret_cast<const float4 *>(tp + 4);
+                    v = make_uint4(pack_bf16x2(s * t0.x, s * t0.y), pack_bf16x2(s * t0.z, s * t0.w),
+                                   pack_bf16x2(s * t1.x, s * t1.y), pack_bf16x2(s * t1.z, s * t1.w));
+                }
+                st16(&As[0][rr * kLDK + jc], v);
+            }
+            // B_a[j][n0 + n] transposed to [n][j]
+            for (int b = tid; b < (KE / 8) * (BN / 8); b += NT) {
+                const int jb = b % (KE / 8), nb = b / (KE / 8);
+                const int n = n0 + nb * 8;
+                uint4 blk[8], tb[8];
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj) {
+                    const int j = jb * 8 + jj;
+                    blk[jj] = (j < RM && n < N) ? ld16(ep.B + ((size_t)a * RM + j) * N + n)
+                                                : make_uint4(0, 0, 0, 0);
+                }
+                transpose8x8(blk, tb);
+#pragma unroll
+                for (int nn = 0; nn < 8; ++nn) st16(&Bs[0][(nb * 8 + nn) * kLDK + jb * 8], tb[nn]);
+            }
+            __syncthreads();
+            for (int kk = 0; kk < KE / 16; ++kk) mfma_step<C>(acc, As[0], Bs[0], wm0, wn0, lane, kk);
+            __syncthreads();
+            p = q_end;
+        }
+    }
+
+    // store: accumulator register v of a 32x32 block holds row (v/4)*8 + (lane/32)*4 + v%4,
+    // column lane%32
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i) {
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j) {
+            const int col = n0 + wn0 + j * 32 + (lane & 31);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int rr = row0 + wm0 + i * 32 + (v / 4) * 8 + (lane >> 5) * 4 + (v % 4);
+                if (rr < M && col < N) {
+                    const int m = PREFILL ? seg.perm[rr] : rr;
+                    const float val = acc[i][j][v];
+                    if (partial != nullptr) {
+                        partial[((size_t)split * M + m) * N + col] = val;
+                    } else if constexpr (YF32) {
+                        reinterpret_cast<float *>(y)[(size_t)m * N + col] = val;
+                    } else {
+                        reinterpret_cast<uint16_t *>(y)[(size_t)m * N + col] = (uint16_t)f32_to_bf16_rne(val);
+                    }
+                }
+            }
+        }
+    }
+}
+
+// y[m][n] = sum over splits (ascending) of partial[split][m][n]; 4 columns per thread.
+template <bool YF32>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restrict__ partial,
+                                                            int M, int N, int ksplit,
+                                                            void *__restrict__ y) {
+    const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    const long total = (long)M * N / 4;
+    if (idx >= total) return;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int z = 0; z < ksplit; ++z) {
+        const float4 v = reinterpret_cast<const float4 *>(partial + (size_t)z * M * N)[idx];
+        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+    if constexpr (YF32) {
+        reinterpret_cast<float4 *>(y)[idx] = acc;
+    } else {
+        uint2 o = make_uint2(pack_bf16x2(acc.x, acc.y), pack_bf16x2(acc.z, acc.w));
+        reinterpret_cast<uint2 *>(y)[idx] = o;
+    }
+}
+
+using CfgPrefill = Cfg<256, 256, 2, 2>;
+using CfgD64 = Cfg<64, 64, 2, 2>;
+using CfgD128x64 = Cfg<128, 64, 2, 2>;
+using CfgD128 = Cfg<128, 128, 2, 2>;
+
+struct DecodePlan {
+    int bm, bn, ksplit, k_per_split;
+};
+
+DecodePlan decode_plan(int M, int K, int N) {
+    DecodePlan p;
+    if (M <= 64) { p.bm = 64; p.bn = 64; }
+    else if (M <= 256) { p.bm = 128; p.bn = 64; }
+    else { p.bm = 128; p.bn = 128; }
+    const long tiles = (long)((M + p.bm - 1) / p.bm) * ((N + p.bn - 1) / p.bn);
+    const int ksteps = (K + kBK - 1) / kBK;
+    int ks = (int)((512 + tiles - 1) / tiles);  // aim at about two workgroups per CU
+    ks = ks < 1 ? 1 : ks;
+    const int max_ks = ksteps / 4 > 0 ? ksteps / 4 : 1;  // at least 4 k steps per split
+    if (ks > max_ks) ks = max_ks;
+    if (ks > 16) ks = 16;
+    const int steps_per = (ksteps + ks - 1) / ks;
+    p.k_per_split = steps_per * kBK;
+    p.ksplit = (K + p.k_per_split - 1) / p.k_per_split;
+    return p;
+}
+
+template <class C, bool PREFILL>
+hipError_t launch_cfg(const uint16_t *x, const uint16_t *W, int M, int K, int N, void *y, bool y_f32,
+                      float *partial, int ksplit, int k_per_split, Seg seg, const LoraEpilogue *lora,
+                      hipStream_t s) {
+    const int n_tm = (M + C::BM - 1) / C::BM, n_tn = (N + C::BN - 1) / C::BN;
+    LoraEpilogue ep{};
+    if (lora) ep = *lora;
+    dim3 grid(n_tm * n_tn, ksplit);
+    if (y_f32)
+        hipLaunchKernelGGL((gemm_kernel<C, PREFILL, true>), grid, dim3(C::NT), 0, s, x, W, M, K, N, y,
+                           partial, k_per_split, n_tm, n_tn, seg, ep);
+    else
+        hipLaunchKernelGGL((gemm_kernel<C, PREFILL, false>), grid, dim3(C::NT), 0, s, x, W, M, K, N, y,
+                           partial, k_per_split, n_tm, n_tn, seg, ep);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t gemm_partial_floats(int M, int K, int N) {
+    const DecodePlan p = decode_plan(M, K, N);
+    return p.ksplit > 1 ? (size_t)p.ksplit * M * N : 0;
+}
+
+hipError_t launch_gemm(const uint16_t *x, const uint16_t *W, int M, int K, int N, void *y,
+                       bool y_f32, bool prefill, Seg seg, const LoraEpilogue *lora,
+                       float *ws_partial, size_t ws_partial_floats, hipStream_t s) {
+    if (prefill)
+        return launch_cfg<CfgPrefill, true>(x, W, M, K, N, y, y_f32, nullptr, 1, K, seg, lora, s);
+
+    const DecodePlan p = decode_plan(M, K, N);
+    float *partial = nullptr;
+    if (p.ksplit > 1) {
+        if ((size_t)p.ksplit * M * N > ws_partial_floats || ws_partial == nullptr)
+            return hipErrorInvalidValue;
+        partial = ws_partial;
+    }
+    hipError_t e;
+    if (p.bm == 64)
+        e = launch_cfg<CfgD64, false>(x, W, M, K, N, y, y_f32, partial, p.ksplit, p.k_per_split, seg, nullptr, s);
+    else if (p.bn == 64)
+        e = launch_cfg<CfgD128x64, false>(x, W, M, K, N, y, y_f32, partial, p.ksplit, p.k_per_split, seg, nullptr, s);
+    else
+        e = launch_cfg<CfgD128, false>(x, W, M, K, N, y, y_f32, partial, p.ksplit, p.k_per_split, seg, nullptr, s);
+    if (e != hipSuccess || p.ksplit == 1) return e;
+    const long threads = (long)M * N / 4;
+    const int grid = (int)((threads + 255) / 256);
+    if (y_f32)
+        hipLaunchKernelGGL(splitk_reduce_kernel<true>, dim3(grid), dim3(256), 0, s, partial, M, N, p.ksplit, y);
+    else
+        hipLaunchKernelGGL(splitk_reduce_kernel<false>, dim3(grid), dim3(256), 0, s, partial, M, N, p.ksplit, y);
+    return hipGetLastError();
+}
+
+}  // namespace lora

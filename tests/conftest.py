@@ -27,3 +27,19 @@ def oracle_lib():
 
     oracle.build()
     return oracle
+
+
+_WORKLOADS = {}
+
+
+@pytest.fixture(scope="session")
+def workload_cache():
+    """Named workloads drawn once per session (config 5 holds about 1.4 GB of pools)."""
+    from synth import make_workload
+
+    def get(config: int):
+        if config not in _WORKLOADS:
+            _WORKLOADS[config] = make_workload(config)
+        return _WORKLOADS[config]
+
+    return get

@@ -1,0 +1,116 @@
+"""The C-ABI library on the host: it loads without a GPU, exports every symbol the header
+declares, sizes workspaces, and rejects bad arguments before enqueueing anything.
+
+CPU only: no call here reaches a kernel launch.  Fake non-NULL device addresses are used
+only where validation fails before any pointer is touched.
+"""
+
+import os
+import re
+
+import pytest
+
+from rank_adapter_gemm_sgmv_amd import lora as L
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                      "lora.h")
+
+FAKE = 1 << 20  # 16/256-byte aligned, never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lora_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert set(names) == set(L.EXPORTS), names
+    for name in names:
+        assert hasattr(L.library(), name), name
+
+
+def test_status_strings():
+    for code, name in L.STATUS.items():
+        assert L.lora_status_string(code).startswith(name)
+    assert "unknown" in L.lora_status_string(99)
+
+
+def test_max_tiles():
+    assert L.lora_max_tiles(0, 4) == 0
+    assert L.lora_max_tiles(16, 4) == 4 + 1
+    assert L.lora_max_tiles(512, 1024) == 512 + 32
+    assert L.lora_max_tiles(4096, 8) == 8 + 256
+
+
+def test_workspace_bytes():
+    assert L.lora_workspace_bytes(0, 4096, 4096, 16, 32) == 0
+    assert L.lora_workspace_bytes(64, 4096, 4096, 12, 32) == 0  # bad rank
+    assert L.lora_workspace_bytes(64, 4095, 4096, 16, 32) == 0  # d_in not a multiple of 8
+    b = L.lora_workspace_bytes(64, 4096, 4096, 16, 32)
+    assert b > 0 and b % 256 == 0
+    # grows with rows, rank and adapters
+    assert L.lora_workspace_bytes(128, 4096, 4096, 16, 32) > b
+    assert L.lora_workspace_bytes(64, 4096, 4096, 64, 32) > b
+    assert L.lora_workspace_bytes(64, 4096, 4096, 16, 4096) > b
+
+
+def _linear(**over):
+    args = dict(x=FAKE, W=FAKE, A=FAKE, B=FAKE, scale=FAKE, ranks=None, ids=FAKE, M=64, d_in=4096,
+                d_out=4096, r_max=16, n_adapters=32, segs=None, y=FAKE, y_dtype=L.LORA_BF16,
+                mode=L.LORA_MODE_DECODE, ws=FAKE, ws_bytes=0, stream=0)
+    args.update(over)
+    return L.lora_linear(**args)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(M=-1), 2), (dict(M=L.LORA_MAX_ROWS + 1), 2), (dict(d_in=12), 2), (dict(d_out=0), 2),
+    (dict(n_adapters=0), 2), (dict(n_adapters=L.LORA_MAX_ADAPTERS + 1), 2),
+    (dict(r_max=12), 3), (dict(r_max=128), 3), (dict(r_max=0), 3),
+    (dict(y_dtype=5), 6), (dict(mode=7), 9),
+    (dict(x=None), 1), (dict(W=None), 1), (dict(ids=None), 1), (dict(ws=None), 1),
+    (dict(x=FAKE + 2), 4), (dict(y=FAKE + 8), 4), (dict(ws=FAKE + 16), 4),
+    (dict(ws_bytes=1024), 5),
+])
+def test_linear_rejects(over, code):
+    with pytest.raises(L.LoraError) as e:
+        _linear(**over)
+    assert e.value.status == code
+
+
+def test_linear_empty_batch_is_noop():
+    _linear(M=0, x=None, y=None, ws=None)  # M = 0 returns LORA_OK, nothing enqueued
+
+
+def test_build_segments_rejects():
+    seg = L.lora_segments_t(FAKE, FAKE, FAKE, FAKE, FAKE)
+    with pytest.raises(L.LoraError) as e:
+        L.lora_build_segments(None, 10, 4, seg, stream=0)
+    assert e.value.status == 1
+    with pytest.raises(L.LoraError) as e:
+        L.lora_build_segments(FAKE, 10, 0, seg, stream=0)
+    assert e.value.status == 2
+    with pytest.raises(L.LoraError) as e:
+        L.lora_build_segments(FAKE, 10, 4, L.lora_segments_t(FAKE, None, FAKE, FAKE, FAKE), stream=0)
+    assert e.value.status == 1
+    with pytest.raises(L.LoraError) as e:
+        L.lora_build_segments(FAKE + 2, 10, 4, seg, stream=0)
+    assert e.value.status == 4
+    L.lora_build_segments(None, 0, 4, seg, stream=0)  # empty batch: no-op
+
+
+def test_shrink_expand_reject():
+    seg = L.lora_segments_t(FAKE, FAKE, FAKE, FAKE, FAKE)
+    with pytest.raises(L.LoraError) as e:
+        L.lora_shrink(FAKE, FAKE, None, 64, 4096, 16, 32, seg, FAKE, FAKE, 16, stream=0)
+    assert e.value.status == 5
+    with pytest.raises(L.LoraError) as e:
+        L.lora_shrink(FAKE, FAKE, None, 64, 4096, 24, 32, seg, FAKE, FAKE, 1 << 30, stream=0)
+    assert e.value.status == 3
+    with pytest.raises(L.LoraError) as e:
+        L.lora_expand(FAKE, FAKE, None, None, 64, 4096, 16, 32, seg, FAKE, 0, stream=0)
+    assert e.value.status == 1
+    with pytest.raises(L.LoraError) as e:
+        L.lora_expand(FAKE, FAKE, FAKE, None, 64, 4096, 16, 32, seg, FAKE, 3, stream=0)
+    assert e.value.status == 6
