@@ -1,0 +1,434 @@
+"""Benchmark of the multi-LoRA batched linear on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step = one lora_linear call (segment build, shrink, base GEMM, expand) on one batch.
+The headline workload is the decode batch of the Llama-2-7B q_proj geometry: x[64, 4096]
+bf16, W[4096, 4096], 32 resident adapters of rank 16, one adapter id per row (uniform,
+unsorted), alpha = 32.  Inputs are synthetic (seeded generator) and resident in HBM before
+the timed region.  Each step uses the next of several device copies of (W, A, B) ("layers"),
+enough to exceed the 256 MB Infinity Cache, so the weights stream from HBM as they would in a
+forward pass over many layers.  The K timed steps are one HIP graph (captured once, checked
+against an eager call) replayed once between two synchronisations.
+
+Prints one JSON line: tokens/s, ms per step, the roofline of the dominant kernel (HIP-event
+duration per launch, algorithmic bytes or flops per launch), the CPU oracle timed on the
+host as a baseline, a per-kernel breakdown, and the same measurements for the other decode
+and prefill workloads under "workloads".
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+MALL_BYTES = 256 << 20       # Infinity Cache
+ROTATE_BYTES = 640 << 20     # device bytes of weights cycled through per rotation
+
+METRIC = "LoRA-linear tokens/s (decode & prefill, 4096²) + % HBM / MFMA peak"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------------------
+# algorithmic work per kernel launch
+# ---------------------------------------------------------------------------------------
+
+
+def algorithmic_work(w, d_in: int, d_out: int, prefill: bool, y_bytes: int = 2) -> dict:
+    """Bytes and flops the method must move / compute, per kernel of one call.
+
+    Adapters count at their true rank and only when touched; x rows with an adapter are read
+    once by the shrink; t is written once and read once (fp32); y is read and written once
+    by the expand on LoRA rows.  The base GEMM reads W and x and writes y once.  Padded
+    ranks, untouched adapters, id -1 rows and split-K partial sums are not counted.
+    """
+    ids, ranks = w.ids, w.ranks
+    M = w.M
+    lora = ids >= 0
+    m_lora = int(lora.sum())
+    touched = np.unique(ids[lora])
+    r_touched = int(ranks[touched].sum()) if len(touched) else 0
+    r_rows = int(ranks[ids[lora]].sum()) if m_lora else 0
+    a_bytes = r_touched * d_in * 2
+    b_bytes = r_touched * d_out * 2
+    t_bytes = r_rows * 4
+    shrink = a_bytes + m_lora * d_in * 2 + t_bytes
+    expand = b_bytes + t_bytes + 2 * m_lora * d_out * y_bytes
+    base_flops = 2.0 * M * d_in * d_out
+    lora_flops = 2.0 * r_rows * (d_in + d_out)
+    gemm_bytes = d_in * d_out * 2 + M * d_in * 2
+    out = {
+        "build_segments": {"bytes": 8 * M, "flops": 0.0},
+        "shrink": {"bytes": shrink, "flops": 2.0 * r_rows * d_in},
+        "shrink_finalize": {"bytes": 0, "flops": 0.0},
+        "splitk_reduce": {"bytes": M * d_out * y_bytes, "flops": 0.0},
+        "expand": {"bytes": expand, "flops": 2.0 * r_rows * d_out},
+        "lora_bytes": shrink + expand,
+        "call_flops": base_flops + lora_flops,
+        "call_bytes": gemm_bytes + M * d_out * y_bytes + shrink + expand,
+    }
+    if prefill:
+        out["gemm_prefill_lora"] = {"bytes": gemm_bytes + M * d_out * y_bytes,
+                                    "flops": base_flops + 2.0 * r_rows * d_out}
+    else:
+        out["gemm_decode"] = {"bytes": gemm_bytes, "flops": base_flops}
+    return out
+
+
+# ---------------------------------------------------------------------------------------
+# device setup
+# ---------------------------------------------------------------------------------------
+
+
+def _bf16(bits, torch):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+class DeviceLayers:
+    """Device copies ("layers") of one projection's weights, cycled step by step."""
+
+    def __init__(self, w, pi, n_layers, rotate_x, torch):
+        p = w.projections[pi]
+        self.d_in, self.d_out = p.d_in, p.d_out
+        self.layers = []
+        x0 = _bf16(p.x, torch)
+        for i in range(n_layers):
+            W = _bf16(p.W, torch)
+            A = _bf16(p.A, torch)
+            B = _bf16(p.B, torch)
+            x = _bf16(p.x, torch) if (rotate_x and i > 0) else x0
+            self.layers.append((x, W, A, B))
+
+
+def layers_needed(w, rotate_x: bool) -> int:
+    per = 0
+    for p in w.projections:
+        per += p.W.nbytes + p.A.nbytes + p.B.nbytes + (p.x.nbytes if rotate_x else 0)
+    return max(1, -(-ROTATE_BYTES // per))
+
+
+class Runner:
+    """One workload on the device: L layers, shared ids / ranks / scale, one output per
+    projection, workspace; `step(i)` enqueues one step (all projections) for layer i % L."""
+
+    def __init__(self, w, mode, torch, L, rotate_x=False, prebuilt_segments=False):
+        self.torch, self.w, self.mode, self.L = torch, w, mode, L
+        self.M, self.n, self.r_max = w.M, w.n_adapters, w.r_max
+        self.ids = torch.from_numpy(w.ids.astype(np.int32)).cuda()
+        self.ranks = torch.from_numpy(w.ranks.astype(np.int32)).cuda()
+        self.scale = torch.from_numpy((w.alpha / w.ranks.astype(np.float32)).astype(np.float32)).cuda()
+        self.projs = [DeviceLayers(w, pi, L, rotate_x, torch) for pi in range(len(w.projections))]
+        self.ys = [torch.empty((w.M, pr.d_out), dtype=torch.bfloat16, device="cuda") for pr in self.projs]
+        nb = max(L_.lora_workspace_bytes(w.M, pr.d_in, pr.d_out, w.r_max, w.n_adapters) for pr in self.projs)
+        self.ws = torch.empty(max(nb, 256), dtype=torch.uint8, device="cuda")
+        self.ws_bytes = nb
+        self.segs = L_.Segments(w.M, w.n_adapters) if prebuilt_segments else None
+
+    def step(self, i):
+        li = i % self.L
+        if self.segs is not None:
+            L_.lora_build_segments(self.ids, self.M, self.n, self.segs)
+        for pr, y in zip(self.projs, self.ys):
+            x, W, A, B = pr.layers[li]
+            L_.lora_linear(x, W, A, B, self.scale, self.ranks, self.ids, self.M, pr.d_in, pr.d_out,
+                           self.r_max, self.n, self.segs, y, L_.LORA_BF16, self.mode, self.ws,
+                           self.ws_bytes)
+
+    def profile(self, i):
+        """Per-kernel HIP-event durations of one step (queued behind a GPU sleep)."""
+        torch = self.torch
+        li = i % self.L
+        torch.cuda._sleep(2_000_000)
+        out = []
+        if self.segs is not None:
+            L_.lora_build_segments(self.ids, self.M, self.n, self.segs)
+        for pr, y in zip(self.projs, self.ys):
+            x, W, A, B = pr.layers[li]
+            ks = L_.lora_linear_profiled(x, W, A, B, self.scale, self.ranks, self.ids, self.M,
+                                         pr.d_in, pr.d_out, self.r_max, self.n, self.segs, y,
+                                         L_.LORA_BF16, self.mode, self.ws, self.ws_bytes)
+            out.append(ks)
+        return out
+
+
+def capture(runner, steps, torch):
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        runner.step(0)  # eager warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for i in range(steps):
+            runner.step(i)
+    torch.cuda.synchronize()
+    return g
+
+
+def check_graph_against_eager(runner, graph, torch):
+    """The graph's outputs equal an eager step on the same (last) layer, bit for bit."""
+    graph.replay()
+    torch.cuda.synchronize()
+    from_graph = [y.clone() for y in runner.ys]
+    last = runner.L - 1  # graphs below always end on a whole number of rotations
+    runner.step(last)
+    torch.cuda.synchronize()
+    for a, b in zip(from_graph, runner.ys):
+        if not torch.equal(a.view(torch.int16), b.view(torch.int16)):
+            raise RuntimeError("graph replay differs from the eager call")
+
+
+def measure(runner, steps, warmup, torch, profile_reps=20):
+    """Timed graph replay of exactly `steps` steps, plus per-kernel averages."""
+    L = runner.L
+    steps_g = steps
+    g = capture(runner, steps_g, torch)
+    gw = capture(runner, max(1, warmup), torch) if warmup > 0 else None
+    if steps_g % L == 0:
+        check_graph_against_eager(runner, g, torch)
+    if gw is not None:
+        gw.replay()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    g.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_total = ev0.elapsed_time(ev1)
+    # eager steps, for reference (host launch cost included)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    n_eager = min(steps, 50)
+    for i in range(n_eager):
+        runner.step(i)
+    torch.cuda.synchronize()
+    eager_ms = (time.perf_counter() - t1) * 1e3 / n_eager
+    # per-kernel durations
+    sums, counts = {}, {}
+    for i in range(profile_reps):
+        for pi, ks in enumerate(runner.profile(i)):
+            for name, ms in ks:
+                key = (pi, name)
+                sums[key] = sums.get(key, 0.0) + ms
+                counts[key] = counts.get(key, 0) + 1
+    kernels = {k: sums[k] / counts[k] for k in sums}
+    del g, gw
+    return ms_total, wall, eager_ms, kernels
+
+
+# ---------------------------------------------------------------------------------------
+# CPU oracle baseline
+# ---------------------------------------------------------------------------------------
+
+
+def cpu_baseline(w, seconds: float):
+    import oracle
+    from synth import bf16_bits_to_f32
+
+    p = w.projections[0]
+    xf, Wf, Af, Bf = (bf16_bits_to_f32(v) for v in (p.x, p.W, p.A, p.B))
+    threads = int(os.environ.get("OMP_NUM_THREADS") or min(16, os.cpu_count() or 1))
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.lora_linear(xf, Wf, Af, Bf, w.alpha, w.ranks, w.ids, n_threads=threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": w.M * reps / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"the full {w.M}-row batch of {w.name}, {reps} oracle calls in {el:.1f} s "
+                      f"(plain C fp32 row loop, OpenMP over rows)"}
+
+
+# ---------------------------------------------------------------------------------------
+# traffic from committed rocprofv3 counter summaries
+# ---------------------------------------------------------------------------------------
+
+
+def kernel_sources_digest() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "rank_adapter_gemm_sgmv_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(workload: str, kernel: str):
+    """HBM bytes per launch from profiles/counters_<workload>.md, if taken on these sources."""
+    path = os.path.join(ROOT, "profiles", f"counters_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"sources_digest:\s*([0-9a-f]+)", text)
+    if not m or m.group(1) != kernel_sources_digest():
+        return None
+    m = re.search(rf"^traffic\s+{re.escape(kernel)}\s+([0-9.eE+]+)", text, re.M)
+    return float(m.group(1)) if m else None
+
+
+# ---------------------------------------------------------------------------------------
+
+
+def roofline_for(name, ms, work, workload):
+    wk = work[name]
+    if name.startswith("gemm_prefill"):
+        achieved = wk["flops"] / (ms * 1e-3) / 1e12
+        r = {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        achieved = wk["bytes"] / (ms * 1e-3) / 1e9
+        r = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    r["frac"] = r["achieved"] / r["peak"]
+    r["kernel"] = name
+    r["us_per_launch"] = ms * 1e3
+    r["algorithmic_per_launch"] = wk["flops"] if r["bound"] == "mfma" else wk["bytes"]
+    r["traffic"] = committed_traffic(workload, name)
+    return r
+
+
+def summarize(w, runner, ms_total, steps, wall, eager_ms, kernels, prefill):
+    projs = w.projections
+    per_proj = []
+    lora_s = base_s = 0.0
+    lora_bytes = 0
+    total_kernel_ms = 0.0
+    for pi, p in enumerate(projs):
+        work = algorithmic_work(w, p.d_in, p.d_out, prefill)
+        ks = {name: ms for (qi, name), ms in kernels.items() if qi == pi}
+        total_kernel_ms += sum(ks.values())
+        entry = {"projection": p.name, "d_in": p.d_in, "d_out": p.d_out,
+                 "kernels_us": {k: round(v * 1e3, 2) for k, v in ks.items()}}
+        gname = "gemm_prefill_lora" if prefill else "gemm_decode"
+        if gname in ks:
+            g_ms = ks[gname]
+            entry["gemm_tflops"] = work[gname]["flops"] / (g_ms * 1e-3) / 1e12
+            entry["gemm_mfma_frac"] = entry["gemm_tflops"] / BF16_PEAK_TFLOPS
+            entry["gemm_gbs"] = work[gname]["bytes"] / (g_ms * 1e-3) / 1e9
+            entry["gemm_hbm_frac"] = entry["gemm_gbs"] / HBM_PEAK_GBS
+            base_s += (g_ms + ks.get("splitk_reduce", 0.0)) * 1e-3
+        lk = [k for k in ("shrink", "shrink_finalize", "expand") if k in ks]
+        if not prefill and lk:
+            l_ms = sum(ks[k] for k in lk)
+            entry["shrink_expand_us"] = l_ms * 1e3
+            entry["shrink_expand_gbs"] = work["lora_bytes"] / (l_ms * 1e-3) / 1e9
+            entry["shrink_expand_hbm_frac"] = entry["shrink_expand_gbs"] / HBM_PEAK_GBS
+            lora_bytes += work["lora_bytes"]
+        lora_s += sum(ks.get(k, 0.0) for k in ("build_segments", "shrink", "shrink_finalize", "expand")) * 1e-3
+        per_proj.append(entry)
+    ms_step = ms_total / steps
+    return {
+        "tokens_per_s": w.M * steps / (ms_total * 1e-3),
+        "ms_per_step": ms_step,
+        "ms_per_step_eager": eager_ms,
+        "kernel_sum_ms": total_kernel_ms,
+        "lora_overhead_vs_base_gemm": (lora_s / base_s) if base_s > 0 else None,
+        "projections": per_proj,
+    }
+
+
+def run_workload(config, mode_name, steps, warmup, torch, profile_reps=20, need_runner=False):
+    from synth import make_workload
+
+    w = make_workload(config).as_bf16()
+    prefill = mode_name == "prefill"
+    mode = L_.LORA_MODE_PREFILL if prefill else L_.LORA_MODE_DECODE
+    rotate_x = prefill
+    L = layers_needed(w, rotate_x)
+    # the graph holds whole rotations so its last step can be checked against an eager one
+    steps = max(L, -(-steps // L) * L) if steps % L else steps
+    runner = Runner(w, mode, torch, L, rotate_x=rotate_x, prebuilt_segments=len(w.projections) > 1)
+    log(f"bench: {w.name} mode={mode_name} layers={L} steps={steps}")
+    ms_total, wall, eager_ms, kernels = measure(runner, steps, warmup, torch, profile_reps)
+    s = summarize(w, runner, ms_total, steps, wall, eager_ms, kernels, prefill)
+    s.update({"workload": w.name, "mode": mode_name, "layers_rotated": L, "steps": steps})
+    return w, s, kernels, steps, ms_total
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=320)
+    ap.add_argument("--warmup", type=int, default=32)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--headline-only", action="store_true", help="skip the other workloads")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (this build runs "
+              "on a single MI355X; see the sharding notes in the design document).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    global L_
+    from rank_adapter_gemm_sgmv_amd import lora as L_
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+
+    # headline: decode, q_proj geometry
+    w, head, kernels, steps, ms_total = run_workload(2, "decode", args.steps, args.warmup, torch)
+    work = algorithmic_work(w, 4096, 4096, False)
+    kmain = {name: ms for (pi, name), ms in kernels.items() if pi == 0}
+    dom = max(kmain, key=lambda k: kmain[k])
+    roof = roofline_for(dom, kmain[dom], work, w.name)
+
+    workloads = {}
+    if not args.headline_only:
+        for cfg, mode_name, st in ((3, "decode", 128), (4, "prefill", 40), (5, "decode", 64),
+                                   (4, "decode", 20), (2, "prefill", 64)):
+            try:
+                _, s, _, _, _ = run_workload(cfg, mode_name, st, 4, torch, profile_reps=8)
+                workloads[f"{s['workload']}:{mode_name}"] = s
+            except Exception as e:  # report, do not hide the headline
+                workloads[f"config{cfg}:{mode_name}"] = {"error": repr(e)}
+            torch.cuda.empty_cache()
+
+    cpu = cpu_baseline(w, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": head["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "M": w.M, "d_in": 4096, "d_out": 4096,
+                   "n_adapters": w.n_adapters, "r_max": w.r_max, "mode": "decode",
+                   "layers_rotated": head["layers_rotated"], "timed_as": "one HIP graph of all steps"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "headline_detail": head,
+        "workloads": workloads,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -150,6 +150,21 @@ lora_status_t lora_linear(const void *x, const void *W, const void *A, const voi
                           lora_dtype_t y_dtype, lora_mode_t mode, void *ws,
                           size_t ws_bytes, void *stream);
 
+/* Measurement aid, not for serving loops: the same launches as lora_linear, with a HIP
+ * event recorded on `stream` before the first kernel and after each kernel.  It then waits
+ * for the last event and writes, in launch order, each kernel's elapsed time in
+ * milliseconds to kernel_ms[i] and its name (a static string) to kernel_names[i], for at
+ * most max_kernels kernels; *n_kernels receives the number written.  kernel_ms,
+ * kernel_names and n_kernels are HOST pointers.  Creates and destroys its own events. */
+lora_status_t lora_linear_profiled(const void *x, const void *W, const void *A, const void *B,
+                                   const float *scale, const int32_t *ranks, const int32_t *ids,
+                                   int32_t M, int32_t d_in, int32_t d_out, int32_t r_max,
+                                   int32_t n_adapters, const lora_segments_t *segs, void *y,
+                                   lora_dtype_t y_dtype, lora_mode_t mode, void *ws,
+                                   size_t ws_bytes, void *stream, float *kernel_ms,
+                                   const char **kernel_names, int32_t max_kernels,
+                                   int32_t *n_kernels);
+
 /* Human-readable name of a status. */
 const char *lora_status_string(lora_status_t status);
 

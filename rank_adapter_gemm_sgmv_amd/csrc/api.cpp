@@ -152,11 +152,45 @@ lora_status_t lora_expand(const float *t, const void *B, const float *scale, con
                                     (hipStream_t)stream));
 }
 
-lora_status_t lora_linear(const void *x, const void *W, const void *A, const void *B,
-                          const float *scale, const int32_t *ranks, const int32_t *ids, int32_t M,
-                          int32_t d_in, int32_t d_out, int32_t r_max, int32_t n_adapters,
-                          const lora_segments_t *segs, void *y, lora_dtype_t y_dtype,
-                          lora_mode_t mode, void *ws, size_t ws_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Records a HIP event on the stream before the first and after every kernel of a call, for
+// lora_linear_profiled.  A null Marker records nothing.
+struct Marker {
+    static constexpr int kMax = 16;
+    hipStream_t s = nullptr;
+    hipEvent_t ev[kMax + 1] = {};
+    const char *names[kMax] = {};
+    int n = 0;
+    hipError_t err = hipSuccess;
+
+    void start() {
+        if (err == hipSuccess) err = hipEventCreate(&ev[0]);
+        if (err == hipSuccess) err = hipEventRecord(ev[0], s);
+    }
+    void mark(const char *name) {
+        if (err != hipSuccess || n >= kMax) return;
+        err = hipEventCreate(&ev[n + 1]);
+        if (err == hipSuccess) err = hipEventRecord(ev[n + 1], s);
+        if (err == hipSuccess) names[n++] = name;
+    }
+    ~Marker() {
+        for (int i = 0; i <= n; ++i)
+            if (ev[i]) (void)hipEventDestroy(ev[i]);
+    }
+};
+
+void mark(Marker *mk, const char *name) {
+    if (mk) mk->mark(name);
+}
+
+lora_status_t check_linear(const void *x, const void *W, const void *A, const void *B,
+                           const float *scale, const int32_t *ranks, const int32_t *ids, int32_t M,
+                           int32_t d_in, int32_t d_out, int32_t r_max, int32_t n_adapters,
+                           const lora_segments_t *segs, void *y, lora_dtype_t y_dtype,
+                           lora_mode_t mode, void *ws, size_t ws_bytes) {
     lora_status_t st = check_common(M, r_max, n_adapters);
     if (st != LORA_OK) return st;
     if (!dim_ok(d_in) || !dim_ok(d_out)) return LORA_ERR_SHAPE;
@@ -171,9 +205,18 @@ lora_status_t lora_linear(const void *x, const void *W, const void *A, const voi
         (ranks && !aligned(ranks, 4)))
         return LORA_ERR_ALIGN;
     if (ws_bytes < lora_workspace_bytes(M, d_in, d_out, r_max, n_adapters)) return LORA_ERR_WORKSPACE;
+    return LORA_OK;
+}
 
+// The launch sequence of lora_linear (arguments already validated, M > 0).
+//   decode : build_segments, shrink, shrink_finalize, gemm [, splitk_reduce], expand
+//   prefill: build_segments, shrink, shrink_finalize, gemm with the LoRA epilogue
+hipError_t run_linear(const void *x, const void *W, const void *A, const void *B,
+                      const float *scale, const int32_t *ranks, const int32_t *ids, int32_t M,
+                      int32_t d_in, int32_t d_out, int32_t r_max, int32_t n_adapters,
+                      const lora_segments_t *segs, void *y, lora_dtype_t y_dtype, lora_mode_t mode,
+                      void *ws, hipStream_t s, Marker *mk) {
     const bool prefill = mode == LORA_MODE_PREFILL || (mode == LORA_MODE_AUTO && M >= LORA_PREFILL_MIN_ROWS);
-    hipStream_t s = (hipStream_t)stream;
     char *p = static_cast<char *>(ws);
     lora_segments_t own = carve_segments(p, M, n_adapters);
     float *t = reinterpret_cast<float *>(p); p += t_bytes(M, r_max);
@@ -181,31 +224,95 @@ lora_status_t lora_linear(const void *x, const void *W, const void *A, const voi
     float *gpart = reinterpret_cast<float *>(p);
     const size_t gpart_floats = gemm_partial_floats(M, d_in, d_out);
 
-    const lora_segments_t use = segs ? *segs : own;
-    const Seg sg = to_seg(use);
+    const Seg sg = to_seg(segs ? *segs : own);
     const uint16_t *xb = static_cast<const uint16_t *>(x);
-    clear_stale_error();
-    hipError_t e = hipSuccess;
-    if (!segs) e = launch_build_segments(ids, M, n_adapters, sg, s);
-    int kc, ksplit;
-    shrink_plan(d_in, &kc, &ksplit);
-    if (e == hipSuccess)
-        e = launch_shrink(xb, static_cast<const uint16_t *>(A), ranks, M, d_in, r_max, n_adapters, sg,
-                          spart, kc, ksplit, s);
-    if (e == hipSuccess) e = launch_shrink_finalize(spart, M, r_max, ksplit, sg, t, s);
-    if (e != hipSuccess) return hip_status(e);
-
     const uint16_t *Wb = static_cast<const uint16_t *>(W);
     const uint16_t *Bb = static_cast<const uint16_t *>(B);
     const bool yf = y_dtype == LORA_F32;
+    hipError_t e;
+    if (!segs) {
+        if ((e = launch_build_segments(ids, M, n_adapters, sg, s)) != hipSuccess) return e;
+        mark(mk, "build_segments");
+    }
+    int kc, ksplit;
+    shrink_plan(d_in, &kc, &ksplit);
+    if ((e = launch_shrink(xb, static_cast<const uint16_t *>(A), ranks, M, d_in, r_max, n_adapters,
+                           sg, spart, kc, ksplit, s)) != hipSuccess)
+        return e;
+    mark(mk, "shrink");
+    if ((e = launch_shrink_finalize(spart, M, r_max, ksplit, sg, t, s)) != hipSuccess) return e;
+    mark(mk, "shrink_finalize");
+    int gsplit = 1;
     if (prefill) {
         LoraEpilogue ep{t, Bb, scale, ids, r_max, n_adapters};
-        e = launch_gemm(xb, Wb, M, d_in, d_out, y, yf, true, sg, &ep, nullptr, 0, s);
-    } else {
-        e = launch_gemm(xb, Wb, M, d_in, d_out, y, yf, false, sg, nullptr, gpart, gpart_floats, s);
-        if (e == hipSuccess)
-            e = launch_expand(t, Bb, scale, ranks, M, d_out, r_max, n_adapters, sg, y, yf, s);
+        if ((e = launch_gemm(xb, Wb, M, d_in, d_out, y, yf, true, sg, &ep, nullptr, 0, &gsplit, s)) != hipSuccess)
+            return e;
+        mark(mk, "gemm_prefill_lora");
+        return hipSuccess;
     }
+    if ((e = launch_gemm(xb, Wb, M, d_in, d_out, y, yf, false, sg, nullptr, gpart, gpart_floats,
+                         &gsplit, s)) != hipSuccess)
+        return e;
+    mark(mk, "gemm_decode");
+    if (gsplit > 1) {
+        if ((e = launch_splitk_reduce(gpart, M, d_out, gsplit, y, yf, s)) != hipSuccess) return e;
+        mark(mk, "splitk_reduce");
+    }
+    if ((e = launch_expand(t, Bb, scale, ranks, M, d_out, r_max, n_adapters, sg, y, yf, s)) != hipSuccess)
+        return e;
+    mark(mk, "expand");
+    return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+lora_status_t lora_linear(const void *x, const void *W, const void *A, const void *B,
+                          const float *scale, const int32_t *ranks, const int32_t *ids, int32_t M,
+                          int32_t d_in, int32_t d_out, int32_t r_max, int32_t n_adapters,
+                          const lora_segments_t *segs, void *y, lora_dtype_t y_dtype,
+                          lora_mode_t mode, void *ws, size_t ws_bytes, void *stream) {
+    lora_status_t st = check_linear(x, W, A, B, scale, ranks, ids, M, d_in, d_out, r_max, n_adapters,
+                                    segs, y, y_dtype, mode, ws, ws_bytes);
+    if (st != LORA_OK || M == 0) return st;
+    clear_stale_error();
+    return hip_status(run_linear(x, W, A, B, scale, ranks, ids, M, d_in, d_out, r_max, n_adapters,
+                                 segs, y, y_dtype, mode, ws, (hipStream_t)stream, nullptr));
+}
+
+lora_status_t lora_linear_profiled(const void *x, const void *W, const void *A, const void *B,
+                                   const float *scale, const int32_t *ranks, const int32_t *ids,
+                                   int32_t M, int32_t d_in, int32_t d_out, int32_t r_max,
+                                   int32_t n_adapters, const lora_segments_t *segs, void *y,
+                                   lora_dtype_t y_dtype, lora_mode_t mode, void *ws,
+                                   size_t ws_bytes, void *stream, float *kernel_ms,
+                                   const char **kernel_names, int32_t max_kernels,
+                                   int32_t *n_kernels) {
+    if (!kernel_ms || !kernel_names || !n_kernels || max_kernels < 0) return LORA_ERR_NULL;
+    *n_kernels = 0;
+    lora_status_t st = check_linear(x, W, A, B, scale, ranks, ids, M, d_in, d_out, r_max, n_adapters,
+                                    segs, y, y_dtype, mode, ws, ws_bytes);
+    if (st != LORA_OK || M == 0) return st;
+    clear_stale_error();
+    Marker mk;
+    mk.s = (hipStream_t)stream;
+    mk.start();
+    hipError_t e = mk.err;
+    if (e == hipSuccess)
+        e = run_linear(x, W, A, B, scale, ranks, ids, M, d_in, d_out, r_max, n_adapters, segs, y,
+                       y_dtype, mode, ws, mk.s, &mk);
+    if (e == hipSuccess) e = mk.err;
+    if (e == hipSuccess) e = hipEventSynchronize(mk.ev[mk.n]);
+    for (int i = 0; e == hipSuccess && i < mk.n; ++i) {
+        float ms = 0.0f;
+        e = hipEventElapsedTime(&ms, mk.ev[i], mk.ev[i + 1]);
+        if (i < max_kernels) {
+            kernel_ms[i] = ms;
+            kernel_names[i] = mk.names[i];
+        }
+    }
+    if (e == hipSuccess) *n_kernels = mk.n < max_kernels ? mk.n : max_kernels;
     return hip_status(e);
 }
 

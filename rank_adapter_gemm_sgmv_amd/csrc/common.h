@@ -79,10 +79,14 @@ struct LoraEpilogue {
 };
 
 // y = x W (+ LoRA epilogue when lora != nullptr).  `prefill` selects the 256x256 tiling
-// and segment-ordered rows; otherwise a decode tiling with split-K partials in `ws`.
+// and segment-ordered rows; otherwise a decode tiling, which may split K: then the partial
+// sums go to ws_partial, *ksplit_out > 1, and launch_splitk_reduce must follow.
 hipError_t launch_gemm(const uint16_t *x, const uint16_t *W, int M, int K, int N, void *y,
                        bool y_f32, bool prefill, Seg seg, const LoraEpilogue *lora,
-                       float *ws_partial, size_t ws_partial_floats, hipStream_t s);
+                       float *ws_partial, size_t ws_partial_floats, int *ksplit_out,
+                       hipStream_t s);
+hipError_t launch_splitk_reduce(const float *partial, int M, int N, int ksplit, void *y,
+                                bool y_f32, hipStream_t s);
 
 // Workspace floats the decode GEMM needs for split-K partials at these sizes.
 size_t gemm_partial_floats(int M, int K, int N);

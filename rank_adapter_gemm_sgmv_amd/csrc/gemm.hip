@@ -353,7 +353,9 @@ size_t gemm_partial_floats(int M, int K, int N) {
 
 hipError_t launch_gemm(const uint16_t *x, const uint16_t *W, int M, int K, int N, void *y,
                        bool y_f32, bool prefill, Seg seg, const LoraEpilogue *lora,
-                       float *ws_partial, size_t ws_partial_floats, hipStream_t s) {
+                       float *ws_partial, size_t ws_partial_floats, int *ksplit_out,
+                       hipStream_t s) {
+    *ksplit_out = 1;
     if (prefill)
         return launch_cfg<CfgPrefill, true>(x, W, M, K, N, y, y_f32, nullptr, 1, K, seg, lora, s);
 
@@ -364,20 +366,22 @@ hipError_t launch_gemm(const uint16_t *x, const uint16_t *W, int M, int K, int N
             return hipErrorInvalidValue;
         partial = ws_partial;
     }
-    hipError_t e;
+    *ksplit_out = p.ksplit;
     if (p.bm == 64)
-        e = launch_cfg<CfgD64, false>(x, W, M, K, N, y, y_f32, partial, p.ksplit, p.k_per_split, seg, nullptr, s);
-    else if (p.bn == 64)
-        e = launch_cfg<CfgD128x64, false>(x, W, M, K, N, y, y_f32, partial, p.ksplit, p.k_per_split, seg, nullptr, s);
-    else
-        e = launch_cfg<CfgD128, false>(x, W, M, K, N, y, y_f32, partial, p.ksplit, p.k_per_split, seg, nullptr, s);
-    if (e != hipSuccess || p.ksplit == 1) return e;
+        return launch_cfg<CfgD64, false>(x, W, M, K, N, y, y_f32, partial, p.ksplit, p.k_per_split, seg, nullptr, s);
+    if (p.bn == 64)
+        return launch_cfg<CfgD128x64, false>(x, W, M, K, N, y, y_f32, partial, p.ksplit, p.k_per_split, seg, nullptr, s);
+    return launch_cfg<CfgD128, false>(x, W, M, K, N, y, y_f32, partial, p.ksplit, p.k_per_split, seg, nullptr, s);
+}
+
+hipError_t launch_splitk_reduce(const float *partial, int M, int N, int ksplit, void *y, bool y_f32,
+                                hipStream_t s) {
     const long threads = (long)M * N / 4;
     const int grid = (int)((threads + 255) / 256);
     if (y_f32)
-        hipLaunchKernelGGL(splitk_reduce_kernel<true>, dim3(grid), dim3(256), 0, s, partial, M, N, p.ksplit, y);
+        hipLaunchKernelGGL(splitk_reduce_kernel<true>, dim3(grid), dim3(256), 0, s, partial, M, N, ksplit, y);
     else
-        hipLaunchKernelGGL(splitk_reduce_kernel<false>, dim3(grid), dim3(256), 0, s, partial, M, N, p.ksplit, y);
+        hipLaunchKernelGGL(splitk_reduce_kernel<false>, dim3(grid), dim3(256), 0, s, partial, M, N, ksplit, y);
     return hipGetLastError();
 }
 
