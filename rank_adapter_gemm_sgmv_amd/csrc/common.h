@@ -85,6 +85,12 @@ hipError_t launch_gemm(const uint16_t *x, const uint16_t *W, int M, int K, int N
                        bool y_f32, bool prefill, Seg seg, const LoraEpilogue *lora,
                        float *ws_partial, size_t ws_partial_floats, int *ksplit_out,
                        hipStream_t s);
+// Large-batch MFMA GEMM (csrc/gemm_big.hip): with lora != nullptr, rows in segment order and
+// the LoRA delta of each adapter run added before the only store (prefill); otherwise plain
+// y = x W in natural row order.
+hipError_t launch_gemm_big(const uint16_t *x, const uint16_t *W, int M, int K, int N, void *y,
+                           bool y_f32, Seg seg, const LoraEpilogue *lora, hipStream_t s);
+
 hipError_t launch_splitk_reduce(const float *partial, int M, int N, int ksplit, void *y,
                                 bool y_f32, hipStream_t s);
 

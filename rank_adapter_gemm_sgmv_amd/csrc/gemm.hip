@@ -356,8 +356,7 @@ hipError_t launch_gemm(const uint16_t *x, const uint16_t *W, int M, int K, int N
                        float *ws_partial, size_t ws_partial_floats, int *ksplit_out,
                        hipStream_t s) {
     *ksplit_out = 1;
-    if (prefill)
-        return launch_cfg<CfgPrefill, true>(x, W, M, K, N, y, y_f32, nullptr, 1, K, seg, lora, s);
+    if (prefill) return launch_gemm_big(x, W, M, K, N, y, y_f32, seg, lora, s);
 
     const DecodePlan p = decode_plan(M, K, N);
     float *partial = nullptr;

@@ -1,0 +1,374 @@
+// gemm_big.hip -- the shared term y = x W on bf16 MFMA for large batches (prefill and the
+// wide decode batches), with the LoRA delta of each adapter run fused into the epilogue.
+//
+// Source: "Multi-LoRA Serving: Why 100 Adapters Fit on One GPU" (dev.to), "Why can't you
+// just merge LoRA weights into the base model?" (x W is one big GEMM across the whole batch)
+// and "How does one batch run 30 different adapters at once?" (prefill is compute-bound; the
+// delta is small next to x W).
+//
+// gfx950 design
+//  * Tile BM x BN (256 x 256, 256 x 128 or 128 x 128), four waves in a 2 x 2 grid, each wave
+//    owning (BM/2) x (BN/2) of the output as 32 x 32 v_mfma_f32_32x32x16_bf16 accumulators.
+//  * K is consumed 32 at a time through a 4-stage LDS ring filled by direct global->LDS
+//    loads (global_load_lds_dwordx4): no staging registers, three stages in flight while one
+//    is multiplied.  Each stage slot is its own __shared__ array, named statically and
+//    reached through __restrict__ parameters, so the compiler can tell the in-flight loads
+//    from the slot being read and only the explicit s_waitcnt below orders them.
+//  * x tile: [BM rows][32 k] (64-byte rows).  A operand = one ds_read_b128 per lane
+//    (8 consecutive k of one row).  The 16-byte chunk c of row r is stored at c ^ ((r/4) % 4),
+//    so the 32 rows a wave reads at once spread over all LDS banks.
+//  * W tile: [32 k][BN n], exactly as W is laid out in HBM (n contiguous), so its loads are
+//    plain row copies.  The B operand needs 8 consecutive k of one column per lane; gfx950's
+//    transposing LDS read (ds_read_b64_tr_b16) delivers 4 of them per instruction: inside a
+//    group of 16 lanes, lane i names 8 bytes (4 columns) of row i/4, and lane j receives
+//    column j of the 4 x 16 block.  Chunk c of row r is stored at c ^ (4 (r % 4)), so the
+//    four rows of one read hit distinct banks.
+//  * Prefill rows are taken in segment order (positions of perm), so a tile holds a few long
+//    runs of one adapter.  After the K loop, every run adds s_a * t[rows, :] B_a[:, cols]
+//    as extra 32-deep MFMA steps (the K-extension [x | s t] [W ; B_a]) before the only store.
+//  * Tiles are handed to XCDs in compact blocks (workgroup b runs on XCD b % 8), so the
+//    x and W panels a tile group shares are read once into that XCD's L2.
+#include "common.h"
+
+namespace lora {
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
+typedef __attribute__((address_space(3))) char lds_char_t;
+
+constexpr int kBK = 32;     // k per stage
+constexpr int kThreads = 256;
+
+template <int BM_, int BN_>
+struct Big {
+    static constexpr int BM = BM_, BN = BN_;
+    static constexpr int WTM = BM / 2, WTN = BN / 2;  // per-wave tile
+    static constexpr int TM = WTM / 32, TN = WTN / 32;
+    static constexpr int XSLOT = BM * kBK * 2 / 16;  // uint4 per x slot
+    static constexpr int WSLOT = kBK * BN * 2 / 16;  // uint4 per W slot
+    static constexpr int XINS = XSLOT / 64 / 4;      // DMA instructions per wave per stage
+    static constexpr int WINS = WSLOT / 64 / 4;
+    static constexpr int PER = XINS + WINS;
+    static constexpr int WROWS = 1024 / (BN * 2);     // W rows per DMA instruction
+    static constexpr int WCH = BN / 8;                // 16-byte chunks per W row
+    static_assert(BN == 128 || BN == 256, "W swizzle needs at least 16 chunks per row");
+    static_assert(BM == 128 || BM == 256, "x tile");
+    static_assert(XINS >= 1 && WINS >= 1, "per-wave DMA split");
+};
+
+// s_waitcnt with only vmcnt = n (n < 64); expcnt and lgkmcnt left at their maxima.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Workgroup barrier that orders LDS accesses in the compiler but adds no vmcnt wait.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS reads have returned
+    asm volatile("s_barrier" ::: "memory");
+}
+
+// ---- one 32-deep MFMA step from an x slot and a W slot --------------------------------
+template <class C>
+__device__ __forceinline__ void mfma_stage(f32x16_t (&acc)[C::TM][C::TN],
+                                           const uint4 *__restrict__ xs,
+                                           const uint4 *__restrict__ ws, int lane, int wm0, int wn0) {
+    const lds_char_t *wsb = (const lds_char_t *)(ws);
+    const int g = lane >> 4, li = lane & 15;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        bf16x8_t af[C::TM], bfr[C::TN];
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i) {
+            const int row = wm0 + 32 * i + (lane & 31);
+            const int lc = 2 * kk + (lane >> 5);
+            af[i] = *reinterpret_cast<const bf16x8_t *>(&xs[row * 4 + (lc ^ ((row >> 2) & 3))]);
+        }
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j) {
+            const int col = wn0 + 32 * j + 16 * (g & 1) + 4 * (li & 3);
+            const int lc = col >> 3, half = (col >> 2) & 1;
+            const int rsw = (li >> 2) << 2;  // (row % 4) * 4 for every row this lane names
+            bf16x4_t lo, hi;
+            {
+                const int r = 16 * kk + 8 * (g >> 1) + (li >> 2);
+                lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                    (lds_bf16x4_t *)(wsb + r * (C::BN * 2) + ((lc ^ rsw) << 4) + half * 8));
+            }
+            {
+                const int r = 16 * kk + 8 * (g >> 1) + 4 + (li >> 2);
+                hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                    (lds_bf16x4_t *)(wsb + r * (C::BN * 2) + ((lc ^ rsw) << 4) + half * 8));
+            }
+            bfr[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+            for (int j = 0; j < C::TN; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    }
+}
+
+// ---- per-lane DMA sources ----------------------------------------------------------------
+// x: instruction q covers tile rows 16q .. 16q+15; lane i fills row 16q + i/4, stored chunk
+// i % 4, which holds logical chunk (i % 4) ^ ((i / 16) % 4).
+// W: instruction q covers tile rows WROWS q ..; lane i fills row WROWS q + i / WCH, stored
+// chunk i % WCH, holding logical chunk (i % WCH) ^ (4 (row % 4)).
+template <class C>
+struct DmaSrc {
+    const uint16_t *xp[C::XINS];  // row start + logical chunk offset, k = 0
+    const uint16_t *wp[C::WINS];  // (row, logical chunk) at k = 0
+};
+
+template <class C>
+__device__ __forceinline__ void issue_stage(const DmaSrc<C> &src, uint4 *__restrict__ xslot,
+                                            uint4 *__restrict__ wslot,
+                                            int wave, int k0, int N) {
+#pragma unroll
+    for (int j = 0; j < C::XINS; ++j) {
+        const int q = wave * C::XINS + j;
+        __builtin_amdgcn_global_load_lds((const void *)(src.xp[j] + k0), (lds_void_t *)&xslot[q * 64], 16, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < C::WINS; ++j) {
+        const int q = wave * C::WINS + j;
+        __builtin_amdgcn_global_load_lds((const void *)(src.wp[j] + (size_t)k0 * N), (lds_void_t *)&wslot[q * 64], 16, 0, 0);
+    }
+}
+
+// Tile order: XCD-major (workgroup b runs on XCD b % 8), then groups of 4 tile rows, column-
+// major inside a group, so each XCD works on a compact block of tiles.
+__device__ __forceinline__ void tile_of(int b, int n_tm, int n_tn, int &tm, int &tn) {
+    const int T = n_tm * n_tn;
+    int lin = b;
+    if ((T % 8) == 0) lin = (b % 8) * (T / 8) + b / 8;
+    constexpr int G = 4;
+    const int group = lin / (G * n_tn);
+    const int first = group * G;
+    const int gsz = min(n_tm - first, G);
+    const int in = lin % (G * n_tn);
+    tm = first + in % gsz;
+    tn = in / gsz;
+}
+
+// Register-path fill of slot 0 with K step k0 .. k0+31 (zero beyond K), for the steps the
+// DMA ring does not cover.
+template <class C, bool SEGROWS>
+__device__ __forceinline__ void fill_stage(uint4 *xs, uint4 *ws, const uint16_t *__restrict__ x,
+                                          const uint16_t *__restrict__ W, int M, int K, int N,
+                                          int row0, int n0, int k0, const int32_t *perm, int tid) {
+    for (int c = tid; c < C::BM * 4; c += kThreads) {
+        const int row = c >> 2, lc = c & 3;
+        const int rr = row0 + row;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        const int k = k0 + lc * 8;
+        if (rr < M && k < K) {
+            const int m = SEGROWS ? perm[rr] : rr;
+            v = ld16(x + (size_t)m * K + k);
+        }
+        xs[row * 4 + (lc ^ ((row >> 2) & 3))] = v;
+    }
+    for (int c = tid; c < kBK * C::WCH; c += kThreads) {
+        const int r = c / C::WCH, lc = c % C::WCH;
+        const int n = n0 + lc * 8;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (k0 + r < K && n < N) v = ld16(W + (size_t)(k0 + r) * N + n);
+        ws[r * C::WCH + (lc ^ ((r & 3) << 2))] = v;
+    }
+}
+
+template <class C, bool SEGROWS, bool LORA, bool YF32>
+__global__ __launch_bounds__(kThreads) void gemm_big_kernel(const uint16_t *__restrict__ x,
+                                                            const uint16_t *__restrict__ W,
+                                                            int M, int K, int N,
+                                                            void *__restrict__ y, int n_tm,
+                                                            int n_tn, Seg seg, LoraEpilogue ep) {
+    __shared__ __attribute__((aligned(1024))) uint4 X0[C::XSLOT];
+    __shared__ __attribute__((aligned(1024))) uint4 X1[C::XSLOT];
+    __shared__ __attribute__((aligned(1024))) uint4 X2[C::XSLOT];
+    __shared__ __attribute__((aligned(1024))) uint4 X3[C::XSLOT];
+    __shared__ __attribute__((aligned(1024))) uint4 W0[C::WSLOT];
+    __shared__ __attribute__((aligned(1024))) uint4 W1[C::WSLOT];
+    __shared__ __attribute__((aligned(1024))) uint4 W2[C::WSLOT];
+    __shared__ __attribute__((aligned(1024))) uint4 W3[C::WSLOT];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm0 = (wave >> 1) * C::WTM, wn0 = (wave & 1) * C::WTN;
+    int tmi, tni;
+    tile_of(blockIdx.x, n_tm, n_tn, tmi, tni);
+    const int row0 = tmi * C::BM, n0 = tni * C::BN;
+
+    // DMA sources of this lane (rows beyond M and columns beyond N are clamped in bounds;
+    // their results are never stored)
+    DmaSrc<C> src;
+#pragma unroll
+    for (int j = 0; j < C::XINS; ++j) {
+        const int q = wave * C::XINS + j;
+        const int row = 16 * q + (lane >> 2);
+        const int lc = (lane & 3) ^ ((lane >> 4) & 3);
+        const int rr = min(row0 + row, M - 1);
+        const int m = SEGROWS ? seg.perm[rr] : rr;
+        src.xp[j] = x + (size_t)m * K + lc * 8;
+    }
+#pragma unroll
+    for (int j = 0; j < C::WINS; ++j) {
+        const int q = wave * C::WINS + j;
+        const int r = C::WROWS * q + lane / C::WCH;
+        const int lc = (lane % C::WCH) ^ ((r & 3) << 2);
+        const int n = min(n0 + lc * 8, N - 8);
+        src.wp[j] = W + (size_t)r * N + n;
+    }
+
+    f32x16_t acc[C::TM][C::TN];
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+    // K steps 0 .. nmain-1 go through the DMA ring, four per loop trip.  Every trip issues
+    // its loads unconditionally (the three stages after the last real one reload the last
+    // real stage into slots that are never read again), so the outstanding-load count is the
+    // same on every path and the explicit wait below is exact.
+    const int nfull = K / kBK;
+    const int nmain = nfull & ~3;
+    if (nmain > 0) {
+        issue_stage<C>(src, X0, W0, wave, 0, N);
+        issue_stage<C>(src, X1, W1, wave, kBK, N);
+        issue_stage<C>(src, X2, W2, wave, 2 * kBK, N);
+#define LORA_BIG_STEP(SS, XC, WC, XN, WN)                                         \
+        wait_vm<2 * C::PER>();                                                   \
+        lds_barrier();                                                           \
+        issue_stage<C>(src, XN, WN, wave, min((SS) + 3, nmain - 1) * kBK, N);    \
+        mfma_stage<C>(acc, XC, WC, lane, wm0, wn0);
+        for (int s = 0; s < nmain; s += 4) {
+            LORA_BIG_STEP(s, X0, W0, X3, W3)
+            LORA_BIG_STEP(s + 1, X1, W1, X0, W0)
+            LORA_BIG_STEP(s + 2, X2, W2, X1, W1)
+            LORA_BIG_STEP(s + 3, X3, W3, X2, W2)
+        }
+#undef LORA_BIG_STEP
+        wait_vm<0>();
+    }
+    // remaining steps (K not a multiple of 128), the last one possibly partial: through
+    // registers into slot 0, zero beyond K
+    for (int k0 = nmain * kBK; k0 < K; k0 += kBK) {
+        lds_barrier();
+        fill_stage<C, SEGROWS>(X0, W0, x, W, M, K, N, row0, n0, k0, seg.perm, tid);
+        __syncthreads();
+        mfma_stage<C>(acc, X0, W0, lane, wm0, wn0);
+    }
+
+    if constexpr (LORA) {
+        // Runs of one adapter among this tile's rows (positions of perm): for each run, 32
+        // rank columns at a time, stage T = scale_a * t[rows, :] (zero outside the run) in
+        // slot 0's x layout and B_a[:, tile columns] (zero beyond r_max) in its W layout, then
+        // one more MFMA step.
+        const int n_lora = seg.meta[1];
+        const int RM = ep.r_max;
+        int p = row0;
+        const int p_end = min(row0 + C::BM, n_lora);
+        while (p < p_end) {
+            const int a = ep.ids[seg.perm[p]];
+            if (a < 0 || a >= ep.n_adapters) break;  // segments not built for these ids
+            const int q_end = min(seg.offsets[a + 1], p_end);
+            if (q_end <= p) break;
+            const float s = ep.scale[a];
+            for (int rc = 0; rc < RM; rc += kBK) {
+                lds_barrier();
+                for (int c = tid; c < C::BM * 4; c += kThreads) {
+                    const int row = c >> 2, lc = c & 3;
+                    const int pos = row0 + row;
+                    const int j = rc + lc * 8;
+                    uint4 v = make_uint4(0, 0, 0, 0);
+                    if (pos >= p && pos < q_end && j < RM) {
+                        const float *tp = ep.t + (size_t)seg.perm[pos] * RM + j;
+                        const float4 t0 = *reinterpret_cast<const float4 *>(tp);
+                        const float4 t1 = *reinterpret_cast<const float4 *>(tp + 4);
+                        v = make_uint4(pack_bf16x2(s * t0.x, s * t0.y), pack_bf16x2(s * t0.z, s * t0.w),
+                                       pack_bf16x2(s * t1.x, s * t1.y), pack_bf16x2(s * t1.z, s * t1.w));
+                    }
+                    X0[row * 4 + (lc ^ ((row >> 2) & 3))] = v;
+                }
+                for (int c = tid; c < kBK * C::WCH; c += kThreads) {
+                    const int r = c / C::WCH, lc = c % C::WCH;
+                    const int n = n0 + lc * 8;
+                    uint4 v = make_uint4(0, 0, 0, 0);
+                    if (rc + r < RM && n < N) v = ld16(ep.B + ((size_t)a * RM + rc + r) * N + n);
+                    W0[r * C::WCH + (lc ^ ((r & 3) << 2))] = v;
+                }
+                __syncthreads();
+                mfma_stage<C>(acc, X0, W0, lane, wm0, wn0);
+            }
+            p = q_end;
+        }
+    }
+
+    // store: accumulator element v of a 32 x 32 block is row (v/4)*8 + (lane/32)*4 + v%4,
+    // column lane%32
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int rr = row0 + wm0 + 32 * i + (v / 4) * 8 + (lane >> 5) * 4 + (v % 4);
+            if (rr >= M) continue;
+            const int m = SEGROWS ? seg.perm[rr] : rr;
+#pragma unroll
+            for (int j = 0; j < C::TN; ++j) {
+                const int col = n0 + wn0 + 32 * j + (lane & 31);
+                if (col < N) {
+                    const float val = acc[i][j][v];
+                    if constexpr (YF32)
+                        reinterpret_cast<float *>(y)[(size_t)m * N + col] = val;
+                    else
+                        reinterpret_cast<uint16_t *>(y)[(size_t)m * N + col] = (uint16_t)f32_to_bf16_rne(val);
+                }
+            }
+        }
+    }
+}
+
+template <class C, bool SEGROWS, bool LORA>
+hipError_t launch_big_cfg(const uint16_t *x, const uint16_t *W, int M, int K, int N, void *y,
+                          bool y_f32, Seg seg, const LoraEpilogue *lora, hipStream_t s) {
+    const int n_tm = (M + C::BM - 1) / C::BM, n_tn = (N + C::BN - 1) / C::BN;
+    LoraEpilogue ep{};
+    if (lora) ep = *lora;
+    const dim3 grid(n_tm * n_tn);
+    if (y_f32)
+        hipLaunchKernelGGL((gemm_big_kernel<C, SEGROWS, LORA, true>), grid, dim3(kThreads), 0, s, x, W,
+                           M, K, N, y, n_tm, n_tn, seg, ep);
+    else
+        hipLaunchKernelGGL((gemm_big_kernel<C, SEGROWS, LORA, false>), grid, dim3(kThreads), 0, s, x, W,
+                           M, K, N, y, n_tm, n_tn, seg, ep);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+// Large-batch GEMM: prefill (segment-ordered rows, LoRA epilogue) when lora != nullptr,
+// else plain y = x W in natural row order.  Needs N >= 8 (N % 8 == 0) and M >= 1.
+hipError_t launch_gemm_big(const uint16_t *x, const uint16_t *W, int M, int K, int N, void *y,
+                           bool y_f32, Seg seg, const LoraEpilogue *lora, hipStream_t s) {
+    const long t256 = (long)((M + 255) / 256) * ((N + 255) / 256);
+    if (lora) {
+        if (t256 >= 192) return launch_big_cfg<Big<256, 256>, true, true>(x, W, M, K, N, y, y_f32, seg, lora, s);
+        if ((long)((M + 255) / 256) * ((N + 127) / 128) >= 192)
+            return launch_big_cfg<Big<256, 128>, true, true>(x, W, M, K, N, y, y_f32, seg, lora, s);
+        return launch_big_cfg<Big<128, 128>, true, true>(x, W, M, K, N, y, y_f32, seg, lora, s);
+    }
+    if (t256 >= 192) return launch_big_cfg<Big<256, 256>, false, false>(x, W, M, K, N, y, y_f32, seg, nullptr, s);
+    if ((long)((M + 255) / 256) * ((N + 127) / 128) >= 192)
+        return launch_big_cfg<Big<256, 128>, false, false>(x, W, M, K, N, y, y_f32, seg, nullptr, s);
+    return launch_big_cfg<Big<128, 128>, false, false>(x, W, M, K, N, y, y_f32, seg, nullptr, s);
+}
+
+}  // namespace lora
