@@ -372,6 +372,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=32)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--headline-only", action="store_true", help="skip the other workloads")
+    ap.add_argument("--workload", type=int, default=2, choices=(2, 3, 4, 5),
+                    help="workload of the headline line (2 = decode q_proj, the default)")
+    ap.add_argument("--mode", default="decode", choices=("decode", "prefill"))
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (this build runs "
@@ -386,9 +389,11 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
 
-    # headline: decode, q_proj geometry
-    w, head, kernels, steps, ms_total = run_workload(2, "decode", args.steps, args.warmup, torch)
-    work = algorithmic_work(w, 4096, 4096, False)
+    # headline: decode, q_proj geometry (unless another workload is asked for)
+    w, head, kernels, steps, ms_total = run_workload(args.workload, args.mode, args.steps,
+                                                     args.warmup, torch)
+    p0 = w.projections[0]
+    work = algorithmic_work(w, p0.d_in, p0.d_out, args.mode == "prefill")
     kmain = {name: ms for (pi, name), ms in kernels.items() if pi == 0}
     dom = max(kmain, key=lambda k: kmain[k])
     roof = roofline_for(dom, kmain[dom], work, w.name)
@@ -404,7 +409,7 @@ def main():
                 workloads[f"config{cfg}:{mode_name}"] = {"error": repr(e)}
             torch.cuda.empty_cache()
 
-    cpu = cpu_baseline(w, args.cpu_seconds)
+    cpu = cpu_baseline(w, args.cpu_seconds) if args.cpu_seconds > 0 else None
 
     line = {
         "metric": METRIC,
@@ -419,8 +424,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": w.name, "M": w.M, "d_in": 4096, "d_out": 4096,
-                   "n_adapters": w.n_adapters, "r_max": w.r_max, "mode": "decode",
+        "config": {"workload": w.name, "M": w.M, "d_in": p0.d_in, "d_out": p0.d_out,
+                   "n_adapters": w.n_adapters, "r_max": w.r_max, "mode": args.mode,
                    "layers_rotated": head["layers_rotated"], "timed_as": "one HIP graph of all steps"},
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -305,6 +305,10 @@ using CfgD64 = Cfg<64, 64, 2, 2>;
 using CfgD128x64 = Cfg<128, 64, 2, 2>;
 using CfgD128 = Cfg<128, 128, 2, 2>;
 
+// Decode batches with enough 128 x 128 output tiles to cover every CU use the large-tile
+// MFMA kernel (no split-K); smaller ones the split-K tilings below.
+bool use_big(int M, int N) { return (long)((M + 127) / 128) * ((N + 127) / 128) >= 256; }
+
 struct DecodePlan {
     int bm, bn, ksplit, k_per_split;
 };
@@ -347,6 +351,7 @@ hipError_t launch_cfg(const uint16_t *x, const uint16_t *W, int M, int K, int N,
 }  // namespace
 
 size_t gemm_partial_floats(int M, int K, int N) {
+    if (use_big(M, N)) return 0;
     const DecodePlan p = decode_plan(M, K, N);
     return p.ksplit > 1 ? (size_t)p.ksplit * M * N : 0;
 }
@@ -357,6 +362,7 @@ hipError_t launch_gemm(const uint16_t *x, const uint16_t *W, int M, int K, int N
                        hipStream_t s) {
     *ksplit_out = 1;
     if (prefill) return launch_gemm_big(x, W, M, K, N, y, y_f32, seg, lora, s);
+    if (use_big(M, N)) return launch_gemm_big(x, W, M, K, N, y, y_f32, seg, nullptr, s);
 
     const DecodePlan p = decode_plan(M, K, N);
     float *partial = nullptr;

@@ -74,45 +74,77 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_barrier" ::: "memory");
 }
 
-// ---- one 32-deep MFMA step from an x slot and a W slot --------------------------------
+// ---- operand fragments of one 32-deep step ------------------------------------------------
+// a[kk][i]: rows wm0 + 32 i + lane % 32, k = 16 kk + 8 (lane / 32) .. +7 (one ds_read_b128);
+// b[kk][j]: column wn0 + 32 j + lane % 32, the same 8 k (two ds_read_b64_tr_b16).
 template <class C>
-__device__ __forceinline__ void mfma_stage(f32x16_t (&acc)[C::TM][C::TN],
-                                           const uint4 *__restrict__ xs,
-                                           const uint4 *__restrict__ ws, int lane, int wm0, int wn0) {
+struct Frags {
+    bf16x8_t a[2][C::TM];
+    bf16x8_t b[2][C::TN];
+};
+
+template <class C>
+__device__ __forceinline__ void read_frags(Frags<C> &f, const uint4 *__restrict__ xs,
+                                           const uint4 *__restrict__ ws, int lane, int wm0,
+                                           int wn0) {
     const lds_char_t *wsb = (const lds_char_t *)(ws);
     const int g = lane >> 4, li = lane & 15;
+    const int rsw = (li >> 2) << 2;  // (row % 4) * 4 for every W row this lane names
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-        bf16x8_t af[C::TM], bfr[C::TN];
 #pragma unroll
         for (int i = 0; i < C::TM; ++i) {
             const int row = wm0 + 32 * i + (lane & 31);
             const int lc = 2 * kk + (lane >> 5);
-            af[i] = *reinterpret_cast<const bf16x8_t *>(&xs[row * 4 + (lc ^ ((row >> 2) & 3))]);
+            f.a[kk][i] = *reinterpret_cast<const bf16x8_t *>(&xs[row * 4 + (lc ^ ((row >> 2) & 3))]);
         }
 #pragma unroll
         for (int j = 0; j < C::TN; ++j) {
             const int col = wn0 + 32 * j + 16 * (g & 1) + 4 * (li & 3);
             const int lc = col >> 3, half = (col >> 2) & 1;
-            const int rsw = (li >> 2) << 2;  // (row % 4) * 4 for every row this lane names
-            bf16x4_t lo, hi;
-            {
-                const int r = 16 * kk + 8 * (g >> 1) + (li >> 2);
-                lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                    (lds_bf16x4_t *)(wsb + r * (C::BN * 2) + ((lc ^ rsw) << 4) + half * 8));
-            }
-            {
-                const int r = 16 * kk + 8 * (g >> 1) + 4 + (li >> 2);
-                hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                    (lds_bf16x4_t *)(wsb + r * (C::BN * 2) + ((lc ^ rsw) << 4) + half * 8));
-            }
-            bfr[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            const int r = 16 * kk + 8 * (g >> 1) + (li >> 2);
+            const lds_char_t *p = wsb + r * (C::BN * 2) + ((lc ^ rsw) << 4) + half * 8;
+            const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)p);
+            const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)(p + 4 * C::BN * 2));
+            f.b[kk][j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         }
+    }
+}
+
+template <class C>
+__device__ __forceinline__ void mfma_frags(f32x16_t (&acc)[C::TM][C::TN], const Frags<C> &f) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
         for (int i = 0; i < C::TM; ++i)
 #pragma unroll
             for (int j = 0; j < C::TN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[kk][i], f.b[kk][j], acc[i][j], 0, 0, 0);
+}
+
+// One 32-deep step straight from LDS (used outside the pipelined loop).
+template <class C>
+__device__ __forceinline__ void mfma_stage(f32x16_t (&acc)[C::TM][C::TN],
+                                           const uint4 *__restrict__ xs,
+                                           const uint4 *__restrict__ ws, int lane, int wm0, int wn0) {
+    Frags<C> f;
+    read_frags<C>(f, xs, ws, lane, wm0, wn0);
+    mfma_frags<C>(acc, f);
+}
+
+// Interleave the LDS reads of the next step's fragments with this step's MFMAs: groups of
+// DS reads, then MFMAs, in order (one scheduling group sequence).
+template <class C>
+__device__ __forceinline__ void interleave_reads_with_mfma() {
+    constexpr int reads = 2 * (C::TM + 2 * C::TN);
+    constexpr int mfmas = 2 * C::TM * C::TN;
+    constexpr int groups = 8;
+    constexpr int rpg = (reads + groups - 1) / groups;
+    constexpr int mpg = mfmas / groups;
+#pragma unroll
+    for (int gi = 0; gi < groups; ++gi) {
+        __builtin_amdgcn_sched_group_barrier(0x100, rpg, 0);  // DS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, mpg, 0);  // MFMA
     }
 }
 
@@ -235,25 +267,35 @@ __global__ __launch_bounds__(kThreads) void gemm_big_kernel(const uint16_t *__re
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
     // K steps 0 .. nmain-1 go through the DMA ring, four per loop trip.  Every trip issues
-    // its loads unconditionally (the three stages after the last real one reload the last
-    // real stage into slots that are never read again), so the outstanding-load count is the
-    // same on every path and the explicit wait below is exact.
+    // its loads unconditionally (stages past the last real one reload the last real stage
+    // into slots that are never multiplied), so the outstanding-load count is the same on
+    // every path and the explicit waits are exact.
     const int nfull = K / kBK;
     const int nmain = nfull & ~3;
     if (nmain > 0) {
+        // Prologue: stages 0..2 in flight, stage 0's fragments in registers, stage 3 issued.
+        // In loop trip s the fragments of stage s are multiplied while those of stage s+1 are
+        // read from LDS and stage s+4 is loaded into the slot stage s occupied.
+        Frags<C> fa, fb;
         issue_stage<C>(src, X0, W0, wave, 0, N);
-        issue_stage<C>(src, X1, W1, wave, kBK, N);
-        issue_stage<C>(src, X2, W2, wave, 2 * kBK, N);
-#define LORA_BIG_STEP(SS, XC, WC, XN, WN)                                         \
+        issue_stage<C>(src, X1, W1, wave, min(1, nmain - 1) * kBK, N);
+        issue_stage<C>(src, X2, W2, wave, min(2, nmain - 1) * kBK, N);
+        wait_vm<2 * C::PER>();
+        lds_barrier();
+        read_frags<C>(fa, X0, W0, lane, wm0, wn0);
+        issue_stage<C>(src, X3, W3, wave, min(3, nmain - 1) * kBK, N);
+#define LORA_BIG_STEP(SS, FC, FN, XN, WN, XF, WF)                                 \
         wait_vm<2 * C::PER>();                                                   \
         lds_barrier();                                                           \
-        issue_stage<C>(src, XN, WN, wave, min((SS) + 3, nmain - 1) * kBK, N);    \
-        mfma_stage<C>(acc, XC, WC, lane, wm0, wn0);
+        issue_stage<C>(src, XF, WF, wave, min((SS) + 4, nmain - 1) * kBK, N);    \
+        read_frags<C>(FN, XN, WN, lane, wm0, wn0);                               \
+        mfma_frags<C>(acc, FC);                                                  \
+        interleave_reads_with_mfma<C>();
         for (int s = 0; s < nmain; s += 4) {
-            LORA_BIG_STEP(s, X0, W0, X3, W3)
-            LORA_BIG_STEP(s + 1, X1, W1, X0, W0)
-            LORA_BIG_STEP(s + 2, X2, W2, X1, W1)
-            LORA_BIG_STEP(s + 3, X3, W3, X2, W2)
+            LORA_BIG_STEP(s, fa, fb, X1, W1, X0, W0)
+            LORA_BIG_STEP(s + 1, fb, fa, X2, W2, X1, W1)
+            LORA_BIG_STEP(s + 2, fa, fb, X3, W3, X2, W2)
+            LORA_BIG_STEP(s + 3, fb, fa, X0, W0, X3, W3)
         }
 #undef LORA_BIG_STEP
         wait_vm<0>();
@@ -313,23 +355,51 @@ __global__ __launch_bounds__(kThreads) void gemm_big_kernel(const uint16_t *__re
     }
 
     // store: accumulator element v of a 32 x 32 block is row (v/4)*8 + (lane/32)*4 + v%4,
-    // column lane%32
+    // column lane%32.
+    if constexpr (YF32) {
 #pragma unroll
-    for (int i = 0; i < C::TM; ++i) {
+        for (int i = 0; i < C::TM; ++i) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int rr = row0 + wm0 + 32 * i + (v / 4) * 8 + (lane >> 5) * 4 + (v % 4);
-            if (rr >= M) continue;
-            const int m = SEGROWS ? seg.perm[rr] : rr;
+            for (int v = 0; v < 16; ++v) {
+                const int rr = row0 + wm0 + 32 * i + (v / 4) * 8 + (lane >> 5) * 4 + (v % 4);
+                if (rr >= M) continue;
+                const int m = SEGROWS ? seg.perm[rr] : rr;
 #pragma unroll
-            for (int j = 0; j < C::TN; ++j) {
-                const int col = n0 + wn0 + 32 * j + (lane & 31);
-                if (col < N) {
-                    const float val = acc[i][j][v];
-                    if constexpr (YF32)
-                        reinterpret_cast<float *>(y)[(size_t)m * N + col] = val;
-                    else
-                        reinterpret_cast<uint16_t *>(y)[(size_t)m * N + col] = (uint16_t)f32_to_bf16_rne(val);
+                for (int j = 0; j < C::TN; ++j) {
+                    const int col = n0 + wn0 + 32 * j + (lane & 31);
+                    if (col < N) reinterpret_cast<float *>(y)[(size_t)m * N + col] = acc[i][j][v];
+                }
+            }
+        }
+    } else {
+        // bf16 y: each wave stages 32 rows of its tile at a time in its own LDS slot, then
+        // writes whole 16-byte pieces of rows (a wave covers several full row segments per
+        // store instruction).  LDS accesses of one wave complete in order, so the staging
+        // needs no barrier beyond the one that frees the slots.
+        lds_barrier();
+        uint16_t *stg = reinterpret_cast<uint16_t *>(wave == 0 ? X0 : wave == 1 ? X1 : wave == 2 ? X2 : X3);
+        constexpr int SROW = C::WTN + 8;  // staged row length (bf16), 16-byte pad
+        constexpr int CPR = C::WTN / 8;   // 16-byte pieces per staged row
+        static_assert(32 * SROW * 2 <= C::XSLOT * 16, "staging fits one slot");
+        uint16_t *yb = reinterpret_cast<uint16_t *>(y);
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i) {
+#pragma unroll
+            for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int r = (v / 4) * 8 + (lane >> 5) * 4 + (v % 4);
+                    stg[r * SROW + 32 * j + (lane & 31)] = (uint16_t)f32_to_bf16_rne(acc[i][j][v]);
+                }
+#pragma unroll
+            for (int c = lane; c < 32 * CPR; c += 64) {
+                const int r = c / CPR, cc = c % CPR;
+                const int rr = row0 + wm0 + 32 * i + r;
+                const int col = n0 + wn0 + 8 * cc;
+                const uint4 val = *reinterpret_cast<const uint4 *>(&stg[r * SROW + 8 * cc]);
+                if (rr < M && col < N) {
+                    const int m = SEGROWS ? seg.perm[rr] : rr;
+                    st16(yb + (size_t)m * N + col, val);
                 }
             }
         }
