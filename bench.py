@@ -86,6 +86,12 @@ def algorithmic_work(w, d_in: int, d_out: int, prefill: bool, y_bytes: int = 2) 
                                     "flops": base_flops + 2.0 * r_rows * d_out}
     else:
         out["gemm_decode"] = {"bytes": gemm_bytes, "flops": base_flops}
+        # small-batch decode path: shrink (A_i, x rows, t), GEMM with the LoRA K-extension
+        # (W, x, the expand's B_i and t), ordered reduction (writes y once)
+        out["decode_shrink"] = {"bytes": shrink, "flops": 2.0 * r_rows * d_in}
+        out["decode_gemm_lora"] = {"bytes": gemm_bytes + b_bytes + t_bytes,
+                                   "flops": base_flops + 2.0 * r_rows * d_out}
+        out["decode_reduce"] = {"bytes": M * d_out * y_bytes, "flops": 0.0}
     return out
 
 
@@ -319,7 +325,8 @@ def summarize(w, runner, ms_total, steps, wall, eager_ms, kernels, prefill):
         total_kernel_ms += sum(ks.values())
         entry = {"projection": p.name, "d_in": p.d_in, "d_out": p.d_out,
                  "kernels_us": {k: round(v * 1e3, 2) for k, v in ks.items()}}
-        gname = "gemm_prefill_lora" if prefill else "gemm_decode"
+        gname = "gemm_prefill_lora" if prefill else (
+            "decode_gemm_lora" if "decode_gemm_lora" in ks else "gemm_decode")
         if gname in ks:
             g_ms = ks[gname]
             entry["gemm_tflops"] = work[gname]["flops"] / (g_ms * 1e-3) / 1e12
@@ -328,7 +335,7 @@ def summarize(w, runner, ms_total, steps, wall, eager_ms, kernels, prefill):
             entry["gemm_hbm_frac"] = entry["gemm_gbs"] / HBM_PEAK_GBS
             base_s += (g_ms + ks.get("splitk_reduce", 0.0)) * 1e-3
         lk = [k for k in ("shrink", "shrink_finalize", "expand") if k in ks]
-        if not prefill and lk:
+        if not prefill and lk and "expand" in ks:
             l_ms = sum(ks[k] for k in lk)
             entry["shrink_expand_us"] = l_ms * 1e3
             entry["shrink_expand_gbs"] = work["lora_bytes"] / (l_ms * 1e-3) / 1e9

@@ -62,9 +62,17 @@ size_t shrink_partial_bytes(int32_t M, int32_t d_in, int32_t r_max) {
 
 size_t t_bytes(int32_t M, int32_t r_max) { return round_up((size_t)M * r_max * sizeof(float)); }
 
-size_t gemm_bytes(int32_t M, int32_t d_in, int32_t d_out) {
-    return round_up(gemm_partial_floats(M, d_in, d_out) * sizeof(float));
+// chunk sums of the decode shrink (small decode batches only)
+size_t tpart_bytes(int32_t M, int32_t d_in, int32_t d_out, int32_t r_max) {
+    if (!decode_gemm_supported(M, d_in, d_out)) return 0;
+    return round_up((size_t)decode_shrink_chunks(d_in, r_max) * M * r_max * sizeof(float));
 }
+
+size_t gemm_bytes(int32_t M, int32_t d_in, int32_t d_out) {
+    const size_t a = gemm_partial_floats(M, d_in, d_out), b = decode_gemm_partial_floats(M, d_in, d_out);
+    return round_up((a > b ? a : b) * sizeof(float));
+}
+
 
 thread_local hipError_t g_last_hip_error = hipSuccess;
 
@@ -92,7 +100,7 @@ size_t lora_workspace_bytes(int32_t M, int32_t d_in, int32_t d_out, int32_t r_ma
     if (check_common(M, r_max, n_adapters) != LORA_OK || !dim_ok(d_in) || !dim_ok(d_out)) return 0;
     if (M == 0) return 0;
     return segments_bytes(M, n_adapters) + t_bytes(M, r_max) + shrink_partial_bytes(M, d_in, r_max) +
-           gemm_bytes(M, d_in, d_out);
+           gemm_bytes(M, d_in, d_out) + tpart_bytes(M, d_in, d_out, r_max);
 }
 
 lora_status_t lora_build_segments(const int32_t *ids, int32_t M, int32_t n_adapters,
@@ -209,7 +217,10 @@ lora_status_t check_linear(const void *x, const void *W, const void *A, const vo
 }
 
 // The launch sequence of lora_linear (arguments already validated, M > 0).
-//   decode : build_segments, shrink, shrink_finalize, gemm [, splitk_reduce], expand
+//   decode, M <= 128 and d_in % 32 == 0: decode_shrink, decode GEMM with the LoRA
+//            K-extension split, its ordered reduction (no segment-building launch: each
+//            kernel groups the <= 128 rows by adapter in LDS; segs is not needed)
+//   decode otherwise: build_segments, shrink, shrink_finalize, gemm [, splitk_reduce], expand
 //   prefill: build_segments, shrink, shrink_finalize, gemm with the LoRA epilogue
 hipError_t run_linear(const void *x, const void *W, const void *A, const void *B,
                       const float *scale, const int32_t *ranks, const int32_t *ids, int32_t M,
@@ -221,7 +232,8 @@ hipError_t run_linear(const void *x, const void *W, const void *A, const void *B
     lora_segments_t own = carve_segments(p, M, n_adapters);
     float *t = reinterpret_cast<float *>(p); p += t_bytes(M, r_max);
     float *spart = reinterpret_cast<float *>(p); p += shrink_partial_bytes(M, d_in, r_max);
-    float *gpart = reinterpret_cast<float *>(p);
+    float *gpart = reinterpret_cast<float *>(p); p += gemm_bytes(M, d_in, d_out);
+    float *tpart = reinterpret_cast<float *>(p);
     const size_t gpart_floats = gemm_partial_floats(M, d_in, d_out);
 
     const Seg sg = to_seg(segs ? *segs : own);
@@ -230,6 +242,19 @@ hipError_t run_linear(const void *x, const void *W, const void *A, const void *B
     const uint16_t *Bb = static_cast<const uint16_t *>(B);
     const bool yf = y_dtype == LORA_F32;
     hipError_t e;
+    if (!prefill && decode_gemm_supported(M, d_in, d_out)) {
+        // small decode batch: three launches, rows grouped by adapter inside each kernel
+        if ((e = launch_decode_shrink(xb, static_cast<const uint16_t *>(A), ids, ranks, M, d_in, r_max,
+                                      n_adapters, tpart, s)) != hipSuccess)
+            return e;
+        mark(mk, "decode_shrink");
+        const DecodeLora lo{tpart, decode_shrink_chunks(d_in, r_max), Bb, scale, ids, r_max, n_adapters};
+        if ((e = launch_decode_gemm(xb, Wb, M, d_in, d_out, y, yf, lo, gpart, s)) != hipSuccess) return e;
+        mark(mk, "decode_gemm_lora");
+        if ((e = launch_decode_reduce(gpart, M, d_in, d_out, y, yf, s)) != hipSuccess) return e;
+        mark(mk, "decode_reduce");
+        return hipSuccess;
+    }
     if (!segs) {
         if ((e = launch_build_segments(ids, M, n_adapters, sg, s)) != hipSuccess) return e;
         mark(mk, "build_segments");
@@ -240,7 +265,8 @@ hipError_t run_linear(const void *x, const void *W, const void *A, const void *B
                            sg, spart, kc, ksplit, s)) != hipSuccess)
         return e;
     mark(mk, "shrink");
-    if ((e = launch_shrink_finalize(spart, M, r_max, ksplit, sg, t, s)) != hipSuccess) return e;
+    if ((e = launch_shrink_finalize(spart, M, r_max, ksplit, sg, t, s)) != hipSuccess)
+        return e;
     mark(mk, "shrink_finalize");
     int gsplit = 1;
     if (prefill) {

@@ -94,6 +94,36 @@ hipError_t launch_gemm_big(const uint16_t *x, const uint16_t *W, int M, int K, i
 hipError_t launch_splitk_reduce(const float *partial, int M, int N, int ksplit, void *y,
                                 bool y_f32, hipStream_t s);
 
+// LoRA operands of the decode GEMM (csrc/decode_gemm.hip).
+struct DecodeLora {
+    const float *tpart;    // [n_chunks][M][r_max]: the decode shrink's chunk sums of t
+    int n_chunks;
+    const uint16_t *B;     // [n][r_max][d_out]
+    const float *scale;    // [n]
+    const int32_t *ids;    // [M]
+    int r_max;
+    int n_adapters;
+};
+
+// Decode batches up to this many rows use the fused decode GEMM when K % 32 == 0.
+constexpr int kDecodeMaxRows = 128;
+bool decode_gemm_supported(int M, int K, int N);
+size_t decode_gemm_partial_floats(int M, int K, int N);
+// y = x W + delta for decode batches: split-K partial tiles plus one split for the LoRA
+// K-extension, then an ordered reduction kernel that rounds once into y.  Needs the decode
+// shrink's chunk sums of t.
+hipError_t launch_decode_gemm(const uint16_t *x, const uint16_t *W, int M, int K, int N, void *y,
+                              bool y_f32, const DecodeLora &lo, float *partial, hipStream_t s);
+
+// Decode shrink (csrc/decode_shrink.hip), M <= kDecodeMaxRows: chunk sums of t = x A_i,
+// tpart[c][m][0:r_max] for rows with an adapter; rows grouped by adapter in LDS.
+int decode_shrink_chunks(int K, int r_max);
+hipError_t launch_decode_shrink(const uint16_t *x, const uint16_t *A, const int32_t *ids,
+                                const int32_t *ranks, int M, int K, int r_max, int n_adapters,
+                                float *tpart, hipStream_t s);
+hipError_t launch_decode_reduce(const float *partial, int M, int K, int N, void *y, bool y_f32,
+                                hipStream_t s);
+
 // Workspace floats the decode GEMM needs for split-K partials at these sizes.
 size_t gemm_partial_floats(int M, int K, int N);
 
