@@ -150,12 +150,13 @@ lora_status_t lora_linear(const void *x, const void *W, const void *A, const voi
                           lora_dtype_t y_dtype, lora_mode_t mode, void *ws,
                           size_t ws_bytes, void *stream);
 
-/* Measurement aid, not for serving loops: the same launches as lora_linear, with a HIP
- * event recorded on `stream` before the first kernel and after each kernel.  It then waits
- * for the last event and writes, in launch order, each kernel's elapsed time in
- * milliseconds to kernel_ms[i] and its name (a static string) to kernel_names[i], for at
- * most max_kernels kernels; *n_kernels receives the number written.  kernel_ms,
- * kernel_names and n_kernels are HOST pointers.  Creates and destroys its own events. */
+/* Measurement aid, not for serving loops: the same launches as lora_linear, each launched
+ * with a start and a stop HIP event that the GPU stamps from that kernel's own dispatch (no
+ * extra packet between kernels), so the times are kernel durations.  It then waits for the
+ * last kernel and writes, in launch order, each kernel's duration in milliseconds to
+ * kernel_ms[i] and its name (a static string) to kernel_names[i], for at most max_kernels
+ * kernels; *n_kernels receives the number written.  kernel_ms, kernel_names and n_kernels
+ * are HOST pointers.  Creates and destroys its own events; not for use during graph capture. */
 lora_status_t lora_linear_profiled(const void *x, const void *W, const void *A, const void *B,
                                    const float *scale, const int32_t *ranks, const int32_t *ids,
                                    int32_t M, int32_t d_in, int32_t d_out, int32_t r_max,

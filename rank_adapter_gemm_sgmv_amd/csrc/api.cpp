@@ -8,6 +8,8 @@
 
 using namespace lora;
 
+thread_local KernelTimer *lora::g_timer = nullptr;
+
 namespace {
 
 constexpr size_t kAlign = 256;
@@ -164,29 +166,14 @@ lora_status_t lora_expand(const float *t, const void *B, const float *scale, con
 
 namespace {
 
-// Records a HIP event on the stream before the first and after every kernel of a call, for
-// lora_linear_profiled.  A null Marker records nothing.
+// Names of the kernels a call launches, in launch order (lora_linear_profiled); their
+// durations come from the KernelTimer events of each launch.  A null Marker records nothing.
 struct Marker {
-    static constexpr int kMax = 16;
-    hipStream_t s = nullptr;
-    hipEvent_t ev[kMax + 1] = {};
+    static constexpr int kMax = KernelTimer::kMax;
     const char *names[kMax] = {};
     int n = 0;
-    hipError_t err = hipSuccess;
-
-    void start() {
-        if (err == hipSuccess) err = hipEventCreate(&ev[0]);
-        if (err == hipSuccess) err = hipEventRecord(ev[0], s);
-    }
     void mark(const char *name) {
-        if (err != hipSuccess || n >= kMax) return;
-        err = hipEventCreate(&ev[n + 1]);
-        if (err == hipSuccess) err = hipEventRecord(ev[n + 1], s);
-        if (err == hipSuccess) names[n++] = name;
-    }
-    ~Marker() {
-        for (int i = 0; i <= n; ++i)
-            if (ev[i]) (void)hipEventDestroy(ev[i]);
+        if (n < kMax) names[n++] = name;
     }
 };
 
@@ -321,24 +308,35 @@ lora_status_t lora_linear_profiled(const void *x, const void *W, const void *A, 
                                     segs, y, y_dtype, mode, ws, ws_bytes);
     if (st != LORA_OK || M == 0) return st;
     clear_stale_error();
+    KernelTimer timer;
+    hipError_t e = hipSuccess;
+    int made = 0;
+    for (; made < KernelTimer::kMax && e == hipSuccess; ++made) {
+        e = hipEventCreate(&timer.start[made]);
+        if (e == hipSuccess) e = hipEventCreate(&timer.stop[made]);
+    }
     Marker mk;
-    mk.s = (hipStream_t)stream;
-    mk.start();
-    hipError_t e = mk.err;
-    if (e == hipSuccess)
+    if (e == hipSuccess) {
+        g_timer = &timer;
         e = run_linear(x, W, A, B, scale, ranks, ids, M, d_in, d_out, r_max, n_adapters, segs, y,
-                       y_dtype, mode, ws, mk.s, &mk);
-    if (e == hipSuccess) e = mk.err;
-    if (e == hipSuccess) e = hipEventSynchronize(mk.ev[mk.n]);
-    for (int i = 0; e == hipSuccess && i < mk.n; ++i) {
+                       y_dtype, mode, ws, (hipStream_t)stream, &mk);
+        g_timer = nullptr;
+    }
+    if (e == hipSuccess && timer.n > 0) e = hipEventSynchronize(timer.stop[timer.n - 1]);
+    const int n = timer.n < mk.n ? timer.n : mk.n;
+    for (int i = 0; e == hipSuccess && i < n; ++i) {
         float ms = 0.0f;
-        e = hipEventElapsedTime(&ms, mk.ev[i], mk.ev[i + 1]);
+        e = hipEventElapsedTime(&ms, timer.start[i], timer.stop[i]);
         if (i < max_kernels) {
             kernel_ms[i] = ms;
             kernel_names[i] = mk.names[i];
         }
     }
-    if (e == hipSuccess) *n_kernels = mk.n < max_kernels ? mk.n : max_kernels;
+    if (e == hipSuccess) *n_kernels = n < max_kernels ? n : max_kernels;
+    for (int i = 0; i < KernelTimer::kMax; ++i) {
+        if (timer.start[i]) (void)hipEventDestroy(timer.start[i]);
+        if (timer.stop[i]) (void)hipEventDestroy(timer.stop[i]);
+    }
     return hip_status(e);
 }
 

@@ -2,6 +2,7 @@
 // liblora_mi355x.so.  Internal: the public interface is include/lora.h.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -51,7 +52,31 @@ __device__ __forceinline__ void unpack8(const uint4 v, float f[8]) {
 __device__ __forceinline__ uint4 ld16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
 __device__ __forceinline__ void st16(void *p, uint4 v) { *reinterpret_cast<uint4 *>(p) = v; }
 
-// ---- launchers (one per kernel family) -------------------------------------------------
+// ---- kernel launches -------------------------------------------------------------------
+// Every kernel of the library is launched through launch().  Normally it is a plain launch;
+// while a KernelTimer is installed for the calling host thread (lora_linear_profiled), the
+// launch carries a start and a stop event that the GPU stamps from the kernel's own dispatch
+// packet, so the elapsed time is the kernel's duration with no extra packet in the stream.
+struct KernelTimer {
+    static constexpr int kMax = 16;
+    hipEvent_t start[kMax] = {};
+    hipEvent_t stop[kMax] = {};
+    int n = 0;
+};
+extern thread_local KernelTimer *g_timer;
+
+template <typename... Args, typename F>
+inline void launch(F kernel, dim3 grid, dim3 block, uint32_t shmem, hipStream_t s, Args... args) {
+    KernelTimer *t = g_timer;
+    if (t != nullptr && t->n < KernelTimer::kMax) {
+        hipExtLaunchKernelGGL(kernel, grid, block, shmem, s, t->start[t->n], t->stop[t->n], 0, args...);
+        ++t->n;
+    } else {
+        hipLaunchKernelGGL(kernel, grid, block, shmem, s, args...);
+    }
+}
+
+// ---- launchers (one kernel each) -------------------------------------------------------
 
 hipError_t launch_build_segments(const int32_t *ids, int M, int n_adapters, Seg seg,
                                  hipStream_t s);

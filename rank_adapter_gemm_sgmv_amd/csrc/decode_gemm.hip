@@ -404,10 +404,10 @@ hipError_t launch_decode_gemm(const uint16_t *x, const uint16_t *W, int M, int K
     const int n_tiles = p.n_tm * p.n_tn;
     const dim3 grid(n_tiles * (p.ks_base + 1));
     if (p.bm == 32)
-        hipLaunchKernelGGL((decode_gemm_kernel<Dec<32>>), grid, dim3(kThreads), 0, s, x, W, M, K, N,
+        launch((decode_gemm_kernel<Dec<32>>), grid, dim3(kThreads), 0, s, x, W, M, K, N,
                            p.n_tm, p.n_tn, p.ks_base, p.k_per_split, partial, lo);
     else
-        hipLaunchKernelGGL((decode_gemm_kernel<Dec<64>>), grid, dim3(kThreads), 0, s, x, W, M, K, N,
+        launch((decode_gemm_kernel<Dec<64>>), grid, dim3(kThreads), 0, s, x, W, M, K, N,
                            p.n_tm, p.n_tn, p.ks_base, p.k_per_split, partial, lo);
     return hipGetLastError();
 }
@@ -419,7 +419,7 @@ hipError_t launch_decode_reduce(const float *partial, int M, int K, int N, void 
     const long threads = (long)M * ((N + 3) / 4);
     const dim3 rgrid((unsigned)((threads + 255) / 256));
 #define RED_LAUNCH(BM, YF)                                                                     \
-    hipLaunchKernelGGL((reduce_partials_kernel<BM, YF>), rgrid, dim3(256), 0, s, partial, M, N, \
+    launch((reduce_partials_kernel<BM, YF>), rgrid, dim3(256), 0, s, partial, M, N, \
                        p.n_tm, p.n_tn, p.ks_base + 1, y)
     if (p.bm == 32) {
         if (y_f32) RED_LAUNCH(32, true); else RED_LAUNCH(32, false);

@@ -147,16 +147,16 @@ hipError_t launch_decode_shrink(const uint16_t *x, const uint16_t *A, const int3
     const dim3 grid(n_chunks * slots);
     switch (r_max) {
         case 8:
-            hipLaunchKernelGGL(decode_shrink_kernel<8>, grid, dim3(kThreads), 0, s, x, A, ids, ranks, M, K, n_adapters, n_chunks, tpart);
+            launch(decode_shrink_kernel<8>, grid, dim3(kThreads), 0, s, x, A, ids, ranks, M, K, n_adapters, n_chunks, tpart);
             break;
         case 16:
-            hipLaunchKernelGGL(decode_shrink_kernel<16>, grid, dim3(kThreads), 0, s, x, A, ids, ranks, M, K, n_adapters, n_chunks, tpart);
+            launch(decode_shrink_kernel<16>, grid, dim3(kThreads), 0, s, x, A, ids, ranks, M, K, n_adapters, n_chunks, tpart);
             break;
         case 32:
-            hipLaunchKernelGGL(decode_shrink_kernel<32>, grid, dim3(kThreads), 0, s, x, A, ids, ranks, M, K, n_adapters, n_chunks, tpart);
+            launch(decode_shrink_kernel<32>, grid, dim3(kThreads), 0, s, x, A, ids, ranks, M, K, n_adapters, n_chunks, tpart);
             break;
         case 64:
-            hipLaunchKernelGGL(decode_shrink_kernel<64>, grid, dim3(kThreads), 0, s, x, A, ids, ranks, M, K, n_adapters, n_chunks, tpart);
+            launch(decode_shrink_kernel<64>, grid, dim3(kThreads), 0, s, x, A, ids, ranks, M, K, n_adapters, n_chunks, tpart);
             break;
         default:
             return hipErrorInvalidValue;

@@ -119,9 +119,9 @@ template <int RM>
 hipError_t launch_rm(const float *t, const uint16_t *B, const float *scale, const int32_t *ranks,
                      int d_out, int n_cc, int grid, Seg seg, void *y, bool y_f32, hipStream_t s) {
     if (y_f32)
-        hipLaunchKernelGGL((expand_kernel<RM, true>), dim3(grid), dim3(64), 0, s, t, B, scale, ranks, d_out, n_cc, seg, y);
+        launch((expand_kernel<RM, true>), dim3(grid), dim3(64), 0, s, t, B, scale, ranks, d_out, n_cc, seg, y);
     else
-        hipLaunchKernelGGL((expand_kernel<RM, false>), dim3(grid), dim3(64), 0, s, t, B, scale, ranks, d_out, n_cc, seg, y);
+        launch((expand_kernel<RM, false>), dim3(grid), dim3(64), 0, s, t, B, scale, ranks, d_out, n_cc, seg, y);
     return hipGetLastError();
 }
 

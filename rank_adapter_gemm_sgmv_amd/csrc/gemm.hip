@@ -340,10 +340,10 @@ hipError_t launch_cfg(const uint16_t *x, const uint16_t *W, int M, int K, int N,
     if (lora) ep = *lora;
     dim3 grid(n_tm * n_tn, ksplit);
     if (y_f32)
-        hipLaunchKernelGGL((gemm_kernel<C, PREFILL, true>), grid, dim3(C::NT), 0, s, x, W, M, K, N, y,
+        launch((gemm_kernel<C, PREFILL, true>), grid, dim3(C::NT), 0, s, x, W, M, K, N, y,
                            partial, k_per_split, n_tm, n_tn, seg, ep);
     else
-        hipLaunchKernelGGL((gemm_kernel<C, PREFILL, false>), grid, dim3(C::NT), 0, s, x, W, M, K, N, y,
+        launch((gemm_kernel<C, PREFILL, false>), grid, dim3(C::NT), 0, s, x, W, M, K, N, y,
                            partial, k_per_split, n_tm, n_tn, seg, ep);
     return hipGetLastError();
 }
@@ -384,9 +384,9 @@ hipError_t launch_splitk_reduce(const float *partial, int M, int N, int ksplit, 
     const long threads = (long)M * N / 4;
     const int grid = (int)((threads + 255) / 256);
     if (y_f32)
-        hipLaunchKernelGGL(splitk_reduce_kernel<true>, dim3(grid), dim3(256), 0, s, partial, M, N, ksplit, y);
+        launch(splitk_reduce_kernel<true>, dim3(grid), dim3(256), 0, s, partial, M, N, ksplit, y);
     else
-        hipLaunchKernelGGL(splitk_reduce_kernel<false>, dim3(grid), dim3(256), 0, s, partial, M, N, ksplit, y);
+        launch(splitk_reduce_kernel<false>, dim3(grid), dim3(256), 0, s, partial, M, N, ksplit, y);
     return hipGetLastError();
 }
 

@@ -414,10 +414,10 @@ hipError_t launch_big_cfg(const uint16_t *x, const uint16_t *W, int M, int K, in
     if (lora) ep = *lora;
     const dim3 grid(n_tm * n_tn);
     if (y_f32)
-        hipLaunchKernelGGL((gemm_big_kernel<C, SEGROWS, LORA, true>), grid, dim3(kThreads), 0, s, x, W,
+        launch((gemm_big_kernel<C, SEGROWS, LORA, true>), grid, dim3(kThreads), 0, s, x, W,
                            M, K, N, y, n_tm, n_tn, seg, ep);
     else
-        hipLaunchKernelGGL((gemm_big_kernel<C, SEGROWS, LORA, false>), grid, dim3(kThreads), 0, s, x, W,
+        launch((gemm_big_kernel<C, SEGROWS, LORA, false>), grid, dim3(kThreads), 0, s, x, W,
                            M, K, N, y, n_tm, n_tn, seg, ep);
     return hipGetLastError();
 }

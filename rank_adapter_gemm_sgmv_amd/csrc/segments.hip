@@ -161,7 +161,7 @@ __global__ __launch_bounds__(kThreads) void build_segments_kernel(const int32_t 
 
 hipError_t launch_build_segments(const int32_t *ids, int M, int n_adapters, Seg seg,
                                  hipStream_t s) {
-    hipLaunchKernelGGL(build_segments_kernel, dim3(1), dim3(kThreads), 0, s, ids, M, n_adapters,
+    launch(build_segments_kernel, dim3(1), dim3(kThreads), 0, s, ids, M, n_adapters,
                        seg);
     return hipGetLastError();
 }

@@ -149,16 +149,16 @@ hipError_t launch_shrink(const uint16_t *x, const uint16_t *A, const int32_t *ra
     const int grid = (int)(items < kMaxGrid ? items : kMaxGrid);
     switch (r_max) {
         case 8:
-            hipLaunchKernelGGL(shrink_kernel<8>, dim3(grid), dim3(kThreads), 0, s, x, A, ranks, M, d_in, seg, partial, ksplit);
+            launch(shrink_kernel<8>, dim3(grid), dim3(kThreads), 0, s, x, A, ranks, M, d_in, seg, partial, ksplit);
             break;
         case 16:
-            hipLaunchKernelGGL(shrink_kernel<16>, dim3(grid), dim3(kThreads), 0, s, x, A, ranks, M, d_in, seg, partial, ksplit);
+            launch(shrink_kernel<16>, dim3(grid), dim3(kThreads), 0, s, x, A, ranks, M, d_in, seg, partial, ksplit);
             break;
         case 32:
-            hipLaunchKernelGGL(shrink_kernel<32>, dim3(grid), dim3(kThreads), 0, s, x, A, ranks, M, d_in, seg, partial, ksplit);
+            launch(shrink_kernel<32>, dim3(grid), dim3(kThreads), 0, s, x, A, ranks, M, d_in, seg, partial, ksplit);
             break;
         case 64:
-            hipLaunchKernelGGL(shrink_kernel<64>, dim3(grid), dim3(kThreads), 0, s, x, A, ranks, M, d_in, seg, partial, ksplit);
+            launch(shrink_kernel<64>, dim3(grid), dim3(kThreads), 0, s, x, A, ranks, M, d_in, seg, partial, ksplit);
             break;
         default:
             return hipErrorInvalidValue;
@@ -170,7 +170,7 @@ hipError_t launch_shrink_finalize(const float *partial, int M, int r_max, int ks
                                   float *t, hipStream_t s) {
     const long threads = (long)M * (r_max / 4);
     const int grid = (int)((threads + 255) / 256);
-    hipLaunchKernelGGL(shrink_finalize_kernel, dim3(grid), dim3(256), 0, s, partial, M, r_max,
+    launch(shrink_finalize_kernel, dim3(grid), dim3(256), 0, s, partial, M, r_max,
                        ksplit, seg, t);
     return hipGetLastError();
 }
