@@ -9,8 +9,8 @@
 //
 // Workgroup (k-chunk c, adapter slot s): the workgroup groups the batch's rows by adapter in
 // LDS (batch_adapters.h), takes the s-th distinct adapter a, holds A_a[chunk, 0:r_max] in
-// registers (each lane one k-slice x 8 rank columns, 16-byte loads, only the column groups
-// below the adapter's rank) and multiplies every row of adapter a with it: 8 fp32 sums per
+// registers (each lane one k-slice x 8 rank columns, 16-byte loads; all r_max columns, the
+// pool's padding being zero) and multiplies every row of adapter a with it: 8 fp32 sums per
 // lane, then an xor butterfly across the k-slices.  So each touched A_a is read from HBM
 // exactly once per batch and untouched adapters cost nothing.  The chunk sums go to
 // tpart[c][m][0:r_max] (rows without an adapter are not written); the consumer adds the
@@ -42,22 +42,19 @@ __global__ __launch_bounds__(kThreads) void decode_shrink_kernel(
     batch_adapters(ba, ids, M, n_adapters);
     if (s >= ba.T) return;  // uniform across the workgroup
     const int a = ba.list[s];
-    const int r = ranks ? min(max(ranks[a], 0), RM) : RM;
+    (void)ranks;  // all r_max columns are read: the pool's padded columns are zero
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int ks = lane % C::KSUB, g = lane / C::KSUB;
     const int k0 = c * C::KC + ks * C::SL;
-    const bool colok = g * 8 < r;
 
-    // A_a[k0 .. k0+SL][8g .. 8g+7] -> registers (zero beyond K or the rank)
-    float av[C::SL][8];
+    // A_a[k0 .. k0+SL][8g .. 8g+7] -> registers.  The loads are unconditional (k beyond K
+    // reads the last row; those terms are dropped below), so they issue back to back.
+    uint4 araw[C::SL];
     const uint16_t *Ap = A + ((size_t)a * K + k0) * RM + g * 8;
+    const uint16_t *Alast = A + ((size_t)a * K + (K - 1)) * RM + g * 8;
 #pragma unroll
-    for (int kk = 0; kk < C::SL; ++kk) {
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (colok && k0 + kk < K) v = ld16(Ap + (size_t)kk * RM);
-        unpack8(v, av[kk]);
-    }
+    for (int kk = 0; kk < C::SL; ++kk) araw[kk] = ld16(k0 + kk < K ? Ap + (size_t)kk * RM : Alast);
 
     // rows of adapter a with row parity == wave, from a ballot mask; the next row's x is
     // loaded while the current one is multiplied
@@ -77,20 +74,16 @@ __global__ __launch_bounds__(kThreads) void decode_shrink_kernel(
         return -1;
     };
     constexpr int XV = C::SL >= 8 ? C::SL / 8 : 1;  // 16-byte x loads per row and lane
+    // x[m][k0 ..]: unconditional loads from in-bounds addresses (row 0 for no row, the last
+    // k for k beyond K); the terms beyond K are dropped in the sums
     auto load_x = [&](int m, uint4 (&xv)[XV]) {
-#pragma unroll
-        for (int v = 0; v < XV; ++v) xv[v] = make_uint4(0, 0, 0, 0);
-        if (m < 0) return;
-        const uint16_t *xp = x + (size_t)m * K + k0;
+        const uint16_t *xr = x + (size_t)(m < 0 ? 0 : m) * K;
         if constexpr (C::SL >= 8) {
 #pragma unroll
-            for (int v = 0; v < XV; ++v)
-                if (k0 + 8 * v < K) xv[v] = ld16(xp + 8 * v);
+            for (int v = 0; v < XV; ++v) xv[v] = ld16(xr + min(k0 + 8 * v, K - 8));
         } else {  // 4 k per slice: one 8-byte load
-            if (k0 < K) {
-                const uint2 h = *reinterpret_cast<const uint2 *>(xp);
-                xv[0] = make_uint4(h.x, h.y, 0, 0);
-            }
+            const uint2 h = *reinterpret_cast<const uint2 *>(xr + min(k0, K - 4));
+            xv[0] = make_uint4(h.x, h.y, 0, 0);
         }
     };
     int m = next_row();
@@ -109,9 +102,11 @@ __global__ __launch_bounds__(kThreads) void decode_shrink_kernel(
             unpack8(xc[v], xf);
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
-                if (8 * v + u < C::SL) {
+                if (8 * v + u < C::SL && k0 + 8 * v + u < K) {
+                    float av[8];
+                    unpack8(araw[8 * v + u], av);
 #pragma unroll
-                    for (int j = 0; j < 8; ++j) acc[j] = fmaf(xf[u], av[8 * v + u][j], acc[j]);
+                    for (int j = 0; j < 8; ++j) acc[j] = fmaf(xf[u], av[j], acc[j]);
                 }
             }
         }
