@@ -58,7 +58,7 @@ lora_segments_t carve_segments(char *&p, int32_t M, int32_t n) {
 
 size_t shrink_partial_bytes(int32_t M, int32_t d_in, int32_t r_max) {
     int kc, ksplit;
-    shrink_plan(d_in, &kc, &ksplit);
+    shrink_plan(d_in, r_max, &kc, &ksplit);
     return round_up((size_t)ksplit * M * r_max * sizeof(float));
 }
 
@@ -132,7 +132,7 @@ lora_status_t lora_shrink(const void *x, const void *A, const int32_t *ranks, in
         return LORA_ERR_ALIGN;
     if (ws_bytes < shrink_partial_bytes(M, d_in, r_max)) return LORA_ERR_WORKSPACE;
     int kc, ksplit;
-    shrink_plan(d_in, &kc, &ksplit);
+    shrink_plan(d_in, r_max, &kc, &ksplit);
     clear_stale_error();
     hipStream_t s = (hipStream_t)stream;
     float *partial = static_cast<float *>(ws);
@@ -247,7 +247,7 @@ hipError_t run_linear(const void *x, const void *W, const void *A, const void *B
         mark(mk, "build_segments");
     }
     int kc, ksplit;
-    shrink_plan(d_in, &kc, &ksplit);
+    shrink_plan(d_in, r_max, &kc, &ksplit);
     if ((e = launch_shrink(xb, static_cast<const uint16_t *>(A), ranks, M, d_in, r_max, n_adapters,
                            sg, spart, kc, ksplit, s)) != hipSuccess)
         return e;

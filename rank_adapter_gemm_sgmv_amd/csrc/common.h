@@ -153,6 +153,6 @@ hipError_t launch_decode_reduce(const float *partial, int M, int K, int N, void 
 size_t gemm_partial_floats(int M, int K, int N);
 
 // Split-K plan of the shrink for d_in.
-void shrink_plan(int d_in, int *kc, int *ksplit);
+void shrink_plan(int d_in, int r_max, int *kc, int *ksplit);
 
 }  // namespace lora

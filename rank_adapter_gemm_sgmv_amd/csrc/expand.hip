@@ -6,12 +6,13 @@
 // LoRA weights into the base model?".  Memory-bound on B_i (same page, "How does one batch
 // run 30 different adapters at once?").
 //
-// Work item = (tile, 512-column chunk), one wave64 each, 8 consecutive columns per lane, so
-// every load of B_i[j, c:c+8] and of y is a 16-byte vector and a wave touches 1 KiB
-// contiguous per B row.  For r_max <= 16 the wave keeps its B_i[0:r, c:c+8] slice in
-// registers and sweeps the tile's rows over it, so B_i comes from HBM once per tile; for
-// larger r_max the rows re-read it from L1/L2.  t[m, :] is uniform across the wave and is
-// read through the scalar cache.  The sum over j runs in ascending order in fp32; then
+// Work item = (tile, column chunk), one wave each.  The wave holds B_i[0:rank, chunk] in
+// registers -- CPL consecutive columns per lane (8 for r_max <= 16, else 4), one load per
+// rank row, rows at or beyond the adapter's rank are neither read nor multiplied -- and
+// streams the tile's rows past it, four at a time: for each row the lane's CPL columns of y
+// and one element of t[m, :] (lane j holds t[m, j], broadcast with readlane) are loaded
+// together for the whole batch, and each B_i row is unpacked once per batch.  So each B_i
+// slice is read once per tile.  The sum over j runs in ascending order in fp32; then
 // y = y + scale * sum is rounded once into y's dtype.  Base-only rows are never touched.
 #include "common.h"
 
@@ -19,97 +20,153 @@ namespace lora {
 
 namespace {
 
-constexpr int kCols = 512;  // columns per work item: 64 lanes x 8
+constexpr int kWavesPerBlock = 4;
 constexpr int kMaxGrid = 1 << 20;
+constexpr int RB = 4;  // rows whose loads are in flight together
 
-template <bool YF32>
-__device__ __forceinline__ void add_into_y(void *y, size_t off, const float acc[8], float s) {
+template <int RM>
+struct ExpandLanes {
+    static constexpr int CPL = RM <= 16 ? 8 : 4;  // columns per lane
+    static constexpr int COLS = 64 * CPL;         // columns per work item
+    static constexpr int BW = CPL / 2;            // 32-bit words of B per rank row and lane
+};
+
+template <int CPL>
+struct Vec;
+template <>
+struct Vec<8> {
+    uint4 v;
+};
+template <>
+struct Vec<4> {
+    uint2 v;
+};
+
+template <int CPL>
+__device__ __forceinline__ Vec<CPL> ldv(const uint16_t *p) {
+    Vec<CPL> r;
+    if constexpr (CPL == 8) r.v = *reinterpret_cast<const uint4 *>(p);
+    else r.v = *reinterpret_cast<const uint2 *>(p);
+    return r;
+}
+
+template <int CPL>
+__device__ __forceinline__ void unpackv(const Vec<CPL> &b, float (&f)[CPL]) {
+    if constexpr (CPL == 8) {
+        unpack8(b.v, f);
+    } else {
+        f[0] = bf16_lo(b.v.x); f[1] = bf16_hi(b.v.x);
+        f[2] = bf16_lo(b.v.y); f[3] = bf16_hi(b.v.y);
+    }
+}
+
+// y row slice: bf16 (CPL * 2 bytes) or f32 (CPL * 4 bytes)
+template <int CPL, bool YF32>
+struct YSlice {
+    float f[CPL];
+};
+
+template <int CPL, bool YF32>
+__device__ __forceinline__ void load_y(YSlice<CPL, YF32> &ys, const void *y, size_t off) {
+    if constexpr (YF32) {
+        const float4 *p = reinterpret_cast<const float4 *>(reinterpret_cast<const float *>(y) + off);
+#pragma unroll
+        for (int q = 0; q < CPL / 4; ++q) {
+            const float4 v = p[q];
+            ys.f[4 * q] = v.x; ys.f[4 * q + 1] = v.y; ys.f[4 * q + 2] = v.z; ys.f[4 * q + 3] = v.w;
+        }
+    } else {
+        const Vec<CPL> v = ldv<CPL>(reinterpret_cast<const uint16_t *>(y) + off);
+        unpackv<CPL>(v, ys.f);
+    }
+}
+
+template <int CPL, bool YF32>
+__device__ __forceinline__ void store_y(void *y, size_t off, const float (&f)[CPL]) {
     if constexpr (YF32) {
         float4 *p = reinterpret_cast<float4 *>(reinterpret_cast<float *>(y) + off);
-        float4 a = p[0], b = p[1];
-        a.x = fmaf(s, acc[0], a.x); a.y = fmaf(s, acc[1], a.y);
-        a.z = fmaf(s, acc[2], a.z); a.w = fmaf(s, acc[3], a.w);
-        b.x = fmaf(s, acc[4], b.x); b.y = fmaf(s, acc[5], b.y);
-        b.z = fmaf(s, acc[6], b.z); b.w = fmaf(s, acc[7], b.w);
-        p[0] = a;
-        p[1] = b;
+#pragma unroll
+        for (int q = 0; q < CPL / 4; ++q) p[q] = make_float4(f[4 * q], f[4 * q + 1], f[4 * q + 2], f[4 * q + 3]);
     } else {
         uint16_t *p = reinterpret_cast<uint16_t *>(y) + off;
-        const uint4 v = ld16(p);
-        float f[8];
-        unpack8(v, f);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) f[e] = fmaf(s, acc[e], f[e]);
-        st16(p, make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
-                           pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7])));
+        if constexpr (CPL == 8) {
+            st16(p, make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
+                               pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7])));
+        } else {
+            *reinterpret_cast<uint2 *>(p) = make_uint2(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]));
+        }
     }
 }
 
 template <int RM, bool YF32>
-__global__ __launch_bounds__(64) void expand_kernel(const float *__restrict__ t,
-                                                    const uint16_t *__restrict__ B,
-                                                    const float *__restrict__ scale,
-                                                    const int32_t *__restrict__ ranks, int d_out,
-                                                    int n_cc, Seg seg, void *__restrict__ y) {
-    const int lane = threadIdx.x;
+__global__ __launch_bounds__(64 * kWavesPerBlock) void expand_kernel(
+    const float *__restrict__ t, const uint16_t *__restrict__ B, const float *__restrict__ scale,
+    const int32_t *__restrict__ ranks, int M, int d_out, int n_cc, Seg seg, void *__restrict__ y) {
+    using L = ExpandLanes<RM>;
+    constexpr int CPL = L::CPL;
+    const int lane = threadIdx.x & 63;
     const int total = seg.meta[3] * n_cc;
-    for (int w = blockIdx.x; w < total; w += gridDim.x) {
+    const int nw = gridDim.x * kWavesPerBlock;
+    for (int w = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6); w < total; w += nw) {
         const int tile = w / n_cc, cc = w % n_cc;
         const int p0 = seg.tiles[2 * tile], a = seg.tiles[2 * tile + 1];
         const int p1 = min(p0 + kTileRows, seg.offsets[a + 1]);
         const int r = ranks ? min(max(ranks[a], 0), RM) : RM;
         const float s = scale[a];
-        const int c = cc * kCols + lane * 8;
-        if (c >= d_out) continue;  // no barriers in this kernel: idle lanes may leave
-        const uint16_t *Bp = B + (size_t)a * RM * d_out + c;
+        const int c = cc * L::COLS + lane * CPL;
+        const bool colok = c < d_out;  // d_out % 8 == 0: a lane's columns are all in or all out
+        const int cl = colok ? c : 0;
 
-        if constexpr (RM <= 16) {
-            uint4 bj[RM];
+        // B_a[0:r, c .. c+CPL): one load per rank row
+        Vec<CPL> bj[RM];
+        const uint16_t *Bp = B + (size_t)a * RM * d_out + cl;
 #pragma unroll
-            for (int j = 0; j < RM; ++j)
-                bj[j] = (j < r) ? ld16(Bp + (size_t)j * d_out) : make_uint4(0, 0, 0, 0);
-            for (int p = p0; p < p1; ++p) {
-                const int m = seg.perm[p];
-                const float *tm = t + (size_t)m * RM;
-                float acc[8];
+        for (int j = 0; j < RM; ++j) {
+            if (j < r) bj[j] = ldv<CPL>(Bp + (size_t)j * d_out);
+            else bj[j].v = {};
+        }
+
+        // rows of the tile in batches of RB: the lane's y slice of each row and t[m, lane]
+        // (lane j < r_max holds t[m, j]; read back with readlane) are loaded together
+        for (int pb = p0; pb < p1; pb += RB) {
+            int mb[RB];
+            YSlice<CPL, YF32> yb[RB];
+            float tv[RB];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
-#pragma unroll
-                for (int j = 0; j < RM; ++j) {
-                    if (j < r) {
-                        float b[8];
-                        unpack8(bj[j], b);
-                        const float tj = tm[j];
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) acc[e] = fmaf(tj, b[e], acc[e]);
-                    }
-                }
-                add_into_y<YF32>(y, (size_t)m * d_out + c, acc, s);
+            for (int i = 0; i < RB; ++i) {
+                mb[i] = seg.perm[min(pb + i, M - 1)];
+                load_y<CPL, YF32>(yb[i], y, (size_t)mb[i] * d_out + cl);
+                tv[i] = t[(size_t)mb[i] * RM + (lane < RM ? lane : 0)];
             }
-        } else {
-            for (int p = p0; p < p1; ++p) {
-                const int m = seg.perm[p];
-                const float *tm = t + (size_t)m * RM;
-                float acc[8];
+            float acc[RB][CPL];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
-                for (int j0 = 0; j0 < r; j0 += 16) {
-                    uint4 bj[16];
+            for (int i = 0; i < RB; ++i)
 #pragma unroll
-                    for (int u = 0; u < 16; ++u)
-                        bj[u] = (j0 + u < r) ? ld16(Bp + (size_t)(j0 + u) * d_out) : make_uint4(0, 0, 0, 0);
+                for (int e = 0; e < CPL; ++e) acc[i][e] = 0.0f;
+            // rank row j outer: B_a[j] is unpacked once per batch and used by all its rows
 #pragma unroll
-                    for (int u = 0; u < 16; ++u) {
-                        if (j0 + u < r) {
-                            float b[8];
-                            unpack8(bj[u], b);
-                            const float tj = tm[j0 + u];
+            for (int j = 0; j < RM; ++j) {
+                if (j < r) {
+                    float b[CPL];
+                    unpackv<CPL>(bj[j], b);
 #pragma unroll
-                            for (int e = 0; e < 8; ++e) acc[e] = fmaf(tj, b[e], acc[e]);
-                        }
+                    for (int i = 0; i < RB; ++i) {
+                        const float tj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(tv[i]), j));
+#pragma unroll
+                        for (int e = 0; e < CPL; ++e) acc[i][e] = fmaf(tj, b[e], acc[i][e]);
                     }
                 }
-                add_into_y<YF32>(y, (size_t)m * d_out + c, acc, s);
+            }
+            if (colok) {
+#pragma unroll
+                for (int i = 0; i < RB; ++i) {
+                    if (pb + i < p1) {
+                        float out[CPL];
+#pragma unroll
+                        for (int e = 0; e < CPL; ++e) out[e] = fmaf(s, acc[i][e], yb[i].f[e]);
+                        store_y<CPL, YF32>(y, (size_t)mb[i] * d_out + c, out);
+                    }
+                }
             }
         }
     }
@@ -117,11 +174,17 @@ __global__ __launch_bounds__(64) void expand_kernel(const float *__restrict__ t,
 
 template <int RM>
 hipError_t launch_rm(const float *t, const uint16_t *B, const float *scale, const int32_t *ranks,
-                     int d_out, int n_cc, int grid, Seg seg, void *y, bool y_f32, hipStream_t s) {
+                     int M, int d_out, int n_adapters, Seg seg, void *y, bool y_f32, hipStream_t s) {
+    using L = ExpandLanes<RM>;
+    const int n_cc = (d_out + L::COLS - 1) / L::COLS;
+    const long items = (long)lora_max_tiles(M, n_adapters) * n_cc;
+    const long blocks = (items + kWavesPerBlock - 1) / kWavesPerBlock;
+    const dim3 grid((unsigned)(blocks < kMaxGrid ? blocks : kMaxGrid));
+    const dim3 block(64 * kWavesPerBlock);
     if (y_f32)
-        launch((expand_kernel<RM, true>), dim3(grid), dim3(64), 0, s, t, B, scale, ranks, d_out, n_cc, seg, y);
+        launch((expand_kernel<RM, true>), grid, block, 0, s, t, B, scale, ranks, M, d_out, n_cc, seg, y);
     else
-        launch((expand_kernel<RM, false>), dim3(grid), dim3(64), 0, s, t, B, scale, ranks, d_out, n_cc, seg, y);
+        launch((expand_kernel<RM, false>), grid, block, 0, s, t, B, scale, ranks, M, d_out, n_cc, seg, y);
     return hipGetLastError();
 }
 
@@ -130,14 +193,11 @@ hipError_t launch_rm(const float *t, const uint16_t *B, const float *scale, cons
 hipError_t launch_expand(const float *t, const uint16_t *B, const float *scale,
                          const int32_t *ranks, int M, int d_out, int r_max, int n_adapters,
                          Seg seg, void *y, bool y_f32, hipStream_t s) {
-    const int n_cc = (d_out + kCols - 1) / kCols;
-    const long items = (long)lora_max_tiles(M, n_adapters) * n_cc;
-    const int grid = (int)(items < kMaxGrid ? items : kMaxGrid);
     switch (r_max) {
-        case 8: return launch_rm<8>(t, B, scale, ranks, d_out, n_cc, grid, seg, y, y_f32, s);
-        case 16: return launch_rm<16>(t, B, scale, ranks, d_out, n_cc, grid, seg, y, y_f32, s);
-        case 32: return launch_rm<32>(t, B, scale, ranks, d_out, n_cc, grid, seg, y, y_f32, s);
-        case 64: return launch_rm<64>(t, B, scale, ranks, d_out, n_cc, grid, seg, y, y_f32, s);
+        case 8: return launch_rm<8>(t, B, scale, ranks, M, d_out, n_adapters, seg, y, y_f32, s);
+        case 16: return launch_rm<16>(t, B, scale, ranks, M, d_out, n_adapters, seg, y, y_f32, s);
+        case 32: return launch_rm<32>(t, B, scale, ranks, M, d_out, n_adapters, seg, y, y_f32, s);
+        case 64: return launch_rm<64>(t, B, scale, ranks, M, d_out, n_adapters, seg, y, y_f32, s);
         default: return hipErrorInvalidValue;
     }
 }
