@@ -269,24 +269,14 @@ def cpu_baseline(w, seconds: float):
 # ---------------------------------------------------------------------------------------
 
 
-def kernel_sources_digest() -> str:
-    import hashlib
-
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "rank_adapter_gemm_sgmv_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h", ".cpp")):
-            with open(os.path.join(csrc, f), "rb") as fh:
-                h.update(f.encode() + fh.read())
-    return h.hexdigest()[:16]
-
-
 def committed_traffic(workload: str, kernel: str):
     """HBM bytes per launch from profiles/counters_<workload>.md, if taken on these sources."""
     path = os.path.join(ROOT, "profiles", f"counters_{workload}.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
+    from rank_adapter_gemm_sgmv_amd.profsum import kernel_sources_digest
+
     m = re.search(r"sources_digest:\s*([0-9a-f]+)", text)
     if not m or m.group(1) != kernel_sources_digest():
         return None
@@ -372,6 +362,33 @@ def run_workload(config, mode_name, steps, warmup, torch, profile_reps=20, need_
     return w, s, kernels, steps, ms_total
 
 
+CALIB_BYTES = 256 << 20
+
+
+def pmc_pass(config, mode_name, steps, torch):
+    """Eager steps of one workload, then the counter calibration kernel: torch.neg over
+    CALIB_BYTES of bf16 (reads CALIB_BYTES, writes CALIB_BYTES), three times.  Meant to run
+    under ``rocprofv3 --pmc``; no timing."""
+    from synth import make_workload
+
+    w = make_workload(config).as_bf16()
+    prefill = mode_name == "prefill"
+    mode = L_.LORA_MODE_PREFILL if prefill else L_.LORA_MODE_DECODE
+    L = layers_needed(w, prefill)
+    runner = Runner(w, mode, torch, L, rotate_x=prefill, prebuilt_segments=len(w.projections) > 1)
+    for i in range(steps):
+        runner.step(i)
+    torch.cuda.synchronize()
+    src = torch.ones(CALIB_BYTES // 2, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"pmc_pass": w.name, "mode": mode_name, "steps": steps, "layers_rotated": L,
+                      "calibration": {"kernel": "torch.neg bf16", "bytes_read": CALIB_BYTES,
+                                      "bytes_written": CALIB_BYTES, "launches": 3}}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -382,6 +399,9 @@ def main():
     ap.add_argument("--workload", type=int, default=2, choices=(2, 3, 4, 5),
                     help="workload of the headline line (2 = decode q_proj, the default)")
     ap.add_argument("--mode", default="decode", choices=("decode", "prefill"))
+    ap.add_argument("--pmc-pass", action="store_true",
+                    help="only eager steps of the chosen workload plus the counter calibration "
+                         "kernel, for rocprofv3 --pmc runs (FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (this build runs "
@@ -395,6 +415,9 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.pmc_pass:
+        pmc_pass(args.workload, args.mode, args.steps, torch)
+        return
 
     # headline: decode, q_proj geometry (unless another workload is asked for)
     w, head, kernels, steps, ms_total = run_workload(args.workload, args.mode, args.steps,
