@@ -1,5 +1,6 @@
 // decode_gemm.hip -- y = x W + (x A_i) B_i * scale_i for small (decode) batches: the shared
-// GEMM streamed from HBM, the split-K reduction and the LoRA expand in one kernel.
+// GEMM streamed from HBM with the LoRA expand as one more K split, then an ordered split-K
+// reduction.
 //
 // Source: "Multi-LoRA Serving: Why 100 Adapters Fit on One GPU" (dev.to), "Why can't you
 // just merge LoRA weights into the base model?" (the layer; x W is one GEMM over the batch)
