@@ -12,16 +12,20 @@
 // offsets; the compact list of adapters present; the segments cut into tiles of
 // LORA_TILE_ROWS positions; and meta = {segments, LoRA rows, invalid ids, tiles}.
 //
-// One workgroup of 1024 threads (16 wave64s):
-//   1. histogram of bucket ids into LDS with LDS atomics (counts do not depend on order);
-//   2. one block-wide exclusive scan of three per-bucket quantities at once: rows, "has
-//      rows" and tiles; each thread owns a contiguous run of buckets;
-//   3. stable scatter, 1024 rows per round: every wave finds the lanes that share its
-//      bucket with one ballot per bit of the bucket number (a peer mask), so a row's rank
-//      among equal ids in its wave is a popcount; the waves then take their slots from the
-//      per-bucket cursors strictly in wave order, which keeps the sort stable without any
-//      order-dependent atomic.
-// The result is identical on every run.
+// One workgroup of 1024 threads (16 wave64s).  Every wave finds the lanes that share its
+// bucket with one ballot per bit of the bucket number (a peer mask), so a row's rank among
+// equal ids inside 64 rows is a popcount.  One block-wide exclusive scan of three per-bucket
+// quantities (rows, "has rows", tiles) gives the offsets.  Two kernels differ in how the
+// waves are ordered for the stable scatter:
+//   * M > 1024 and n_adapters < 960 (build_segments_small_kernel): wave w owns a contiguous chunk of
+//     rows and counts its rows per bucket into an LDS table pos[w][bucket]; a per-bucket
+//     scan over the waves turns the table into each wave's first position per bucket, and
+//     every wave then scatters its chunk independently.
+//   * otherwise (build_segments_kernel): histogram by LDS atomics (counts do not depend
+//     on order), then 1024 rows per round, the waves of a round taking their slots from the
+//     per-bucket cursors strictly in wave order.
+// No order-dependent atomic reaches perm: the result is identical on every run, and the
+// same for both kernels.
 #include "common.h"
 
 namespace lora {
@@ -40,35 +44,15 @@ __device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
     return v;
 }
 
-__global__ __launch_bounds__(kThreads) void build_segments_kernel(const int32_t *__restrict__ ids,
-                                                                  int M, int n, Seg seg) {
-    // cnt[b]: count of bucket b (b = n collects base-only and invalid ids), later the
-    // next free position of bucket b in perm.
-    __shared__ int32_t cnt[LORA_MAX_ADAPTERS + 1];
-    __shared__ int32_t wave_tot[3][kWaves];
-    __shared__ int32_t bad_total;
-
+// Step 2 of both kernels: cnt[0..n) holds the row count of every bucket (cnt[n] is not
+// read).  Writes offsets, seg_adapter, tiles and meta, and leaves cnt[b] = first position of
+// bucket b in perm (cnt[n] = first base-only position).  Contains three barriers; every
+// thread of the workgroup must call it.
+__device__ void scan_buckets(int32_t *cnt, int32_t (*wave_tot)[kWaves], int n, int bad_total,
+                             Seg seg) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-
-    for (int b = tid; b <= n; b += kThreads) cnt[b] = 0;
-    if (tid == 0) bad_total = 0;
-    __syncthreads();
-
-    // 1. histogram
-    int bad = 0;
-    for (int m = tid; m < M; m += kThreads) {
-        const int id = ids[m];
-        int b = id;
-        if (id < 0 || id >= n) {
-            b = n;
-            bad += (id != -1);
-        }
-        atomicAdd(&cnt[b], 1);
-    }
-    if (bad) atomicAdd(&bad_total, bad);
-    __syncthreads();
-
-    // 2. exclusive scans over buckets 0..n-1 of (rows, present, tiles)
+    // exclusive scans over buckets 0..n-1 of (rows, present, tiles); each thread owns a
+    // contiguous run of buckets
     const int per = (n + kThreads - 1) / kThreads;
     const int b0 = min(tid * per, n), b1 = min(b0 + per, n);
     int rows = 0, segs = 0, tiles = 0;
@@ -121,6 +105,50 @@ __global__ __launch_bounds__(kThreads) void build_segments_kernel(const int32_t 
         seg.meta[3] = ttl;
     }
     __syncthreads();
+}
+
+// bucket of a row: its adapter, or n for base-only and invalid ids
+__device__ __forceinline__ int bucket_of(int id, int n) { return (id < 0 || id >= n) ? n : id; }
+
+// Lanes of this wave whose bucket equals mine (valid lanes only): one ballot per bit.
+__device__ __forceinline__ uint64_t peer_mask(int b, bool valid, int nbits) {
+    uint64_t peers = __ballot(valid);
+    for (int bit = 0; bit < nbits; ++bit) {
+        const bool set = (b >> bit) & 1;
+        const uint64_t bal = __ballot(valid && set);
+        peers &= set ? bal : ~bal;
+    }
+    return peers;
+}
+
+// Any n.  The stable scatter takes 1024 rows per round and the waves of a round in order.
+__global__ __launch_bounds__(kThreads) void build_segments_kernel(const int32_t *__restrict__ ids,
+                                                                  int M, int n, Seg seg) {
+    // cnt[b] (dynamic LDS, n + 1 entries): count of bucket b (b = n collects base-only and
+    // invalid ids), later the next free position of bucket b in perm.
+    extern __shared__ int32_t dyn[];
+    int32_t *cnt = dyn;
+    __shared__ int32_t wave_tot[3][kWaves];
+    __shared__ int32_t bad_total;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+    for (int b = tid; b <= n; b += kThreads) cnt[b] = 0;
+    if (tid == 0) bad_total = 0;
+    __syncthreads();
+
+    // 1. histogram
+    int bad = 0;
+    for (int m = tid; m < M; m += kThreads) {
+        const int id = ids[m];
+        bad += (id != -1 && (id < 0 || id >= n));
+        atomicAdd(&cnt[bucket_of(id, n)], 1);
+    }
+    if (bad) atomicAdd(&bad_total, bad);
+    __syncthreads();
+
+    // 2. offsets, segments, tiles
+    scan_buckets(cnt, wave_tot, n, bad_total, seg);
 
     // 3. stable scatter
     const int nbits = 32 - __clz(n);  // bits of the largest bucket number, n
@@ -128,17 +156,8 @@ __global__ __launch_bounds__(kThreads) void build_segments_kernel(const int32_t 
     for (int c0 = 0; c0 < M; c0 += kThreads) {
         const int m = c0 + tid;
         const bool valid = m < M;
-        int b = 0;
-        if (valid) {
-            const int id = ids[m];
-            b = (id < 0 || id >= n) ? n : id;
-        }
-        uint64_t peers = __ballot(valid);
-        for (int bit = 0; bit < nbits; ++bit) {
-            const bool set = (b >> bit) & 1;
-            const uint64_t bal = __ballot(valid && set);
-            peers &= set ? bal : ~bal;
-        }
+        const int b = valid ? bucket_of(ids[m], n) : 0;
+        const uint64_t peers = peer_mask(b, valid, nbits);
         const int rank = __popcll(peers & lanes_below);
         const int same = __popcll(peers);
         const int waves_used = min(kWaves, (M - c0 + 63) / 64);
@@ -157,12 +176,110 @@ __global__ __launch_bounds__(kThreads) void build_segments_kernel(const int32_t 
     }
 }
 
+// n < kSmallN.  Wave w owns the contiguous rows [w C, (w+1) C), C a multiple of 64, and
+// walks them in order twice: first counting its rows per bucket into pos[w][b], then -- once
+// pos[w][b] has become the first perm position of bucket b's rows in wave w (bucket start
+// plus the counts of waves < w) -- writing perm.  Rows of one bucket thus keep their order
+// inside a wave and across waves, with no order-dependent step shared between waves, and
+// the workgroup needs only the barriers of the scans.
+// Dynamic LDS: cnt[n + 1], then pos[kWaves][n + 1] (row stride n + 1); at most 64 KiB.
+constexpr int kSmallN = 960;
+
+__global__ __launch_bounds__(kThreads) void build_segments_small_kernel(
+    const int32_t *__restrict__ ids, int M, int n, Seg seg) {
+    extern __shared__ int32_t dyn[];
+    const int nb = n + 1;
+    int32_t *cnt = dyn;
+    int32_t *pos = dyn + nb;
+    __shared__ int32_t wave_tot[3][kWaves];
+    __shared__ int32_t bad_total;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    for (int i = tid; i < kWaves * nb; i += kThreads) pos[i] = 0;
+    if (tid == 0) bad_total = 0;
+    __syncthreads();
+
+    const int C = ((M + kWaves - 1) / kWaves + 63) & ~63;
+    const int r0 = wave * C, r1 = min(r0 + C, M);
+    const int nbits = 32 - __clz(n);
+    const uint64_t lanes_below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+
+    // 1. per-wave histogram (one writer per (wave, bucket) per block of 64 rows: the peer
+    //    group's lowest lane; a wave's LDS instructions execute in order).  The ids of four
+    //    blocks are loaded together.
+    int bad = 0;
+    for (int c0 = r0; c0 < r1; c0 += 4 * 64) {
+        int bq[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int m = c0 + 64 * q + lane;
+            const int id = m < r1 ? ids[m] : -1;
+            bq[q] = bucket_of(id, n);
+            bad += (id != -1 && bq[q] == n);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const bool valid = c0 + 64 * q + lane < r1;
+            const uint64_t peers = peer_mask(bq[q], valid, nbits);
+            if (valid && __popcll(peers & lanes_below) == 0) pos[wave * nb + bq[q]] += __popcll(peers);
+        }
+    }
+    if (bad) atomicAdd(&bad_total, bad);
+    __syncthreads();
+
+    // per bucket: totals, and pos[w][b] = rows of bucket b in waves < w
+    for (int b = tid; b <= n; b += kThreads) {
+        int c[kWaves];
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) c[w] = pos[w * nb + b];  // all reads first
+        int run = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            pos[w * nb + b] = run;
+            run += c[w];
+        }
+        cnt[b] = run;
+    }
+    __syncthreads();
+
+    // 2. offsets, segments, tiles; cnt[b] becomes the first position of bucket b
+    scan_buckets(cnt, wave_tot, n, bad_total, seg);
+
+    // 3. scatter: the same walk as step 1
+    for (int c0 = r0; c0 < r1; c0 += 4 * 64) {
+        int bq[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int m = c0 + 64 * q + lane;
+            bq[q] = m < r1 ? bucket_of(ids[m], n) : n;
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int m = c0 + 64 * q + lane;
+            const bool valid = m < r1;
+            const uint64_t peers = peer_mask(bq[q], valid, nbits);
+            const int rank = __popcll(peers & lanes_below);
+            if (valid) {
+                const int base = cnt[bq[q]] + pos[wave * nb + bq[q]];
+                if (rank == 0) pos[wave * nb + bq[q]] += __popcll(peers);
+                seg.perm[base + rank] = m;
+            }
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_build_segments(const int32_t *ids, int M, int n_adapters, Seg seg,
                                  hipStream_t s) {
-    launch(build_segments_kernel, dim3(1), dim3(kThreads), 0, s, ids, M, n_adapters,
-                       seg);
+    const uint32_t nb = (uint32_t)n_adapters + 1;
+    // up to 1024 rows the scatter is one round of at most 16 wave steps, which costs less
+    // than the table's extra pass
+    if (n_adapters < kSmallN && M > kThreads)
+        launch(build_segments_small_kernel, dim3(1), dim3(kThreads), (kWaves + 1) * nb * 4, s, ids, M,
+               n_adapters, seg);
+    else
+        launch(build_segments_kernel, dim3(1), dim3(kThreads), nb * 4, s, ids, M, n_adapters, seg);
     return hipGetLastError();
 }
 

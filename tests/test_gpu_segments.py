@@ -1,7 +1,8 @@
 """GPU segment builder vs the oracle's stable counting sort: bit-exact.
 
 Covers the ids of the five named workloads, random batches (ragged sizes, 1..16384
-adapters), the degenerate cases (one row, all rows base-only, all rows one adapter, one
+adapters, both sides of the 960-adapter switch between the two builder kernels), the
+degenerate cases (one row, all rows base-only, all rows one adapter, one
 adapter in the pool) and out-of-range ids (counted in meta[2], treated as base-only).
 """
 
@@ -57,6 +58,10 @@ CASES = [
     ("ragged 1025", None, 1024),
     ("large 5000", None, 16384),
     ("large 20000 zipf-like", None, 300),
+    ("edge 3000", None, 959),
+    ("edge 2100", None, 960),
+    ("long 100000", None, 600),
+    ("contiguous 4096 runs", np.repeat(np.arange(8, dtype=np.int32), 512), 8),
 ]
 
 
