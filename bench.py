@@ -86,12 +86,13 @@ def algorithmic_work(w, d_in: int, d_out: int, prefill: bool, y_bytes: int = 2) 
                                     "flops": base_flops + 2.0 * r_rows * d_out}
     else:
         out["gemm_decode"] = {"bytes": gemm_bytes, "flops": base_flops}
-        # small-batch decode path: shrink (A_i, x rows, t), GEMM with the LoRA K-extension
-        # (W, x, the expand's B_i and t), ordered reduction (writes y once)
-        out["decode_shrink"] = {"bytes": shrink, "flops": 2.0 * r_rows * d_in}
-        out["decode_gemm_lora"] = {"bytes": gemm_bytes + b_bytes + t_bytes,
-                                   "flops": base_flops + 2.0 * r_rows * d_out}
-        out["decode_reduce"] = {"bytes": M * d_out * y_bytes, "flops": 0.0}
+        # small-batch decode path: the split-K GEMM (W, x) whose workgroups also run the
+        # shrink (the touched A_i, t written), then the ordered reduction with the expand
+        # (the touched B_i, t read, y written once)
+        out["decode_gemm_shrink"] = {"bytes": gemm_bytes + a_bytes + t_bytes,
+                                     "flops": base_flops + 2.0 * r_rows * d_in}
+        out["decode_reduce_lora"] = {"bytes": b_bytes + t_bytes + M * d_out * y_bytes,
+                                     "flops": 2.0 * r_rows * d_out}
     return out
 
 
@@ -316,7 +317,7 @@ def summarize(w, runner, ms_total, steps, wall, eager_ms, kernels, prefill):
         entry = {"projection": p.name, "d_in": p.d_in, "d_out": p.d_out,
                  "kernels_us": {k: round(v * 1e3, 2) for k, v in ks.items()}}
         gname = "gemm_prefill_lora" if prefill else (
-            "decode_gemm_lora" if "decode_gemm_lora" in ks else "gemm_decode")
+            "decode_gemm_shrink" if "decode_gemm_shrink" in ks else "gemm_decode")
         if gname in ks:
             g_ms = ks[gname]
             entry["gemm_tflops"] = work[gname]["flops"] / (g_ms * 1e-3) / 1e12
@@ -339,7 +340,8 @@ def summarize(w, runner, ms_total, steps, wall, eager_ms, kernels, prefill):
         "ms_per_step": ms_step,
         "ms_per_step_eager": eager_ms,
         "kernel_sum_ms": total_kernel_ms,
-        "lora_overhead_vs_base_gemm": (lora_s / base_s) if base_s > 0 else None,
+        # segment path only: the small-batch path overlaps the shrink with the GEMM
+        "lora_overhead_vs_base_gemm": (lora_s / base_s) if base_s > 0 and lora_s > 0 else None,
         "projections": per_proj,
     }
 

@@ -204,9 +204,10 @@ lora_status_t check_linear(const void *x, const void *W, const void *A, const vo
 }
 
 // The launch sequence of lora_linear (arguments already validated, M > 0).
-//   decode, M <= 128 and d_in % 32 == 0: decode_shrink, decode GEMM with the LoRA
-//            K-extension split, its ordered reduction (no segment-building launch: each
-//            kernel groups the <= 128 rows by adapter in LDS; segs is not needed)
+//   decode, M <= 128 and d_in % 32 == 0: the split-K GEMM of x W, whose workgroups also
+//            compute the LoRA shrink's chunk sums, then the ordered reduction that adds
+//            scale_a t B_a (no segment-building launch: rows are grouped by adapter in LDS;
+//            segs is not needed)
 //   decode otherwise: build_segments, shrink, shrink_finalize, gemm [, splitk_reduce], expand
 //   prefill: build_segments, shrink, shrink_finalize, gemm with the LoRA epilogue
 hipError_t run_linear(const void *x, const void *W, const void *A, const void *B,
@@ -230,16 +231,16 @@ hipError_t run_linear(const void *x, const void *W, const void *A, const void *B
     const bool yf = y_dtype == LORA_F32;
     hipError_t e;
     if (!prefill && decode_gemm_supported(M, d_in, d_out)) {
-        // small decode batch: three launches, rows grouped by adapter inside each kernel
-        if ((e = launch_decode_shrink(xb, static_cast<const uint16_t *>(A), ids, ranks, M, d_in, r_max,
-                                      n_adapters, tpart, s)) != hipSuccess)
-            return e;
-        mark(mk, "decode_shrink");
+        // small decode batch: the GEMM's workgroups also compute the shrink's chunk sums
+        // (while their first W stages load), then one reduction adds the splits and the
+        // expand
         const DecodeLora lo{tpart, decode_shrink_chunks(d_in, r_max), Bb, scale, ids, r_max, n_adapters};
-        if ((e = launch_decode_gemm(xb, Wb, M, d_in, d_out, y, yf, lo, gpart, s)) != hipSuccess) return e;
-        mark(mk, "decode_gemm_lora");
-        if ((e = launch_decode_reduce(gpart, M, d_in, d_out, y, yf, s)) != hipSuccess) return e;
-        mark(mk, "decode_reduce");
+        if ((e = launch_decode_gemm(xb, Wb, static_cast<const uint16_t *>(A), M, d_in, d_out, lo,
+                                    gpart, s)) != hipSuccess)
+            return e;
+        mark(mk, "decode_gemm_shrink");
+        if ((e = launch_decode_reduce(gpart, M, d_in, d_out, y, yf, lo, s)) != hipSuccess) return e;
+        mark(mk, "decode_reduce_lora");
         return hipSuccess;
     }
     if (!segs) {

@@ -119,9 +119,9 @@ hipError_t launch_gemm_big(const uint16_t *x, const uint16_t *W, int M, int K, i
 hipError_t launch_splitk_reduce(const float *partial, int M, int N, int ksplit, void *y,
                                 bool y_f32, hipStream_t s);
 
-// LoRA operands of the decode GEMM (csrc/decode_gemm.hip).
+// LoRA operands of the small-batch decode reduction (csrc/decode_gemm.hip).
 struct DecodeLora {
-    const float *tpart;    // [n_chunks][M][r_max]: the decode shrink's chunk sums of t
+    float *tpart;          // [n_chunks][M][r_max]: the shrink's chunk sums of t (written by the GEMM)
     int n_chunks;
     const uint16_t *B;     // [n][r_max][d_out]
     const float *scale;    // [n]
@@ -130,24 +130,21 @@ struct DecodeLora {
     int n_adapters;
 };
 
-// Decode batches up to this many rows use the fused decode GEMM when K % 32 == 0.
+// Decode batches up to this many rows use the small-batch path when K % 32 == 0.
 constexpr int kDecodeMaxRows = 128;
 bool decode_gemm_supported(int M, int K, int N);
 size_t decode_gemm_partial_floats(int M, int K, int N);
-// y = x W + delta for decode batches: split-K partial tiles plus one split for the LoRA
-// K-extension, then an ordered reduction kernel that rounds once into y.  Needs the decode
-// shrink's chunk sums of t.
-hipError_t launch_decode_gemm(const uint16_t *x, const uint16_t *W, int M, int K, int N, void *y,
-                              bool y_f32, const DecodeLora &lo, float *partial, hipStream_t s);
+// Split-K partial tiles of x W for a decode batch; the same launch writes the LoRA
+// shrink's chunk sums lo.tpart[c][m][0:r_max] (rows grouped by adapter in LDS).
+hipError_t launch_decode_gemm(const uint16_t *x, const uint16_t *W, const uint16_t *A, int M,
+                              int K, int N, const DecodeLora &lo, float *partial, hipStream_t s);
 
-// Decode shrink (csrc/decode_shrink.hip), M <= kDecodeMaxRows: chunk sums of t = x A_i,
-// tpart[c][m][0:r_max] for rows with an adapter; rows grouped by adapter in LDS.
+// Number of k-chunks of the small-batch shrink (csrc/decode_shrink.h).
 int decode_shrink_chunks(int K, int r_max);
-hipError_t launch_decode_shrink(const uint16_t *x, const uint16_t *A, const int32_t *ids,
-                                const int32_t *ranks, int M, int K, int r_max, int n_adapters,
-                                float *tpart, hipStream_t s);
+// y = (split partials added in order) + scale_a * t B_a, t from the decode shrink's chunk
+// sums; rounds once into y.
 hipError_t launch_decode_reduce(const float *partial, int M, int K, int N, void *y, bool y_f32,
-                                hipStream_t s);
+                                const DecodeLora &lo, hipStream_t s);
 
 // Workspace floats the decode GEMM needs for split-K partials at these sizes.
 size_t gemm_partial_floats(int M, int K, int N);

@@ -1,6 +1,6 @@
 // decode_gemm.hip -- y = x W + (x A_i) B_i * scale_i for small (decode) batches: the shared
-// GEMM streamed from HBM with the LoRA expand as one more K split, then an ordered split-K
-// reduction.
+// GEMM streamed from HBM in K splits, then one kernel that adds the splits in order together
+// with the LoRA expand of every row.
 //
 // Source: "Multi-LoRA Serving: Why 100 Adapters Fit on One GPU" (dev.to), "Why can't you
 // just merge LoRA weights into the base model?" (the layer; x W is one GEMM over the batch)
@@ -10,23 +10,27 @@
 // the expand step).
 //
 // gfx950 design.  With one row per request, x W is bound by reading W once from HBM.
-// Needs the shrink's chunk sums of t (decode_shrink.hip); groups the rows by adapter itself.
-//  * Output tile = BM rows (all of a small batch) x 64 columns; the K range of each tile is
-//    split over `ksplit` workgroups, and inside a workgroup over its four waves.  Each wave
-//    streams its own K sub-range through its own 4-stage LDS ring filled by direct
-//    global->LDS loads, so the K loop has no workgroup barrier at all: only this wave's
-//    s_waitcnt orders its loads and reads.  Three stages (24 KiB per wave) are in flight.
-//  * x tile [BM][32] and W tile [32][64] per stage, XOR-swizzled as in the large GEMM; the
-//    W operand is read with the transposing LDS read (ds_read_b64_tr_b16).
-//  * The LoRA expand is one more split of each tile: the K-extension [x | s t] [W ; B_a].
-//    Its k runs over (adapter of the batch, rank), its W rows are the stacked B_a rows of
-//    the batch's adapters (streamed once per column tile by the same DMA ring), and its x
-//    rows hold scale_a * t[m, :] for the rows of adapter a and zero elsewhere.  So every
-//    touched B_a is read from HBM once, and the delta lands in the same fp32 sums as x W.
+//  * Output tile = BM rows (all of a small batch, padded to 32 or 64) x 64 columns; the K
+//    range of each tile is split over `ks` workgroups (tiles x ks fills the 256 CUs once)
+//    and, inside a workgroup, over its four waves.  Each wave streams its own K sub-range
+//    through its own 4-stage LDS ring filled by direct global->LDS loads, so the K loop has
+//    no workgroup barrier at all: only this wave's s_waitcnt orders its loads and reads.
+//    Three stages (24 KiB per wave) are in flight.
+//  * x tile [BM][32] and W tile [32][64] per stage, XOR-swizzled; the W operand is read with
+//    the transposing LDS read (ds_read_b64_tr_b16); v_mfma_f32_32x32x16_bf16.
+//  * x W does not depend on the LoRA shrink, so the same workgroups also run it: after
+//    grouping the batch's rows by adapter in LDS and issuing the first ring stages, each
+//    pair of waves takes its share of the shrink's work items (decode_shrink.h), whose
+//    loads overlap those stages, and then streams its K range.  The shrink costs no launch
+//    of its own.
 //  * The four waves' partial tiles are added through LDS in wave order and each workgroup
-//    writes its partial tile; a second small kernel adds the partials in split order and
-//    rounds once into y, so the result does not depend on scheduling.
-#include "batch_adapters.h"
+//    writes its partial tile.
+//  * reduce_lora_kernel then writes y[m, :] = (sum of the split partials, in split order)
+//    + scale_a * (t[m, :] B_a) with t[m, :] summed from the shrink's chunk sums in chunk
+//    order, in fp32, rounded once into y's dtype; each touched B_a row slice is read once
+//    from HBM (rows of one adapter share it through L2).  No atomics: the result does not
+//    depend on scheduling.
+#include "decode_shrink.h"
 
 namespace lora {
 
@@ -144,15 +148,14 @@ __device__ __forceinline__ void reduce_waves(const f32x16_t (&acc)[C::TM][C::TN]
     }
 }
 
-// Workgroup (tile, split).  Splits 0 .. ks_base-1 cover K; split ks_base (the extension
-// split) multiplies the LoRA K-extension [s t] [B stacked over the batch's adapters]: its
-// k runs over (adapter slot s, rank j), its x rows hold scale_a * t[m, j] for the rows m of
-// the slot's adapter a (zero for other rows) and its W rows are B_a[j, tile columns].
-// Each split writes its partial tile; reduce_partials_kernel adds them in split order.
-template <class C>
+// Workgroup (tile, split): split `split` covers K rows [split k_per_split, +k_per_split) and
+// writes its partial tile; reduce_lora_kernel adds the splits in order.  Before its K loop
+// the workgroup runs shrink work items blockIdx.x * 2 + wave / 2, stepping by 2 gridDim.x.
+template <class C, int RM>
 __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(
-    const uint16_t *__restrict__ x, const uint16_t *__restrict__ W, int M, int K, int N, int n_tm,
-    int n_tn, int ks_base, int k_per_split, float *__restrict__ partial, DecodeLora lo) {
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ W, const uint16_t *__restrict__ A,
+    int M, int K, int N, int n_tm, int n_tn, int k_per_split, float *__restrict__ partial,
+    DecodeLora lo) {
     // stage s of wave w: X{s}[w * XSLOT ..], W{s}[w * WSLOT ..]
     __shared__ __attribute__((aligned(1024))) uint4 XS0[kWaves * C::XSLOT];
     __shared__ __attribute__((aligned(1024))) uint4 XS1[kWaves * C::XSLOT];
@@ -162,19 +165,24 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(
     __shared__ __attribute__((aligned(1024))) uint4 WS1[kWaves * C::WSLOT];
     __shared__ __attribute__((aligned(1024))) uint4 WS2[kWaves * C::WSLOT];
     __shared__ __attribute__((aligned(1024))) uint4 WS3[kWaves * C::WSLOT];
-    // extension split only: the batch's adapters, and t / scale / slot of the tile's rows
     __shared__ BatchAdapters ba;
-    __shared__ __attribute__((aligned(16))) float s_t[C::BM * 64];
-    __shared__ float s_scale[C::BM];
-    __shared__ int32_t s_slot[C::BM];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n_tiles = n_tm * n_tn;
+    // shrink items name adapters directly when the pool is no larger than the batch (rows
+    // found by a ballot over ids), else through the batch's distinct adapters in LDS
+    const bool by_id = lo.n_adapters <= M;
+    int id0 = -1, id1 = -1;
+    if (by_id) {
+        id0 = lane < M ? lo.ids[lane] : -1;
+        id1 = lane + 64 < M ? lo.ids[lane + 64] : -1;
+    } else {
+        batch_adapters(ba, lo.ids, M, lo.n_adapters);
+    }
     // block -> (tile, split): the splits of one tile are n_tiles apart
     const int tile = blockIdx.x % n_tiles, split = blockIdx.x / n_tiles;
     const int tm = tile % n_tm, tn = tile / n_tm;
     const int m0 = tm * C::BM, n0 = tn * kBN;
-    const bool ext = split == ks_base;
 
     DecSrc<C> src;
 #pragma unroll
@@ -184,14 +192,11 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(
         const int m = min(m0 + row, M - 1);
         src.xp[q] = x + (size_t)m * K + lc * 8;
     }
-    int wrow[C::WINS], wcol[C::WINS];
 #pragma unroll
     for (int q = 0; q < C::WINS; ++q) {
         const int r = 8 * q + (lane >> 3);
         const int lc = (lane & 7) ^ wsw(r);
-        wrow[q] = r;
-        wcol[q] = min(n0 + lc * 8, N - 8);
-        src.wp[q] = W + (size_t)r * N + wcol[q];
+        src.wp[q] = W + (size_t)r * N + min(n0 + lc * 8, N - 8);
     }
 
     f32x16_t acc[C::TM][C::TN];
@@ -203,128 +208,54 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
     const int xo = wave * C::XSLOT, wo = wave * C::WSLOT;
 
-    if (!ext) {
-        // ---- base term: this wave's part of the split's K range --------------------------
-        const int ks0 = split * k_per_split;
-        const int ks1 = min(K, ks0 + k_per_split);
-        const int per_wave = k_per_split / kWaves;  // multiple of 32
-        const int kw0 = min(ks1, ks0 + wave * per_wave);
-        const int kw1 = min(ks1, kw0 + per_wave);
-        const int nst = (kw1 - kw0) / kBK;
-        // k of stage s (stages past the last reload the last one; an empty range loads k=0)
+    // this wave's part of the split's K range
+    const int ks0 = split * k_per_split;
+    const int ks1 = min(K, ks0 + k_per_split);
+    const int per_wave = k_per_split / kWaves;  // multiple of 32
+    const int kw0 = min(ks1, ks0 + wave * per_wave);
+    const int kw1 = min(ks1, kw0 + per_wave);
+    const int nst = (kw1 - kw0) / kBK;
+    // k of stage s (stages past the last reload the last one; an empty range loads k=0)
 #define KLOAD(S) (nst > 0 ? kw0 + min((S), nst - 1) * kBK : 0)
-        dec_issue<C>(src, XS0 + xo, WS0 + wo, KLOAD(0), N);
-        dec_issue<C>(src, XS1 + xo, WS1 + wo, KLOAD(1), N);
-        dec_issue<C>(src, XS2 + xo, WS2 + wo, KLOAD(2), N);
-#define DEC_STEP(SS, XC, WC, XN, WN)                                   \
-        wait_vm<2 * C::PER>();                                         \
-        wait_lgkm0();                                                  \
-        dec_issue<C>(src, XN + xo, WN + wo, KLOAD((SS) + 3), N);       \
-        if ((SS) < nst) dec_mfma<C>(acc, XC + xo, WC + wo, lane);
-        for (int s = 0; s < nst; s += 4) {
-            DEC_STEP(s, XS0, WS0, XS3, WS3)
-            DEC_STEP(s + 1, XS1, WS1, XS0, WS0)
-            DEC_STEP(s + 2, XS2, WS2, XS1, WS1)
-            DEC_STEP(s + 3, XS3, WS3, XS2, WS2)
+    dec_issue<C>(src, XS0 + xo, WS0 + wo, KLOAD(0), N);
+    dec_issue<C>(src, XS1 + xo, WS1 + wo, KLOAD(1), N);
+    dec_issue<C>(src, XS2 + xo, WS2 + wo, KLOAD(2), N);
+    // the shrink's work items, while the first stages load: wave pair wave / 2, rows of
+    // parity wave % 2
+    {
+        const uint64_t par = (wave & 1) ? 0xAAAAAAAAAAAAAAAAull : 0x5555555555555555ull;
+        const int n_items = lo.n_chunks * (by_id ? lo.n_adapters : ba.T);
+        for (int w = blockIdx.x * 2 + (wave >> 1); w < n_items; w += gridDim.x * 2) {
+            const int c = w % lo.n_chunks, s = w / lo.n_chunks;
+            int a;
+            uint64_t r0, r1;
+            if (by_id) {
+                a = s;
+                r0 = __ballot(id0 == a);
+                r1 = __ballot(id1 == a);
+            } else {
+                a = ba.list[s];
+                r0 = __ballot(lane < M && ba.slot[lane] == s);
+                r1 = __ballot(lane + 64 < M && ba.slot[lane + 64] == s);
+            }
+            if ((r0 | r1) == 0) continue;  // an adapter of the pool without rows in the batch
+            decode_shrink_item<RM>(x, A, M, K, c, a, r0 & par, r1 & par, lane, lo.tpart);
         }
+    }
+#define DEC_STEP(SS, XC, WC, XN, WN)                                   \
+    wait_vm<2 * C::PER>();                                             \
+    wait_lgkm0();                                                      \
+    dec_issue<C>(src, XN + xo, WN + wo, KLOAD((SS) + 3), N);           \
+    if ((SS) < nst) dec_mfma<C>(acc, XC + xo, WC + wo, lane);
+    for (int s = 0; s < nst; s += 4) {
+        DEC_STEP(s, XS0, WS0, XS3, WS3)
+        DEC_STEP(s + 1, XS1, WS1, XS0, WS0)
+        DEC_STEP(s + 2, XS2, WS2, XS1, WS1)
+        DEC_STEP(s + 3, XS3, WS3, XS2, WS2)
+    }
 #undef DEC_STEP
 #undef KLOAD
-        wait_vm<0>();
-    } else {
-        // ---- LoRA K-extension -------------------------------------------------------------
-        const int RM = lo.r_max;
-        const int lr = 31 - __clz(RM);  // r_max is a power of two
-        batch_adapters(ba, lo.ids, M, lo.n_adapters);
-        const int T = ba.T;
-        for (int r = tid; r < C::BM; r += kThreads) {
-            const int m = m0 + r;
-            const int sl = m < M ? ba.slot[m] : -1;
-            s_slot[r] = sl;
-            s_scale[r] = sl >= 0 ? lo.scale[ba.id[m]] : 0.0f;
-        }
-        // t of the tile's rows: the shrink's chunk sums added in chunk order
-        for (int cq = tid; cq < C::BM * (RM / 4); cq += kThreads) {
-            const int r = cq / (RM / 4), j = (cq % (RM / 4)) * 4;
-            const int m = m0 + r;
-            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (m < M && ba.slot[m] >= 0) {
-                const float *tp = lo.tpart + (size_t)m * RM + j;
-                const size_t cs = (size_t)M * RM;
-                for (int c0 = 0; c0 < lo.n_chunks; c0 += 8) {  // 8 loads in flight, added in order
-                    float4 u[8];
-#pragma unroll
-                    for (int i = 0; i < 8; ++i)
-                        u[i] = c0 + i < lo.n_chunks ? *reinterpret_cast<const float4 *>(tp + (c0 + i) * cs)
-                                                    : make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        v.x += u[i].x; v.y += u[i].y; v.z += u[i].z; v.w += u[i].w;
-                    }
-                }
-            }
-            *reinterpret_cast<float4 *>(&s_t[r * RM + j]) = v;
-        }
-        __syncthreads();
-        const int ES = (T * RM + kBK - 1) / kBK;  // extension steps
-        const int pe = (ES + kWaves - 1) / kWaves;
-        const int e0 = wave * pe;
-        const int nst = max(0, min(ES, e0 + pe) - e0);
-        // W rows of extension step e: stacked row k = 32 e + r -> (adapter slot s, rank j)
-        auto issue_ext = [&](uint4 *__restrict__ xslot, uint4 *__restrict__ wslot, int step) {
-            const int e = e0 + (nst > 0 ? min(step, nst - 1) : 0);
-#pragma unroll
-            for (int q = 0; q < C::XINS; ++q)  // placeholder x (overwritten before use)
-                __builtin_amdgcn_global_load_lds((const void *)src.xp[q], (lds_void_t *)&xslot[q * 64], 16, 0, 0);
-#pragma unroll
-            for (int q = 0; q < C::WINS; ++q) {
-                const int k = e * kBK + wrow[q];
-                const int sl = k >> lr, j = k & (RM - 1);
-                const int a = sl < T ? ba.list[sl] : 0;
-                const uint16_t *p = lo.B + ((size_t)a * RM + j) * N + wcol[q];
-                __builtin_amdgcn_global_load_lds((const void *)p, (lds_void_t *)&wslot[q * 64], 16, 0, 0);
-            }
-        };
-        // x rows of extension step e: scale_a * t[m, j .. j+7] where the row's adapter is the
-        // step's adapter slot, else zero
-        auto fill_ext = [&](uint4 *__restrict__ xslot, int step) {
-            const int e = e0 + step;
-#pragma unroll
-            for (int i = 0; i < C::BM * 4 / 64; ++i) {
-                const int c = lane + 64 * i;
-                const int row = c >> 2, lc = c & 3;
-                const int k = e * kBK + lc * 8;
-                const int sl = k >> lr, j = k & (RM - 1);
-                uint4 v = make_uint4(0, 0, 0, 0);
-                if (sl < T && s_slot[row] == sl) {
-                    const float sc = s_scale[row];
-                    const float4 t0 = *reinterpret_cast<const float4 *>(&s_t[row * RM + j]);
-                    const float4 t1 = *reinterpret_cast<const float4 *>(&s_t[row * RM + j + 4]);
-                    v = make_uint4(pack_bf16x2(sc * t0.x, sc * t0.y), pack_bf16x2(sc * t0.z, sc * t0.w),
-                                   pack_bf16x2(sc * t1.x, sc * t1.y), pack_bf16x2(sc * t1.z, sc * t1.w));
-                }
-                xslot[row * 4 + (lc ^ ((row >> 2) & 3))] = v;
-            }
-        };
-        issue_ext(XS0 + xo, WS0 + wo, 0);
-        issue_ext(XS1 + xo, WS1 + wo, 1);
-        issue_ext(XS2 + xo, WS2 + wo, 2);
-#define EXT_STEP(SS, XC, WC, XN, WN)                                   \
-        wait_vm<2 * C::PER>();                                         \
-        wait_lgkm0();                                                  \
-        issue_ext(XN + xo, WN + wo, (SS) + 3);                         \
-        if ((SS) < nst) {                                              \
-            fill_ext(XC + xo, (SS));                                   \
-            dec_mfma<C>(acc, XC + xo, WC + wo, lane);                  \
-        }
-        for (int s = 0; s < nst; s += 4) {
-            EXT_STEP(s, XS0, WS0, XS3, WS3)
-            EXT_STEP(s + 1, XS1, WS1, XS0, WS0)
-            EXT_STEP(s + 2, XS2, WS2, XS1, WS1)
-            EXT_STEP(s + 3, XS3, WS3, XS2, WS2)
-        }
-#undef EXT_STEP
-        wait_vm<0>();
-    }
+    wait_vm<0>();
     __syncthreads();
 
     float sum[C::BM / 4];
@@ -337,24 +268,78 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(
     for (int q = 0; q < C::BM / 4; ++q) mine[(wave + 4 * q) * kBN + lane] = sum[q];
 }
 
-// y[m][n] = sum over splits (in order) of the partial tiles; 4 columns per thread.
-template <int BM, bool YF32>
-__global__ __launch_bounds__(256) void reduce_partials_kernel(const float *__restrict__ partial,
-                                                              int M, int N, int n_tm, int n_tn,
-                                                              int n_splits, void *__restrict__ y) {
-    const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
-    const int nq = (N + 3) / 4;
-    if (idx >= (long)M * nq) return;
-    const int m = (int)(idx / nq), n = (int)(idx % nq) * 4;
-    const int tile = (m / BM) + (n / kBN) * n_tm;
-    const int off = (m % BM) * kBN + (n % kBN);
+// y[m, n .. n+3] = (sum over splits, in order, of the partial tiles)
+//                  + scale_a * sum_j t[m, j] B_a[j, n .. n+3]   (a = ids[m], when valid)
+// with t[m, j] = sum over the shrink's chunks, in order, of tpart[c][m][j].  Block (column
+// chunk of 1024, row m), 256 threads x 4 columns.  The partial and B loads are issued
+// before t is summed, so their latency overlaps it.
+template <int BM, int RM, bool YF32>
+__global__ __launch_bounds__(256) void reduce_lora_kernel(const float *__restrict__ partial,
+                                                          int M, int N, int n_tm, int n_tn,
+                                                          int n_splits, DecodeLora lo,
+                                                          void *__restrict__ y) {
+    constexpr int kMaxSplits = 16;
+    __shared__ float s_t[RM];
+    const int m = blockIdx.y;
+    const int n = (blockIdx.x * 256 + threadIdx.x) * 4;
+    const bool col_ok = n < N;
+    const int nc = col_ok ? n : 0;
+    const int id = lo.ids[m];
+    const bool has = id >= 0 && id < lo.n_adapters;
+    const int a = has ? id : 0;
+
+    // split partials of (m, nc .. nc+3)
+    const int tile = (m / BM) + (nc / kBN) * n_tm;
     const size_t stride = (size_t)n_tm * n_tn * BM * kBN;
-    const float *p = partial + (size_t)tile * BM * kBN + off;
-    float4 acc = *reinterpret_cast<const float4 *>(p);
-    for (int sp = 1; sp < n_splits; ++sp) {
-        const float4 v = *reinterpret_cast<const float4 *>(p + sp * stride);
-        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    const float *pp = partial + (size_t)tile * BM * kBN + (m % BM) * kBN + (nc % kBN);
+    float4 pv[kMaxSplits];
+#pragma unroll
+    for (int sp = 0; sp < kMaxSplits; ++sp)
+        if (sp < n_splits) pv[sp] = *reinterpret_cast<const float4 *>(pp + sp * stride);
+    // B_a[j, nc .. nc+3] for every rank row (zero beyond the adapter's rank: padded pool)
+    uint2 bv[RM];
+    const uint16_t *bp = lo.B + (size_t)a * RM * N + nc;
+#pragma unroll
+    for (int j = 0; j < RM; ++j) bv[j] = *reinterpret_cast<const uint2 *>(bp + (size_t)j * N);
+    // t[m, j]: thread j adds the chunks in order, eight loads in flight
+    if (has && threadIdx.x < RM) {
+        const int j = threadIdx.x;
+        const float *tp = lo.tpart + (size_t)m * RM + j;
+        const size_t cs = (size_t)M * RM;
+        float t = 0.0f;
+        for (int c0 = 0; c0 < lo.n_chunks; c0 += 8) {
+            float u[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) u[i] = c0 + i < lo.n_chunks ? tp[(c0 + i) * cs] : 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) t += u[i];
+        }
+        s_t[j] = t;
     }
+    __syncthreads();
+
+    float4 acc = pv[0];
+#pragma unroll
+    for (int sp = 1; sp < kMaxSplits; ++sp) {
+        if (sp < n_splits) {
+            acc.x += pv[sp].x; acc.y += pv[sp].y; acc.z += pv[sp].z; acc.w += pv[sp].w;
+        }
+    }
+    if (has) {
+        float d0 = 0.f, d1 = 0.f, d2 = 0.f, d3 = 0.f;
+#pragma unroll
+        for (int j = 0; j < RM; ++j) {
+            const float tj = s_t[j];
+            d0 = fmaf(tj, bf16_lo(bv[j].x), d0);
+            d1 = fmaf(tj, bf16_hi(bv[j].x), d1);
+            d2 = fmaf(tj, bf16_lo(bv[j].y), d2);
+            d3 = fmaf(tj, bf16_hi(bv[j].y), d3);
+        }
+        const float sc = lo.scale[a];
+        acc.x = fmaf(sc, d0, acc.x); acc.y = fmaf(sc, d1, acc.y);
+        acc.z = fmaf(sc, d2, acc.z); acc.w = fmaf(sc, d3, acc.w);
+    }
+    if (!col_ok) return;
     if constexpr (YF32) {
         *reinterpret_cast<float4 *>(reinterpret_cast<float *>(y) + (size_t)m * N + n) = acc;
     } else {
@@ -364,24 +349,24 @@ __global__ __launch_bounds__(256) void reduce_partials_kernel(const float *__res
 }
 
 struct DecPlan {
-    int bm, n_tm, n_tn, ks_base, k_per_split;
+    int bm, n_tm, n_tn, ks, k_per_split;  // ks splits of K per tile
 };
 
-// ks_base splits of K per tile plus the extension split, aiming at one workgroup per CU.
+// Splits of K per tile so that tiles x splits fills the 256 CUs once (at most 16 splits).
 DecPlan dec_plan(int M, int K, int N) {
     DecPlan p;
     p.bm = M <= 32 ? 32 : 64;
     p.n_tm = (M + p.bm - 1) / p.bm;
     p.n_tn = (N + kBN - 1) / kBN;
     const long tiles = (long)p.n_tm * p.n_tn;
-    const int kq = K / (kBK * kWaves);  // whole 128-deep quanta
-    int ks = (int)(256 / tiles) - 1;
+    const int kq = K / (kBK * kWaves);  // whole 128-deep quanta (K >= 128)
+    int ks = (int)(256 / tiles);
     if (ks < 1) ks = 1;
-    if (ks > kq) ks = kq > 0 ? kq : 1;
+    if (ks > kq) ks = kq;
     if (ks > 16) ks = 16;
     const int q_per = (kq + ks - 1) / ks;
-    p.k_per_split = (q_per > 0 ? q_per : 1) * kBK * kWaves;
-    p.ks_base = (K + p.k_per_split - 1) / p.k_per_split;
+    p.k_per_split = q_per * kBK * kWaves;
+    p.ks = (K + p.k_per_split - 1) / p.k_per_split;
     return p;
 }
 
@@ -394,39 +379,65 @@ bool decode_gemm_supported(int M, int K, int N) {
 size_t decode_gemm_partial_floats(int M, int K, int N) {
     if (!decode_gemm_supported(M, K, N)) return 0;
     const DecPlan p = dec_plan(M, K, N);
-    return (size_t)(p.ks_base + 1) * p.n_tm * p.n_tn * p.bm * kBN;
+    return (size_t)p.ks * p.n_tm * p.n_tn * p.bm * kBN;
 }
 
-hipError_t launch_decode_gemm(const uint16_t *x, const uint16_t *W, int M, int K, int N, void *y,
-                              bool y_f32, const DecodeLora &lo, float *partial, hipStream_t s) {
-    if (!decode_gemm_supported(M, K, N) || partial == nullptr || lo.tpart == nullptr)
+int decode_shrink_chunks(int K, int r_max) {
+    const int kc = decode_shrink_chunk_k(r_max);
+    return (K + kc - 1) / kc;
+}
+
+hipError_t launch_decode_gemm(const uint16_t *x, const uint16_t *W, const uint16_t *A, int M,
+                              int K, int N, const DecodeLora &lo, float *partial, hipStream_t s) {
+    if (!decode_gemm_supported(M, K, N) || partial == nullptr || lo.tpart == nullptr ||
+        lo.n_chunks != decode_shrink_chunks(K, lo.r_max))
         return hipErrorInvalidValue;
     const DecPlan p = dec_plan(M, K, N);
-    const int n_tiles = p.n_tm * p.n_tn;
-    const dim3 grid(n_tiles * (p.ks_base + 1));
-    if (p.bm == 32)
-        launch((decode_gemm_kernel<Dec<32>>), grid, dim3(kThreads), 0, s, x, W, M, K, N,
-                           p.n_tm, p.n_tn, p.ks_base, p.k_per_split, partial, lo);
-    else
-        launch((decode_gemm_kernel<Dec<64>>), grid, dim3(kThreads), 0, s, x, W, M, K, N,
-                           p.n_tm, p.n_tn, p.ks_base, p.k_per_split, partial, lo);
+    const dim3 grid(p.n_tm * p.n_tn * p.ks);
+#define GEMM_LAUNCH(BM, RMX)                                                                  \
+    launch((decode_gemm_kernel<Dec<BM>, RMX>), grid, dim3(kThreads), 0, s, x, W, A, M, K, N,   \
+           p.n_tm, p.n_tn, p.k_per_split, partial, lo)
+#define GEMM_RANK(BM)                                                                         \
+    switch (lo.r_max) {                                                                       \
+        case 8: GEMM_LAUNCH(BM, 8); break;                                                    \
+        case 16: GEMM_LAUNCH(BM, 16); break;                                                  \
+        case 32: GEMM_LAUNCH(BM, 32); break;                                                  \
+        case 64: GEMM_LAUNCH(BM, 64); break;                                                  \
+        default: return hipErrorInvalidValue;                                                 \
+    }
+    if (p.bm == 32) {
+        GEMM_RANK(32)
+    } else {
+        GEMM_RANK(64)
+    }
+#undef GEMM_RANK
+#undef GEMM_LAUNCH
     return hipGetLastError();
 }
 
 hipError_t launch_decode_reduce(const float *partial, int M, int K, int N, void *y, bool y_f32,
-                                hipStream_t s) {
-    if (!decode_gemm_supported(M, K, N) || partial == nullptr) return hipErrorInvalidValue;
+                                const DecodeLora &lo, hipStream_t s) {
+    if (!decode_gemm_supported(M, K, N) || partial == nullptr || lo.tpart == nullptr ||
+        (lo.r_max != 8 && lo.r_max != 16 && lo.r_max != 32 && lo.r_max != 64))
+        return hipErrorInvalidValue;
     const DecPlan p = dec_plan(M, K, N);
-    const long threads = (long)M * ((N + 3) / 4);
-    const dim3 rgrid((unsigned)((threads + 255) / 256));
-#define RED_LAUNCH(BM, YF)                                                                     \
-    launch((reduce_partials_kernel<BM, YF>), rgrid, dim3(256), 0, s, partial, M, N, \
-                       p.n_tm, p.n_tn, p.ks_base + 1, y)
-    if (p.bm == 32) {
-        if (y_f32) RED_LAUNCH(32, true); else RED_LAUNCH(32, false);
-    } else {
-        if (y_f32) RED_LAUNCH(64, true); else RED_LAUNCH(64, false);
+    const dim3 rgrid((unsigned)((N + 1023) / 1024), (unsigned)M);
+#define RED_LAUNCH(BM, RMX, YF)                                                             \
+    launch((reduce_lora_kernel<BM, RMX, YF>), rgrid, dim3(256), 0, s, partial, M, N, p.n_tm,    \
+           p.n_tn, p.ks, lo, y)
+#define RED_RANK(BM, YF)                                                                    \
+    switch (lo.r_max) {                                                                     \
+        case 8: RED_LAUNCH(BM, 8, YF); break;                                               \
+        case 16: RED_LAUNCH(BM, 16, YF); break;                                             \
+        case 32: RED_LAUNCH(BM, 32, YF); break;                                             \
+        default: RED_LAUNCH(BM, 64, YF); break;                                             \
     }
+    if (p.bm == 32) {
+        if (y_f32) { RED_RANK(32, true) } else { RED_RANK(32, false) }
+    } else {
+        if (y_f32) { RED_RANK(64, true) } else { RED_RANK(64, false) }
+    }
+#undef RED_RANK
 #undef RED_LAUNCH
     return hipGetLastError();
 }

@@ -1,5 +1,5 @@
-// decode_shrink.hip -- t = x A_i for a small (decode) batch in one launch, without a
-// separate segment-building kernel.
+// decode_shrink.h -- the shrink t = x A_i of a small (decode) batch, as work items that the
+// decode GEMM's workgroups run before their K loop (no launch of its own).
 //
 // Source: the adapter "shrink" of "Multi-LoRA Serving: Sharing One GPU Across Adapters"
 // (cloudai.pt), "MoE Models Raise the Bar" (split-K for these skinny products); the
@@ -7,44 +7,40 @@
 // (dev.to), "How does one batch run 30 different adapters at once?", bound by reading the
 // adapter weights.
 //
-// Workgroup (k-chunk c, adapter slot s): the workgroup groups the batch's rows by adapter in
-// LDS (batch_adapters.h), takes the s-th distinct adapter a, holds A_a[chunk, 0:r_max] in
-// registers (each lane one k-slice x 8 rank columns, 16-byte loads; all r_max columns, the
-// pool's padding being zero) and multiplies every row of adapter a with it: 8 fp32 sums per
-// lane, then an xor butterfly across the k-slices.  So each touched A_a is read from HBM
+// Work item (k-chunk c, adapter a), taken by a pair of waves: the pair holds
+// A_a[chunk, 0:r_max] in registers (each lane one k-slice x 8 rank columns, 16-byte loads;
+// all r_max columns, the pool's padding being zero) and multiplies every row of adapter a
+// with it -- each wave takes the rows of one parity, given as ballot masks over rows 0..63
+// and 64..127 -- with 8 fp32 sums per lane and an xor butterfly across the k-slices.  The
+// caller names the adapters either directly (item = (chunk, adapter id), rows found by a
+// ballot over ids) or through the batch's distinct adapters grouped in LDS
+// (batch_adapters.h).  So each touched A_a is read from HBM
 // exactly once per batch and untouched adapters cost nothing.  The chunk sums go to
 // tpart[c][m][0:r_max] (rows without an adapter are not written); the consumer adds the
 // chunks in ascending order.
+#pragma once
+
 #include "batch_adapters.h"
 
 namespace lora {
 
-namespace {
-
-constexpr int kThreads = 128;  // 2 waves; >= kDecodeMaxRows for the grouping
-
 template <int RM>
-struct ShrinkCfg {
+struct DecodeShrinkCfg {
     static constexpr int KC = RM == 64 ? 128 : 256;  // k per chunk
     static constexpr int JG = RM / 8;                // 8-column groups per lane row
     static constexpr int KSUB = 64 / JG;             // k-slices across the lanes of a wave
     static constexpr int SL = KC / KSUB;             // k per slice (4, 8, 16 or 16)
+    static constexpr int XV = SL >= 8 ? SL / 8 : 1;  // 16-byte x loads per row and lane
 };
 
-template <int RM>
-__global__ __launch_bounds__(kThreads) void decode_shrink_kernel(
-    const uint16_t *__restrict__ x, const uint16_t *__restrict__ A, const int32_t *__restrict__ ids,
-    const int32_t *__restrict__ ranks, int M, int K, int n_adapters, int n_chunks,
-    float *__restrict__ tpart) {
-    using C = ShrinkCfg<RM>;
-    __shared__ BatchAdapters ba;
-    const int c = blockIdx.x % n_chunks, s = blockIdx.x / n_chunks;
-    batch_adapters(ba, ids, M, n_adapters);
-    if (s >= ba.T) return;  // uniform across the workgroup
-    const int a = ba.list[s];
-    (void)ranks;  // all r_max columns are read: the pool's padded columns are zero
+inline int decode_shrink_chunk_k(int r_max) { return r_max == 64 ? 128 : 256; }
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+template <int RM>
+__device__ __forceinline__ void decode_shrink_item(const uint16_t *__restrict__ x,
+                                                   const uint16_t *__restrict__ A, int M, int K,
+                                                   int c, int a, uint64_t mk0, uint64_t mk1,
+                                                   int lane, float *__restrict__ tpart) {
+    using C = DecodeShrinkCfg<RM>;
     const int ks = lane % C::KSUB, g = lane / C::KSUB;
     const int k0 = c * C::KC + ks * C::SL;
 
@@ -56,10 +52,8 @@ __global__ __launch_bounds__(kThreads) void decode_shrink_kernel(
 #pragma unroll
     for (int kk = 0; kk < C::SL; ++kk) araw[kk] = ld16(k0 + kk < K ? Ap + (size_t)kk * RM : Alast);
 
-    // rows of adapter a with row parity == wave, from a ballot mask; the next row's x is
-    // loaded while the current one is multiplied
-    uint64_t mk0 = __ballot(lane < M && ba.slot[lane] == s && (lane & 1) == wave);
-    uint64_t mk1 = __ballot(lane + 64 < M && ba.slot[lane + 64] == s && (lane & 1) == wave);
+    // this wave's rows (mk0: rows 0..63, mk1: rows 64..127); the next row's x is loaded while
+    // the current one is multiplied
     auto next_row = [&]() -> int {
         if (mk0) {
             const int b = __ffsll((unsigned long long)mk0) - 1;
@@ -73,31 +67,30 @@ __global__ __launch_bounds__(kThreads) void decode_shrink_kernel(
         }
         return -1;
     };
-    constexpr int XV = C::SL >= 8 ? C::SL / 8 : 1;  // 16-byte x loads per row and lane
     // x[m][k0 ..]: unconditional loads from in-bounds addresses (row 0 for no row, the last
     // k for k beyond K); the terms beyond K are dropped in the sums
-    auto load_x = [&](int m, uint4 (&xv)[XV]) {
+    auto load_x = [&](int m, uint4 (&xv)[C::XV]) {
         const uint16_t *xr = x + (size_t)(m < 0 ? 0 : m) * K;
         if constexpr (C::SL >= 8) {
 #pragma unroll
-            for (int v = 0; v < XV; ++v) xv[v] = ld16(xr + min(k0 + 8 * v, K - 8));
+            for (int v = 0; v < C::XV; ++v) xv[v] = ld16(xr + min(k0 + 8 * v, K - 8));
         } else {  // 4 k per slice: one 8-byte load
             const uint2 h = *reinterpret_cast<const uint2 *>(xr + min(k0, K - 4));
             xv[0] = make_uint4(h.x, h.y, 0, 0);
         }
     };
     int m = next_row();
-    uint4 xc[XV];
+    uint4 xc[C::XV];
     load_x(m, xc);
     while (m >= 0) {
         const int mn = next_row();
-        uint4 xn[XV];
+        uint4 xn[C::XV];
         load_x(mn, xn);
         float acc[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
 #pragma unroll
-        for (int v = 0; v < XV; ++v) {
+        for (int v = 0; v < C::XV; ++v) {
             float xf[8];
             unpack8(xc[v], xf);
 #pragma unroll
@@ -122,41 +115,8 @@ __global__ __launch_bounds__(kThreads) void decode_shrink_kernel(
         }
         m = mn;
 #pragma unroll
-        for (int v = 0; v < XV; ++v) xc[v] = xn[v];
+        for (int v = 0; v < C::XV; ++v) xc[v] = xn[v];
     }
-}
-
-}  // namespace
-
-int decode_shrink_chunks(int K, int r_max) {
-    const int kc = r_max == 64 ? 128 : 256;
-    return (K + kc - 1) / kc;
-}
-
-hipError_t launch_decode_shrink(const uint16_t *x, const uint16_t *A, const int32_t *ids,
-                                const int32_t *ranks, int M, int K, int r_max, int n_adapters,
-                                float *tpart, hipStream_t s) {
-    if (M < 1 || M > kDecodeMaxRows) return hipErrorInvalidValue;
-    const int n_chunks = decode_shrink_chunks(K, r_max);
-    const int slots = M < n_adapters ? M : n_adapters;
-    const dim3 grid(n_chunks * slots);
-    switch (r_max) {
-        case 8:
-            launch(decode_shrink_kernel<8>, grid, dim3(kThreads), 0, s, x, A, ids, ranks, M, K, n_adapters, n_chunks, tpart);
-            break;
-        case 16:
-            launch(decode_shrink_kernel<16>, grid, dim3(kThreads), 0, s, x, A, ids, ranks, M, K, n_adapters, n_chunks, tpart);
-            break;
-        case 32:
-            launch(decode_shrink_kernel<32>, grid, dim3(kThreads), 0, s, x, A, ids, ranks, M, K, n_adapters, n_chunks, tpart);
-            break;
-        case 64:
-            launch(decode_shrink_kernel<64>, grid, dim3(kThreads), 0, s, x, A, ids, ranks, M, K, n_adapters, n_chunks, tpart);
-            break;
-        default:
-            return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
 }
 
 }  // namespace lora

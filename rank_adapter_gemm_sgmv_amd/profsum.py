@@ -25,9 +25,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 
 # kernel function name -> name of the step in lora_linear_profiled / bench.py
 _STEP_OF_KERNEL = [
-    ("decode_shrink_kernel", "decode_shrink"),
-    ("decode_gemm_kernel", "decode_gemm_lora"),
-    ("reduce_partials_kernel", "decode_reduce"),
+    ("decode_gemm_kernel", "decode_gemm_shrink"),
+    ("reduce_lora_kernel", "decode_reduce_lora"),
     ("build_segments_kernel", "build_segments"),
     ("shrink_finalize_kernel", "shrink_finalize"),
     ("shrink_lds_kernel", "shrink"),

@@ -122,12 +122,17 @@ RANDOM = [
     (9, 1500, 256, 512, 5, 16, 0.1, DECODE),
     (10, 64, 4096, 128, 9, 64, 1.0, DECODE),   # every row base-only
     (11, 640, 2048, 256, 200, 32, 0.0, PREFILL),  # many short runs inside prefill tiles
-    # fused decode GEMM (M <= 128, d_in % 32 == 0): tile / split-K / ragged-column variety
+    # small-batch decode path (M <= 128, d_in % 32 == 0): tile / split-K / ragged-column
+    # variety; pools no larger than the batch name adapters directly
     (15, 64, 1024, 520, 9, 16, 0.2, DECODE),
     (16, 128, 2048, 264, 40, 32, 0.1, DECODE),
     (17, 33, 4096, 4104, 5, 64, 0.3, DECODE),
     (18, 2, 128, 64, 3, 8, 0.0, DECODE),
     (19, 97, 11008, 136, 17, 16, 0.25, DECODE),
+    # pools larger than the batch: the shrink finds the batch's adapters by grouping in LDS
+    (20, 100, 2048, 1000, 300, 16, 0.1, DECODE),
+    (21, 128, 512, 256, 1024, 64, 0.0, DECODE),
+    (22, 64, 512, 136, 65, 8, 0.5, DECODE),
 ]
 
 
