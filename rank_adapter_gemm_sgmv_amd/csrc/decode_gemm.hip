@@ -18,11 +18,10 @@
 //    Three stages (24 KiB per wave) are in flight.
 //  * x tile [BM][32] and W tile [32][64] per stage, XOR-swizzled; the W operand is read with
 //    the transposing LDS read (ds_read_b64_tr_b16); v_mfma_f32_32x32x16_bf16.
-//  * x W does not depend on the LoRA shrink, so the same workgroups also run it: after
-//    grouping the batch's rows by adapter in LDS and issuing the first ring stages, each
-//    pair of waves takes its share of the shrink's work items (decode_shrink.h), whose
-//    loads overlap those stages, and then streams its K range.  The shrink costs no launch
-//    of its own.
+//  * x W does not depend on the LoRA shrink, so the same workgroups also run it: each has
+//    four more waves that take the shrink's work items (decode_shrink.h) side by side with
+//    the four streaming W, on the same CU (which holds one such workgroup: its LDS ring is
+//    128 KiB).  The shrink costs no launch and, mostly, no time of its own.
 //  * The four waves' partial tiles are added through LDS in wave order and each workgroup
 //    writes its partial tile.
 //  * reduce_lora_kernel then writes y[m, :] = (sum of the split partials, in split order)
@@ -45,8 +44,9 @@ typedef __attribute__((address_space(3))) char lds_char_t;
 
 constexpr int kBN = 64;
 constexpr int kBK = 32;
-constexpr int kWaves = 4;
+constexpr int kWaves = 4;                // waves streaming x W
 constexpr int kThreads = 64 * kWaves;
+constexpr int kBlock = 2 * kThreads;      // plus as many running the shrink beside them
 
 template <int BM_>
 struct Dec {
@@ -125,20 +125,22 @@ __device__ __forceinline__ void dec_issue(const DecSrc<C> &src, uint4 *__restric
 }
 
 // Cross-wave reduction: each wave's accumulators go to LDS (accumulator layout, lane-minor)
-// and are added in wave order into row-major elements; thread tid owns rows tid/64 + 4q
-// and column tid % 64.
+// and, after a barrier, are added in wave order into row-major elements; thread tid owns
+// rows tid/64 + 4q and column tid % 64.
 template <class C>
-__device__ __forceinline__ void reduce_waves(const f32x16_t (&acc)[C::TM][C::TN], float *red_mine,
-                                             const float *r0, const float *r1, const float *r2,
-                                             const float *r3, int lane, int wave,
-                                             float (&sum)[C::BM / 4]) {
+__device__ __forceinline__ void reduce_waves_put(const f32x16_t (&acc)[C::TM][C::TN], float *red_mine,
+                                                 int lane) {
 #pragma unroll
     for (int i = 0; i < C::TM; ++i)
 #pragma unroll
         for (int j = 0; j < C::TN; ++j)
 #pragma unroll
             for (int v = 0; v < 16; ++v) red_mine[((i * C::TN + j) * 16 + v) * 64 + lane] = acc[i][j][v];
-    __syncthreads();
+}
+template <class C>
+__device__ __forceinline__ void reduce_waves_sum(const float *r0, const float *r1, const float *r2,
+                                                 const float *r3, int lane, int wave,
+                                                 float (&sum)[C::BM / 4]) {
 #pragma unroll
     for (int q = 0; q < C::BM / 4; ++q) {
         const int r = wave + 4 * q, c = lane;
@@ -148,15 +150,17 @@ __device__ __forceinline__ void reduce_waves(const f32x16_t (&acc)[C::TM][C::TN]
     }
 }
 
-// Workgroup (tile, split): split `split` covers K rows [split k_per_split, +k_per_split) and
-// writes its partial tile; reduce_lora_kernel adds the splits in order.  Before its K loop
-// the workgroup runs shrink work items blockIdx.x * 2 + wave / 2, stepping by 2 gridDim.x.
+// Workgroup (tile, split), eight waves.  Waves 0-3 stream split `split` of K (rows
+// [split k_per_split, +k_per_split)) and write its partial tile; reduce_lora_kernel adds the
+// splits in order.  Waves 4-7, side by side on the same CU, run the shrink's work items
+// blockIdx.x * 2 + (wave - 4) / 2, stepping by 2 gridDim.x (a pair per item, rows of parity
+// wave % 2).
 template <class C, int RM>
-__global__ __launch_bounds__(kThreads) void decode_gemm_kernel(
+__global__ __launch_bounds__(kBlock) void decode_gemm_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ W, const uint16_t *__restrict__ A,
     int M, int K, int N, int n_tm, int n_tn, int k_per_split, float *__restrict__ partial,
     DecodeLora lo) {
-    // stage s of wave w: X{s}[w * XSLOT ..], W{s}[w * WSLOT ..]
+    // stage s of GEMM wave w: X{s}[w * XSLOT ..], W{s}[w * WSLOT ..]
     __shared__ __attribute__((aligned(1024))) uint4 XS0[kWaves * C::XSLOT];
     __shared__ __attribute__((aligned(1024))) uint4 XS1[kWaves * C::XSLOT];
     __shared__ __attribute__((aligned(1024))) uint4 XS2[kWaves * C::XSLOT];
@@ -167,37 +171,15 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(
     __shared__ __attribute__((aligned(1024))) uint4 WS3[kWaves * C::WSLOT];
     __shared__ BatchAdapters ba;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n_tiles = n_tm * n_tn;
+    // block -> (tile, split): the splits of one tile are n_tiles apart
+    const int tile = blockIdx.x % n_tiles, split = blockIdx.x / n_tiles;
     // shrink items name adapters directly when the pool is no larger than the batch (rows
     // found by a ballot over ids), else through the batch's distinct adapters in LDS
     const bool by_id = lo.n_adapters <= M;
-    int id0 = -1, id1 = -1;
-    if (by_id) {
-        id0 = lane < M ? lo.ids[lane] : -1;
-        id1 = lane + 64 < M ? lo.ids[lane + 64] : -1;
-    } else {
-        batch_adapters(ba, lo.ids, M, lo.n_adapters);
-    }
-    // block -> (tile, split): the splits of one tile are n_tiles apart
-    const int tile = blockIdx.x % n_tiles, split = blockIdx.x / n_tiles;
-    const int tm = tile % n_tm, tn = tile / n_tm;
-    const int m0 = tm * C::BM, n0 = tn * kBN;
-
-    DecSrc<C> src;
-#pragma unroll
-    for (int q = 0; q < C::XINS; ++q) {
-        const int row = 16 * q + (lane >> 2);
-        const int lc = (lane & 3) ^ ((lane >> 4) & 3);
-        const int m = min(m0 + row, M - 1);
-        src.xp[q] = x + (size_t)m * K + lc * 8;
-    }
-#pragma unroll
-    for (int q = 0; q < C::WINS; ++q) {
-        const int r = 8 * q + (lane >> 3);
-        const int lc = (lane & 7) ^ wsw(r);
-        src.wp[q] = W + (size_t)r * N + min(n0 + lc * 8, N - 8);
-    }
+    if (!by_id) batch_adapters(ba, lo.ids, M, lo.n_adapters);  // every thread: barriers
 
     f32x16_t acc[C::TM][C::TN];
 #pragma unroll
@@ -206,26 +188,62 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(
         for (int j = 0; j < C::TN; ++j)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-    const int xo = wave * C::XSLOT, wo = wave * C::WSLOT;
 
-    // this wave's part of the split's K range
-    const int ks0 = split * k_per_split;
-    const int ks1 = min(K, ks0 + k_per_split);
-    const int per_wave = k_per_split / kWaves;  // multiple of 32
-    const int kw0 = min(ks1, ks0 + wave * per_wave);
-    const int kw1 = min(ks1, kw0 + per_wave);
-    const int nst = (kw1 - kw0) / kBK;
-    // k of stage s (stages past the last reload the last one; an empty range loads k=0)
+    if (wave < kWaves) {
+        // ---- x W over this wave's part of the split's K range ------------------------------
+        const int tm = tile % n_tm, tn = tile / n_tm;
+        const int m0 = tm * C::BM, n0 = tn * kBN;
+        DecSrc<C> src;
+#pragma unroll
+        for (int q = 0; q < C::XINS; ++q) {
+            const int row = 16 * q + (lane >> 2);
+            const int lc = (lane & 3) ^ ((lane >> 4) & 3);
+            const int m = min(m0 + row, M - 1);
+            src.xp[q] = x + (size_t)m * K + lc * 8;
+        }
+#pragma unroll
+        for (int q = 0; q < C::WINS; ++q) {
+            const int r = 8 * q + (lane >> 3);
+            const int lc = (lane & 7) ^ wsw(r);
+            src.wp[q] = W + (size_t)r * N + min(n0 + lc * 8, N - 8);
+        }
+        const int xo = wave * C::XSLOT, wo = wave * C::WSLOT;
+        const int ks0 = split * k_per_split;
+        const int ks1 = min(K, ks0 + k_per_split);
+        const int per_wave = k_per_split / kWaves;  // multiple of 32
+        const int kw0 = min(ks1, ks0 + wave * per_wave);
+        const int kw1 = min(ks1, kw0 + per_wave);
+        const int nst = (kw1 - kw0) / kBK;
+        // k of stage s (stages past the last reload the last one; an empty range loads k=0)
 #define KLOAD(S) (nst > 0 ? kw0 + min((S), nst - 1) * kBK : 0)
-    dec_issue<C>(src, XS0 + xo, WS0 + wo, KLOAD(0), N);
-    dec_issue<C>(src, XS1 + xo, WS1 + wo, KLOAD(1), N);
-    dec_issue<C>(src, XS2 + xo, WS2 + wo, KLOAD(2), N);
-    // the shrink's work items, while the first stages load: wave pair wave / 2, rows of
-    // parity wave % 2
-    {
+        dec_issue<C>(src, XS0 + xo, WS0 + wo, KLOAD(0), N);
+        dec_issue<C>(src, XS1 + xo, WS1 + wo, KLOAD(1), N);
+        dec_issue<C>(src, XS2 + xo, WS2 + wo, KLOAD(2), N);
+#define DEC_STEP(SS, XC, WC, XN, WN)                                   \
+        wait_vm<2 * C::PER>();                                         \
+        wait_lgkm0();                                                  \
+        dec_issue<C>(src, XN + xo, WN + wo, KLOAD((SS) + 3), N);       \
+        if ((SS) < nst) dec_mfma<C>(acc, XC + xo, WC + wo, lane);
+        for (int s = 0; s < nst; s += 4) {
+            DEC_STEP(s, XS0, WS0, XS3, WS3)
+            DEC_STEP(s + 1, XS1, WS1, XS0, WS0)
+            DEC_STEP(s + 2, XS2, WS2, XS1, WS1)
+            DEC_STEP(s + 3, XS3, WS3, XS2, WS2)
+        }
+#undef DEC_STEP
+#undef KLOAD
+        wait_vm<0>();
+    } else {
+        // ---- the shrink's work items ---------------------------------------------------------
+        const int pair = (wave - kWaves) >> 1;
+        int id0 = -1, id1 = -1;
+        if (by_id) {
+            id0 = lane < M ? lo.ids[lane] : -1;
+            id1 = lane + 64 < M ? lo.ids[lane + 64] : -1;
+        }
         const uint64_t par = (wave & 1) ? 0xAAAAAAAAAAAAAAAAull : 0x5555555555555555ull;
         const int n_items = lo.n_chunks * (by_id ? lo.n_adapters : ba.T);
-        for (int w = blockIdx.x * 2 + (wave >> 1); w < n_items; w += gridDim.x * 2) {
+        for (int w = blockIdx.x * 2 + pair; w < n_items; w += gridDim.x * 2) {
             const int c = w % lo.n_chunks, s = w / lo.n_chunks;
             int a;
             uint64_t r0, r1;
@@ -242,30 +260,20 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(
             decode_shrink_item<RM>(x, A, M, K, c, a, r0 & par, r1 & par, lane, lo.tpart);
         }
     }
-#define DEC_STEP(SS, XC, WC, XN, WN)                                   \
-    wait_vm<2 * C::PER>();                                             \
-    wait_lgkm0();                                                      \
-    dec_issue<C>(src, XN + xo, WN + wo, KLOAD((SS) + 3), N);           \
-    if ((SS) < nst) dec_mfma<C>(acc, XC + xo, WC + wo, lane);
-    for (int s = 0; s < nst; s += 4) {
-        DEC_STEP(s, XS0, WS0, XS3, WS3)
-        DEC_STEP(s + 1, XS1, WS1, XS0, WS0)
-        DEC_STEP(s + 2, XS2, WS2, XS1, WS1)
-        DEC_STEP(s + 3, XS3, WS3, XS2, WS2)
-    }
-#undef DEC_STEP
-#undef KLOAD
-    wait_vm<0>();
-    __syncthreads();
+    __syncthreads();  // every GEMM wave is done with the W stages
 
-    float sum[C::BM / 4];
     float *red = reinterpret_cast<float *>(wave == 0 ? WS0 : wave == 1 ? WS1 : wave == 2 ? WS2 : WS3);
-    reduce_waves<C>(acc, red, reinterpret_cast<const float *>(WS0), reinterpret_cast<const float *>(WS1),
-                    reinterpret_cast<const float *>(WS2), reinterpret_cast<const float *>(WS3), lane,
-                    wave, sum);
-    float *mine = partial + ((size_t)split * n_tiles + tile) * C::TILE;
+    if (wave < kWaves) reduce_waves_put<C>(acc, red, lane);
+    __syncthreads();
+    if (wave < kWaves) {
+        float sum[C::BM / 4];
+        reduce_waves_sum<C>(reinterpret_cast<const float *>(WS0), reinterpret_cast<const float *>(WS1),
+                            reinterpret_cast<const float *>(WS2), reinterpret_cast<const float *>(WS3),
+                            lane, wave, sum);
+        float *mine = partial + ((size_t)split * n_tiles + tile) * C::TILE;
 #pragma unroll
-    for (int q = 0; q < C::BM / 4; ++q) mine[(wave + 4 * q) * kBN + lane] = sum[q];
+        for (int q = 0; q < C::BM / 4; ++q) mine[(wave + 4 * q) * kBN + lane] = sum[q];
+    }
 }
 
 // y[m, n .. n+3] = (sum over splits, in order, of the partial tiles)
@@ -395,7 +403,7 @@ hipError_t launch_decode_gemm(const uint16_t *x, const uint16_t *W, const uint16
     const DecPlan p = dec_plan(M, K, N);
     const dim3 grid(p.n_tm * p.n_tn * p.ks);
 #define GEMM_LAUNCH(BM, RMX)                                                                  \
-    launch((decode_gemm_kernel<Dec<BM>, RMX>), grid, dim3(kThreads), 0, s, x, W, A, M, K, N,   \
+    launch((decode_gemm_kernel<Dec<BM>, RMX>), grid, dim3(kBlock), 0, s, x, W, A, M, K, N,     \
            p.n_tm, p.n_tn, p.k_per_split, partial, lo)
 #define GEMM_RANK(BM)                                                                         \
     switch (lo.r_max) {                                                                       \
