@@ -7,8 +7,11 @@
 // delta is small next to x W).
 //
 // gfx950 design
-//  * Tile BM x BN (256 x 256, 256 x 128 or 128 x 128), four waves in a 2 x 2 grid, each wave
-//    owning (BM/2) x (BN/2) of the output as 32 x 32 v_mfma_f32_32x32x16_bf16 accumulators.
+//  * Tile BM x BN (256 x 256, 256 x 128 or 128 x 128).  256 x 256 tiles use eight waves in a
+//    2 x 4 grid (each owns 128 x 64 of the output: 128 accumulator registers, so two waves
+//    share a SIMD and one issues MFMAs while the other waits on LDS or the barrier); the
+//    smaller tiles use four waves in a 2 x 2 grid.  Accumulators are 32 x 32
+//    v_mfma_f32_32x32x16_bf16 blocks.
 //  * K is consumed 32 at a time through a 4-stage LDS ring filled by direct global->LDS
 //    loads (global_load_lds_dwordx4): no staging registers, three stages in flight while one
 //    is multiplied.  Each stage slot is its own __shared__ array, named statically and
@@ -42,23 +45,27 @@ typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
 typedef __attribute__((address_space(3))) char lds_char_t;
 
 constexpr int kBK = 32;     // k per stage
-constexpr int kThreads = 256;
 
-template <int BM_, int BN_>
+// Tile BM x BN computed by WM x WN waves, each owning (BM / WM) x (BN / WN).
+template <int BM_, int BN_, int WM_ = 2, int WN_ = 2>
 struct Big {
-    static constexpr int BM = BM_, BN = BN_;
-    static constexpr int WTM = BM / 2, WTN = BN / 2;  // per-wave tile
+    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+    static constexpr int NW = WM * WN, NT = 64 * NW;  // waves, threads
+    static constexpr int WTM = BM / WM, WTN = BN / WN;  // per-wave tile
     static constexpr int TM = WTM / 32, TN = WTN / 32;
     static constexpr int XSLOT = BM * kBK * 2 / 16;  // uint4 per x slot
     static constexpr int WSLOT = kBK * BN * 2 / 16;  // uint4 per W slot
-    static constexpr int XINS = XSLOT / 64 / 4;      // DMA instructions per wave per stage
-    static constexpr int WINS = WSLOT / 64 / 4;
+    static constexpr int XINS = XSLOT / 64 / NW;     // DMA instructions per wave per stage
+    static constexpr int WINS = WSLOT / 64 / NW;
     static constexpr int PER = XINS + WINS;
     static constexpr int WROWS = 1024 / (BN * 2);     // W rows per DMA instruction
     static constexpr int WCH = BN / 8;                // 16-byte chunks per W row
     static_assert(BN == 128 || BN == 256, "W swizzle needs at least 16 chunks per row");
     static_assert(BM == 128 || BM == 256, "x tile");
     static_assert(XINS >= 1 && WINS >= 1, "per-wave DMA split");
+    static_assert(XINS * 64 * NW == XSLOT && WINS * 64 * NW == WSLOT, "whole DMA instructions");
+    static_assert(NW == 4 || NW == 8, "four or eight waves (staging slots)");
+    static_assert(TM >= 1 && TN >= 1, "per-wave tile of whole 32 x 32 blocks");
 };
 
 // s_waitcnt with only vmcnt = n (n < 64); expcnt and lgkmcnt left at their maxima.
@@ -196,7 +203,7 @@ template <class C, bool SEGROWS>
 __device__ __forceinline__ void fill_stage(uint4 *xs, uint4 *ws, const uint16_t *__restrict__ x,
                                           const uint16_t *__restrict__ W, int M, int K, int N,
                                           int row0, int n0, int k0, const int32_t *perm, int tid) {
-    for (int c = tid; c < C::BM * 4; c += kThreads) {
+    for (int c = tid; c < C::BM * 4; c += C::NT) {
         const int row = c >> 2, lc = c & 3;
         const int rr = row0 + row;
         uint4 v = make_uint4(0, 0, 0, 0);
@@ -207,7 +214,7 @@ __device__ __forceinline__ void fill_stage(uint4 *xs, uint4 *ws, const uint16_t 
         }
         xs[row * 4 + (lc ^ ((row >> 2) & 3))] = v;
     }
-    for (int c = tid; c < kBK * C::WCH; c += kThreads) {
+    for (int c = tid; c < kBK * C::WCH; c += C::NT) {
         const int r = c / C::WCH, lc = c % C::WCH;
         const int n = n0 + lc * 8;
         uint4 v = make_uint4(0, 0, 0, 0);
@@ -217,7 +224,7 @@ __device__ __forceinline__ void fill_stage(uint4 *xs, uint4 *ws, const uint16_t 
 }
 
 template <class C, bool SEGROWS, bool LORA, bool YF32>
-__global__ __launch_bounds__(kThreads) void gemm_big_kernel(const uint16_t *__restrict__ x,
+__global__ __launch_bounds__(C::NT) void gemm_big_kernel(const uint16_t *__restrict__ x,
                                                             const uint16_t *__restrict__ W,
                                                             int M, int K, int N,
                                                             void *__restrict__ y, int n_tm,
@@ -232,7 +239,7 @@ __global__ __launch_bounds__(kThreads) void gemm_big_kernel(const uint16_t *__re
     __shared__ __attribute__((aligned(1024))) uint4 W3[C::WSLOT];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm0 = (wave >> 1) * C::WTM, wn0 = (wave & 1) * C::WTN;
+    const int wm0 = (wave / C::WN) * C::WTM, wn0 = (wave % C::WN) * C::WTN;
     int tmi, tni;
     tile_of(blockIdx.x, n_tm, n_tn, tmi, tni);
     const int row0 = tmi * C::BM, n0 = tni * C::BN;
@@ -326,7 +333,7 @@ __global__ __launch_bounds__(kThreads) void gemm_big_kernel(const uint16_t *__re
             const float s = ep.scale[a];
             for (int rc = 0; rc < RM; rc += kBK) {
                 lds_barrier();
-                for (int c = tid; c < C::BM * 4; c += kThreads) {
+                for (int c = tid; c < C::BM * 4; c += C::NT) {
                     const int row = c >> 2, lc = c & 3;
                     const int pos = row0 + row;
                     const int j = rc + lc * 8;
@@ -340,7 +347,7 @@ __global__ __launch_bounds__(kThreads) void gemm_big_kernel(const uint16_t *__re
                     }
                     X0[row * 4 + (lc ^ ((row >> 2) & 3))] = v;
                 }
-                for (int c = tid; c < kBK * C::WCH; c += kThreads) {
+                for (int c = tid; c < kBK * C::WCH; c += C::NT) {
                     const int r = c / C::WCH, lc = c % C::WCH;
                     const int n = n0 + lc * 8;
                     uint4 v = make_uint4(0, 0, 0, 0);
@@ -377,10 +384,14 @@ __global__ __launch_bounds__(kThreads) void gemm_big_kernel(const uint16_t *__re
         // store instruction).  LDS accesses of one wave complete in order, so the staging
         // needs no barrier beyond the one that frees the slots.
         lds_barrier();
-        uint16_t *stg = reinterpret_cast<uint16_t *>(wave == 0 ? X0 : wave == 1 ? X1 : wave == 2 ? X2 : X3);
+        // wave w stages in slot w of X0 .. X3, W0 .. W3
+        uint4 *const sl = wave == 0 ? X0 : wave == 1 ? X1 : wave == 2 ? X2 : wave == 3 ? X3
+                        : wave == 4 ? W0 : wave == 5 ? W1 : wave == 6 ? W2 : W3;
+        uint16_t *stg = reinterpret_cast<uint16_t *>(sl);
         constexpr int SROW = C::WTN + 8;  // staged row length (bf16), 16-byte pad
         constexpr int CPR = C::WTN / 8;   // 16-byte pieces per staged row
-        static_assert(32 * SROW * 2 <= C::XSLOT * 16, "staging fits one slot");
+        static_assert(32 * SROW * 2 <= C::XSLOT * 16 && 32 * SROW * 2 <= C::WSLOT * 16,
+                      "staging fits one slot");
         uint16_t *yb = reinterpret_cast<uint16_t *>(y);
 #pragma unroll
         for (int i = 0; i < C::TM; ++i) {
@@ -414,10 +425,10 @@ hipError_t launch_big_cfg(const uint16_t *x, const uint16_t *W, int M, int K, in
     if (lora) ep = *lora;
     const dim3 grid(n_tm * n_tn);
     if (y_f32)
-        launch((gemm_big_kernel<C, SEGROWS, LORA, true>), grid, dim3(kThreads), 0, s, x, W,
+        launch((gemm_big_kernel<C, SEGROWS, LORA, true>), grid, dim3(C::NT), 0, s, x, W,
                            M, K, N, y, n_tm, n_tn, seg, ep);
     else
-        launch((gemm_big_kernel<C, SEGROWS, LORA, false>), grid, dim3(kThreads), 0, s, x, W,
+        launch((gemm_big_kernel<C, SEGROWS, LORA, false>), grid, dim3(C::NT), 0, s, x, W,
                            M, K, N, y, n_tm, n_tn, seg, ep);
     return hipGetLastError();
 }
@@ -430,12 +441,12 @@ hipError_t launch_gemm_big(const uint16_t *x, const uint16_t *W, int M, int K, i
                            bool y_f32, Seg seg, const LoraEpilogue *lora, hipStream_t s) {
     const long t256 = (long)((M + 255) / 256) * ((N + 255) / 256);
     if (lora) {
-        if (t256 >= 192) return launch_big_cfg<Big<256, 256>, true, true>(x, W, M, K, N, y, y_f32, seg, lora, s);
+        if (t256 >= 192) return launch_big_cfg<Big<256, 256, 2, 4>, true, true>(x, W, M, K, N, y, y_f32, seg, lora, s);
         if ((long)((M + 255) / 256) * ((N + 127) / 128) >= 192)
             return launch_big_cfg<Big<256, 128>, true, true>(x, W, M, K, N, y, y_f32, seg, lora, s);
         return launch_big_cfg<Big<128, 128>, true, true>(x, W, M, K, N, y, y_f32, seg, lora, s);
     }
-    if (t256 >= 192) return launch_big_cfg<Big<256, 256>, false, false>(x, W, M, K, N, y, y_f32, seg, nullptr, s);
+    if (t256 >= 192) return launch_big_cfg<Big<256, 256, 2, 4>, false, false>(x, W, M, K, N, y, y_f32, seg, nullptr, s);
     if ((long)((M + 255) / 256) * ((N + 127) / 128) >= 192)
         return launch_big_cfg<Big<256, 128>, false, false>(x, W, M, K, N, y, y_f32, seg, nullptr, s);
     return launch_big_cfg<Big<128, 128>, false, false>(x, W, M, K, N, y, y_f32, seg, nullptr, s);
