@@ -117,14 +117,14 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void expand_kernel(
         const bool colok = c < d_out;  // d_out % 8 == 0: a lane's columns are all in or all out
         const int cl = colok ? c : 0;
 
-        // B_a[0:r, c .. c+CPL): one load per rank row
+        // B_a[0:r, c .. c+CPL): one load per rank row, all issued together.  Rows at or
+        // beyond the rank load row r - 1 again (the same cache lines: no extra HBM bytes)
+        // and are multiplied by zero below.
         Vec<CPL> bj[RM];
         const uint16_t *Bp = B + (size_t)a * RM * d_out + cl;
+        const int rl = r > 0 ? r - 1 : 0;
 #pragma unroll
-        for (int j = 0; j < RM; ++j) {
-            if (j < r) bj[j] = ldv<CPL>(Bp + (size_t)j * d_out);
-            else bj[j].v = {};
-        }
+        for (int j = 0; j < RM; ++j) bj[j] = ldv<CPL>(Bp + (size_t)min(j, rl) * d_out);
 
         // rows of the tile in batches of RB: the lane's y slice of each row and t[m, lane]
         // (lane j < r_max holds t[m, j]; read back with readlane) are loaded together
@@ -143,10 +143,20 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void expand_kernel(
             for (int i = 0; i < RB; ++i)
 #pragma unroll
                 for (int e = 0; e < CPL; ++e) acc[i][e] = 0.0f;
+            // keep B packed across the row loop: unpacking it once outside would hold
+            // RM x CPL floats live and serialise its loads
+#pragma unroll
+            for (int j = 0; j < RM; ++j) {
+                if constexpr (CPL == 8) {
+                    asm volatile("" : "+v"(bj[j].v.x), "+v"(bj[j].v.y), "+v"(bj[j].v.z), "+v"(bj[j].v.w));
+                } else {
+                    asm volatile("" : "+v"(bj[j].v.x), "+v"(bj[j].v.y));
+                }
+            }
             // rank row j outer: B_a[j] is unpacked once per batch and used by all its rows
 #pragma unroll
             for (int j = 0; j < RM; ++j) {
-                if (j < r) {
+                if (j < r) {  // uniform: the wave's adapter
                     float b[CPL];
                     unpackv<CPL>(bj[j], b);
 #pragma unroll
