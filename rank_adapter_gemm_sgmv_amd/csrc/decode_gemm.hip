@@ -288,6 +288,7 @@ __global__ __launch_bounds__(256) void reduce_lora_kernel(const float *__restric
                                                           void *__restrict__ y) {
     constexpr int kMaxSplits = 16;
     __shared__ float s_t[RM];
+    constexpr int kTpartMax = 8192;  // n_chunks x RM floats staged in LDS
     const int m = blockIdx.y;
     const int n = (blockIdx.x * 256 + threadIdx.x) * 4;
     const bool col_ok = n < N;
@@ -309,20 +310,24 @@ __global__ __launch_bounds__(256) void reduce_lora_kernel(const float *__restric
     const uint16_t *bp = lo.B + (size_t)a * RM * N + nc;
 #pragma unroll
     for (int j = 0; j < RM; ++j) bv[j] = *reinterpret_cast<const uint2 *>(bp + (size_t)j * N);
-    // t[m, j]: thread j adds the chunks in order, eight loads in flight
+    // t[m, j] = sum over chunks c, in order, of tpart[c][m][j]: the block loads the
+    // n_chunks x RM values at once (one or a few per thread) into LDS, then thread j adds
+    // its column in chunk order (for very long d_in, thread j reads its column directly)
+    __shared__ float s_tp[kTpartMax];
+    const size_t cs = (size_t)M * RM;
+    const int nv = lo.n_chunks * RM;
+    const bool staged = nv <= kTpartMax;
+    if (has && staged)
+        for (int v = threadIdx.x; v < nv; v += 256) s_tp[v] = lo.tpart[(v / RM) * cs + (size_t)m * RM + v % RM];
+    __syncthreads();
     if (has && threadIdx.x < RM) {
-        const int j = threadIdx.x;
-        const float *tp = lo.tpart + (size_t)m * RM + j;
-        const size_t cs = (size_t)M * RM;
         float t = 0.0f;
-        for (int c0 = 0; c0 < lo.n_chunks; c0 += 8) {
-            float u[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) u[i] = c0 + i < lo.n_chunks ? tp[(c0 + i) * cs] : 0.0f;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) t += u[i];
+        if (staged) {
+            for (int c = 0; c < lo.n_chunks; ++c) t += s_tp[c * RM + threadIdx.x];
+        } else {
+            for (int c = 0; c < lo.n_chunks; ++c) t += lo.tpart[c * cs + (size_t)m * RM + threadIdx.x];
         }
-        s_t[j] = t;
+        s_t[threadIdx.x] = t;
     }
     __syncthreads();
 

@@ -133,6 +133,8 @@ RANDOM = [
     (20, 100, 2048, 1000, 300, 16, 0.1, DECODE),
     (21, 128, 512, 256, 1024, 64, 0.0, DECODE),
     (22, 64, 512, 136, 65, 8, 0.5, DECODE),
+    # long d_in: the reduction sums t's 130 chunks straight from memory (too many for LDS)
+    (23, 8, 16640, 64, 5, 64, 0.0, DECODE),
 ]
 
 
