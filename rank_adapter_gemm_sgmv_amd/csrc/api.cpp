@@ -234,7 +234,7 @@ hipError_t run_linear(const void *x, const void *W, const void *A, const void *B
         // small decode batch: the GEMM's workgroups also compute the shrink's chunk sums
         // (while their first W stages load), then one reduction adds the splits and the
         // expand
-        const DecodeLora lo{tpart, decode_shrink_chunks(d_in, r_max), Bb, scale, ids, r_max, n_adapters};
+        const DecodeLora lo{tpart, decode_shrink_chunks(d_in, r_max), Bb, scale, ids, ranks, r_max, n_adapters};
         if ((e = launch_decode_gemm(xb, Wb, static_cast<const uint16_t *>(A), M, d_in, d_out, lo,
                                     gpart, s)) != hipSuccess)
             return e;

@@ -126,11 +126,14 @@ struct DecodeLora {
     const uint16_t *B;     // [n][r_max][d_out]
     const float *scale;    // [n]
     const int32_t *ids;    // [M]
+    const int32_t *ranks;  // [n] true ranks, or nullptr (= r_max)
     int r_max;
     int n_adapters;
 };
 
-// Decode batches up to this many rows use the small-batch path when K % 32 == 0.
+// Decode batches up to this many rows use the small-batch path when K % 32 == 0.  (256
+// rows measured slower than the segment path: the shrink's work items outnumber the
+// shrink waves eight to one.)
 constexpr int kDecodeMaxRows = 128;
 bool decode_gemm_supported(int M, int K, int N);
 size_t decode_gemm_partial_floats(int M, int K, int N);

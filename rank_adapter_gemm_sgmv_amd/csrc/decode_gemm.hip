@@ -174,8 +174,12 @@ __global__ __launch_bounds__(kBlock) void decode_gemm_kernel(
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n_tiles = n_tm * n_tn;
-    // block -> (tile, split): the splits of one tile are n_tiles apart
-    const int tile = blockIdx.x % n_tiles, split = blockIdx.x / n_tiles;
+    // block -> (split, column tile, row tile).  With two row tiles, row tile fastest over
+    // consecutive blocks of one XCD (workgroup b runs on XCD b % 8), so both read a W column
+    // panel through that XCD's L2
+    int lin = blockIdx.x;
+    if (n_tm > 1 && (gridDim.x & 7) == 0) lin = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+    const int tile = lin % n_tiles, split = lin / n_tiles;
     // shrink items name adapters directly when the pool is no larger than the batch (rows
     // found by a ballot over ids), else through the batch's distinct adapters in LDS
     const bool by_id = lo.n_adapters <= M;
@@ -236,28 +240,25 @@ __global__ __launch_bounds__(kBlock) void decode_gemm_kernel(
     } else {
         // ---- the shrink's work items ---------------------------------------------------------
         const int pair = (wave - kWaves) >> 1;
-        int id0 = -1, id1 = -1;
-        if (by_id) {
-            id0 = lane < M ? lo.ids[lane] : -1;
-            id1 = lane + 64 < M ? lo.ids[lane + 64] : -1;
-        }
+        int idq[kRowWords];
+#pragma unroll
+        for (int q = 0; q < kRowWords; ++q) idq[q] = by_id && lane + 64 * q < M ? lo.ids[lane + 64 * q] : -1;
         const uint64_t par = (wave & 1) ? 0xAAAAAAAAAAAAAAAAull : 0x5555555555555555ull;
         const int n_items = lo.n_chunks * (by_id ? lo.n_adapters : ba.T);
         for (int w = blockIdx.x * 2 + pair; w < n_items; w += gridDim.x * 2) {
             const int c = w % lo.n_chunks, s = w / lo.n_chunks;
-            int a;
-            uint64_t r0, r1;
-            if (by_id) {
-                a = s;
-                r0 = __ballot(id0 == a);
-                r1 = __ballot(id1 == a);
-            } else {
-                a = ba.list[s];
-                r0 = __ballot(lane < M && ba.slot[lane] == s);
-                r1 = __ballot(lane + 64 < M && ba.slot[lane + 64] == s);
+            const int a = by_id ? s : ba.list[s];
+            RowMask mk;
+            uint64_t any = 0;
+#pragma unroll
+            for (int q = 0; q < kRowWords; ++q) {
+                const int m = lane + 64 * q;
+                const uint64_t r = by_id ? __ballot(idq[q] == a) : __ballot(m < M && ba.slot[m] == s);
+                any |= r;
+                mk.w[q] = r & par;
             }
-            if ((r0 | r1) == 0) continue;  // an adapter of the pool without rows in the batch
-            decode_shrink_item<RM>(x, A, M, K, c, a, r0 & par, r1 & par, lane, lo.tpart);
+            if (any == 0) continue;  // an adapter of the pool without rows in the batch
+            decode_shrink_item<RM>(x, A, M, K, c, a, mk, lane, lo.tpart);
         }
     }
     __syncthreads();  // every GEMM wave is done with the W stages
@@ -305,11 +306,13 @@ __global__ __launch_bounds__(256) void reduce_lora_kernel(const float *__restric
 #pragma unroll
     for (int sp = 0; sp < kMaxSplits; ++sp)
         if (sp < n_splits) pv[sp] = *reinterpret_cast<const float4 *>(pp + sp * stride);
-    // B_a[j, nc .. nc+3] for every rank row (zero beyond the adapter's rank: padded pool)
+    // B_a[j, nc .. nc+3] for the adapter's rank rows, all issued together (rows at or beyond
+    // the rank reload row r - 1, the same cache lines, and are skipped in the sum)
+    const int r = !has ? 1 : lo.ranks ? min(max(lo.ranks[a], 1), RM) : RM;
     uint2 bv[RM];
     const uint16_t *bp = lo.B + (size_t)a * RM * N + nc;
 #pragma unroll
-    for (int j = 0; j < RM; ++j) bv[j] = *reinterpret_cast<const uint2 *>(bp + (size_t)j * N);
+    for (int j = 0; j < RM; ++j) bv[j] = *reinterpret_cast<const uint2 *>(bp + (size_t)min(j, r - 1) * N);
     // t[m, j] = sum over chunks c, in order, of tpart[c][m][j]: the block loads the
     // n_chunks x RM values at once (one or a few per thread) into LDS, then thread j adds
     // its column in chunk order (for very long d_in, thread j reads its column directly)
@@ -342,7 +345,7 @@ __global__ __launch_bounds__(256) void reduce_lora_kernel(const float *__restric
         float d0 = 0.f, d1 = 0.f, d2 = 0.f, d3 = 0.f;
 #pragma unroll
         for (int j = 0; j < RM; ++j) {
-            const float tj = s_t[j];
+            const float tj = j < r ? s_t[j] : 0.0f;  // rows past the rank add nothing
             d0 = fmaf(tj, bf16_lo(bv[j].x), d0);
             d1 = fmaf(tj, bf16_hi(bv[j].x), d1);
             d2 = fmaf(tj, bf16_lo(bv[j].y), d2);

@@ -10,8 +10,9 @@
 // Work item (k-chunk c, adapter a), taken by a pair of waves: the pair holds
 // A_a[chunk, 0:r_max] in registers (each lane one k-slice x 8 rank columns, 16-byte loads;
 // all r_max columns, the pool's padding being zero) and multiplies every row of adapter a
-// with it -- each wave takes the rows of one parity, given as ballot masks over rows 0..63
-// and 64..127 -- with 8 fp32 sums per lane and an xor butterfly across the k-slices.  The
+// with it -- each wave takes the rows of one parity, given as ballot masks over the batch's
+// rows (at most kDecodeMaxRows) -- with 8 fp32 sums per lane and an xor butterfly across
+// the k-slices.  The
 // caller names the adapters either directly (item = (chunk, adapter id), rows found by a
 // ballot over ids) or through the batch's distinct adapters grouped in LDS
 // (batch_adapters.h).  So each touched A_a is read from HBM
@@ -35,11 +36,17 @@ struct DecodeShrinkCfg {
 
 inline int decode_shrink_chunk_k(int r_max) { return r_max == 64 ? 128 : 256; }
 
+// Row masks of one wave: bit i of word q is row 64 q + i.
+constexpr int kRowWords = kDecodeMaxRows / 64;
+struct RowMask {
+    uint64_t w[kRowWords];
+};
+
 template <int RM>
 __device__ __forceinline__ void decode_shrink_item(const uint16_t *__restrict__ x,
                                                    const uint16_t *__restrict__ A, int M, int K,
-                                                   int c, int a, uint64_t mk0, uint64_t mk1,
-                                                   int lane, float *__restrict__ tpart) {
+                                                   int c, int a, RowMask mk, int lane,
+                                                   float *__restrict__ tpart) {
     using C = DecodeShrinkCfg<RM>;
     const int ks = lane % C::KSUB, g = lane / C::KSUB;
     const int k0 = c * C::KC + ks * C::SL;
@@ -52,18 +59,16 @@ __device__ __forceinline__ void decode_shrink_item(const uint16_t *__restrict__ 
 #pragma unroll
     for (int kk = 0; kk < C::SL; ++kk) araw[kk] = ld16(k0 + kk < K ? Ap + (size_t)kk * RM : Alast);
 
-    // this wave's rows (mk0: rows 0..63, mk1: rows 64..127); the next row's x is loaded while
-    // the current one is multiplied
+    // this wave's rows, lowest first; the next row's x is loaded while the current one is
+    // multiplied
     auto next_row = [&]() -> int {
-        if (mk0) {
-            const int b = __ffsll((unsigned long long)mk0) - 1;
-            mk0 &= mk0 - 1;
-            return b;
-        }
-        if (mk1) {
-            const int b = __ffsll((unsigned long long)mk1) - 1;
-            mk1 &= mk1 - 1;
-            return b + 64;
+#pragma unroll
+        for (int q = 0; q < kRowWords; ++q) {
+            if (mk.w[q]) {
+                const int b = __ffsll((unsigned long long)mk.w[q]) - 1;
+                mk.w[q] &= mk.w[q] - 1;
+                return b + 64 * q;
+            }
         }
         return -1;
     };

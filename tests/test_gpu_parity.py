@@ -135,6 +135,10 @@ RANDOM = [
     (22, 64, 512, 136, 65, 8, 0.5, DECODE),
     # long d_in: the reduction sums t's 130 chunks straight from memory (too many for LDS)
     (23, 8, 16640, 64, 5, 64, 0.0, DECODE),
+    # just past the small-batch limit (129 rows: the segment path), and at it
+    (24, 200, 1024, 520, 40, 32, 0.1, DECODE),
+    (25, 128, 2048, 264, 300, 64, 0.2, DECODE),
+    (26, 129, 512, 128, 3, 8, 0.0, DECODE),
 ]
 
 
