@@ -208,6 +208,8 @@ lora_status_t check_linear(const void *x, const void *W, const void *A, const vo
 //            compute the LoRA shrink's chunk sums, then the ordered reduction that adds
 //            scale_a t B_a (no segment-building launch: rows are grouped by adapter in LDS;
 //            segs is not needed)
+//   decode, 128 < M <= 256 and d_in % 32 == 0: build_segments, shrink (chunk sums), the
+//            split-K GEMM, the ordered reduction with the expand
 //   decode otherwise: build_segments, shrink, shrink_finalize, gemm [, splitk_reduce], expand
 //   prefill: build_segments, shrink, shrink_finalize, gemm with the LoRA epilogue
 hipError_t run_linear(const void *x, const void *W, const void *A, const void *B,
@@ -230,15 +232,37 @@ hipError_t run_linear(const void *x, const void *W, const void *A, const void *B
     const uint16_t *Bb = static_cast<const uint16_t *>(B);
     const bool yf = y_dtype == LORA_F32;
     hipError_t e;
-    if (!prefill && decode_gemm_supported(M, d_in, d_out)) {
+    const DecodeLora lo{tpart, decode_shrink_chunks(d_in, r_max), Bb, scale, ids, ranks, r_max, n_adapters};
+    if (!prefill && decode_fused_supported(M, d_in, d_out)) {
         // small decode batch: the GEMM's workgroups also compute the shrink's chunk sums
-        // (while their first W stages load), then one reduction adds the splits and the
-        // expand
-        const DecodeLora lo{tpart, decode_shrink_chunks(d_in, r_max), Bb, scale, ids, ranks, r_max, n_adapters};
+        // (beside their W stream), then one reduction adds the splits and the expand
         if ((e = launch_decode_gemm(xb, Wb, static_cast<const uint16_t *>(A), M, d_in, d_out, lo,
-                                    gpart, s)) != hipSuccess)
+                                    true, gpart, s)) != hipSuccess)
             return e;
         mark(mk, "decode_gemm_shrink");
+        if ((e = launch_decode_reduce(gpart, M, d_in, d_out, y, yf, lo, s)) != hipSuccess) return e;
+        mark(mk, "decode_reduce_lora");
+        return hipSuccess;
+    }
+    if (!prefill && decode_gemm_supported(M, d_in, d_out)) {
+        // medium decode batch: segment build and the segment-path shrink, whose per-chunk
+        // partial sums have the layout the decode reduction reads; the split-K GEMM; the
+        // reduction with the expand
+        if (!segs) {
+            if ((e = launch_build_segments(ids, M, n_adapters, sg, s)) != hipSuccess) return e;
+            mark(mk, "build_segments");
+        }
+        int kc, ksplit;
+        shrink_plan(d_in, r_max, &kc, &ksplit);
+        if (ksplit != lo.n_chunks) return hipErrorInvalidValue;
+        if ((e = launch_shrink(xb, static_cast<const uint16_t *>(A), ranks, M, d_in, r_max, n_adapters,
+                               sg, tpart, kc, ksplit, s)) != hipSuccess)
+            return e;
+        mark(mk, "shrink");
+        if ((e = launch_decode_gemm(xb, Wb, static_cast<const uint16_t *>(A), M, d_in, d_out, lo,
+                                    false, gpart, s)) != hipSuccess)
+            return e;
+        mark(mk, "decode_gemm");
         if ((e = launch_decode_reduce(gpart, M, d_in, d_out, y, yf, lo, s)) != hipSuccess) return e;
         mark(mk, "decode_reduce_lora");
         return hipSuccess;

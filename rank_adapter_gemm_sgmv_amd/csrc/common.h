@@ -135,12 +135,17 @@ struct DecodeLora {
 // rows measured slower than the segment path: the shrink's work items outnumber the
 // shrink waves eight to one.)
 constexpr int kDecodeMaxRows = 128;
-bool decode_gemm_supported(int M, int K, int N);
+// The split-K decode GEMM + LoRA reduction serve batches up to this many rows (beyond
+// kDecodeMaxRows with the segment-path shrink writing the chunk sums).
+constexpr int kDecodeGemmMaxRows = 256;
+bool decode_gemm_supported(int M, int K, int N);  // M <= kDecodeGemmMaxRows
+bool decode_fused_supported(int M, int K, int N);  // and M <= kDecodeMaxRows
 size_t decode_gemm_partial_floats(int M, int K, int N);
-// Split-K partial tiles of x W for a decode batch; the same launch writes the LoRA
-// shrink's chunk sums lo.tpart[c][m][0:r_max] (rows grouped by adapter in LDS).
+// Split-K partial tiles of x W for a decode batch; with_shrink (M <= kDecodeMaxRows): the
+// same launch writes the LoRA shrink's chunk sums lo.tpart[c][m][0:r_max].
 hipError_t launch_decode_gemm(const uint16_t *x, const uint16_t *W, const uint16_t *A, int M,
-                              int K, int N, const DecodeLora &lo, float *partial, hipStream_t s);
+                              int K, int N, const DecodeLora &lo, bool with_shrink, float *partial,
+                              hipStream_t s);
 
 // Number of k-chunks of the small-batch shrink (csrc/decode_shrink.h).
 int decode_shrink_chunks(int K, int r_max);

@@ -150,16 +150,17 @@ __device__ __forceinline__ void reduce_waves_sum(const float *r0, const float *r
     }
 }
 
-// Workgroup (tile, split), eight waves.  Waves 0-3 stream split `split` of K (rows
-// [split k_per_split, +k_per_split)) and write its partial tile; reduce_lora_kernel adds the
-// splits in order.  Waves 4-7, side by side on the same CU, run the shrink's work items
+// Workgroup (tile, split), eight waves (four without the shrink).  Waves 0-3 stream split
+// `split` of K (rows [split k_per_split, +k_per_split)) and write its partial tile;
+// reduce_lora_kernel adds the splits in order.  With with_shrink (M <= kDecodeMaxRows),
+// waves 4-7, side by side on the same CU, run the shrink's work items
 // blockIdx.x * 2 + (wave - 4) / 2, stepping by 2 gridDim.x (a pair per item, rows of parity
-// wave % 2).
+// wave % 2); without it the shrink's chunk sums come from the segment-path shrink.
 template <class C, int RM>
 __global__ __launch_bounds__(kBlock) void decode_gemm_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ W, const uint16_t *__restrict__ A,
     int M, int K, int N, int n_tm, int n_tn, int k_per_split, float *__restrict__ partial,
-    DecodeLora lo) {
+    DecodeLora lo, int with_shrink) {
     // stage s of GEMM wave w: X{s}[w * XSLOT ..], W{s}[w * WSLOT ..]
     __shared__ __attribute__((aligned(1024))) uint4 XS0[kWaves * C::XSLOT];
     __shared__ __attribute__((aligned(1024))) uint4 XS1[kWaves * C::XSLOT];
@@ -183,7 +184,7 @@ __global__ __launch_bounds__(kBlock) void decode_gemm_kernel(
     // shrink items name adapters directly when the pool is no larger than the batch (rows
     // found by a ballot over ids), else through the batch's distinct adapters in LDS
     const bool by_id = lo.n_adapters <= M;
-    if (!by_id) batch_adapters(ba, lo.ids, M, lo.n_adapters);  // every thread: barriers
+    if (with_shrink && !by_id) batch_adapters(ba, lo.ids, M, lo.n_adapters);  // every thread: barriers
 
     f32x16_t acc[C::TM][C::TN];
 #pragma unroll
@@ -389,7 +390,12 @@ DecPlan dec_plan(int M, int K, int N) {
 }  // namespace
 
 bool decode_gemm_supported(int M, int K, int N) {
-    return M >= 1 && M <= kDecodeMaxRows && K % kBK == 0 && K >= kBK * kWaves && N >= 8 && N % 4 == 0;
+    return M >= 1 && M <= kDecodeGemmMaxRows && K % kBK == 0 && K >= kBK * kWaves && N >= 8 &&
+           N % 4 == 0;
+}
+
+bool decode_fused_supported(int M, int K, int N) {
+    return decode_gemm_supported(M, K, N) && M <= kDecodeMaxRows;
 }
 
 size_t decode_gemm_partial_floats(int M, int K, int N) {
@@ -404,15 +410,18 @@ int decode_shrink_chunks(int K, int r_max) {
 }
 
 hipError_t launch_decode_gemm(const uint16_t *x, const uint16_t *W, const uint16_t *A, int M,
-                              int K, int N, const DecodeLora &lo, float *partial, hipStream_t s) {
+                              int K, int N, const DecodeLora &lo, bool with_shrink, float *partial,
+                              hipStream_t s) {
     if (!decode_gemm_supported(M, K, N) || partial == nullptr || lo.tpart == nullptr ||
-        lo.n_chunks != decode_shrink_chunks(K, lo.r_max))
+        lo.n_chunks != decode_shrink_chunks(K, lo.r_max) || (with_shrink && M > kDecodeMaxRows))
         return hipErrorInvalidValue;
     const DecPlan p = dec_plan(M, K, N);
     const dim3 grid(p.n_tm * p.n_tn * p.ks);
+    const dim3 block(with_shrink ? kBlock : kThreads);
+    const int ws = with_shrink ? 1 : 0;
 #define GEMM_LAUNCH(BM, RMX)                                                                  \
-    launch((decode_gemm_kernel<Dec<BM>, RMX>), grid, dim3(kBlock), 0, s, x, W, A, M, K, N,     \
-           p.n_tm, p.n_tn, p.k_per_split, partial, lo)
+    launch((decode_gemm_kernel<Dec<BM>, RMX>), grid, block, 0, s, x, W, A, M, K, N, p.n_tm,    \
+           p.n_tn, p.k_per_split, partial, lo, ws)
 #define GEMM_RANK(BM)                                                                         \
     switch (lo.r_max) {                                                                       \
         case 8: GEMM_LAUNCH(BM, 8); break;                                                    \
