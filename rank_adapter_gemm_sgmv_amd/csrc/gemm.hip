@@ -18,9 +18,10 @@
 //
 // Tilings: prefill 256 x 256 (4 waves of 128 x 128, 16 accumulators of 32 x 32 each);
 // decode 64 x 64, 128 x 64 or 128 x 128 with split-K partial sums reduced by a second
-// kernel in split order.  Prefill tiles are mapped XCD-aware: workgroup b runs on XCD b % 8,
-// so each XCD is handed a compact 4 x 8 block of tiles and its L2 serves the x and W panels
-// those tiles share.
+// kernel in split order.  Tiles are mapped XCD-aware: workgroup b runs on XCD b % 8, so
+// each XCD is handed compact groups of 4 tile rows and its L2 serves the x and W panels those
+// tiles share (without it, the row tiles of a decode W panel land on four XCDs and W is
+// fetched from HBM about four times).
 //
 // Prefill epilogue (segment-ordered rows): the tile's rows are positions of perm, so each
 // tile holds a few long runs of one adapter.  For every run, T = scale_a * t[rows, :] (bf16)
@@ -68,7 +69,7 @@ struct Cfg {
     static_assert(BM * (kBK / 8) % NT == 0, "x chunks must divide evenly");
 };
 
-// Prefill tile order: XCD-major, then groups of 4 tile rows, column-major inside a group.
+// Tile order: XCD-major, then groups of 4 tile rows, column-major inside a group.
 __device__ __forceinline__ void tile_coords(int b, int n_tm, int n_tn, bool xcd_remap, int &tm,
                                             int &tn) {
     const int T = n_tm * n_tn;
@@ -163,7 +164,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(const uint16_t *__restrict_
     const int wm0 = (wave / C::WN) * C::WTM, wn0 = (wave % C::WN) * C::WTN;
 
     int tmi, tni;
-    tile_coords(blockIdx.x, n_tm, n_tn, PREFILL, tmi, tni);
+    tile_coords(blockIdx.x, n_tm, n_tn, true, tmi, tni);
     const int row0 = tmi * BM, n0 = tni * BN;
     const int split = blockIdx.y;
     const int kz0 = split * k_per_split;
