@@ -349,6 +349,26 @@ def summarize(w, runner, ms_total, steps, wall, eager_ms, kernels, prefill):
     }
 
 
+def base_only_ms(w, runner, steps, torch):
+    """ms per step of the same launches with every id = -1 (no row has an adapter): what
+    this path costs for the bare base model, to compare the LoRA step against."""
+    keep = runner.ids
+    runner.ids = torch.full_like(keep, -1)
+    try:
+        g = capture(runner, steps, torch)
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        g.replay()
+        ev1.record()
+        torch.cuda.synchronize()
+        ms = ev0.elapsed_time(ev1) / steps
+        del g
+    finally:
+        runner.ids = keep
+    return ms
+
+
 def run_workload(config, mode_name, steps, warmup, torch, profile_reps=20, need_runner=False):
     from synth import make_workload
 
@@ -364,6 +384,9 @@ def run_workload(config, mode_name, steps, warmup, torch, profile_reps=20, need_
     ms_total, wall, eager_ms, kernels = measure(runner, steps, warmup, torch, profile_reps)
     s = summarize(w, runner, ms_total, steps, wall, eager_ms, kernels, prefill)
     s.update({"workload": w.name, "mode": mode_name, "layers_rotated": L, "steps": steps})
+    base_ms = base_only_ms(w, runner, steps, torch)
+    s["base_only_ms_per_step"] = base_ms
+    s["lora_overhead_vs_base_only"] = s["ms_per_step"] / base_ms - 1.0
     return w, s, kernels, steps, ms_total
 
 
