@@ -432,8 +432,8 @@ def main():
                          "kernel, for rocprofv3 --pmc runs (FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (this build runs "
-              "on a single MI355X; see the sharding notes in the design document).", file=sys.stderr)
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (the library runs "
+              "on a single MI355X; sharding across GPUs is not implemented).", file=sys.stderr)
         sys.exit(2)
 
     import torch
