@@ -86,11 +86,11 @@ def algorithmic_work(w, d_in: int, d_out: int, prefill: bool, y_bytes: int = 2) 
                                     "flops": base_flops + 2.0 * r_rows * d_out}
     else:
         out["gemm_decode"] = {"bytes": gemm_bytes, "flops": base_flops}
-        # small-batch decode path: the split-K GEMM (W, x) whose workgroups also run the
-        # shrink (the touched A_i, t written), then the ordered reduction with the expand
-        # (the touched B_i, t read, y written once)
-        out["decode_gemm_shrink"] = {"bytes": gemm_bytes + a_bytes + t_bytes,
-                                     "flops": base_flops + 2.0 * r_rows * d_in}
+        # small-batch decode path: one split-K GEMM over W and the touched A_i side by side
+        # (x read; t leaves as split partials, not counted), then the ordered reduction with
+        # the expand (the touched B_i, t read, y written once)
+        out["decode_gemm_lora"] = {"bytes": gemm_bytes + a_bytes,
+                                   "flops": base_flops + 2.0 * r_rows * d_in}
         # medium decode batches: the same GEMM without the shrink (W, x)
         out["decode_gemm"] = {"bytes": gemm_bytes, "flops": base_flops}
         out["decode_reduce_lora"] = {"bytes": b_bytes + t_bytes + M * d_out * y_bytes,
@@ -319,7 +319,7 @@ def summarize(w, runner, ms_total, steps, wall, eager_ms, kernels, prefill):
         entry = {"projection": p.name, "d_in": p.d_in, "d_out": p.d_out,
                  "kernels_us": {k: round(v * 1e3, 2) for k, v in ks.items()}}
         gname = "gemm_prefill_lora" if prefill else (
-            "decode_gemm_shrink" if "decode_gemm_shrink" in ks else
+            "decode_gemm_lora" if "decode_gemm_lora" in ks else
             "decode_gemm" if "decode_gemm" in ks else "gemm_decode")
         if gname in ks:
             g_ms = ks[gname]

@@ -64,14 +64,9 @@ size_t shrink_partial_bytes(int32_t M, int32_t d_in, int32_t r_max) {
 
 size_t t_bytes(int32_t M, int32_t r_max) { return round_up((size_t)M * r_max * sizeof(float)); }
 
-// chunk sums of the decode shrink (small decode batches only)
-size_t tpart_bytes(int32_t M, int32_t d_in, int32_t d_out, int32_t r_max) {
-    if (!decode_gemm_supported(M, d_in, d_out)) return 0;
-    return round_up((size_t)decode_shrink_chunks(d_in, r_max) * M * r_max * sizeof(float));
-}
-
-size_t gemm_bytes(int32_t M, int32_t d_in, int32_t d_out) {
-    const size_t a = gemm_partial_floats(M, d_in, d_out), b = decode_gemm_partial_floats(M, d_in, d_out);
+size_t gemm_bytes(int32_t M, int32_t d_in, int32_t d_out, int32_t r_max, int32_t n_adapters) {
+    const size_t a = gemm_partial_floats(M, d_in, d_out),
+                 b = decode_gemm_partial_floats(M, d_in, d_out, r_max, n_adapters);
     return round_up((a > b ? a : b) * sizeof(float));
 }
 
@@ -102,7 +97,7 @@ size_t lora_workspace_bytes(int32_t M, int32_t d_in, int32_t d_out, int32_t r_ma
     if (check_common(M, r_max, n_adapters) != LORA_OK || !dim_ok(d_in) || !dim_ok(d_out)) return 0;
     if (M == 0) return 0;
     return segments_bytes(M, n_adapters) + t_bytes(M, r_max) + shrink_partial_bytes(M, d_in, r_max) +
-           gemm_bytes(M, d_in, d_out) + tpart_bytes(M, d_in, d_out, r_max);
+           gemm_bytes(M, d_in, d_out, r_max, n_adapters);
 }
 
 lora_status_t lora_build_segments(const int32_t *ids, int32_t M, int32_t n_adapters,
@@ -222,8 +217,7 @@ hipError_t run_linear(const void *x, const void *W, const void *A, const void *B
     lora_segments_t own = carve_segments(p, M, n_adapters);
     float *t = reinterpret_cast<float *>(p); p += t_bytes(M, r_max);
     float *spart = reinterpret_cast<float *>(p); p += shrink_partial_bytes(M, d_in, r_max);
-    float *gpart = reinterpret_cast<float *>(p); p += gemm_bytes(M, d_in, d_out);
-    float *tpart = reinterpret_cast<float *>(p);
+    float *gpart = reinterpret_cast<float *>(p);
     const size_t gpart_floats = gemm_partial_floats(M, d_in, d_out);
 
     const Seg sg = to_seg(segs ? *segs : own);
@@ -232,15 +226,18 @@ hipError_t run_linear(const void *x, const void *W, const void *A, const void *B
     const uint16_t *Bb = static_cast<const uint16_t *>(B);
     const bool yf = y_dtype == LORA_F32;
     hipError_t e;
-    const DecodeLora lo{tpart, decode_shrink_chunks(d_in, r_max), Bb, scale, ids, ranks, r_max, n_adapters};
+    int kc, ksplit;
+    shrink_plan(d_in, r_max, &kc, &ksplit);
     if (!prefill && decode_fused_supported(M, d_in, d_out)) {
-        // small decode batch: the GEMM's workgroups also compute the shrink's chunk sums
-        // (beside their W stream), then one reduction adds the splits and the expand
+        // small decode batch: x W and the shrink x A_i as tiles of one split-K GEMM (the
+        // row -> adapter slot map, when needed, goes to the t region), then one reduction
+        // adds the splits and the expand
+        const DecodeLora lo{nullptr, 0, reinterpret_cast<int32_t *>(t), Bb, scale, ids, ranks, r_max, n_adapters};
         if ((e = launch_decode_gemm(xb, Wb, static_cast<const uint16_t *>(A), M, d_in, d_out, lo,
                                     true, gpart, s)) != hipSuccess)
             return e;
-        mark(mk, "decode_gemm_shrink");
-        if ((e = launch_decode_reduce(gpart, M, d_in, d_out, y, yf, lo, s)) != hipSuccess) return e;
+        mark(mk, "decode_gemm_lora");
+        if ((e = launch_decode_reduce(gpart, M, d_in, d_out, y, yf, lo, true, s)) != hipSuccess) return e;
         mark(mk, "decode_reduce_lora");
         return hipSuccess;
     }
@@ -252,18 +249,15 @@ hipError_t run_linear(const void *x, const void *W, const void *A, const void *B
             if ((e = launch_build_segments(ids, M, n_adapters, sg, s)) != hipSuccess) return e;
             mark(mk, "build_segments");
         }
-        int kc, ksplit;
-        shrink_plan(d_in, r_max, &kc, &ksplit);
-        if (ksplit != lo.n_chunks) return hipErrorInvalidValue;
+        const DecodeLora lo{spart, ksplit, nullptr, Bb, scale, ids, ranks, r_max, n_adapters};
         if ((e = launch_shrink(xb, static_cast<const uint16_t *>(A), ranks, M, d_in, r_max, n_adapters,
-                               sg, tpart, kc, ksplit, s)) != hipSuccess)
+                               sg, spart, kc, ksplit, s)) != hipSuccess)
             return e;
         mark(mk, "shrink");
-        if ((e = launch_decode_gemm(xb, Wb, static_cast<const uint16_t *>(A), M, d_in, d_out, lo,
-                                    false, gpart, s)) != hipSuccess)
+        if ((e = launch_decode_gemm(xb, Wb, nullptr, M, d_in, d_out, lo, false, gpart, s)) != hipSuccess)
             return e;
         mark(mk, "decode_gemm");
-        if ((e = launch_decode_reduce(gpart, M, d_in, d_out, y, yf, lo, s)) != hipSuccess) return e;
+        if ((e = launch_decode_reduce(gpart, M, d_in, d_out, y, yf, lo, false, s)) != hipSuccess) return e;
         mark(mk, "decode_reduce_lora");
         return hipSuccess;
     }
@@ -271,8 +265,6 @@ hipError_t run_linear(const void *x, const void *W, const void *A, const void *B
         if ((e = launch_build_segments(ids, M, n_adapters, sg, s)) != hipSuccess) return e;
         mark(mk, "build_segments");
     }
-    int kc, ksplit;
-    shrink_plan(d_in, r_max, &kc, &ksplit);
     if ((e = launch_shrink(xb, static_cast<const uint16_t *>(A), ranks, M, d_in, r_max, n_adapters,
                            sg, spart, kc, ksplit, s)) != hipSuccess)
         return e;

@@ -119,10 +119,13 @@ hipError_t launch_gemm_big(const uint16_t *x, const uint16_t *W, int M, int K, i
 hipError_t launch_splitk_reduce(const float *partial, int M, int N, int ksplit, void *y,
                                 bool y_f32, hipStream_t s);
 
-// LoRA operands of the small-batch decode reduction (csrc/decode_gemm.hip).
+// LoRA operands of the small-batch decode GEMM and reduction (csrc/decode_gemm.hip).
 struct DecodeLora {
-    float *tpart;          // [n_chunks][M][r_max]: the shrink's chunk sums of t (written by the GEMM)
+    const float *tpart;    // [n_chunks][M][r_max]: the segment-path shrink's chunk sums of t
+                           // (calls without adapter tiles)
     int n_chunks;
+    int32_t *slots;        // [M]: row -> adapter slot, written by the GEMM when the pool is
+                           // larger than the batch (calls with adapter tiles)
     const uint16_t *B;     // [n][r_max][d_out]
     const float *scale;    // [n]
     const int32_t *ids;    // [M]
@@ -131,28 +134,29 @@ struct DecodeLora {
     int n_adapters;
 };
 
-// Decode batches up to this many rows use the small-batch path when K % 32 == 0.  (256
-// rows measured slower than the segment path: the shrink's work items outnumber the
-// shrink waves eight to one.)
+// Decode batches up to this many rows take the fused path (x W and x A_i as tiles of one
+// split-K launch) when d_in % 32 == 0: the slot tables of batch_adapters.h hold this many
+// rows, and beyond it one adapter tile per distinct adapter costs more than the
+// segment-path shrink.
 constexpr int kDecodeMaxRows = 128;
 // The split-K decode GEMM + LoRA reduction serve batches up to this many rows (beyond
 // kDecodeMaxRows with the segment-path shrink writing the chunk sums).
 constexpr int kDecodeGemmMaxRows = 256;
 bool decode_gemm_supported(int M, int K, int N);  // M <= kDecodeGemmMaxRows
 bool decode_fused_supported(int M, int K, int N);  // and M <= kDecodeMaxRows
-size_t decode_gemm_partial_floats(int M, int K, int N);
-// Split-K partial tiles of x W for a decode batch; with_shrink (M <= kDecodeMaxRows): the
-// same launch writes the LoRA shrink's chunk sums lo.tpart[c][m][0:r_max].
+// Split partial floats of the decode GEMM at these sizes (adapter tiles included where the
+// fused path applies).
+size_t decode_gemm_partial_floats(int M, int K, int N, int r_max, int n_adapters);
+// Split-K partial tiles of x W for a decode batch; with `adapters` (M <= kDecodeMaxRows)
+// the same launch also streams the batch's adapters' A as extra tiles (the LoRA shrink).
 hipError_t launch_decode_gemm(const uint16_t *x, const uint16_t *W, const uint16_t *A, int M,
-                              int K, int N, const DecodeLora &lo, bool with_shrink, float *partial,
+                              int K, int N, const DecodeLora &lo, bool adapters, float *partial,
                               hipStream_t s);
 
-// Number of k-chunks of the small-batch shrink (csrc/decode_shrink.h).
-int decode_shrink_chunks(int K, int r_max);
-// y = (split partials added in order) + scale_a * t B_a, t from the decode shrink's chunk
-// sums; rounds once into y.
+// y = (split partials added in order) + scale_a * t B_a, t from the adapter tiles' splits
+// (`adapters`) or from the segment-path shrink's chunk sums; rounds once into y.
 hipError_t launch_decode_reduce(const float *partial, int M, int K, int N, void *y, bool y_f32,
-                                const DecodeLora &lo, hipStream_t s);
+                                const DecodeLora &lo, bool adapters, hipStream_t s);
 
 // Workspace floats the decode GEMM needs for split-K partials at these sizes.
 size_t gemm_partial_floats(int M, int K, int N);

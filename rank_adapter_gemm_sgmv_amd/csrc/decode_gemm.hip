@@ -18,18 +18,20 @@
 //    Three stages (24 KiB per wave) are in flight.
 //  * x tile [BM][32] and W tile [32][64] per stage, XOR-swizzled; the W operand is read with
 //    the transposing LDS read (ds_read_b64_tr_b16); v_mfma_f32_32x32x16_bf16.
-//  * x W does not depend on the LoRA shrink, so the same workgroups also run it: each has
-//    four more waves that take the shrink's work items (decode_shrink.h) side by side with
-//    the four streaming W, on the same CU (which holds one such workgroup: its LDS ring is
-//    128 KiB).  The shrink costs no launch and, mostly, no time of its own.
+//  * The LoRA shrink t = x A_a is the same kind of product: the batch's adapters, laid side
+//    by side, are 64 / r_max adapters per extra 64-column "adapter tile" whose rows are
+//    A_a[k, 0:r_max] (row stride r_max instead of N).  Those tiles run in the same launch,
+//    split and streamed exactly like the W tiles, so every touched A_a is read from HBM
+//    once, at the same rate as W, with no latency chain of its own.  A tile computes t for
+//    every row of the batch against its adapters; the reduction keeps each row's own.
 //  * The four waves' partial tiles are added through LDS in wave order and each workgroup
 //    writes its partial tile.
 //  * reduce_lora_kernel then writes y[m, :] = (sum of the split partials, in split order)
-//    + scale_a * (t[m, :] B_a) with t[m, :] summed from the shrink's chunk sums in chunk
-//    order, in fp32, rounded once into y's dtype; each touched B_a row slice is read once
-//    from HBM (rows of one adapter share it through L2).  No atomics: the result does not
-//    depend on scheduling.
-#include "decode_shrink.h"
+//    + scale_a * (t[m, :] B_a) with t[m, :] summed over the splits of row m's adapter tile,
+//    in split order, in fp32, rounded once into y's dtype; each touched B_a row slice is
+//    read once from HBM (rows of one adapter share it through L2).  No atomics: the result
+//    does not depend on scheduling.
+#include "batch_adapters.h"
 
 namespace lora {
 
@@ -46,7 +48,6 @@ constexpr int kBN = 64;
 constexpr int kBK = 32;
 constexpr int kWaves = 4;                // waves streaming x W
 constexpr int kThreads = 64 * kWaves;
-constexpr int kBlock = 2 * kThreads;      // plus as many running the shrink beside them
 
 template <int BM_>
 struct Dec {
@@ -112,16 +113,26 @@ struct DecSrc {
     const uint16_t *wp[C::WINS];
 };
 
-// One stage of this wave: x[rows][k0 .. k0+31] and W[k0 .. k0+31][tile columns].
+// Direct global -> LDS load of 16 bytes per lane: lane i's bytes land at LDS address
+// m0 + 16 i.  Issued from asm so that the compiler adds no wait of its own for it: its
+// tracking of these loads cannot always tell the ring's stages apart and then waited for
+// every load in flight (vmcnt 0) before reading a stage; the waits here are the explicit
+// per-stage ones.  One wait state must separate the write of m0 from the load.
+__device__ __forceinline__ void dma16(const void *g, const lds_void_t *l) {
+    const uint32_t m = (uint32_t)(uintptr_t)l;
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m)
+                 : "memory", "m0");
+}
+
+// One stage of this wave: x[rows][k0 .. k0+31] and rows k0 .. k0+31 of the 64-column tile
+// (row stride ldw).
 template <class C>
 __device__ __forceinline__ void dec_issue(const DecSrc<C> &src, uint4 *__restrict__ xslot,
-                                          uint4 *__restrict__ wslot, int k0, int N) {
+                                          uint4 *__restrict__ wslot, int k0, size_t ldw) {
 #pragma unroll
-    for (int q = 0; q < C::XINS; ++q)
-        __builtin_amdgcn_global_load_lds((const void *)(src.xp[q] + k0), (lds_void_t *)&xslot[q * 64], 16, 0, 0);
+    for (int q = 0; q < C::XINS; ++q) dma16(src.xp[q] + k0, (const lds_void_t *)&xslot[q * 64]);
 #pragma unroll
-    for (int q = 0; q < C::WINS; ++q)
-        __builtin_amdgcn_global_load_lds((const void *)(src.wp[q] + (size_t)k0 * N), (lds_void_t *)&wslot[q * 64], 16, 0, 0);
+    for (int q = 0; q < C::WINS; ++q) dma16(src.wp[q] + (size_t)k0 * ldw, (const lds_void_t *)&wslot[q * 64]);
 }
 
 // Cross-wave reduction: each wave's accumulators go to LDS (accumulator layout, lane-minor)
@@ -150,18 +161,26 @@ __device__ __forceinline__ void reduce_waves_sum(const float *r0, const float *r
     }
 }
 
-// Workgroup (tile, split), eight waves (four without the shrink).  Waves 0-3 stream split
-// `split` of K (rows [split k_per_split, +k_per_split)) and write its partial tile;
-// reduce_lora_kernel adds the splits in order.  With with_shrink (M <= kDecodeMaxRows),
-// waves 4-7, side by side on the same CU, run the shrink's work items
-// blockIdx.x * 2 + (wave - 4) / 2, stepping by 2 gridDim.x (a pair per item, rows of parity
-// wave % 2); without it the shrink's chunk sums come from the segment-path shrink.
+// Column tiles: n_tn tiles of W, then n_lt adapter tiles.  Adapter "slots" are numbered
+// 0 .. T-1: with a pool no larger than the batch, slot = adapter id (T = n_adapters), else
+// the batch's distinct adapters in order of first use (batch_adapters.h).  Adapter tile lt
+// holds slots lt * APT .. lt * APT + APT - 1, each r_max columns wide.
+template <int RM>
+struct AdapterTiles {
+    static_assert(RM == 8 || RM == 16 || RM == 32 || RM == 64, "rank bucket");
+    static constexpr int APT = kBN / RM;  // adapters per tile
+};
+
+// Workgroup (tile, split), four waves.  Each wave streams its quarter of split `split` of K
+// (rows [split k_per_split, +k_per_split)) for one 64-column tile -- of W, or of the
+// adapters' A laid side by side -- and the workgroup writes its partial tile;
+// reduce_lora_kernel adds the splits in order.
 template <class C, int RM>
-__global__ __launch_bounds__(kBlock) void decode_gemm_kernel(
+__global__ __launch_bounds__(kThreads) void decode_gemm_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ W, const uint16_t *__restrict__ A,
-    int M, int K, int N, int n_tm, int n_tn, int k_per_split, float *__restrict__ partial,
-    DecodeLora lo, int with_shrink) {
-    // stage s of GEMM wave w: X{s}[w * XSLOT ..], W{s}[w * WSLOT ..]
+    int M, int K, int N, int n_tm, int n_tn, int n_lt, int k_per_split, float *__restrict__ partial,
+    DecodeLora lo) {
+    // stage s of wave w: X{s}[w * XSLOT ..], W{s}[w * WSLOT ..]
     __shared__ __attribute__((aligned(1024))) uint4 XS0[kWaves * C::XSLOT];
     __shared__ __attribute__((aligned(1024))) uint4 XS1[kWaves * C::XSLOT];
     __shared__ __attribute__((aligned(1024))) uint4 XS2[kWaves * C::XSLOT];
@@ -171,20 +190,62 @@ __global__ __launch_bounds__(kBlock) void decode_gemm_kernel(
     __shared__ __attribute__((aligned(1024))) uint4 WS2[kWaves * C::WSLOT];
     __shared__ __attribute__((aligned(1024))) uint4 WS3[kWaves * C::WSLOT];
     __shared__ BatchAdapters ba;
+    constexpr int APT = AdapterTiles<RM>::APT;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int n_tiles = n_tm * n_tn;
+    const int n_cols = n_tn + n_lt;
+    const int n_tiles = n_tm * n_cols;
     // block -> (split, column tile, row tile).  With two row tiles, row tile fastest over
     // consecutive blocks of one XCD (workgroup b runs on XCD b % 8), so both read a W column
     // panel through that XCD's L2
     int lin = blockIdx.x;
     if (n_tm > 1 && (gridDim.x & 7) == 0) lin = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
     const int tile = lin % n_tiles, split = lin / n_tiles;
-    // shrink items name adapters directly when the pool is no larger than the batch (rows
-    // found by a ballot over ids), else through the batch's distinct adapters in LDS
-    const bool by_id = lo.n_adapters <= M;
-    if (with_shrink && !by_id) batch_adapters(ba, lo.ids, M, lo.n_adapters);  // every thread: barriers
+    const int tm = tile % n_tm, tn = tile / n_tm;
+    const int m0 = tm * C::BM;
+
+    // per-lane sources of the 64-column tile: W, or the adapters of this adapter tile
+    DecSrc<C> src;
+    size_t ldw = (size_t)N;
+    if (tn < n_tn) {
+        const int n0 = tn * kBN;
+#pragma unroll
+        for (int q = 0; q < C::WINS; ++q) {
+            const int r = 8 * q + (lane >> 3);
+            const int lc = (lane & 7) ^ wsw(r);
+            src.wp[q] = W + (size_t)r * N + min(n0 + lc * 8, N - 8);
+        }
+    } else {
+        const int lt = tn - n_tn;
+        const bool by_id = lo.n_adapters <= M;
+        int T = lo.n_adapters;
+        if (!by_id) {
+            batch_adapters(ba, lo.ids, M, lo.n_adapters);  // every thread: barriers
+            T = ba.T;
+            // one workgroup leaves the row -> slot map for the reduction
+            if (lt == 0 && split == 0 && tm == 0)
+                for (int m = tid; m < M; m += kThreads) lo.slots[m] = ba.slot[m];
+        }
+        if (lt * APT >= T) return;  // no adapter of the batch in this tile (whole workgroup)
+#pragma unroll
+        for (int q = 0; q < C::WINS; ++q) {
+            const int r = 8 * q + (lane >> 3);
+            const int col = ((lane & 7) ^ wsw(r)) * 8;
+            const int sl = lt * APT + col / RM;
+            // slots past the last read a valid adapter; their columns are never used
+            const int a = sl < T ? (by_id ? sl : ba.list[sl]) : (by_id ? 0 : ba.list[0]);
+            src.wp[q] = A + ((size_t)a * K + r) * RM + col % RM;
+        }
+        ldw = RM;
+    }
+#pragma unroll
+    for (int q = 0; q < C::XINS; ++q) {
+        const int row = 16 * q + (lane >> 2);
+        const int lc = (lane & 3) ^ ((lane >> 4) & 3);
+        const int m = min(m0 + row, M - 1);
+        src.xp[q] = x + (size_t)m * K + lc * 8;
+    }
 
     f32x16_t acc[C::TM][C::TN];
 #pragma unroll
@@ -194,103 +255,61 @@ __global__ __launch_bounds__(kBlock) void decode_gemm_kernel(
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-    if (wave < kWaves) {
-        // ---- x W over this wave's part of the split's K range ------------------------------
-        const int tm = tile % n_tm, tn = tile / n_tm;
-        const int m0 = tm * C::BM, n0 = tn * kBN;
-        DecSrc<C> src;
-#pragma unroll
-        for (int q = 0; q < C::XINS; ++q) {
-            const int row = 16 * q + (lane >> 2);
-            const int lc = (lane & 3) ^ ((lane >> 4) & 3);
-            const int m = min(m0 + row, M - 1);
-            src.xp[q] = x + (size_t)m * K + lc * 8;
-        }
-#pragma unroll
-        for (int q = 0; q < C::WINS; ++q) {
-            const int r = 8 * q + (lane >> 3);
-            const int lc = (lane & 7) ^ wsw(r);
-            src.wp[q] = W + (size_t)r * N + min(n0 + lc * 8, N - 8);
-        }
-        const int xo = wave * C::XSLOT, wo = wave * C::WSLOT;
-        const int ks0 = split * k_per_split;
-        const int ks1 = min(K, ks0 + k_per_split);
-        const int per_wave = k_per_split / kWaves;  // multiple of 32
-        const int kw0 = min(ks1, ks0 + wave * per_wave);
-        const int kw1 = min(ks1, kw0 + per_wave);
-        const int nst = (kw1 - kw0) / kBK;
-        // k of stage s (stages past the last reload the last one; an empty range loads k=0)
+    const int xo = wave * C::XSLOT, wo = wave * C::WSLOT;
+    const int ks0 = split * k_per_split;
+    const int ks1 = min(K, ks0 + k_per_split);
+    const int per_wave = k_per_split / kWaves;  // multiple of 32
+    const int kw0 = min(ks1, ks0 + wave * per_wave);
+    const int kw1 = min(ks1, kw0 + per_wave);
+    const int nst = (kw1 - kw0) / kBK;
+    // k of stage s (stages past the last reload the last one; an empty range loads k=0)
 #define KLOAD(S) (nst > 0 ? kw0 + min((S), nst - 1) * kBK : 0)
-        dec_issue<C>(src, XS0 + xo, WS0 + wo, KLOAD(0), N);
-        dec_issue<C>(src, XS1 + xo, WS1 + wo, KLOAD(1), N);
-        dec_issue<C>(src, XS2 + xo, WS2 + wo, KLOAD(2), N);
-#define DEC_STEP(SS, XC, WC, XN, WN)                                   \
-        wait_vm<2 * C::PER>();                                         \
-        wait_lgkm0();                                                  \
-        dec_issue<C>(src, XN + xo, WN + wo, KLOAD((SS) + 3), N);       \
-        if ((SS) < nst) dec_mfma<C>(acc, XC + xo, WC + wo, lane);
-        for (int s = 0; s < nst; s += 4) {
-            DEC_STEP(s, XS0, WS0, XS3, WS3)
-            DEC_STEP(s + 1, XS1, WS1, XS0, WS0)
-            DEC_STEP(s + 2, XS2, WS2, XS1, WS1)
-            DEC_STEP(s + 3, XS3, WS3, XS2, WS2)
-        }
+    dec_issue<C>(src, XS0 + xo, WS0 + wo, KLOAD(0), ldw);
+    dec_issue<C>(src, XS1 + xo, WS1 + wo, KLOAD(1), ldw);
+    dec_issue<C>(src, XS2 + xo, WS2 + wo, KLOAD(2), ldw);
+#define DEC_STEP(SS, XC, WC, XN, WN)                               \
+    wait_vm<2 * C::PER>();                                         \
+    wait_lgkm0();                                                  \
+    dec_issue<C>(src, XN + xo, WN + wo, KLOAD((SS) + 3), ldw);     \
+    if ((SS) < nst) dec_mfma<C>(acc, XC + xo, WC + wo, lane);
+    for (int s = 0; s < nst; s += 4) {
+        DEC_STEP(s, XS0, WS0, XS3, WS3)
+        DEC_STEP(s + 1, XS1, WS1, XS0, WS0)
+        DEC_STEP(s + 2, XS2, WS2, XS1, WS1)
+        DEC_STEP(s + 3, XS3, WS3, XS2, WS2)
+    }
 #undef DEC_STEP
 #undef KLOAD
-        wait_vm<0>();
-    } else {
-        // ---- the shrink's work items ---------------------------------------------------------
-        const int pair = (wave - kWaves) >> 1;
-        int idq[kRowWords];
-#pragma unroll
-        for (int q = 0; q < kRowWords; ++q) idq[q] = by_id && lane + 64 * q < M ? lo.ids[lane + 64 * q] : -1;
-        const uint64_t par = (wave & 1) ? 0xAAAAAAAAAAAAAAAAull : 0x5555555555555555ull;
-        const int n_items = lo.n_chunks * (by_id ? lo.n_adapters : ba.T);
-        for (int w = blockIdx.x * 2 + pair; w < n_items; w += gridDim.x * 2) {
-            const int c = w % lo.n_chunks, s = w / lo.n_chunks;
-            const int a = by_id ? s : ba.list[s];
-            RowMask mk;
-            uint64_t any = 0;
-#pragma unroll
-            for (int q = 0; q < kRowWords; ++q) {
-                const int m = lane + 64 * q;
-                const uint64_t r = by_id ? __ballot(idq[q] == a) : __ballot(m < M && ba.slot[m] == s);
-                any |= r;
-                mk.w[q] = r & par;
-            }
-            if (any == 0) continue;  // an adapter of the pool without rows in the batch
-            decode_shrink_item<RM>(x, A, M, K, c, a, mk, lane, lo.tpart);
-        }
-    }
-    __syncthreads();  // every GEMM wave is done with the W stages
+    wait_vm<0>();
+    __syncthreads();  // every wave is done with the stages
 
     float *red = reinterpret_cast<float *>(wave == 0 ? WS0 : wave == 1 ? WS1 : wave == 2 ? WS2 : WS3);
-    if (wave < kWaves) reduce_waves_put<C>(acc, red, lane);
+    reduce_waves_put<C>(acc, red, lane);
     __syncthreads();
-    if (wave < kWaves) {
-        float sum[C::BM / 4];
-        reduce_waves_sum<C>(reinterpret_cast<const float *>(WS0), reinterpret_cast<const float *>(WS1),
-                            reinterpret_cast<const float *>(WS2), reinterpret_cast<const float *>(WS3),
-                            lane, wave, sum);
-        float *mine = partial + ((size_t)split * n_tiles + tile) * C::TILE;
+    float sum[C::BM / 4];
+    reduce_waves_sum<C>(reinterpret_cast<const float *>(WS0), reinterpret_cast<const float *>(WS1),
+                        reinterpret_cast<const float *>(WS2), reinterpret_cast<const float *>(WS3),
+                        lane, wave, sum);
+    float *mine = partial + ((size_t)split * n_tiles + tile) * C::TILE;
 #pragma unroll
-        for (int q = 0; q < C::BM / 4; ++q) mine[(wave + 4 * q) * kBN + lane] = sum[q];
-    }
+    for (int q = 0; q < C::BM / 4; ++q) mine[(wave + 4 * q) * kBN + lane] = sum[q];
 }
 
 // y[m, n .. n+3] = (sum over splits, in order, of the partial tiles)
 //                  + scale_a * sum_j t[m, j] B_a[j, n .. n+3]   (a = ids[m], when valid)
-// with t[m, j] = sum over the shrink's chunks, in order, of tpart[c][m][j].  Block (column
-// chunk of 1024, row m), 256 threads x 4 columns.  The partial and B loads are issued
-// before t is summed, so their latency overlaps it.
+// with t[m, j] the sum, in order, of n_t parts tsrc[c * t_stride + ...]: the splits of row
+// m's adapter tile (n_lt > 0), or the segment-path shrink's chunk sums tpart[c][m][j]
+// (n_lt == 0).  Block (column chunk of 1024, row m), 256 threads x 4 columns.  The partial
+// and B loads are issued before t is summed, so their latency overlaps it.
 template <int BM, int RM, bool YF32>
 __global__ __launch_bounds__(256) void reduce_lora_kernel(const float *__restrict__ partial,
                                                           int M, int N, int n_tm, int n_tn,
-                                                          int n_splits, DecodeLora lo,
+                                                          int n_lt, int n_splits, DecodeLora lo,
                                                           void *__restrict__ y) {
     constexpr int kMaxSplits = 16;
+    constexpr int APT = AdapterTiles<RM>::APT;
     __shared__ float s_t[RM];
-    constexpr int kTpartMax = 8192;  // n_chunks x RM floats staged in LDS
+    constexpr int kTpartMax = 8192;  // n_t x RM floats staged in LDS
     const int m = blockIdx.y;
     const int n = (blockIdx.x * 256 + threadIdx.x) * 4;
     const bool col_ok = n < N;
@@ -298,10 +317,11 @@ __global__ __launch_bounds__(256) void reduce_lora_kernel(const float *__restric
     const int id = lo.ids[m];
     const bool has = id >= 0 && id < lo.n_adapters;
     const int a = has ? id : 0;
+    const int n_tiles = n_tm * (n_tn + n_lt);
+    const size_t stride = (size_t)n_tiles * BM * kBN;  // one split of the partial tiles
 
     // split partials of (m, nc .. nc+3)
     const int tile = (m / BM) + (nc / kBN) * n_tm;
-    const size_t stride = (size_t)n_tm * n_tn * BM * kBN;
     const float *pp = partial + (size_t)tile * BM * kBN + (m % BM) * kBN + (nc % kBN);
     float4 pv[kMaxSplits];
 #pragma unroll
@@ -314,22 +334,36 @@ __global__ __launch_bounds__(256) void reduce_lora_kernel(const float *__restric
     const uint16_t *bp = lo.B + (size_t)a * RM * N + nc;
 #pragma unroll
     for (int j = 0; j < RM; ++j) bv[j] = *reinterpret_cast<const uint2 *>(bp + (size_t)min(j, r - 1) * N);
-    // t[m, j] = sum over chunks c, in order, of tpart[c][m][j]: the block loads the
-    // n_chunks x RM values at once (one or a few per thread) into LDS, then thread j adds
-    // its column in chunk order (for very long d_in, thread j reads its column directly)
+    // where the parts of t[m, :] are
+    const float *tsrc;
+    size_t t_stride;
+    int n_t;
+    if (n_lt > 0) {
+        const int sl = !has ? 0 : lo.n_adapters <= M ? id : lo.slots[m];
+        const int ttile = (m / BM) + (n_tn + sl / APT) * n_tm;
+        tsrc = partial + (size_t)ttile * BM * kBN + (m % BM) * kBN + (sl % APT) * RM;
+        t_stride = stride;
+        n_t = n_splits;
+    } else {
+        tsrc = lo.tpart + (size_t)m * RM;
+        t_stride = (size_t)M * RM;
+        n_t = lo.n_chunks;
+    }
+    // t[m, j] = sum over parts c, in order: the block loads the n_t x RM values at once (one
+    // or a few per thread) into LDS, then thread j adds its column in order (for very many
+    // parts, thread j reads its column directly)
     __shared__ float s_tp[kTpartMax];
-    const size_t cs = (size_t)M * RM;
-    const int nv = lo.n_chunks * RM;
+    const int nv = n_t * RM;
     const bool staged = nv <= kTpartMax;
     if (has && staged)
-        for (int v = threadIdx.x; v < nv; v += 256) s_tp[v] = lo.tpart[(v / RM) * cs + (size_t)m * RM + v % RM];
+        for (int v = threadIdx.x; v < nv; v += 256) s_tp[v] = tsrc[(v / RM) * t_stride + v % RM];
     __syncthreads();
     if (has && threadIdx.x < RM) {
         float t = 0.0f;
         if (staged) {
-            for (int c = 0; c < lo.n_chunks; ++c) t += s_tp[c * RM + threadIdx.x];
+            for (int c = 0; c < n_t; ++c) t += s_tp[c * RM + threadIdx.x];
         } else {
-            for (int c = 0; c < lo.n_chunks; ++c) t += lo.tpart[c * cs + (size_t)m * RM + threadIdx.x];
+            for (int c = 0; c < n_t; ++c) t += tsrc[c * t_stride + threadIdx.x];
         }
         s_t[threadIdx.x] = t;
     }
@@ -366,16 +400,24 @@ __global__ __launch_bounds__(256) void reduce_lora_kernel(const float *__restric
 }
 
 struct DecPlan {
-    int bm, n_tm, n_tn, ks, k_per_split;  // ks splits of K per tile
+    int bm, n_tm, n_tn, n_lt, ks, k_per_split;  // ks splits of K per tile
 };
 
+// Adapter tiles of a fused call (0 when the call has none).
+int adapter_tiles(int M, int r_max, int n_adapters) {
+    const int apt = kBN / r_max;
+    const int slots = n_adapters < M ? n_adapters : M;
+    return (slots + apt - 1) / apt;
+}
+
 // Splits of K per tile so that tiles x splits fills the 256 CUs once (at most 16 splits).
-DecPlan dec_plan(int M, int K, int N) {
+DecPlan dec_plan(int M, int K, int N, int n_lt) {
     DecPlan p;
     p.bm = M <= 32 ? 32 : 64;
     p.n_tm = (M + p.bm - 1) / p.bm;
     p.n_tn = (N + kBN - 1) / kBN;
-    const long tiles = (long)p.n_tm * p.n_tn;
+    p.n_lt = n_lt;
+    const long tiles = (long)p.n_tm * (p.n_tn + n_lt);
     const int kq = K / (kBK * kWaves);  // whole 128-deep quanta (K >= 128)
     int ks = (int)(256 / tiles);
     if (ks < 1) ks = 1;
@@ -386,6 +428,8 @@ DecPlan dec_plan(int M, int K, int N) {
     p.ks = (K + p.k_per_split - 1) / p.k_per_split;
     return p;
 }
+
+bool rank_ok(int r_max) { return r_max == 8 || r_max == 16 || r_max == 32 || r_max == 64; }
 
 }  // namespace
 
@@ -398,37 +442,32 @@ bool decode_fused_supported(int M, int K, int N) {
     return decode_gemm_supported(M, K, N) && M <= kDecodeMaxRows;
 }
 
-size_t decode_gemm_partial_floats(int M, int K, int N) {
-    if (!decode_gemm_supported(M, K, N)) return 0;
-    const DecPlan p = dec_plan(M, K, N);
-    return (size_t)p.ks * p.n_tm * p.n_tn * p.bm * kBN;
-}
-
-int decode_shrink_chunks(int K, int r_max) {
-    const int kc = decode_shrink_chunk_k(r_max);
-    return (K + kc - 1) / kc;
+size_t decode_gemm_partial_floats(int M, int K, int N, int r_max, int n_adapters) {
+    if (!decode_gemm_supported(M, K, N) || !rank_ok(r_max)) return 0;
+    const int n_lt = decode_fused_supported(M, K, N) ? adapter_tiles(M, r_max, n_adapters) : 0;
+    const DecPlan p = dec_plan(M, K, N, n_lt);
+    return (size_t)p.ks * p.n_tm * (p.n_tn + p.n_lt) * p.bm * kBN;
 }
 
 hipError_t launch_decode_gemm(const uint16_t *x, const uint16_t *W, const uint16_t *A, int M,
-                              int K, int N, const DecodeLora &lo, bool with_shrink, float *partial,
+                              int K, int N, const DecodeLora &lo, bool adapters, float *partial,
                               hipStream_t s) {
-    if (!decode_gemm_supported(M, K, N) || partial == nullptr || lo.tpart == nullptr ||
-        lo.n_chunks != decode_shrink_chunks(K, lo.r_max) || (with_shrink && M > kDecodeMaxRows))
+    if (!decode_gemm_supported(M, K, N) || partial == nullptr || !rank_ok(lo.r_max) ||
+        (adapters && (M > kDecodeMaxRows || A == nullptr || lo.ids == nullptr ||
+                      (lo.n_adapters > M && lo.slots == nullptr))))
         return hipErrorInvalidValue;
-    const DecPlan p = dec_plan(M, K, N);
-    const dim3 grid(p.n_tm * p.n_tn * p.ks);
-    const dim3 block(with_shrink ? kBlock : kThreads);
-    const int ws = with_shrink ? 1 : 0;
+    const int n_lt = adapters ? adapter_tiles(M, lo.r_max, lo.n_adapters) : 0;
+    const DecPlan p = dec_plan(M, K, N, n_lt);
+    const dim3 grid(p.n_tm * (p.n_tn + p.n_lt) * p.ks);
 #define GEMM_LAUNCH(BM, RMX)                                                                  \
-    launch((decode_gemm_kernel<Dec<BM>, RMX>), grid, block, 0, s, x, W, A, M, K, N, p.n_tm,    \
-           p.n_tn, p.k_per_split, partial, lo, ws)
+    launch((decode_gemm_kernel<Dec<BM>, RMX>), grid, dim3(kThreads), 0, s, x, W, A, M, K, N,   \
+           p.n_tm, p.n_tn, p.n_lt, p.k_per_split, partial, lo)
 #define GEMM_RANK(BM)                                                                         \
     switch (lo.r_max) {                                                                       \
         case 8: GEMM_LAUNCH(BM, 8); break;                                                    \
         case 16: GEMM_LAUNCH(BM, 16); break;                                                  \
         case 32: GEMM_LAUNCH(BM, 32); break;                                                  \
-        case 64: GEMM_LAUNCH(BM, 64); break;                                                  \
-        default: return hipErrorInvalidValue;                                                 \
+        default: GEMM_LAUNCH(BM, 64); break;                                                  \
     }
     if (p.bm == 32) {
         GEMM_RANK(32)
@@ -441,15 +480,17 @@ hipError_t launch_decode_gemm(const uint16_t *x, const uint16_t *W, const uint16
 }
 
 hipError_t launch_decode_reduce(const float *partial, int M, int K, int N, void *y, bool y_f32,
-                                const DecodeLora &lo, hipStream_t s) {
-    if (!decode_gemm_supported(M, K, N) || partial == nullptr || lo.tpart == nullptr ||
-        (lo.r_max != 8 && lo.r_max != 16 && lo.r_max != 32 && lo.r_max != 64))
+                                const DecodeLora &lo, bool adapters, hipStream_t s) {
+    if (!decode_gemm_supported(M, K, N) || partial == nullptr || !rank_ok(lo.r_max) ||
+        (adapters && lo.n_adapters > M && lo.slots == nullptr) ||
+        (!adapters && (lo.tpart == nullptr || lo.n_chunks < 1)))
         return hipErrorInvalidValue;
-    const DecPlan p = dec_plan(M, K, N);
+    const int n_lt = adapters ? adapter_tiles(M, lo.r_max, lo.n_adapters) : 0;
+    const DecPlan p = dec_plan(M, K, N, n_lt);
     const dim3 rgrid((unsigned)((N + 1023) / 1024), (unsigned)M);
 #define RED_LAUNCH(BM, RMX, YF)                                                             \
     launch((reduce_lora_kernel<BM, RMX, YF>), rgrid, dim3(256), 0, s, partial, M, N, p.n_tm,    \
-           p.n_tn, p.ks, lo, y)
+           p.n_tn, p.n_lt, p.ks, lo, y)
 #define RED_RANK(BM, YF)                                                                    \
     switch (lo.r_max) {                                                                     \
         case 8: RED_LAUNCH(BM, 8, YF); break;                                               \

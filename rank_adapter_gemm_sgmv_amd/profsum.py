@@ -25,12 +25,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 
 # kernel function name -> name of the step in lora_linear_profiled / bench.py
 _STEP_OF_KERNEL = [
-    ("decode_gemm_kernel", "decode_gemm_shrink"),
+    ("decode_gemm_kernel", "decode_gemm_lora"),
     ("reduce_lora_kernel", "decode_reduce_lora"),
     ("build_segments_kernel", "build_segments"),
+    ("build_segments_small_kernel", "build_segments"),
     ("shrink_finalize_kernel", "shrink_finalize"),
-    ("shrink_lds_kernel", "shrink"),
-    ("shrink_reg_kernel", "shrink"),
+    ("shrink_mfma_kernel", "shrink"),
     ("splitk_reduce_kernel", "splitk_reduce"),
     ("expand_kernel", "expand"),
     ("gemm_big_kernel", "gemm"),
@@ -56,13 +56,17 @@ def short_name(n: str) -> str:
     return n.replace("lora::", "")[:90]
 
 
-def step_of(kernel_name: str, mode: str):
+def step_of(kernel_name: str, mode: str, separate_shrink: bool = False):
+    """Step of a kernel; the decode GEMM is "decode_gemm" where a separate shrink kernel
+    ran beside it (batches of 129-256 rows), else the fused "decode_gemm_lora"."""
     base = short_name(kernel_name)
     fn = base.split("<")[0]
     for k, step in _STEP_OF_KERNEL:
         if fn == k:
             if step == "gemm":
                 return "gemm_prefill_lora" if mode == "prefill" else "gemm_decode"
+            if step == "decode_gemm_lora" and separate_shrink:
+                return "decode_gemm"
             return step
     return None
 
@@ -107,8 +111,9 @@ def counters_table(fetch_csv, write_csv, workload, mode, calib_bytes, fetch_cmd,
 
     def by_step(rows):
         d = {}
+        sep = any(step_of(n, mode) == "shrink" for n, _ in rows)
         for n, v in rows:
-            s = step_of(n, mode)
+            s = step_of(n, mode, sep)
             if s is not None:
                 d.setdefault(s, []).append(v)
         return d
