@@ -49,16 +49,18 @@ constexpr int kBK = 32;
 constexpr int kWaves = 4;                // waves streaming x W
 constexpr int kThreads = 64 * kWaves;
 
+// A wave's W stages are 32 rows deep (4 in its ring); its x stages are 64 deep (2 in its
+// ring), so that one direct load covers 8 whole 128-byte rows of x rather than 16 half rows:
+// x costs as few memory requests per byte as W.
 template <int BM_>
 struct Dec {
     static constexpr int BM = BM_;
     static constexpr int TM = BM / 32, TN = kBN / 32;
-    static constexpr int XSLOT = BM * kBK * 2 / 16;  // uint4 per wave per stage (x)
-    static constexpr int WSLOT = kBK * kBN * 2 / 16; // uint4 per wave per stage (W)
-    static constexpr int XINS = XSLOT / 64;          // DMA instructions per wave per stage
-    static constexpr int WINS = WSLOT / 64;
-    static constexpr int PER = XINS + WINS;
-    static constexpr int TILE = BM * kBN;             // floats per tile
+    static constexpr int XSLOT = BM * 2 * kBK * 2 / 16;  // uint4 per wave per x stage (64 deep)
+    static constexpr int WSLOT = kBK * kBN * 2 / 16;     // uint4 per wave per W stage
+    static constexpr int XINS = XSLOT / 64;              // direct loads per x stage
+    static constexpr int WINS = WSLOT / 64;              // direct loads per W stage
+    static constexpr int TILE = BM * kBN;                 // floats per tile
     static_assert(BM == 32 || BM == 64, "decode tile rows");
     static_assert(TILE <= kWaves * WSLOT * 4, "a wave's partial tile fits one W stage array");
 };
@@ -75,9 +77,11 @@ __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F
 // the two 16-lane groups read together, fall on distinct banks.
 __device__ __forceinline__ int wsw(int r) { return ((r >> 1) & 1) << 2; }
 
+// x stage rows are 128 bytes (8 chunks of 16 bytes); chunk c of row r is stored at c ^ (r % 8).
+// `half` picks k 0..31 or 32..63 of the stage.
 template <class C>
 __device__ __forceinline__ void dec_mfma(f32x16_t (&acc)[C::TM][C::TN], const uint4 *__restrict__ xs,
-                                         const uint4 *__restrict__ ws, int lane) {
+                                         int half, const uint4 *__restrict__ ws, int lane) {
     const lds_char_t *wsb = (const lds_char_t *)(ws);
     const int g = lane >> 4, li = lane & 15;
 #pragma unroll
@@ -86,8 +90,8 @@ __device__ __forceinline__ void dec_mfma(f32x16_t (&acc)[C::TM][C::TN], const ui
 #pragma unroll
         for (int i = 0; i < C::TM; ++i) {
             const int row = 32 * i + (lane & 31);
-            const int lc = 2 * kk + (lane >> 5);
-            af[i] = *reinterpret_cast<const bf16x8_t *>(&xs[row * 4 + (lc ^ ((row >> 2) & 3))]);
+            const int lc = 4 * half + 2 * kk + (lane >> 5);
+            af[i] = *reinterpret_cast<const bf16x8_t *>(&xs[row * 8 + (lc ^ (row & 7))]);
         }
 #pragma unroll
         for (int j = 0; j < C::TN; ++j) {
@@ -124,15 +128,18 @@ __device__ __forceinline__ void dma16(const void *g, const lds_void_t *l) {
                  : "memory", "m0");
 }
 
-// One stage of this wave: x[rows][k0 .. k0+31] and rows k0 .. k0+31 of the 64-column tile
-// (row stride ldw).
+// A W stage of this wave: rows k0 .. k0+31 of the 64-column tile (row stride ldw).
 template <class C>
-__device__ __forceinline__ void dec_issue(const DecSrc<C> &src, uint4 *__restrict__ xslot,
-                                          uint4 *__restrict__ wslot, int k0, size_t ldw) {
-#pragma unroll
-    for (int q = 0; q < C::XINS; ++q) dma16(src.xp[q] + k0, (const lds_void_t *)&xslot[q * 64]);
+__device__ __forceinline__ void dec_issue_w(const DecSrc<C> &src, uint4 *__restrict__ wslot, int k0,
+                                            size_t ldw) {
 #pragma unroll
     for (int q = 0; q < C::WINS; ++q) dma16(src.wp[q] + (size_t)k0 * ldw, (const lds_void_t *)&wslot[q * 64]);
+}
+// An x stage of this wave: x[rows][k0 .. k0+63].
+template <class C>
+__device__ __forceinline__ void dec_issue_x(const DecSrc<C> &src, uint4 *__restrict__ xslot, int k0) {
+#pragma unroll
+    for (int q = 0; q < C::XINS; ++q) dma16(src.xp[q] + k0, (const lds_void_t *)&xslot[q * 64]);
 }
 
 // Cross-wave reduction: each wave's accumulators go to LDS (accumulator layout, lane-minor)
@@ -180,11 +187,9 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ W, const uint16_t *__restrict__ A,
     int M, int K, int N, int n_tm, int n_tn, int n_lt, int k_per_split, float *__restrict__ partial,
     DecodeLora lo) {
-    // stage s of wave w: X{s}[w * XSLOT ..], W{s}[w * WSLOT ..]
+    // x stage u of wave w: X{u % 2}[w * XSLOT ..]; W stage s: W{s % 4}[w * WSLOT ..]
     __shared__ __attribute__((aligned(1024))) uint4 XS0[kWaves * C::XSLOT];
     __shared__ __attribute__((aligned(1024))) uint4 XS1[kWaves * C::XSLOT];
-    __shared__ __attribute__((aligned(1024))) uint4 XS2[kWaves * C::XSLOT];
-    __shared__ __attribute__((aligned(1024))) uint4 XS3[kWaves * C::XSLOT];
     __shared__ __attribute__((aligned(1024))) uint4 WS0[kWaves * C::WSLOT];
     __shared__ __attribute__((aligned(1024))) uint4 WS1[kWaves * C::WSLOT];
     __shared__ __attribute__((aligned(1024))) uint4 WS2[kWaves * C::WSLOT];
@@ -241,9 +246,10 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(
     }
 #pragma unroll
     for (int q = 0; q < C::XINS; ++q) {
-        const int row = 16 * q + (lane >> 2);
-        const int lc = (lane & 3) ^ ((lane >> 4) & 3);
-        const int m = min(m0 + row, M - 1);
+        // lane l fills position l % 8 of row 8 q + l / 8: chunk (l % 8) ^ (l / 8)
+        const int row = 8 * q + (lane >> 3);
+        const int lc = (lane & 7) ^ (lane >> 3);
+        const int m = min(m0 + row, M - 1);  // rows past the batch repeat its last
         src.xp[q] = x + (size_t)m * K + lc * 8;
     }
 
@@ -262,24 +268,41 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(
     const int kw0 = min(ks1, ks0 + wave * per_wave);
     const int kw1 = min(ks1, kw0 + per_wave);
     const int nst = (kw1 - kw0) / kBK;
-    // k of stage s (stages past the last reload the last one; an empty range loads k=0)
-#define KLOAD(S) (nst > 0 ? kw0 + min((S), nst - 1) * kBK : 0)
-    dec_issue<C>(src, XS0 + xo, WS0 + wo, KLOAD(0), ldw);
-    dec_issue<C>(src, XS1 + xo, WS1 + wo, KLOAD(1), ldw);
-    dec_issue<C>(src, XS2 + xo, WS2 + wo, KLOAD(2), ldw);
-#define DEC_STEP(SS, XC, WC, XN, WN)                               \
-    wait_vm<2 * C::PER>();                                         \
-    wait_lgkm0();                                                  \
-    dec_issue<C>(src, XN + xo, WN + wo, KLOAD((SS) + 3), ldw);     \
-    if ((SS) < nst) dec_mfma<C>(acc, XC + xo, WC + wo, lane);
+    // W stage s holds k = KW(s), x stage u holds k = KX(u) .. +63; stages past the last
+    // reload the last one (an empty range loads k = 0), and an x stage that would run past K
+    // starts at K - 64 instead, its second half then holding the wave's last step
+    const int kxl = nst > 0 ? min(kw0 + ((nst - 1) >> 1) * 2 * kBK, K - 2 * kBK) : 0;
+#define KW(S) (nst > 0 ? kw0 + min((S), nst - 1) * kBK : 0)
+#define KX(U) (nst > 0 ? min(kw0 + (U) * 2 * kBK, kxl) : 0)
+    // Issue order: x(0), W(0), W(1), W(2); then step s issues x(s / 2 + 1) when s is even,
+    // and W(s + 3).  When step s starts, what was issued after the stages it needs is two W
+    // stages at an even step (after x(s / 2)), and two W stages and x(s / 2 + 1) at an odd
+    // step (after W(s)).
+    dec_issue_x<C>(src, XS0 + xo, KX(0));
+    dec_issue_w<C>(src, WS0 + wo, KW(0), ldw);
+    dec_issue_w<C>(src, WS1 + wo, KW(1), ldw);
+    dec_issue_w<C>(src, WS2 + wo, KW(2), ldw);
+#define DEC_EVEN(SS, XC, XN, WC, WN)                                                  \
+    wait_vm<2 * C::WINS>();                                                           \
+    wait_lgkm0();                                                                     \
+    dec_issue_x<C>(src, XN + xo, KX((SS) / 2 + 1));                                   \
+    dec_issue_w<C>(src, WN + wo, KW((SS) + 3), ldw);                                  \
+    if ((SS) < nst) dec_mfma<C>(acc, XC + xo, (kw0 + (SS) * kBK - KX((SS) / 2)) / kBK, WC + wo, lane);
+#define DEC_ODD(SS, XC, WC, WN)                                                       \
+    wait_vm<2 * C::WINS + C::XINS>();                                                 \
+    wait_lgkm0();                                                                     \
+    dec_issue_w<C>(src, WN + wo, KW((SS) + 3), ldw);                                  \
+    if ((SS) < nst) dec_mfma<C>(acc, XC + xo, (kw0 + (SS) * kBK - KX((SS) / 2)) / kBK, WC + wo, lane);
     for (int s = 0; s < nst; s += 4) {
-        DEC_STEP(s, XS0, WS0, XS3, WS3)
-        DEC_STEP(s + 1, XS1, WS1, XS0, WS0)
-        DEC_STEP(s + 2, XS2, WS2, XS1, WS1)
-        DEC_STEP(s + 3, XS3, WS3, XS2, WS2)
+        DEC_EVEN(s, XS0, XS1, WS0, WS3)
+        DEC_ODD(s + 1, XS0, WS1, WS0)
+        DEC_EVEN(s + 2, XS1, XS0, WS2, WS1)
+        DEC_ODD(s + 3, XS1, WS3, WS2)
     }
-#undef DEC_STEP
-#undef KLOAD
+#undef DEC_EVEN
+#undef DEC_ODD
+#undef KW
+#undef KX
     wait_vm<0>();
     __syncthreads();  // every wave is done with the stages
 
