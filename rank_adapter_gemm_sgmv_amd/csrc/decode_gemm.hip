@@ -233,6 +233,15 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(
                 for (int m = tid; m < M; m += kThreads) lo.slots[m] = ba.slot[m];
         }
         if (lt * APT >= T) return;  // no adapter of the batch in this tile (whole workgroup)
+        if (by_id) {
+            // numbered by id, a tile may hold only adapters no row of the batch uses
+            bool used = false;
+            for (int m = tid; m < M; m += kThreads) {
+                const int d = lo.ids[m] - lt * APT;
+                used |= d >= 0 && d < APT;
+            }
+            if (!__syncthreads_or(used)) return;  // whole workgroup
+        }
 #pragma unroll
         for (int q = 0; q < C::WINS; ++q) {
             const int r = 8 * q + (lane >> 3);
