@@ -10,22 +10,24 @@
 // the expand step).
 //
 // gfx950 design.  With one row per request, x W is bound by reading W once from HBM.
-//  * Output tile = BM rows (all of a small batch, padded to 32 or 64) x 64 columns; the K
+//  * Output tile = BM rows (all of a small batch, padded to 32 or 64) x 128 columns; the K
 //    range of each tile is split over `ks` workgroups (tiles x ks fills the 256 CUs once)
 //    and, inside a workgroup, over its four waves.  Each wave streams its own K sub-range
-//    through its own 4-stage LDS ring filled by direct global->LDS loads, so the K loop has
-//    no workgroup barrier at all: only this wave's s_waitcnt orders its loads and reads.
-//    Three stages (24 KiB per wave) are in flight.
-//  * x tile [BM][32] and W tile [32][64] per stage, XOR-swizzled; the W operand is read with
-//    the transposing LDS read (ds_read_b64_tr_b16); v_mfma_f32_32x32x16_bf16.
+//    through its own LDS ring filled by direct global->LDS loads, so the K loop has no
+//    workgroup barrier at all: only this wave's s_waitcnt orders its loads and reads.
+//  * Per wave: four W stages of 16 x 128 (256-byte rows) and two x stages of BM x 64
+//    (128-byte rows), XOR-swizzled, every direct load covering whole rows; the W operand is
+//    read with the transposing LDS read (ds_read_b64_tr_b16); v_mfma_f32_32x32x16_bf16.  A
+//    tile twice as wide as the MFMA needs reads each x byte for twice the W bytes, and the
+//    workgroup's memory traffic (W and x through the same CU) is what bounds it.
 //  * The LoRA shrink t = x A_a is the same kind of product: the batch's adapters, laid side
-//    by side, are 64 / r_max adapters per extra 64-column "adapter tile" whose rows are
+//    by side, are 128 / r_max adapters per extra "adapter tile" whose rows are
 //    A_a[k, 0:r_max] (row stride r_max instead of N).  Those tiles run in the same launch,
 //    split and streamed exactly like the W tiles, so every touched A_a is read from HBM
 //    once, at the same rate as W, with no latency chain of its own.  A tile computes t for
 //    every row of the batch against its adapters; the reduction keeps each row's own.
-//  * The four waves' partial tiles are added through LDS in wave order and each workgroup
-//    writes its partial tile.
+//  * The four waves' partial tiles are added through LDS in wave order (16-byte vectors of
+//    four rows) and each workgroup writes its partial tile.
 //  * reduce_lora_kernel then writes y[m, :] = (sum of the split partials, in split order)
 //    + scale_a * (t[m, :] B_a) with t[m, :] summed over the splits of row m's adapter tile,
 //    in split order, in fp32, rounded once into y's dtype; each touched B_a row slice is
@@ -44,25 +46,27 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4_t;
 typedef __attribute__((address_space(3))) char lds_char_t;
 
-constexpr int kBN = 64;
-constexpr int kBK = 32;
-constexpr int kWaves = 4;                // waves streaming x W
+constexpr int kBN = 128;  // columns of a tile
+constexpr int kBKW = 16;  // k of a W stage (one step)
+constexpr int kBKX = 64;  // k of an x stage (four steps)
+constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 
-// A wave's W stages are 32 rows deep (4 in its ring); its x stages are 64 deep (2 in its
-// ring), so that one direct load covers 8 whole 128-byte rows of x rather than 16 half rows:
-// x costs as few memory requests per byte as W.
+// Per wave: four W stages of 16 rows x 128 columns (256-byte rows, one direct load covers 4
+// whole rows) and two x stages of BM rows x 64 k (128-byte rows, 8 whole rows per load).  A
+// 128-column tile reads each x byte for twice the W bytes a 64-column tile did.
 template <int BM_>
 struct Dec {
     static constexpr int BM = BM_;
     static constexpr int TM = BM / 32, TN = kBN / 32;
-    static constexpr int XSLOT = BM * 2 * kBK * 2 / 16;  // uint4 per wave per x stage (64 deep)
-    static constexpr int WSLOT = kBK * kBN * 2 / 16;     // uint4 per wave per W stage
+    static constexpr int XSLOT = BM * kBKX * 2 / 16;     // uint4 per x stage
+    static constexpr int WSLOT = kBKW * kBN * 2 / 16;    // uint4 per W stage
     static constexpr int XINS = XSLOT / 64;              // direct loads per x stage
     static constexpr int WINS = WSLOT / 64;              // direct loads per W stage
+    static constexpr int WAVE = 2 * XSLOT + 4 * WSLOT;   // uint4 of LDS per wave
     static constexpr int TILE = BM * kBN;                 // floats per tile
     static_assert(BM == 32 || BM == 64, "decode tile rows");
-    static_assert(TILE <= kWaves * WSLOT * 4, "a wave's partial tile fits one W stage array");
+    static_assert(TILE * 4 <= WAVE * 16, "a wave's partial tile fits its part of the LDS");
 };
 
 template <int N>
@@ -72,43 +76,39 @@ __device__ __forceinline__ void wait_vm() {
 }
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
-// W tile rows are 128 bytes (8 chunks of 16 bytes); chunk c of row r is stored at
-// c ^ (4 ((r / 2) % 2)), so the 4 rows x 32 bytes of one transposing read of 16 lanes, and
-// the two 16-lane groups read together, fall on distinct banks.
-__device__ __forceinline__ int wsw(int r) { return ((r >> 1) & 1) << 2; }
+// W stage rows are 256 bytes (16 chunks of 16 bytes); chunk c of row r is stored at
+// c ^ (2 (r % 4)), so the 4 rows x 32 bytes of one transposing read of 16 lanes fall on
+// distinct banks.  x stage rows are 128 bytes; chunk c of row r is stored at c ^ (r % 8).
+__device__ __forceinline__ int wsw(int r) { return (r & 3) << 1; }
 
-// x stage rows are 128 bytes (8 chunks of 16 bytes); chunk c of row r is stored at c ^ (r % 8).
-// `half` picks k 0..31 or 32..63 of the stage.
+// acc += x[rows, k .. k+15] W[k .. k+15, tile]: `quarter` picks the x stage's 16 k.
 template <class C>
 __device__ __forceinline__ void dec_mfma(f32x16_t (&acc)[C::TM][C::TN], const uint4 *__restrict__ xs,
-                                         int half, const uint4 *__restrict__ ws, int lane) {
+                                         int quarter, const uint4 *__restrict__ ws, int lane) {
     const lds_char_t *wsb = (const lds_char_t *)(ws);
     const int g = lane >> 4, li = lane & 15;
+    bf16x8_t af[C::TM], bfr[C::TN];
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-        bf16x8_t af[C::TM], bfr[C::TN];
-#pragma unroll
-        for (int i = 0; i < C::TM; ++i) {
-            const int row = 32 * i + (lane & 31);
-            const int lc = 4 * half + 2 * kk + (lane >> 5);
-            af[i] = *reinterpret_cast<const bf16x8_t *>(&xs[row * 8 + (lc ^ (row & 7))]);
-        }
-#pragma unroll
-        for (int j = 0; j < C::TN; ++j) {
-            const int col = 32 * j + 16 * (g & 1) + 4 * (li & 3);
-            const int lc = col >> 3, half = (col >> 2) & 1;
-            const int r = 16 * kk + 8 * (g >> 1) + (li >> 2);
-            const lds_char_t *p = wsb + r * (kBN * 2) + ((lc ^ wsw(r)) << 4) + half * 8;
-            const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)p);
-            const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)(p + 4 * kBN * 2));
-            bfr[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        }
-#pragma unroll
-        for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-            for (int j = 0; j < C::TN; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    for (int i = 0; i < C::TM; ++i) {
+        const int row = 32 * i + (lane & 31);
+        const int lc = 2 * quarter + (lane >> 5);
+        af[i] = *reinterpret_cast<const bf16x8_t *>(&xs[row * 8 + (lc ^ (row & 7))]);
     }
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) {
+        const int col = 32 * j + 16 * (g & 1) + 4 * (li & 3);
+        const int lc = col >> 3, half = (col >> 2) & 1;
+        const int r = 8 * (g >> 1) + (li >> 2);
+        const lds_char_t *p = wsb + r * (kBN * 2) + ((lc ^ wsw(r)) << 4) + half * 8;
+        const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)p);
+        const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)(p + 4 * kBN * 2));
+        bfr[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
 }
 
 template <class C>
@@ -128,7 +128,7 @@ __device__ __forceinline__ void dma16(const void *g, const lds_void_t *l) {
                  : "memory", "m0");
 }
 
-// A W stage of this wave: rows k0 .. k0+31 of the 64-column tile (row stride ldw).
+// A W stage of this wave: rows k0 .. k0+15 of the tile (row stride ldw).
 template <class C>
 __device__ __forceinline__ void dec_issue_w(const DecSrc<C> &src, uint4 *__restrict__ wslot, int k0,
                                             size_t ldw) {
@@ -142,30 +142,37 @@ __device__ __forceinline__ void dec_issue_x(const DecSrc<C> &src, uint4 *__restr
     for (int q = 0; q < C::XINS; ++q) dma16(src.xp[q] + k0, (const lds_void_t *)&xslot[q * 64]);
 }
 
-// Cross-wave reduction: each wave's accumulators go to LDS (accumulator layout, lane-minor)
-// and, after a barrier, are added in wave order into row-major elements; thread tid owns
-// rows tid/64 + 4q and column tid % 64.
+// Cross-wave reduction.  Value v of lane l in the wave's MFMA block (i, j) is row
+// 32 i + 8 (v / 4) + 4 (l / 32) + v % 4, column 32 j + l % 32: the four values v = 4 q ..
+// 4 q + 3 are four consecutive rows of one column.  Each wave stores them as one 16-byte
+// vector per lane (16 B x 64 lanes contiguous per (i, j, q)); after a barrier, thread tid
+// owns column tid % 128 and the row groups (4 rows) tid / 128 + 2 g, and adds the four
+// waves' vectors in wave order.
 template <class C>
-__device__ __forceinline__ void reduce_waves_put(const f32x16_t (&acc)[C::TM][C::TN], float *red_mine,
+__device__ __forceinline__ void reduce_waves_put(const f32x16_t (&acc)[C::TM][C::TN], float4 *red_mine,
                                                  int lane) {
 #pragma unroll
     for (int i = 0; i < C::TM; ++i)
 #pragma unroll
         for (int j = 0; j < C::TN; ++j)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) red_mine[((i * C::TN + j) * 16 + v) * 64 + lane] = acc[i][j][v];
+            for (int q = 0; q < 4; ++q)
+                red_mine[((i * C::TN + j) * 4 + q) * 64 + lane] =
+                    make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
 }
+// rows 4 g .. 4 g + 3 of column col, summed over the waves in order
 template <class C>
-__device__ __forceinline__ void reduce_waves_sum(const float *r0, const float *r1, const float *r2,
-                                                 const float *r3, int lane, int wave,
-                                                 float (&sum)[C::BM / 4]) {
+__device__ __forceinline__ float4 reduce_waves_group(const float4 *red, int g, int col) {
+    const int i = g >> 3, q = (g >> 1) & 3, h = g & 1, j = col >> 5;
+    const int e = ((i * C::TN + j) * 4 + q) * 64 + 32 * h + (col & 31);
+    constexpr int WV = C::TILE / 4;  // float4 per wave
+    float4 s = red[e];
 #pragma unroll
-    for (int q = 0; q < C::BM / 4; ++q) {
-        const int r = wave + 4 * q, c = lane;
-        const int i = r >> 5, rr = r & 31, j = c >> 5, cc = c & 31;
-        const int e = ((i * C::TN + j) * 16 + (rr >> 3) * 4 + (rr & 3)) * 64 + ((rr >> 2) & 1) * 32 + cc;
-        sum[q] = ((r0[e] + r1[e]) + r2[e]) + r3[e];
+    for (int w = 1; w < kWaves; ++w) {
+        const float4 v = red[w * WV + e];
+        s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
     }
+    return s;
 }
 
 // Column tiles: n_tn tiles of W, then n_lt adapter tiles.  Adapter "slots" are numbered
@@ -187,13 +194,8 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ W, const uint16_t *__restrict__ A,
     int M, int K, int N, int n_tm, int n_tn, int n_lt, int k_per_split, float *__restrict__ partial,
     DecodeLora lo) {
-    // x stage u of wave w: X{u % 2}[w * XSLOT ..]; W stage s: W{s % 4}[w * WSLOT ..]
-    __shared__ __attribute__((aligned(1024))) uint4 XS0[kWaves * C::XSLOT];
-    __shared__ __attribute__((aligned(1024))) uint4 XS1[kWaves * C::XSLOT];
-    __shared__ __attribute__((aligned(1024))) uint4 WS0[kWaves * C::WSLOT];
-    __shared__ __attribute__((aligned(1024))) uint4 WS1[kWaves * C::WSLOT];
-    __shared__ __attribute__((aligned(1024))) uint4 WS2[kWaves * C::WSLOT];
-    __shared__ __attribute__((aligned(1024))) uint4 WS3[kWaves * C::WSLOT];
+    // wave w's part: x stages 0, 1 then W stages 0 .. 3; after the K loop, its partial tile
+    __shared__ __attribute__((aligned(1024))) uint4 lds[kWaves * C::WAVE];
     __shared__ BatchAdapters ba;
     constexpr int APT = AdapterTiles<RM>::APT;
 
@@ -210,15 +212,17 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(
     const int tm = tile % n_tm, tn = tile / n_tm;
     const int m0 = tm * C::BM;
 
-    // per-lane sources of the 64-column tile: W, or the adapters of this adapter tile
+    // per-lane sources of the tile: W, or the adapters of this adapter tile.  Direct load q of
+    // a W stage: lane l fills position l % 16 of row 4 q + l / 16, i.e. chunk
+    // (l % 16) ^ wsw(row) of the row's 16.
     DecSrc<C> src;
     size_t ldw = (size_t)N;
     if (tn < n_tn) {
         const int n0 = tn * kBN;
 #pragma unroll
         for (int q = 0; q < C::WINS; ++q) {
-            const int r = 8 * q + (lane >> 3);
-            const int lc = (lane & 7) ^ wsw(r);
+            const int r = 4 * q + (lane >> 4);
+            const int lc = (lane & 15) ^ wsw(r);
             src.wp[q] = W + (size_t)r * N + min(n0 + lc * 8, N - 8);
         }
     } else {
@@ -244,8 +248,8 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(
         }
 #pragma unroll
         for (int q = 0; q < C::WINS; ++q) {
-            const int r = 8 * q + (lane >> 3);
-            const int col = ((lane & 7) ^ wsw(r)) * 8;
+            const int r = 4 * q + (lane >> 4);
+            const int col = ((lane & 15) ^ wsw(r)) * 8;
             const int sl = lt * APT + col / RM;
             // slots past the last read a valid adapter; their columns are never used
             const int a = sl < T ? (by_id ? sl : ba.list[sl]) : (by_id ? 0 : ba.list[0]);
@@ -270,61 +274,63 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-    const int xo = wave * C::XSLOT, wo = wave * C::WSLOT;
+    uint4 *const mine_lds = lds + wave * C::WAVE;
+    uint4 *const X0 = mine_lds, *const X1 = mine_lds + C::XSLOT;
+    uint4 *const W0 = mine_lds + 2 * C::XSLOT, *const W1 = W0 + C::WSLOT, *const W2 = W1 + C::WSLOT,
+                 *const W3 = W2 + C::WSLOT;
     const int ks0 = split * k_per_split;
     const int ks1 = min(K, ks0 + k_per_split);
-    const int per_wave = k_per_split / kWaves;  // multiple of 32
+    const int per_wave = k_per_split / kWaves;  // multiple of 16
     const int kw0 = min(ks1, ks0 + wave * per_wave);
     const int kw1 = min(ks1, kw0 + per_wave);
-    const int nst = (kw1 - kw0) / kBK;
-    // W stage s holds k = KW(s), x stage u holds k = KX(u) .. +63; stages past the last
+    const int nst = (kw1 - kw0) / kBKW;
+    // W stage s holds k = KW(s) .. +15, x stage u holds k = KX(u) .. +63; stages past the last
     // reload the last one (an empty range loads k = 0), and an x stage that would run past K
-    // starts at K - 64 instead, its second half then holding the wave's last step
-    const int kxl = nst > 0 ? min(kw0 + ((nst - 1) >> 1) * 2 * kBK, K - 2 * kBK) : 0;
-#define KW(S) (nst > 0 ? kw0 + min((S), nst - 1) * kBK : 0)
-#define KX(U) (nst > 0 ? min(kw0 + (U) * 2 * kBK, kxl) : 0)
-    // Issue order: x(0), W(0), W(1), W(2); then step s issues x(s / 2 + 1) when s is even,
-    // and W(s + 3).  When step s starts, what was issued after the stages it needs is two W
-    // stages at an even step (after x(s / 2)), and two W stages and x(s / 2 + 1) at an odd
-    // step (after W(s)).
-    dec_issue_x<C>(src, XS0 + xo, KX(0));
-    dec_issue_w<C>(src, WS0 + wo, KW(0), ldw);
-    dec_issue_w<C>(src, WS1 + wo, KW(1), ldw);
-    dec_issue_w<C>(src, WS2 + wo, KW(2), ldw);
-#define DEC_EVEN(SS, XC, XN, WC, WN)                                                  \
-    wait_vm<2 * C::WINS>();                                                           \
-    wait_lgkm0();                                                                     \
-    dec_issue_x<C>(src, XN + xo, KX((SS) / 2 + 1));                                   \
-    dec_issue_w<C>(src, WN + wo, KW((SS) + 3), ldw);                                  \
-    if ((SS) < nst) dec_mfma<C>(acc, XC + xo, (kw0 + (SS) * kBK - KX((SS) / 2)) / kBK, WC + wo, lane);
-#define DEC_ODD(SS, XC, WC, WN)                                                       \
-    wait_vm<2 * C::WINS + C::XINS>();                                                 \
-    wait_lgkm0();                                                                     \
-    dec_issue_w<C>(src, WN + wo, KW((SS) + 3), ldw);                                  \
-    if ((SS) < nst) dec_mfma<C>(acc, XC + xo, (kw0 + (SS) * kBK - KX((SS) / 2)) / kBK, WC + wo, lane);
+    // starts at K - 64 instead, its later quarters then holding the wave's last steps
+    const int kxl = nst > 0 ? min(kw0 + ((nst - 1) >> 2) * kBKX, K - kBKX) : 0;
+#define KW(S) (nst > 0 ? kw0 + min((S), nst - 1) * kBKW : 0)
+#define KX(U) (nst > 0 ? min(kw0 + (U) * kBKX, kxl) : 0)
+    // Issue order: x(0), W(0), W(1), W(2); then step s issues x(s / 4 + 1) when s % 4 == 0,
+    // then W(s + 3).  When step s starts, what was issued after the stages it needs (W(s),
+    // and x(s / 4), which is older) is two W stages when s % 4 is 0 or 3, and two W stages
+    // and an x stage when it is 1 or 2.
+    dec_issue_x<C>(src, X0, KX(0));
+    dec_issue_w<C>(src, W0, KW(0), ldw);
+    dec_issue_w<C>(src, W1, KW(1), ldw);
+    dec_issue_w<C>(src, W2, KW(2), ldw);
+#define DEC_STEP(SS, PAT, XC, XN, WC, WN)                                                     \
+    if (PAT == 0 || PAT == 3) wait_vm<2 * C::WINS>();                                         \
+    else wait_vm<2 * C::WINS + C::XINS>();                                                    \
+    wait_lgkm0();                                                                             \
+    if (PAT == 0) dec_issue_x<C>(src, XN, KX((SS) / 4 + 1));                                  \
+    dec_issue_w<C>(src, WN, KW((SS) + 3), ldw);                                               \
+    if ((SS) < nst) dec_mfma<C>(acc, XC, (kw0 + (SS) * kBKW - KX((SS) / 4)) / kBKW, WC, lane);
     for (int s = 0; s < nst; s += 4) {
-        DEC_EVEN(s, XS0, XS1, WS0, WS3)
-        DEC_ODD(s + 1, XS0, WS1, WS0)
-        DEC_EVEN(s + 2, XS1, XS0, WS2, WS1)
-        DEC_ODD(s + 3, XS1, WS3, WS2)
+        // x stage s / 4 is in X0 when s / 4 is even
+        uint4 *const XC = (s & 4) ? X1 : X0, *const XN = (s & 4) ? X0 : X1;
+        DEC_STEP(s, 0, XC, XN, W0, W3)
+        DEC_STEP(s + 1, 1, XC, XN, W1, W0)
+        DEC_STEP(s + 2, 2, XC, XN, W2, W1)
+        DEC_STEP(s + 3, 3, XC, XN, W3, W2)
     }
-#undef DEC_EVEN
-#undef DEC_ODD
+#undef DEC_STEP
 #undef KW
 #undef KX
     wait_vm<0>();
-    __syncthreads();  // every wave is done with the stages
+    __syncthreads();  // every wave is done with its stages
 
-    float *red = reinterpret_cast<float *>(wave == 0 ? WS0 : wave == 1 ? WS1 : wave == 2 ? WS2 : WS3);
-    reduce_waves_put<C>(acc, red, lane);
+    float4 *const red = reinterpret_cast<float4 *>(lds);
+    reduce_waves_put<C>(acc, red + wave * (C::TILE / 4), lane);
     __syncthreads();
-    float sum[C::BM / 4];
-    reduce_waves_sum<C>(reinterpret_cast<const float *>(WS0), reinterpret_cast<const float *>(WS1),
-                        reinterpret_cast<const float *>(WS2), reinterpret_cast<const float *>(WS3),
-                        lane, wave, sum);
     float *mine = partial + ((size_t)split * n_tiles + tile) * C::TILE;
+    const int col = tid & 127;
 #pragma unroll
-    for (int q = 0; q < C::BM / 4; ++q) mine[(wave + 4 * q) * kBN + lane] = sum[q];
+    for (int q = 0; q < C::BM / 8; ++q) {
+        const int g = (tid >> 7) + 2 * q;  // rows 4 g .. 4 g + 3
+        const float4 s = reduce_waves_group<C>(red, g, col);
+        float *o = mine + (4 * g) * kBN + col;
+        o[0] = s.x; o[kBN] = s.y; o[2 * kBN] = s.z; o[3 * kBN] = s.w;
+    }
 }
 
 // y[m, n .. n+3] = (sum over splits, in order, of the partial tiles)
@@ -450,13 +456,13 @@ DecPlan dec_plan(int M, int K, int N, int n_lt) {
     p.n_tn = (N + kBN - 1) / kBN;
     p.n_lt = n_lt;
     const long tiles = (long)p.n_tm * (p.n_tn + n_lt);
-    const int kq = K / (kBK * kWaves);  // whole 128-deep quanta (K >= 128)
+    const int kq = K / (kBKW * kWaves);  // whole 64-deep quanta (a step per wave)
     int ks = (int)(256 / tiles);
     if (ks < 1) ks = 1;
     if (ks > kq) ks = kq;
     if (ks > 16) ks = 16;
     const int q_per = (kq + ks - 1) / ks;
-    p.k_per_split = q_per * kBK * kWaves;
+    p.k_per_split = q_per * kBKW * kWaves;
     p.ks = (K + p.k_per_split - 1) / p.k_per_split;
     return p;
 }
@@ -466,7 +472,7 @@ bool rank_ok(int r_max) { return r_max == 8 || r_max == 16 || r_max == 32 || r_m
 }  // namespace
 
 bool decode_gemm_supported(int M, int K, int N) {
-    return M >= 1 && M <= kDecodeGemmMaxRows && K % kBK == 0 && K >= kBK * kWaves && N >= 8 &&
+    return M >= 1 && M <= kDecodeGemmMaxRows && K % 32 == 0 && K >= 128 && N >= 8 &&
            N % 4 == 0;
 }
 
