@@ -186,7 +186,7 @@ struct AdapterTiles {
 };
 
 // Workgroup (tile, split), four waves.  Each wave streams its quarter of split `split` of K
-// (rows [split k_per_split, +k_per_split)) for one 64-column tile -- of W, or of the
+// (rows [split k_per_split, +k_per_split)) for one 128-column tile -- of W, or of the
 // adapters' A laid side by side -- and the workgroup writes its partial tile;
 // reduce_lora_kernel adds the splits in order.
 template <class C, int RM>
@@ -456,14 +456,14 @@ DecPlan dec_plan(int M, int K, int N, int n_lt) {
     p.n_tn = (N + kBN - 1) / kBN;
     p.n_lt = n_lt;
     const long tiles = (long)p.n_tm * (p.n_tn + n_lt);
-    const int kq = K / (kBKW * kWaves);  // whole 64-deep quanta (a step per wave)
+    const int kq = (K + kBKW * kWaves - 1) / (kBKW * kWaves);  // 64-deep quanta (a step per wave)
     int ks = (int)(256 / tiles);
     if (ks < 1) ks = 1;
     if (ks > kq) ks = kq;
     if (ks > 16) ks = 16;
     const int q_per = (kq + ks - 1) / ks;
     p.k_per_split = q_per * kBKW * kWaves;
-    p.ks = (K + p.k_per_split - 1) / p.k_per_split;
+    p.ks = (K + p.k_per_split - 1) / p.k_per_split;  // <= ks <= 16, what the reduction adds
     return p;
 }
 

@@ -139,6 +139,12 @@ RANDOM = [
     (24, 200, 1024, 520, 40, 32, 0.1, DECODE),
     (25, 128, 2048, 264, 300, 64, 0.2, DECODE),
     (26, 129, 512, 128, 3, 8, 0.0, DECODE),
+    # d_in a multiple of 32 but not of 64: the last 64-deep x stage of a wave starts at
+    # d_in - 64; with 17 64-deep quanta the split plan must still stay within 16 splits
+    (27, 40, 1056, 200, 50, 16, 0.2, DECODE),
+    (28, 24, 160, 72, 9, 64, 0.0, DECODE),
+    (29, 150, 544, 264, 40, 32, 0.1, DECODE),
+    (30, 64, 4160, 256, 8, 16, 0.1, DECODE),
 ]
 
 
