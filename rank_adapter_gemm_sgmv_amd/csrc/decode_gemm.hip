@@ -365,13 +365,13 @@ __global__ __launch_bounds__(256) void reduce_lora_kernel(const float *__restric
 #pragma unroll
     for (int sp = 0; sp < kMaxSplits; ++sp)
         if (sp < n_splits) pv[sp] = *reinterpret_cast<const float4 *>(pp + sp * stride);
-    // B_a[j, nc .. nc+3] for the adapter's rank rows, all issued together (rows at or beyond
-    // the rank reload row r - 1, the same cache lines, and are skipped in the sum)
-    const int r = !has ? 1 : lo.ranks ? min(max(lo.ranks[a], 1), RM) : RM;
+    // B_a[j, nc .. nc+3] for the adapter's rank rows, issued together (the rank is uniform
+    // in the block, so rows at or beyond it are neither loaded nor added)
+    const int r = !has ? 0 : lo.ranks ? min(max(lo.ranks[a], 1), RM) : RM;
     uint2 bv[RM];
     const uint16_t *bp = lo.B + (size_t)a * RM * N + nc;
 #pragma unroll
-    for (int j = 0; j < RM; ++j) bv[j] = *reinterpret_cast<const uint2 *>(bp + (size_t)min(j, r - 1) * N);
+    for (int j = 0; j < RM; ++j) bv[j] = j < r ? *reinterpret_cast<const uint2 *>(bp + (size_t)j * N) : make_uint2(0, 0);
     // where the parts of t[m, :] are
     const float *tsrc;
     size_t t_stride;
