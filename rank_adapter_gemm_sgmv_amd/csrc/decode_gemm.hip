@@ -316,7 +316,20 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(
 #undef DEC_STEP
 #undef KW
 #undef KX
+    // The reduction that follows starts with dependent loads of these small tables (a row's
+    // adapter, then its rank and scale, then B); left to it they come from HBM.  Touched here
+    // (loads from asm, results unused), they are in every XCD's L2 by then.  The registers
+    // they land in are handed to an empty asm after the wait below, so that the compiler
+    // gives them to nothing else while the loads are in flight.
+    uint32_t d0, d1, d2;
+    {
+        const int mm = min(tid, M - 1), aa = min(tid, lo.n_adapters - 1);
+        asm volatile("global_load_dword %0, %1, off" : "=v"(d0) : "v"(lo.ids + mm));
+        asm volatile("global_load_dword %0, %1, off" : "=v"(d1) : "v"(lo.scale + aa));
+        asm volatile("global_load_dword %0, %1, off" : "=v"(d2) : "v"(lo.ranks ? lo.ranks + aa : lo.ids + mm));
+    }
     wait_vm<0>();
+    asm volatile("" ::"v"(d0), "v"(d1), "v"(d2));
     __syncthreads();  // every wave is done with its stages
 
     float4 *const red = reinterpret_cast<float4 *>(lds);
@@ -366,12 +379,17 @@ __global__ __launch_bounds__(256) void reduce_lora_kernel(const float *__restric
     for (int sp = 0; sp < kMaxSplits; ++sp)
         if (sp < n_splits) pv[sp] = *reinterpret_cast<const float4 *>(pp + sp * stride);
     // B_a[j, nc .. nc+3] for the adapter's rank rows, issued together (the rank is uniform
-    // in the block, so rows at or beyond it are neither loaded nor added)
+    // in the block, so rows at or beyond it are not added, and above r_max 16 not loaded)
     const int r = !has ? 0 : lo.ranks ? min(max(lo.ranks[a], 1), RM) : RM;
     uint2 bv[RM];
     const uint16_t *bp = lo.B + (size_t)a * RM * N + nc;
 #pragma unroll
-    for (int j = 0; j < RM; ++j) bv[j] = j < r ? *reinterpret_cast<const uint2 *>(bp + (size_t)j * N) : make_uint2(0, 0);
+    for (int j = 0; j < RM; ++j) {
+        // at r_max <= 16 every row is loaded (the pool's padding rows exist), so the loads
+        // need not wait for the rank
+        if constexpr (RM <= 16) bv[j] = *reinterpret_cast<const uint2 *>(bp + (size_t)j * N);
+        else bv[j] = j < r ? *reinterpret_cast<const uint2 *>(bp + (size_t)j * N) : make_uint2(0, 0);
+    }
     // where the parts of t[m, :] are
     const float *tsrc;
     size_t t_stride;
