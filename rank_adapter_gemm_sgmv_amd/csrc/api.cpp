@@ -199,10 +199,10 @@ lora_status_t check_linear(const void *x, const void *W, const void *A, const vo
 }
 
 // The launch sequence of lora_linear (arguments already validated, M > 0).
-//   decode, M <= 128 and d_in % 32 == 0: the split-K GEMM of x W, whose workgroups also
-//            compute the LoRA shrink's chunk sums, then the ordered reduction that adds
-//            scale_a t B_a (no segment-building launch: rows are grouped by adapter in LDS;
-//            segs is not needed)
+//   decode, M <= 128 and d_in % 32 == 0: one split-K GEMM over W and the batch's adapters'
+//            A laid side by side (the shrink as extra column tiles), then the ordered
+//            reduction that adds scale_a t B_a (no segment-building launch: adapters are
+//            numbered by id or grouped in LDS; segs is not needed)
 //   decode, 128 < M <= 256 and d_in % 32 == 0: build_segments, shrink (chunk sums), the
 //            split-K GEMM, the ordered reduction with the expand
 //   decode otherwise: build_segments, shrink, shrink_finalize, gemm [, splitk_reduce], expand
