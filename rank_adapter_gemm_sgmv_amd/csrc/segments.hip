@@ -207,6 +207,11 @@ __global__ __launch_bounds__(kThreads) void build_segments_small_kernel(
     // 1. per-wave histogram (one writer per (wave, bucket) per block of 64 rows: the peer
     //    group's lowest lane; a wave's LDS instructions execute in order).  The ids of four
     //    blocks are loaded together.
+    // A wave whose chunk is one pass (C <= 256 rows: M <= 4096) keeps its buckets and peer
+    // masks in registers for the scatter instead of reloading its ids.
+    const bool one_pass = r1 - r0 <= 4 * 64;
+    int kb[4];
+    uint64_t kp[4];
     int bad = 0;
     for (int c0 = r0; c0 < r1; c0 += 4 * 64) {
         int bq[4];
@@ -222,6 +227,8 @@ __global__ __launch_bounds__(kThreads) void build_segments_small_kernel(
             const bool valid = c0 + 64 * q + lane < r1;
             const uint64_t peers = peer_mask(bq[q], valid, nbits);
             if (valid && __popcll(peers & lanes_below) == 0) pos[wave * nb + bq[q]] += __popcll(peers);
+            kb[q] = bq[q];
+            kp[q] = peers;
         }
     }
     if (bad) atomicAdd(&bad_total, bad);
@@ -248,16 +255,27 @@ __global__ __launch_bounds__(kThreads) void build_segments_small_kernel(
     // 3. scatter: the same walk as step 1
     for (int c0 = r0; c0 < r1; c0 += 4 * 64) {
         int bq[4];
+        uint64_t pq[4];
+        if (one_pass) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int m = c0 + 64 * q + lane;
-            bq[q] = m < r1 ? bucket_of(ids[m], n) : n;
+            for (int q = 0; q < 4; ++q) {
+                bq[q] = kb[q];
+                pq[q] = kp[q];
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int m = c0 + 64 * q + lane;
+                bq[q] = m < r1 ? bucket_of(ids[m], n) : n;
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) pq[q] = peer_mask(bq[q], c0 + 64 * q + lane < r1, nbits);
         }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int m = c0 + 64 * q + lane;
             const bool valid = m < r1;
-            const uint64_t peers = peer_mask(bq[q], valid, nbits);
+            const uint64_t peers = pq[q];
             const int rank = __popcll(peers & lanes_below);
             if (valid) {
                 const int base = cnt[bq[q]] + pos[wave * nb + bq[q]];
