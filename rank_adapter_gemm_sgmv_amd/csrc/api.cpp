@@ -284,8 +284,8 @@ hipError_t run_linear(const void *x, const void *W, const void *A, const void *B
                          &gsplit, s)) != hipSuccess)
         return e;
     mark(mk, "gemm_decode");
-    if (gsplit > 1) {
-        if ((e = launch_splitk_reduce(gpart, M, d_out, gsplit, y, yf, s)) != hipSuccess) return e;
+    if (gsplit != 1) {
+        if ((e = launch_splitk_reduce(gpart, M, d_in, d_out, gsplit, y, yf, s)) != hipSuccess) return e;
         mark(mk, "splitk_reduce");
     }
     if ((e = launch_expand(t, Bb, scale, ranks, M, d_out, r_max, n_adapters, sg, y, yf, s)) != hipSuccess)

@@ -105,7 +105,8 @@ struct LoraEpilogue {
 
 // y = x W (+ LoRA epilogue when lora != nullptr).  `prefill` selects the 256x256 tiling
 // and segment-ordered rows; otherwise a decode tiling, which may split K: then the partial
-// sums go to ws_partial, *ksplit_out > 1, and launch_splitk_reduce must follow.
+// sums go to ws_partial, *ksplit_out != 1 (> 1 split-K slices, -1 stream-K), and
+// launch_splitk_reduce must follow.
 hipError_t launch_gemm(const uint16_t *x, const uint16_t *W, int M, int K, int N, void *y,
                        bool y_f32, bool prefill, Seg seg, const LoraEpilogue *lora,
                        float *ws_partial, size_t ws_partial_floats, int *ksplit_out,
@@ -116,7 +117,22 @@ hipError_t launch_gemm(const uint16_t *x, const uint16_t *W, int M, int K, int N
 hipError_t launch_gemm_big(const uint16_t *x, const uint16_t *W, int M, int K, int N, void *y,
                            bool y_f32, Seg seg, const LoraEpilogue *lora, hipStream_t s);
 
-hipError_t launch_splitk_reduce(const float *partial, int M, int N, int ksplit, void *y,
+// Stream-K decode GEMM (csrc/gemm_big.hip) for batches of 257-1024 rows whose 256 x 256
+// tiles are too few to fill the chip: L lanes of equal K length, n_tm workgroups per lane.
+struct SkPlan {
+    bool use;
+    int n_tm, n_tn, L;
+};
+SkPlan sk_plan(int M, int K, int N);
+size_t sk_partial_floats(const SkPlan &p);
+hipError_t launch_gemm_sk(const uint16_t *x, const uint16_t *W, int M, int K, int N,
+                          const SkPlan &p, float *partial, hipStream_t s);
+hipError_t launch_sk_reduce(const float *partial, int M, int K, int N, const SkPlan &p, void *y,
+                            bool y_f32, hipStream_t s);
+
+// Adds the decode GEMM's partial sums into y after launch_gemm reported *ksplit_out != 1:
+// ksplit > 1 split-K slices in order, or -1 for the stream-K partial tiles.
+hipError_t launch_splitk_reduce(const float *partial, int M, int K, int N, int ksplit, void *y,
                                 bool y_f32, hipStream_t s);
 
 // LoRA operands of the small-batch decode GEMM and reduction (csrc/decode_gemm.hip).

@@ -352,6 +352,8 @@ hipError_t launch_cfg(const uint16_t *x, const uint16_t *W, int M, int K, int N,
 }  // namespace
 
 size_t gemm_partial_floats(int M, int K, int N) {
+    const SkPlan sp = sk_plan(M, K, N);
+    if (sp.use) return sk_partial_floats(sp);
     if (use_big(M, N)) return 0;
     const DecodePlan p = decode_plan(M, K, N);
     return p.ksplit > 1 ? (size_t)p.ksplit * M * N : 0;
@@ -363,6 +365,13 @@ hipError_t launch_gemm(const uint16_t *x, const uint16_t *W, int M, int K, int N
                        hipStream_t s) {
     *ksplit_out = 1;
     if (prefill) return launch_gemm_big(x, W, M, K, N, y, y_f32, seg, lora, s);
+    const SkPlan sp = sk_plan(M, K, N);
+    if (sp.use) {
+        if (sk_partial_floats(sp) > ws_partial_floats || ws_partial == nullptr)
+            return hipErrorInvalidValue;
+        *ksplit_out = -1;
+        return launch_gemm_sk(x, W, M, K, N, sp, ws_partial, s);
+    }
     if (use_big(M, N)) return launch_gemm_big(x, W, M, K, N, y, y_f32, seg, nullptr, s);
 
     const DecodePlan p = decode_plan(M, K, N);
@@ -380,8 +389,9 @@ hipError_t launch_gemm(const uint16_t *x, const uint16_t *W, int M, int K, int N
     return launch_cfg<CfgD128, false>(x, W, M, K, N, y, y_f32, partial, p.ksplit, p.k_per_split, seg, nullptr, s);
 }
 
-hipError_t launch_splitk_reduce(const float *partial, int M, int N, int ksplit, void *y, bool y_f32,
-                                hipStream_t s) {
+hipError_t launch_splitk_reduce(const float *partial, int M, int K, int N, int ksplit, void *y,
+                                bool y_f32, hipStream_t s) {
+    if (ksplit < 0) return launch_sk_reduce(partial, M, K, N, sk_plan(M, K, N), y, y_f32, s);
     const long threads = (long)M * N / 4;
     const int grid = (int)((threads + 255) / 256);
     if (y_f32)

@@ -417,6 +417,161 @@ __global__ __launch_bounds__(C::NT) void gemm_big_kernel(const uint16_t *__restr
     }
 }
 
+// ---- stream-K decode GEMM -----------------------------------------------------------------
+// Decode batches of a few hundred rows have too few 256 x 256 output tiles to fill the chip
+// (512 x 11008: 86 tiles on 256 CUs), and smaller tiles lose the large tile's MFMA rate.
+// Instead the K steps of all column panels, laid end to end panel after panel, are cut into
+// L equal lanes.  Each lane is run by n_tm workgroups, one per 256-row tile, placed on the
+// same XCD (workgroup b runs on XCD b % 8), so the W panel they share is read once into that
+// XCD's L2.  A lane's range may start inside one panel and end inside the next: for every
+// panel it meets, the lane writes its fp32 partial tile to slot (lane + panel) * n_tm + tm.
+// lane + panel differs for every (lane, panel) pair that meets, because panels and lanes
+// both advance along the one K line.  sk_reduce_kernel adds a panel's slots in lane order,
+// so the sum does not depend on scheduling.
+
+// First K step (of the panel-major line of `total` steps) of lane l out of L.  Lanes start
+// on multiples of 4 steps and K is a multiple of 4 steps (128), so every (lane, panel) piece
+// is a whole number of trips of the 4-stage ring.
+__device__ __forceinline__ int sk_start(int l, int total, int L) {
+    return 4 * (int)(((long)l * (total / 4)) / L);
+}
+
+template <class C>
+__global__ __launch_bounds__(C::NT) void gemm_sk_kernel(const uint16_t *__restrict__ x,
+                                                        const uint16_t *__restrict__ W,
+                                                        int M, int K, int N,
+                                                        float *__restrict__ partial, int n_tm,
+                                                        int n_tn, int L) {
+    __shared__ __attribute__((aligned(1024))) uint4 X0[C::XSLOT];
+    __shared__ __attribute__((aligned(1024))) uint4 X1[C::XSLOT];
+    __shared__ __attribute__((aligned(1024))) uint4 X2[C::XSLOT];
+    __shared__ __attribute__((aligned(1024))) uint4 X3[C::XSLOT];
+    __shared__ __attribute__((aligned(1024))) uint4 W0[C::WSLOT];
+    __shared__ __attribute__((aligned(1024))) uint4 W1[C::WSLOT];
+    __shared__ __attribute__((aligned(1024))) uint4 W2[C::WSLOT];
+    __shared__ __attribute__((aligned(1024))) uint4 W3[C::WSLOT];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm0 = (wave / C::WN) * C::WTM, wn0 = (wave % C::WN) * C::WTN;
+    const int b = blockIdx.x;
+    const int tm = (b >> 3) % n_tm;
+    const int ln = (b / (8 * n_tm)) * 8 + (b & 7);
+    const int KI = K / kBK;
+    const int total = n_tn * KI;
+    const int s0 = sk_start(ln, total, L), s1 = sk_start(ln + 1, total, L);
+    const int row0 = tm * C::BM;
+
+    DmaSrc<C> src;
+#pragma unroll
+    for (int j = 0; j < C::XINS; ++j) {
+        const int q = wave * C::XINS + j;
+        const int row = 16 * q + (lane >> 2);
+        const int lc = (lane & 3) ^ ((lane >> 4) & 3);
+        src.xp[j] = x + (size_t)min(row0 + row, M - 1) * K + lc * 8;
+    }
+
+    for (int p = s0 / KI; p * KI < s1; ++p) {
+        const int kb = max(s0, p * KI) - p * KI;
+        const int n = min(s1, (p + 1) * KI) - p * KI - kb;  // steps of this panel, 4 | n
+        const int n0 = p * C::BN;
+#pragma unroll
+        for (int j = 0; j < C::WINS; ++j) {
+            const int q = wave * C::WINS + j;
+            const int r = C::WROWS * q + lane / C::WCH;
+            const int lc = (lane % C::WCH) ^ ((r & 3) << 2);
+            src.wp[j] = W + (size_t)r * N + min(n0 + lc * 8, N - 8);
+        }
+        f32x16_t acc[C::TM][C::TN];
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+            for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+        // every wave is done reading the previous panel's slots before they are refilled
+        lds_barrier();
+        // The ring of the large kernel over steps kb .. kb+n-1; loads past the last step
+        // reload the last step (in bounds, never multiplied), so every step issues one stage
+        // and the waits stay exact.
+        const int last = kb + n - 1;
+        Frags<C> fa, fb;
+        issue_stage<C>(src, X0, W0, wave, kb * kBK, N);
+        issue_stage<C>(src, X1, W1, wave, min(kb + 1, last) * kBK, N);
+        issue_stage<C>(src, X2, W2, wave, min(kb + 2, last) * kBK, N);
+        wait_vm<2 * C::PER>();
+        lds_barrier();
+        read_frags<C>(fa, X0, W0, lane, wm0, wn0);
+        issue_stage<C>(src, X3, W3, wave, min(kb + 3, last) * kBK, N);
+#define LORA_SK_STEP(SS, FC, FN, XN, WN, XF, WF)                                  \
+        wait_vm<2 * C::PER>();                                                   \
+        lds_barrier();                                                           \
+        issue_stage<C>(src, XF, WF, wave, min(kb + (SS) + 4, last) * kBK, N);    \
+        read_frags<C>(FN, XN, WN, lane, wm0, wn0);                               \
+        mfma_frags<C>(acc, FC);                                                  \
+        interleave_reads_with_mfma<C>();
+        for (int s = 0; s < n; s += 4) {
+            LORA_SK_STEP(s, fa, fb, X1, W1, X0, W0)
+            LORA_SK_STEP(s + 1, fb, fa, X2, W2, X1, W1)
+            LORA_SK_STEP(s + 2, fa, fb, X3, W3, X2, W2)
+            LORA_SK_STEP(s + 3, fb, fa, X0, W0, X3, W3)
+        }
+#undef LORA_SK_STEP
+        wait_vm<0>();
+
+        // partial tile, row-major [BM][BN]: accumulator element v of a 32 x 32 block is row
+        // (v/4)*8 + (lane/32)*4 + v%4, column lane%32 (each store covers two 128-byte rows)
+        float *P = partial + (size_t)((ln + p) * n_tm + tm) * (C::BM * C::BN) +
+                   (wm0 + (lane >> 5) * 4) * C::BN + wn0 + (lane & 31);
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+            for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    P[(32 * i + (v / 4) * 8 + (v % 4)) * C::BN + 32 * j] = acc[i][j][v];
+    }
+}
+
+// y[m][n .. n+7] = sum over the lanes that meet column panel n / BN, in lane order, of
+// their partial tiles; one thread per 8 columns of one row.
+template <class C, bool YF32>
+__global__ __launch_bounds__(256) void sk_reduce_kernel(const float *__restrict__ partial,
+                                                        int M, int K, int N, int n_tm,
+                                                        int n_tn, int L,
+                                                        void *__restrict__ y) {
+    const int groups = N / 8;
+    const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (long)M * groups) return;
+    const int m = (int)(idx / groups), n = (int)(idx % groups) * 8;
+    const int tm = m / C::BM, r = m % C::BM, p = n / C::BN, c = n % C::BN;
+    const int KI = K / kBK, total = n_tn * KI;
+    const int k0 = p * KI, k1 = k0 + KI;
+    // the lane whose range holds the panel's first step
+    int l = (int)(((long)k0 * L) / total);
+    while (l > 0 && sk_start(l, total, L) > k0) --l;
+    while (l + 1 < L && sk_start(l + 1, total, L) <= k0) ++l;
+    float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (; l < L && sk_start(l, total, L) < k1; ++l) {
+        const float *P = partial + ((size_t)((l + p) * n_tm + tm) * C::BM + r) * C::BN + c;
+        const float4 u = *reinterpret_cast<const float4 *>(P);
+        const float4 v = *reinterpret_cast<const float4 *>(P + 4);
+        a[0] += u.x; a[1] += u.y; a[2] += u.z; a[3] += u.w;
+        a[4] += v.x; a[5] += v.y; a[6] += v.z; a[7] += v.w;
+    }
+    if constexpr (YF32) {
+        float *yf = reinterpret_cast<float *>(y) + (size_t)m * N + n;
+        *reinterpret_cast<float4 *>(yf) = make_float4(a[0], a[1], a[2], a[3]);
+        *reinterpret_cast<float4 *>(yf + 4) = make_float4(a[4], a[5], a[6], a[7]);
+    } else {
+        st16(reinterpret_cast<uint16_t *>(y) + (size_t)m * N + n,
+             make_uint4(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]),
+                        pack_bf16x2(a[4], a[5]), pack_bf16x2(a[6], a[7])));
+    }
+}
+
+using CfgSk = Big<256, 256, 2, 4>;
+
 template <class C, bool SEGROWS, bool LORA>
 hipError_t launch_big_cfg(const uint16_t *x, const uint16_t *W, int M, int K, int N, void *y,
                           bool y_f32, Seg seg, const LoraEpilogue *lora, hipStream_t s) {
@@ -450,6 +605,43 @@ hipError_t launch_gemm_big(const uint16_t *x, const uint16_t *W, int M, int K, i
     if ((long)((M + 255) / 256) * ((N + 127) / 128) >= 192)
         return launch_big_cfg<Big<256, 128>, false, false>(x, W, M, K, N, y, y_f32, seg, nullptr, s);
     return launch_big_cfg<Big<128, 128>, false, false>(x, W, M, K, N, y, y_f32, seg, nullptr, s);
+}
+
+
+SkPlan sk_plan(int M, int K, int N) {
+    SkPlan p{};
+    if (M <= kDecodeGemmMaxRows || M > 1024 || K % (4 * kBK) != 0 || N % 8 != 0) return p;
+    p.n_tm = (M + CfgSk::BM - 1) / CfgSk::BM;
+    p.n_tn = (N + CfgSk::BN - 1) / CfgSk::BN;
+    if ((long)p.n_tm * p.n_tn >= 192) return p;  // the data-parallel tiling fills the chip
+    p.L = (256 / p.n_tm) / 8 * 8;
+    if ((long)p.n_tn * (K / kBK) < 8L * p.L) return p;  // at least 8 K steps per lane
+    p.use = true;
+    return p;
+}
+
+size_t sk_partial_floats(const SkPlan &p) {
+    return p.use ? (size_t)(p.L + p.n_tn - 1) * p.n_tm * CfgSk::BM * CfgSk::BN : 0;
+}
+
+hipError_t launch_gemm_sk(const uint16_t *x, const uint16_t *W, int M, int K, int N,
+                          const SkPlan &p, float *partial, hipStream_t s) {
+    launch(gemm_sk_kernel<CfgSk>, dim3(p.L * p.n_tm), dim3(CfgSk::NT), 0, s, x, W, M, K, N,
+           partial, p.n_tm, p.n_tn, p.L);
+    return hipGetLastError();
+}
+
+hipError_t launch_sk_reduce(const float *partial, int M, int K, int N, const SkPlan &p, void *y,
+                            bool y_f32, hipStream_t s) {
+    const long threads = (long)M * (N / 8);
+    const dim3 grid((unsigned)((threads + 255) / 256));
+    if (y_f32)
+        launch(sk_reduce_kernel<CfgSk, true>, grid, dim3(256), 0, s, partial, M, K, N, p.n_tm,
+               p.n_tn, p.L, y);
+    else
+        launch(sk_reduce_kernel<CfgSk, false>, grid, dim3(256), 0, s, partial, M, K, N, p.n_tm,
+               p.n_tn, p.L, y);
+    return hipGetLastError();
 }
 
 }  // namespace lora

@@ -32,9 +32,11 @@ _STEP_OF_KERNEL = [
     ("shrink_finalize_kernel", "shrink_finalize"),
     ("shrink_mfma_kernel", "shrink"),
     ("splitk_reduce_kernel", "splitk_reduce"),
+    ("sk_reduce_kernel", "splitk_reduce"),
     ("expand_kernel", "expand"),
     ("gemm_big_kernel", "gemm"),
     ("gemm_kernel", "gemm"),
+    ("gemm_sk_kernel", "gemm"),
 ]
 _CALIB = "neg_kernel"
 

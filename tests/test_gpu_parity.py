@@ -145,6 +145,11 @@ RANDOM = [
     (28, 24, 160, 72, 9, 64, 0.0, DECODE),
     (29, 150, 544, 264, 40, 32, 0.1, DECODE),
     (30, 64, 4160, 256, 8, 16, 0.1, DECODE),
+    # stream-K decode GEMM (257-1024 rows, d_in % 128 == 0): 2, 3 and 4 row tiles per
+    # lane, ragged last row tile and column panel
+    (31, 300, 4096, 2056, 50, 16, 0.1, DECODE),
+    (32, 700, 2048, 2600, 90, 32, 0.2, DECODE),
+    (33, 1000, 2048, 2056, 400, 8, 0.0, DECODE),
 ]
 
 
