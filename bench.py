@@ -335,6 +335,14 @@ def summarize(w, runner, ms_total, steps, wall, eager_ms, kernels, prefill):
             entry["shrink_expand_gbs"] = work["lora_bytes"] / (l_ms * 1e-3) / 1e9
             entry["shrink_expand_hbm_frac"] = entry["shrink_expand_gbs"] / HBM_PEAK_GBS
             lora_bytes += work["lora_bytes"]
+        elif not prefill and "shrink" in ks and "decode_reduce_lora" in ks:
+            # medium and stream-K decode paths: the shrink, then the pass that adds the GEMM's
+            # partial sums and the expand (its bytes: B_i, t, y written once)
+            l_ms = sum(ks[k] for k in ("shrink", "shrink_finalize", "decode_reduce_lora") if k in ks)
+            l_bytes = work["shrink"]["bytes"] + work["decode_reduce_lora"]["bytes"]
+            entry["shrink_reduce_lora_us"] = l_ms * 1e3
+            entry["shrink_reduce_lora_gbs"] = l_bytes / (l_ms * 1e-3) / 1e9
+            entry["shrink_reduce_lora_hbm_frac"] = entry["shrink_reduce_lora_gbs"] / HBM_PEAK_GBS
         lora_s += sum(ks.get(k, 0.0) for k in ("build_segments", "shrink", "shrink_finalize", "expand")) * 1e-3
         per_proj.append(entry)
     ms_step = ms_total / steps

@@ -205,6 +205,9 @@ lora_status_t check_linear(const void *x, const void *W, const void *A, const vo
 //            numbered by id or grouped in LDS; segs is not needed)
 //   decode, 128 < M <= 256 and d_in % 32 == 0: build_segments, shrink (chunk sums), the
 //            split-K GEMM, the ordered reduction with the expand
+//   decode, 256 < M <= 1024, d_in % 128 == 0 and few 256 x 256 tiles: build_segments,
+//            shrink, shrink_finalize, the stream-K GEMM, one pass adding its partial tiles
+//            and the expand
 //   decode otherwise: build_segments, shrink, shrink_finalize, gemm [, splitk_reduce], expand
 //   prefill: build_segments, shrink, shrink_finalize, gemm with the LoRA epilogue
 hipError_t run_linear(const void *x, const void *W, const void *A, const void *B,
@@ -284,8 +287,16 @@ hipError_t run_linear(const void *x, const void *W, const void *A, const void *B
                          &gsplit, s)) != hipSuccess)
         return e;
     mark(mk, "gemm_decode");
-    if (gsplit != 1) {
-        if ((e = launch_splitk_reduce(gpart, M, d_in, d_out, gsplit, y, yf, s)) != hipSuccess) return e;
+    if (gsplit < 0) {
+        // stream-K partial tiles: one pass adds them and the expand, rows in segment order
+        if ((e = launch_sk_reduce_lora(gpart, M, d_in, d_out, sk_plan(M, d_in, d_out), sg, t, Bb,
+                                       scale, ids, ranks, r_max, n_adapters, y, yf, s)) != hipSuccess)
+            return e;
+        mark(mk, "decode_reduce_lora");
+        return hipSuccess;
+    }
+    if (gsplit > 1) {
+        if ((e = launch_splitk_reduce(gpart, M, d_out, gsplit, y, yf, s)) != hipSuccess) return e;
         mark(mk, "splitk_reduce");
     }
     if ((e = launch_expand(t, Bb, scale, ranks, M, d_out, r_max, n_adapters, sg, y, yf, s)) != hipSuccess)

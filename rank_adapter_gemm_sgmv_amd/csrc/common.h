@@ -105,8 +105,8 @@ struct LoraEpilogue {
 
 // y = x W (+ LoRA epilogue when lora != nullptr).  `prefill` selects the 256x256 tiling
 // and segment-ordered rows; otherwise a decode tiling, which may split K: then the partial
-// sums go to ws_partial, *ksplit_out != 1 (> 1 split-K slices, -1 stream-K), and
-// launch_splitk_reduce must follow.
+// sums go to ws_partial and *ksplit_out != 1: > 1 split-K slices (launch_splitk_reduce must
+// follow), or -1 stream-K partial tiles (launch_sk_reduce_lora must follow).
 hipError_t launch_gemm(const uint16_t *x, const uint16_t *W, int M, int K, int N, void *y,
                        bool y_f32, bool prefill, Seg seg, const LoraEpilogue *lora,
                        float *ws_partial, size_t ws_partial_floats, int *ksplit_out,
@@ -127,12 +127,15 @@ SkPlan sk_plan(int M, int K, int N);
 size_t sk_partial_floats(const SkPlan &p);
 hipError_t launch_gemm_sk(const uint16_t *x, const uint16_t *W, int M, int K, int N,
                           const SkPlan &p, float *partial, hipStream_t s);
-hipError_t launch_sk_reduce(const float *partial, int M, int K, int N, const SkPlan &p, void *y,
-                            bool y_f32, hipStream_t s);
+// y = (the stream-K partial tiles added in lane order) + scale_a t B_a on rows with an
+// adapter, rows in segment order; rounds once into y.
+hipError_t launch_sk_reduce_lora(const float *partial, int M, int K, int N, const SkPlan &p,
+                                 Seg seg, const float *t, const uint16_t *B, const float *scale,
+                                 const int32_t *ids, const int32_t *ranks, int r_max,
+                                 int n_adapters, void *y, bool y_f32, hipStream_t s);
 
-// Adds the decode GEMM's partial sums into y after launch_gemm reported *ksplit_out != 1:
-// ksplit > 1 split-K slices in order, or -1 for the stream-K partial tiles.
-hipError_t launch_splitk_reduce(const float *partial, int M, int K, int N, int ksplit, void *y,
+// Adds the split-K decode GEMM's ksplit > 1 partial slices into y, in order.
+hipError_t launch_splitk_reduce(const float *partial, int M, int N, int ksplit, void *y,
                                 bool y_f32, hipStream_t s);
 
 // LoRA operands of the small-batch decode GEMM and reduction (csrc/decode_gemm.hip).

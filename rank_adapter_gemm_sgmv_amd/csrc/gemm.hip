@@ -389,9 +389,8 @@ hipError_t launch_gemm(const uint16_t *x, const uint16_t *W, int M, int K, int N
     return launch_cfg<CfgD128, false>(x, W, M, K, N, y, y_f32, partial, p.ksplit, p.k_per_split, seg, nullptr, s);
 }
 
-hipError_t launch_splitk_reduce(const float *partial, int M, int K, int N, int ksplit, void *y,
-                                bool y_f32, hipStream_t s) {
-    if (ksplit < 0) return launch_sk_reduce(partial, M, K, N, sk_plan(M, K, N), y, y_f32, s);
+hipError_t launch_splitk_reduce(const float *partial, int M, int N, int ksplit, void *y, bool y_f32,
+                                hipStream_t s) {
     const long threads = (long)M * N / 4;
     const int grid = (int)((threads + 255) / 256);
     if (y_f32)

@@ -533,40 +533,82 @@ __global__ __launch_bounds__(C::NT) void gemm_sk_kernel(const uint16_t *__restri
     }
 }
 
-// y[m][n .. n+7] = sum over the lanes that meet column panel n / BN, in lane order, of
-// their partial tiles; one thread per 8 columns of one row.
+// y[m][n .. n+7] = (partial tiles of the lanes that meet column panel n / BN, added in lane
+// order) + scale_a * sum_{j < rank_a} t[m][j] B_a[j][n .. n+7] for a = ids[m] >= 0 (rows
+// with id -1, or an id out of range, take the first term alone), rounded once into y.
+// Rows are taken in segment order (positions of perm), so rows of one adapter are neighbours
+// and share B_a's rows through L1 and L2.  A block covers 8 positions x 256 columns (one
+// panel), 8 columns per thread; blocks are handed to XCDs in contiguous runs (block b runs
+// on XCD b % 8), panel-major, so one XCD reads a panel's partial slots and B columns.
 template <class C, bool YF32>
-__global__ __launch_bounds__(256) void sk_reduce_kernel(const float *__restrict__ partial,
-                                                        int M, int K, int N, int n_tm,
-                                                        int n_tn, int L,
-                                                        void *__restrict__ y) {
-    const int groups = N / 8;
-    const long idx = (long)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= (long)M * groups) return;
-    const int m = (int)(idx / groups), n = (int)(idx % groups) * 8;
-    const int tm = m / C::BM, r = m % C::BM, p = n / C::BN, c = n % C::BN;
+__global__ __launch_bounds__(256) void sk_reduce_lora_kernel(
+    const float *__restrict__ partial, int M, int K, int N, int n_tm, int n_tn, int L, Seg seg,
+    const float *__restrict__ t, const uint16_t *__restrict__ B, const float *__restrict__ scale,
+    const int32_t *__restrict__ ids, const int32_t *__restrict__ ranks, int r_max,
+    int n_adapters, void *__restrict__ y) {
+    static_assert(C::BN == 256, "one panel per block");
+    const int G = (M + 7) / 8;  // position groups
+    const int nblk = G * n_tn;
+    int lin = blockIdx.x;
+    if ((nblk & 7) == 0) lin = (lin & 7) * (nblk >> 3) + (lin >> 3);
+    const int p = lin / G, g = lin % G;
+    const int pos = g * 8 + (threadIdx.x >> 5);
+    const int n = p * C::BN + (threadIdx.x & 31) * 8;
+    if (pos >= M || n >= N) return;
+    const int m = seg.perm[pos];
+    const int a = ids[m];
+    const int tm = m / C::BM, r = m % C::BM, c = n % C::BN;
     const int KI = K / kBK, total = n_tn * KI;
     const int k0 = p * KI, k1 = k0 + KI;
     // the lane whose range holds the panel's first step
     int l = (int)(((long)k0 * L) / total);
     while (l > 0 && sk_start(l, total, L) > k0) --l;
     while (l + 1 < L && sk_start(l + 1, total, L) <= k0) ++l;
-    float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (; l < L && sk_start(l, total, L) < k1; ++l) {
         const float *P = partial + ((size_t)((l + p) * n_tm + tm) * C::BM + r) * C::BN + c;
         const float4 u = *reinterpret_cast<const float4 *>(P);
         const float4 v = *reinterpret_cast<const float4 *>(P + 4);
-        a[0] += u.x; a[1] += u.y; a[2] += u.z; a[3] += u.w;
-        a[4] += v.x; a[5] += v.y; a[6] += v.z; a[7] += v.w;
+        acc[0] += u.x; acc[1] += u.y; acc[2] += u.z; acc[3] += u.w;
+        acc[4] += v.x; acc[5] += v.y; acc[6] += v.z; acc[7] += v.w;
+    }
+    if (a >= 0 && a < n_adapters) {
+        // rank rounded up to whole groups of 4 (entries of t and B beyond the rank are zero)
+        int rk = ranks ? ranks[a] : r_max;
+        rk = min((rk + 3) & ~3, r_max);
+        const float sc = scale[a];
+        const float *tr = t + (size_t)m * r_max;
+        const uint16_t *Bp = B + (size_t)a * r_max * N + n;
+        float d[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < rk; j += 4) {
+            const float4 tv = *reinterpret_cast<const float4 *>(tr + j);
+            const uint4 b0 = ld16(Bp + (size_t)j * N), b1 = ld16(Bp + (size_t)(j + 1) * N);
+            const uint4 b2 = ld16(Bp + (size_t)(j + 2) * N), b3 = ld16(Bp + (size_t)(j + 3) * N);
+            float f[8];
+            unpack8(b0, f);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) d[q] += tv.x * f[q];
+            unpack8(b1, f);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) d[q] += tv.y * f[q];
+            unpack8(b2, f);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) d[q] += tv.z * f[q];
+            unpack8(b3, f);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) d[q] += tv.w * f[q];
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[q] += sc * d[q];
     }
     if constexpr (YF32) {
         float *yf = reinterpret_cast<float *>(y) + (size_t)m * N + n;
-        *reinterpret_cast<float4 *>(yf) = make_float4(a[0], a[1], a[2], a[3]);
-        *reinterpret_cast<float4 *>(yf + 4) = make_float4(a[4], a[5], a[6], a[7]);
+        *reinterpret_cast<float4 *>(yf) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        *reinterpret_cast<float4 *>(yf + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
     } else {
         st16(reinterpret_cast<uint16_t *>(y) + (size_t)m * N + n,
-             make_uint4(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]),
-                        pack_bf16x2(a[4], a[5]), pack_bf16x2(a[6], a[7])));
+             make_uint4(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                        pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])));
     }
 }
 
@@ -631,16 +673,17 @@ hipError_t launch_gemm_sk(const uint16_t *x, const uint16_t *W, int M, int K, in
     return hipGetLastError();
 }
 
-hipError_t launch_sk_reduce(const float *partial, int M, int K, int N, const SkPlan &p, void *y,
-                            bool y_f32, hipStream_t s) {
-    const long threads = (long)M * (N / 8);
-    const dim3 grid((unsigned)((threads + 255) / 256));
+hipError_t launch_sk_reduce_lora(const float *partial, int M, int K, int N, const SkPlan &p,
+                                 Seg seg, const float *t, const uint16_t *B, const float *scale,
+                                 const int32_t *ids, const int32_t *ranks, int r_max,
+                                 int n_adapters, void *y, bool y_f32, hipStream_t s) {
+    const dim3 grid((unsigned)(((M + 7) / 8) * p.n_tn));
     if (y_f32)
-        launch(sk_reduce_kernel<CfgSk, true>, grid, dim3(256), 0, s, partial, M, K, N, p.n_tm,
-               p.n_tn, p.L, y);
+        launch(sk_reduce_lora_kernel<CfgSk, true>, grid, dim3(256), 0, s, partial, M, K, N, p.n_tm,
+               p.n_tn, p.L, seg, t, B, scale, ids, ranks, r_max, n_adapters, y);
     else
-        launch(sk_reduce_kernel<CfgSk, false>, grid, dim3(256), 0, s, partial, M, K, N, p.n_tm,
-               p.n_tn, p.L, y);
+        launch(sk_reduce_lora_kernel<CfgSk, false>, grid, dim3(256), 0, s, partial, M, K, N, p.n_tm,
+               p.n_tn, p.L, seg, t, B, scale, ids, ranks, r_max, n_adapters, y);
     return hipGetLastError();
 }
 

@@ -32,7 +32,7 @@ _STEP_OF_KERNEL = [
     ("shrink_finalize_kernel", "shrink_finalize"),
     ("shrink_mfma_kernel", "shrink"),
     ("splitk_reduce_kernel", "splitk_reduce"),
-    ("sk_reduce_kernel", "splitk_reduce"),
+    ("sk_reduce_lora_kernel", "decode_reduce_lora"),
     ("expand_kernel", "expand"),
     ("gemm_big_kernel", "gemm"),
     ("gemm_kernel", "gemm"),
