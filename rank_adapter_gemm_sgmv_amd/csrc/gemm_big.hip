@@ -429,6 +429,13 @@ __global__ __launch_bounds__(C::NT) void gemm_big_kernel(const uint16_t *__restr
 // both advance along the one K line.  sk_reduce_kernel adds a panel's slots in lane order,
 // so the sum does not depend on scheduling.
 
+// Lane run by the workgroups of each rank: lanes sorted by the K offset at which they
+// start inside their panel, so the ranks an XCD gets (16 when L = 128) read neighbouring
+// K slices of x and share them through that XCD's L2.
+struct SkLanes {
+    uint8_t lane[256];
+};
+
 // First K step (of the panel-major line of `total` steps) of lane l out of L.  Lanes start
 // on multiples of 4 steps and K is a multiple of 4 steps (128), so every (lane, panel) piece
 // is a whole number of trips of the 4-stage ring.
@@ -441,7 +448,7 @@ __global__ __launch_bounds__(C::NT) void gemm_sk_kernel(const uint16_t *__restri
                                                         const uint16_t *__restrict__ W,
                                                         int M, int K, int N,
                                                         float *__restrict__ partial, int n_tm,
-                                                        int n_tn, int L) {
+                                                        int n_tn, int L, SkLanes lanes) {
     __shared__ __attribute__((aligned(1024))) uint4 X0[C::XSLOT];
     __shared__ __attribute__((aligned(1024))) uint4 X1[C::XSLOT];
     __shared__ __attribute__((aligned(1024))) uint4 X2[C::XSLOT];
@@ -453,9 +460,11 @@ __global__ __launch_bounds__(C::NT) void gemm_sk_kernel(const uint16_t *__restri
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm0 = (wave / C::WN) * C::WTM, wn0 = (wave % C::WN) * C::WTN;
+    // workgroup b runs on XCD b % 8; its n_tm row tiles of one lane are consecutive there
     const int b = blockIdx.x;
-    const int tm = (b >> 3) % n_tm;
-    const int ln = (b / (8 * n_tm)) * 8 + (b & 7);
+    const int i = b >> 3;
+    const int tm = i % n_tm;
+    const int ln = lanes.lane[(b & 7) * (L >> 3) + i / n_tm];
     const int KI = K / kBK;
     const int total = n_tn * KI;
     const int s0 = sk_start(ln, total, L), s1 = sk_start(ln + 1, total, L);
@@ -668,8 +677,21 @@ size_t sk_partial_floats(const SkPlan &p) {
 
 hipError_t launch_gemm_sk(const uint16_t *x, const uint16_t *W, int M, int K, int N,
                           const SkPlan &p, float *partial, hipStream_t s) {
+    // lanes in order of (K offset of their first step inside its panel, lane)
+    const int KI = K / kBK, total = p.n_tn * KI;
+    int off[256];
+    SkLanes lanes;
+    for (int l = 0; l < p.L; ++l) {
+        off[l] = (4 * (int)(((long)l * (total / 4)) / p.L)) % KI;
+        int r = l;  // insertion sort, stable
+        while (r > 0 && off[lanes.lane[r - 1]] > off[l]) {
+            lanes.lane[r] = lanes.lane[r - 1];
+            --r;
+        }
+        lanes.lane[r] = (uint8_t)l;
+    }
     launch(gemm_sk_kernel<CfgSk>, dim3(p.L * p.n_tm), dim3(CfgSk::NT), 0, s, x, W, M, K, N,
-           partial, p.n_tm, p.n_tn, p.L);
+           partial, p.n_tm, p.n_tn, p.L, lanes);
     return hipGetLastError();
 }
 
