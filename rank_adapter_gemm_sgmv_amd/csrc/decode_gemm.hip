@@ -381,10 +381,13 @@ __global__ __launch_bounds__(256) void reduce_lora_kernel(const float *__restric
     // B_a[j, nc .. nc+3] for the adapter's rank rows, issued together (the rank is uniform
     // in the block, so rows at or beyond it are not added, and above r_max 16 not loaded)
     const int r = !has ? 0 : lo.ranks ? min(max(lo.ranks[a], 1), RM) : RM;
-    uint2 bv[RM];
+    // the first BCH rank rows of B are loaded here; above r_max 16 the rest follow in chunks
+    // of 16 rows after t is summed (all 64 at once would take 128 registers)
+    constexpr int BCH = RM <= 16 ? RM : 16;
+    uint2 bv[BCH];
     const uint16_t *bp = lo.B + (size_t)a * RM * N + nc;
 #pragma unroll
-    for (int j = 0; j < RM; ++j) {
+    for (int j = 0; j < BCH; ++j) {
         // at r_max <= 16 every row is loaded (the pool's padding rows exist), so the loads
         // need not wait for the rank
         if constexpr (RM <= 16) bv[j] = *reinterpret_cast<const uint2 *>(bp + (size_t)j * N);
@@ -435,12 +438,25 @@ __global__ __launch_bounds__(256) void reduce_lora_kernel(const float *__restric
     if (has) {
         float d0 = 0.f, d1 = 0.f, d2 = 0.f, d3 = 0.f;
 #pragma unroll
-        for (int j = 0; j < RM; ++j) {
+        for (int j = 0; j < BCH; ++j) {
             const float tj = j < r ? s_t[j] : 0.0f;  // rows past the rank add nothing
             d0 = fmaf(tj, bf16_lo(bv[j].x), d0);
             d1 = fmaf(tj, bf16_hi(bv[j].x), d1);
             d2 = fmaf(tj, bf16_lo(bv[j].y), d2);
             d3 = fmaf(tj, bf16_hi(bv[j].y), d3);
+        }
+        for (int j0 = BCH; j0 < r; j0 += BCH) {  // r is uniform in the block
+#pragma unroll
+            for (int j = 0; j < BCH; ++j)
+                bv[j] = j0 + j < r ? *reinterpret_cast<const uint2 *>(bp + (size_t)(j0 + j) * N) : make_uint2(0, 0);
+#pragma unroll
+            for (int j = 0; j < BCH; ++j) {
+                const float tj = j0 + j < r ? s_t[j0 + j] : 0.0f;
+                d0 = fmaf(tj, bf16_lo(bv[j].x), d0);
+                d1 = fmaf(tj, bf16_hi(bv[j].x), d1);
+                d2 = fmaf(tj, bf16_lo(bv[j].y), d2);
+                d3 = fmaf(tj, bf16_hi(bv[j].y), d3);
+            }
         }
         const float sc = lo.scale[a];
         acc.x = fmaf(sc, d0, acc.x); acc.y = fmaf(sc, d1, acc.y);
