@@ -206,7 +206,7 @@ lora_status_t check_linear(const void *x, const void *W, const void *A, const vo
 //   decode, 128 < M <= 256 and d_in % 32 == 0: build_segments, shrink (chunk sums), the
 //            split-K GEMM, the ordered reduction with the expand
 //   decode, 256 < M <= 1024, d_in % 128 == 0 and few 256 x 256 tiles: build_segments,
-//            shrink, shrink_finalize, the stream-K GEMM, one pass adding its partial tiles
+//            shrink (chunk sums), the stream-K GEMM, one pass adding its partial tiles, t
 //            and the expand
 //   decode otherwise: build_segments, shrink, shrink_finalize, gemm [, splitk_reduce], expand
 //   prefill: build_segments, shrink, shrink_finalize, gemm with the LoRA epilogue
@@ -272,9 +272,13 @@ hipError_t run_linear(const void *x, const void *W, const void *A, const void *B
                            sg, spart, kc, ksplit, s)) != hipSuccess)
         return e;
     mark(mk, "shrink");
-    if ((e = launch_shrink_finalize(spart, M, r_max, ksplit, sg, t, s)) != hipSuccess)
-        return e;
-    mark(mk, "shrink_finalize");
+    // the stream-K reduction adds the shrink's chunk sums itself; the other consumers read t
+    const bool stream_k = !prefill && sk_plan(M, d_in, d_out).use;
+    if (!stream_k) {
+        if ((e = launch_shrink_finalize(spart, M, r_max, ksplit, sg, t, s)) != hipSuccess)
+            return e;
+        mark(mk, "shrink_finalize");
+    }
     int gsplit = 1;
     if (prefill) {
         LoraEpilogue ep{t, Bb, scale, ids, r_max, n_adapters};
@@ -288,9 +292,11 @@ hipError_t run_linear(const void *x, const void *W, const void *A, const void *B
         return e;
     mark(mk, "gemm_decode");
     if (gsplit < 0) {
-        // stream-K partial tiles: one pass adds them and the expand, rows in segment order
-        if ((e = launch_sk_reduce_lora(gpart, M, d_in, d_out, sk_plan(M, d_in, d_out), sg, t, Bb,
-                                       scale, ids, ranks, r_max, n_adapters, y, yf, s)) != hipSuccess)
+        // stream-K partial tiles: one pass adds them, t from the chunk sums, and the expand,
+        // rows in segment order
+        if ((e = launch_sk_reduce_lora(gpart, M, d_in, d_out, sk_plan(M, d_in, d_out), sg, spart,
+                                       ksplit, Bb, scale, ids, ranks, r_max, n_adapters, y, yf,
+                                       s)) != hipSuccess)
             return e;
         mark(mk, "decode_reduce_lora");
         return hipSuccess;

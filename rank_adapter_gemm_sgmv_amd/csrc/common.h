@@ -128,11 +128,12 @@ size_t sk_partial_floats(const SkPlan &p);
 hipError_t launch_gemm_sk(const uint16_t *x, const uint16_t *W, int M, int K, int N,
                           const SkPlan &p, float *partial, hipStream_t s);
 // y = (the stream-K partial tiles added in lane order) + scale_a t B_a on rows with an
-// adapter, rows in segment order; rounds once into y.
+// adapter, rows in segment order; t summed from the shrink's n_chunks chunk sums; rounds
+// once into y.
 hipError_t launch_sk_reduce_lora(const float *partial, int M, int K, int N, const SkPlan &p,
-                                 Seg seg, const float *t, const uint16_t *B, const float *scale,
-                                 const int32_t *ids, const int32_t *ranks, int r_max,
-                                 int n_adapters, void *y, bool y_f32, hipStream_t s);
+                                 Seg seg, const float *tpart, int n_chunks, const uint16_t *B,
+                                 const float *scale, const int32_t *ids, const int32_t *ranks,
+                                 int r_max, int n_adapters, void *y, bool y_f32, hipStream_t s);
 
 // Adds the split-K decode GEMM's ksplit > 1 partial slices into y, in order.
 hipError_t launch_splitk_reduce(const float *partial, int M, int N, int ksplit, void *y,

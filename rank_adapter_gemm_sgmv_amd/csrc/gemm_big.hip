@@ -545,6 +545,9 @@ __global__ __launch_bounds__(C::NT) void gemm_sk_kernel(const uint16_t *__restri
 // y[m][n .. n+7] = (partial tiles of the lanes that meet column panel n / BN, added in lane
 // order) + scale_a * sum_{j < rank_a} t[m][j] B_a[j][n .. n+7] for a = ids[m] >= 0 (rows
 // with id -1, or an id out of range, take the first term alone), rounded once into y.
+// t comes as the shrink's k-chunk partial sums [n_chunks][M][r_max]: each block adds them for
+// its 8 rows in LDS (threads of one (row, 4 ranks) group take every TPP-th chunk, and their
+// sums are combined in thread order, so t does not depend on scheduling).
 // Rows are taken in segment order (positions of perm), so rows of one adapter are neighbours
 // and share B_a's rows through L1 and L2.  A block covers 8 positions x 256 columns (one
 // panel), 8 columns per thread; blocks are handed to XCDs in contiguous runs (block b runs
@@ -552,45 +555,81 @@ __global__ __launch_bounds__(C::NT) void gemm_sk_kernel(const uint16_t *__restri
 template <class C, bool YF32>
 __global__ __launch_bounds__(256) void sk_reduce_lora_kernel(
     const float *__restrict__ partial, int M, int K, int N, int n_tm, int n_tn, int L, Seg seg,
-    const float *__restrict__ t, const uint16_t *__restrict__ B, const float *__restrict__ scale,
-    const int32_t *__restrict__ ids, const int32_t *__restrict__ ranks, int r_max,
-    int n_adapters, void *__restrict__ y) {
+    const float *__restrict__ tpart, int n_chunks, const uint16_t *__restrict__ B,
+    const float *__restrict__ scale, const int32_t *__restrict__ ids,
+    const int32_t *__restrict__ ranks, int r_max, int n_adapters, void *__restrict__ y) {
     static_assert(C::BN == 256, "one panel per block");
+    __shared__ float4 s_part[256];
+    __shared__ float s_t[8][64];
     const int G = (M + 7) / 8;  // position groups
     const int nblk = G * n_tn;
     int lin = blockIdx.x;
     if ((nblk & 7) == 0) lin = (lin & 7) * (nblk >> 3) + (lin >> 3);
     const int p = lin / G, g = lin % G;
-    const int pos = g * 8 + (threadIdx.x >> 5);
+    const int pl = threadIdx.x >> 5;
+    const int pos = g * 8 + pl;
     const int n = p * C::BN + (threadIdx.x & 31) * 8;
-    if (pos >= M || n >= N) return;
-    const int m = seg.perm[pos];
-    const int a = ids[m];
-    const int tm = m / C::BM, r = m % C::BM, c = n % C::BN;
-    const int KI = K / kBK, total = n_tn * KI;
-    const int k0 = p * KI, k1 = k0 + KI;
-    // the lane whose range holds the panel's first step
-    int l = (int)(((long)k0 * L) / total);
-    while (l > 0 && sk_start(l, total, L) > k0) --l;
-    while (l + 1 < L && sk_start(l + 1, total, L) <= k0) ++l;
+    const bool live = pos < M && n < N;
+    // this thread's partial tiles first, so their loads overlap the t sums below
+    int m = 0, a = -1;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (; l < L && sk_start(l, total, L) < k1; ++l) {
-        const float *P = partial + ((size_t)((l + p) * n_tm + tm) * C::BM + r) * C::BN + c;
-        const float4 u = *reinterpret_cast<const float4 *>(P);
-        const float4 v = *reinterpret_cast<const float4 *>(P + 4);
-        acc[0] += u.x; acc[1] += u.y; acc[2] += u.z; acc[3] += u.w;
-        acc[4] += v.x; acc[5] += v.y; acc[6] += v.z; acc[7] += v.w;
+    if (live) {
+        m = seg.perm[pos];
+        a = ids[m];
+        const int tm = m / C::BM, r = m % C::BM, c = n % C::BN;
+        const int KI = K / kBK, total = n_tn * KI;
+        const int k0 = p * KI, k1 = k0 + KI;
+        // the lane whose range holds the panel's first step
+        int l = (int)(((long)k0 * L) / total);
+        while (l > 0 && sk_start(l, total, L) > k0) --l;
+        while (l + 1 < L && sk_start(l + 1, total, L) <= k0) ++l;
+        for (; l < L && sk_start(l, total, L) < k1; ++l) {
+            const float *P = partial + ((size_t)((l + p) * n_tm + tm) * C::BM + r) * C::BN + c;
+            const float4 u = *reinterpret_cast<const float4 *>(P);
+            const float4 v = *reinterpret_cast<const float4 *>(P + 4);
+            acc[0] += u.x; acc[1] += u.y; acc[2] += u.z; acc[3] += u.w;
+            acc[4] += v.x; acc[5] += v.y; acc[6] += v.z; acc[7] += v.w;
+        }
     }
+    {
+        // t of the block's rows: group q = (row, ranks 4 jq .. 4 jq + 3), TPP threads each
+        const int groups = 8 * (r_max / 4), TPP = 256 / groups;
+        const int q = threadIdx.x / TPP, h = threadIdx.x % TPP;
+        const int rl = q / (r_max / 4), jq = q % (r_max / 4);
+        const int ps = g * 8 + rl;
+        float4 ts = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (ps < M && ps < seg.meta[1]) {  // a LoRA row: its chunk sums were written
+            const float *src = tpart + (size_t)seg.perm[ps] * r_max + 4 * jq;
+            const size_t cs = (size_t)M * r_max;
+            for (int ch = h; ch < n_chunks; ch += TPP) {
+                const float4 v = *reinterpret_cast<const float4 *>(src + ch * cs);
+                ts.x += v.x; ts.y += v.y; ts.z += v.z; ts.w += v.w;
+            }
+        }
+        s_part[threadIdx.x] = ts;
+        __syncthreads();
+        if (h == 0) {
+            float4 tv = s_part[threadIdx.x];
+            for (int i = 1; i < TPP; ++i) {
+                const float4 v = s_part[threadIdx.x + i];
+                tv.x += v.x; tv.y += v.y; tv.z += v.z; tv.w += v.w;
+            }
+            s_t[rl][4 * jq] = tv.x; s_t[rl][4 * jq + 1] = tv.y;
+            s_t[rl][4 * jq + 2] = tv.z; s_t[rl][4 * jq + 3] = tv.w;
+        }
+        __syncthreads();
+    }
+    if (!live) return;
     if (a >= 0 && a < n_adapters) {
         // rank rounded up to whole groups of 4 (entries of t and B beyond the rank are zero)
         int rk = ranks ? ranks[a] : r_max;
         rk = min((rk + 3) & ~3, r_max);
         const float sc = scale[a];
-        const float *tr = t + (size_t)m * r_max;
+        const float *tr = &s_t[pl][0];
         const uint16_t *Bp = B + (size_t)a * r_max * N + n;
         float d[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         for (int j = 0; j < rk; j += 4) {
-            const float4 tv = *reinterpret_cast<const float4 *>(tr + j);
+            const float4 tv = make_float4(tr[j], tr[j + 1], tr[j + 2], tr[j + 3]);
             const uint4 b0 = ld16(Bp + (size_t)j * N), b1 = ld16(Bp + (size_t)(j + 1) * N);
             const uint4 b2 = ld16(Bp + (size_t)(j + 2) * N), b3 = ld16(Bp + (size_t)(j + 3) * N);
             float f[8];
@@ -696,16 +735,17 @@ hipError_t launch_gemm_sk(const uint16_t *x, const uint16_t *W, int M, int K, in
 }
 
 hipError_t launch_sk_reduce_lora(const float *partial, int M, int K, int N, const SkPlan &p,
-                                 Seg seg, const float *t, const uint16_t *B, const float *scale,
-                                 const int32_t *ids, const int32_t *ranks, int r_max,
-                                 int n_adapters, void *y, bool y_f32, hipStream_t s) {
+                                 Seg seg, const float *tpart, int n_chunks, const uint16_t *B,
+                                 const float *scale, const int32_t *ids, const int32_t *ranks,
+                                 int r_max, int n_adapters, void *y, bool y_f32, hipStream_t s) {
+    if (r_max < 8 || r_max > 64 || (r_max & (r_max - 1)) != 0) return hipErrorInvalidValue;
     const dim3 grid((unsigned)(((M + 7) / 8) * p.n_tn));
     if (y_f32)
         launch(sk_reduce_lora_kernel<CfgSk, true>, grid, dim3(256), 0, s, partial, M, K, N, p.n_tm,
-               p.n_tn, p.L, seg, t, B, scale, ids, ranks, r_max, n_adapters, y);
+               p.n_tn, p.L, seg, tpart, n_chunks, B, scale, ids, ranks, r_max, n_adapters, y);
     else
         launch(sk_reduce_lora_kernel<CfgSk, false>, grid, dim3(256), 0, s, partial, M, K, N, p.n_tm,
-               p.n_tn, p.L, seg, t, B, scale, ids, ranks, r_max, n_adapters, y);
+               p.n_tn, p.L, seg, tpart, n_chunks, B, scale, ids, ranks, r_max, n_adapters, y);
     return hipGetLastError();
 }
 
