@@ -150,6 +150,32 @@ lora_status_t lora_linear(const void *x, const void *W, const void *A, const voi
                           lora_dtype_t y_dtype, lora_mode_t mode, void *ws,
                           size_t ws_bytes, void *stream);
 
+/* The whole layer, as lora_linear, on a rank-compact adapter pool: no adapter is padded to
+ * r_max.  Padding every adapter to the largest rank wastes memory and bandwidth when ranks
+ * differ ([P1], "Where does multi-LoRA serving actually break?"); serving mixed ranks is
+ * what good systems support ([P2], "Limits and pitfalls"), S-LoRA by keeping adapters of
+ * different ranks together in one pool ([P3], "How S-LoRA Proved the Model").  Layout (all
+ * device memory, caller-owned):
+ *   ranks[i]         rank r_i of adapter i: a multiple of 8 in [8, r_max]
+ *   rank_offsets[i]  its first rank row: r_0 + ... + r_{i-1} for a packed pool (any
+ *                    non-overlapping placement with rank_offsets[i] + r_i <= pool_rows works)
+ *   A                bf16 [pool_rows * d_in]: A_i = [d_in][r_i] row-major at element
+ *                    rank_offsets[i] * d_in
+ *   B                bf16 [pool_rows][d_out]: B_i = rows rank_offsets[i] .. + r_i - 1
+ *   pool_rows        rank rows in the pool, 1 <= pool_rows <= n_adapters * r_max
+ * scale[i] = alpha_i / r_i as for lora_linear.  An adapter whose rank is not a multiple of 8
+ * or whose rows leave the pool adds nothing (the kernels never read outside the pool).
+ * Returns LORA_ERR_NULL when ranks or rank_offsets is NULL, LORA_ERR_SHAPE when pool_rows is
+ * out of range, otherwise as lora_linear.  The result equals lora_linear's on the same
+ * adapters zero-padded to r_max (up to the order of fp32 additions). */
+lora_status_t lora_linear_compact(const void *x, const void *W, const void *A, const void *B,
+                                  const float *scale, const int32_t *ranks,
+                                  const int32_t *rank_offsets, int32_t pool_rows,
+                                  const int32_t *ids, int32_t M, int32_t d_in, int32_t d_out,
+                                  int32_t r_max, int32_t n_adapters, const lora_segments_t *segs,
+                                  void *y, lora_dtype_t y_dtype, lora_mode_t mode, void *ws,
+                                  size_t ws_bytes, void *stream);
+
 /* Measurement aid, not for serving loops: the same launches as lora_linear, each launched
  * with a start and a stop HIP event that the GPU stamps from that kernel's own dispatch (no
  * extra packet between kernels), so the times are kernel durations.  It then waits for the
@@ -165,6 +191,15 @@ lora_status_t lora_linear_profiled(const void *x, const void *W, const void *A, 
                                    size_t ws_bytes, void *stream, float *kernel_ms,
                                    const char **kernel_names, int32_t max_kernels,
                                    int32_t *n_kernels);
+
+/* Measurement aid: lora_linear_profiled for lora_linear_compact's arguments. */
+lora_status_t lora_linear_compact_profiled(
+    const void *x, const void *W, const void *A, const void *B, const float *scale,
+    const int32_t *ranks, const int32_t *rank_offsets, int32_t pool_rows, const int32_t *ids,
+    int32_t M, int32_t d_in, int32_t d_out, int32_t r_max, int32_t n_adapters,
+    const lora_segments_t *segs, void *y, lora_dtype_t y_dtype, lora_mode_t mode, void *ws,
+    size_t ws_bytes, void *stream, float *kernel_ms, const char **kernel_names,
+    int32_t max_kernels, int32_t *n_kernels);
 
 /* Human-readable name of a status. */
 const char *lora_status_string(lora_status_t status);

@@ -133,7 +133,8 @@ lora_status_t lora_shrink(const void *x, const void *A, const int32_t *ranks, in
     float *partial = static_cast<float *>(ws);
     const Seg sg = to_seg(seg);
     hipError_t e = launch_shrink(static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(A),
-                                 ranks, M, d_in, r_max, n_adapters, sg, partial, kc, ksplit, s);
+                                 ranks, nullptr, 0, M, d_in, r_max, n_adapters, sg, partial, kc,
+                                 ksplit, s);
     if (e == hipSuccess) e = launch_shrink_finalize(partial, M, r_max, ksplit, sg, t, s);
     return hip_status(e);
 }
@@ -152,9 +153,9 @@ lora_status_t lora_expand(const float *t, const void *B, const float *scale, con
         (ranks && !aligned(ranks, 4)))
         return LORA_ERR_ALIGN;
     clear_stale_error();
-    return hip_status(launch_expand(t, static_cast<const uint16_t *>(B), scale, ranks, M, d_out,
-                                    r_max, n_adapters, to_seg(seg), y, y_dtype == LORA_F32,
-                                    (hipStream_t)stream));
+    return hip_status(launch_expand(t, static_cast<const uint16_t *>(B), scale, ranks, nullptr, 0,
+                                    M, d_out, r_max, n_adapters, to_seg(seg), y,
+                                    y_dtype == LORA_F32, (hipStream_t)stream));
 }
 
 }  // extern "C"
@@ -198,6 +199,16 @@ lora_status_t check_linear(const void *x, const void *W, const void *A, const vo
     return LORA_OK;
 }
 
+// Extra arguments of a rank-compact pool: the table of first rank rows and the pool's
+// rank-row count (at least one row, at most what the padded pool would hold).
+lora_status_t check_compact(const int32_t *ranks, const int32_t *rank_offsets, int32_t pool_rows,
+                            int32_t r_max, int32_t n_adapters) {
+    if (!ranks || !rank_offsets) return LORA_ERR_NULL;
+    if (!aligned(rank_offsets, 4)) return LORA_ERR_ALIGN;
+    if (pool_rows < 1 || (int64_t)pool_rows > (int64_t)n_adapters * r_max) return LORA_ERR_SHAPE;
+    return LORA_OK;
+}
+
 // The launch sequence of lora_linear (arguments already validated, M > 0).
 //   decode, M <= 128 and d_in % 32 == 0: one split-K GEMM over W and the batch's adapters'
 //            A laid side by side (the shrink as extra column tiles), then the ordered
@@ -211,8 +222,9 @@ lora_status_t check_linear(const void *x, const void *W, const void *A, const vo
 //   decode otherwise: build_segments, shrink, shrink_finalize, gemm [, splitk_reduce], expand
 //   prefill: build_segments, shrink, shrink_finalize, gemm with the LoRA epilogue
 hipError_t run_linear(const void *x, const void *W, const void *A, const void *B,
-                      const float *scale, const int32_t *ranks, const int32_t *ids, int32_t M,
-                      int32_t d_in, int32_t d_out, int32_t r_max, int32_t n_adapters,
+                      const float *scale, const int32_t *ranks, const int32_t *roff,
+                      int32_t pool_rows, const int32_t *ids, int32_t M, int32_t d_in,
+                      int32_t d_out, int32_t r_max, int32_t n_adapters,
                       const lora_segments_t *segs, void *y, lora_dtype_t y_dtype, lora_mode_t mode,
                       void *ws, hipStream_t s, Marker *mk) {
     const bool prefill = mode == LORA_MODE_PREFILL || (mode == LORA_MODE_AUTO && M >= LORA_PREFILL_MIN_ROWS);
@@ -231,11 +243,13 @@ hipError_t run_linear(const void *x, const void *W, const void *A, const void *B
     hipError_t e;
     int kc, ksplit;
     shrink_plan(d_in, r_max, &kc, &ksplit);
-    if (!prefill && decode_fused_supported(M, d_in, d_out)) {
+    // (the fused path lays adapters side by side at row stride r_max: padded pools only)
+    if (!prefill && roff == nullptr && decode_fused_supported(M, d_in, d_out)) {
         // small decode batch: x W and the shrink x A_i as tiles of one split-K GEMM (the
         // row -> adapter slot map, when needed, goes to the t region), then one reduction
         // adds the splits and the expand
-        const DecodeLora lo{nullptr, 0, reinterpret_cast<int32_t *>(t), Bb, scale, ids, ranks, r_max, n_adapters};
+        const DecodeLora lo{nullptr, 0, reinterpret_cast<int32_t *>(t), Bb, scale, ids, ranks, r_max,
+                            n_adapters, nullptr, 0};
         if ((e = launch_decode_gemm(xb, Wb, static_cast<const uint16_t *>(A), M, d_in, d_out, lo,
                                     true, gpart, s)) != hipSuccess)
             return e;
@@ -252,8 +266,9 @@ hipError_t run_linear(const void *x, const void *W, const void *A, const void *B
             if ((e = launch_build_segments(ids, M, n_adapters, sg, s)) != hipSuccess) return e;
             mark(mk, "build_segments");
         }
-        const DecodeLora lo{spart, ksplit, nullptr, Bb, scale, ids, ranks, r_max, n_adapters};
-        if ((e = launch_shrink(xb, static_cast<const uint16_t *>(A), ranks, M, d_in, r_max, n_adapters,
+        const DecodeLora lo{spart, ksplit, nullptr, Bb, scale, ids, ranks, r_max, n_adapters, roff,
+                            pool_rows};
+        if ((e = launch_shrink(xb, static_cast<const uint16_t *>(A), ranks, roff, pool_rows, M, d_in, r_max, n_adapters,
                                sg, spart, kc, ksplit, s)) != hipSuccess)
             return e;
         mark(mk, "shrink");
@@ -268,7 +283,7 @@ hipError_t run_linear(const void *x, const void *W, const void *A, const void *B
         if ((e = launch_build_segments(ids, M, n_adapters, sg, s)) != hipSuccess) return e;
         mark(mk, "build_segments");
     }
-    if ((e = launch_shrink(xb, static_cast<const uint16_t *>(A), ranks, M, d_in, r_max, n_adapters,
+    if ((e = launch_shrink(xb, static_cast<const uint16_t *>(A), ranks, roff, pool_rows, M, d_in, r_max, n_adapters,
                            sg, spart, kc, ksplit, s)) != hipSuccess)
         return e;
     mark(mk, "shrink");
@@ -281,7 +296,7 @@ hipError_t run_linear(const void *x, const void *W, const void *A, const void *B
     }
     int gsplit = 1;
     if (prefill) {
-        LoraEpilogue ep{t, Bb, scale, ids, r_max, n_adapters};
+        LoraEpilogue ep{t, Bb, scale, ids, r_max, n_adapters, ranks, roff, pool_rows};
         if ((e = launch_gemm(xb, Wb, M, d_in, d_out, y, yf, true, sg, &ep, nullptr, 0, &gsplit, s)) != hipSuccess)
             return e;
         mark(mk, "gemm_prefill_lora");
@@ -295,8 +310,8 @@ hipError_t run_linear(const void *x, const void *W, const void *A, const void *B
         // stream-K partial tiles: one pass adds them, t from the chunk sums, and the expand,
         // rows in segment order
         if ((e = launch_sk_reduce_lora(gpart, M, d_in, d_out, sk_plan(M, d_in, d_out), sg, spart,
-                                       ksplit, Bb, scale, ids, ranks, r_max, n_adapters, y, yf,
-                                       s)) != hipSuccess)
+                                       ksplit, Bb, scale, ids, ranks, roff, pool_rows, r_max,
+                                       n_adapters, y, yf, s)) != hipSuccess)
             return e;
         mark(mk, "decode_reduce_lora");
         return hipSuccess;
@@ -305,7 +320,8 @@ hipError_t run_linear(const void *x, const void *W, const void *A, const void *B
         if ((e = launch_splitk_reduce(gpart, M, d_out, gsplit, y, yf, s)) != hipSuccess) return e;
         mark(mk, "splitk_reduce");
     }
-    if ((e = launch_expand(t, Bb, scale, ranks, M, d_out, r_max, n_adapters, sg, y, yf, s)) != hipSuccess)
+    if ((e = launch_expand(t, Bb, scale, ranks, roff, pool_rows, M, d_out, r_max, n_adapters, sg, y,
+                           yf, s)) != hipSuccess)
         return e;
     mark(mk, "expand");
     return hipSuccess;
@@ -324,23 +340,41 @@ lora_status_t lora_linear(const void *x, const void *W, const void *A, const voi
                                     segs, y, y_dtype, mode, ws, ws_bytes);
     if (st != LORA_OK || M == 0) return st;
     clear_stale_error();
-    return hip_status(run_linear(x, W, A, B, scale, ranks, ids, M, d_in, d_out, r_max, n_adapters,
-                                 segs, y, y_dtype, mode, ws, (hipStream_t)stream, nullptr));
+    return hip_status(run_linear(x, W, A, B, scale, ranks, nullptr, 0, ids, M, d_in, d_out, r_max,
+                                 n_adapters, segs, y, y_dtype, mode, ws, (hipStream_t)stream,
+                                 nullptr));
 }
 
-lora_status_t lora_linear_profiled(const void *x, const void *W, const void *A, const void *B,
-                                   const float *scale, const int32_t *ranks, const int32_t *ids,
-                                   int32_t M, int32_t d_in, int32_t d_out, int32_t r_max,
-                                   int32_t n_adapters, const lora_segments_t *segs, void *y,
-                                   lora_dtype_t y_dtype, lora_mode_t mode, void *ws,
-                                   size_t ws_bytes, void *stream, float *kernel_ms,
-                                   const char **kernel_names, int32_t max_kernels,
-                                   int32_t *n_kernels) {
-    if (!kernel_ms || !kernel_names || !n_kernels || max_kernels < 0) return LORA_ERR_NULL;
-    *n_kernels = 0;
+lora_status_t lora_linear_compact(const void *x, const void *W, const void *A, const void *B,
+                                  const float *scale, const int32_t *ranks,
+                                  const int32_t *rank_offsets, int32_t pool_rows,
+                                  const int32_t *ids, int32_t M, int32_t d_in, int32_t d_out,
+                                  int32_t r_max, int32_t n_adapters, const lora_segments_t *segs,
+                                  void *y, lora_dtype_t y_dtype, lora_mode_t mode, void *ws,
+                                  size_t ws_bytes, void *stream) {
     lora_status_t st = check_linear(x, W, A, B, scale, ranks, ids, M, d_in, d_out, r_max, n_adapters,
                                     segs, y, y_dtype, mode, ws, ws_bytes);
+    if (st == LORA_OK) st = check_compact(ranks, rank_offsets, pool_rows, r_max, n_adapters);
     if (st != LORA_OK || M == 0) return st;
+    clear_stale_error();
+    return hip_status(run_linear(x, W, A, B, scale, ranks, rank_offsets, pool_rows, ids, M, d_in,
+                                 d_out, r_max, n_adapters, segs, y, y_dtype, mode, ws,
+                                 (hipStream_t)stream, nullptr));
+}
+
+}  // extern "C"
+
+namespace {
+
+// lora_linear / lora_linear_compact with each launch timed by start / stop events taken
+// from its own dispatch packet (arguments already validated, M > 0).
+lora_status_t run_profiled(const void *x, const void *W, const void *A, const void *B,
+                           const float *scale, const int32_t *ranks, const int32_t *roff,
+                           int32_t pool_rows, const int32_t *ids, int32_t M, int32_t d_in,
+                           int32_t d_out, int32_t r_max, int32_t n_adapters,
+                           const lora_segments_t *segs, void *y, lora_dtype_t y_dtype,
+                           lora_mode_t mode, void *ws, void *stream, float *kernel_ms,
+                           const char **kernel_names, int32_t max_kernels, int32_t *n_kernels) {
     clear_stale_error();
     KernelTimer timer;
     hipError_t e = hipSuccess;
@@ -352,8 +386,8 @@ lora_status_t lora_linear_profiled(const void *x, const void *W, const void *A, 
     Marker mk;
     if (e == hipSuccess) {
         g_timer = &timer;
-        e = run_linear(x, W, A, B, scale, ranks, ids, M, d_in, d_out, r_max, n_adapters, segs, y,
-                       y_dtype, mode, ws, (hipStream_t)stream, &mk);
+        e = run_linear(x, W, A, B, scale, ranks, roff, pool_rows, ids, M, d_in, d_out, r_max,
+                       n_adapters, segs, y, y_dtype, mode, ws, (hipStream_t)stream, &mk);
         g_timer = nullptr;
     }
     if (e == hipSuccess && timer.n > 0) e = hipEventSynchronize(timer.stop[timer.n - 1]);
@@ -372,6 +406,46 @@ lora_status_t lora_linear_profiled(const void *x, const void *W, const void *A, 
         if (timer.stop[i]) (void)hipEventDestroy(timer.stop[i]);
     }
     return hip_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+lora_status_t lora_linear_profiled(const void *x, const void *W, const void *A, const void *B,
+                                   const float *scale, const int32_t *ranks, const int32_t *ids,
+                                   int32_t M, int32_t d_in, int32_t d_out, int32_t r_max,
+                                   int32_t n_adapters, const lora_segments_t *segs, void *y,
+                                   lora_dtype_t y_dtype, lora_mode_t mode, void *ws,
+                                   size_t ws_bytes, void *stream, float *kernel_ms,
+                                   const char **kernel_names, int32_t max_kernels,
+                                   int32_t *n_kernels) {
+    if (!kernel_ms || !kernel_names || !n_kernels || max_kernels < 0) return LORA_ERR_NULL;
+    *n_kernels = 0;
+    lora_status_t st = check_linear(x, W, A, B, scale, ranks, ids, M, d_in, d_out, r_max, n_adapters,
+                                    segs, y, y_dtype, mode, ws, ws_bytes);
+    if (st != LORA_OK || M == 0) return st;
+    return run_profiled(x, W, A, B, scale, ranks, nullptr, 0, ids, M, d_in, d_out, r_max,
+                        n_adapters, segs, y, y_dtype, mode, ws, stream, kernel_ms, kernel_names,
+                        max_kernels, n_kernels);
+}
+
+lora_status_t lora_linear_compact_profiled(
+    const void *x, const void *W, const void *A, const void *B, const float *scale,
+    const int32_t *ranks, const int32_t *rank_offsets, int32_t pool_rows, const int32_t *ids,
+    int32_t M, int32_t d_in, int32_t d_out, int32_t r_max, int32_t n_adapters,
+    const lora_segments_t *segs, void *y, lora_dtype_t y_dtype, lora_mode_t mode, void *ws,
+    size_t ws_bytes, void *stream, float *kernel_ms, const char **kernel_names,
+    int32_t max_kernels, int32_t *n_kernels) {
+    if (!kernel_ms || !kernel_names || !n_kernels || max_kernels < 0) return LORA_ERR_NULL;
+    *n_kernels = 0;
+    lora_status_t st = check_linear(x, W, A, B, scale, ranks, ids, M, d_in, d_out, r_max, n_adapters,
+                                    segs, y, y_dtype, mode, ws, ws_bytes);
+    if (st == LORA_OK) st = check_compact(ranks, rank_offsets, pool_rows, r_max, n_adapters);
+    if (st != LORA_OK || M == 0) return st;
+    return run_profiled(x, W, A, B, scale, ranks, rank_offsets, pool_rows, ids, M, d_in, d_out,
+                        r_max, n_adapters, segs, y, y_dtype, mode, ws, stream, kernel_ms,
+                        kernel_names, max_kernels, n_kernels);
 }
 
 const char *lora_status_string(lora_status_t status) {

@@ -57,7 +57,8 @@ struct MfmaShrink {
 template <int RM>
 __global__ __launch_bounds__(64 * kWavesPerBlock) void shrink_mfma_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ A, const int32_t *__restrict__ ranks,
-    int M, int d_in, Seg seg, float *__restrict__ partial, int n_chunks, int kc) {
+    const int32_t *__restrict__ roff, int pool_rows, int M, int d_in, Seg seg,
+    float *__restrict__ partial, int n_chunks, int kc) {
     using C = MfmaShrink<RM>;
     __shared__ __attribute__((aligned(16))) char lds[kWavesPerBlock][C::LDS];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -74,12 +75,16 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void shrink_mfma_kernel(
         const int tile = w / n_chunks, c = w % n_chunks;
         const int p0 = seg.tiles[2 * tile], a = seg.tiles[2 * tile + 1];
         const int rows = min(p0 + kTileRows, seg.offsets[a + 1]) - p0;
-        const int r = ranks ? min(max(ranks[a], 0), RM) : RM;
+        int r = ranks ? min(max(ranks[a], 0), RM) : RM;
+        const int row0 = adapter_row0(roff, pool_rows, a, RM, r);
+        // row stride of A_a: r_max in a padded pool, the rank in a compact one, where the
+        // groups at or beyond the rank are not loaded (they belong to the next adapter)
+        const int rs = roff ? r : RM;
         const int k_lo = c * kc, k_hi = min(k_lo + kc, d_in);
         // this lane's x row (rows beyond the tile repeat its last row; their sums are dropped)
         const int mrow = seg.perm[p0 + min(li, rows - 1)];
         const uint16_t *xr = x + (size_t)mrow * d_in;
-        const uint16_t *Aa = A + (size_t)a * d_in * RM;
+        const uint16_t *Aa = A + (size_t)row0 * d_in;
 
         f32x4_t acc[C::NB];
 #pragma unroll
@@ -91,7 +96,8 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void shrink_mfma_kernel(
 #pragma unroll
             for (int i = 0; i < C::AL; ++i) {
                 const int f = lane + 64 * i, kr = kb + f / C::GR, gr = f % C::GR;
-                av[i] = ld16(Aa + (size_t)min(kr, d_in - 1) * RM + gr * 8);
+                av[i] = (roff == nullptr || gr * 8 < r) ? ld16(Aa + (size_t)min(kr, d_in - 1) * rs + gr * 8)
+                                                        : make_uint4(0, 0, 0, 0);
             }
             uint4 xv[C::STEPS];
 #pragma unroll
@@ -173,18 +179,19 @@ void shrink_plan(int d_in, int r_max, int *kc, int *ksplit) {
     *ksplit = (d_in + *kc - 1) / *kc;
 }
 
-hipError_t launch_shrink(const uint16_t *x, const uint16_t *A, const int32_t *ranks, int M,
-                         int d_in, int r_max, int n_adapters, Seg seg, float *partial, int kc,
-                         int ksplit, hipStream_t s) {
+hipError_t launch_shrink(const uint16_t *x, const uint16_t *A, const int32_t *ranks,
+                         const int32_t *roff, int pool_rows, int M, int d_in, int r_max,
+                         int n_adapters, Seg seg, float *partial, int kc, int ksplit,
+                         hipStream_t s) {
     const long items = (long)lora_max_tiles(M, n_adapters) * ksplit;
     const long wblocks = (items + kWavesPerBlock - 1) / kWavesPerBlock;
     const dim3 wgrid((unsigned)(wblocks < kMaxGrid ? wblocks : kMaxGrid));
     const dim3 wblock(64 * kWavesPerBlock);
     switch (r_max) {
-        case 8: launch(shrink_mfma_kernel<8>, wgrid, wblock, 0, s, x, A, ranks, M, d_in, seg, partial, ksplit, kc); break;
-        case 16: launch(shrink_mfma_kernel<16>, wgrid, wblock, 0, s, x, A, ranks, M, d_in, seg, partial, ksplit, kc); break;
-        case 32: launch(shrink_mfma_kernel<32>, wgrid, wblock, 0, s, x, A, ranks, M, d_in, seg, partial, ksplit, kc); break;
-        case 64: launch(shrink_mfma_kernel<64>, wgrid, wblock, 0, s, x, A, ranks, M, d_in, seg, partial, ksplit, kc); break;
+        case 8: launch(shrink_mfma_kernel<8>, wgrid, wblock, 0, s, x, A, ranks, roff, pool_rows, M, d_in, seg, partial, ksplit, kc); break;
+        case 16: launch(shrink_mfma_kernel<16>, wgrid, wblock, 0, s, x, A, ranks, roff, pool_rows, M, d_in, seg, partial, ksplit, kc); break;
+        case 32: launch(shrink_mfma_kernel<32>, wgrid, wblock, 0, s, x, A, ranks, roff, pool_rows, M, d_in, seg, partial, ksplit, kc); break;
+        case 64: launch(shrink_mfma_kernel<64>, wgrid, wblock, 0, s, x, A, ranks, roff, pool_rows, M, d_in, seg, partial, ksplit, kc); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

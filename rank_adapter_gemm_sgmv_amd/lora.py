@@ -32,8 +32,8 @@ STATUS = {
 
 # every symbol include/lora.h declares
 EXPORTS = ("lora_max_tiles", "lora_workspace_bytes", "lora_build_segments", "lora_shrink",
-           "lora_expand", "lora_linear", "lora_linear_profiled", "lora_status_string",
-           "lora_last_hip_error")
+           "lora_expand", "lora_linear", "lora_linear_profiled", "lora_linear_compact",
+           "lora_linear_compact_profiled", "lora_status_string", "lora_last_hip_error")
 
 
 class LoraError(RuntimeError):
@@ -81,6 +81,13 @@ def _load():
     lib.lora_linear_profiled.argtypes = lib.lora_linear.argtypes + [
         ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_char_p), I, ctypes.POINTER(I)]
     lib.lora_linear_profiled.restype = ctypes.c_int
+    lib.lora_linear_compact.argtypes = [P, P, P, P, P, P, P, I, P, I, I, I, I, I,
+                                        ctypes.POINTER(lora_segments_t), P, ctypes.c_int,
+                                        ctypes.c_int, P, S, P]
+    lib.lora_linear_compact.restype = ctypes.c_int
+    lib.lora_linear_compact_profiled.argtypes = lib.lora_linear_compact.argtypes + [
+        ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_char_p), I, ctypes.POINTER(I)]
+    lib.lora_linear_compact_profiled.restype = ctypes.c_int
     lib.lora_status_string.argtypes = [ctypes.c_int]
     lib.lora_status_string.restype = ctypes.c_char_p
     lib.lora_last_hip_error.argtypes = []
@@ -185,6 +192,35 @@ def lora_linear_profiled(x, W, A, B, scale, ranks, ids, M: int, d_in: int, d_out
                                      _ptr(ids), M, d_in, d_out, r_max, n_adapters, seg_p, _ptr(y),
                                      y_dtype, mode, _ptr(ws), ws_bytes, _stream(stream), ms, names,
                                      max_kernels, ctypes.byref(n)), "lora_linear_profiled")
+    return [(names[i].decode(), float(ms[i])) for i in range(n.value)]
+
+
+def lora_linear_compact(x, W, A, B, scale, ranks, rank_offsets, pool_rows: int, ids, M: int,
+                        d_in: int, d_out: int, r_max: int, n_adapters: int, segs, y, y_dtype: int,
+                        mode: int, ws, ws_bytes: int, stream=None) -> None:
+    """lora_linear on a rank-compact pool (A_i, B_i stored at rank r_i from rank row
+    rank_offsets[i] of pool_rows rows)."""
+    seg_p = None if segs is None else ctypes.byref(_seg_struct(segs))
+    _check(_lib.lora_linear_compact(_ptr(x), _ptr(W), _ptr(A), _ptr(B), _ptr(scale), _ptr(ranks),
+                                    _ptr(rank_offsets), pool_rows, _ptr(ids), M, d_in, d_out,
+                                    r_max, n_adapters, seg_p, _ptr(y), y_dtype, mode, _ptr(ws),
+                                    ws_bytes, _stream(stream)), "lora_linear_compact")
+
+
+def lora_linear_compact_profiled(x, W, A, B, scale, ranks, rank_offsets, pool_rows: int, ids,
+                                 M: int, d_in: int, d_out: int, r_max: int, n_adapters: int,
+                                 segs, y, y_dtype: int, mode: int, ws, ws_bytes: int,
+                                 stream=None, max_kernels: int = 16):
+    """lora_linear_compact with per-kernel HIP event timing; returns [(kernel name, ms)]."""
+    seg_p = None if segs is None else ctypes.byref(_seg_struct(segs))
+    ms = (ctypes.c_float * max_kernels)()
+    names = (ctypes.c_char_p * max_kernels)()
+    n = ctypes.c_int32(0)
+    _check(_lib.lora_linear_compact_profiled(
+        _ptr(x), _ptr(W), _ptr(A), _ptr(B), _ptr(scale), _ptr(ranks), _ptr(rank_offsets),
+        pool_rows, _ptr(ids), M, d_in, d_out, r_max, n_adapters, seg_p, _ptr(y), y_dtype, mode,
+        _ptr(ws), ws_bytes, _stream(stream), ms, names, max_kernels, ctypes.byref(n)),
+        "lora_linear_compact_profiled")
     return [(names[i].decode(), float(ms[i])) for i in range(n.value)]
 
 

@@ -9,6 +9,7 @@ from .workloads import (  # noqa: F401
     Projection,
     Workload,
     bf16_bits_to_f32,
+    compact_pool,
     f32_to_bf16_bits,
     make_workload,
     pool_param_count,

@@ -114,3 +114,29 @@ def test_shrink_expand_reject():
     with pytest.raises(L.LoraError) as e:
         L.lora_expand(FAKE, FAKE, FAKE, None, 64, 4096, 16, 32, seg, FAKE, 3, stream=0)
     assert e.value.status == 6
+
+
+def _compact(**over):
+    ws = L.lora_workspace_bytes(64, 4096, 4096, 64, 32)
+    args = dict(x=FAKE, W=FAKE, A=FAKE, B=FAKE, scale=FAKE, ranks=FAKE, rank_offsets=FAKE,
+                pool_rows=256, ids=FAKE, M=64, d_in=4096, d_out=4096, r_max=64, n_adapters=32,
+                segs=None, y=FAKE, y_dtype=L.LORA_BF16, mode=L.LORA_MODE_DECODE, ws=FAKE,
+                ws_bytes=ws, stream=0)
+    args.update(over)
+    return L.lora_linear_compact(**args)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(ranks=None), 1), (dict(rank_offsets=None), 1), (dict(rank_offsets=FAKE + 2), 4),
+    (dict(pool_rows=0), 2), (dict(pool_rows=32 * 64 + 1), 2),
+    # the checks lora_linear makes come first
+    (dict(r_max=12), 3), (dict(ws_bytes=1024), 5), (dict(x=None), 1),
+])
+def test_linear_compact_rejects(over, code):
+    with pytest.raises(L.LoraError) as e:
+        _compact(**over)
+    assert e.value.status == code
+
+
+def test_linear_compact_empty_batch_is_noop():
+    _compact(M=0, x=None, y=None, ws=None)

@@ -4,8 +4,8 @@ import numpy as np
 import pytest
 import torch
 
-from synth import (CONFIGS, bf16_bits_to_f32, f32_to_bf16_bits, make_workload, random_case,
-                   zipf_probs)
+from synth import (CONFIGS, bf16_bits_to_f32, compact_pool, f32_to_bf16_bits, make_workload,
+                   random_case, zipf_probs)
 
 
 def test_bf16_rounding_matches_torch():
@@ -86,3 +86,25 @@ def test_random_case_padding():
     for i, r in enumerate(w.ranks):
         assert 1 <= r <= 16
         assert not np.any(p.A[i, :, r:]) and not np.any(p.B[i, r:, :])
+
+
+def test_compact_pool_is_the_padded_pool_at_true_rank():
+    """The rank-compact layout holds exactly the unpadded part of every adapter: its size is
+    sum r_i (d_in + d_out) elements (the per-adapter count of the pages' adapter-size
+    formula, at each adapter's own rank), and every block maps back to A[i, :, :r_i] and
+    B[i, :r_i, :]."""
+    w = make_workload(3)
+    p = w.projections[0]
+    A_c, B_c, off, rows = compact_pool(p.A, p.B, w.ranks)
+    n, d_in, r_max = p.A.shape
+    d_out = p.B.shape[2]
+    assert rows == int(w.ranks.sum())
+    assert A_c.size + B_c.size == sum(int(r) * (d_in + d_out) for r in w.ranks)
+    assert off[0] == 0 and np.all(np.diff(off) == w.ranks[:-1])
+    for i in range(n):
+        o, r = int(off[i]), int(w.ranks[i])
+        assert np.array_equal(A_c[o * d_in:(o + r) * d_in].reshape(d_in, r), p.A[i, :, :r])
+        assert np.array_equal(B_c[o:o + r], p.B[i, :r, :])
+        assert not np.any(p.A[i, :, r:]) and not np.any(p.B[i, r:, :])  # nothing dropped
+    # every rank of this workload is a multiple of 8, as the compact entry point requires
+    assert np.all(w.ranks % 8 == 0)
