@@ -110,23 +110,31 @@ def _bf16(bits, torch):
 class DeviceLayers:
     """Device copies ("layers") of one projection's weights, cycled step by step."""
 
-    def __init__(self, w, pi, n_layers, rotate_x, torch):
+    def __init__(self, w, pi, n_layers, rotate_x, torch, compact=False):
         p = w.projections[pi]
         self.d_in, self.d_out = p.d_in, p.d_out
         self.layers = []
+        A_h, B_h = p.A, p.B
+        self.off, self.pool_rows = None, 0
+        if compact:  # the same adapters stored at their own rank (lora_linear_compact)
+            from synth import compact_pool
+
+            A_h, B_h, off, self.pool_rows = compact_pool(p.A, p.B, w.ranks)
+            self.off = torch.from_numpy(off).cuda()
         x0 = _bf16(p.x, torch)
         for i in range(n_layers):
             W = _bf16(p.W, torch)
-            A = _bf16(p.A, torch)
-            B = _bf16(p.B, torch)
+            A = _bf16(A_h, torch)
+            B = _bf16(B_h, torch)
             x = _bf16(p.x, torch) if (rotate_x and i > 0) else x0
             self.layers.append((x, W, A, B))
 
 
-def layers_needed(w, rotate_x: bool) -> int:
+def layers_needed(w, rotate_x: bool, compact: bool = False) -> int:
     per = 0
     for p in w.projections:
-        per += p.W.nbytes + p.A.nbytes + p.B.nbytes + (p.x.nbytes if rotate_x else 0)
+        pool = (int(w.ranks.sum()) * (p.d_in + p.d_out) * 2) if compact else p.A.nbytes + p.B.nbytes
+        per += p.W.nbytes + pool + (p.x.nbytes if rotate_x else 0)
     return max(1, -(-ROTATE_BYTES // per))
 
 
@@ -134,13 +142,15 @@ class Runner:
     """One workload on the device: L layers, shared ids / ranks / scale, one output per
     projection, workspace; `step(i)` enqueues one step (all projections) for layer i % L."""
 
-    def __init__(self, w, mode, torch, L, rotate_x=False, prebuilt_segments=False):
+    def __init__(self, w, mode, torch, L, rotate_x=False, prebuilt_segments=False, compact=False):
         self.torch, self.w, self.mode, self.L = torch, w, mode, L
+        self.compact = compact
         self.M, self.n, self.r_max = w.M, w.n_adapters, w.r_max
         self.ids = torch.from_numpy(w.ids.astype(np.int32)).cuda()
         self.ranks = torch.from_numpy(w.ranks.astype(np.int32)).cuda()
         self.scale = torch.from_numpy((w.alpha / w.ranks.astype(np.float32)).astype(np.float32)).cuda()
-        self.projs = [DeviceLayers(w, pi, L, rotate_x, torch) for pi in range(len(w.projections))]
+        self.projs = [DeviceLayers(w, pi, L, rotate_x, torch, compact)
+                      for pi in range(len(w.projections))]
         self.ys = [torch.empty((w.M, pr.d_out), dtype=torch.bfloat16, device="cuda") for pr in self.projs]
         nb = max(L_.lora_workspace_bytes(w.M, pr.d_in, pr.d_out, w.r_max, w.n_adapters) for pr in self.projs)
         self.ws = torch.empty(max(nb, 256), dtype=torch.uint8, device="cuda")
@@ -153,6 +163,12 @@ class Runner:
             L_.lora_build_segments(self.ids, self.M, self.n, self.segs)
         for pr, y in zip(self.projs, self.ys):
             x, W, A, B = pr.layers[li]
+            if self.compact:
+                L_.lora_linear_compact(x, W, A, B, self.scale, self.ranks, pr.off, pr.pool_rows,
+                                       self.ids, self.M, pr.d_in, pr.d_out, self.r_max, self.n,
+                                       self.segs, y, L_.LORA_BF16, self.mode, self.ws,
+                                       self.ws_bytes)
+                continue
             L_.lora_linear(x, W, A, B, self.scale, self.ranks, self.ids, self.M, pr.d_in, pr.d_out,
                            self.r_max, self.n, self.segs, y, L_.LORA_BF16, self.mode, self.ws,
                            self.ws_bytes)
@@ -167,9 +183,15 @@ class Runner:
             L_.lora_build_segments(self.ids, self.M, self.n, self.segs)
         for pr, y in zip(self.projs, self.ys):
             x, W, A, B = pr.layers[li]
-            ks = L_.lora_linear_profiled(x, W, A, B, self.scale, self.ranks, self.ids, self.M,
-                                         pr.d_in, pr.d_out, self.r_max, self.n, self.segs, y,
-                                         L_.LORA_BF16, self.mode, self.ws, self.ws_bytes)
+            if self.compact:
+                ks = L_.lora_linear_compact_profiled(
+                    x, W, A, B, self.scale, self.ranks, pr.off, pr.pool_rows, self.ids, self.M,
+                    pr.d_in, pr.d_out, self.r_max, self.n, self.segs, y, L_.LORA_BF16, self.mode,
+                    self.ws, self.ws_bytes)
+            else:
+                ks = L_.lora_linear_profiled(x, W, A, B, self.scale, self.ranks, self.ids, self.M,
+                                             pr.d_in, pr.d_out, self.r_max, self.n, self.segs, y,
+                                             L_.LORA_BF16, self.mode, self.ws, self.ws_bytes)
             out.append(ks)
         return out
 
@@ -377,21 +399,24 @@ def base_only_ms(w, runner, steps, torch):
     return ms
 
 
-def run_workload(config, mode_name, steps, warmup, torch, profile_reps=20, need_runner=False):
+def run_workload(config, mode_name, steps, warmup, torch, profile_reps=20, need_runner=False,
+                 compact=False):
     from synth import make_workload
 
     w = make_workload(config).as_bf16()
     prefill = mode_name == "prefill"
     mode = L_.LORA_MODE_PREFILL if prefill else L_.LORA_MODE_DECODE
     rotate_x = prefill
-    L = layers_needed(w, rotate_x)
+    L = layers_needed(w, rotate_x, compact)
     # the graph holds whole rotations so its last step can be checked against an eager one
     steps = max(L, -(-steps // L) * L) if steps % L else steps
-    runner = Runner(w, mode, torch, L, rotate_x=rotate_x, prebuilt_segments=len(w.projections) > 1)
-    log(f"bench: {w.name} mode={mode_name} layers={L} steps={steps}")
+    runner = Runner(w, mode, torch, L, rotate_x=rotate_x, prebuilt_segments=len(w.projections) > 1,
+                    compact=compact)
+    log(f"bench: {w.name} mode={mode_name} layers={L} steps={steps} compact={compact}")
     ms_total, wall, eager_ms, kernels = measure(runner, steps, warmup, torch, profile_reps)
     s = summarize(w, runner, ms_total, steps, wall, eager_ms, kernels, prefill)
-    s.update({"workload": w.name, "mode": mode_name, "layers_rotated": L, "steps": steps})
+    s.update({"workload": w.name, "mode": mode_name, "layers_rotated": L, "steps": steps,
+              "pool": "rank-compact (lora_linear_compact)" if compact else "padded to r_max"})
     base_ms = base_only_ms(w, runner, steps, torch)
     s["base_only_ms_per_step"] = base_ms
     s["lora_overhead_vs_base_only"] = s["ms_per_step"] / base_ms - 1.0
@@ -466,11 +491,13 @@ def main():
 
     workloads = {}
     if not args.headline_only:
-        for cfg, mode_name, st in ((3, "decode", 128), (4, "prefill", 40), (5, "decode", 64),
-                                   (4, "decode", 20), (2, "prefill", 64)):
+        for cfg, mode_name, st, comp in ((3, "decode", 128, False), (3, "decode", 128, True),
+                                         (4, "prefill", 40, False), (5, "decode", 64, False),
+                                         (4, "decode", 20, False), (2, "prefill", 64, False)):
             try:
-                _, s, _, _, _ = run_workload(cfg, mode_name, st, 4, torch, profile_reps=8)
-                workloads[f"{s['workload']}:{mode_name}"] = s
+                _, s, _, _, _ = run_workload(cfg, mode_name, st, 4, torch, profile_reps=8,
+                                             compact=comp)
+                workloads[f"{s['workload']}:{mode_name}{'-compact' if comp else ''}"] = s
             except Exception as e:  # report, do not hide the headline
                 workloads[f"config{cfg}:{mode_name}"] = {"error": repr(e)}
             torch.cuda.empty_cache()

@@ -390,10 +390,14 @@ __global__ __launch_bounds__(256) void reduce_lora_kernel(const float *__restric
     // in a padded pool at r_max <= 16 every row is loaded (the padding rows exist), so the
     // loads need not wait for the rank; a compact pool's rows past the rank are the next
     // adapter's
-    const bool all_rows = RM <= 16 && lo.roff == nullptr;
+    if (RM <= 16 && lo.roff == nullptr) {
 #pragma unroll
-    for (int j = 0; j < BCH; ++j)
-        bv[j] = (all_rows || j < r) ? *reinterpret_cast<const uint2 *>(bp + (size_t)j * N) : make_uint2(0, 0);
+        for (int j = 0; j < BCH; ++j) bv[j] = *reinterpret_cast<const uint2 *>(bp + (size_t)j * N);
+    } else {
+#pragma unroll
+        for (int j = 0; j < BCH; ++j)
+            bv[j] = j < r ? *reinterpret_cast<const uint2 *>(bp + (size_t)j * N) : make_uint2(0, 0);
+    }
     // where the parts of t[m, :] are
     const float *tsrc;
     size_t t_stride;

@@ -54,7 +54,9 @@ struct MfmaShrink {
 // hands each lane 4 consecutive k of one column.  Column groups at or beyond the adapter's
 // rank are written to LDS as zeros.  All global loads are issued unconditionally (clamped
 // addresses; out-of-range values are masked at use), so they are all in flight together.
-template <int RM>
+// COMPACT: the pool is rank-compact (roff names each adapter's first rank row); otherwise
+// padded to r_max (roff is not read).
+template <int RM, bool COMPACT>
 __global__ __launch_bounds__(64 * kWavesPerBlock) void shrink_mfma_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ A, const int32_t *__restrict__ ranks,
     const int32_t *__restrict__ roff, int pool_rows, int M, int d_in, Seg seg,
@@ -76,10 +78,10 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void shrink_mfma_kernel(
         const int p0 = seg.tiles[2 * tile], a = seg.tiles[2 * tile + 1];
         const int rows = min(p0 + kTileRows, seg.offsets[a + 1]) - p0;
         int r = ranks ? min(max(ranks[a], 0), RM) : RM;
-        const int row0 = adapter_row0(roff, pool_rows, a, RM, r);
+        const int row0 = adapter_row0(COMPACT ? roff : nullptr, pool_rows, a, RM, r);
         // row stride of A_a: r_max in a padded pool, the rank in a compact one, where the
         // groups at or beyond the rank are not loaded (they belong to the next adapter)
-        const int rs = roff ? r : RM;
+        const int rs = COMPACT ? r : RM;
         const int k_lo = c * kc, k_hi = min(k_lo + kc, d_in);
         // this lane's x row (rows beyond the tile repeat its last row; their sums are dropped)
         const int mrow = seg.perm[p0 + min(li, rows - 1)];
@@ -93,11 +95,21 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void shrink_mfma_kernel(
         for (int kb = k_lo; kb < k_hi; kb += C::KS) {
             // A_a[kb .. kb+KS, 0:RM]: unit f = lane + 64 i is (row f / GR, group f % GR)
             uint4 av[C::AL];
+            if constexpr (!COMPACT) {
+                // padded pool: every group is loaded (the padding is zeros), so the loads do
+                // not wait for the rank
 #pragma unroll
-            for (int i = 0; i < C::AL; ++i) {
-                const int f = lane + 64 * i, kr = kb + f / C::GR, gr = f % C::GR;
-                av[i] = (roff == nullptr || gr * 8 < r) ? ld16(Aa + (size_t)min(kr, d_in - 1) * rs + gr * 8)
-                                                        : make_uint4(0, 0, 0, 0);
+                for (int i = 0; i < C::AL; ++i) {
+                    const int f = lane + 64 * i, kr = kb + f / C::GR, gr = f % C::GR;
+                    av[i] = ld16(Aa + (size_t)min(kr, d_in - 1) * RM + gr * 8);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < C::AL; ++i) {
+                    const int f = lane + 64 * i, kr = kb + f / C::GR, gr = f % C::GR;
+                    av[i] = gr * 8 < r ? ld16(Aa + (size_t)min(kr, d_in - 1) * rs + gr * 8)
+                                       : make_uint4(0, 0, 0, 0);
+                }
             }
             uint4 xv[C::STEPS];
 #pragma unroll
@@ -187,13 +199,21 @@ hipError_t launch_shrink(const uint16_t *x, const uint16_t *A, const int32_t *ra
     const long wblocks = (items + kWavesPerBlock - 1) / kWavesPerBlock;
     const dim3 wgrid((unsigned)(wblocks < kMaxGrid ? wblocks : kMaxGrid));
     const dim3 wblock(64 * kWavesPerBlock);
+#define LORA_SHRINK_LAUNCH(RMV)                                                                  \
+    if (roff)                                                                                    \
+        launch(shrink_mfma_kernel<RMV, true>, wgrid, wblock, 0, s, x, A, ranks, roff, pool_rows, \
+               M, d_in, seg, partial, ksplit, kc);                                               \
+    else                                                                                         \
+        launch(shrink_mfma_kernel<RMV, false>, wgrid, wblock, 0, s, x, A, ranks, roff, pool_rows,\
+               M, d_in, seg, partial, ksplit, kc);
     switch (r_max) {
-        case 8: launch(shrink_mfma_kernel<8>, wgrid, wblock, 0, s, x, A, ranks, roff, pool_rows, M, d_in, seg, partial, ksplit, kc); break;
-        case 16: launch(shrink_mfma_kernel<16>, wgrid, wblock, 0, s, x, A, ranks, roff, pool_rows, M, d_in, seg, partial, ksplit, kc); break;
-        case 32: launch(shrink_mfma_kernel<32>, wgrid, wblock, 0, s, x, A, ranks, roff, pool_rows, M, d_in, seg, partial, ksplit, kc); break;
-        case 64: launch(shrink_mfma_kernel<64>, wgrid, wblock, 0, s, x, A, ranks, roff, pool_rows, M, d_in, seg, partial, ksplit, kc); break;
+        case 8: LORA_SHRINK_LAUNCH(8) break;
+        case 16: LORA_SHRINK_LAUNCH(16) break;
+        case 32: LORA_SHRINK_LAUNCH(32) break;
+        case 64: LORA_SHRINK_LAUNCH(64) break;
         default: return hipErrorInvalidValue;
     }
+#undef LORA_SHRINK_LAUNCH
     return hipGetLastError();
 }
 
