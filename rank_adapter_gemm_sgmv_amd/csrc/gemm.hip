@@ -1,5 +1,5 @@
-// gemm.hip -- the shared base term y = x W on bf16 MFMA (gfx950), with the LoRA delta
-// fused into the epilogue for prefill.
+// gemm.hip -- the shared base term y = x W on bf16 MFMA (gfx950) for the decode shapes no
+// other GEMM of the library takes (split-K tilings), and the dispatch between the GEMMs.
 //
 // Source: "Multi-LoRA Serving: Why 100 Adapters Fit on One GPU" (dev.to), "Why can't you
 // just merge LoRA weights into the base model?": the x W term is one big GEMM across the
@@ -16,18 +16,12 @@
 // Pipeline: LDS double buffer, one barrier per 64-deep k step; the global loads of step
 // k+1 are in flight while step k's MFMAs run.
 //
-// Tilings: prefill 256 x 256 (4 waves of 128 x 128, 16 accumulators of 32 x 32 each);
-// decode 64 x 64, 128 x 64 or 128 x 128 with split-K partial sums reduced by a second
+// Tilings: 64 x 64, 128 x 64 or 128 x 128 with split-K partial sums reduced by a second
 // kernel in split order.  Tiles are mapped XCD-aware: workgroup b runs on XCD b % 8, so
 // each XCD is handed compact groups of 4 tile rows and its L2 serves the x and W panels those
 // tiles share (without it, the row tiles of a decode W panel land on four XCDs and W is
 // fetched from HBM about four times).
-//
-// Prefill epilogue (segment-ordered rows): the tile's rows are positions of perm, so each
-// tile holds a few long runs of one adapter.  For every run, T = scale_a * t[rows, :] (bf16)
-// and B_a[:, tile columns] (transposed in registers as above) are staged in LDS and added to
-// the accumulators by r_max / 16 more MFMA steps -- the K-extension [x | T] [W ; B_a] -- before
-// the only store of y.  Rows with id -1 get no delta.
+
 #include "common.h"
 
 namespace lora {
@@ -150,12 +144,12 @@ __device__ __forceinline__ void store_tile(const uint4 (&xr)[C::XCH], const uint
     }
 }
 
-template <class C, bool PREFILL, bool YF32>
+template <class C, bool YF32>
 __global__ __launch_bounds__(C::NT) void gemm_kernel(const uint16_t *__restrict__ x,
                                                      const uint16_t *__restrict__ W, int M, int K,
                                                      int N, void *__restrict__ y,
                                                      float *__restrict__ partial, int k_per_split,
-                                                     int n_tm, int n_tn, Seg seg, LoraEpilogue ep) {
+                                                     int n_tm, int n_tn) {
     constexpr int BM = C::BM, BN = C::BN, NT = C::NT;
     __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * kLDK];
     __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * kLDK];
@@ -176,7 +170,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(const uint16_t *__restrict_
     for (int i = 0; i < C::XCH; ++i) {
         const int rr = row0 + (tid + i * NT) / (kBK / 8);
         int m = -1;
-        if (rr < M) m = PREFILL ? seg.perm[rr] : rr;
+        if (rr < M) m = rr;
         xrow[i] = m;
     }
 
@@ -205,55 +199,6 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(const uint16_t *__restrict_
         __syncthreads();
     }
 
-    if constexpr (PREFILL) {
-        // LoRA delta for the runs of one adapter inside this tile's rows (positions of perm).
-        const int n_lora = seg.meta[1];
-        const int RM = ep.r_max;
-        const int KE = RM < 16 ? 16 : RM;  // k extent of the extension, multiple of 16
-        int p = row0;
-        const int p_end = min(row0 + BM, n_lora);
-        while (p < p_end) {
-            const int a = ep.ids[seg.perm[p]];
-            if (a < 0 || a >= ep.n_adapters) break;  // segments not built for these ids
-            const int q_end = min(seg.offsets[a + 1], p_end);
-            if (q_end <= p) break;
-            const float s = ep.scale[a];
-            // T rows: scale_a * t for rows of this run, zero elsewhere
-            for (int c = tid; c < BM * (KE / 8); c += NT) {
-                const int rr = c / (KE / 8), jc = (c % (KE / 8)) * 8;
-                const int pos = row0 + rr;
-                uint4 v = make_uint4(0, 0, 0, 0);
-                if (pos >= p && pos < q_end && jc < RM) {
-                    const float *tp = ep.t + (size_t)seg.perm[pos] * RM + jc;
-                    const float4 t0 = *reinterpret_cast<const float4 *>(tp);
-                    const float4 t1 = *reinterpret_cast<const float4 *>(tp + 4);
-                    v = make_uint4(pack_bf16x2(s * t0.x, s * t0.y), pack_bf16x2(s * t0.z, s * t0.w),
-                                   pack_bf16x2(s * t1.x, s * t1.y), pack_bf16x2(s * t1.z, s * t1.w));
-                }
-                st16(&As[0][rr * kLDK + jc], v);
-            }
-            // B_a[j][n0 + n] transposed to [n][j]
-            for (int b = tid; b < (KE / 8) * (BN / 8); b += NT) {
-                const int jb = b % (KE / 8), nb = b / (KE / 8);
-                const int n = n0 + nb * 8;
-                uint4 blk[8], tb[8];
-#pragma unroll
-                for (int jj = 0; jj < 8; ++jj) {
-                    const int j = jb * 8 + jj;
-                    blk[jj] = (j < RM && n < N) ? ld16(ep.B + ((size_t)a * RM + j) * N + n)
-                                                : make_uint4(0, 0, 0, 0);
-                }
-                transpose8x8(blk, tb);
-#pragma unroll
-                for (int nn = 0; nn < 8; ++nn) st16(&Bs[0][(nb * 8 + nn) * kLDK + jb * 8], tb[nn]);
-            }
-            __syncthreads();
-            for (int kk = 0; kk < KE / 16; ++kk) mfma_step<C>(acc, As[0], Bs[0], wm0, wn0, lane, kk);
-            __syncthreads();
-            p = q_end;
-        }
-    }
-
     // store: accumulator register v of a 32x32 block holds row (v/4)*8 + (lane/32)*4 + v%4,
     // column lane%32
 #pragma unroll
@@ -265,7 +210,7 @@ __global__ __launch_bounds__(C::NT) void gemm_kernel(const uint16_t *__restrict_
             for (int v = 0; v < 16; ++v) {
                 const int rr = row0 + wm0 + i * 32 + (v / 4) * 8 + (lane >> 5) * 4 + (v % 4);
                 if (rr < M && col < N) {
-                    const int m = PREFILL ? seg.perm[rr] : rr;
+                    const int m = rr;
                     const float val = acc[i][j][v];
                     if (partial != nullptr) {
                         partial[((size_t)split * M + m) * N + col] = val;
@@ -301,7 +246,6 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restr
     }
 }
 
-using CfgPrefill = Cfg<256, 256, 2, 2>;
 using CfgD64 = Cfg<64, 64, 2, 2>;
 using CfgD128x64 = Cfg<128, 64, 2, 2>;
 using CfgD128 = Cfg<128, 128, 2, 2>;
@@ -332,20 +276,17 @@ DecodePlan decode_plan(int M, int K, int N) {
     return p;
 }
 
-template <class C, bool PREFILL>
+template <class C>
 hipError_t launch_cfg(const uint16_t *x, const uint16_t *W, int M, int K, int N, void *y, bool y_f32,
-                      float *partial, int ksplit, int k_per_split, Seg seg, const LoraEpilogue *lora,
-                      hipStream_t s) {
+                      float *partial, int ksplit, int k_per_split, hipStream_t s) {
     const int n_tm = (M + C::BM - 1) / C::BM, n_tn = (N + C::BN - 1) / C::BN;
-    LoraEpilogue ep{};
-    if (lora) ep = *lora;
     dim3 grid(n_tm * n_tn, ksplit);
     if (y_f32)
-        launch((gemm_kernel<C, PREFILL, true>), grid, dim3(C::NT), 0, s, x, W, M, K, N, y,
-                           partial, k_per_split, n_tm, n_tn, seg, ep);
+        launch((gemm_kernel<C, true>), grid, dim3(C::NT), 0, s, x, W, M, K, N, y, partial,
+               k_per_split, n_tm, n_tn);
     else
-        launch((gemm_kernel<C, PREFILL, false>), grid, dim3(C::NT), 0, s, x, W, M, K, N, y,
-                           partial, k_per_split, n_tm, n_tn, seg, ep);
+        launch((gemm_kernel<C, false>), grid, dim3(C::NT), 0, s, x, W, M, K, N, y, partial,
+               k_per_split, n_tm, n_tn);
     return hipGetLastError();
 }
 
@@ -383,10 +324,10 @@ hipError_t launch_gemm(const uint16_t *x, const uint16_t *W, int M, int K, int N
     }
     *ksplit_out = p.ksplit;
     if (p.bm == 64)
-        return launch_cfg<CfgD64, false>(x, W, M, K, N, y, y_f32, partial, p.ksplit, p.k_per_split, seg, nullptr, s);
+        return launch_cfg<CfgD64>(x, W, M, K, N, y, y_f32, partial, p.ksplit, p.k_per_split, s);
     if (p.bn == 64)
-        return launch_cfg<CfgD128x64, false>(x, W, M, K, N, y, y_f32, partial, p.ksplit, p.k_per_split, seg, nullptr, s);
-    return launch_cfg<CfgD128, false>(x, W, M, K, N, y, y_f32, partial, p.ksplit, p.k_per_split, seg, nullptr, s);
+        return launch_cfg<CfgD128x64>(x, W, M, K, N, y, y_f32, partial, p.ksplit, p.k_per_split, s);
+    return launch_cfg<CfgD128>(x, W, M, K, N, y, y_f32, partial, p.ksplit, p.k_per_split, s);
 }
 
 hipError_t launch_splitk_reduce(const float *partial, int M, int N, int ksplit, void *y, bool y_f32,

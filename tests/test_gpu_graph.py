@@ -10,28 +10,54 @@ import pytest
 
 from synth import random_case
 
-from .gpu_util import log, to_device
+from .gpu_util import bf16_dev, log, to_device
 
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("mode", [1, 2], ids=["decode", "prefill"])
-def test_graph_replays_match_eager(mode):
+GRAPH_CASES = [
+    # seed, M, d_in, d_out, n, r_max, mode (1 decode, 2 prefill), rank-compact pool
+    (91, 96, 1024, 768, 12, 16, 1, False),   # small-batch fused decode path
+    (92, 96, 1024, 768, 12, 16, 2, False),   # prefill
+    (93, 200, 1024, 520, 40, 32, 1, False),  # medium decode path
+    (94, 300, 4096, 2056, 50, 64, 1, False),  # stream-K decode path
+    (95, 300, 4096, 2056, 50, 64, 1, True),   # stream-K, compact pool
+    (96, 200, 1024, 520, 40, 32, 2, True),    # prefill, compact pool
+]
+
+
+@pytest.mark.parametrize("case", GRAPH_CASES,
+                         ids=[f"M{c[1]}-{'dec' if c[6] == 1 else 'pre'}{'-compact' if c[7] else ''}"
+                              for c in GRAPH_CASES])
+def test_graph_replays_match_eager(case):
     import torch
 
     from rank_adapter_gemm_sgmv_amd import lora as L
+    from synth import compact_pool
 
-    log(f"graph: mode {mode}")
-    w = random_case(90 + mode, 96, 1024, 768, 12, 16, base_frac=0.2)
+    seed, M, d_in, d_out, n, r_max, mode, compact = case
+    log(f"graph: {case}")
+    ranks = None
+    if compact:
+        ranks = (8 * np.random.default_rng(seed).integers(1, r_max // 8 + 1, size=n)).astype(np.int32)
+    w = random_case(seed, M, d_in, d_out, n, r_max, ranks=ranks, base_frac=0.2)
     dw = to_device(w)
     p = dw.projs[0]
-    M, n, r = w.M, w.n_adapters, w.r_max
+    r = w.r_max
     y = torch.empty((M, p.d_out), dtype=torch.bfloat16, device="cuda")
     ws, nb = L.workspace(M, p.d_in, p.d_out, r, n)
+    if compact:
+        wb = w.as_bf16().projections[0]
+        A_c, B_c, off, rows = compact_pool(wb.A, wb.B, w.ranks)
+        A_c, B_c, off = bf16_dev(A_c), bf16_dev(B_c), torch.from_numpy(off).cuda()
 
     def call():
-        L.lora_linear(p.x, p.W, p.A, p.B, dw.scale, dw.ranks, dw.ids, M, p.d_in, p.d_out, r, n,
-                      None, y, L.LORA_BF16, mode, ws, nb)
+        if compact:
+            L.lora_linear_compact(p.x, p.W, A_c, B_c, dw.scale, dw.ranks, off, rows, dw.ids, M,
+                                  p.d_in, p.d_out, r, n, None, y, L.LORA_BF16, mode, ws, nb)
+        else:
+            L.lora_linear(p.x, p.W, p.A, p.B, dw.scale, dw.ranks, dw.ids, M, p.d_in, p.d_out, r, n,
+                          None, y, L.LORA_BF16, mode, ws, nb)
 
     call()
     torch.cuda.synchronize()
