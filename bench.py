@@ -426,7 +426,7 @@ def run_workload(config, mode_name, steps, warmup, torch, profile_reps=20, need_
 CALIB_BYTES = 256 << 20
 
 
-def pmc_pass(config, mode_name, steps, torch):
+def pmc_pass(config, mode_name, steps, torch, compact=False):
     """Eager steps of one workload, then the counter calibration kernel: torch.neg over
     CALIB_BYTES of bf16 (reads CALIB_BYTES, writes CALIB_BYTES), three times.  Meant to run
     under ``rocprofv3 --pmc``; no timing."""
@@ -435,8 +435,9 @@ def pmc_pass(config, mode_name, steps, torch):
     w = make_workload(config).as_bf16()
     prefill = mode_name == "prefill"
     mode = L_.LORA_MODE_PREFILL if prefill else L_.LORA_MODE_DECODE
-    L = layers_needed(w, prefill)
-    runner = Runner(w, mode, torch, L, rotate_x=prefill, prebuilt_segments=len(w.projections) > 1)
+    L = layers_needed(w, prefill, compact)
+    runner = Runner(w, mode, torch, L, rotate_x=prefill, prebuilt_segments=len(w.projections) > 1,
+                    compact=compact)
     for i in range(steps):
         runner.step(i)
     torch.cuda.synchronize()
@@ -445,7 +446,8 @@ def pmc_pass(config, mode_name, steps, torch):
     for _ in range(3):
         torch.neg(src, out=dst)
     torch.cuda.synchronize()
-    print(json.dumps({"pmc_pass": w.name, "mode": mode_name, "steps": steps, "layers_rotated": L,
+    print(json.dumps({"pmc_pass": w.name, "mode": mode_name, "compact": compact, "steps": steps,
+                      "layers_rotated": L,
                       "calibration": {"kernel": "torch.neg bf16", "bytes_read": CALIB_BYTES,
                                       "bytes_written": CALIB_BYTES, "launches": 3}}), flush=True)
 
@@ -460,6 +462,9 @@ def main():
     ap.add_argument("--workload", type=int, default=2, choices=(2, 3, 4, 5),
                     help="workload of the headline line (2 = decode q_proj, the default)")
     ap.add_argument("--mode", default="decode", choices=("decode", "prefill"))
+    ap.add_argument("--compact", action="store_true",
+                    help="serve the headline (or --pmc-pass) workload from its rank-compact pool "
+                         "(lora_linear_compact)")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="only eager steps of the chosen workload plus the counter calibration "
                          "kernel, for rocprofv3 --pmc runs (FETCH_SIZE / WRITE_SIZE)")
@@ -477,17 +482,17 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     if args.pmc_pass:
-        pmc_pass(args.workload, args.mode, args.steps, torch)
+        pmc_pass(args.workload, args.mode, args.steps, torch, args.compact)
         return
 
     # headline: decode, q_proj geometry (unless another workload is asked for)
     w, head, kernels, steps, ms_total = run_workload(args.workload, args.mode, args.steps,
-                                                     args.warmup, torch)
+                                                     args.warmup, torch, compact=args.compact)
     p0 = w.projections[0]
     work = algorithmic_work(w, p0.d_in, p0.d_out, args.mode == "prefill")
     kmain = {name: ms for (pi, name), ms in kernels.items() if pi == 0}
     dom = max(kmain, key=lambda k: kmain[k])
-    roof = roofline_for(dom, kmain[dom], work, w.name)
+    roof = roofline_for(dom, kmain[dom], work, w.name + ("_compact" if args.compact else ""))
 
     workloads = {}
     if not args.headline_only:
@@ -519,7 +524,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "M": w.M, "d_in": p0.d_in, "d_out": p0.d_out,
                    "n_adapters": w.n_adapters, "r_max": w.r_max, "mode": args.mode,
-                   "layers_rotated": head["layers_rotated"], "timed_as": "one HIP graph of all steps"},
+                   "layers_rotated": head["layers_rotated"], "timed_as": "one HIP graph of all steps",
+                   "pool": head["pool"]},
         "roofline": roof,
         "cpu_baseline": cpu,
         "headline_detail": head,
