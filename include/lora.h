@@ -108,7 +108,8 @@ typedef struct {
 /* Upper bound on the number of tiles: min(M, n_adapters) + M / LORA_TILE_ROWS. */
 int32_t lora_max_tiles(int32_t M, int32_t n_adapters);
 
-/* Workspace bytes needed by lora_linear and lora_shrink for these sizes (0 when M = 0).
+/* Workspace bytes needed by lora_linear, lora_linear_compact and lora_shrink for these sizes
+ * (0 when M = 0).
  * Returns 0 for arguments that the calls would reject. */
 size_t lora_workspace_bytes(int32_t M, int32_t d_in, int32_t d_out, int32_t r_max,
                             int32_t n_adapters);
