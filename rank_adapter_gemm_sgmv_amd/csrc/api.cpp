@@ -221,6 +221,9 @@ lora_status_t check_compact(const int32_t *ranks, const int32_t *rank_offsets, i
 //            and the expand
 //   decode otherwise: build_segments, shrink, shrink_finalize, gemm [, splitk_reduce], expand
 //   prefill: build_segments, shrink, shrink_finalize, gemm with the LoRA epilogue
+// A rank-compact pool (roff != nullptr, lora_linear_compact) takes the same sequences, except
+// that decode batches of at most 128 rows take the second one (the first lays adapters side
+// by side at row stride r_max).
 hipError_t run_linear(const void *x, const void *W, const void *A, const void *B,
                       const float *scale, const int32_t *ranks, const int32_t *roff,
                       int32_t pool_rows, const int32_t *ids, int32_t M, int32_t d_in,
