@@ -214,8 +214,8 @@ lora_status_t check_compact(const int32_t *ranks, const int32_t *rank_offsets, i
 //            A laid side by side (the shrink as extra column tiles), then the ordered
 //            reduction that adds scale_a t B_a (no segment-building launch: adapters are
 //            numbered by id or grouped in LDS; segs is not needed)
-//   decode, 128 < M <= 256 and d_in % 32 == 0: build_segments, shrink (chunk sums), the
-//            split-K GEMM, the ordered reduction with the expand
+//   decode, 128 < M <= 256 and d_in % 32 == 0: the split-K GEMM with build_segments in one
+//            extra workgroup, shrink (chunk sums), the ordered reduction with the expand
 //   decode, 256 < M <= 1024, d_in % 128 == 0 and few 256 x 256 tiles: build_segments,
 //            shrink (chunk sums), the stream-K GEMM, one pass adding its partial tiles, t
 //            and the expand
@@ -254,7 +254,7 @@ hipError_t run_linear(const void *x, const void *W, const void *A, const void *B
         const DecodeLora lo{nullptr, 0, reinterpret_cast<int32_t *>(t), Bb, scale, ids, ranks, r_max,
                             n_adapters, nullptr, 0};
         if ((e = launch_decode_gemm(xb, Wb, static_cast<const uint16_t *>(A), M, d_in, d_out, lo,
-                                    true, gpart, s)) != hipSuccess)
+                                    true, gpart, nullptr, s)) != hipSuccess)
             return e;
         mark(mk, "decode_gemm_lora");
         if ((e = launch_decode_reduce(gpart, M, d_in, d_out, y, yf, lo, true, s)) != hipSuccess) return e;
@@ -262,22 +262,21 @@ hipError_t run_linear(const void *x, const void *W, const void *A, const void *B
         return hipSuccess;
     }
     if (!prefill && decode_gemm_supported(M, d_in, d_out)) {
-        // medium decode batch: segment build and the segment-path shrink, whose per-chunk
-        // partial sums have the layout the decode reduction reads; the split-K GEMM; the
-        // reduction with the expand
-        if (!segs) {
-            if ((e = launch_build_segments(ids, M, n_adapters, sg, s)) != hipSuccess) return e;
-            mark(mk, "build_segments");
-        }
+        // medium decode batch: the split-K GEMM, with the segment build in one extra
+        // workgroup of the same launch (unless the caller passed segments); then the
+        // segment-path shrink, whose per-chunk partial sums have the layout the decode
+        // reduction reads; the reduction with the expand
         const DecodeLora lo{spart, ksplit, nullptr, Bb, scale, ids, ranks, r_max, n_adapters, roff,
                             pool_rows};
+        const SegBuild bld{ids, n_adapters, sg};
+        if ((e = launch_decode_gemm(xb, Wb, nullptr, M, d_in, d_out, lo, false, gpart,
+                                    segs ? nullptr : &bld, s)) != hipSuccess)
+            return e;
+        mark(mk, "decode_gemm");
         if ((e = launch_shrink(xb, static_cast<const uint16_t *>(A), ranks, roff, pool_rows, M, d_in, r_max, n_adapters,
                                sg, spart, kc, ksplit, s)) != hipSuccess)
             return e;
         mark(mk, "shrink");
-        if ((e = launch_decode_gemm(xb, Wb, nullptr, M, d_in, d_out, lo, false, gpart, s)) != hipSuccess)
-            return e;
-        mark(mk, "decode_gemm");
         if ((e = launch_decode_reduce(gpart, M, d_in, d_out, y, yf, lo, false, s)) != hipSuccess) return e;
         mark(mk, "decode_reduce_lora");
         return hipSuccess;

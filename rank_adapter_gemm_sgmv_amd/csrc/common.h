@@ -179,6 +179,14 @@ struct DecodeLora {
     int pool_rows;
 };
 
+// The segment build the medium-batch decode GEMM launch runs in one extra workgroup beside
+// the GEMM (the GEMM itself does not read segments; the shrink launched after it does).
+struct SegBuild {
+    const int32_t *ids;  // [M]
+    int n_adapters;
+    Seg seg;
+};
+
 // Decode batches up to this many rows take the fused path (x W and x A_i as tiles of one
 // split-K launch) when d_in % 32 == 0: the slot tables of batch_adapters.h hold this many
 // rows, and beyond it one adapter tile per distinct adapter costs more than the
@@ -194,9 +202,10 @@ bool decode_fused_supported(int M, int K, int N);  // and M <= kDecodeMaxRows
 size_t decode_gemm_partial_floats(int M, int K, int N, int r_max, int n_adapters);
 // Split-K partial tiles of x W for a decode batch; with `adapters` (M <= kDecodeMaxRows)
 // the same launch also streams the batch's adapters' A as extra tiles (the LoRA shrink).
+// build (nullable): also build the segments of these ids, in one more workgroup.
 hipError_t launch_decode_gemm(const uint16_t *x, const uint16_t *W, const uint16_t *A, int M,
                               int K, int N, const DecodeLora &lo, bool adapters, float *partial,
-                              hipStream_t s);
+                              const SegBuild *build, hipStream_t s);
 
 // y = (split partials added in order) + scale_a * t B_a, t from the adapter tiles' splits
 // (`adapters`) or from the segment-path shrink's chunk sums; rounds once into y.

@@ -34,6 +34,7 @@
 //    read once from HBM (rows of one adapter share it through L2).  No atomics: the result
 //    does not depend on scheduling.
 #include "batch_adapters.h"
+#include "segments_block.h"
 
 namespace lora {
 
@@ -193,11 +194,24 @@ template <class C, int RM>
 __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ W, const uint16_t *__restrict__ A,
     int M, int K, int N, int n_tm, int n_tn, int n_lt, int k_per_split, float *__restrict__ partial,
-    DecodeLora lo) {
+    DecodeLora lo, int n_gemm_blocks, SegBuild build) {
     // wave w's part: x stages 0, 1 then W stages 0 .. 3; after the K loop, its partial tile
     __shared__ __attribute__((aligned(1024))) uint4 lds[kWaves * C::WAVE];
     __shared__ BatchAdapters ba;
     constexpr int APT = AdapterTiles<RM>::APT;
+
+    if ((int)blockIdx.x >= n_gemm_blocks) {
+        // the extra workgroup: the segment build, in this kernel's LDS (the launch is a grid of
+        // one workgroup per CU or fewer, so it runs beside the GEMM on a CU of its own)
+        static_assert(kWaves * C::WAVE * 16 >= (LORA_MAX_ADAPTERS + 1) * 4 + 64 * 4,
+                      "the builder's tables fit the GEMM's LDS");
+        int32_t *cnt = reinterpret_cast<int32_t *>(lds);
+        int32_t(*wave_tot)[kWaves] =
+            reinterpret_cast<int32_t(*)[kWaves]>(cnt + ((build.n_adapters + 1 + 15) & ~15));
+        build_segments_block<kThreads>(build.ids, M, build.n_adapters, build.seg, cnt, wave_tot,
+                                       &wave_tot[3][0]);
+        return;
+    }
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -207,7 +221,7 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(
     // consecutive blocks of one XCD (workgroup b runs on XCD b % 8), so both read a W column
     // panel through that XCD's L2
     int lin = blockIdx.x;
-    if (n_tm > 1 && (gridDim.x & 7) == 0) lin = (blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+    if (n_tm > 1 && (n_gemm_blocks & 7) == 0) lin = (blockIdx.x & 7) * (n_gemm_blocks >> 3) + (blockIdx.x >> 3);
     const int tile = lin % n_tiles, split = lin / n_tiles;
     const int tm = tile % n_tm, tn = tile / n_tm;
     const int m0 = tm * C::BM;
@@ -528,17 +542,21 @@ size_t decode_gemm_partial_floats(int M, int K, int N, int r_max, int n_adapters
 
 hipError_t launch_decode_gemm(const uint16_t *x, const uint16_t *W, const uint16_t *A, int M,
                               int K, int N, const DecodeLora &lo, bool adapters, float *partial,
-                              hipStream_t s) {
+                              const SegBuild *build, hipStream_t s) {
     if (!decode_gemm_supported(M, K, N) || partial == nullptr || !rank_ok(lo.r_max) ||
         (adapters && (M > kDecodeMaxRows || A == nullptr || lo.ids == nullptr ||
                       (lo.n_adapters > M && lo.slots == nullptr))))
         return hipErrorInvalidValue;
     const int n_lt = adapters ? adapter_tiles(M, lo.r_max, lo.n_adapters) : 0;
     const DecPlan p = dec_plan(M, K, N, n_lt);
-    const dim3 grid(p.n_tm * (p.n_tn + p.n_lt) * p.ks);
+    if (build && (build->ids == nullptr || build->n_adapters < 1 || build->n_adapters > LORA_MAX_ADAPTERS))
+        return hipErrorInvalidValue;
+    const int n_gemm = p.n_tm * (p.n_tn + p.n_lt) * p.ks;
+    const dim3 grid(n_gemm + (build ? 1 : 0));
+    const SegBuild bld = build ? *build : SegBuild{nullptr, 1, Seg{}};
 #define GEMM_LAUNCH(BM, RMX)                                                                  \
     launch((decode_gemm_kernel<Dec<BM>, RMX>), grid, dim3(kThreads), 0, s, x, W, A, M, K, N,   \
-           p.n_tm, p.n_tn, p.n_lt, p.k_per_split, partial, lo)
+           p.n_tm, p.n_tn, p.n_lt, p.k_per_split, partial, lo, n_gemm, bld)
 #define GEMM_RANK(BM)                                                                         \
     switch (lo.r_max) {                                                                       \
         case 8: GEMM_LAUNCH(BM, 8); break;                                                    \
