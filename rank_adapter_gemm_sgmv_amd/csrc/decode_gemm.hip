@@ -190,7 +190,8 @@ struct AdapterTiles {
 // (rows [split k_per_split, +k_per_split)) for one 128-column tile -- of W, or of the
 // adapters' A laid side by side -- and the workgroup writes its partial tile;
 // reduce_lora_kernel adds the splits in order.
-template <class C, int RM>
+// BUILD: one more workgroup (the last) builds the segments instead (see SegBuild).
+template <class C, int RM, bool BUILD>
 __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ W, const uint16_t *__restrict__ A,
     int M, int K, int N, int n_tm, int n_tn, int n_lt, int k_per_split, float *__restrict__ partial,
@@ -200,7 +201,7 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(
     __shared__ BatchAdapters ba;
     constexpr int APT = AdapterTiles<RM>::APT;
 
-    if ((int)blockIdx.x >= n_gemm_blocks) {
+    if (BUILD && (int)blockIdx.x >= n_gemm_blocks) {
         // the extra workgroup: the segment build, in this kernel's LDS (the launch is a grid of
         // one workgroup per CU or fewer, so it runs beside the GEMM on a CU of its own)
         static_assert(kWaves * C::WAVE * 16 >= (LORA_MAX_ADAPTERS + 1) * 4 + 64 * 4,
@@ -366,15 +367,16 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(
 // m's adapter tile (n_lt > 0), or the segment-path shrink's chunk sums tpart[c][m][j]
 // (n_lt == 0).  Block (column chunk of 1024, row m), 256 threads x 4 columns.  The partial
 // and B loads are issued before t is summed, so their latency overlaps it.
-template <int BM, int RM, bool YF32>
+// MS: the most splits the launch can have (4 or 16; registers for the split partials).
+template <int BM, int RM, bool YF32, int MS>
 __global__ __launch_bounds__(256) void reduce_lora_kernel(const float *__restrict__ partial,
                                                           int M, int N, int n_tm, int n_tn,
                                                           int n_lt, int n_splits, DecodeLora lo,
                                                           void *__restrict__ y) {
-    constexpr int kMaxSplits = 16;
+    constexpr int kMaxSplits = MS;
     constexpr int APT = AdapterTiles<RM>::APT;
     __shared__ float s_t[RM];
-    constexpr int kTpartMax = 8192;  // n_t x RM floats staged in LDS
+    constexpr int kTpartMax = 4096;  // n_t x RM floats staged in LDS
     const int m = blockIdx.y;
     const int n = (blockIdx.x * 256 + threadIdx.x) * 4;
     const bool col_ok = n < N;
@@ -456,18 +458,19 @@ __global__ __launch_bounds__(256) void reduce_lora_kernel(const float *__restric
     }
     if (has) {
         float d0 = 0.f, d1 = 0.f, d2 = 0.f, d3 = 0.f;
+        // chunk j0 is multiplied while chunk j0 + BCH is being loaded (r is uniform in the
+        // block; rows past the rank add nothing)
 #pragma unroll
-        for (int j = 0; j < BCH; ++j) {
-            const float tj = j < r ? s_t[j] : 0.0f;  // rows past the rank add nothing
-            d0 = fmaf(tj, bf16_lo(bv[j].x), d0);
-            d1 = fmaf(tj, bf16_hi(bv[j].x), d1);
-            d2 = fmaf(tj, bf16_lo(bv[j].y), d2);
-            d3 = fmaf(tj, bf16_hi(bv[j].y), d3);
-        }
-        for (int j0 = BCH; j0 < r; j0 += BCH) {  // r is uniform in the block
+        for (int j0 = 0; j0 < RM; j0 += BCH) {
+            if (j0 >= r) break;
+            uint2 nb[BCH];
+            const bool more = RM > BCH && j0 + BCH < r;
+            if (more) {
 #pragma unroll
-            for (int j = 0; j < BCH; ++j)
-                bv[j] = j0 + j < r ? *reinterpret_cast<const uint2 *>(bp + (size_t)(j0 + j) * N) : make_uint2(0, 0);
+                for (int j = 0; j < BCH; ++j)
+                    nb[j] = j0 + BCH + j < r ? *reinterpret_cast<const uint2 *>(bp + (size_t)(j0 + BCH + j) * N)
+                                             : make_uint2(0, 0);
+            }
 #pragma unroll
             for (int j = 0; j < BCH; ++j) {
                 const float tj = j0 + j < r ? s_t[j0 + j] : 0.0f;
@@ -475,6 +478,10 @@ __global__ __launch_bounds__(256) void reduce_lora_kernel(const float *__restric
                 d1 = fmaf(tj, bf16_hi(bv[j].x), d1);
                 d2 = fmaf(tj, bf16_lo(bv[j].y), d2);
                 d3 = fmaf(tj, bf16_hi(bv[j].y), d3);
+            }
+            if (more) {
+#pragma unroll
+                for (int j = 0; j < BCH; ++j) bv[j] = nb[j];
             }
         }
         const float sc = lo.scale[a];
@@ -555,8 +562,12 @@ hipError_t launch_decode_gemm(const uint16_t *x, const uint16_t *W, const uint16
     const dim3 grid(n_gemm + (build ? 1 : 0));
     const SegBuild bld = build ? *build : SegBuild{nullptr, 1, Seg{}};
 #define GEMM_LAUNCH(BM, RMX)                                                                  \
-    launch((decode_gemm_kernel<Dec<BM>, RMX>), grid, dim3(kThreads), 0, s, x, W, A, M, K, N,   \
-           p.n_tm, p.n_tn, p.n_lt, p.k_per_split, partial, lo, n_gemm, bld)
+    if (build)                                                                                \
+        launch((decode_gemm_kernel<Dec<BM>, RMX, true>), grid, dim3(kThreads), 0, s, x, W, A, M, \
+               K, N, p.n_tm, p.n_tn, p.n_lt, p.k_per_split, partial, lo, n_gemm, bld);         \
+    else                                                                                      \
+        launch((decode_gemm_kernel<Dec<BM>, RMX, false>), grid, dim3(kThreads), 0, s, x, W, A, M,\
+               K, N, p.n_tm, p.n_tn, p.n_lt, p.k_per_split, partial, lo, n_gemm, bld)
 #define GEMM_RANK(BM)                                                                         \
     switch (lo.r_max) {                                                                       \
         case 8: GEMM_LAUNCH(BM, 8); break;                                                    \
@@ -584,8 +595,12 @@ hipError_t launch_decode_reduce(const float *partial, int M, int K, int N, void 
     const DecPlan p = dec_plan(M, K, N, n_lt);
     const dim3 rgrid((unsigned)((N + 1023) / 1024), (unsigned)M);
 #define RED_LAUNCH(BM, RMX, YF)                                                             \
-    launch((reduce_lora_kernel<BM, RMX, YF>), rgrid, dim3(256), 0, s, partial, M, N, p.n_tm,    \
-           p.n_tn, p.n_lt, p.ks, lo, y)
+    if (p.ks <= 4)                                                                          \
+        launch((reduce_lora_kernel<BM, RMX, YF, 4>), rgrid, dim3(256), 0, s, partial, M, N,     \
+               p.n_tm, p.n_tn, p.n_lt, p.ks, lo, y);                                         \
+    else                                                                                    \
+        launch((reduce_lora_kernel<BM, RMX, YF, 16>), rgrid, dim3(256), 0, s, partial, M, N,    \
+               p.n_tm, p.n_tn, p.n_lt, p.ks, lo, y)
 #define RED_RANK(BM, YF)                                                                    \
     switch (lo.r_max) {                                                                     \
         case 8: RED_LAUNCH(BM, 8, YF); break;                                               \
