@@ -13,6 +13,13 @@
         bytes: traffic = FETCH_SIZE * 1024 * N / FETCH_calib + WRITE_SIZE * 1024 * N / WRITE_calib.
         The output carries the digest of the kernel sources it was taken on; bench.py reports
         the traffic only while the sources still have that digest.
+
+    python -m rank_adapter_gemm_sgmv_amd.profsum mfma CSV --workload NAME --mode decode|prefill \
+            --command C [--xcds 8] [--simds 1024]
+        MFMA use per kernel of the path from one ``rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES
+        GRBM_GUI_ACTIVE SQ_INSTS_VALU_MFMA_MOPS_BF16`` run: MFMA busy cycles per SIMD, the
+        fraction of the dispatch's duration they fill at the nominal clock (= the fraction of
+        the nominal bf16 peak), and the bf16 MFMA flops the hardware counted (MOPS x 512).
 """
 import argparse
 import csv
@@ -142,6 +149,52 @@ def counters_table(fetch_csv, write_csv, workload, mode, calib_bytes, fetch_cmd,
     return "\n".join(out)
 
 
+def per_dispatch_full(counter_csv: str):
+    """{dispatch: {"name", "ns", counter: summed value}} from a counter-collection CSV."""
+    acc = {}
+    for r in csv.DictReader(open(counter_csv)):
+        key = int(r["Dispatch_Id"])
+        d = acc.setdefault(key, {"name": r["Kernel_Name"],
+                                 "ns": float(r["End_Timestamp"]) - float(r["Start_Timestamp"])})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return acc
+
+
+def mfma_table(csv_path, workload, mode, command, xcds=8, simds=1024, ghz=2.4) -> str:
+    rows = per_dispatch_full(csv_path)
+    sep = any(step_of(d["name"], mode) == "shrink" for d in rows.values())
+    by = {}
+    for d in rows.values():
+        step = step_of(d["name"], mode, sep)
+        if step is None or "SQ_VALU_MFMA_BUSY_CYCLES" not in d:
+            continue
+        by.setdefault(step, []).append(d)
+    out = [f"# MFMA use per launch: {workload} ({mode})", "",
+           f"sources_digest: {kernel_sources_digest()}", "",
+           "Command (from the repository root on the GPU host):", "", "```", command, "```", "",
+           f"busy cycles per SIMD = SQ_VALU_MFMA_BUSY_CYCLES / {simds}; busy at {ghz} GHz = those "
+           f"cycles at the nominal clock over the dispatch's duration (the fraction of the nominal "
+           "bf16 peak the kernel reaches; the counter run serialises dispatches, so durations are "
+           "a little longer than in the timed runs); bf16 GFLOP = SQ_INSTS_VALU_MFMA_MOPS_BF16 x "
+           f"512, what the MFMA units executed.  GRBM_GUI_ACTIVE / {xcds} covers the whole "
+           "counter-collection window of a dispatch, not the kernel alone, so it is listed but not "
+           "used as a clock.", "",
+           "| step | dispatches | duration us | MFMA busy cycles per SIMD | busy at nominal clock | "
+           "bf16 MFMA GFLOP per launch | GRBM_GUI_ACTIVE / XCDs |",
+           "|---|---|---|---|---|---|---|"]
+    for step in sorted(by):
+        ds = by[step]
+        n = len(ds)
+        ns = sum(d["ns"] for d in ds) / n
+        gui = sum(d.get("GRBM_GUI_ACTIVE", 0.0) for d in ds) / n / xcds
+        busy = sum(d.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) for d in ds) / n / simds
+        flops = sum(d.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) for d in ds) / n * 512
+        frac = busy / (ghz * ns) if ns > 0 else 0.0
+        out.append(f"| {step} | {n} | {ns / 1e3:.2f} | {busy:.0f} | {100 * frac:.1f}% | "
+                   f"{flops / 1e9:.2f} | {gui:.0f} |")
+    return "\n".join(out) + "\n"
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(prog="profsum")
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -157,9 +210,18 @@ def main(argv=None):
     c.add_argument("--calib-bytes", type=int, required=True)
     c.add_argument("--fetch-command", required=True)
     c.add_argument("--write-command", required=True)
+    f = sub.add_parser("mfma")
+    f.add_argument("csv")
+    f.add_argument("--workload", required=True)
+    f.add_argument("--mode", choices=("decode", "prefill"), required=True)
+    f.add_argument("--command", required=True)
+    f.add_argument("--xcds", type=int, default=8)
+    f.add_argument("--simds", type=int, default=1024)
     a = ap.parse_args(argv)
     if a.cmd == "trace":
         sys.stdout.write(trace_table(a.stats_csv, a.title, a.command))
+    elif a.cmd == "mfma":
+        sys.stdout.write(mfma_table(a.csv, a.workload, a.mode, a.command, a.xcds, a.simds))
     else:
         sys.stdout.write(counters_table(a.fetch, a.write, a.workload, a.mode, a.calib_bytes,
                                         a.fetch_command, a.write_command))
