@@ -99,7 +99,12 @@ def _check(code: int, what: str) -> None:
 
 
 def _threads(n: Optional[int]) -> int:
-    return int(n) if n else (os.cpu_count() or 1)
+    """Explicit count, else OMP_NUM_THREADS when set (a shared host's CPU share), else
+    every core."""
+    if n:
+        return int(n)
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    return int(env) if env.isdigit() and int(env) > 0 else (os.cpu_count() or 1)
 
 
 def build_segments(ids, n_adapters: int, tile_rows: int, lib=None) -> dict:

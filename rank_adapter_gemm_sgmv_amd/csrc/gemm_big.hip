@@ -317,12 +317,16 @@ __global__ __launch_bounds__(C::NT) void gemm_big_kernel(const uint16_t *__restr
     }
 
     if constexpr (LORA) {
-        // Runs of one adapter among this tile's rows (positions of perm): for each run, 32
+        // Runs of one adapter among this tile's rows (positions of perm): for each run, 16
         // rank columns at a time, stage T = scale_a * t[rows, :] (zero outside the run) in
-        // slot 0's x layout and B_a[:, tile columns] (zero beyond r_max) in its W layout, then
-        // one more MFMA step.
+        // slot 0's x layout as a pair of bf16 values per element -- k slots 0..15 the value
+        // rounded to bf16, slots 16..31 the remainder (exact in fp32) rounded to bf16 -- and
+        // B_a's same 16 rank rows twice in its W layout (zero beyond the rank), then one more
+        // MFMA step.  The pair carries scale * t to about 16 significant bits, so the delta is
+        // not rounded to bf16 precision before it is added.
         const int n_lora = seg.meta[1];
         const int RM = ep.r_max;
+        constexpr int kHalf = kBK / 2;
         int p = row0;
         const int p_end = min(row0 + C::BM, n_lora);
         while (p < p_end) {
@@ -335,27 +339,34 @@ __global__ __launch_bounds__(C::NT) void gemm_big_kernel(const uint16_t *__restr
             // in a compact one
             int ra = ep.roff ? min(max(ep.ranks[a], 0), RM) : RM;
             const int brow0 = adapter_row0(ep.roff, ep.pool_rows, a, RM, ra);
-            for (int rc = 0; rc < RM; rc += kBK) {
+            for (int rc = 0; rc < RM; rc += kHalf) {
                 lds_barrier();
                 for (int c = tid; c < C::BM * 4; c += C::NT) {
                     const int row = c >> 2, lc = c & 3;
                     const int pos = row0 + row;
-                    const int j = rc + lc * 8;
+                    const int j = rc + (lc & 1) * 8;
                     uint4 v = make_uint4(0, 0, 0, 0);
                     if (pos >= p && pos < q_end && j < RM) {
                         const float *tp = ep.t + (size_t)seg.perm[pos] * RM + j;
                         const float4 t0 = *reinterpret_cast<const float4 *>(tp);
                         const float4 t1 = *reinterpret_cast<const float4 *>(tp + 4);
-                        v = make_uint4(pack_bf16x2(s * t0.x, s * t0.y), pack_bf16x2(s * t0.z, s * t0.w),
-                                       pack_bf16x2(s * t1.x, s * t1.y), pack_bf16x2(s * t1.z, s * t1.w));
+                        float f[8] = {s * t0.x, s * t0.y, s * t0.z, s * t0.w,
+                                      s * t1.x, s * t1.y, s * t1.z, s * t1.w};
+                        if (lc >= 2) {  // the remainder after rounding to bf16
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) f[e] -= __uint_as_float(f32_to_bf16_rne(f[e]) << 16);
+                        }
+                        v = make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
+                                       pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7]));
                     }
                     X0[row * 4 + (lc ^ ((row >> 2) & 3))] = v;
                 }
                 for (int c = tid; c < kBK * C::WCH; c += C::NT) {
                     const int r = c / C::WCH, lc = c % C::WCH;
+                    const int rank = rc + (r & (kHalf - 1));
                     const int n = n0 + lc * 8;
                     uint4 v = make_uint4(0, 0, 0, 0);
-                    if (rc + r < ra && n < N) v = ld16(ep.B + ((size_t)brow0 + rc + r) * N + n);
+                    if (rank < ra && n < N) v = ld16(ep.B + ((size_t)brow0 + rank) * N + n);
                     W0[r * C::WCH + (lc ^ ((r & 3) << 2))] = v;
                 }
                 __syncthreads();

@@ -13,6 +13,7 @@ from .workloads import (  # noqa: F401
     f32_to_bf16_bits,
     make_workload,
     pool_param_count,
+    random_alpha,
     random_case,
     zipf_probs,
 )

@@ -258,14 +258,24 @@ def make_workload(config: int, seed: Optional[int] = None) -> Workload:
     return Workload(spec["name"], ids, ranks, alpha, r_max, projs, storage, seed)
 
 
+def random_alpha(seed: int, n_adapters: int, lo: float = 1.0, hi: float = 64.0) -> np.ndarray:
+    """Per-adapter alpha_i, uniform over [lo, hi) in float32, from a stream of its own
+    (PCG64 seeded with [seed, 1]), so that drawing it changes no other draw of a case.
+    alpha_i / r_i is then a different, almost never power-of-two scale for every adapter."""
+    rng = np.random.Generator(np.random.PCG64([int(seed), 1]))
+    return rng.uniform(lo, hi, size=int(n_adapters)).astype(np.float32)
+
+
 def random_case(seed: int, M: int, d_in: int, d_out: int, n_adapters: int, r_max: int,
                 ranks: Optional[Sequence[int]] = None, ids: Optional[Sequence[int]] = None,
-                base_frac: float = 0.2, alpha_per_rank: float = 2.0, storage: str = "bf16",
-                x_std: float = 1.0, w_std: float = 0.02, ab_std: float = 0.02) -> Workload:
+                base_frac: float = 0.2, alpha_per_rank: Optional[float] = None,
+                storage: str = "bf16", x_std: float = 1.0, w_std: float = 0.02,
+                ab_std: float = 0.02) -> Workload:
     """A small seeded case with free shapes, for parity sweeps and edge cases.
 
     ids default to uniform over adapters with a fraction ``base_frac`` of rows set to -1;
-    ranks default to uniform over [1, r_max].
+    ranks default to uniform over [1, r_max]; alpha defaults to ``random_alpha(seed, n)``
+    (a distinct scale alpha_i / r_i per adapter), or alpha_per_rank * r_i when given.
     """
     rng = np.random.Generator(np.random.PCG64(seed))
     if ids is None:
@@ -280,7 +290,10 @@ def random_case(seed: int, M: int, d_in: int, d_out: int, n_adapters: int, r_max
     else:
         ranks_a = np.asarray(ranks)
     ranks_a = ranks_a.astype(np.int32)
-    alpha = (np.float32(alpha_per_rank) * ranks_a.astype(np.float32)).astype(np.float32)
+    if alpha_per_rank is None:
+        alpha = random_alpha(seed, n_adapters)
+    else:
+        alpha = (np.float32(alpha_per_rank) * ranks_a.astype(np.float32)).astype(np.float32)
     x = _normal(rng, (M, d_in), x_std, storage)
     W = _normal(rng, (d_in, d_out), w_std, storage)
     A = _normal(rng, (n_adapters, d_in, r_max), ab_std, storage)

@@ -3,7 +3,7 @@ and the parity rule.
 
 The rule for floating-point outputs: max|y_gpu - y_ref| <= 2e-2 * max|y_ref| and
 mean relative error sum|y_gpu - y_ref| / sum|y_ref| <= 5e-3, over the whole output of a call
-(or over the sampled rows at full sizes).
+(every row; max|y_ref| is taken over that whole output).
 """
 
 from __future__ import annotations
