@@ -31,8 +31,10 @@
  *    B_i r_max x d_out: the transposes of [P1]'s "A: r x d_in, B: d_out x r" in "How much
  *    memory does one LoRA adapter actually cost?", same r * (d_in + d_out) parameters.
  *  - Limits.  0 <= M <= LORA_MAX_ROWS (M = 0 is a no-op that returns LORA_OK);
- *    d_in, d_out positive multiples of 8; r_max one of 8, 16, 32, 64;
- *    1 <= n_adapters <= LORA_MAX_ADAPTERS.
+ *    d_in, d_out positive multiples of 8; 1 <= r_max <= 64 (the pages' static maximum rank,
+ *    vLLM's max_lora_rank, [P1] "What does a working multi-LoRA config look like?");
+ *    1 <= n_adapters <= LORA_MAX_ADAPTERS.  The kernels work at the rank bucket of r_max
+ *    (8, 16, 32 or 64); any r_max is exact, since padded ranks add exact zeros.
  *  - Pool contents (caller's contract).  Every adapter is padded to r_max ([P1], "What
  *    does a working multi-LoRA config look like?" and "Where does multi-LoRA serving
  *    actually break?", rank padding): ranks[i] in [1, r_max], and the entries of A_i beyond
@@ -40,12 +42,14 @@
  *    is computed by the caller.  ranks may be NULL, meaning every adapter has rank r_max.
  *    Registering an adapter is a plain device copy into slot i of A and B plus ranks[i] and
  *    scale[i] ([P2], "How it works", "Loading and swapping adapters"); no call is needed.
- *  - ids.  ids[m] in [-1, n_adapters).  An id outside that range is counted in meta[2] on
- *    the device and its row is treated as base-only; nothing faults.
+ *  - ids.  ids[m] in [-1, n_adapters).  An id outside that range is treated as base-only on
+ *    the device (and counted in meta[2] where segments are built); nothing faults.  Callers
+ *    that want the error reported pass LORA_MODE_CHECKED (below).
  *  - Streams.  `stream` is a hipStream_t (NULL = the default stream).  Every call only
- *    enqueues work on it and returns; none synchronises.  The library keeps no state
- *    between calls and allocates nothing: the caller owns every buffer, including the
- *    workspace.  Calls that share a workspace or segment buffers must not overlap in time.
+ *    enqueues work on it and returns; none synchronises, except the checked mode and the
+ *    measurement aids (named below).  The library keeps no state between calls and
+ *    allocates no device memory: the caller owns every buffer, including the workspace.
+ *    Calls that share a workspace or segment buffers must not overlap in time.
  *  - Errors.  Arguments are validated on the host before anything is enqueued; on a
  *    validation error nothing is enqueued and the call returns the status.  LORA_ERR_HIP
  *    reports a failed launch; lora_last_hip_error() names the HIP error.
@@ -68,21 +72,34 @@ typedef enum {
     LORA_OK = 0,
     LORA_ERR_NULL = 1,      /* a required pointer is NULL */
     LORA_ERR_SHAPE = 2,     /* M, d_in, d_out or n_adapters out of range */
-    LORA_ERR_RANK = 3,      /* r_max not one of 8, 16, 32, 64 */
+    LORA_ERR_RANK = 3,      /* r_max outside [1, 64]; (checked mode) a rank outside [1, r_max] */
     LORA_ERR_ALIGN = 4,     /* a pointer is not aligned as required */
     LORA_ERR_WORKSPACE = 5, /* ws_bytes smaller than lora_workspace_bytes() */
     LORA_ERR_DTYPE = 6,     /* unknown lora_dtype_t */
     LORA_ERR_HIP = 7,       /* a kernel launch failed */
-    LORA_ERR_BAD_ID = 8,    /* reserved: invalid ids are counted on the device in meta[2] */
-    LORA_ERR_MODE = 9       /* unknown lora_mode_t */
+    LORA_ERR_BAD_ID = 8,    /* (checked mode) an id outside [-1, n_adapters) */
+    LORA_ERR_MODE = 9,      /* unknown lora_mode_t */
+    LORA_ERR_POOL = 10      /* (checked mode) a compact-pool adapter's rows leave the pool */
 } lora_status_t;
 
 typedef enum { LORA_BF16 = 0, LORA_F32 = 1 } lora_dtype_t;
 
-/* DECODE: y = x W on a decode-shaped GEMM, then y += delta (two roundings of a bf16 y).
- * PREFILL: x W with the delta added in the GEMM epilogue before the only store.
- * AUTO: PREFILL when M >= LORA_PREFILL_MIN_ROWS, else DECODE. */
+/* How lora_linear runs the layer ([P1], "How does one batch run 30 different adapters at
+ * once?": decode is bound by the weight bytes read, prefill by the xW GEMM, which dilutes
+ * the delta further):
+ * DECODE: the decode sequence -- a split-K or stream-K GEMM whose partial sums are added
+ *   with the delta in one pass that rounds y once.
+ * PREFILL: x W on the large-tile GEMM with the delta added in its epilogue before the only
+ *   store: scale * t enters the epilogue's bf16 MFMAs as a pair of bf16 values (the value
+ *   rounded to bf16 and the remainder rounded to bf16), about 16 significant bits.
+ * AUTO: PREFILL when M >= LORA_PREFILL_MIN_ROWS, else DECODE.
+ * LORA_MODE_CHECKED may be OR-ed into any mode (lora_linear, lora_linear_compact): the call
+ * first waits for `stream`, copies ids, ranks and rank_offsets to host memory and checks
+ * them -- ids in [-1, n_adapters) (else LORA_ERR_BAD_ID), ranks in [1, r_max] (else
+ * LORA_ERR_RANK), compact adapters inside the pool (else LORA_ERR_POOL) -- and enqueues
+ * nothing when one fails.  For tests and debugging; not for graph capture. */
 typedef enum { LORA_MODE_AUTO = 0, LORA_MODE_DECODE = 1, LORA_MODE_PREFILL = 2 } lora_mode_t;
+#define LORA_MODE_CHECKED 0x100
 #define LORA_PREFILL_MIN_ROWS 1024
 
 /* Rows grouped by adapter, as built by lora_build_segments.  All device buffers, owned by
@@ -105,12 +122,17 @@ typedef struct {
     int32_t *meta;
 } lora_segments_t;
 
-/* Upper bound on the number of tiles: min(M, n_adapters) + M / LORA_TILE_ROWS. */
+/* Upper bound on the number of tiles: min(M, n_adapters) + M / LORA_TILE_ROWS.  Sizing of
+ * the segment buffers that lora_build_segments fills ([P1], "How does one batch run 30
+ * different adapters at once?": no padding of the token dimension).  Returns 0 when M <= 0
+ * or n_adapters <= 0. */
 int32_t lora_max_tiles(int32_t M, int32_t n_adapters);
 
-/* Workspace bytes needed by lora_linear, lora_linear_compact and lora_shrink for these sizes
- * (0 when M = 0).
- * Returns 0 for arguments that the calls would reject. */
+/* Workspace bytes needed by lora_linear, lora_linear_compact, lora_shrink and
+ * lora_shrink_compact for these sizes (0 when M = 0): the segment buffers, t and the split-K
+ * partial sums of the shrink and of the base GEMM ([P3], "MoE Models Raise the Bar": split-K
+ * for the skinny products).  Returns 0 for arguments that the calls would reject.  The
+ * workspace is caller-owned device memory; its contents need no initialisation. */
 size_t lora_workspace_bytes(int32_t M, int32_t d_in, int32_t d_out, int32_t r_max,
                             int32_t n_adapters);
 
@@ -118,32 +140,67 @@ size_t lora_workspace_bytes(int32_t M, int32_t d_in, int32_t d_out, int32_t r_ma
  * and a stable scatter into perm, all on the device in one launch.  The grouping is what
  * lets one pass serve every adapter of the batch ([P1], "How does one batch run 30
  * different adapters at once?"; [P2], "Going deeper", grouping by adapter).
- * ids: int32[M] (device).  Output: seg (see lora_segments_t).  Deterministic. */
+ * ids: int32[M] (device).  Output: seg (see lora_segments_t; caller-owned device buffers).
+ * Invalid ids are counted in meta[2] and grouped with the base-only rows.  Deterministic.
+ * Errors: LORA_ERR_SHAPE (M or n_adapters out of range), LORA_ERR_NULL, LORA_ERR_ALIGN
+ * (4-byte ids and buffers, 8-byte tiles), LORA_ERR_HIP. */
 lora_status_t lora_build_segments(const int32_t *ids, int32_t M, int32_t n_adapters,
                                   lora_segments_t seg, void *stream);
 
-/* Shrink: t[m, j] = sum_k x[m, k] A[ids[m], k, j] for rows with an adapter (j < r_max,
- * columns beyond the adapter's rank are 0), t[m, :] = 0 for base-only rows.  seg must have
- * been built for the same ids, M and n_adapters.  ws: at least
- * lora_workspace_bytes(M, d_in, 8, r_max, n_adapters) bytes (split-K partial sums).  The
- * partial sums are added in a fixed order: the result is deterministic. */
+/* Shrink, the first step of the delta ([P3], "MoE Models Raise the Bar"; the [B, d_in] x
+ * [d_in, r] product of [P1], "How does one batch run 30 different adapters at once?"):
+ * t[m, j] = sum_k x[m, k] A[ids[m], k, j] for rows with an adapter (j < r_max; columns
+ * beyond the adapter's rank are 0), t[m, :] = 0 for base-only rows.
+ * x[M, d_in], A[n_adapters, d_in, r_max] (padded pool), t[M, r_max] fp32 (device; t is
+ * written, 16-byte aligned at its start).  seg must have been built for the same ids, M and
+ * n_adapters.  ws: at least lora_workspace_bytes(M, d_in, 8, r_max, n_adapters) bytes
+ * (split-K partial sums).  The partial sums are added in a fixed order: deterministic.
+ * Errors: as lora_linear's validation (LORA_ERR_SHAPE, _RANK, _NULL, _ALIGN, _WORKSPACE). */
 lora_status_t lora_shrink(const void *x, const void *A, const int32_t *ranks, int32_t M,
                           int32_t d_in, int32_t r_max, int32_t n_adapters,
                           lora_segments_t seg, float *t, void *ws, size_t ws_bytes,
                           void *stream);
 
-/* Expand: y[m, :] += scale[i] * sum_{j < ranks[i]} t[m, j] B[i, j, :] for every row m with
- * adapter i = ids[m] >= 0; base-only rows of y are not read or written.  One rounding per
- * element of y.  seg as for lora_shrink. */
+/* Shrink on a rank-compact pool (layout as for lora_linear_compact): the same t[M, r_max] as
+ * lora_shrink on the adapters zero-padded to r_max ([P1], "Where does multi-LoRA serving
+ * actually break?": padding wastes bandwidth when ranks differ).  ranks and rank_offsets
+ * are required (LORA_ERR_NULL); pool_rows in [1, n_adapters * r_max] (LORA_ERR_SHAPE). */
+lora_status_t lora_shrink_compact(const void *x, const void *A, const int32_t *ranks,
+                                  const int32_t *rank_offsets, int32_t pool_rows, int32_t M,
+                                  int32_t d_in, int32_t r_max, int32_t n_adapters,
+                                  lora_segments_t seg, float *t, void *ws, size_t ws_bytes,
+                                  void *stream);
+
+/* Expand, the second step of the delta, scaled as in the layer equation ([P3], "MoE Models
+ * Raise the Bar"; [P1], "Why can't you just merge LoRA weights into the base model?"):
+ * y[m, :] += scale[i] * sum_{j < ranks[i]} t[m, j] B[i, j, :] for every row m with adapter
+ * i = ids[m] >= 0; base-only rows of y are neither read nor written.  t[M, r_max] fp32
+ * (4-byte aligned), B[n_adapters, r_max, d_out], y[M, d_out] in y_dtype (read and written).
+ * One rounding per element of y.  seg as for lora_shrink.  No workspace.
+ * Errors: LORA_ERR_SHAPE, _RANK, _DTYPE, _NULL, _ALIGN, _HIP. */
 lora_status_t lora_expand(const float *t, const void *B, const float *scale,
                           const int32_t *ranks, int32_t M, int32_t d_out, int32_t r_max,
                           int32_t n_adapters, lora_segments_t seg, void *y,
                           lora_dtype_t y_dtype, void *stream);
 
-/* The whole layer: y = x W + (x A_i) B_i scale_i, overwriting y[M, d_out].
+/* Expand on a rank-compact pool (layout as for lora_linear_compact; same cite as
+ * lora_shrink_compact): B is [pool_rows][d_out].  ranks and rank_offsets are required. */
+lora_status_t lora_expand_compact(const float *t, const void *B, const float *scale,
+                                  const int32_t *ranks, const int32_t *rank_offsets,
+                                  int32_t pool_rows, int32_t M, int32_t d_out, int32_t r_max,
+                                  int32_t n_adapters, lora_segments_t seg, void *y,
+                                  lora_dtype_t y_dtype, void *stream);
+
+/* The whole layer of [P1], "Why can't you just merge LoRA weights into the base model?":
+ * y = x W + (x A_i) B_i scale_i, overwriting y[M, d_out]; one shared GEMM over the mixed
+ * batch plus every row's own delta ([P2], "How it works", "Batching across different
+ * adapters"), rows with id -1 bit-identical to a base-only call.
  * segs: NULL to build the segments inside the workspace from ids, or segments already
  * built for these ids (lets several projections of one batch share one build).
- * ws: at least lora_workspace_bytes(M, d_in, d_out, r_max, n_adapters) bytes. */
+ * ws: at least lora_workspace_bytes(M, d_in, d_out, r_max, n_adapters) bytes.
+ * mode: see lora_mode_t (LORA_MODE_CHECKED may be OR-ed in).
+ * Errors: LORA_ERR_SHAPE, _RANK, _DTYPE, _MODE, _NULL, _ALIGN, _WORKSPACE before anything
+ * is enqueued; with LORA_MODE_CHECKED also _BAD_ID, _RANK; LORA_ERR_HIP on a failed launch. */
 lora_status_t lora_linear(const void *x, const void *W, const void *A, const void *B,
                           const float *scale, const int32_t *ranks, const int32_t *ids,
                           int32_t M, int32_t d_in, int32_t d_out, int32_t r_max,
@@ -157,15 +214,16 @@ lora_status_t lora_linear(const void *x, const void *W, const void *A, const voi
  * what good systems support ([P2], "Limits and pitfalls"), S-LoRA by keeping adapters of
  * different ranks together in one pool ([P3], "How S-LoRA Proved the Model").  Layout (all
  * device memory, caller-owned):
- *   ranks[i]         rank r_i of adapter i: a multiple of 8 in [8, r_max]
+ *   ranks[i]         rank r_i of adapter i, any value in [1, r_max]
  *   rank_offsets[i]  its first rank row: r_0 + ... + r_{i-1} for a packed pool (any
  *                    non-overlapping placement with rank_offsets[i] + r_i <= pool_rows works)
  *   A                bf16 [pool_rows * d_in]: A_i = [d_in][r_i] row-major at element
  *                    rank_offsets[i] * d_in
  *   B                bf16 [pool_rows][d_out]: B_i = rows rank_offsets[i] .. + r_i - 1
  *   pool_rows        rank rows in the pool, 1 <= pool_rows <= n_adapters * r_max
- * scale[i] = alpha_i / r_i as for lora_linear.  An adapter whose rank is not a multiple of 8
- * or whose rows leave the pool adds nothing (the kernels never read outside the pool).
+ * scale[i] = alpha_i / r_i as for lora_linear.  Tables that break this contract never make a
+ * kernel read outside the pool: an adapter whose rows leave it adds nothing, and a rank above
+ * r_max is clamped; LORA_MODE_CHECKED reports both (LORA_ERR_POOL, LORA_ERR_RANK).
  * Returns LORA_ERR_NULL when ranks or rank_offsets is NULL, LORA_ERR_SHAPE when pool_rows is
  * out of range, otherwise as lora_linear.  The result equals lora_linear's on the same
  * adapters zero-padded to r_max (up to the order of fp32 additions). */
@@ -177,7 +235,9 @@ lora_status_t lora_linear_compact(const void *x, const void *W, const void *A, c
                                   void *y, lora_dtype_t y_dtype, lora_mode_t mode, void *ws,
                                   size_t ws_bytes, void *stream);
 
-/* Measurement aid, not for serving loops: the same launches as lora_linear, each launched
+/* Measurement aid, not for serving loops (it times the per-kernel costs that [P1], "How does
+ * one batch run 30 different adapters at once?", attributes to decode and prefill; the pages
+ * define no such call): the same launches as lora_linear, each launched
  * with a start and a stop HIP event that the GPU stamps from that kernel's own dispatch (no
  * extra packet between kernels), so the times are kernel durations.  It then waits for the
  * last kernel and writes, in launch order, each kernel's duration in milliseconds to
@@ -202,7 +262,8 @@ lora_status_t lora_linear_compact_profiled(
     size_t ws_bytes, void *stream, float *kernel_ms, const char **kernel_names,
     int32_t max_kernels, int32_t *n_kernels);
 
-/* Human-readable name of a status. */
+/* Human-readable name of a status (error reporting of this ABI; no passage of the pages
+ * defines it).  Never NULL; unknown values give "unknown lora_status_t". */
 const char *lora_status_string(lora_status_t status);
 
 /* The HIP error string of the last call on this host thread that returned LORA_ERR_HIP

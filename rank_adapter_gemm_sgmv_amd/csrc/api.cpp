@@ -1,8 +1,10 @@
 // api.cpp -- the C ABI of liblora_mi355x.so (include/lora.h): host-side validation,
-// workspace layout and the launch sequence of each call.  No call allocates, synchronises
-// or keeps state.
+// workspace layout and the launch sequence of each call.  No call allocates device memory or
+// keeps state; only the checked mode and the measurement aids synchronise.
 #include <stdint.h>
 #include <string.h>
+
+#include <vector>
 
 #include "common.h"
 
@@ -19,7 +21,7 @@ size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-bool rank_ok(int32_t r_max) { return r_max == 8 || r_max == 16 || r_max == 32 || r_max == 64; }
+bool rank_ok(int32_t r_max) { return r_max >= 1 && r_max <= 64; }
 
 bool dim_ok(int32_t d) { return d > 0 && d <= kMaxDim && d % 8 == 0; }
 
@@ -56,17 +58,21 @@ lora_segments_t carve_segments(char *&p, int32_t M, int32_t n) {
     return s;
 }
 
+// Internal buffers (t, partial sums) are laid out at the kernel rank bucket of r_max.
 size_t shrink_partial_bytes(int32_t M, int32_t d_in, int32_t r_max) {
+    const int rb = rank_bucket(r_max);
     int kc, ksplit;
-    shrink_plan(d_in, r_max, &kc, &ksplit);
-    return round_up((size_t)ksplit * M * r_max * sizeof(float));
+    shrink_plan(d_in, rb, &kc, &ksplit);
+    return round_up((size_t)ksplit * M * rb * sizeof(float));
 }
 
-size_t t_bytes(int32_t M, int32_t r_max) { return round_up((size_t)M * r_max * sizeof(float)); }
+size_t t_bytes(int32_t M, int32_t r_max) {
+    return round_up((size_t)M * rank_bucket(r_max) * sizeof(float));
+}
 
 size_t gemm_bytes(int32_t M, int32_t d_in, int32_t d_out, int32_t r_max, int32_t n_adapters) {
     const size_t a = gemm_partial_floats(M, d_in, d_out),
-                 b = decode_gemm_partial_floats(M, d_in, d_out, r_max, n_adapters);
+                 b = decode_gemm_partial_floats(M, d_in, d_out, rank_bucket(r_max), n_adapters);
     return round_up((a > b ? a : b) * sizeof(float));
 }
 
@@ -113,9 +119,26 @@ lora_status_t lora_build_segments(const int32_t *ids, int32_t M, int32_t n_adapt
     return hip_status(launch_build_segments(ids, M, n_adapters, to_seg(seg), (hipStream_t)stream));
 }
 
-lora_status_t lora_shrink(const void *x, const void *A, const int32_t *ranks, int32_t M,
-                          int32_t d_in, int32_t r_max, int32_t n_adapters, lora_segments_t seg,
-                          float *t, void *ws, size_t ws_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Extra arguments of a rank-compact pool: the table of first rank rows and the pool's
+// rank-row count (at least one row, at most what the padded pool would hold).
+lora_status_t check_compact(const int32_t *ranks, const int32_t *rank_offsets, int32_t pool_rows,
+                            int32_t r_max, int32_t n_adapters) {
+    if (!ranks || !rank_offsets) return LORA_ERR_NULL;
+    if (!aligned(rank_offsets, 4)) return LORA_ERR_ALIGN;
+    if (pool_rows < 1 || (int64_t)pool_rows > (int64_t)n_adapters * r_max) return LORA_ERR_SHAPE;
+    return LORA_OK;
+}
+
+// lora_shrink / lora_shrink_compact (roff != nullptr): validated here, then the segment-path
+// shrink and the ordered sum of its chunks into t[M][r_max].
+lora_status_t shrink_call(const void *x, const void *A, const int32_t *ranks, const int32_t *roff,
+                          int32_t pool_rows, int32_t M, int32_t d_in, int32_t r_max,
+                          int32_t n_adapters, lora_segments_t seg, float *t, void *ws,
+                          size_t ws_bytes, void *stream) {
     lora_status_t st = check_common(M, r_max, n_adapters);
     if (st != LORA_OK) return st;
     if (!dim_ok(d_in)) return LORA_ERR_SHAPE;
@@ -126,22 +149,24 @@ lora_status_t lora_shrink(const void *x, const void *A, const int32_t *ranks, in
         (ranks && !aligned(ranks, 4)))
         return LORA_ERR_ALIGN;
     if (ws_bytes < shrink_partial_bytes(M, d_in, r_max)) return LORA_ERR_WORKSPACE;
+    const int rb = rank_bucket(r_max);
     int kc, ksplit;
-    shrink_plan(d_in, r_max, &kc, &ksplit);
+    shrink_plan(d_in, rb, &kc, &ksplit);
     clear_stale_error();
     hipStream_t s = (hipStream_t)stream;
     float *partial = static_cast<float *>(ws);
     const Seg sg = to_seg(seg);
     hipError_t e = launch_shrink(static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(A),
-                                 ranks, nullptr, 0, M, d_in, r_max, n_adapters, sg, partial, kc,
-                                 ksplit, s);
-    if (e == hipSuccess) e = launch_shrink_finalize(partial, M, r_max, ksplit, sg, t, s);
+                                 ranks, roff, pool_rows, r_max, M, d_in, rb, n_adapters, sg, partial,
+                                 kc, ksplit, s);
+    if (e == hipSuccess) e = launch_shrink_finalize(partial, M, rb, ksplit, sg, t, r_max, s);
     return hip_status(e);
 }
 
-lora_status_t lora_expand(const float *t, const void *B, const float *scale, const int32_t *ranks,
-                          int32_t M, int32_t d_out, int32_t r_max, int32_t n_adapters,
-                          lora_segments_t seg, void *y, lora_dtype_t y_dtype, void *stream) {
+lora_status_t expand_call(const float *t, const void *B, const float *scale, const int32_t *ranks,
+                          const int32_t *roff, int32_t pool_rows, int32_t M, int32_t d_out,
+                          int32_t r_max, int32_t n_adapters, lora_segments_t seg, void *y,
+                          lora_dtype_t y_dtype, void *stream) {
     lora_status_t st = check_common(M, r_max, n_adapters);
     if (st != LORA_OK) return st;
     if (!dim_ok(d_out)) return LORA_ERR_SHAPE;
@@ -149,13 +174,55 @@ lora_status_t lora_expand(const float *t, const void *B, const float *scale, con
     if (M == 0) return LORA_OK;
     if (!t || !B || !scale || !y) return LORA_ERR_NULL;
     if ((st = check_seg(seg)) != LORA_OK) return st;
-    if (!aligned(t, 16) || !aligned(B, 16) || !aligned(y, 16) || !aligned(scale, 4) ||
+    if (!aligned(t, 4) || !aligned(B, 16) || !aligned(y, 16) || !aligned(scale, 4) ||
         (ranks && !aligned(ranks, 4)))
         return LORA_ERR_ALIGN;
     clear_stale_error();
-    return hip_status(launch_expand(t, static_cast<const uint16_t *>(B), scale, ranks, nullptr, 0,
-                                    M, d_out, r_max, n_adapters, to_seg(seg), y,
-                                    y_dtype == LORA_F32, (hipStream_t)stream));
+    return hip_status(launch_expand(t, r_max, static_cast<const uint16_t *>(B), scale, ranks, roff,
+                                    pool_rows, r_max, M, d_out, rank_bucket(r_max), n_adapters,
+                                    to_seg(seg), y, y_dtype == LORA_F32, (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+lora_status_t lora_shrink(const void *x, const void *A, const int32_t *ranks, int32_t M,
+                          int32_t d_in, int32_t r_max, int32_t n_adapters, lora_segments_t seg,
+                          float *t, void *ws, size_t ws_bytes, void *stream) {
+    return shrink_call(x, A, ranks, nullptr, 0, M, d_in, r_max, n_adapters, seg, t, ws, ws_bytes,
+                       stream);
+}
+
+lora_status_t lora_shrink_compact(const void *x, const void *A, const int32_t *ranks,
+                                  const int32_t *rank_offsets, int32_t pool_rows, int32_t M,
+                                  int32_t d_in, int32_t r_max, int32_t n_adapters,
+                                  lora_segments_t seg, float *t, void *ws, size_t ws_bytes,
+                                  void *stream) {
+    lora_status_t st = check_common(M, r_max, n_adapters);
+    if (st == LORA_OK) st = check_compact(ranks, rank_offsets, pool_rows, r_max, n_adapters);
+    if (st != LORA_OK) return st;
+    return shrink_call(x, A, ranks, rank_offsets, pool_rows, M, d_in, r_max, n_adapters, seg, t, ws,
+                       ws_bytes, stream);
+}
+
+lora_status_t lora_expand(const float *t, const void *B, const float *scale, const int32_t *ranks,
+                          int32_t M, int32_t d_out, int32_t r_max, int32_t n_adapters,
+                          lora_segments_t seg, void *y, lora_dtype_t y_dtype, void *stream) {
+    return expand_call(t, B, scale, ranks, nullptr, 0, M, d_out, r_max, n_adapters, seg, y, y_dtype,
+                       stream);
+}
+
+lora_status_t lora_expand_compact(const float *t, const void *B, const float *scale,
+                                  const int32_t *ranks, const int32_t *rank_offsets,
+                                  int32_t pool_rows, int32_t M, int32_t d_out, int32_t r_max,
+                                  int32_t n_adapters, lora_segments_t seg, void *y,
+                                  lora_dtype_t y_dtype, void *stream) {
+    lora_status_t st = check_common(M, r_max, n_adapters);
+    if (st == LORA_OK) st = check_compact(ranks, rank_offsets, pool_rows, r_max, n_adapters);
+    if (st != LORA_OK) return st;
+    return expand_call(t, B, scale, ranks, rank_offsets, pool_rows, M, d_out, r_max, n_adapters, seg,
+                       y, y_dtype, stream);
 }
 
 }  // extern "C"
@@ -186,7 +253,8 @@ lora_status_t check_linear(const void *x, const void *W, const void *A, const vo
     if (st != LORA_OK) return st;
     if (!dim_ok(d_in) || !dim_ok(d_out)) return LORA_ERR_SHAPE;
     if (y_dtype != LORA_BF16 && y_dtype != LORA_F32) return LORA_ERR_DTYPE;
-    if (mode != LORA_MODE_AUTO && mode != LORA_MODE_DECODE && mode != LORA_MODE_PREFILL)
+    const int bm = mode & ~LORA_MODE_CHECKED;
+    if (bm != LORA_MODE_AUTO && bm != LORA_MODE_DECODE && bm != LORA_MODE_PREFILL)
         return LORA_ERR_MODE;
     if (M == 0) return LORA_OK;
     if (!x || !W || !A || !B || !scale || !ids || !y || !ws) return LORA_ERR_NULL;
@@ -199,13 +267,27 @@ lora_status_t check_linear(const void *x, const void *W, const void *A, const vo
     return LORA_OK;
 }
 
-// Extra arguments of a rank-compact pool: the table of first rank rows and the pool's
-// rank-row count (at least one row, at most what the padded pool would hold).
-lora_status_t check_compact(const int32_t *ranks, const int32_t *rank_offsets, int32_t pool_rows,
-                            int32_t r_max, int32_t n_adapters) {
-    if (!ranks || !rank_offsets) return LORA_ERR_NULL;
-    if (!aligned(rank_offsets, 4)) return LORA_ERR_ALIGN;
-    if (pool_rows < 1 || (int64_t)pool_rows > (int64_t)n_adapters * r_max) return LORA_ERR_SHAPE;
+// LORA_MODE_CHECKED: wait for the stream (the tables may be written by work queued on it),
+// copy ids, ranks and rank_offsets to host memory and check them: every id in [-1, n),
+// every rank in [1, r_max], and in a compact pool every adapter's rows inside the pool.
+// Returns LORA_ERR_BAD_ID, LORA_ERR_RANK or LORA_ERR_POOL for the first violation found.
+lora_status_t check_tables(const int32_t *ids, int32_t M, const int32_t *ranks,
+                           const int32_t *roff, int32_t pool_rows, int32_t r_max,
+                           int32_t n_adapters, hipStream_t s) {
+    hipError_t e = hipStreamSynchronize(s);
+    std::vector<int32_t> h_ids(M), h_ranks(ranks ? n_adapters : 0), h_off(roff ? n_adapters : 0);
+    if (e == hipSuccess) e = hipMemcpy(h_ids.data(), ids, (size_t)M * 4, hipMemcpyDeviceToHost);
+    if (e == hipSuccess && ranks)
+        e = hipMemcpy(h_ranks.data(), ranks, (size_t)n_adapters * 4, hipMemcpyDeviceToHost);
+    if (e == hipSuccess && roff)
+        e = hipMemcpy(h_off.data(), roff, (size_t)n_adapters * 4, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_status(e);
+    for (int32_t m = 0; m < M; ++m)
+        if (h_ids[m] < -1 || h_ids[m] >= n_adapters) return LORA_ERR_BAD_ID;
+    for (int32_t a = 0; a < (int32_t)h_ranks.size(); ++a)
+        if (h_ranks[a] < 1 || h_ranks[a] > r_max) return LORA_ERR_RANK;
+    for (int32_t a = 0; a < (int32_t)h_off.size(); ++a)
+        if (h_off[a] < 0 || (int64_t)h_off[a] + h_ranks[a] > pool_rows) return LORA_ERR_POOL;
     return LORA_OK;
 }
 
@@ -221,9 +303,10 @@ lora_status_t check_compact(const int32_t *ranks, const int32_t *rank_offsets, i
 //            and the expand
 //   decode otherwise: build_segments, shrink, shrink_finalize, gemm [, splitk_reduce], expand
 //   prefill: build_segments, shrink, shrink_finalize, gemm with the LoRA epilogue
-// A rank-compact pool (roff != nullptr, lora_linear_compact) takes the same sequences, except
-// that decode batches of at most 128 rows take the second one (the first lays adapters side
-// by side at row stride r_max).
+// A rank-compact pool (roff != nullptr, lora_linear_compact), and a padded pool whose r_max is
+// not a rank bucket (8, 16, 32, 64), take the same sequences, except that decode batches of
+// at most 128 rows take the second one (the first lays adapters side by side at row stride
+// r_max = the bucket).
 hipError_t run_linear(const void *x, const void *W, const void *A, const void *B,
                       const float *scale, const int32_t *ranks, const int32_t *roff,
                       int32_t pool_rows, const int32_t *ids, int32_t M, int32_t d_in,
@@ -244,15 +327,19 @@ hipError_t run_linear(const void *x, const void *W, const void *A, const void *B
     const uint16_t *Bb = static_cast<const uint16_t *>(B);
     const bool yf = y_dtype == LORA_F32;
     hipError_t e;
+    // kernels work at the rank bucket rb (t and partial sums rb wide); a padded pool's rank
+    // rows per adapter are the caller's r_max (pstride)
+    const int rb = rank_bucket(r_max), pstride = r_max;
     int kc, ksplit;
-    shrink_plan(d_in, r_max, &kc, &ksplit);
-    // (the fused path lays adapters side by side at row stride r_max: padded pools only)
-    if (!prefill && roff == nullptr && decode_fused_supported(M, d_in, d_out)) {
+    shrink_plan(d_in, rb, &kc, &ksplit);
+    // (the fused path lays adapters side by side at row stride rb: padded pools whose stride
+    // is the bucket only)
+    if (!prefill && roff == nullptr && r_max == rb && decode_fused_supported(M, d_in, d_out)) {
         // small decode batch: x W and the shrink x A_i as tiles of one split-K GEMM (the
         // row -> adapter slot map, when needed, goes to the t region), then one reduction
         // adds the splits and the expand
-        const DecodeLora lo{nullptr, 0, reinterpret_cast<int32_t *>(t), Bb, scale, ids, ranks, r_max,
-                            n_adapters, nullptr, 0};
+        const DecodeLora lo{nullptr, 0, reinterpret_cast<int32_t *>(t), Bb, scale, ids, ranks, rb,
+                            n_adapters, nullptr, 0, pstride};
         if ((e = launch_decode_gemm(xb, Wb, static_cast<const uint16_t *>(A), M, d_in, d_out, lo,
                                     true, gpart, nullptr, s)) != hipSuccess)
             return e;
@@ -266,15 +353,15 @@ hipError_t run_linear(const void *x, const void *W, const void *A, const void *B
         // workgroup of the same launch (unless the caller passed segments); then the
         // segment-path shrink, whose per-chunk partial sums have the layout the decode
         // reduction reads; the reduction with the expand
-        const DecodeLora lo{spart, ksplit, nullptr, Bb, scale, ids, ranks, r_max, n_adapters, roff,
-                            pool_rows};
+        const DecodeLora lo{spart, ksplit, nullptr, Bb, scale, ids, ranks, rb, n_adapters, roff,
+                            pool_rows, pstride};
         const SegBuild bld{ids, n_adapters, sg};
         if ((e = launch_decode_gemm(xb, Wb, nullptr, M, d_in, d_out, lo, false, gpart,
                                     segs ? nullptr : &bld, s)) != hipSuccess)
             return e;
         mark(mk, "decode_gemm");
-        if ((e = launch_shrink(xb, static_cast<const uint16_t *>(A), ranks, roff, pool_rows, M, d_in, r_max, n_adapters,
-                               sg, spart, kc, ksplit, s)) != hipSuccess)
+        if ((e = launch_shrink(xb, static_cast<const uint16_t *>(A), ranks, roff, pool_rows, pstride, M,
+                               d_in, rb, n_adapters, sg, spart, kc, ksplit, s)) != hipSuccess)
             return e;
         mark(mk, "shrink");
         if ((e = launch_decode_reduce(gpart, M, d_in, d_out, y, yf, lo, false, s)) != hipSuccess) return e;
@@ -285,20 +372,20 @@ hipError_t run_linear(const void *x, const void *W, const void *A, const void *B
         if ((e = launch_build_segments(ids, M, n_adapters, sg, s)) != hipSuccess) return e;
         mark(mk, "build_segments");
     }
-    if ((e = launch_shrink(xb, static_cast<const uint16_t *>(A), ranks, roff, pool_rows, M, d_in, r_max, n_adapters,
-                           sg, spart, kc, ksplit, s)) != hipSuccess)
+    if ((e = launch_shrink(xb, static_cast<const uint16_t *>(A), ranks, roff, pool_rows, pstride, M, d_in,
+                           rb, n_adapters, sg, spart, kc, ksplit, s)) != hipSuccess)
         return e;
     mark(mk, "shrink");
     // the stream-K reduction adds the shrink's chunk sums itself; the other consumers read t
     const bool stream_k = !prefill && sk_plan(M, d_in, d_out).use;
     if (!stream_k) {
-        if ((e = launch_shrink_finalize(spart, M, r_max, ksplit, sg, t, s)) != hipSuccess)
+        if ((e = launch_shrink_finalize(spart, M, rb, ksplit, sg, t, rb, s)) != hipSuccess)
             return e;
         mark(mk, "shrink_finalize");
     }
     int gsplit = 1;
     if (prefill) {
-        LoraEpilogue ep{t, Bb, scale, ids, r_max, n_adapters, ranks, roff, pool_rows};
+        LoraEpilogue ep{t, Bb, scale, ids, rb, n_adapters, ranks, roff, pool_rows, pstride};
         if ((e = launch_gemm(xb, Wb, M, d_in, d_out, y, yf, true, sg, &ep, nullptr, 0, &gsplit, s)) != hipSuccess)
             return e;
         mark(mk, "gemm_prefill_lora");
@@ -312,7 +399,7 @@ hipError_t run_linear(const void *x, const void *W, const void *A, const void *B
         // stream-K partial tiles: one pass adds them, t from the chunk sums, and the expand,
         // rows in segment order
         if ((e = launch_sk_reduce_lora(gpart, M, d_in, d_out, sk_plan(M, d_in, d_out), sg, spart,
-                                       ksplit, Bb, scale, ids, ranks, roff, pool_rows, r_max,
+                                       ksplit, Bb, scale, ids, ranks, roff, pool_rows, pstride, rb,
                                        n_adapters, y, yf, s)) != hipSuccess)
             return e;
         mark(mk, "decode_reduce_lora");
@@ -322,8 +409,8 @@ hipError_t run_linear(const void *x, const void *W, const void *A, const void *B
         if ((e = launch_splitk_reduce(gpart, M, d_out, gsplit, y, yf, s)) != hipSuccess) return e;
         mark(mk, "splitk_reduce");
     }
-    if ((e = launch_expand(t, Bb, scale, ranks, roff, pool_rows, M, d_out, r_max, n_adapters, sg, y,
-                           yf, s)) != hipSuccess)
+    if ((e = launch_expand(t, rb, Bb, scale, ranks, roff, pool_rows, pstride, M, d_out, rb, n_adapters,
+                           sg, y, yf, s)) != hipSuccess)
         return e;
     mark(mk, "expand");
     return hipSuccess;
@@ -342,8 +429,12 @@ lora_status_t lora_linear(const void *x, const void *W, const void *A, const voi
                                     segs, y, y_dtype, mode, ws, ws_bytes);
     if (st != LORA_OK || M == 0) return st;
     clear_stale_error();
+    if ((mode & LORA_MODE_CHECKED) &&
+        (st = check_tables(ids, M, ranks, nullptr, 0, r_max, n_adapters, (hipStream_t)stream)) != LORA_OK)
+        return st;
     return hip_status(run_linear(x, W, A, B, scale, ranks, nullptr, 0, ids, M, d_in, d_out, r_max,
-                                 n_adapters, segs, y, y_dtype, mode, ws, (hipStream_t)stream,
+                                 n_adapters, segs, y, y_dtype,
+                                 (lora_mode_t)(mode & ~LORA_MODE_CHECKED), ws, (hipStream_t)stream,
                                  nullptr));
 }
 
@@ -359,9 +450,14 @@ lora_status_t lora_linear_compact(const void *x, const void *W, const void *A, c
     if (st == LORA_OK) st = check_compact(ranks, rank_offsets, pool_rows, r_max, n_adapters);
     if (st != LORA_OK || M == 0) return st;
     clear_stale_error();
+    if ((mode & LORA_MODE_CHECKED) &&
+        (st = check_tables(ids, M, ranks, rank_offsets, pool_rows, r_max, n_adapters,
+                           (hipStream_t)stream)) != LORA_OK)
+        return st;
     return hip_status(run_linear(x, W, A, B, scale, ranks, rank_offsets, pool_rows, ids, M, d_in,
-                                 d_out, r_max, n_adapters, segs, y, y_dtype, mode, ws,
-                                 (hipStream_t)stream, nullptr));
+                                 d_out, r_max, n_adapters, segs, y, y_dtype,
+                                 (lora_mode_t)(mode & ~LORA_MODE_CHECKED), ws, (hipStream_t)stream,
+                                 nullptr));
 }
 
 }  // extern "C"
@@ -389,7 +485,8 @@ lora_status_t run_profiled(const void *x, const void *W, const void *A, const vo
     if (e == hipSuccess) {
         g_timer = &timer;
         e = run_linear(x, W, A, B, scale, ranks, roff, pool_rows, ids, M, d_in, d_out, r_max,
-                       n_adapters, segs, y, y_dtype, mode, ws, (hipStream_t)stream, &mk);
+                       n_adapters, segs, y, y_dtype, (lora_mode_t)(mode & ~LORA_MODE_CHECKED), ws,
+                       (hipStream_t)stream, &mk);
         g_timer = nullptr;
     }
     if (e == hipSuccess && timer.n > 0) e = hipEventSynchronize(timer.stop[timer.n - 1]);
@@ -455,13 +552,14 @@ const char *lora_status_string(lora_status_t status) {
         case LORA_OK: return "LORA_OK";
         case LORA_ERR_NULL: return "LORA_ERR_NULL: a required pointer is NULL";
         case LORA_ERR_SHAPE: return "LORA_ERR_SHAPE: M, d_in, d_out or n_adapters out of range";
-        case LORA_ERR_RANK: return "LORA_ERR_RANK: r_max must be 8, 16, 32 or 64";
+        case LORA_ERR_RANK: return "LORA_ERR_RANK: r_max outside [1, 64], or (checked mode) a rank outside [1, r_max]";
         case LORA_ERR_ALIGN: return "LORA_ERR_ALIGN: a pointer is not aligned as required";
         case LORA_ERR_WORKSPACE: return "LORA_ERR_WORKSPACE: workspace smaller than lora_workspace_bytes()";
         case LORA_ERR_DTYPE: return "LORA_ERR_DTYPE: unknown output dtype";
         case LORA_ERR_HIP: return "LORA_ERR_HIP: a kernel launch failed";
         case LORA_ERR_BAD_ID: return "LORA_ERR_BAD_ID: adapter id out of range";
         case LORA_ERR_MODE: return "LORA_ERR_MODE: unknown mode";
+        case LORA_ERR_POOL: return "LORA_ERR_POOL: (checked mode) an adapter's rank rows leave the compact pool";
     }
     return "unknown lora_status_t";
 }

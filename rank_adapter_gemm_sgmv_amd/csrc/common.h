@@ -53,21 +53,26 @@ __device__ __forceinline__ uint4 ld16(const void *p) { return *reinterpret_cast<
 __device__ __forceinline__ void st16(void *p, uint4 v) { *reinterpret_cast<uint4 *>(p) = v; }
 
 // ---- where an adapter's rank rows are ----------------------------------------------------
-// A padded pool (roff == nullptr) holds adapter a at rank rows a * r_max .. a * r_max + r_max
-// - 1 (rows beyond its rank are zero): A_a = A[a] is [d_in][r_max], B_a = B[a] is
-// [r_max][d_out].  A rank-compact pool holds it at rank rows roff[a] .. roff[a] + rank - 1 of
-// its pool_rows rank rows: A_a is the [d_in][rank] block at element roff[a] * d_in of A,
-// B_a the [rank][d_out] block at row roff[a] of B.  r is the adapter's rank, already clamped
-// to [0, r_max]; in a compact pool an adapter whose rank is not a multiple of 8 or whose rows
-// leave the pool gets r = 0 (it adds nothing), so no access leaves the pool.  Returns the
-// first rank row (0 when r becomes 0).
-__device__ __forceinline__ int adapter_row0(const int32_t *roff, int pool_rows, int a, int r_max,
+// A padded pool (roff == nullptr) holds adapter a at rank rows a * stride .. a * stride +
+// stride - 1, stride being the caller's r_max (rows beyond the adapter's rank are zero):
+// A_a = A[a] is [d_in][stride], B_a = B[a] is [stride][d_out].  A rank-compact pool holds it
+// at rank rows roff[a] .. roff[a] + rank - 1 of its pool_rows rank rows: A_a is the
+// [d_in][rank] block at element roff[a] * d_in of A, B_a the [rank][d_out] block at row
+// roff[a] of B.  r is the adapter's rank, already clamped to [0, width]; in a compact pool an
+// adapter whose rows leave the pool gets r = 0 (it adds nothing; the checked mode of the
+// ABI reports such a table), so no access leaves the pool.  Returns the first rank row (0
+// when r becomes 0).
+__device__ __forceinline__ int adapter_row0(const int32_t *roff, int pool_rows, int a, int stride,
                                             int &r) {
-    if (roff == nullptr) return a * r_max;
+    if (roff == nullptr) return a * stride;
     const int o = roff[a];
-    if ((r & 7) != 0 || o < 0 || o > pool_rows - r) r = 0;
+    if (o < 0 || o > pool_rows - r) r = 0;
     return r > 0 ? o : 0;
 }
+
+// Kernel rank bucket of a pool whose widest adapter has r_max rank rows: t, the shrink's
+// partial sums and every other internal buffer use the bucket as their row width.
+constexpr int rank_bucket(int r_max) { return r_max <= 8 ? 8 : r_max <= 16 ? 16 : r_max <= 32 ? 32 : 64; }
 
 // ---- kernel launches -------------------------------------------------------------------
 // Every kernel of the library is launched through launch().  Normally it is a plain launch;
@@ -100,16 +105,21 @@ hipError_t launch_build_segments(const int32_t *ids, int M, int n_adapters, Seg 
 
 // Split-K shrink: partial[ks][m][j] for rows of every tile; ks = 0..ksplit-1, chunks of
 // kc columns of x.  Followed by launch_shrink_finalize to sum the partials into t.
+// r_max: the kernel rank bucket (8, 16, 32 or 64; the partial sums' row width); pstride: the
+// padded pool's rank-row stride per adapter (the caller's r_max, <= the bucket; not read for
+// a compact pool).
 hipError_t launch_shrink(const uint16_t *x, const uint16_t *A, const int32_t *ranks,
-                         const int32_t *roff, int pool_rows, int M, int d_in, int r_max,
-                         int n_adapters, Seg seg, float *partial, int kc, int ksplit,
+                         const int32_t *roff, int pool_rows, int pstride, int M, int d_in,
+                         int r_max, int n_adapters, Seg seg, float *partial, int kc, int ksplit,
                          hipStream_t s);
+// t[m][0 : t_stride) from the partial sums (t_stride <= r_max, the bucket).
 hipError_t launch_shrink_finalize(const float *partial, int M, int r_max, int ksplit, Seg seg,
-                                  float *t, hipStream_t s);
+                                  float *t, int t_stride, hipStream_t s);
 
-hipError_t launch_expand(const float *t, const uint16_t *B, const float *scale,
-                         const int32_t *ranks, const int32_t *roff, int pool_rows, int M,
-                         int d_out, int r_max, int n_adapters, Seg seg, void *y, bool y_f32,
+// t rows are t_stride floats apart (t_stride >= the widest rank).
+hipError_t launch_expand(const float *t, int t_stride, const uint16_t *B, const float *scale,
+                         const int32_t *ranks, const int32_t *roff, int pool_rows, int pstride,
+                         int M, int d_out, int r_max, int n_adapters, Seg seg, void *y, bool y_f32,
                          hipStream_t s);
 
 // LoRA epilogue arguments of the prefill GEMM (rows are taken in segment order).
@@ -123,6 +133,7 @@ struct LoraEpilogue {
     const int32_t *ranks;  // [n], read only for a rank-compact pool
     const int32_t *roff;   // [n] first rank row of each adapter (rank-compact pool), or nullptr
     int pool_rows;
+    int pstride;           // padded pool: rank rows per adapter (<= r_max, the bucket)
 };
 
 // y = x W (+ LoRA epilogue when lora != nullptr).  `prefill` selects the 256x256 tiling
@@ -155,8 +166,8 @@ hipError_t launch_gemm_sk(const uint16_t *x, const uint16_t *W, int M, int K, in
 hipError_t launch_sk_reduce_lora(const float *partial, int M, int K, int N, const SkPlan &p,
                                  Seg seg, const float *tpart, int n_chunks, const uint16_t *B,
                                  const float *scale, const int32_t *ids, const int32_t *ranks,
-                                 const int32_t *roff, int pool_rows, int r_max, int n_adapters,
-                                 void *y, bool y_f32, hipStream_t s);
+                                 const int32_t *roff, int pool_rows, int pstride, int r_max,
+                                 int n_adapters, void *y, bool y_f32, hipStream_t s);
 
 // Adds the split-K decode GEMM's ksplit > 1 partial slices into y, in order.
 hipError_t launch_splitk_reduce(const float *partial, int M, int N, int ksplit, void *y,
@@ -172,11 +183,12 @@ struct DecodeLora {
     const uint16_t *B;     // [n][r_max][d_out]
     const float *scale;    // [n]
     const int32_t *ids;    // [M]
-    const int32_t *ranks;  // [n] true ranks, or nullptr (= r_max)
-    int r_max;
+    const int32_t *ranks;  // [n] true ranks, or nullptr (= pstride)
+    int r_max;             // the kernel rank bucket
     int n_adapters;
     const int32_t *roff;   // [n] first rank row of each adapter (rank-compact pool), or nullptr
     int pool_rows;
+    int pstride;           // padded pool: rank rows per adapter (<= r_max)
 };
 
 // The segment build the medium-batch decode GEMM launch runs in one extra workgroup beside

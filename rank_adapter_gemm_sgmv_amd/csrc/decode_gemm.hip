@@ -396,8 +396,9 @@ __global__ __launch_bounds__(256) void reduce_lora_kernel(const float *__restric
         if (sp < n_splits) pv[sp] = *reinterpret_cast<const float4 *>(pp + sp * stride);
     // B_a[j, nc .. nc+3] for the adapter's rank rows, issued together (the rank is uniform
     // in the block, so rows at or beyond it are not added, and above r_max 16 not loaded)
-    int r = !has ? 0 : lo.ranks ? min(max(lo.ranks[a], 1), RM) : RM;
-    const int row0 = adapter_row0(lo.roff, lo.pool_rows, a, RM, r);
+    const int width = lo.roff ? RM : lo.pstride;
+    int r = !has ? 0 : lo.ranks ? min(max(lo.ranks[a], 1), width) : width;
+    const int row0 = adapter_row0(lo.roff, lo.pool_rows, a, lo.pstride, r);
     // the first BCH rank rows of B are loaded here; above r_max 16 the rest follow in chunks
     // of 16 rows after t is summed (all 64 at once would take 128 registers)
     constexpr int BCH = RM <= 16 ? RM : 16;
@@ -405,8 +406,8 @@ __global__ __launch_bounds__(256) void reduce_lora_kernel(const float *__restric
     const uint16_t *bp = lo.B + (size_t)row0 * N + nc;
     // in a padded pool at r_max <= 16 every row is loaded (the padding rows exist), so the
     // loads need not wait for the rank; a compact pool's rows past the rank are the next
-    // adapter's
-    if (RM <= 16 && lo.roff == nullptr) {
+    // adapter's, and so are a padded pool's past its stride when that is below the bucket
+    if (RM <= 16 && lo.roff == nullptr && lo.pstride == RM) {
 #pragma unroll
         for (int j = 0; j < BCH; ++j) bv[j] = *reinterpret_cast<const uint2 *>(bp + (size_t)j * N);
     } else {

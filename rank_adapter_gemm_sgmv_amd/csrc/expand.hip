@@ -98,11 +98,14 @@ __device__ __forceinline__ void store_y(void *y, size_t off, const float (&f)[CP
     }
 }
 
+// t rows are t_stride floats apart; a padded pool (roff == nullptr) holds pstride <= RM rank
+// rows per adapter.
 template <int RM, bool YF32>
 __global__ __launch_bounds__(64 * kWavesPerBlock) void expand_kernel(
-    const float *__restrict__ t, const uint16_t *__restrict__ B, const float *__restrict__ scale,
-    const int32_t *__restrict__ ranks, const int32_t *__restrict__ roff, int pool_rows, int M,
-    int d_out, int n_cc, Seg seg, void *__restrict__ y) {
+    const float *__restrict__ t, int t_stride, const uint16_t *__restrict__ B,
+    const float *__restrict__ scale, const int32_t *__restrict__ ranks,
+    const int32_t *__restrict__ roff, int pool_rows, int pstride, int M, int d_out, int n_cc,
+    Seg seg, void *__restrict__ y) {
     using L = ExpandLanes<RM>;
     constexpr int CPL = L::CPL;
     const int lane = threadIdx.x & 63;
@@ -112,8 +115,9 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void expand_kernel(
         const int tile = w / n_cc, cc = w % n_cc;
         const int p0 = seg.tiles[2 * tile], a = seg.tiles[2 * tile + 1];
         const int p1 = min(p0 + kTileRows, seg.offsets[a + 1]);
-        int r = ranks ? min(max(ranks[a], 0), RM) : RM;
-        const int row0 = adapter_row0(roff, pool_rows, a, RM, r);
+        const int width = roff ? RM : pstride;
+        int r = ranks ? min(max(ranks[a], 0), width) : width;
+        const int row0 = adapter_row0(roff, pool_rows, a, pstride, r);
         const float s = scale[a];
         const int c = cc * L::COLS + lane * CPL;
         const bool colok = c < d_out;  // d_out % 8 == 0: a lane's columns are all in or all out
@@ -138,7 +142,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void expand_kernel(
             for (int i = 0; i < RB; ++i) {
                 mb[i] = seg.perm[min(pb + i, M - 1)];
                 load_y<CPL, YF32>(yb[i], y, (size_t)mb[i] * d_out + cl);
-                tv[i] = t[(size_t)mb[i] * RM + (lane < RM ? lane : 0)];
+                tv[i] = t[(size_t)mb[i] * t_stride + (lane < r ? lane : 0)];
             }
             float acc[RB][CPL];
 #pragma unroll
@@ -185,9 +189,9 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void expand_kernel(
 }
 
 template <int RM>
-hipError_t launch_rm(const float *t, const uint16_t *B, const float *scale, const int32_t *ranks,
-                     const int32_t *roff, int pool_rows, int M, int d_out, int n_adapters, Seg seg,
-                     void *y, bool y_f32, hipStream_t s) {
+hipError_t launch_rm(const float *t, int t_stride, const uint16_t *B, const float *scale,
+                     const int32_t *ranks, const int32_t *roff, int pool_rows, int pstride, int M,
+                     int d_out, int n_adapters, Seg seg, void *y, bool y_f32, hipStream_t s) {
     using L = ExpandLanes<RM>;
     const int n_cc = (d_out + L::COLS - 1) / L::COLS;
     const long items = (long)lora_max_tiles(M, n_adapters) * n_cc;
@@ -195,25 +199,26 @@ hipError_t launch_rm(const float *t, const uint16_t *B, const float *scale, cons
     const dim3 grid((unsigned)(blocks < kMaxGrid ? blocks : kMaxGrid));
     const dim3 block(64 * kWavesPerBlock);
     if (y_f32)
-        launch((expand_kernel<RM, true>), grid, block, 0, s, t, B, scale, ranks, roff, pool_rows, M, d_out,
-               n_cc, seg, y);
+        launch((expand_kernel<RM, true>), grid, block, 0, s, t, t_stride, B, scale, ranks, roff,
+               pool_rows, pstride, M, d_out, n_cc, seg, y);
     else
-        launch((expand_kernel<RM, false>), grid, block, 0, s, t, B, scale, ranks, roff, pool_rows, M, d_out,
-               n_cc, seg, y);
+        launch((expand_kernel<RM, false>), grid, block, 0, s, t, t_stride, B, scale, ranks, roff,
+               pool_rows, pstride, M, d_out, n_cc, seg, y);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_expand(const float *t, const uint16_t *B, const float *scale,
-                         const int32_t *ranks, const int32_t *roff, int pool_rows, int M,
-                         int d_out, int r_max, int n_adapters, Seg seg, void *y, bool y_f32,
+hipError_t launch_expand(const float *t, int t_stride, const uint16_t *B, const float *scale,
+                         const int32_t *ranks, const int32_t *roff, int pool_rows, int pstride,
+                         int M, int d_out, int r_max, int n_adapters, Seg seg, void *y, bool y_f32,
                          hipStream_t s) {
+    if ((roff == nullptr && (pstride < 1 || pstride > r_max)) || t_stride < 1) return hipErrorInvalidValue;
     switch (r_max) {
-        case 8: return launch_rm<8>(t, B, scale, ranks, roff, pool_rows, M, d_out, n_adapters, seg, y, y_f32, s);
-        case 16: return launch_rm<16>(t, B, scale, ranks, roff, pool_rows, M, d_out, n_adapters, seg, y, y_f32, s);
-        case 32: return launch_rm<32>(t, B, scale, ranks, roff, pool_rows, M, d_out, n_adapters, seg, y, y_f32, s);
-        case 64: return launch_rm<64>(t, B, scale, ranks, roff, pool_rows, M, d_out, n_adapters, seg, y, y_f32, s);
+        case 8: return launch_rm<8>(t, t_stride, B, scale, ranks, roff, pool_rows, pstride, M, d_out, n_adapters, seg, y, y_f32, s);
+        case 16: return launch_rm<16>(t, t_stride, B, scale, ranks, roff, pool_rows, pstride, M, d_out, n_adapters, seg, y, y_f32, s);
+        case 32: return launch_rm<32>(t, t_stride, B, scale, ranks, roff, pool_rows, pstride, M, d_out, n_adapters, seg, y, y_f32, s);
+        case 64: return launch_rm<64>(t, t_stride, B, scale, ranks, roff, pool_rows, pstride, M, d_out, n_adapters, seg, y, y_f32, s);
         default: return hipErrorInvalidValue;
     }
 }

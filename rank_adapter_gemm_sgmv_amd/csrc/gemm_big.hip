@@ -335,10 +335,10 @@ __global__ __launch_bounds__(C::NT) void gemm_big_kernel(const uint16_t *__restr
             const int q_end = min(seg.offsets[a + 1], p_end);
             if (q_end <= p) break;
             const float s = ep.scale[a];
-            // B_a's rank rows: all r_max of a padded pool (zero past the rank), the rank's
-            // in a compact one
-            int ra = ep.roff ? min(max(ep.ranks[a], 0), RM) : RM;
-            const int brow0 = adapter_row0(ep.roff, ep.pool_rows, a, RM, ra);
+            // B_a's rank rows: all of a padded pool's stride (zero past the rank), the
+            // rank's in a compact one
+            int ra = ep.roff ? min(max(ep.ranks[a], 0), RM) : ep.pstride;
+            const int brow0 = adapter_row0(ep.roff, ep.pool_rows, a, ep.pstride, ra);
             for (int rc = 0; rc < RM; rc += kHalf) {
                 lds_barrier();
                 for (int c = tid; c < C::BM * 4; c += C::NT) {
@@ -572,8 +572,8 @@ __global__ __launch_bounds__(256) void sk_reduce_lora_kernel(
     const float *__restrict__ partial, int M, int K, int N, int n_tm, int n_tn, int L, Seg seg,
     const float *__restrict__ tpart, int n_chunks, const uint16_t *__restrict__ B,
     const float *__restrict__ scale, const int32_t *__restrict__ ids,
-    const int32_t *__restrict__ ranks, const int32_t *__restrict__ roff, int pool_rows, int r_max,
-    int n_adapters, void *__restrict__ y) {
+    const int32_t *__restrict__ ranks, const int32_t *__restrict__ roff, int pool_rows, int pstride,
+    int r_max, int n_adapters, void *__restrict__ y) {
     static_assert(C::BN == 256, "one panel per block");
     __shared__ float4 s_part[256];
     __shared__ float s_t[8][64];
@@ -637,19 +637,24 @@ __global__ __launch_bounds__(256) void sk_reduce_lora_kernel(
     }
     if (!live) return;
     if (a >= 0 && a < n_adapters) {
-        // padded pool: the rank rounded up to whole groups of 4 (entries of t and B beyond
-        // the rank are zero); compact pool: the rank itself, a multiple of 8
-        int rk = ranks ? ranks[a] : r_max;
-        rk = roff ? min(max(rk, 0), r_max) : min((rk + 3) & ~3, r_max);
-        const int row0 = adapter_row0(roff, pool_rows, a, r_max, rk);
+        // the adapter's rank rows: all of a padded pool's stride, or fewer when ranks are
+        // given (entries of t and B beyond the rank are zero), in groups of 4; rows past the
+        // last row of the adapter are not loaded (they may be the next adapter's, or past
+        // the pool)
+        const int width = roff ? r_max : pstride;
+        int rk = ranks ? min(max(ranks[a], 0), width) : width;
+        const int row0 = adapter_row0(roff, pool_rows, a, pstride, rk);
         const float sc = scale[a];
         const float *tr = &s_t[pl][0];
         const uint16_t *Bp = B + (size_t)row0 * N + n;
+        const uint4 z = make_uint4(0, 0, 0, 0);
         float d[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         for (int j = 0; j < rk; j += 4) {
             const float4 tv = make_float4(tr[j], tr[j + 1], tr[j + 2], tr[j + 3]);
-            const uint4 b0 = ld16(Bp + (size_t)j * N), b1 = ld16(Bp + (size_t)(j + 1) * N);
-            const uint4 b2 = ld16(Bp + (size_t)(j + 2) * N), b3 = ld16(Bp + (size_t)(j + 3) * N);
+            const uint4 b0 = ld16(Bp + (size_t)j * N);
+            const uint4 b1 = j + 1 < rk ? ld16(Bp + (size_t)(j + 1) * N) : z;
+            const uint4 b2 = j + 2 < rk ? ld16(Bp + (size_t)(j + 2) * N) : z;
+            const uint4 b3 = j + 3 < rk ? ld16(Bp + (size_t)(j + 3) * N) : z;
             float f[8];
             unpack8(b0, f);
 #pragma unroll
@@ -755,18 +760,19 @@ hipError_t launch_gemm_sk(const uint16_t *x, const uint16_t *W, int M, int K, in
 hipError_t launch_sk_reduce_lora(const float *partial, int M, int K, int N, const SkPlan &p,
                                  Seg seg, const float *tpart, int n_chunks, const uint16_t *B,
                                  const float *scale, const int32_t *ids, const int32_t *ranks,
-                                 const int32_t *roff, int pool_rows, int r_max, int n_adapters,
-                                 void *y, bool y_f32, hipStream_t s) {
+                                 const int32_t *roff, int pool_rows, int pstride, int r_max,
+                                 int n_adapters, void *y, bool y_f32, hipStream_t s) {
     if (r_max < 8 || r_max > 64 || (r_max & (r_max - 1)) != 0) return hipErrorInvalidValue;
+    if (roff == nullptr && (pstride < 1 || pstride > r_max)) return hipErrorInvalidValue;
     const dim3 grid((unsigned)(((M + 7) / 8) * p.n_tn));
     if (y_f32)
         launch(sk_reduce_lora_kernel<CfgSk, true>, grid, dim3(256), 0, s, partial, M, K, N, p.n_tm,
-               p.n_tn, p.L, seg, tpart, n_chunks, B, scale, ids, ranks, roff, pool_rows, r_max,
-               n_adapters, y);
+               p.n_tn, p.L, seg, tpart, n_chunks, B, scale, ids, ranks, roff, pool_rows, pstride,
+               r_max, n_adapters, y);
     else
         launch(sk_reduce_lora_kernel<CfgSk, false>, grid, dim3(256), 0, s, partial, M, K, N, p.n_tm,
-               p.n_tn, p.L, seg, tpart, n_chunks, B, scale, ids, ranks, roff, pool_rows, r_max,
-               n_adapters, y);
+               p.n_tn, p.L, seg, tpart, n_chunks, B, scale, ids, ranks, roff, pool_rows, pstride,
+               r_max, n_adapters, y);
     return hipGetLastError();
 }
 

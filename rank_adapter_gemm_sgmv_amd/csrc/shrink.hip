@@ -54,12 +54,17 @@ struct MfmaShrink {
 // hands each lane 4 consecutive k of one column.  Column groups at or beyond the adapter's
 // rank are written to LDS as zeros.  All global loads are issued unconditionally (clamped
 // addresses; out-of-range values are masked at use), so they are all in flight together.
-// COMPACT: the pool is rank-compact (roff names each adapter's first rank row); otherwise
-// padded to r_max (roff is not read).
-template <int RM, bool COMPACT>
+// VARW: the rows of A_a are not RM wide -- a rank-compact pool (roff names each adapter's
+// first rank row, rows are rank wide) or a padded pool whose stride is below the bucket
+// (pstride < RM).  Otherwise the pool is padded at stride RM (roff and pstride not read).
+// A width that is not a multiple of 8 cannot be read in 16-byte groups per k row; such a
+// chunk of A_a is read as one flat run of 16-byte vectors instead (it starts 16-byte aligned:
+// d_in and the chunk's first k are multiples of 8) and scattered element by element into
+// the zeroed LDS rows.
+template <int RM, bool VARW>
 __global__ __launch_bounds__(64 * kWavesPerBlock) void shrink_mfma_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ A, const int32_t *__restrict__ ranks,
-    const int32_t *__restrict__ roff, int pool_rows, int M, int d_in, Seg seg,
+    const int32_t *__restrict__ roff, int pool_rows, int pstride, int M, int d_in, Seg seg,
     float *__restrict__ partial, int n_chunks, int kc) {
     using C = MfmaShrink<RM>;
     __shared__ __attribute__((aligned(16))) char lds[kWavesPerBlock][C::LDS];
@@ -77,11 +82,13 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void shrink_mfma_kernel(
         const int tile = w / n_chunks, c = w % n_chunks;
         const int p0 = seg.tiles[2 * tile], a = seg.tiles[2 * tile + 1];
         const int rows = min(p0 + kTileRows, seg.offsets[a + 1]) - p0;
-        int r = ranks ? min(max(ranks[a], 0), RM) : RM;
-        const int row0 = adapter_row0(COMPACT ? roff : nullptr, pool_rows, a, RM, r);
-        // row stride of A_a: r_max in a padded pool, the rank in a compact one, where the
-        // groups at or beyond the rank are not loaded (they belong to the next adapter)
-        const int rs = COMPACT ? r : RM;
+        // width of A_a's rows: RM, the padded stride, or (compact) the rank
+        const int width = !VARW ? RM : roff ? RM : pstride;
+        int r = ranks ? min(max(ranks[a], 0), width) : width;
+        const int row0 = adapter_row0(VARW ? roff : nullptr, pool_rows, a, VARW ? pstride : RM, r);
+        // row stride of A_a: in a compact pool the groups at or beyond the rank are not
+        // loaded (they belong to the next adapter)
+        const int rs = !VARW ? RM : roff ? r : pstride;
         const int k_lo = c * kc, k_hi = min(k_lo + kc, d_in);
         // this lane's x row (rows beyond the tile repeat its last row; their sums are dropped)
         const int mrow = seg.perm[p0 + min(li, rows - 1)];
@@ -95,7 +102,10 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void shrink_mfma_kernel(
         for (int kb = k_lo; kb < k_hi; kb += C::KS) {
             // A_a[kb .. kb+KS, 0:RM]: unit f = lane + 64 i is (row f / GR, group f % GR)
             uint4 av[C::AL];
-            if constexpr (!COMPACT) {
+            // (VARW) rows of a width that is not a multiple of 8: the flat run of the chunk
+            const bool flat = VARW && (rs & 7) != 0;
+            const int nvec = flat ? min(C::KS, k_hi - kb) * rs / 8 : 0;
+            if constexpr (!VARW) {
                 // padded pool: every group is loaded (the padding is zeros), so the loads do
                 // not wait for the rank
 #pragma unroll
@@ -103,22 +113,53 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void shrink_mfma_kernel(
                     const int f = lane + 64 * i, kr = kb + f / C::GR, gr = f % C::GR;
                     av[i] = ld16(Aa + (size_t)min(kr, d_in - 1) * RM + gr * 8);
                 }
-            } else {
+            } else if (!flat) {
 #pragma unroll
                 for (int i = 0; i < C::AL; ++i) {
                     const int f = lane + 64 * i, kr = kb + f / C::GR, gr = f % C::GR;
                     av[i] = gr * 8 < r ? ld16(Aa + (size_t)min(kr, d_in - 1) * rs + gr * 8)
                                        : make_uint4(0, 0, 0, 0);
                 }
+            } else {
+                // nvec <= KS * rs / 8 <= KS * RM / 8 = 64 * AL vectors, all inside A_a
+                const uint16_t *src = Aa + (size_t)kb * rs;
+#pragma unroll
+                for (int i = 0; i < C::AL; ++i) {
+                    const int v = lane + 64 * i;
+                    av[i] = v < nvec ? ld16(src + (size_t)v * 8) : make_uint4(0, 0, 0, 0);
+                }
             }
             uint4 xv[C::STEPS];
 #pragma unroll
             for (int st = 0; st < C::STEPS; ++st) xv[st] = ld16(xr + min(kb + 32 * st + 8 * g, d_in - 8));
+            if (!flat) {
 #pragma unroll
-            for (int i = 0; i < C::AL; ++i) {
-                const int f = lane + 64 * i, kr = f / C::GR, gr = f % C::GR;
-                const bool ok = kb + kr < k_hi && gr * 8 < r;
-                *reinterpret_cast<uint4 *>(wg + kr * C::LROW + gr * 16) = ok ? av[i] : make_uint4(0, 0, 0, 0);
+                for (int i = 0; i < C::AL; ++i) {
+                    const int f = lane + 64 * i, kr = f / C::GR, gr = f % C::GR;
+                    const bool ok = kb + kr < k_hi && gr * 8 < r;
+                    *reinterpret_cast<uint4 *>(wg + kr * C::LROW + gr * 16) = ok ? av[i] : make_uint4(0, 0, 0, 0);
+                }
+            } else {
+                // zero the wave's rows (columns at or beyond rs, rows at or beyond k_hi stay
+                // zero), wait for those writes, then place element e of the run at k row
+                // e / rs, column e % rs
+                for (int v = lane; v < C::KS * C::LROW / 16; v += 64)
+                    *reinterpret_cast<uint4 *>(wg + v * 16) = make_uint4(0, 0, 0, 0);
+                __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+#pragma unroll
+                for (int i = 0; i < C::AL; ++i) {
+                    const int v = lane + 64 * i;
+                    if (v < nvec) {
+                        int kr = (8 * v) / rs, j = (8 * v) % rs;
+                        const uint32_t wv4[4] = {av[i].x, av[i].y, av[i].z, av[i].w};
+#pragma unroll
+                        for (int q = 0; q < 8; ++q) {
+                            const uint16_t e = (uint16_t)(q & 1 ? wv4[q >> 1] >> 16 : wv4[q >> 1] & 0xFFFFu);
+                            *reinterpret_cast<uint16_t *>(wg + kr * C::LROW + j * 2) = e;
+                            if (++j == rs) { j = 0; ++kr; }
+                        }
+                    }
+                }
             }
             __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
 #pragma unroll
@@ -154,16 +195,18 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void shrink_mfma_kernel(
     }
 }
 
-// t[m, :] = sum over chunks (ascending) of partial[chunk][m][:] for LoRA rows; 0 for
+// t[m, 0:t_stride) = sum over chunks (ascending) of partial[chunk][m][:] for LoRA rows; 0 for
 // base-only rows.  One thread per 4 columns of one position of perm; eight chunk loads are
-// in flight at a time and added in chunk order.
+// in flight at a time and added in chunk order.  Rows of t are t_stride floats apart
+// (t_stride <= RM; 16-byte stores when it is a multiple of 4).
 __global__ __launch_bounds__(256) void shrink_finalize_kernel(const float *__restrict__ partial,
                                                               int M, int RM, int ksplit, Seg seg,
-                                                              float *__restrict__ t) {
+                                                              float *__restrict__ t, int t_stride) {
     const int per_row = RM / 4;
     const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= (long)M * per_row) return;
     const int p = (int)(idx / per_row), j = (int)(idx % per_row) * 4;
+    if (j >= t_stride) return;
     const int m = seg.perm[p];
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     if (p < seg.meta[1]) {
@@ -181,7 +224,13 @@ __global__ __launch_bounds__(256) void shrink_finalize_kernel(const float *__res
             }
         }
     }
-    *reinterpret_cast<float4 *>(t + (size_t)m * RM + j) = acc;
+    float *dst = t + (size_t)m * t_stride + j;
+    if ((t_stride & 3) == 0) {
+        *reinterpret_cast<float4 *>(dst) = acc;
+    } else {
+        const float a4[4] = {acc.x, acc.y, acc.z, acc.w};
+        for (int q = 0; q < 4 && j + q < t_stride; ++q) dst[q] = a4[q];
+    }
 }
 
 }  // namespace
@@ -192,20 +241,22 @@ void shrink_plan(int d_in, int r_max, int *kc, int *ksplit) {
 }
 
 hipError_t launch_shrink(const uint16_t *x, const uint16_t *A, const int32_t *ranks,
-                         const int32_t *roff, int pool_rows, int M, int d_in, int r_max,
-                         int n_adapters, Seg seg, float *partial, int kc, int ksplit,
+                         const int32_t *roff, int pool_rows, int pstride, int M, int d_in,
+                         int r_max, int n_adapters, Seg seg, float *partial, int kc, int ksplit,
                          hipStream_t s) {
+    if (roff == nullptr && (pstride < 1 || pstride > r_max)) return hipErrorInvalidValue;
     const long items = (long)lora_max_tiles(M, n_adapters) * ksplit;
     const long wblocks = (items + kWavesPerBlock - 1) / kWavesPerBlock;
     const dim3 wgrid((unsigned)(wblocks < kMaxGrid ? wblocks : kMaxGrid));
     const dim3 wblock(64 * kWavesPerBlock);
+    const bool varw = roff != nullptr || pstride != r_max;
 #define LORA_SHRINK_LAUNCH(RMV)                                                                  \
-    if (roff)                                                                                    \
+    if (varw)                                                                                    \
         launch(shrink_mfma_kernel<RMV, true>, wgrid, wblock, 0, s, x, A, ranks, roff, pool_rows, \
-               M, d_in, seg, partial, ksplit, kc);                                               \
+               pstride, M, d_in, seg, partial, ksplit, kc);                                      \
     else                                                                                         \
         launch(shrink_mfma_kernel<RMV, false>, wgrid, wblock, 0, s, x, A, ranks, roff, pool_rows,\
-               M, d_in, seg, partial, ksplit, kc);
+               pstride, M, d_in, seg, partial, ksplit, kc);
     switch (r_max) {
         case 8: LORA_SHRINK_LAUNCH(8) break;
         case 16: LORA_SHRINK_LAUNCH(16) break;
@@ -218,10 +269,12 @@ hipError_t launch_shrink(const uint16_t *x, const uint16_t *A, const int32_t *ra
 }
 
 hipError_t launch_shrink_finalize(const float *partial, int M, int r_max, int ksplit, Seg seg,
-                                  float *t, hipStream_t s) {
+                                  float *t, int t_stride, hipStream_t s) {
+    if (t_stride < 1 || t_stride > r_max) return hipErrorInvalidValue;
     const long threads = (long)M * (r_max / 4);
     const int grid = (int)((threads + 255) / 256);
-    launch(shrink_finalize_kernel, dim3(grid), dim3(256), 0, s, partial, M, r_max, ksplit, seg, t);
+    launch(shrink_finalize_kernel, dim3(grid), dim3(256), 0, s, partial, M, r_max, ksplit, seg, t,
+           t_stride);
     return hipGetLastError();
 }
 

@@ -23,17 +23,19 @@ LORA_PREFILL_MIN_ROWS = 1024
 
 LORA_BF16, LORA_F32 = 0, 1
 LORA_MODE_AUTO, LORA_MODE_DECODE, LORA_MODE_PREFILL = 0, 1, 2
+LORA_MODE_CHECKED = 0x100  # OR-ed into a mode: sync, check ids and adapter tables on the host
 
 STATUS = {
     0: "LORA_OK", 1: "LORA_ERR_NULL", 2: "LORA_ERR_SHAPE", 3: "LORA_ERR_RANK",
     4: "LORA_ERR_ALIGN", 5: "LORA_ERR_WORKSPACE", 6: "LORA_ERR_DTYPE", 7: "LORA_ERR_HIP",
-    8: "LORA_ERR_BAD_ID", 9: "LORA_ERR_MODE",
+    8: "LORA_ERR_BAD_ID", 9: "LORA_ERR_MODE", 10: "LORA_ERR_POOL",
 }
 
 # every symbol include/lora.h declares
 EXPORTS = ("lora_max_tiles", "lora_workspace_bytes", "lora_build_segments", "lora_shrink",
-           "lora_expand", "lora_linear", "lora_linear_profiled", "lora_linear_compact",
-           "lora_linear_compact_profiled", "lora_status_string", "lora_last_hip_error")
+           "lora_shrink_compact", "lora_expand", "lora_expand_compact", "lora_linear",
+           "lora_linear_profiled", "lora_linear_compact", "lora_linear_compact_profiled",
+           "lora_status_string", "lora_last_hip_error")
 
 
 class LoraError(RuntimeError):
@@ -72,8 +74,13 @@ def _load():
     lib.lora_build_segments.restype = ctypes.c_int
     lib.lora_shrink.argtypes = [P, P, P, I, I, I, I, lora_segments_t, P, P, S, P]
     lib.lora_shrink.restype = ctypes.c_int
+    lib.lora_shrink_compact.argtypes = [P, P, P, P, I, I, I, I, I, lora_segments_t, P, P, S, P]
+    lib.lora_shrink_compact.restype = ctypes.c_int
     lib.lora_expand.argtypes = [P, P, P, P, I, I, I, I, lora_segments_t, P, ctypes.c_int, P]
     lib.lora_expand.restype = ctypes.c_int
+    lib.lora_expand_compact.argtypes = [P, P, P, P, P, I, I, I, I, I, lora_segments_t, P,
+                                        ctypes.c_int, P]
+    lib.lora_expand_compact.restype = ctypes.c_int
     lib.lora_linear.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I,
                                 ctypes.POINTER(lora_segments_t), P, ctypes.c_int, ctypes.c_int,
                                 P, S, P]
@@ -162,6 +169,20 @@ def lora_shrink(x, A, ranks, M: int, d_in: int, r_max: int, n_adapters: int, seg
     _check(_lib.lora_shrink(_ptr(x), _ptr(A), _ptr(ranks), M, d_in, r_max, n_adapters,
                             _seg_struct(seg), _ptr(t), _ptr(ws), ws_bytes, _stream(stream)),
            "lora_shrink")
+
+
+def lora_shrink_compact(x, A, ranks, rank_offsets, pool_rows: int, M: int, d_in: int, r_max: int,
+                        n_adapters: int, seg, t, ws, ws_bytes: int, stream=None) -> None:
+    _check(_lib.lora_shrink_compact(_ptr(x), _ptr(A), _ptr(ranks), _ptr(rank_offsets), pool_rows,
+                                    M, d_in, r_max, n_adapters, _seg_struct(seg), _ptr(t),
+                                    _ptr(ws), ws_bytes, _stream(stream)), "lora_shrink_compact")
+
+
+def lora_expand_compact(t, B, scale, ranks, rank_offsets, pool_rows: int, M: int, d_out: int,
+                        r_max: int, n_adapters: int, seg, y, y_dtype: int, stream=None) -> None:
+    _check(_lib.lora_expand_compact(_ptr(t), _ptr(B), _ptr(scale), _ptr(ranks), _ptr(rank_offsets),
+                                    pool_rows, M, d_out, r_max, n_adapters, _seg_struct(seg),
+                                    _ptr(y), y_dtype, _stream(stream)), "lora_expand_compact")
 
 
 def lora_expand(t, B, scale, ranks, M: int, d_out: int, r_max: int, n_adapters: int, seg, y,

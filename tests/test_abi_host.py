@@ -46,7 +46,11 @@ def test_max_tiles():
 
 def test_workspace_bytes():
     assert L.lora_workspace_bytes(0, 4096, 4096, 16, 32) == 0
-    assert L.lora_workspace_bytes(64, 4096, 4096, 12, 32) == 0  # bad rank
+    assert L.lora_workspace_bytes(64, 4096, 4096, 65, 32) == 0  # bad rank
+    assert L.lora_workspace_bytes(64, 4096, 4096, 0, 32) == 0
+    # any r_max in [1, 64] is sized at its rank bucket
+    assert L.lora_workspace_bytes(64, 4096, 4096, 12, 32) == L.lora_workspace_bytes(64, 4096, 4096, 16, 32)
+    assert L.lora_workspace_bytes(64, 4096, 4096, 1, 32) == L.lora_workspace_bytes(64, 4096, 4096, 8, 32)
     assert L.lora_workspace_bytes(64, 4095, 4096, 16, 32) == 0  # d_in not a multiple of 8
     b = L.lora_workspace_bytes(64, 4096, 4096, 16, 32)
     assert b > 0 and b % 256 == 0
@@ -67,8 +71,8 @@ def _linear(**over):
 @pytest.mark.parametrize("over,code", [
     (dict(M=-1), 2), (dict(M=L.LORA_MAX_ROWS + 1), 2), (dict(d_in=12), 2), (dict(d_out=0), 2),
     (dict(n_adapters=0), 2), (dict(n_adapters=L.LORA_MAX_ADAPTERS + 1), 2),
-    (dict(r_max=12), 3), (dict(r_max=128), 3), (dict(r_max=0), 3),
-    (dict(y_dtype=5), 6), (dict(mode=7), 9),
+    (dict(r_max=65), 3), (dict(r_max=128), 3), (dict(r_max=0), 3), (dict(r_max=-8), 3),
+    (dict(y_dtype=5), 6), (dict(mode=7), 9), (dict(mode=0x103), 9), (dict(mode=0x200), 9),
     (dict(x=None), 1), (dict(W=None), 1), (dict(ids=None), 1), (dict(ws=None), 1),
     (dict(x=FAKE + 2), 4), (dict(y=FAKE + 8), 4), (dict(ws=FAKE + 16), 4),
     (dict(ws_bytes=1024), 5),
@@ -106,7 +110,7 @@ def test_shrink_expand_reject():
         L.lora_shrink(FAKE, FAKE, None, 64, 4096, 16, 32, seg, FAKE, FAKE, 16, stream=0)
     assert e.value.status == 5
     with pytest.raises(L.LoraError) as e:
-        L.lora_shrink(FAKE, FAKE, None, 64, 4096, 24, 32, seg, FAKE, FAKE, 1 << 30, stream=0)
+        L.lora_shrink(FAKE, FAKE, None, 64, 4096, 65, 32, seg, FAKE, FAKE, 1 << 30, stream=0)
     assert e.value.status == 3
     with pytest.raises(L.LoraError) as e:
         L.lora_expand(FAKE, FAKE, None, None, 64, 4096, 16, 32, seg, FAKE, 0, stream=0)
@@ -130,7 +134,7 @@ def _compact(**over):
     (dict(ranks=None), 1), (dict(rank_offsets=None), 1), (dict(rank_offsets=FAKE + 2), 4),
     (dict(pool_rows=0), 2), (dict(pool_rows=32 * 64 + 1), 2),
     # the checks lora_linear makes come first
-    (dict(r_max=12), 3), (dict(ws_bytes=1024), 5), (dict(x=None), 1),
+    (dict(r_max=0), 3), (dict(ws_bytes=1024), 5), (dict(x=None), 1),
 ])
 def test_linear_compact_rejects(over, code):
     with pytest.raises(L.LoraError) as e:
@@ -140,3 +144,33 @@ def test_linear_compact_rejects(over, code):
 
 def test_linear_compact_empty_batch_is_noop():
     _compact(M=0, x=None, y=None, ws=None)
+
+
+def test_shrink_expand_compact_reject():
+    seg = L.lora_segments_t(FAKE, FAKE, FAKE, FAKE, FAKE)
+    ws = 1 << 30
+    with pytest.raises(L.LoraError) as e:  # ranks and offsets are required
+        L.lora_shrink_compact(FAKE, FAKE, None, FAKE, 64, 64, 4096, 16, 32, seg, FAKE, FAKE, ws, stream=0)
+    assert e.value.status == 1
+    with pytest.raises(L.LoraError) as e:
+        L.lora_shrink_compact(FAKE, FAKE, FAKE, None, 64, 64, 4096, 16, 32, seg, FAKE, FAKE, ws, stream=0)
+    assert e.value.status == 1
+    with pytest.raises(L.LoraError) as e:  # pool larger than n * r_max
+        L.lora_shrink_compact(FAKE, FAKE, FAKE, FAKE, 32 * 16 + 1, 64, 4096, 16, 32, seg, FAKE, FAKE,
+                              ws, stream=0)
+    assert e.value.status == 2
+    with pytest.raises(L.LoraError) as e:
+        L.lora_expand_compact(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 64, 4096, 16, 32, seg, FAKE, 0, stream=0)
+    assert e.value.status == 2
+    with pytest.raises(L.LoraError) as e:
+        L.lora_expand_compact(FAKE, FAKE, FAKE, FAKE, FAKE + 2, 64, 64, 4096, 16, 32, seg, FAKE, 0,
+                              stream=0)
+    assert e.value.status == 4
+    # M = 0: no-op after the argument checks
+    L.lora_shrink_compact(None, None, FAKE, FAKE, 64, 0, 4096, 16, 32, seg, None, None, 0, stream=0)
+    L.lora_expand_compact(None, None, None, FAKE, FAKE, 64, 0, 4096, 16, 32, seg, None, 0, stream=0)
+
+
+def test_status_pool():
+    assert L.lora_status_string(10).startswith("LORA_ERR_POOL")
+    assert L.LORA_MODE_CHECKED == 0x100
