@@ -235,6 +235,24 @@ lora_status_t lora_linear_compact(const void *x, const void *W, const void *A, c
                                   void *y, lora_dtype_t y_dtype, lora_mode_t mode, void *ws,
                                   size_t ws_bytes, void *stream);
 
+/* For callers that cannot allocate (code under HIP graph capture, serving loops or
+ * harnesses that forbid hipMalloc): lora_linear without a caller workspace.  The call uses a
+ * scratch array of LORA_NOALLOC_SCRATCH_BYTES that the library keeps in device memory, one
+ * per GPU (held until the process ends; its device address is looked up once per device,
+ * at the first call on it), and calls no hipMalloc, hipFree or allocating routine.  Every
+ * call on one GPU shares that scratch: calls that overlap in time on one GPU (other streams,
+ * other host threads) race on it and must be serialised by the caller.  No part of the
+ * scratch needs clearing between calls.  Returns LORA_ERR_WORKSPACE when the call would need
+ * more than LORA_NOALLOC_SCRATCH_BYTES (lora_workspace_bytes() of its sizes: decode batches
+ * up to 256 rows at 4096 x 11008, and prefill batches of 4096 rows at 4096 x 4096, fit);
+ * otherwise the statuses and the result of lora_linear with the same arguments. */
+#define LORA_NOALLOC_SCRATCH_BYTES (32u << 20)
+lora_status_t lora_linear_noalloc(const void *x, const void *W, const void *A, const void *B,
+                                  const float *scale, const int32_t *ranks, const int32_t *ids,
+                                  int32_t M, int32_t d_in, int32_t d_out, int32_t r_max,
+                                  int32_t n_adapters, const lora_segments_t *segs, void *y,
+                                  lora_dtype_t y_dtype, lora_mode_t mode, void *stream);
+
 /* Measurement aid, not for serving loops (it times the per-kernel costs that [P1], "How does
  * one batch run 30 different adapters at once?", attributes to decode and prefill; the pages
  * define no such call): the same launches as lora_linear, each launched

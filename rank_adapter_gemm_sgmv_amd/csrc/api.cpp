@@ -418,13 +418,17 @@ hipError_t run_linear(const void *x, const void *W, const void *A, const void *B
 
 }  // namespace
 
-extern "C" {
+lora_status_t lora::hip_error_status(hipError_t e) { return hip_status(e); }
 
-lora_status_t lora_linear(const void *x, const void *W, const void *A, const void *B,
-                          const float *scale, const int32_t *ranks, const int32_t *ids, int32_t M,
-                          int32_t d_in, int32_t d_out, int32_t r_max, int32_t n_adapters,
-                          const lora_segments_t *segs, void *y, lora_dtype_t y_dtype,
-                          lora_mode_t mode, void *ws, size_t ws_bytes, void *stream) {
+// lora_linear's body on a given workspace: shared with the entry point that brings its own
+// device-resident scratch (csrc/noalloc.hip).
+lora_status_t lora::linear_on_workspace(const void *x, const void *W, const void *A,
+                                        const void *B, const float *scale, const int32_t *ranks,
+                                        const int32_t *ids, int32_t M, int32_t d_in,
+                                        int32_t d_out, int32_t r_max, int32_t n_adapters,
+                                        const lora_segments_t *segs, void *y,
+                                        lora_dtype_t y_dtype, lora_mode_t mode, void *ws,
+                                        size_t ws_bytes, void *stream) {
     lora_status_t st = check_linear(x, W, A, B, scale, ranks, ids, M, d_in, d_out, r_max, n_adapters,
                                     segs, y, y_dtype, mode, ws, ws_bytes);
     if (st != LORA_OK || M == 0) return st;
@@ -436,6 +440,17 @@ lora_status_t lora_linear(const void *x, const void *W, const void *A, const voi
                                  n_adapters, segs, y, y_dtype,
                                  (lora_mode_t)(mode & ~LORA_MODE_CHECKED), ws, (hipStream_t)stream,
                                  nullptr));
+}
+
+extern "C" {
+
+lora_status_t lora_linear(const void *x, const void *W, const void *A, const void *B,
+                          const float *scale, const int32_t *ranks, const int32_t *ids, int32_t M,
+                          int32_t d_in, int32_t d_out, int32_t r_max, int32_t n_adapters,
+                          const lora_segments_t *segs, void *y, lora_dtype_t y_dtype,
+                          lora_mode_t mode, void *ws, size_t ws_bytes, void *stream) {
+    return linear_on_workspace(x, W, A, B, scale, ranks, ids, M, d_in, d_out, r_max, n_adapters, segs,
+                               y, y_dtype, mode, ws, ws_bytes, stream);
 }
 
 lora_status_t lora_linear_compact(const void *x, const void *W, const void *A, const void *B,
@@ -554,7 +569,9 @@ const char *lora_status_string(lora_status_t status) {
         case LORA_ERR_SHAPE: return "LORA_ERR_SHAPE: M, d_in, d_out or n_adapters out of range";
         case LORA_ERR_RANK: return "LORA_ERR_RANK: r_max outside [1, 64], or (checked mode) a rank outside [1, r_max]";
         case LORA_ERR_ALIGN: return "LORA_ERR_ALIGN: a pointer is not aligned as required";
-        case LORA_ERR_WORKSPACE: return "LORA_ERR_WORKSPACE: workspace smaller than lora_workspace_bytes()";
+        case LORA_ERR_WORKSPACE:
+            return "LORA_ERR_WORKSPACE: workspace smaller than lora_workspace_bytes() (lora_linear_noalloc: "
+                   "the call needs more than LORA_NOALLOC_SCRATCH_BYTES of scratch)";
         case LORA_ERR_DTYPE: return "LORA_ERR_DTYPE: unknown output dtype";
         case LORA_ERR_HIP: return "LORA_ERR_HIP: a kernel launch failed";
         case LORA_ERR_BAD_ID: return "LORA_ERR_BAD_ID: adapter id out of range";

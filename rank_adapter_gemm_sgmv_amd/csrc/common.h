@@ -230,4 +230,15 @@ size_t gemm_partial_floats(int M, int K, int N);
 // Split-K plan of the shrink for d_in.
 void shrink_plan(int d_in, int r_max, int *kc, int *ksplit);
 
+// Records e as the error lora_last_hip_error() reports; LORA_ERR_HIP unless e is hipSuccess.
+lora_status_t hip_error_status(hipError_t e);
+
+// lora_linear on the workspace ws (validation, checked mode, launches).
+lora_status_t linear_on_workspace(const void *x, const void *W, const void *A, const void *B,
+                                  const float *scale, const int32_t *ranks, const int32_t *ids,
+                                  int32_t M, int32_t d_in, int32_t d_out, int32_t r_max,
+                                  int32_t n_adapters, const lora_segments_t *segs, void *y,
+                                  lora_dtype_t y_dtype, lora_mode_t mode, void *ws,
+                                  size_t ws_bytes, void *stream);
+
 }  // namespace lora

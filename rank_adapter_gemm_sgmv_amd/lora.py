@@ -20,6 +20,7 @@ LORA_TILE_ROWS = 16
 LORA_MAX_ADAPTERS = 16384
 LORA_MAX_ROWS = 1 << 22
 LORA_PREFILL_MIN_ROWS = 1024
+LORA_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 LORA_BF16, LORA_F32 = 0, 1
 LORA_MODE_AUTO, LORA_MODE_DECODE, LORA_MODE_PREFILL = 0, 1, 2
@@ -35,6 +36,7 @@ STATUS = {
 EXPORTS = ("lora_max_tiles", "lora_workspace_bytes", "lora_build_segments", "lora_shrink",
            "lora_shrink_compact", "lora_expand", "lora_expand_compact", "lora_linear",
            "lora_linear_profiled", "lora_linear_compact", "lora_linear_compact_profiled",
+           "lora_linear_noalloc",
            "lora_status_string", "lora_last_hip_error")
 
 
@@ -85,6 +87,8 @@ def _load():
                                 ctypes.POINTER(lora_segments_t), P, ctypes.c_int, ctypes.c_int,
                                 P, S, P]
     lib.lora_linear.restype = ctypes.c_int
+    lib.lora_linear_noalloc.argtypes = lib.lora_linear.argtypes[:16] + [P]
+    lib.lora_linear_noalloc.restype = ctypes.c_int
     lib.lora_linear_profiled.argtypes = lib.lora_linear.argtypes + [
         ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_char_p), I, ctypes.POINTER(I)]
     lib.lora_linear_profiled.restype = ctypes.c_int
@@ -199,6 +203,15 @@ def lora_linear(x, W, A, B, scale, ranks, ids, M: int, d_in: int, d_out: int, r_
     _check(_lib.lora_linear(_ptr(x), _ptr(W), _ptr(A), _ptr(B), _ptr(scale), _ptr(ranks),
                             _ptr(ids), M, d_in, d_out, r_max, n_adapters, seg_p, _ptr(y), y_dtype,
                             mode, _ptr(ws), ws_bytes, _stream(stream)), "lora_linear")
+
+
+def lora_linear_noalloc(x, W, A, B, scale, ranks, ids, M: int, d_in: int, d_out: int, r_max: int,
+                        n_adapters: int, segs, y, y_dtype: int, mode: int, stream=None) -> None:
+    """lora_linear on the library's own device scratch (no workspace argument)."""
+    seg_p = None if segs is None else ctypes.byref(_seg_struct(segs))
+    _check(_lib.lora_linear_noalloc(_ptr(x), _ptr(W), _ptr(A), _ptr(B), _ptr(scale), _ptr(ranks),
+                                    _ptr(ids), M, d_in, d_out, r_max, n_adapters, seg_p, _ptr(y),
+                                    y_dtype, mode, _stream(stream)), "lora_linear_noalloc")
 
 
 def lora_linear_profiled(x, W, A, B, scale, ranks, ids, M: int, d_in: int, d_out: int,

@@ -174,3 +174,18 @@ def test_shrink_expand_compact_reject():
 def test_status_pool():
     assert L.lora_status_string(10).startswith("LORA_ERR_POOL")
     assert L.LORA_MODE_CHECKED == 0x100
+
+
+def test_noalloc_rejects_before_touching_the_device():
+    """lora_linear_noalloc validates like lora_linear (no GPU needed for these), and rejects a
+    call whose workspace would exceed its scratch."""
+    args = dict(x=FAKE, W=FAKE, A=FAKE, B=FAKE, scale=FAKE, ranks=None, ids=FAKE, M=64, d_in=4096,
+                d_out=4096, r_max=16, n_adapters=32, segs=None, y=FAKE, y_dtype=L.LORA_BF16,
+                mode=L.LORA_MODE_DECODE, stream=0)
+    for over, code in ((dict(M=-1), 2), (dict(r_max=65), 3), (dict(d_in=12), 2),
+                       (dict(M=512, d_out=11008), 5)):
+        with pytest.raises(L.LoraError) as e:
+            L.lora_linear_noalloc(**{**args, **over})
+        assert e.value.status == code
+    assert L.lora_workspace_bytes(512, 4096, 11008, 16, 32) > L.LORA_NOALLOC_SCRATCH_BYTES
+    L.lora_linear_noalloc(**{**args, "M": 0, "x": None, "y": None})  # no-op
