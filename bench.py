@@ -8,13 +8,18 @@ bf16, W[4096, 4096], 32 resident adapters of rank 16, one adapter id per row (un
 unsorted), alpha = 32.  Inputs are synthetic (seeded generator) and resident in HBM before
 the timed region.  Each step uses the next of several device copies of (W, A, B) ("layers"),
 enough to exceed the 256 MB Infinity Cache, so the weights stream from HBM as they would in a
-forward pass over many layers.  The K timed steps are one HIP graph (captured once, checked
-against an eager call) replayed once between two synchronisations.
+forward pass over many layers.  Exactly K steps are captured as one HIP graph (checked
+against an eager call of its last step) and replayed once between two synchronisations:
+that replay gives `value` and `ms_per_step`.
 
-Prints one JSON line: tokens/s, ms per step, the roofline of the dominant kernel (HIP-event
-duration per launch, algorithmic bytes or flops per launch), the CPU oracle timed on the
-host as a baseline, a per-kernel breakdown, and the same measurements for the other decode
-and prefill workloads under "workloads".
+Also reported, outside that timed region: the spread of further replays of the same graph
+(p10 / p50 / p90 per step), single calls timed one by one with HIP events (cold: a 512 MiB
+write evicts L2 and the Infinity Cache before each call; warm: the same call repeated), the
+roofline of the dominant kernel (HIP-event duration per launch, algorithmic bytes or flops
+per launch), the CPU oracle timed on the host on every workload, a per-kernel breakdown,
+the other decode and prefill workloads under "workloads", and three sweeps: step time
+against the number of distinct adapters in a 64-row batch, against the adapters' rank, and
+decode against prefill sequence over the batch size (where LORA_MODE_AUTO switches).
 """
 
 from __future__ import annotations
@@ -211,27 +216,60 @@ def capture(runner, steps, torch):
     return g
 
 
-def check_graph_against_eager(runner, graph, torch):
-    """The graph's outputs equal an eager step on the same (last) layer, bit for bit."""
+def check_graph_against_eager(runner, graph, torch, steps):
+    """The graph's outputs equal an eager call of its last step, bit for bit."""
     graph.replay()
     torch.cuda.synchronize()
     from_graph = [y.clone() for y in runner.ys]
-    last = runner.L - 1  # graphs below always end on a whole number of rotations
-    runner.step(last)
+    runner.step(steps - 1)
     torch.cuda.synchronize()
     for a, b in zip(from_graph, runner.ys):
         if not torch.equal(a.view(torch.int16), b.view(torch.int16)):
             raise RuntimeError("graph replay differs from the eager call")
 
 
-def measure(runner, steps, warmup, torch, profile_reps=20):
-    """Timed graph replay of exactly `steps` steps, plus per-kernel averages."""
-    L = runner.L
-    steps_g = steps
-    g = capture(runner, steps_g, torch)
+FLUSH_BYTES = 512 << 20  # more than L2 (8 x 4 MB) and the 256 MB Infinity Cache together
+
+
+def pct(v, q):
+    return float(np.percentile(np.asarray(v, np.float64), q))
+
+
+def spread(v):
+    return {"p10": pct(v, 10), "p50": pct(v, 50), "p90": pct(v, 90), "n": len(v)}
+
+
+def per_call_times(runner, torch, reps):
+    """Single calls (one step each, layer 0), each between two HIP events on the stream:
+    cold (a FLUSH_BYTES write before each call, outside its events) and warm (the same call
+    back to back).  Returns µs spreads."""
+    g = capture(runner, 1, torch)
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    out = {}
+    for kind in ("cold", "warm"):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        g.replay()
+        torch.cuda.synchronize()
+        for e0, e1 in evs:
+            if kind == "cold":
+                flush.fill_(1)
+            e0.record()
+            g.replay()
+            e1.record()
+        torch.cuda.synchronize()
+        out[kind] = {k: (v * 1e3 if k != "n" else v)
+                     for k, v in spread([e0.elapsed_time(e1) for e0, e1 in evs]).items()}
+    del g, flush
+    return out
+
+
+def measure(runner, steps, warmup, torch, profile_reps=20, replays=9, call_reps=100):
+    """Timed graph replay of exactly `steps` steps, further replays for the spread, single
+    calls cold and warm, plus per-kernel averages."""
+    g = capture(runner, steps, torch)
     gw = capture(runner, max(1, warmup), torch) if warmup > 0 else None
-    if steps_g % L == 0:
-        check_graph_against_eager(runner, g, torch)
+    check_graph_against_eager(runner, g, torch, steps)
     if gw is not None:
         gw.replay()
     torch.cuda.synchronize()
@@ -244,6 +282,14 @@ def measure(runner, steps, warmup, torch, profile_reps=20):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_total = ev0.elapsed_time(ev1)
+    # the spread over further replays of the same graph (ms per step)
+    per_step = []
+    for _ in range(replays):
+        ev0.record()
+        g.replay()
+        ev1.record()
+        torch.cuda.synchronize()
+        per_step.append(ev0.elapsed_time(ev1) / steps)
     # eager steps, for reference (host launch cost included)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -252,6 +298,8 @@ def measure(runner, steps, warmup, torch, profile_reps=20):
         runner.step(i)
     torch.cuda.synchronize()
     eager_ms = (time.perf_counter() - t1) * 1e3 / n_eager
+    del g, gw
+    calls = per_call_times(runner, torch, call_reps) if call_reps > 0 else None
     # per-kernel durations
     sums, counts = {}, {}
     for i in range(profile_reps):
@@ -261,8 +309,7 @@ def measure(runner, steps, warmup, torch, profile_reps=20):
                 sums[key] = sums.get(key, 0.0) + ms
                 counts[key] = counts.get(key, 0) + 1
     kernels = {k: sums[k] / counts[k] for k in sums}
-    del g, gw
-    return ms_total, wall, eager_ms, kernels
+    return ms_total, wall, eager_ms, kernels, spread(per_step), calls
 
 
 # ---------------------------------------------------------------------------------------
@@ -270,13 +317,54 @@ def measure(runner, steps, warmup, torch, profile_reps=20):
 # ---------------------------------------------------------------------------------------
 
 
-def cpu_baseline(w, seconds: float):
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def host_threads() -> int:
+    """Cores this process may use: its CPU affinity, capped by OMP_NUM_THREADS when that is
+    set (the host's CPU share on a shared machine)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    return min(n, int(env)) if env.isdigit() and int(env) > 0 else n
+
+
+def oracle_call_s(w, threads: int, reps: int) -> float:
+    """Median wall time of `reps` oracle calls over every projection of w (inputs already
+    widened to fp32, outside the timing)."""
+    import oracle
+    from synth import bf16_bits_to_f32
+
+    ps = [tuple(bf16_bits_to_f32(v) for v in (p.x, p.W, p.A, p.B)) for p in w.projections]
+    ts = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        for xf, Wf, Af, Bf in ps:
+            oracle.lora_linear(xf, Wf, Af, Bf, w.alpha, w.ranks, w.ids, n_threads=threads)
+        ts.append(time.perf_counter() - t0)
+    return float(np.median(ts))
+
+
+def cpu_baseline(w, seconds: float, all_workloads=None):
+    """The oracle on the host: the headline workload for about `seconds` (the reported
+    value), then every workload once or three times on all allowed threads, and the small
+    ones on one thread."""
     import oracle
     from synth import bf16_bits_to_f32
 
     p = w.projections[0]
     xf, Wf, Af, Bf = (bf16_bits_to_f32(v) for v in (p.x, p.W, p.A, p.B))
-    threads = int(os.environ.get("OMP_NUM_THREADS") or min(16, os.cpu_count() or 1))
+    threads = host_threads()
     reps, t0 = 0, time.perf_counter()
     while True:
         oracle.lora_linear(xf, Wf, Af, Bf, w.alpha, w.ranks, w.ids, n_threads=threads)
@@ -284,9 +372,21 @@ def cpu_baseline(w, seconds: float):
         el = time.perf_counter() - t0
         if el >= seconds:
             break
-    return {"value": w.M * reps / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"the full {w.M}-row batch of {w.name}, {reps} oracle calls in {el:.1f} s "
-                      f"(plain C fp32 row loop, OpenMP over rows)"}
+    out = {"value": w.M * reps / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "sample": f"the full {w.M}-row batch of {w.name}, {reps} oracle calls in {el:.1f} s "
+                     f"(plain C fp32 row loop, OpenMP over rows)",
+           "cpu_model": cpu_model(), "host_cpu_count": os.cpu_count()}
+    per = {}
+    for name, wl in (all_workloads or {}).items():
+        small = wl.M * sum(q.d_in * q.d_out for q in wl.projections) <= 256 * 4096 * 4096
+        entry = {}
+        for th in ((threads, 1) if small else (threads,)):
+            sec = oracle_call_s(wl, th, 3 if small else 1)
+            entry[f"threads_{th}"] = {"s_per_call": sec, "tokens_per_s": wl.M / sec}
+        per[name] = entry
+    if per:
+        out["per_workload"] = per
+    return out
 
 
 # ---------------------------------------------------------------------------------------
@@ -300,7 +400,7 @@ def committed_traffic(workload: str, kernel: str):
     if not os.path.exists(path):
         return None
     text = open(path).read()
-    from rank_adapter_gemm_sgmv_amd.profsum import kernel_sources_digest
+    from profsum import kernel_sources_digest
 
     m = re.search(r"sources_digest:\s*([0-9a-f]+)", text)
     if not m or m.group(1) != kernel_sources_digest():
@@ -399,28 +499,101 @@ def base_only_ms(w, runner, steps, torch):
     return ms
 
 
-def run_workload(config, mode_name, steps, warmup, torch, profile_reps=20, need_runner=False,
-                 compact=False):
+_WORKLOADS = {}
+
+
+def workload(config):
     from synth import make_workload
 
-    w = make_workload(config).as_bf16()
+    if config not in _WORKLOADS:
+        _WORKLOADS[config] = make_workload(config).as_bf16()
+    return _WORKLOADS[config]
+
+
+def run_workload(config, mode_name, steps, warmup, torch, profile_reps=20, compact=False,
+                 call_reps=100):
+    w = workload(config)
     prefill = mode_name == "prefill"
     mode = L_.LORA_MODE_PREFILL if prefill else L_.LORA_MODE_DECODE
     rotate_x = prefill
     L = layers_needed(w, rotate_x, compact)
-    # the graph holds whole rotations so its last step can be checked against an eager one
-    steps = max(L, -(-steps // L) * L) if steps % L else steps
     runner = Runner(w, mode, torch, L, rotate_x=rotate_x, prebuilt_segments=len(w.projections) > 1,
                     compact=compact)
     log(f"bench: {w.name} mode={mode_name} layers={L} steps={steps} compact={compact}")
-    ms_total, wall, eager_ms, kernels = measure(runner, steps, warmup, torch, profile_reps)
+    ms_total, wall, eager_ms, kernels, reps, calls = measure(runner, steps, warmup, torch,
+                                                             profile_reps, call_reps=call_reps)
     s = summarize(w, runner, ms_total, steps, wall, eager_ms, kernels, prefill)
     s.update({"workload": w.name, "mode": mode_name, "layers_rotated": L, "steps": steps,
-              "pool": "rank-compact (lora_linear_compact)" if compact else "padded to r_max"})
+              "pool": "rank-compact (lora_linear_compact)" if compact else "padded to r_max",
+              "ms_per_step_replays": reps, "us_per_call": calls})
     base_ms = base_only_ms(w, runner, steps, torch)
     s["base_only_ms_per_step"] = base_ms
     s["lora_overhead_vs_base_only"] = s["ms_per_step"] / base_ms - 1.0
+    del runner
     return w, s, kernels, steps, ms_total
+
+
+# ---------------------------------------------------------------------------------------
+# sweeps
+# ---------------------------------------------------------------------------------------
+
+
+def step_ms(w, mode, torch, steps, rotate_x=False):
+    """ms per step of one graph of `steps` steps (weights rotated as in the workloads), and
+    the same with every id = -1."""
+    L = layers_needed(w, rotate_x)
+    runner = Runner(w, mode, torch, L, rotate_x=rotate_x)
+    g = capture(runner, steps, torch)
+    g.replay()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ts = []
+    for _ in range(3):
+        ev0.record()
+        g.replay()
+        ev1.record()
+        torch.cuda.synchronize()
+        ts.append(ev0.elapsed_time(ev1) / steps)
+    del g
+    base = base_only_ms(w, runner, steps, torch)
+    del runner
+    torch.cuda.empty_cache()
+    return float(np.median(ts)), base
+
+
+def sweeps(torch, steps=32):
+    """Decode q_proj geometry (x[64, 4096], W[4096, 4096]) with a varied adapter count and
+    rank, and decode vs prefill sequence over the batch size.  Inputs: synth.random_case."""
+    from synth import random_case
+
+    out = {"adapters": [], "rank": [], "auto_threshold": []}
+    M, d = 64, 4096
+    rng = np.random.default_rng(7)
+    for T in (1, 2, 4, 8, 16, 32, 64):  # distinct adapters among the 64 rows (pool of 128, r 16)
+        ids = rng.permutation(np.arange(M) % T).astype(np.int32)
+        w = random_case(500 + T, M, d, d, 128, 16, ranks=[16] * 128, ids=ids, base_frac=0.0)
+        ms, base = step_ms(w, L_.LORA_MODE_DECODE, torch, steps)
+        out["adapters"].append({"distinct_adapters": T, "ms_per_step": ms, "base_only_ms": base,
+                                "lora_overhead_vs_base_only": ms / base - 1.0})
+        log(f"sweep: adapters {T}: {ms * 1e3:.2f} us")
+    for r in (8, 16, 32, 64):  # 32 adapters of rank r, uniform ids
+        w = random_case(600 + r, M, d, d, 32, r, ranks=[r] * 32, base_frac=0.0)
+        ms, base = step_ms(w, L_.LORA_MODE_DECODE, torch, steps)
+        out["rank"].append({"rank": r, "distinct_adapters": int(len(np.unique(w.ids))),
+                            "ms_per_step": ms, "base_only_ms": base,
+                            "lora_overhead_vs_base_only": ms / base - 1.0})
+        log(f"sweep: rank {r}: {ms * 1e3:.2f} us")
+    for m in (256, 512, 768, 1024, 1536, 2048):  # 8 adapters of rank 16, runs of M/8 rows
+        ids = np.repeat(np.arange(8), m // 8).astype(np.int32)
+        w = random_case(700 + m, m, d, d, 8, 16, ranks=[16] * 8, ids=ids, base_frac=0.0)
+        dec, _ = step_ms(w, L_.LORA_MODE_DECODE, torch, 8, rotate_x=True)
+        pre, _ = step_ms(w, L_.LORA_MODE_PREFILL, torch, 8, rotate_x=True)
+        out["auto_threshold"].append({"M": m, "decode_ms": dec, "prefill_ms": pre})
+        log(f"sweep: M {m}: decode {dec * 1e3:.1f} us, prefill {pre * 1e3:.1f} us")
+    faster = [e["M"] for e in out["auto_threshold"] if e["prefill_ms"] < e["decode_ms"]]
+    out["prefill_faster_from_rows"] = min(faster) if faster else None
+    out["lora_prefill_min_rows"] = L_.LORA_PREFILL_MIN_ROWS
+    return out
 
 
 CALIB_BYTES = 256 << 20
@@ -457,8 +630,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=320)
     ap.add_argument("--warmup", type=int, default=32)
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--headline-only", action="store_true", help="skip the other workloads")
+    ap.add_argument("--cpu-seconds", type=float, default=5.0,
+                    help="seconds of oracle calls on the headline workload (0: no CPU baseline)")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="skip the other workloads, the sweeps and the per-workload CPU runs")
+    ap.add_argument("--no-sweeps", action="store_true", help="skip the sweeps")
     ap.add_argument("--workload", type=int, default=2, choices=(2, 3, 4, 5),
                     help="workload of the headline line (2 = decode q_proj, the default)")
     ap.add_argument("--mode", default="decode", choices=("decode", "prefill"))
@@ -507,7 +683,18 @@ def main():
                 workloads[f"config{cfg}:{mode_name}"] = {"error": repr(e)}
             torch.cuda.empty_cache()
 
-    cpu = cpu_baseline(w, args.cpu_seconds) if args.cpu_seconds > 0 else None
+    sw = None
+    if not args.headline_only and not args.no_sweeps:
+        try:
+            sw = sweeps(torch)
+        except Exception as e:  # report, do not hide the headline
+            sw = {"error": repr(e)}
+        torch.cuda.empty_cache()
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        others = None if args.headline_only else {workload(c).name: workload(c) for c in (1, 2, 3, 4, 5)}
+        cpu = cpu_baseline(w, args.cpu_seconds, others)
 
     line = {
         "metric": METRIC,
@@ -524,12 +711,16 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "M": w.M, "d_in": p0.d_in, "d_out": p0.d_out,
                    "n_adapters": w.n_adapters, "r_max": w.r_max, "mode": args.mode,
-                   "layers_rotated": head["layers_rotated"], "timed_as": "one HIP graph of all steps",
+                   "layers_rotated": head["layers_rotated"],
+                   "timed_as": "one HIP graph of exactly the K steps, replayed once",
                    "pool": head["pool"]},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "spread": {"ms_per_step_replays": head["ms_per_step_replays"],
+                   "us_per_call": head["us_per_call"]},
         "headline_detail": head,
         "workloads": workloads,
+        "sweeps": sw,
     }
     print(json.dumps(line), flush=True)
 

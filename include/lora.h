@@ -100,7 +100,7 @@ typedef enum { LORA_BF16 = 0, LORA_F32 = 1 } lora_dtype_t;
  * nothing when one fails.  For tests and debugging; not for graph capture. */
 typedef enum { LORA_MODE_AUTO = 0, LORA_MODE_DECODE = 1, LORA_MODE_PREFILL = 2 } lora_mode_t;
 #define LORA_MODE_CHECKED 0x100
-#define LORA_PREFILL_MIN_ROWS 1024
+#define LORA_PREFILL_MIN_ROWS 768 /* measured: decode and prefill sequences cost the same at 768 rows (4096 x 4096, r 16) */
 
 /* Rows grouped by adapter, as built by lora_build_segments.  All device buffers, owned by
  * the caller, sized for the M and n_adapters of the batch:
@@ -164,7 +164,8 @@ lora_status_t lora_shrink(const void *x, const void *A, const int32_t *ranks, in
 /* Shrink on a rank-compact pool (layout as for lora_linear_compact): the same t[M, r_max] as
  * lora_shrink on the adapters zero-padded to r_max ([P1], "Where does multi-LoRA serving
  * actually break?": padding wastes bandwidth when ranks differ).  ranks and rank_offsets
- * are required (LORA_ERR_NULL); pool_rows in [1, n_adapters * r_max] (LORA_ERR_SHAPE). */
+ * are required (LORA_ERR_NULL); pool_rows in [1, n_adapters * round_up(r_max, 8)]
+ * (LORA_ERR_SHAPE). */
 lora_status_t lora_shrink_compact(const void *x, const void *A, const int32_t *ranks,
                                   const int32_t *rank_offsets, int32_t pool_rows, int32_t M,
                                   int32_t d_in, int32_t r_max, int32_t n_adapters,
@@ -214,13 +215,15 @@ lora_status_t lora_linear(const void *x, const void *W, const void *A, const voi
  * what good systems support ([P2], "Limits and pitfalls"), S-LoRA by keeping adapters of
  * different ranks together in one pool ([P3], "How S-LoRA Proved the Model").  Layout (all
  * device memory, caller-owned):
- *   ranks[i]         rank r_i of adapter i, any value in [1, r_max]
- *   rank_offsets[i]  its first rank row: r_0 + ... + r_{i-1} for a packed pool (any
- *                    non-overlapping placement with rank_offsets[i] + r_i <= pool_rows works)
- *   A                bf16 [pool_rows * d_in]: A_i = [d_in][r_i] row-major at element
+ *   ranks[i]         rank r_i of adapter i, any value in [1, r_max]; the adapter occupies
+ *                    w_i = round_up(r_i, 8) rank rows (so every k row of A_i starts 16-byte
+ *                    aligned), rank rows r_i .. w_i - 1 zero
+ *   rank_offsets[i]  its first rank row: w_0 + ... + w_{i-1} for a packed pool (any
+ *                    non-overlapping placement with rank_offsets[i] + w_i <= pool_rows works)
+ *   A                bf16 [pool_rows * d_in]: A_i = [d_in][w_i] row-major at element
  *                    rank_offsets[i] * d_in
- *   B                bf16 [pool_rows][d_out]: B_i = rows rank_offsets[i] .. + r_i - 1
- *   pool_rows        rank rows in the pool, 1 <= pool_rows <= n_adapters * r_max
+ *   B                bf16 [pool_rows][d_out]: B_i = rows rank_offsets[i] .. + w_i - 1
+ *   pool_rows        rank rows in the pool, 1 <= pool_rows <= n_adapters * round_up(r_max, 8)
  * scale[i] = alpha_i / r_i as for lora_linear.  Tables that break this contract never make a
  * kernel read outside the pool: an adapter whose rows leave it adds nothing, and a rank above
  * r_max is clamped; LORA_MODE_CHECKED reports both (LORA_ERR_POOL, LORA_ERR_RANK).

@@ -1,10 +1,10 @@
 """Summaries of rocprofv3 output for the profiles/ folder.
 
-    python -m rank_adapter_gemm_sgmv_amd.profsum trace STATS_CSV --title T --command C
+    python profsum.py trace STATS_CSV --title T --command C
         kernel-trace statistics (``rocprofv3 --kernel-trace --stats --output-format csv``)
         as a markdown table.
 
-    python -m rank_adapter_gemm_sgmv_amd.profsum counters --fetch CSV --write CSV \
+    python profsum.py counters --fetch CSV --write CSV \
             --workload NAME --mode decode|prefill --calib-bytes N --fetch-command C --write-command C
         HBM traffic per launch of each kernel of the path, from two ``rocprofv3 --pmc`` runs
         of ``bench.py --pmc-pass`` (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch).  Both
@@ -14,7 +14,7 @@
         The output carries the digest of the kernel sources it was taken on; bench.py reports
         the traffic only while the sources still have that digest.
 
-    python -m rank_adapter_gemm_sgmv_amd.profsum mfma CSV --workload NAME --mode decode|prefill \
+    python profsum.py mfma CSV --workload NAME --mode decode|prefill \
             --command C [--xcds 8] [--simds 1024]
         MFMA use per kernel of the path from one ``rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES
         GRBM_GUI_ACTIVE SQ_INSTS_VALU_MFMA_MOPS_BF16`` run: MFMA busy cycles per SIMD, the
@@ -49,9 +49,9 @@ _CALIB = "neg_kernel"
 
 
 def kernel_sources_digest() -> str:
-    """sha256 (16 hex digits) over the names and bytes of csrc/*.hip, *.h, *.cpp."""
+    """sha256 (16 hex digits) over the names and bytes of the library's csrc/*.hip, *.h, *.cpp."""
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "csrc")
+    csrc = os.path.join(ROOT, "rank_adapter_gemm_sgmv_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
         if f.endswith((".hip", ".h", ".cpp")):
             with open(os.path.join(csrc, f), "rb") as fh:

@@ -129,7 +129,8 @@ lora_status_t check_compact(const int32_t *ranks, const int32_t *rank_offsets, i
                             int32_t r_max, int32_t n_adapters) {
     if (!ranks || !rank_offsets) return LORA_ERR_NULL;
     if (!aligned(rank_offsets, 4)) return LORA_ERR_ALIGN;
-    if (pool_rows < 1 || (int64_t)pool_rows > (int64_t)n_adapters * r_max) return LORA_ERR_SHAPE;
+    if (pool_rows < 1 || (int64_t)pool_rows > (int64_t)n_adapters * ((r_max + 7) & ~7))
+        return LORA_ERR_SHAPE;
     return LORA_OK;
 }
 
@@ -269,7 +270,8 @@ lora_status_t check_linear(const void *x, const void *W, const void *A, const vo
 
 // LORA_MODE_CHECKED: wait for the stream (the tables may be written by work queued on it),
 // copy ids, ranks and rank_offsets to host memory and check them: every id in [-1, n),
-// every rank in [1, r_max], and in a compact pool every adapter's rows inside the pool.
+// every rank in [1, r_max], and in a compact pool every adapter's round_up(rank, 8) rows
+// inside the pool.
 // Returns LORA_ERR_BAD_ID, LORA_ERR_RANK or LORA_ERR_POOL for the first violation found.
 lora_status_t check_tables(const int32_t *ids, int32_t M, const int32_t *ranks,
                            const int32_t *roff, int32_t pool_rows, int32_t r_max,
@@ -287,7 +289,8 @@ lora_status_t check_tables(const int32_t *ids, int32_t M, const int32_t *ranks,
     for (int32_t a = 0; a < (int32_t)h_ranks.size(); ++a)
         if (h_ranks[a] < 1 || h_ranks[a] > r_max) return LORA_ERR_RANK;
     for (int32_t a = 0; a < (int32_t)h_off.size(); ++a)
-        if (h_off[a] < 0 || (int64_t)h_off[a] + h_ranks[a] > pool_rows) return LORA_ERR_POOL;
+        if (h_off[a] < 0 || (int64_t)h_off[a] + ((h_ranks[a] + 7) & ~7) > pool_rows)
+            return LORA_ERR_POOL;
     return LORA_OK;
 }
 

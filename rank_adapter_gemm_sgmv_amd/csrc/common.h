@@ -55,18 +55,19 @@ __device__ __forceinline__ void st16(void *p, uint4 v) { *reinterpret_cast<uint4
 // ---- where an adapter's rank rows are ----------------------------------------------------
 // A padded pool (roff == nullptr) holds adapter a at rank rows a * stride .. a * stride +
 // stride - 1, stride being the caller's r_max (rows beyond the adapter's rank are zero):
-// A_a = A[a] is [d_in][stride], B_a = B[a] is [stride][d_out].  A rank-compact pool holds it
-// at rank rows roff[a] .. roff[a] + rank - 1 of its pool_rows rank rows: A_a is the
-// [d_in][rank] block at element roff[a] * d_in of A, B_a the [rank][d_out] block at row
-// roff[a] of B.  r is the adapter's rank, already clamped to [0, width]; in a compact pool an
-// adapter whose rows leave the pool gets r = 0 (it adds nothing; the checked mode of the
-// ABI reports such a table), so no access leaves the pool.  Returns the first rank row (0
-// when r becomes 0).
+// A_a = A[a] is [d_in][stride], B_a = B[a] is [stride][d_out].  A rank-compact pool holds an
+// adapter of rank r in w = round_up(r, 8) rank rows roff[a] .. roff[a] + w - 1 of its
+// pool_rows rank rows (rank rows r .. w - 1 zero): A_a is the [d_in][w] block at element
+// roff[a] * d_in of A, B_a the [w][d_out] block at row roff[a] of B; so every k row of A_a
+// starts 16-byte aligned.  r is the adapter's rank, already clamped to [0, width]; in a
+// compact pool an adapter whose rows leave the pool gets r = 0 (it adds nothing; the checked
+// mode of the ABI reports such a table), so no access leaves the pool.  Returns the first
+// rank row (0 when r becomes 0).
 __device__ __forceinline__ int adapter_row0(const int32_t *roff, int pool_rows, int a, int stride,
                                             int &r) {
     if (roff == nullptr) return a * stride;
     const int o = roff[a];
-    if (o < 0 || o > pool_rows - r) r = 0;
+    if (o < 0 || o > pool_rows - ((r + 7) & ~7)) r = 0;
     return r > 0 ? o : 0;
 }
 

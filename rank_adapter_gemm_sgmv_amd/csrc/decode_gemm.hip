@@ -368,7 +368,9 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(
 // (n_lt == 0).  Block (column chunk of 1024, row m), 256 threads x 4 columns.  The partial
 // and B loads are issued before t is summed, so their latency overlaps it.
 // MS: the most splits the launch can have (4 or 16; registers for the split partials).
-template <int BM, int RM, bool YF32, int MS>
+// PADRM: the pool is padded at stride RM (no roff, pstride == RM); the row addressing then
+// uses the compile-time stride (a runtime stride measured 2 us slower at 256 rows, r_max 64).
+template <int BM, int RM, bool YF32, int MS, bool PADRM>
 __global__ __launch_bounds__(256) void reduce_lora_kernel(const float *__restrict__ partial,
                                                           int M, int N, int n_tm, int n_tn,
                                                           int n_lt, int n_splits, DecodeLora lo,
@@ -396,9 +398,9 @@ __global__ __launch_bounds__(256) void reduce_lora_kernel(const float *__restric
         if (sp < n_splits) pv[sp] = *reinterpret_cast<const float4 *>(pp + sp * stride);
     // B_a[j, nc .. nc+3] for the adapter's rank rows, issued together (the rank is uniform
     // in the block, so rows at or beyond it are not added, and above r_max 16 not loaded)
-    const int width = lo.roff ? RM : lo.pstride;
+    const int width = PADRM || lo.roff ? RM : lo.pstride;
     int r = !has ? 0 : lo.ranks ? min(max(lo.ranks[a], 1), width) : width;
-    const int row0 = adapter_row0(lo.roff, lo.pool_rows, a, lo.pstride, r);
+    const int row0 = PADRM ? a * RM : adapter_row0(lo.roff, lo.pool_rows, a, lo.pstride, r);
     // the first BCH rank rows of B are loaded here; above r_max 16 the rest follow in chunks
     // of 16 rows after t is summed (all 64 at once would take 128 registers)
     constexpr int BCH = RM <= 16 ? RM : 16;
@@ -407,7 +409,7 @@ __global__ __launch_bounds__(256) void reduce_lora_kernel(const float *__restric
     // in a padded pool at r_max <= 16 every row is loaded (the padding rows exist), so the
     // loads need not wait for the rank; a compact pool's rows past the rank are the next
     // adapter's, and so are a padded pool's past its stride when that is below the bucket
-    if (RM <= 16 && lo.roff == nullptr && lo.pstride == RM) {
+    if (RM <= 16 && PADRM) {
 #pragma unroll
         for (int j = 0; j < BCH; ++j) bv[j] = *reinterpret_cast<const uint2 *>(bp + (size_t)j * N);
     } else {
@@ -595,13 +597,20 @@ hipError_t launch_decode_reduce(const float *partial, int M, int K, int N, void 
     const int n_lt = adapters ? adapter_tiles(M, lo.r_max, lo.n_adapters) : 0;
     const DecPlan p = dec_plan(M, K, N, n_lt);
     const dim3 rgrid((unsigned)((N + 1023) / 1024), (unsigned)M);
-#define RED_LAUNCH(BM, RMX, YF)                                                             \
-    if (p.ks <= 4)                                                                          \
-        launch((reduce_lora_kernel<BM, RMX, YF, 4>), rgrid, dim3(256), 0, s, partial, M, N,     \
-               p.n_tm, p.n_tn, p.n_lt, p.ks, lo, y);                                         \
+    const bool padrm = lo.roff == nullptr && lo.pstride == lo.r_max;
+#define RED_ONE(BM, RMX, YF, MSX)                                                           \
+    if (padrm)                                                                              \
+        launch((reduce_lora_kernel<BM, RMX, YF, MSX, true>), rgrid, dim3(256), 0, s, partial, M,\
+               N, p.n_tm, p.n_tn, p.n_lt, p.ks, lo, y);                                      \
     else                                                                                    \
-        launch((reduce_lora_kernel<BM, RMX, YF, 16>), rgrid, dim3(256), 0, s, partial, M, N,    \
-               p.n_tm, p.n_tn, p.n_lt, p.ks, lo, y)
+        launch((reduce_lora_kernel<BM, RMX, YF, MSX, false>), rgrid, dim3(256), 0, s, partial, \
+               M, N, p.n_tm, p.n_tn, p.n_lt, p.ks, lo, y)
+#define RED_LAUNCH(BM, RMX, YF)                                                             \
+    if (p.ks <= 4) {                                                                        \
+        RED_ONE(BM, RMX, YF, 4);                                                            \
+    } else {                                                                                \
+        RED_ONE(BM, RMX, YF, 16);                                                           \
+    }
 #define RED_RANK(BM, YF)                                                                    \
     switch (lo.r_max) {                                                                     \
         case 8: RED_LAUNCH(BM, 8, YF); break;                                               \
@@ -616,6 +625,7 @@ hipError_t launch_decode_reduce(const float *partial, int M, int K, int N, void 
     }
 #undef RED_RANK
 #undef RED_LAUNCH
+#undef RED_ONE
     return hipGetLastError();
 }
 

@@ -54,14 +54,17 @@ struct MfmaShrink {
 // hands each lane 4 consecutive k of one column.  Column groups at or beyond the adapter's
 // rank are written to LDS as zeros.  All global loads are issued unconditionally (clamped
 // addresses; out-of-range values are masked at use), so they are all in flight together.
-// VARW: the rows of A_a are not RM wide -- a rank-compact pool (roff names each adapter's
-// first rank row, rows are rank wide) or a padded pool whose stride is below the bucket
-// (pstride < RM).  Otherwise the pool is padded at stride RM (roff and pstride not read).
-// A width that is not a multiple of 8 cannot be read in 16-byte groups per k row; such a
-// chunk of A_a is read as one flat run of 16-byte vectors instead (it starts 16-byte aligned:
-// d_in and the chunk's first k are multiples of 8) and scattered element by element into
-// the zeroed LDS rows.
-template <int RM, bool VARW>
+// LAYOUT of the pool's rows of A_a:
+//   kPadRM   padded at stride RM (roff and pstride not read);
+//   kVarW    rows not RM wide but a multiple of 8: a rank-compact pool (roff names each
+//            adapter's first rank row; an adapter of rank r occupies round_up(r, 8) rows) or a
+//            padded pool whose stride pstride (< RM) is a multiple of 8;
+//   kFlat    a padded pool whose stride is not a multiple of 8: its k rows cannot be read in
+//            16-byte groups, so each chunk of A_a is read element by element (eight 2-byte
+//            loads in flight per lane) and scattered into the zeroed LDS rows.  A separate
+//            instantiation, so that the other layouts keep their registers and occupancy.
+enum { kPadRM = 0, kVarW = 1, kFlat = 2 };
+template <int RM, int LAYOUT>
 __global__ __launch_bounds__(64 * kWavesPerBlock) void shrink_mfma_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ A, const int32_t *__restrict__ ranks,
     const int32_t *__restrict__ roff, int pool_rows, int pstride, int M, int d_in, Seg seg,
@@ -82,13 +85,14 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void shrink_mfma_kernel(
         const int tile = w / n_chunks, c = w % n_chunks;
         const int p0 = seg.tiles[2 * tile], a = seg.tiles[2 * tile + 1];
         const int rows = min(p0 + kTileRows, seg.offsets[a + 1]) - p0;
-        // width of A_a's rows: RM, the padded stride, or (compact) the rank
+        constexpr bool VARW = LAYOUT != kPadRM;
+        // width of A_a's rows: RM, the padded stride, or (compact) the rank rounded up to 8
         const int width = !VARW ? RM : roff ? RM : pstride;
         int r = ranks ? min(max(ranks[a], 0), width) : width;
         const int row0 = adapter_row0(VARW ? roff : nullptr, pool_rows, a, VARW ? pstride : RM, r);
         // row stride of A_a: in a compact pool the groups at or beyond the rank are not
-        // loaded (they belong to the next adapter)
-        const int rs = !VARW ? RM : roff ? r : pstride;
+        // loaded (they are zero or belong to the next adapter)
+        const int rs = !VARW ? RM : roff ? (r + 7) & ~7 : pstride;
         const int k_lo = c * kc, k_hi = min(k_lo + kc, d_in);
         // this lane's x row (rows beyond the tile repeat its last row; their sums are dropped)
         const int mrow = seg.perm[p0 + min(li, rows - 1)];
@@ -100,11 +104,42 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void shrink_mfma_kernel(
         for (int b = 0; b < C::NB; ++b) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
         for (int kb = k_lo; kb < k_hi; kb += C::KS) {
+            // (kFlat) rows of a width that is not a multiple of 8: the chunk's run of rs-wide
+            // rows, element by element
+            constexpr bool flat = LAYOUT == kFlat;
+            if constexpr (flat) {
+                // zero the wave's rows (columns at or beyond rs, rows at or beyond k_hi stay
+                // zero), wait for those writes, then place element e of the run at k row
+                // e / rs, column e % rs (rows kb .. k_hi - 1 of A_a: all inside it)
+                for (int v = lane; v < C::KS * C::LROW / 16; v += 64)
+                    *reinterpret_cast<uint4 *>(wg + v * 16) = make_uint4(0, 0, 0, 0);
+                __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+                const int n_el = min(C::KS, k_hi - kb) * rs;
+                const int step_k = 64 / rs, step_j = 64 - step_k * rs;
+                const uint16_t *src = Aa + (size_t)kb * rs;
+#pragma unroll 1
+                for (int e0 = 0; e0 < n_el; e0 += 64 * 8) {
+                    uint16_t h[8];
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) {
+                        const int e = e0 + lane + 64 * q;
+                        h[q] = e < n_el ? src[e] : (uint16_t)0;
+                    }
+                    // element e0 + lane + 64 q sits at k row kr, column j: one division per
+                    // batch, then steps of 64 elements
+                    int kr = (e0 + lane) / rs, j = (e0 + lane) - kr * rs;
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) {
+                        if (e0 + lane + 64 * q < n_el)
+                            *reinterpret_cast<uint16_t *>(wg + kr * C::LROW + j * 2) = h[q];
+                        j += step_j;
+                        kr += step_k;
+                        if (j >= rs) { j -= rs; ++kr; }
+                    }
+                }
+            }
             // A_a[kb .. kb+KS, 0:RM]: unit f = lane + 64 i is (row f / GR, group f % GR)
             uint4 av[C::AL];
-            // (VARW) rows of a width that is not a multiple of 8: the flat run of the chunk
-            const bool flat = VARW && (rs & 7) != 0;
-            const int nvec = flat ? min(C::KS, k_hi - kb) * rs / 8 : 0;
             if constexpr (!VARW) {
                 // padded pool: every group is loaded (the padding is zeros), so the loads do
                 // not wait for the rank
@@ -120,14 +155,6 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void shrink_mfma_kernel(
                     av[i] = gr * 8 < r ? ld16(Aa + (size_t)min(kr, d_in - 1) * rs + gr * 8)
                                        : make_uint4(0, 0, 0, 0);
                 }
-            } else {
-                // nvec <= KS * rs / 8 <= KS * RM / 8 = 64 * AL vectors, all inside A_a
-                const uint16_t *src = Aa + (size_t)kb * rs;
-#pragma unroll
-                for (int i = 0; i < C::AL; ++i) {
-                    const int v = lane + 64 * i;
-                    av[i] = v < nvec ? ld16(src + (size_t)v * 8) : make_uint4(0, 0, 0, 0);
-                }
             }
             uint4 xv[C::STEPS];
 #pragma unroll
@@ -138,27 +165,6 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void shrink_mfma_kernel(
                     const int f = lane + 64 * i, kr = f / C::GR, gr = f % C::GR;
                     const bool ok = kb + kr < k_hi && gr * 8 < r;
                     *reinterpret_cast<uint4 *>(wg + kr * C::LROW + gr * 16) = ok ? av[i] : make_uint4(0, 0, 0, 0);
-                }
-            } else {
-                // zero the wave's rows (columns at or beyond rs, rows at or beyond k_hi stay
-                // zero), wait for those writes, then place element e of the run at k row
-                // e / rs, column e % rs
-                for (int v = lane; v < C::KS * C::LROW / 16; v += 64)
-                    *reinterpret_cast<uint4 *>(wg + v * 16) = make_uint4(0, 0, 0, 0);
-                __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-#pragma unroll
-                for (int i = 0; i < C::AL; ++i) {
-                    const int v = lane + 64 * i;
-                    if (v < nvec) {
-                        int kr = (8 * v) / rs, j = (8 * v) % rs;
-                        const uint32_t wv4[4] = {av[i].x, av[i].y, av[i].z, av[i].w};
-#pragma unroll
-                        for (int q = 0; q < 8; ++q) {
-                            const uint16_t e = (uint16_t)(q & 1 ? wv4[q >> 1] >> 16 : wv4[q >> 1] & 0xFFFFu);
-                            *reinterpret_cast<uint16_t *>(wg + kr * C::LROW + j * 2) = e;
-                            if (++j == rs) { j = 0; ++kr; }
-                        }
-                    }
                 }
             }
             __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
@@ -249,14 +255,17 @@ hipError_t launch_shrink(const uint16_t *x, const uint16_t *A, const int32_t *ra
     const long wblocks = (items + kWavesPerBlock - 1) / kWavesPerBlock;
     const dim3 wgrid((unsigned)(wblocks < kMaxGrid ? wblocks : kMaxGrid));
     const dim3 wblock(64 * kWavesPerBlock);
-    const bool varw = roff != nullptr || pstride != r_max;
+    const int layout = roff != nullptr       ? kVarW
+                       : pstride == r_max    ? kPadRM
+                       : (pstride & 7) != 0  ? kFlat
+                                             : kVarW;
+#define LORA_SHRINK_ONE(RMV, LAY)                                                                \
+    launch(shrink_mfma_kernel<RMV, LAY>, wgrid, wblock, 0, s, x, A, ranks, roff, pool_rows,      \
+           pstride, M, d_in, seg, partial, ksplit, kc)
 #define LORA_SHRINK_LAUNCH(RMV)                                                                  \
-    if (varw)                                                                                    \
-        launch(shrink_mfma_kernel<RMV, true>, wgrid, wblock, 0, s, x, A, ranks, roff, pool_rows, \
-               pstride, M, d_in, seg, partial, ksplit, kc);                                      \
-    else                                                                                         \
-        launch(shrink_mfma_kernel<RMV, false>, wgrid, wblock, 0, s, x, A, ranks, roff, pool_rows,\
-               pstride, M, d_in, seg, partial, ksplit, kc);
+    if (layout == kPadRM) LORA_SHRINK_ONE(RMV, kPadRM);                                          \
+    else if (layout == kVarW) LORA_SHRINK_ONE(RMV, kVarW);                                       \
+    else LORA_SHRINK_ONE(RMV, kFlat);
     switch (r_max) {
         case 8: LORA_SHRINK_LAUNCH(8) break;
         case 16: LORA_SHRINK_LAUNCH(16) break;
@@ -265,6 +274,7 @@ hipError_t launch_shrink(const uint16_t *x, const uint16_t *A, const int32_t *ra
         default: return hipErrorInvalidValue;
     }
 #undef LORA_SHRINK_LAUNCH
+#undef LORA_SHRINK_ONE
     return hipGetLastError();
 }
 

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(PKG, "liblora_mi355x.so")
 LORA_TILE_ROWS = 16
 LORA_MAX_ADAPTERS = 16384
 LORA_MAX_ROWS = 1 << 22
-LORA_PREFILL_MIN_ROWS = 1024
+LORA_PREFILL_MIN_ROWS = 768
 LORA_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 LORA_BF16, LORA_F32 = 0, 1

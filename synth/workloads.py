@@ -163,19 +163,24 @@ def _zero_padding(A: np.ndarray, B: np.ndarray, ranks: np.ndarray) -> None:
 
 def compact_pool(A: np.ndarray, B: np.ndarray, ranks: np.ndarray):
     """The same adapters stored at their own rank instead of padded to r_max: a storage
-    layout, no arithmetic.  Returns (A_c, B_c, offsets, pool_rows): A_c is flat with A_i =
-    A[i, :, :r_i] (a [d_in][r_i] block) at element offsets[i] * d_in, B_c is [pool_rows, d_out]
-    with B_i = B[i, :r_i, :] at rows offsets[i] .., offsets[i] = r_0 + ... + r_{i-1}."""
-    n, d_in, _ = A.shape
+    layout, no arithmetic.  Adapter i occupies w_i = round_up(r_i, 8) rank rows (its rows
+    r_i .. w_i - 1 zero).  Returns (A_c, B_c, offsets, pool_rows): A_c is flat with A_i =
+    A[i, :, :w_i] (a [d_in][w_i] block, columns past r_max zero) at element offsets[i] * d_in,
+    B_c is [pool_rows, d_out] with B_i = B[i, :w_i, :] at rows offsets[i] ..,
+    offsets[i] = w_0 + ... + w_{i-1}."""
+    n, d_in, r_max = A.shape
     d_out = B.shape[2]
     r = np.asarray(ranks, dtype=np.int64)
-    offsets = np.concatenate([[0], np.cumsum(r)[:-1]]).astype(np.int32)
-    pool_rows = int(r.sum())
+    w = (r + 7) // 8 * 8
+    offsets = np.concatenate([[0], np.cumsum(w)[:-1]]).astype(np.int32)
+    pool_rows = int(w.sum())
     A_c = np.zeros(pool_rows * d_in, dtype=A.dtype)
     B_c = np.zeros((pool_rows, d_out), dtype=B.dtype)
     for i in range(n):
-        o, ri = int(offsets[i]), int(r[i])
-        A_c[o * d_in:(o + ri) * d_in] = np.ascontiguousarray(A[i, :, :ri]).reshape(-1)
+        o, ri, wi = int(offsets[i]), int(r[i]), int(w[i])
+        blk = np.zeros((d_in, wi), dtype=A.dtype)
+        blk[:, :ri] = A[i, :, :ri]
+        A_c[o * d_in:(o + wi) * d_in] = blk.reshape(-1)
         B_c[o:o + ri] = B[i, :ri, :]
     return A_c, B_c, offsets, pool_rows
 

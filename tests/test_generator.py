@@ -106,5 +106,19 @@ def test_compact_pool_is_the_padded_pool_at_true_rank():
         assert np.array_equal(A_c[o * d_in:(o + r) * d_in].reshape(d_in, r), p.A[i, :, :r])
         assert np.array_equal(B_c[o:o + r], p.B[i, :r, :])
         assert not np.any(p.A[i, :, r:]) and not np.any(p.B[i, r:, :])  # nothing dropped
-    # every rank of this workload is a multiple of 8, as the compact entry point requires
-    assert np.all(w.ranks % 8 == 0)
+    # every rank of this workload is a multiple of 8: no adapter needs rows of zeros
+
+
+def test_compact_pool_rounds_each_adapter_up_to_8_rows():
+    """Ranks that are not multiples of 8 occupy round_up(r, 8) rank rows, the extra rows
+    zero, so that every k row of A_i starts 16-byte aligned."""
+    w = random_case(5, 8, 64, 40, 6, 24, ranks=[1, 8, 12, 17, 24, 3])
+    p = w.projections[0]
+    A_c, B_c, off, rows = compact_pool(p.A, p.B, w.ranks)
+    widths = [8, 8, 16, 24, 24, 8]
+    assert rows == sum(widths) and list(off) == list(np.cumsum([0] + widths[:-1]))
+    for i, (r, wd) in enumerate(zip(w.ranks, widths)):
+        o = int(off[i])
+        blk = A_c[o * 64:(o + wd) * 64].reshape(64, wd)
+        assert np.array_equal(blk[:, :r], p.A[i, :, :r]) and not np.any(blk[:, r:])
+        assert np.array_equal(B_c[o:o + r], p.B[i, :r, :]) and not np.any(B_c[o + r:o + wd])
