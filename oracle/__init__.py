@@ -8,8 +8,10 @@ from .oracle import (  # noqa: F401
     OracleError,
     build,
     build_segments,
+    fp8_e4m3_decode,
     library_path,
     lora_expand,
     lora_linear,
+    lora_linear_fp8w,
     lora_shrink,
 )

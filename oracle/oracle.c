@@ -37,6 +37,7 @@
  * stable counting sort of the rows by adapter id, base-only rows last.
  */
 
+#include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -250,5 +251,101 @@ int oracle_lora_linear(const float *x, const float *W, const float *A, const flo
         free(t);
         free(d);
     }
+    return status;
+}
+
+/* ---------------------------------------------------------------------------------------
+ * Quantized base ([P1], "Where does multi-LoRA serving actually break?", item 4: a base
+ * stored at low precision served beside higher-precision adapters; the delta runs in a
+ * different type than the base).  The base weight is held as 8-bit floating point codes of
+ * the E4M3 format of the OCP 8-bit floating point specification ("E4M3FN"): 1 sign bit, 4
+ * exponent bits with bias 7, 3 mantissa bits; exponent field 0 encodes the subnormals
+ * m * 2^-9; the code whose exponent and mantissa bits are all ones is NaN; there is no
+ * infinity.  The codes are laid out W8[d_out][d_in] (each output column's d_in codes
+ * contiguous), with one fp32 scale per output column.
+ * ------------------------------------------------------------------------------------- */
+float oracle_fp8_e4m3_decode(uint8_t code) {
+    const int sign = code >> 7, e = (code >> 3) & 15, m = code & 7;
+    if (e == 15 && m == 7) return NAN;
+    const float v = e == 0 ? ldexpf((float)m, -9) : ldexpf(1.0f + (float)m / 8.0f, e - 7);
+    return sign ? -v : v;
+}
+
+void oracle_fp8_e4m3_decode_array(const uint8_t *codes, int64_t n, float *out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_fp8_e4m3_decode(codes[i]);
+}
+
+/* The layer with the quantized base:
+ *
+ *   y[m][c] = w_scale[c] * sum_k x[m][k] dec(W8[c][k])              (shared base, k ascending)
+ *   if ids[m] = i >= 0:  y[m][c] += (alpha_i / r_i) * sum_j (sum_k x[m][k] A[i][k][j]) B[i][j][c]
+ *
+ * i.e. x W_eff with W_eff[k][c] = w_scale[c] dec(W8[c][k]), the scale applied to the fp32
+ * sum; the delta exactly as in oracle_lora_linear.  rows / n_rows as there. */
+int oracle_lora_linear_fp8w(const float *x, const uint8_t *W8, const float *w_scale,
+                            const float *A, const float *B, const float *alpha,
+                            const int32_t *ranks, const int32_t *ids, int32_t M, int32_t d_in,
+                            int32_t d_out, int32_t r_max, int32_t n_adapters, const int32_t *rows,
+                            int32_t n_rows, float *y, int32_t n_threads) {
+    if (M < 0 || d_in < 1 || d_out < 1 || r_max < 1 || n_adapters < 1) return ORACLE_ERR_ARG;
+    if (!ids_valid(ids, M, n_adapters)) return ORACLE_ERR_BAD_ID;
+    const int32_t count = rows ? n_rows : M;
+    if (count < 0) return ORACLE_ERR_ARG;
+    for (int32_t q = 0; rows && q < count; ++q)
+        if (rows[q] < 0 || rows[q] >= M) return ORACLE_ERR_ARG;
+    /* dec(W8) as an fp32 table Wd[k][c] (decoding is exact) */
+    float *Wd = (float *)malloc((size_t)d_in * d_out * sizeof(float));
+    if (!Wd) return ORACLE_ERR_NOMEM;
+    for (int32_t c = 0; c < d_out; ++c)
+        for (int32_t k = 0; k < d_in; ++k)
+            Wd[(size_t)k * d_out + c] = oracle_fp8_e4m3_decode(W8[(size_t)c * d_in + k]);
+    int status = ORACLE_OK;
+    (void)n_threads;
+#pragma omp parallel num_threads(n_threads > 0 ? n_threads : 1)
+    {
+        float *t = (float *)malloc((size_t)r_max * sizeof(float));
+        float *d = (float *)malloc((size_t)d_out * sizeof(float));
+        if (!t || !d) {
+#pragma omp atomic write
+            status = ORACLE_ERR_NOMEM;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int32_t q = 0; q < count; ++q) {
+            if (!t || !d) continue;
+            const int32_t m = rows ? rows[q] : q;
+            const float *xrow = x + (size_t)m * d_in;
+            float *yrow = y + (size_t)q * d_out;
+
+            /* shared base term: sum_k x dec(W8), then times the column's scale */
+            for (int32_t c = 0; c < d_out; ++c) yrow[c] = 0.0f;
+            for (int32_t k = 0; k < d_in; ++k) {
+                const float xv = xrow[k];
+                const float *wdrow = Wd + (size_t)k * d_out;
+                for (int32_t c = 0; c < d_out; ++c) yrow[c] += xv * wdrow[c];
+            }
+            for (int32_t c = 0; c < d_out; ++c) yrow[c] = w_scale[c] * yrow[c];
+
+            const int32_t i = ids[m];
+            if (i == -1) continue; /* base only */
+
+            for (int32_t j = 0; j < r_max; ++j) t[j] = 0.0f;
+            for (int32_t k = 0; k < d_in; ++k) {
+                const float xv = xrow[k];
+                const float *arow8 = A + ((size_t)i * d_in + k) * r_max;
+                for (int32_t j = 0; j < r_max; ++j) t[j] += xv * arow8[j];
+            }
+            for (int32_t c = 0; c < d_out; ++c) d[c] = 0.0f;
+            for (int32_t j = 0; j < r_max; ++j) {
+                const float tj = t[j];
+                const float *brow8 = B + ((size_t)i * r_max + j) * d_out;
+                for (int32_t c = 0; c < d_out; ++c) d[c] += tj * brow8[c];
+            }
+            const float sc = alpha[i] / (float)ranks[i];
+            for (int32_t c = 0; c < d_out; ++c) yrow[c] += sc * d[c];
+        }
+        free(t);
+        free(d);
+    }
+    free(Wd);
     return status;
 }

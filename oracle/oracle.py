@@ -66,6 +66,10 @@ def _bind(lib):
     lib.oracle_lora_shrink.argtypes = [P, P, P, I, I, I, I, P, I]
     lib.oracle_lora_expand.argtypes = [P, P, P, P, P, I, I, I, I, P, I]
     lib.oracle_lora_linear.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, P, I, P, I]
+    lib.oracle_lora_linear_fp8w.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, P, I, P, I]
+    lib.oracle_lora_linear_fp8w.restype = ctypes.c_int
+    lib.oracle_fp8_e4m3_decode_array.argtypes = [P, ctypes.c_int64, P]
+    lib.oracle_fp8_e4m3_decode_array.restype = None
     for f in (lib.oracle_build_segments, lib.oracle_lora_shrink, lib.oracle_lora_expand,
               lib.oracle_lora_linear):
         f.restype = ctypes.c_int
@@ -177,4 +181,41 @@ def lora_linear(x, W, A, B, alpha, ranks, ids, rows=None, n_threads: Optional[in
                                   _ptr(ids), M, d_in, d_out, r_max, n,
                                   None if rows_a is None else _ptr(rows_a), n_rows, _ptr(y),
                                   _threads(n_threads)), "lora_linear")
+    return y
+
+
+def fp8_e4m3_decode(codes, lib=None) -> np.ndarray:
+    """float32 values of OCP E4M3 fp8 codes (uint8), from the format definition."""
+    lib = lib or _load()
+    c = np.ascontiguousarray(np.asarray(codes, dtype=np.uint8))
+    out = np.empty(c.shape, np.float32)
+    lib.oracle_fp8_e4m3_decode_array(_ptr(c), int(c.size), _ptr(out))
+    return out
+
+
+def lora_linear_fp8w(x, W8, w_scale, A, B, alpha, ranks, ids, rows=None,
+                     n_threads: Optional[int] = None, lib=None) -> np.ndarray:
+    """y = x W_eff + (x A_i) B_i alpha_i / r_i per row, float32, with the base weight given as
+    fp8 codes W8[d_out, d_in] (uint8, OCP E4M3) and per-column scales w_scale[d_out]:
+    W_eff[k, c] = w_scale[c] * dec(W8[c, k]), the scale applied to the fp32 sum over k."""
+    lib = lib or _load()
+    x, A, B = _f32(x), _f32(A), _f32(B)
+    W8 = np.ascontiguousarray(np.asarray(W8, dtype=np.uint8))
+    w_scale = np.ascontiguousarray(w_scale, np.float32)
+    alpha, ranks, ids = np.ascontiguousarray(alpha, np.float32), _i32(ranks), _i32(ids)
+    M, d_in = x.shape
+    d_out, d_in2 = W8.shape
+    n, d_in3, r_max = A.shape
+    assert d_in2 == d_in and d_in3 == d_in and B.shape == (n, r_max, d_out)
+    assert w_scale.shape == (d_out,) and ids.shape == (M,)
+    if rows is None:
+        rows_a, n_rows, out_rows = None, 0, M
+    else:
+        rows_a = _i32(rows)
+        n_rows = out_rows = int(rows_a.shape[0])
+    y = np.empty((out_rows, d_out), np.float32)
+    _check(lib.oracle_lora_linear_fp8w(_ptr(x), _ptr(W8), _ptr(w_scale), _ptr(A), _ptr(B),
+                                       _ptr(alpha), _ptr(ranks), _ptr(ids), M, d_in, d_out, r_max,
+                                       n, None if rows_a is None else _ptr(rows_a), n_rows,
+                                       _ptr(y), _threads(n_threads)), "lora_linear_fp8w")
     return y

@@ -11,6 +11,7 @@ from .workloads import (  # noqa: F401
     bf16_bits_to_f32,
     compact_pool,
     f32_to_bf16_bits,
+    fp8_base,
     make_workload,
     pool_param_count,
     random_alpha,

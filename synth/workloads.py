@@ -185,6 +185,32 @@ def compact_pool(A: np.ndarray, B: np.ndarray, ranks: np.ndarray):
     return A_c, B_c, offsets, pool_rows
 
 
+def fp8_base(seed: int, d_in: int, d_out: int, uniform_codes: bool = False, std: float = 0.02):
+    """A base weight stored as fp8 E4M3 codes: W8[d_out, d_in] (uint8; each output column's
+    d_in codes contiguous) and per-column scales w_scale[d_out] (float32), drawn from a stream
+    of their own (PCG64 seeded with [seed, 8]).  No arithmetic of the layer: the codes are an
+    input.
+
+    default: values N(0, 1) * 64 clipped to +-448, converted to E4M3 by torch's float8_e4m3fn
+    cast, and scales std / 64 * U[0.75, 1.25), so the effective weight w_scale * dec(W8) has
+    about the spread of the bf16 workloads' N(0, std) weights.
+    uniform_codes: every code other than the two NaN codes, uniformly (subnormals, zeros and
+    the largest values included).
+    """
+    import torch
+
+    rng = np.random.Generator(np.random.PCG64([int(seed), 8]))
+    if uniform_codes:
+        valid = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+        W8 = valid[rng.integers(0, len(valid), size=(d_out, d_in))]
+    else:
+        v = np.clip(rng.standard_normal((d_out, d_in), dtype=np.float32) * np.float32(64.0),
+                    -448.0, 448.0)
+        W8 = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    w_scale = (np.float32(std / 64.0) * rng.uniform(0.75, 1.25, size=d_out)).astype(np.float32)
+    return np.ascontiguousarray(W8, dtype=np.uint8), w_scale
+
+
 def pool_param_count(n_adapters: int, d_in: int, d_out: int, rank: int) -> int:
     """Element count of a stacked pool A[n, d_in, rank] + B[n, rank, d_out]."""
     return int(n_adapters) * int(rank) * (int(d_in) + int(d_out))

@@ -27,6 +27,13 @@ What pins what:
     both alpha and r changes nothing.
   * rows are independent: permuting rows permutes the output bit-exactly.
   * segments: equal to Python's stable sorted() plus numpy bincount / cumsum.
+  * quantized base ([P1] "Where does multi-LoRA serving actually break?", item 4): the fp8
+    E4M3 decode equals torch's float8_e4m3fn conversion on every non-NaN code and gives the
+    values the OCP 8-bit floating point specification fixes for E4M3 (largest normal 448,
+    smallest normal 2^-6, smallest subnormal 2^-9, NaN at S.1111.111, -0 at 0x80); with unit
+    scales the fp8 layer equals the bf16 layer on the same (exactly representable) weights,
+    bit for bit; a power-of-two column scale scales the base term exactly; and the fp8 layer
+    agrees with numpy float64 on the dequantized weight within the float32 bound.
 """
 
 from __future__ import annotations
@@ -64,6 +71,12 @@ class Orc:
 
     def segments(self, *a, **k):
         return self.mod.build_segments(*a, lib=self.lib, **k)
+
+    def linear_fp8w(self, *a, **k):
+        return self.mod.lora_linear_fp8w(*a, lib=self.lib, **k)
+
+    def fp8_decode(self, *a, **k):
+        return self.mod.fp8_e4m3_decode(*a, lib=self.lib, **k)
 
 
 def _int_case(seed, M, d_in, d_out, n, r_max, scale_int=2, base_frac=0.25):
@@ -289,6 +302,82 @@ def pin_segments(orc: Orc) -> None:
                 assert np.array_equal(got[key], ref[key]), (key, ids, tile_rows)
 
 
+# ---------------------------------------------------------------------------------------
+# quantized (fp8 E4M3) base
+
+
+def _fp8_case(seed, M, d_in, d_out, n, r_max, scale=None):
+    """A random case plus fp8 codes W8[d_out, d_in] (every non-NaN code drawn uniformly) and
+    column scales; W8 is an input, drawn, not computed from a float weight."""
+    from synth import fp8_base
+
+    w = random_case(seed, M, d_in, d_out, n, r_max, storage="f32", base_frac=0.25)
+    W8, w_scale = fp8_base(seed, d_in, d_out, uniform_codes=True)
+    if scale is not None:
+        w_scale = np.full(d_out, scale, np.float32)
+    return w, W8, w_scale
+
+
+def pin_fp8_decode(orc: Orc) -> None:
+    import torch
+
+    codes = np.arange(256, dtype=np.uint8)
+    got = orc.fp8_decode(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy()
+    nan = np.isnan(ref)
+    assert list(np.flatnonzero(nan)) == [0x7F, 0xFF] and np.all(np.isnan(got[nan]))
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+    # values the format fixes
+    fixed = {0x7E: 448.0, 0xFE: -448.0, 0x08: 2.0 ** -6, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9,
+             0x38: 1.0, 0x39: 1.125, 0x40: 2.0, 0xC0: -2.0, 0x00: 0.0}
+    for c, v in fixed.items():
+        assert got[c] == v, (hex(c), got[c], v)
+    assert got[0x80] == 0.0 and np.signbit(got[0x80])
+    # strictly increasing over the positive codes
+    assert np.all(np.diff(got[0x00:0x7F].astype(np.float64)) > 0)
+
+
+def pin_fp8_equals_bf16_layer(orc: Orc) -> None:
+    """Unit scales: the fp8 layer is the bf16/fp32 layer on W[k, c] = dec(W8[c, k])."""
+    for seed, (M, d_in, d_out, n, r_max) in enumerate([(9, 40, 24, 3, 8), (5, 16, 72, 2, 4)]):
+        w, W8, w_scale = _fp8_case(900 + seed, M, d_in, d_out, n, r_max, scale=1.0)
+        p = w.projections[0]
+        W = np.ascontiguousarray(orc.fp8_decode(W8).T)
+        y8 = orc.linear_fp8w(p.x, W8, w_scale, p.A, p.B, w.alpha, w.ranks, w.ids)
+        y = orc.linear(p.x, W, p.A, p.B, w.alpha, w.ranks, w.ids)
+        assert np.array_equal(y8, y)
+
+
+def pin_fp8_scale(orc: Orc) -> None:
+    """A power-of-two scale on column c multiplies the base term of column c exactly."""
+    w, W8, _ = _fp8_case(910, 7, 32, 20, 2, 8, scale=1.0)
+    p = w.projections[0]
+    base = np.full(w.M, -1, np.int32)
+    y1 = orc.linear_fp8w(p.x, W8, np.ones(20, np.float32), p.A, p.B, w.alpha, w.ranks, base)
+    sc = (2.0 ** np.arange(-4, 16)).astype(np.float32)
+    y2 = orc.linear_fp8w(p.x, W8, sc, p.A, p.B, w.alpha, w.ranks, base)
+    assert np.array_equal(y2, y1 * sc[None, :])
+
+
+def pin_fp8_float64(orc: Orc) -> None:
+    """The fp8 layer vs numpy float64 on the dequantized weight, within the float32 bound."""
+    w, W8, w_scale = _fp8_case(920, 11, 64, 48, 4, 16)
+    p = w.projections[0]
+    Wd = (orc.fp8_decode(W8).astype(np.float64) * w_scale[:, None].astype(np.float64)).T
+    y = orc.linear_fp8w(p.x, W8, w_scale, p.A, p.B, w.alpha, w.ranks, w.ids)
+    x, A, B = (np.asarray(v, np.float64) for v in (p.x, p.A, p.B))
+    s = w.alpha.astype(np.float64) / w.ranks
+    ref = x @ Wd
+    for m in range(w.M):
+        i = int(w.ids[m])
+        if i >= 0:
+            ref[m] += s[i] * ((x[m] @ A[i]) @ B[i])
+    bound = _abs_bound(p.x, Wd, p.A, p.B, s, w.ids, 5)
+    assert np.all(np.abs(y - ref) <= bound)
+
+
 ALL_PINS = [pin_exact_merged_rational, pin_integer_exact, pin_merged_float64,
             pin_single_adapter_float64, pin_base_rows, pin_zero_padding, pin_scale,
-            pin_row_permutation, pin_segments]
+            pin_row_permutation, pin_segments, pin_fp8_decode, pin_fp8_equals_bf16_layer,
+            pin_fp8_scale, pin_fp8_float64]

@@ -54,6 +54,24 @@ MUTANTS = [
     ("segments_unstable",
      "for (int32_t m = 0; m < M; ++m) {\n        if (ids[m] >= 0) perm[cursor[ids[m]]++] = m;",
      "for (int32_t m = M - 1; m >= 0; --m) {\n        if (ids[m] >= 0) perm[cursor[ids[m]]++] = m;"),
+    ("fp8_bias_8",
+     "ldexpf(1.0f + (float)m / 8.0f, e - 7)",
+     "ldexpf(1.0f + (float)m / 8.0f, e - 8)"),
+    ("fp8_subnormal_as_normal",
+     "e == 0 ? ldexpf((float)m, -9)",
+     "e == 0 ? ldexpf(1.0f + (float)m / 8.0f, -7)"),
+    ("fp8_sign_dropped",
+     "return sign ? -v : v;",
+     "return v;"),
+    ("fp8_scale_dropped",
+     "for (int32_t c = 0; c < d_out; ++c) yrow[c] = w_scale[c] * yrow[c];",
+     "for (int32_t c = 0; c < d_out; ++c) yrow[c] = yrow[c];"),
+    ("fp8_W8_transposed_read",
+     "Wd[(size_t)k * d_out + c] = oracle_fp8_e4m3_decode(W8[(size_t)c * d_in + k]);",
+     "Wd[(size_t)k * d_out + c] = oracle_fp8_e4m3_decode(W8[(size_t)k * d_out + c]);"),
+    ("fp8_delta_dropped",
+     "for (int32_t c = 0; c < d_out; ++c) yrow[c] += sc * d[c];",
+     "for (int32_t c = 0; c < d_out; ++c) yrow[c] += 0.0f * d[c];"),
     ("base_rows_first",
      "int32_t base_pos = n_lora_rows;",
      "int32_t base_pos = n_lora_rows; for (int32_t i = 0; i < n_adapters; ++i) { offsets[i] += M - n_lora_rows; cursor[i] += M - n_lora_rows; } base_pos = 0;"),
