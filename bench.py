@@ -98,6 +98,9 @@ def algorithmic_work(w, d_in: int, d_out: int, prefill: bool, y_bytes: int = 2) 
                                    "flops": base_flops + 2.0 * r_rows * d_in}
         # medium decode batches: the same GEMM without the shrink (W, x)
         out["decode_gemm"] = {"bytes": gemm_bytes, "flops": base_flops}
+        # fp8 base: W8 (one byte per weight) + per-column scales + x
+        out["decode_gemm_fp8"] = {"bytes": d_in * d_out + 4 * d_out + M * d_in * 2,
+                                  "flops": base_flops}
         out["decode_reduce_lora"] = {"bytes": b_bytes + t_bytes + M * d_out * y_bytes,
                                      "flops": 2.0 * r_rows * d_out}
     return out
@@ -113,12 +116,20 @@ def _bf16(bits, torch):
 
 
 class DeviceLayers:
-    """Device copies ("layers") of one projection's weights, cycled step by step."""
+    """Device copies ("layers") of one projection's weights, cycled step by step.  With fp8,
+    the base weight of every layer is fp8 E4M3 codes W8[d_out, d_in] plus column scales."""
 
-    def __init__(self, w, pi, n_layers, rotate_x, torch, compact=False):
+    def __init__(self, w, pi, n_layers, rotate_x, torch, compact=False, fp8=False):
         p = w.projections[pi]
         self.d_in, self.d_out = p.d_in, p.d_out
         self.layers = []
+        self.w_scale = None
+        W_h = p.W
+        if fp8:
+            from synth import fp8_base
+
+            W_h, ws_h = fp8_base(w.seed, p.d_in, p.d_out)
+            self.w_scale = torch.from_numpy(ws_h).cuda()
         A_h, B_h = p.A, p.B
         self.off, self.pool_rows = None, 0
         if compact:  # the same adapters stored at their own rank (lora_linear_compact)
@@ -128,18 +139,18 @@ class DeviceLayers:
             self.off = torch.from_numpy(off).cuda()
         x0 = _bf16(p.x, torch)
         for i in range(n_layers):
-            W = _bf16(p.W, torch)
+            W = torch.from_numpy(W_h).cuda() if fp8 else _bf16(W_h, torch)
             A = _bf16(A_h, torch)
             B = _bf16(B_h, torch)
             x = _bf16(p.x, torch) if (rotate_x and i > 0) else x0
             self.layers.append((x, W, A, B))
 
 
-def layers_needed(w, rotate_x: bool, compact: bool = False) -> int:
+def layers_needed(w, rotate_x: bool, compact: bool = False, fp8: bool = False) -> int:
     per = 0
     for p in w.projections:
         pool = (int(w.ranks.sum()) * (p.d_in + p.d_out) * 2) if compact else p.A.nbytes + p.B.nbytes
-        per += p.W.nbytes + pool + (p.x.nbytes if rotate_x else 0)
+        per += (p.W.nbytes // 2 if fp8 else p.W.nbytes) + pool + (p.x.nbytes if rotate_x else 0)
     return max(1, -(-ROTATE_BYTES // per))
 
 
@@ -147,14 +158,15 @@ class Runner:
     """One workload on the device: L layers, shared ids / ranks / scale, one output per
     projection, workspace; `step(i)` enqueues one step (all projections) for layer i % L."""
 
-    def __init__(self, w, mode, torch, L, rotate_x=False, prebuilt_segments=False, compact=False):
+    def __init__(self, w, mode, torch, L, rotate_x=False, prebuilt_segments=False, compact=False,
+                 fp8=False):
         self.torch, self.w, self.mode, self.L = torch, w, mode, L
-        self.compact = compact
+        self.compact, self.fp8 = compact, fp8
         self.M, self.n, self.r_max = w.M, w.n_adapters, w.r_max
         self.ids = torch.from_numpy(w.ids.astype(np.int32)).cuda()
         self.ranks = torch.from_numpy(w.ranks.astype(np.int32)).cuda()
         self.scale = torch.from_numpy((w.alpha / w.ranks.astype(np.float32)).astype(np.float32)).cuda()
-        self.projs = [DeviceLayers(w, pi, L, rotate_x, torch, compact)
+        self.projs = [DeviceLayers(w, pi, L, rotate_x, torch, compact, fp8)
                       for pi in range(len(w.projections))]
         self.ys = [torch.empty((w.M, pr.d_out), dtype=torch.bfloat16, device="cuda") for pr in self.projs]
         nb = max(L_.lora_workspace_bytes(w.M, pr.d_in, pr.d_out, w.r_max, w.n_adapters) for pr in self.projs)
@@ -168,6 +180,11 @@ class Runner:
             L_.lora_build_segments(self.ids, self.M, self.n, self.segs)
         for pr, y in zip(self.projs, self.ys):
             x, W, A, B = pr.layers[li]
+            if self.fp8:
+                L_.lora_linear_fp8w(x, W, pr.w_scale, A, B, self.scale, self.ranks, self.ids, self.M,
+                                    pr.d_in, pr.d_out, self.r_max, self.n, self.segs, y,
+                                    L_.LORA_BF16, self.mode, self.ws, self.ws_bytes)
+                continue
             if self.compact:
                 L_.lora_linear_compact(x, W, A, B, self.scale, self.ranks, pr.off, pr.pool_rows,
                                        self.ids, self.M, pr.d_in, pr.d_out, self.r_max, self.n,
@@ -188,7 +205,12 @@ class Runner:
             L_.lora_build_segments(self.ids, self.M, self.n, self.segs)
         for pr, y in zip(self.projs, self.ys):
             x, W, A, B = pr.layers[li]
-            if self.compact:
+            if self.fp8:
+                ks = L_.lora_linear_fp8w_profiled(
+                    x, W, pr.w_scale, A, B, self.scale, self.ranks, self.ids, self.M, pr.d_in,
+                    pr.d_out, self.r_max, self.n, self.segs, y, L_.LORA_BF16, self.mode, self.ws,
+                    self.ws_bytes)
+            elif self.compact:
                 ks = L_.lora_linear_compact_profiled(
                     x, W, A, B, self.scale, self.ranks, pr.off, pr.pool_rows, self.ids, self.M,
                     pr.d_in, pr.d_out, self.r_max, self.n, self.segs, y, L_.LORA_BF16, self.mode,
@@ -442,6 +464,7 @@ def summarize(w, runner, ms_total, steps, wall, eager_ms, kernels, prefill):
                  "kernels_us": {k: round(v * 1e3, 2) for k, v in ks.items()}}
         gname = "gemm_prefill_lora" if prefill else (
             "decode_gemm_lora" if "decode_gemm_lora" in ks else
+            "decode_gemm_fp8" if "decode_gemm_fp8" in ks else
             "decode_gemm" if "decode_gemm" in ks else "gemm_decode")
         if gname in ks:
             g_ms = ks[gname]
@@ -511,20 +534,21 @@ def workload(config):
 
 
 def run_workload(config, mode_name, steps, warmup, torch, profile_reps=20, compact=False,
-                 call_reps=100):
+                 call_reps=100, fp8=False):
     w = workload(config)
     prefill = mode_name == "prefill"
     mode = L_.LORA_MODE_PREFILL if prefill else L_.LORA_MODE_DECODE
     rotate_x = prefill
-    L = layers_needed(w, rotate_x, compact)
+    L = layers_needed(w, rotate_x, compact, fp8)
     runner = Runner(w, mode, torch, L, rotate_x=rotate_x, prebuilt_segments=len(w.projections) > 1,
-                    compact=compact)
-    log(f"bench: {w.name} mode={mode_name} layers={L} steps={steps} compact={compact}")
+                    compact=compact, fp8=fp8)
+    log(f"bench: {w.name} mode={mode_name} layers={L} steps={steps} compact={compact} fp8={fp8}")
     ms_total, wall, eager_ms, kernels, reps, calls = measure(runner, steps, warmup, torch,
                                                              profile_reps, call_reps=call_reps)
     s = summarize(w, runner, ms_total, steps, wall, eager_ms, kernels, prefill)
     s.update({"workload": w.name, "mode": mode_name, "layers_rotated": L, "steps": steps,
               "pool": "rank-compact (lora_linear_compact)" if compact else "padded to r_max",
+              "base": "fp8 E4M3 W8[d_out, d_in] + column scales (lora_linear_fp8w)" if fp8 else "bf16 W",
               "ms_per_step_replays": reps, "us_per_call": calls})
     base_ms = base_only_ms(w, runner, steps, torch)
     s["base_only_ms_per_step"] = base_ms
@@ -672,13 +696,14 @@ def main():
 
     workloads = {}
     if not args.headline_only:
-        for cfg, mode_name, st, comp in ((3, "decode", 128, False), (3, "decode", 128, True),
-                                         (4, "prefill", 40, False), (5, "decode", 64, False),
-                                         (4, "decode", 20, False), (2, "prefill", 64, False)):
+        for cfg, mode_name, st, var in ((3, "decode", 128, ""), (3, "decode", 128, "compact"),
+                                        (4, "prefill", 40, ""), (5, "decode", 64, ""),
+                                        (4, "decode", 20, ""), (2, "prefill", 64, ""),
+                                        (2, "decode", 128, "fp8base")):
             try:
                 _, s, _, _, _ = run_workload(cfg, mode_name, st, 4, torch, profile_reps=8,
-                                             compact=comp)
-                workloads[f"{s['workload']}:{mode_name}{'-compact' if comp else ''}"] = s
+                                             compact=var == "compact", fp8=var == "fp8base")
+                workloads[f"{s['workload']}:{mode_name}{'-' + var if var else ''}"] = s
             except Exception as e:  # report, do not hide the headline
                 workloads[f"config{cfg}:{mode_name}"] = {"error": repr(e)}
             torch.cuda.empty_cache()

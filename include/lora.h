@@ -238,6 +238,37 @@ lora_status_t lora_linear_compact(const void *x, const void *W, const void *A, c
                                   void *y, lora_dtype_t y_dtype, lora_mode_t mode, void *ws,
                                   size_t ws_bytes, void *stream);
 
+/* The whole layer with a quantized base ([P1], "Where does multi-LoRA serving actually
+ * break?", item 4: a base stored at low precision served beside higher-precision adapters,
+ * so the delta runs in another type than the base and the base -- the denominator of the
+ * LoRA overhead -- gets cheaper).  The base weight is fp8: W8 holds E4M3 codes of the OCP
+ * 8-bit floating point format (1 sign, 4 exponent bits of bias 7, 3 mantissa bits;
+ * subnormals; no infinity), laid out W8[d_out][d_in] (each output column's d_in codes
+ * contiguous, 16-byte aligned), with one fp32 scale per output column, w_scale[d_out]:
+ *     y = x W_eff + (x A_i) B_i scale_i,   W_eff[k, c] = w_scale[c] * dec(W8[c, k]).
+ * x, A, B, scale, ranks, ids, y, segs and the workspace as for lora_linear (bf16 adapters,
+ * padded pool, any r_max in [1, 64]).  Decode batches: M <= 256, d_in a multiple of 64 and at
+ * least 128 (else LORA_ERR_SHAPE); mode LORA_MODE_AUTO or LORA_MODE_DECODE, LORA_MODE_CHECKED
+ * may be OR-ed in (LORA_MODE_PREFILL gives LORA_ERR_MODE).  Workspace: lora_workspace_bytes()
+ * of the same sizes.  Errors as lora_linear. */
+lora_status_t lora_linear_fp8w(const void *x, const void *W8, const float *w_scale, const void *A,
+                               const void *B, const float *scale, const int32_t *ranks,
+                               const int32_t *ids, int32_t M, int32_t d_in, int32_t d_out,
+                               int32_t r_max, int32_t n_adapters, const lora_segments_t *segs,
+                               void *y, lora_dtype_t y_dtype, lora_mode_t mode, void *ws,
+                               size_t ws_bytes, void *stream);
+
+/* Measurement aid: lora_linear_profiled for lora_linear_fp8w's arguments. */
+lora_status_t lora_linear_fp8w_profiled(const void *x, const void *W8, const float *w_scale,
+                                        const void *A, const void *B, const float *scale,
+                                        const int32_t *ranks, const int32_t *ids, int32_t M,
+                                        int32_t d_in, int32_t d_out, int32_t r_max,
+                                        int32_t n_adapters, const lora_segments_t *segs, void *y,
+                                        lora_dtype_t y_dtype, lora_mode_t mode, void *ws,
+                                        size_t ws_bytes, void *stream, float *kernel_ms,
+                                        const char **kernel_names, int32_t max_kernels,
+                                        int32_t *n_kernels);
+
 /* For callers that cannot allocate (code under HIP graph capture, serving loops or
  * harnesses that forbid hipMalloc): lora_linear without a caller workspace.  The call uses a
  * scratch array of LORA_NOALLOC_SCRATCH_BYTES that the library keeps in device memory, one

@@ -423,6 +423,71 @@ hipError_t run_linear(const void *x, const void *W, const void *A, const void *B
 
 lora_status_t lora::hip_error_status(hipError_t e) { return hip_status(e); }
 
+namespace {
+
+// lora_linear_fp8w: the quantized-base decode sequence (arguments already validated, M > 0):
+// the fp8 decode GEMM (with the segment build in one extra workgroup unless segments are
+// given), the segment-path shrink (chunk sums), and the decode reduction that adds the GEMM's
+// scaled split partials and the expand.
+hipError_t run_fp8w(const void *x, const void *W8, const float *w_scale, const void *A,
+                    const void *B, const float *scale, const int32_t *ranks, const int32_t *ids,
+                    int32_t M, int32_t d_in, int32_t d_out, int32_t r_max, int32_t n_adapters,
+                    const lora_segments_t *segs, void *y, lora_dtype_t y_dtype, void *ws,
+                    hipStream_t s, Marker *mk) {
+    char *p = static_cast<char *>(ws);
+    lora_segments_t own = carve_segments(p, M, n_adapters);
+    p += t_bytes(M, r_max);
+    float *spart = reinterpret_cast<float *>(p); p += shrink_partial_bytes(M, d_in, r_max);
+    float *gpart = reinterpret_cast<float *>(p);
+    const Seg sg = to_seg(segs ? *segs : own);
+    const uint16_t *xb = static_cast<const uint16_t *>(x);
+    const int rb = rank_bucket(r_max);
+    int kc, ksplit;
+    shrink_plan(d_in, rb, &kc, &ksplit);
+    const DecodeLora lo{spart, ksplit, nullptr, static_cast<const uint16_t *>(B), scale, ids, ranks,
+                        rb, n_adapters, nullptr, 0, r_max};
+    const SegBuild bld{ids, n_adapters, sg};
+    hipError_t e = launch_decode_gemm_fp8(xb, static_cast<const uint8_t *>(W8), w_scale, M, d_in,
+                                          d_out, gpart, segs ? nullptr : &bld, s);
+    if (e != hipSuccess) return e;
+    mark(mk, "decode_gemm_fp8");
+    if ((e = launch_shrink(xb, static_cast<const uint16_t *>(A), ranks, nullptr, 0, r_max, M, d_in,
+                           rb, n_adapters, sg, spart, kc, ksplit, s)) != hipSuccess)
+        return e;
+    mark(mk, "shrink");
+    if ((e = launch_decode_reduce(gpart, M, d_in, d_out, y, y_dtype == LORA_F32, lo, false, s)) !=
+        hipSuccess)
+        return e;
+    mark(mk, "decode_reduce_lora");
+    return hipSuccess;
+}
+
+lora_status_t check_fp8w(const void *x, const void *W8, const float *w_scale, const void *A,
+                         const void *B, const float *scale, const int32_t *ranks,
+                         const int32_t *ids, int32_t M, int32_t d_in, int32_t d_out,
+                         int32_t r_max, int32_t n_adapters, const lora_segments_t *segs, void *y,
+                         lora_dtype_t y_dtype, lora_mode_t mode, void *ws, size_t ws_bytes) {
+    lora_status_t st = check_common(M, r_max, n_adapters);
+    if (st != LORA_OK) return st;
+    if (!dim_ok(d_in) || !dim_ok(d_out) || d_in % 64 != 0 || d_in < 128 ||
+        M > kDecodeGemmMaxRows)
+        return LORA_ERR_SHAPE;
+    if (y_dtype != LORA_BF16 && y_dtype != LORA_F32) return LORA_ERR_DTYPE;
+    const int bm = mode & ~LORA_MODE_CHECKED;
+    if (bm != LORA_MODE_AUTO && bm != LORA_MODE_DECODE) return LORA_ERR_MODE;
+    if (M == 0) return LORA_OK;
+    if (!x || !W8 || !w_scale || !A || !B || !scale || !ids || !y || !ws) return LORA_ERR_NULL;
+    if (segs && (st = check_seg(*segs)) != LORA_OK) return st;
+    if (!aligned(x, 16) || !aligned(W8, 16) || !aligned(A, 16) || !aligned(B, 16) ||
+        !aligned(y, 16) || !aligned(ws, kAlign) || !aligned(scale, 4) || !aligned(w_scale, 4) ||
+        !aligned(ids, 4) || (ranks && !aligned(ranks, 4)))
+        return LORA_ERR_ALIGN;
+    if (ws_bytes < lora_workspace_bytes(M, d_in, d_out, r_max, n_adapters)) return LORA_ERR_WORKSPACE;
+    return LORA_OK;
+}
+
+}  // namespace
+
 // lora_linear's body on a given workspace: shared with the entry point that brings its own
 // device-resident scratch (csrc/noalloc.hip).
 lora_status_t lora::linear_on_workspace(const void *x, const void *W, const void *A,
@@ -478,19 +543,34 @@ lora_status_t lora_linear_compact(const void *x, const void *W, const void *A, c
                                  nullptr));
 }
 
+lora_status_t lora_linear_fp8w(const void *x, const void *W8, const float *w_scale, const void *A,
+                               const void *B, const float *scale, const int32_t *ranks,
+                               const int32_t *ids, int32_t M, int32_t d_in, int32_t d_out,
+                               int32_t r_max, int32_t n_adapters, const lora_segments_t *segs,
+                               void *y, lora_dtype_t y_dtype, lora_mode_t mode, void *ws,
+                               size_t ws_bytes, void *stream) {
+    lora_status_t st = check_fp8w(x, W8, w_scale, A, B, scale, ranks, ids, M, d_in, d_out, r_max,
+                                  n_adapters, segs, y, y_dtype, mode, ws, ws_bytes);
+    if (st != LORA_OK || M == 0) return st;
+    clear_stale_error();
+    if ((mode & LORA_MODE_CHECKED) &&
+        (st = check_tables(ids, M, ranks, nullptr, 0, r_max, n_adapters, (hipStream_t)stream)) != LORA_OK)
+        return st;
+    return hip_status(run_fp8w(x, W8, w_scale, A, B, scale, ranks, ids, M, d_in, d_out, r_max,
+                               n_adapters, segs, y, y_dtype, ws, (hipStream_t)stream, nullptr));
+}
+
 }  // extern "C"
 
 namespace {
 
 // lora_linear / lora_linear_compact with each launch timed by start / stop events taken
 // from its own dispatch packet (arguments already validated, M > 0).
-lora_status_t run_profiled(const void *x, const void *W, const void *A, const void *B,
-                           const float *scale, const int32_t *ranks, const int32_t *roff,
-                           int32_t pool_rows, const int32_t *ids, int32_t M, int32_t d_in,
-                           int32_t d_out, int32_t r_max, int32_t n_adapters,
-                           const lora_segments_t *segs, void *y, lora_dtype_t y_dtype,
-                           lora_mode_t mode, void *ws, void *stream, float *kernel_ms,
-                           const char **kernel_names, int32_t max_kernels, int32_t *n_kernels) {
+// `run(marker)` enqueues a call's launches; each is timed by start / stop events taken from its
+// own dispatch packet.  Waits for the last one and reports the durations in launch order.
+template <class F>
+lora_status_t time_launches(F run, float *kernel_ms, const char **kernel_names, int32_t max_kernels,
+                            int32_t *n_kernels) {
     clear_stale_error();
     KernelTimer timer;
     hipError_t e = hipSuccess;
@@ -502,9 +582,7 @@ lora_status_t run_profiled(const void *x, const void *W, const void *A, const vo
     Marker mk;
     if (e == hipSuccess) {
         g_timer = &timer;
-        e = run_linear(x, W, A, B, scale, ranks, roff, pool_rows, ids, M, d_in, d_out, r_max,
-                       n_adapters, segs, y, y_dtype, (lora_mode_t)(mode & ~LORA_MODE_CHECKED), ws,
-                       (hipStream_t)stream, &mk);
+        e = run(&mk);
         g_timer = nullptr;
     }
     if (e == hipSuccess && timer.n > 0) e = hipEventSynchronize(timer.stop[timer.n - 1]);
@@ -523,6 +601,22 @@ lora_status_t run_profiled(const void *x, const void *W, const void *A, const vo
         if (timer.stop[i]) (void)hipEventDestroy(timer.stop[i]);
     }
     return hip_status(e);
+}
+
+lora_status_t run_profiled(const void *x, const void *W, const void *A, const void *B,
+                           const float *scale, const int32_t *ranks, const int32_t *roff,
+                           int32_t pool_rows, const int32_t *ids, int32_t M, int32_t d_in,
+                           int32_t d_out, int32_t r_max, int32_t n_adapters,
+                           const lora_segments_t *segs, void *y, lora_dtype_t y_dtype,
+                           lora_mode_t mode, void *ws, void *stream, float *kernel_ms,
+                           const char **kernel_names, int32_t max_kernels, int32_t *n_kernels) {
+    return time_launches(
+        [&](Marker *mk) {
+            return run_linear(x, W, A, B, scale, ranks, roff, pool_rows, ids, M, d_in, d_out, r_max,
+                              n_adapters, segs, y, y_dtype, (lora_mode_t)(mode & ~LORA_MODE_CHECKED),
+                              ws, (hipStream_t)stream, mk);
+        },
+        kernel_ms, kernel_names, max_kernels, n_kernels);
 }
 
 }  // namespace
@@ -563,6 +657,28 @@ lora_status_t lora_linear_compact_profiled(
     return run_profiled(x, W, A, B, scale, ranks, rank_offsets, pool_rows, ids, M, d_in, d_out,
                         r_max, n_adapters, segs, y, y_dtype, mode, ws, stream, kernel_ms,
                         kernel_names, max_kernels, n_kernels);
+}
+
+lora_status_t lora_linear_fp8w_profiled(const void *x, const void *W8, const float *w_scale,
+                                        const void *A, const void *B, const float *scale,
+                                        const int32_t *ranks, const int32_t *ids, int32_t M,
+                                        int32_t d_in, int32_t d_out, int32_t r_max,
+                                        int32_t n_adapters, const lora_segments_t *segs, void *y,
+                                        lora_dtype_t y_dtype, lora_mode_t mode, void *ws,
+                                        size_t ws_bytes, void *stream, float *kernel_ms,
+                                        const char **kernel_names, int32_t max_kernels,
+                                        int32_t *n_kernels) {
+    if (!kernel_ms || !kernel_names || !n_kernels || max_kernels < 0) return LORA_ERR_NULL;
+    *n_kernels = 0;
+    lora_status_t st = check_fp8w(x, W8, w_scale, A, B, scale, ranks, ids, M, d_in, d_out, r_max,
+                                  n_adapters, segs, y, y_dtype, mode, ws, ws_bytes);
+    if (st != LORA_OK || M == 0) return st;
+    return time_launches(
+        [&](Marker *mk) {
+            return run_fp8w(x, W8, w_scale, A, B, scale, ranks, ids, M, d_in, d_out, r_max,
+                            n_adapters, segs, y, y_dtype, ws, (hipStream_t)stream, mk);
+        },
+        kernel_ms, kernel_names, max_kernels, n_kernels);
 }
 
 const char *lora_status_string(lora_status_t status) {

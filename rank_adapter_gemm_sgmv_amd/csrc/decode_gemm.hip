@@ -543,11 +543,24 @@ bool decode_fused_supported(int M, int K, int N) {
     return decode_gemm_supported(M, K, N) && M <= kDecodeMaxRows;
 }
 
+DecodeSplits decode_splits(int M, int K, int N) {
+    const DecPlan p = dec_plan(M, K, N, 0);
+    return DecodeSplits{p.bm, p.n_tm, p.n_tn, p.ks, p.k_per_split};
+}
+
 size_t decode_gemm_partial_floats(int M, int K, int N, int r_max, int n_adapters) {
-    if (!decode_gemm_supported(M, K, N) || !rank_ok(r_max)) return 0;
-    const int n_lt = decode_fused_supported(M, K, N) ? adapter_tiles(M, r_max, n_adapters) : 0;
-    const DecPlan p = dec_plan(M, K, N, n_lt);
-    return (size_t)p.ks * p.n_tm * (p.n_tn + p.n_lt) * p.bm * kBN;
+    if (!decode_gemm_supported(M, K, N)) return 0;
+    // every plan a call of these sizes may run: without adapter tiles (batches of 129-256
+    // rows, rank-compact pools, strides that are not a rank bucket, the fp8 base), and with
+    // them (the fused small-batch path); the latter has more tiles but may have fewer splits
+    const DecPlan p0 = dec_plan(M, K, N, 0);
+    size_t f = (size_t)p0.ks * p0.n_tm * p0.n_tn * p0.bm * kBN;
+    if (rank_ok(r_max) && decode_fused_supported(M, K, N)) {
+        const DecPlan p = dec_plan(M, K, N, adapter_tiles(M, r_max, n_adapters));
+        const size_t fa = (size_t)p.ks * p.n_tm * (p.n_tn + p.n_lt) * p.bm * kBN;
+        if (fa > f) f = fa;
+    }
+    return f;
 }
 
 hipError_t launch_decode_gemm(const uint16_t *x, const uint16_t *W, const uint16_t *A, int M,

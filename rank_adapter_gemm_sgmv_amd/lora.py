@@ -36,7 +36,7 @@ STATUS = {
 EXPORTS = ("lora_max_tiles", "lora_workspace_bytes", "lora_build_segments", "lora_shrink",
            "lora_shrink_compact", "lora_expand", "lora_expand_compact", "lora_linear",
            "lora_linear_profiled", "lora_linear_compact", "lora_linear_compact_profiled",
-           "lora_linear_noalloc",
+           "lora_linear_noalloc", "lora_linear_fp8w", "lora_linear_fp8w_profiled",
            "lora_status_string", "lora_last_hip_error")
 
 
@@ -87,6 +87,13 @@ def _load():
                                 ctypes.POINTER(lora_segments_t), P, ctypes.c_int, ctypes.c_int,
                                 P, S, P]
     lib.lora_linear.restype = ctypes.c_int
+    lib.lora_linear_fp8w.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I,
+                                     ctypes.POINTER(lora_segments_t), P, ctypes.c_int, ctypes.c_int,
+                                     P, S, P]
+    lib.lora_linear_fp8w.restype = ctypes.c_int
+    lib.lora_linear_fp8w_profiled.argtypes = lib.lora_linear_fp8w.argtypes + [
+        ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_char_p), I, ctypes.POINTER(I)]
+    lib.lora_linear_fp8w_profiled.restype = ctypes.c_int
     lib.lora_linear_noalloc.argtypes = lib.lora_linear.argtypes[:16] + [P]
     lib.lora_linear_noalloc.restype = ctypes.c_int
     lib.lora_linear_profiled.argtypes = lib.lora_linear.argtypes + [
@@ -203,6 +210,32 @@ def lora_linear(x, W, A, B, scale, ranks, ids, M: int, d_in: int, d_out: int, r_
     _check(_lib.lora_linear(_ptr(x), _ptr(W), _ptr(A), _ptr(B), _ptr(scale), _ptr(ranks),
                             _ptr(ids), M, d_in, d_out, r_max, n_adapters, seg_p, _ptr(y), y_dtype,
                             mode, _ptr(ws), ws_bytes, _stream(stream)), "lora_linear")
+
+
+def lora_linear_fp8w(x, W8, w_scale, A, B, scale, ranks, ids, M: int, d_in: int, d_out: int,
+                     r_max: int, n_adapters: int, segs, y, y_dtype: int, mode: int, ws,
+                     ws_bytes: int, stream=None) -> None:
+    """lora_linear with an fp8 (E4M3) base: W8[d_out, d_in] codes (uint8), w_scale[d_out]."""
+    seg_p = None if segs is None else ctypes.byref(_seg_struct(segs))
+    _check(_lib.lora_linear_fp8w(_ptr(x), _ptr(W8), _ptr(w_scale), _ptr(A), _ptr(B), _ptr(scale),
+                                 _ptr(ranks), _ptr(ids), M, d_in, d_out, r_max, n_adapters, seg_p,
+                                 _ptr(y), y_dtype, mode, _ptr(ws), ws_bytes, _stream(stream)),
+           "lora_linear_fp8w")
+
+
+def lora_linear_fp8w_profiled(x, W8, w_scale, A, B, scale, ranks, ids, M: int, d_in: int,
+                              d_out: int, r_max: int, n_adapters: int, segs, y, y_dtype: int,
+                              mode: int, ws, ws_bytes: int, stream=None, max_kernels: int = 16):
+    """lora_linear_fp8w with per-kernel HIP event timing; returns [(kernel name, ms), ...]."""
+    seg_p = None if segs is None else ctypes.byref(_seg_struct(segs))
+    ms = (ctypes.c_float * max_kernels)()
+    names = (ctypes.c_char_p * max_kernels)()
+    n = ctypes.c_int32(0)
+    _check(_lib.lora_linear_fp8w_profiled(
+        _ptr(x), _ptr(W8), _ptr(w_scale), _ptr(A), _ptr(B), _ptr(scale), _ptr(ranks), _ptr(ids), M,
+        d_in, d_out, r_max, n_adapters, seg_p, _ptr(y), y_dtype, mode, _ptr(ws), ws_bytes,
+        _stream(stream), ms, names, max_kernels, ctypes.byref(n)), "lora_linear_fp8w_profiled")
+    return [(names[i].decode(), float(ms[i])) for i in range(n.value)]
 
 
 def lora_linear_noalloc(x, W, A, B, scale, ranks, ids, M: int, d_in: int, d_out: int, r_max: int,

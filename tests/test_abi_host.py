@@ -21,7 +21,7 @@ FAKE = 1 << 20  # 16/256-byte aligned, never dereferenced
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(lora_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(lora_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_every_declared_symbol_is_exported():
@@ -189,3 +189,20 @@ def test_noalloc_rejects_before_touching_the_device():
         assert e.value.status == code
     assert L.lora_workspace_bytes(512, 4096, 11008, 16, 32) > L.LORA_NOALLOC_SCRATCH_BYTES
     L.lora_linear_noalloc(**{**args, "M": 0, "x": None, "y": None})  # no-op
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(d_in=4104), 2), (dict(d_in=64), 2), (dict(M=257), 2), (dict(r_max=65), 3),
+    (dict(mode=L.LORA_MODE_PREFILL), 9), (dict(mode=5), 9), (dict(w_scale=None), 1),
+    (dict(W8=None), 1), (dict(W8=FAKE + 8), 4), (dict(w_scale=FAKE + 2), 4),
+    (dict(ws_bytes=1024), 5), (dict(y_dtype=4), 6),
+])
+def test_linear_fp8w_rejects(over, code):
+    args = dict(x=FAKE, W8=FAKE, w_scale=FAKE, A=FAKE, B=FAKE, scale=FAKE, ranks=None, ids=FAKE,
+                M=64, d_in=4096, d_out=4096, r_max=16, n_adapters=32, segs=None, y=FAKE,
+                y_dtype=L.LORA_BF16, mode=L.LORA_MODE_DECODE, ws=FAKE,
+                ws_bytes=L.lora_workspace_bytes(64, 4096, 4096, 16, 32), stream=0)
+    args.update(over)
+    with pytest.raises(L.LoraError) as e:
+        L.lora_linear_fp8w(**args)
+    assert e.value.status == code
