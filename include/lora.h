@@ -247,7 +247,7 @@ lora_status_t lora_linear_compact(const void *x, const void *W, const void *A, c
  * contiguous, 16-byte aligned), with one fp32 scale per output column, w_scale[d_out]:
  *     y = x W_eff + (x A_i) B_i scale_i,   W_eff[k, c] = w_scale[c] * dec(W8[c, k]).
  * x, A, B, scale, ranks, ids, y, segs and the workspace as for lora_linear (bf16 adapters,
- * padded pool, any r_max in [1, 64]).  Decode batches: M <= 256, d_in a multiple of 64 and at
+ * padded pool, any r_max in [1, 64]).  Decode batches: M <= 256, d_in a multiple of 32 and at
  * least 128 (else LORA_ERR_SHAPE); mode LORA_MODE_AUTO or LORA_MODE_DECODE, LORA_MODE_CHECKED
  * may be OR-ed in (LORA_MODE_PREFILL gives LORA_ERR_MODE).  Workspace: lora_workspace_bytes()
  * of the same sizes.  Errors as lora_linear. */

@@ -469,7 +469,7 @@ lora_status_t check_fp8w(const void *x, const void *W8, const float *w_scale, co
                          lora_dtype_t y_dtype, lora_mode_t mode, void *ws, size_t ws_bytes) {
     lora_status_t st = check_common(M, r_max, n_adapters);
     if (st != LORA_OK) return st;
-    if (!dim_ok(d_in) || !dim_ok(d_out) || d_in % 64 != 0 || d_in < 128 ||
+    if (!dim_ok(d_in) || !dim_ok(d_out) || d_in % 32 != 0 || d_in < 128 ||
         M > kDecodeGemmMaxRows)
         return LORA_ERR_SHAPE;
     if (y_dtype != LORA_BF16 && y_dtype != LORA_F32) return LORA_ERR_DTYPE;

@@ -230,9 +230,9 @@ struct DecodeSplits {
 DecodeSplits decode_splits(int M, int K, int N);
 
 // x W_eff for a decode batch whose base weight is fp8 E4M3 codes W8[N][K] with per-column
-// scales w_scale[N] (csrc/fp8_gemm.hip): the scaled partial tiles of decode_splits(M, K, N).
-// K % 64 == 0, M <= kDecodeGemmMaxRows.  build (nullable): also build the segments of these
-// ids in one more workgroup.
+// scales w_scale[N] (csrc/decode_gemm.hip): the scaled partial tiles of decode_splits(M, K, N).
+// As decode_gemm_supported, and N % 8 == 0.  build (nullable): also build the segments of
+// these ids in one more workgroup.
 hipError_t launch_decode_gemm_fp8(const uint16_t *x, const uint8_t *W8, const float *w_scale,
                                   int M, int K, int N, float *partial, const SegBuild *build,
                                   hipStream_t s);

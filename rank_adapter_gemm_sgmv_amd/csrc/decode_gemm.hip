@@ -361,6 +361,177 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(
     }
 }
 
+// ---- the same split-K GEMM with an fp8 base weight -----------------------------------------
+// W8 holds E4M3 codes (OCP 8-bit floating point) laid out W8[N][K] -- each output column's K
+// codes contiguous -- with one fp32 scale per column: W_eff[k, n] = w_scale[n] dec(W8[n, k]).
+// Tiles and splits are decode_gemm_kernel's (dec_plan without adapter tiles), so the decode
+// reduction adds these partial tiles unchanged; the partial tile is multiplied by the columns'
+// scales before it is stored.
+//
+// At decode sizes both GEMMs are bound by the memory requests the CU can issue -- the cache
+// lines each load instruction touches -- not by HBM: W8[N][K] gives a column's codes as a
+// contiguous run, so a 16-byte piece per column touched one line per lane and kept the
+// texture unit waiting on L1 (TA_ADDR_STALLED_BY_TC_CYCLES 4.5x the bf16 kernel's).  Here:
+//  * the four waves split the 128 columns (32 each) and each load of W8 covers 8 columns x
+//    128 codes (whole 128-byte lines); x is loaded once per workgroup and shared;
+//  * a stage is 128 k: x[BM rows][128 k] (loaded by all waves) and each wave's W8[32 cols]
+//    [128 k]; three stages in a ring, two ahead, one barrier per stage (a fourth slot,
+//    three ahead, measured no faster);
+//  * W stage of a wave: column c, 16-k chunk kc at LDS slot 8 c + (kc ^ ((c >> 1) & 7)), so an
+//    MFMA's B operand (8 codes of 32 columns, ds_read_b64) has 2-way bank conflicts at most;
+//    x stage: row r, 8-k chunk lc at slot 16 r + (lc ^ (r % 16));
+//  * codes become bf16 with v_cvt_scalef32_pk_bf16_fp8 (scale 1: exact, every E4M3 value is a
+//    bf16 value) for v_mfma_f32_32x32x16_bf16, with two accumulator sets (even and odd steps)
+//    and no branch inside a stage, so the LDS reads of all eight steps can be issued ahead
+//    of the MFMAs (with a branch per step and one set: 16.3 us at 64 x 4096 x 4096, now
+//    11.6 us); each wave writes its columns of the partial tile straight from its
+//    accumulators.
+constexpr int kF8K = 128;  // k per fp8 stage
+
+template <int BM_>
+struct DecF8 {
+    static constexpr int BM = BM_;
+    static constexpr int TM = BM / 32;
+    static constexpr int XSLOT = BM * kF8K * 2 / 16;      // uint4 per x stage
+    static constexpr int WSLOT_W = 32 * kF8K / 16;         // uint4 per W stage of one wave
+    static constexpr int XI = XSLOT / kWaves / 64;         // x loads per wave per stage
+    static constexpr int WI = WSLOT_W / 64;                // W loads per wave per stage (4)
+    static constexpr int SLOT = XSLOT + kWaves * WSLOT_W;  // uint4 per ring slot
+    static constexpr int TILE = BM * kBN;
+    static constexpr int BUILD16 = ((LORA_MAX_ADAPTERS + 1 + 15) / 16 * 64 + 64 * 4 + 15) / 16;
+    static constexpr int LDS16 = 3 * SLOT > BUILD16 ? 3 * SLOT : BUILD16;  // uint4 of LDS
+    static_assert(XI >= 1 && XSLOT % (kWaves * 64) == 0, "whole x loads per wave");
+};
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) u32x2_t lds_u32x2_t;
+
+// 8 codes (two dwords) -> 8 bf16
+__device__ __forceinline__ bf16x8_t dec_fp8x8(uint32_t lo, uint32_t hi) {
+    const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+    const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+    const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+    const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+    return bf16x8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// Workgroup (tile, split): rows m0 .. m0 + BM of x, columns n0 .. n0 + 127 (wave w: 32 w ..),
+// k in the split.  BUILD: one more workgroup (the last) builds the segments instead.
+template <class C, bool BUILD>
+__global__ __launch_bounds__(kThreads) void decode_gemm_fp8_kernel(
+    const uint16_t *__restrict__ x, const uint8_t *__restrict__ W8, const float *__restrict__ w_scale,
+    int M, int K, int N, int n_tm, int n_tn, int k_per_split, float *__restrict__ partial,
+    int n_gemm_blocks, SegBuild build) {
+    __shared__ __attribute__((aligned(1024))) uint4 lds[C::LDS16];
+
+    if (BUILD && (int)blockIdx.x >= n_gemm_blocks) {
+        int32_t *cnt = reinterpret_cast<int32_t *>(lds);
+        int32_t(*wave_tot)[kWaves] =
+            reinterpret_cast<int32_t(*)[kWaves]>(cnt + ((build.n_adapters + 1 + 15) & ~15));
+        build_segments_block<kThreads>(build.ids, M, build.n_adapters, build.seg, cnt, wave_tot,
+                                       &wave_tot[3][0]);
+        return;
+    }
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n_tiles = n_tm * n_tn;
+    int lin = blockIdx.x;
+    if (n_tm > 1 && (n_gemm_blocks & 7) == 0) lin = (blockIdx.x & 7) * (n_gemm_blocks >> 3) + (blockIdx.x >> 3);
+    const int tile = lin % n_tiles, split = lin / n_tiles;
+    const int tm = tile % n_tm, tn = tile / n_tm;
+    const int m0 = tm * C::BM, n0 = tn * kBN;
+    const int ks0 = split * k_per_split;
+    const int ks1 = min(K, ks0 + k_per_split);
+    const int nst = (ks1 - ks0) / kBKW;        // 16-k steps (K % 32 == 0)
+    const int nsg = (nst + 7) >> 3;             // 128-k stages
+    const int klast = ks0 + (nst - 1) * kBKW;   // first k of the last step
+
+    // W8 load q of a stage, lane l: column c = 8 q + l / 8 of the wave's 32 (columns past N
+    // read the last one, never used), chunk (l % 8) ^ ((c >> 1) & 7), to slot 64 q + l = 8 c +
+    // (l % 8)
+    const uint8_t *wp[C::WI];
+    int wkc[C::WI];
+#pragma unroll
+    for (int q = 0; q < C::WI; ++q) {
+        const int c = 8 * q + (lane >> 3);
+        wp[q] = W8 + (size_t)min(n0 + 32 * wave + c, N - 1) * K;
+        wkc[q] = (lane & 7) ^ ((c >> 1) & 7);
+    }
+    // x load q of a stage, lane l (this wave's part): row r = 4 (XI wave + q) + l / 16, chunk
+    // (l % 16) ^ (r % 16), to slot 16 r + (l % 16) (rows past the batch repeat its last)
+    const uint16_t *xp[C::XI];
+    int xlc[C::XI];
+#pragma unroll
+    for (int q = 0; q < C::XI; ++q) {
+        const int r = 4 * (C::XI * wave + q) + (lane >> 4);
+        xp[q] = x + (size_t)min(m0 + r, M - 1) * K;
+        xlc[q] = (lane & 15) ^ (r & 15);
+    }
+
+    auto issue = [&](int u, uint4 *slot) {
+        // stage u: codes and x from k0 = ks0 + 128 u; chunks past the split's last step
+        // repeat it (W) or stop at K (x) -- their steps are not computed
+        const int k0 = ks0 + kF8K * min(u, nsg - 1);
+        uint4 *xs = slot, *ws = slot + C::XSLOT + wave * C::WSLOT_W;
+#pragma unroll
+        for (int q = 0; q < C::XI; ++q)
+            dma16(xp[q] + min(k0 + 8 * xlc[q], K - 8), (const lds_void_t *)&xs[(C::XI * wave + q) * 64]);
+#pragma unroll
+        for (int q = 0; q < C::WI; ++q)
+            dma16(wp[q] + min(k0 + 16 * wkc[q], klast), (const lds_void_t *)&ws[q * 64]);
+    };
+
+    // two accumulator sets (even and odd steps) so that twice as many MFMA chains are
+    // independent; added at the end
+    f32x16_t acc[C::TM][2];
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][0][v] = acc[i][1][v] = 0.0f;
+
+    uint4 *const S0 = lds, *const S1 = lds + C::SLOT, *const S2 = lds + 2 * C::SLOT;
+    issue(0, S0);
+    issue(1, S1);
+    const int c = lane & 31, g = lane >> 5;
+    for (int u = 0; u < nsg; ++u) {
+        uint4 *const SC = (u % 3 == 0) ? S0 : (u % 3 == 1) ? S1 : S2;
+        uint4 *const SN = (u % 3 == 0) ? S2 : (u % 3 == 1) ? S0 : S1;  // slot of stage u + 2
+        wait_vm<C::XI + C::WI>();  // this wave's loads of stage u are in (stage u + 1's pending)
+        __syncthreads();           // every wave's loads of stage u are in; stage u - 1 is done
+        issue(u + 2, SN);
+        const uint4 *xs = SC;
+        const lds_char_t *ws = (const lds_char_t *)(SC + C::XSLOT + wave * C::WSLOT_W);
+        // steps past the split's last carry zero codes (a select, not a branch, so the
+        // compiler may issue every step's LDS reads ahead of the MFMAs)
+#pragma unroll
+        for (int st = 0; st < 8; ++st) {
+            const u32x2_t v = *(const lds_u32x2_t *)(ws + (8 * c + (st ^ ((c >> 1) & 7))) * 16 + 8 * g);
+            const bool ok = 8 * u + st < nst;
+            const bf16x8_t b = dec_fp8x8(ok ? v[0] : 0u, ok ? v[1] : 0u);
+#pragma unroll
+            for (int i = 0; i < C::TM; ++i) {
+                const int r = 32 * i + c;
+                const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(&xs[16 * r + ((2 * st + g) ^ (r & 15))]);
+                acc[i][st & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[i][st & 1], 0, 0, 0);
+            }
+        }
+    }
+    wait_vm<0>();  // the ring's last (unused) loads land before the workgroup ends
+
+    // the wave's 32 columns of the scaled partial tile: element v of block i is row
+    // 32 i + (v / 4) * 8 + g * 4 + v % 4, column c
+    const int col = n0 + 32 * wave + c;
+    const float sc = w_scale[min(col, N - 1)];
+    float *P = partial + ((size_t)split * n_tiles + tile) * C::TILE + 32 * wave + c;
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+            P[(size_t)(32 * i + (v / 4) * 8 + g * 4 + v % 4) * kBN] = sc * (acc[i][0][v] + acc[i][1][v]);
+}
+
 // y[m, n .. n+3] = (sum over splits, in order, of the partial tiles)
 //                  + scale_a * sum_j t[m, j] B_a[j, n .. n+3]   (a = ids[m], when valid)
 // with t[m, j] the sum, in order, of n_t parts tsrc[c * t_stride + ...]: the splits of row
@@ -598,6 +769,33 @@ hipError_t launch_decode_gemm(const uint16_t *x, const uint16_t *W, const uint16
     }
 #undef GEMM_RANK
 #undef GEMM_LAUNCH
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_gemm_fp8(const uint16_t *x, const uint8_t *W8, const float *w_scale,
+                                  int M, int K, int N, float *partial, const SegBuild *build,
+                                  hipStream_t s) {
+    if (!decode_gemm_supported(M, K, N) || N % 8 != 0 || partial == nullptr || w_scale == nullptr)
+        return hipErrorInvalidValue;
+    if (build && (build->ids == nullptr || build->n_adapters < 1 || build->n_adapters > LORA_MAX_ADAPTERS))
+        return hipErrorInvalidValue;
+    const DecPlan p = dec_plan(M, K, N, 0);
+    const int n_gemm = p.n_tm * p.n_tn * p.ks;
+    const dim3 grid(n_gemm + (build ? 1 : 0));
+    const SegBuild bld = build ? *build : SegBuild{nullptr, 1, Seg{}};
+#define F8_LAUNCH(BM)                                                                          \
+    if (build)                                                                                 \
+        launch((decode_gemm_fp8_kernel<DecF8<BM>, true>), grid, dim3(kThreads), 0, s, x, W8,     \
+               w_scale, M, K, N, p.n_tm, p.n_tn, p.k_per_split, partial, n_gemm, bld);          \
+    else                                                                                       \
+        launch((decode_gemm_fp8_kernel<DecF8<BM>, false>), grid, dim3(kThreads), 0, s, x, W8,    \
+               w_scale, M, K, N, p.n_tm, p.n_tn, p.k_per_split, partial, n_gemm, bld)
+    if (p.bm == 32) {
+        F8_LAUNCH(32);
+    } else {
+        F8_LAUNCH(64);
+    }
+#undef F8_LAUNCH
     return hipGetLastError();
 }
 
