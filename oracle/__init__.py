@@ -14,4 +14,5 @@ from .oracle import (  # noqa: F401
     lora_linear,
     lora_linear_fp8w,
     lora_shrink,
+    moe_lora_linear,
 )

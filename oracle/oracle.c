@@ -349,3 +349,83 @@ int oracle_lora_linear_fp8w(const float *x, const uint8_t *W8, const float *w_sc
     free(Wd);
     return status;
 }
+
+/* ---------------------------------------------------------------------------------------
+ * MoE-LoRA ([P3], "MoE Models Raise the Bar": in a routed expert layer every adapted
+ * projection of every expert carries the request's adapter, and the adapter's shrink and
+ * expand run inside the expert routing kernel).  Token m is routed to top_k experts
+ * (topk_ids[m][j], -1 = no expert in that slot) with routing weights topk_w[m][j]; it
+ * carries adapter ids[m] (-1 = the bare base).  Expert e has its own base weight
+ * W[e][d_in][d_out] and, for every adapter i, its own pair A[i][e][d_in][r_max],
+ * B[i][e][r_max][d_out] (padded to r_max with zeros).  Per (token, slot), with e = topk_ids:
+ *
+ *   y[m][j][c] = topk_w[m][j] * ( sum_k x[m][k] W[e][k][c]
+ *                                 + (alpha_i / r_i) sum_q (sum_k x[m][k] A[i][e][k][q]) B[i][e][q][c] )
+ *
+ * (the adapter term only when i = ids[m] >= 0), and y[m][j][:] = 0 for a slot with no
+ * expert.  topk_w NULL means weight 1.  Sums ascending, fp32, as in oracle_lora_linear; the
+ * routing weight multiplies the finished row.
+ * ------------------------------------------------------------------------------------- */
+int oracle_moe_lora_linear(const float *x, const float *W, const float *A, const float *B,
+                           const float *alpha, const int32_t *ranks, const int32_t *ids,
+                           const int32_t *topk_ids, const float *topk_w, int32_t M, int32_t top_k,
+                           int32_t n_experts, int32_t d_in, int32_t d_out, int32_t r_max,
+                           int32_t n_adapters, float *y, int32_t n_threads) {
+    if (M < 0 || top_k < 1 || n_experts < 1 || d_in < 1 || d_out < 1 || r_max < 1 ||
+        n_adapters < 1)
+        return ORACLE_ERR_ARG;
+    if (!ids_valid(ids, M, n_adapters)) return ORACLE_ERR_BAD_ID;
+    for (int64_t p = 0; p < (int64_t)M * top_k; ++p)
+        if (topk_ids[p] < -1 || topk_ids[p] >= n_experts) return ORACLE_ERR_BAD_ID;
+    int status = ORACLE_OK;
+    (void)n_threads;
+#pragma omp parallel num_threads(n_threads > 0 ? n_threads : 1)
+    {
+        float *tq = (float *)malloc((size_t)r_max * sizeof(float));
+        float *dq = (float *)malloc((size_t)d_out * sizeof(float));
+        if (!tq || !dq) {
+#pragma omp atomic write
+            status = ORACLE_ERR_NOMEM;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t p = 0; p < (int64_t)M * top_k; ++p) {
+            if (!tq || !dq) continue;
+            const int32_t m = (int32_t)(p / top_k);
+            const int32_t e = topk_ids[p];
+            float *out = y + (size_t)p * d_out;
+            for (int32_t c = 0; c < d_out; ++c) out[c] = 0.0f;
+            if (e < 0) continue; /* empty slot */
+            const float *xrow = x + (size_t)m * d_in;
+            const float *We = W + (size_t)e * d_in * d_out;
+            for (int32_t k = 0; k < d_in; ++k) {
+                const float xv = xrow[k];
+                const float *werow = We + (size_t)k * d_out;
+                for (int32_t c = 0; c < d_out; ++c) out[c] += xv * werow[c];
+            }
+            const int32_t i = ids[m];
+            if (i >= 0) {
+                const float *Aie = A + ((size_t)i * n_experts + e) * d_in * r_max;
+                const float *Bie = B + ((size_t)i * n_experts + e) * r_max * d_out;
+                for (int32_t q = 0; q < r_max; ++q) tq[q] = 0.0f;
+                for (int32_t k = 0; k < d_in; ++k) {
+                    const float xv = xrow[k];
+                    for (int32_t q = 0; q < r_max; ++q) tq[q] += xv * Aie[(size_t)k * r_max + q];
+                }
+                for (int32_t c = 0; c < d_out; ++c) dq[c] = 0.0f;
+                for (int32_t q = 0; q < r_max; ++q) {
+                    const float tv = tq[q];
+                    for (int32_t c = 0; c < d_out; ++c) dq[c] += tv * Bie[(size_t)q * d_out + c];
+                }
+                const float sa = alpha[i] / (float)ranks[i];
+                for (int32_t c = 0; c < d_out; ++c) out[c] += sa * dq[c];
+            }
+            if (topk_w) {
+                const float wt = topk_w[p];
+                for (int32_t c = 0; c < d_out; ++c) out[c] = wt * out[c];
+            }
+        }
+        free(tq);
+        free(dq);
+    }
+    return status;
+}

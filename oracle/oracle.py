@@ -68,6 +68,8 @@ def _bind(lib):
     lib.oracle_lora_linear.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, P, I, P, I]
     lib.oracle_lora_linear_fp8w.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, P, I, P, I]
     lib.oracle_lora_linear_fp8w.restype = ctypes.c_int
+    lib.oracle_moe_lora_linear.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, P, I]
+    lib.oracle_moe_lora_linear.restype = ctypes.c_int
     lib.oracle_fp8_e4m3_decode_array.argtypes = [P, ctypes.c_int64, P]
     lib.oracle_fp8_e4m3_decode_array.restype = None
     for f in (lib.oracle_build_segments, lib.oracle_lora_shrink, lib.oracle_lora_expand,
@@ -218,4 +220,30 @@ def lora_linear_fp8w(x, W8, w_scale, A, B, alpha, ranks, ids, rows=None,
                                        _ptr(alpha), _ptr(ranks), _ptr(ids), M, d_in, d_out, r_max,
                                        n, None if rows_a is None else _ptr(rows_a), n_rows,
                                        _ptr(y), _threads(n_threads)), "lora_linear_fp8w")
+    return y
+
+
+def moe_lora_linear(x, W, A, B, alpha, ranks, ids, topk_ids, topk_w=None,
+                    n_threads: Optional[int] = None, lib=None) -> np.ndarray:
+    """MoE-LoRA per (token, slot): y[m, j] = topk_w[m, j] * (x_m W_e + (x_m A[i, e]) B[i, e]
+    alpha_i / r_i) with e = topk_ids[m, j] (-1: zero row), i = ids[m] (-1: no adapter term).
+    W[E, d_in, d_out], A[n, E, d_in, r_max], B[n, E, r_max, d_out]; returns y[M, top_k, d_out]."""
+    lib = lib or _load()
+    x, W, A, B = _f32(x), _f32(W), _f32(A), _f32(B)
+    alpha, ranks, ids = np.ascontiguousarray(alpha, np.float32), _i32(ranks), _i32(ids)
+    topk_ids = _i32(topk_ids)
+    M, d_in = x.shape
+    E, d_in2, d_out = W.shape
+    n, E2, d_in3, r_max = A.shape
+    top_k = int(topk_ids.shape[1]) if topk_ids.ndim == 2 else 1
+    assert d_in2 == d_in and d_in3 == d_in and E2 == E and B.shape == (n, E, r_max, d_out)
+    assert topk_ids.shape == (M, top_k) and ids.shape == (M,)
+    tw = None if topk_w is None else np.ascontiguousarray(topk_w, np.float32)
+    if tw is not None:
+        assert tw.shape == (M, top_k)
+    y = np.empty((M, top_k, d_out), np.float32)
+    _check(lib.oracle_moe_lora_linear(_ptr(x), _ptr(W), _ptr(A), _ptr(B), _ptr(alpha), _ptr(ranks),
+                                      _ptr(ids), _ptr(topk_ids), None if tw is None else _ptr(tw),
+                                      M, top_k, E, d_in, d_out, r_max, n, _ptr(y),
+                                      _threads(n_threads)), "moe_lora_linear")
     return y

@@ -13,6 +13,9 @@ from .workloads import (  # noqa: F401
     f32_to_bf16_bits,
     fp8_base,
     make_workload,
+    MoeWorkload,
+    make_moe_workload,
+    moe_case,
     pool_param_count,
     random_alpha,
     random_case,

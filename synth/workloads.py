@@ -332,3 +332,107 @@ def random_case(seed: int, M: int, d_in: int, d_out: int, n_adapters: int, r_max
     _zero_padding(A, B, ranks_a)
     return Workload(f"random_{seed}", ids_a, ranks_a, alpha, int(r_max),
                     [Projection("proj", x, W, A, B)], storage, int(seed))
+
+
+# --------------------------------------------------------------------------------------
+# MoE-LoRA inputs
+# --------------------------------------------------------------------------------------
+
+
+@dataclasses.dataclass
+class MoeWorkload:
+    """A routed expert projection with per-expert adapters ("Multi-LoRA Serving: Sharing One
+    GPU Across Adapters", "MoE Models Raise the Bar").  Layouts (row-major):
+      x [M, d_in]        W [E, d_in, d_out]          topk_ids [M, top_k] (-1: empty slot)
+      A [n, E, d_in, r_max]   B [n, E, r_max, d_out]   topk_w [M, top_k] float32
+    ids [M] is each token's adapter (-1: none), ranks / alpha per adapter."""
+
+    name: str
+    x: np.ndarray
+    W: np.ndarray
+    A: np.ndarray
+    B: np.ndarray
+    ids: np.ndarray
+    topk_ids: np.ndarray
+    topk_w: np.ndarray
+    ranks: np.ndarray
+    alpha: np.ndarray
+    r_max: int
+    seed: int
+
+    @property
+    def M(self) -> int:
+        return int(self.x.shape[0])
+
+    @property
+    def top_k(self) -> int:
+        return int(self.topk_ids.shape[1])
+
+    @property
+    def n_experts(self) -> int:
+        return int(self.W.shape[0])
+
+    @property
+    def n_adapters(self) -> int:
+        return int(self.ranks.shape[0])
+
+    @property
+    def d_in(self) -> int:
+        return int(self.W.shape[1])
+
+    @property
+    def d_out(self) -> int:
+        return int(self.W.shape[2])
+
+
+def moe_case(seed: int, M: int, top_k: int, n_experts: int, d_in: int, d_out: int,
+             n_adapters: int, r_max: int, ranks: Optional[Sequence[int]] = None,
+             base_frac: float = 0.2, empty_frac: float = 0.0, zipf_s: float = 0.0,
+             name: Optional[str] = None, storage: str = "bf16") -> MoeWorkload:
+    """A seeded MoE-LoRA case.  Router (synthetic): each token picks top_k distinct experts,
+    uniformly or with Zipf(zipf_s) popularity when zipf_s > 0, routing weights are a softmax
+    of N(0, 1) logits over its picks; a fraction empty_frac of slots is left empty (-1).
+    Adapter ids uniform over the pool with base_frac of tokens -1; ranks uniform over
+    [1, r_max] unless given, alpha from ``random_alpha``.  Values N(0, 1) for x, N(0, 0.02)
+    for W, A, B, rounded to bf16; adapter entries past the rank are zero."""
+    rng = np.random.Generator(np.random.PCG64([int(seed), 9]))
+    E = int(n_experts)
+    p = zipf_probs(E, zipf_s) if zipf_s > 0 else np.full(E, 1.0 / E)
+    topk = np.stack([rng.choice(E, size=top_k, replace=False, p=p) for _ in range(M)]).astype(np.int32) \
+        if M else np.zeros((0, top_k), np.int32)
+    logits = rng.standard_normal((M, top_k))
+    w = np.exp(logits - logits.max(axis=1, keepdims=True)) if M else logits
+    w = (w / w.sum(axis=1, keepdims=True)).astype(np.float32) if M else w.astype(np.float32)
+    if empty_frac > 0 and M:
+        topk[rng.random((M, top_k)) < empty_frac] = -1
+    ids = rng.integers(0, n_adapters, size=M)
+    if base_frac > 0 and M:
+        ids[rng.random(M) < base_frac] = -1
+    ids = ids.astype(np.int32)
+    ranks_a = (rng.integers(1, r_max + 1, size=n_adapters) if ranks is None
+               else np.asarray(ranks)).astype(np.int32)
+    alpha = random_alpha(seed, n_adapters)
+    x = _normal(rng, (M, d_in), 1.0, storage)
+    W = _normal(rng, (E, d_in, d_out), 0.02, storage)
+    A = _normal(rng, (n_adapters, E, d_in, r_max), 0.02, storage)
+    B = _normal(rng, (n_adapters, E, r_max, d_out), 0.02, storage)
+    for i, r in enumerate(ranks_a.tolist()):
+        if r < r_max:
+            A[i, :, :, r:] = 0
+            B[i, :, r:, :] = 0
+    return MoeWorkload(name or f"moe_{seed}", x, W, A, B, ids, topk, w, ranks_a, alpha,
+                       int(r_max), int(seed))
+
+
+MOE_DECODE = dict(name="moe_decode_64tok_32exp_top4_2880_8ad_r16", M=64, top_k=4, n_experts=32,
+                  d_in=2880, d_out=2880, n_adapters=8, r_max=16, base_frac=0.1)
+
+
+def make_moe_workload(seed: int = 1006) -> MoeWorkload:
+    """The MoE decode workload: 64 tokens routed top-4 over 32 experts of 2880 x 2880 (the
+    expert width of the GPT-OSS 20B model the pages report MoE-LoRA results on), 8 adapters
+    of rank 16 (alpha drawn per adapter), 10% of tokens without an adapter."""
+    spec = dict(MOE_DECODE)
+    return moe_case(seed, spec.pop("M"), spec.pop("top_k"), spec.pop("n_experts"),
+                    spec.pop("d_in"), spec.pop("d_out"), spec.pop("n_adapters"),
+                    spec.pop("r_max"), ranks=[16] * 8, **spec)

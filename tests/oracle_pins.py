@@ -34,6 +34,10 @@ What pins what:
     scales the fp8 layer equals the bf16 layer on the same (exactly representable) weights,
     bit for bit; a power-of-two column scale scales the base term exactly; and the fp8 layer
     agrees with numpy float64 on the dequantized weight within the float32 bound.
+  * MoE-LoRA ([P3] "MoE Models Raise the Bar"): one expert, top-1, unit weights is the dense
+    layer bit for bit; every routed slot is the dense layer on that expert's weights and
+    adapter pair times its routing weight, bit for bit; empty slots are zero rows; doubling
+    the routing weights doubles the output exactly; float64 within the float32 bound.
 """
 
 from __future__ import annotations
@@ -77,6 +81,9 @@ class Orc:
 
     def fp8_decode(self, *a, **k):
         return self.mod.fp8_e4m3_decode(*a, lib=self.lib, **k)
+
+    def moe(self, *a, **k):
+        return self.mod.moe_lora_linear(*a, lib=self.lib, **k)
 
 
 def _int_case(seed, M, d_in, d_out, n, r_max, scale_int=2, base_frac=0.25):
@@ -377,7 +384,76 @@ def pin_fp8_float64(orc: Orc) -> None:
     assert np.all(np.abs(y - ref) <= bound)
 
 
+# ---------------------------------------------------------------------------------------
+# MoE-LoRA
+
+
+def _moe(seed, M=9, top_k=2, E=4, d_in=24, d_out=20, n=3, r_max=4, empty=0.2):
+    from synth import moe_case
+
+    return moe_case(seed, M, top_k, E, d_in, d_out, n, r_max, base_frac=0.25, empty_frac=empty,
+                    storage="f32")
+
+
+def pin_moe_single_expert_is_dense(orc: Orc) -> None:
+    from synth import moe_case
+
+    w = moe_case(930, 11, 1, 1, 32, 24, 3, 8, base_frac=0.3, storage="f32")
+    y = orc.moe(w.x, w.W, w.A, w.B, w.alpha, w.ranks, w.ids, w.topk_ids)
+    ref = orc.linear(w.x, w.W[0], w.A[:, 0], w.B[:, 0], w.alpha, w.ranks, w.ids)
+    assert np.array_equal(y[:, 0, :], ref)
+
+
+def pin_moe_slots_are_dense_rows(orc: Orc) -> None:
+    """y[m, j] = w[m, j] * dense(x, W_e, A[:, e], B[:, e])[m] for e = topk_ids[m, j]."""
+    w = _moe(931)
+    y = orc.moe(w.x, w.W, w.A, w.B, w.alpha, w.ranks, w.ids, w.topk_ids, w.topk_w)
+    dense = [orc.linear(w.x, w.W[e], np.ascontiguousarray(w.A[:, e]), np.ascontiguousarray(w.B[:, e]),
+                        w.alpha, w.ranks, w.ids) for e in range(w.n_experts)]
+    for m in range(w.M):
+        for j in range(w.top_k):
+            e = int(w.topk_ids[m, j])
+            if e < 0:
+                assert not np.any(y[m, j])
+            else:
+                assert np.array_equal(y[m, j], w.topk_w[m, j] * dense[e][m])
+    assert (w.topk_ids < 0).any() and (w.topk_ids >= 0).any()
+
+
+def pin_moe_weight_linearity(orc: Orc) -> None:
+    w = _moe(932)
+    y1 = orc.moe(w.x, w.W, w.A, w.B, w.alpha, w.ranks, w.ids, w.topk_ids, w.topk_w)
+    y2 = orc.moe(w.x, w.W, w.A, w.B, w.alpha, w.ranks, w.ids, w.topk_ids, 2 * w.topk_w)
+    y0 = orc.moe(w.x, w.W, w.A, w.B, w.alpha, w.ranks, w.ids, w.topk_ids)
+    assert np.array_equal(y2, 2 * y1)
+    nz = w.topk_ids >= 0
+    assert np.array_equal(y1[nz], w.topk_w[nz][:, None] * y0[nz])
+
+
+def pin_moe_float64(orc: Orc) -> None:
+    w = _moe(933, M=7, top_k=3, E=5, d_in=40, d_out=28, n=4, r_max=8, empty=0.1)
+    y = orc.moe(w.x, w.W, w.A, w.B, w.alpha, w.ranks, w.ids, w.topk_ids, w.topk_w)
+    x, W, A, B = (np.asarray(v, np.float64) for v in (w.x, w.W, w.A, w.B))
+    s = w.alpha.astype(np.float64) / w.ranks
+    for m in range(w.M):
+        for j in range(w.top_k):
+            e = int(w.topk_ids[m, j])
+            if e < 0:
+                assert not np.any(y[m, j])
+                continue
+            i = int(w.ids[m])
+            ref = x[m] @ W[e]
+            mag = np.abs(x[m]) @ np.abs(W[e])
+            if i >= 0:
+                ref = ref + s[i] * ((x[m] @ A[i, e]) @ B[i, e])
+                mag = mag + abs(s[i]) * ((np.abs(x[m]) @ np.abs(A[i, e])) @ np.abs(B[i, e]))
+            ref = ref * float(w.topk_w[m, j])
+            bound = gamma(w.d_in + w.r_max + 6) * mag * abs(float(w.topk_w[m, j])) * 1.001 + 1e-30
+            assert np.all(np.abs(y[m, j] - ref) <= bound)
+
+
 ALL_PINS = [pin_exact_merged_rational, pin_integer_exact, pin_merged_float64,
             pin_single_adapter_float64, pin_base_rows, pin_zero_padding, pin_scale,
             pin_row_permutation, pin_segments, pin_fp8_decode, pin_fp8_equals_bf16_layer,
-            pin_fp8_scale, pin_fp8_float64]
+            pin_fp8_scale, pin_fp8_float64, pin_moe_single_expert_is_dense,
+            pin_moe_slots_are_dense_rows, pin_moe_weight_linearity, pin_moe_float64]

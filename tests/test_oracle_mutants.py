@@ -72,6 +72,21 @@ MUTANTS = [
     ("fp8_delta_dropped",
      "for (int32_t c = 0; c < d_out; ++c) yrow[c] += sc * d[c];",
      "for (int32_t c = 0; c < d_out; ++c) yrow[c] += 0.0f * d[c];"),
+    ("moe_wrong_expert",
+     "const float *We = W + (size_t)e * d_in * d_out;",
+     "const float *We = W + (size_t)((e + 1) % n_experts) * d_in * d_out;"),
+    ("moe_adapter_expert_swapped",
+     "const float *Aie = A + ((size_t)i * n_experts + e) * d_in * r_max;",
+     "const float *Aie = A + ((size_t)e * n_adapters + i) % ((size_t)n_adapters * n_experts) * d_in * r_max;"),
+    ("moe_weight_dropped",
+     "for (int32_t c = 0; c < d_out; ++c) out[c] = wt * out[c];",
+     "for (int32_t c = 0; c < d_out; ++c) out[c] = out[c];"),
+    ("moe_empty_slot_gets_expert0",
+     "if (e < 0) continue; /* empty slot */",
+     "if (e < 0 && n_experts < 0) continue;"),
+    ("moe_delta_unscaled",
+     "for (int32_t c = 0; c < d_out; ++c) out[c] += sa * dq[c];",
+     "for (int32_t c = 0; c < d_out; ++c) out[c] += dq[c];"),
     ("base_rows_first",
      "int32_t base_pos = n_lora_rows;",
      "int32_t base_pos = n_lora_rows; for (int32_t i = 0; i < n_adapters; ++i) { offsets[i] += M - n_lora_rows; cursor[i] += M - n_lora_rows; } base_pos = 0;"),
