@@ -7,6 +7,7 @@ deliberately broken copies of it (test_oracle_mutants.py).
 Sources, cited by title and section:
   [P1] "Multi-LoRA Serving: Why 100 Adapters Fit on One GPU" (dev.to)
   [P2] "Serving Many LoRA Adapters From One Base Model" (ai-tldr.dev)
+  [P3] "Multi-LoRA Serving: Sharing One GPU Across Adapters" (cloudai.pt)
 
 What pins what:
   * merge identity, exact: [P1] "Why can't you just merge LoRA weights into the base
@@ -36,7 +37,8 @@ What pins what:
     agrees with numpy float64 on the dequantized weight within the float32 bound.
   * MoE-LoRA ([P3] "MoE Models Raise the Bar"): one expert, top-1, unit weights is the dense
     layer bit for bit; every routed slot is the dense layer on that expert's weights and
-    adapter pair times its routing weight, bit for bit; empty slots are zero rows; doubling
+    adapter pair times its routing weight, bit for bit; the merged weight W_e + s A_ie B_ie
+    per (expert, adapter) exactly on integer inputs; empty slots are zero rows; doubling
     the routing weights doubles the output exactly; float64 within the float32 bound.
 """
 
@@ -430,6 +432,40 @@ def pin_moe_weight_linearity(orc: Orc) -> None:
     assert np.array_equal(y1[nz], w.topk_w[nz][:, None] * y0[nz])
 
 
+def pin_moe_merged_integer(orc: Orc) -> None:
+    """The merged-weight identity per (expert, adapter), exactly: small-integer inputs,
+    alpha / r in {2, 3} and power-of-two routing weights make every float32 step exact, so
+    y[m, j] = w[m, j] * x_m (W_e + s_i A[i, e] B[i, e]) in int64 arithmetic, bit for bit."""
+    rng = np.random.default_rng(934)
+    for scale_int in (2, 3):
+        M, top_k, E, d_in, d_out, n, r_max = 23, 3, 5, 32, 24, 4, 8
+        x = rng.integers(-3, 4, size=(M, d_in)).astype(np.float32)
+        W = rng.integers(-3, 4, size=(E, d_in, d_out)).astype(np.float32)
+        A = rng.integers(-3, 4, size=(n, E, d_in, r_max)).astype(np.float32)
+        B = rng.integers(-3, 4, size=(n, E, r_max, d_out)).astype(np.float32)
+        ranks = rng.integers(1, r_max + 1, size=n).astype(np.int32)
+        for i, r in enumerate(ranks):
+            A[i, :, :, r:] = 0
+            B[i, :, r:, :] = 0
+        alpha = (scale_int * ranks).astype(np.float32)
+        ids = rng.integers(-1, n, size=M).astype(np.int32)
+        topk = np.stack([rng.permutation(E)[:top_k] for _ in range(M)]).astype(np.int32)
+        topk[rng.random((M, top_k)) < 0.15] = -1
+        tw = (2.0 ** rng.integers(-3, 2, size=(M, top_k))).astype(np.float32)
+        y = orc.moe(x, W, A, B, alpha, ranks, ids, topk, tw)
+        xi, Wi, Ai, Bi = (v.astype(np.int64) for v in (x, W, A, B))
+        for m in range(M):
+            for j in range(top_k):
+                e = int(topk[m, j])
+                if e < 0:
+                    assert not np.any(y[m, j])
+                    continue
+                i = int(ids[m])
+                Wm = Wi[e] + (scale_int * (Ai[i, e] @ Bi[i, e]) if i >= 0 else 0)
+                ref = (xi[m] @ Wm).astype(np.float64) * float(tw[m, j])
+                assert np.array_equal(y[m, j], ref.astype(np.float32)), (scale_int, m, j)
+
+
 def pin_moe_float64(orc: Orc) -> None:
     w = _moe(933, M=7, top_k=3, E=5, d_in=40, d_out=28, n=4, r_max=8, empty=0.1)
     y = orc.moe(w.x, w.W, w.A, w.B, w.alpha, w.ranks, w.ids, w.topk_ids, w.topk_w)
@@ -456,4 +492,5 @@ ALL_PINS = [pin_exact_merged_rational, pin_integer_exact, pin_merged_float64,
             pin_single_adapter_float64, pin_base_rows, pin_zero_padding, pin_scale,
             pin_row_permutation, pin_segments, pin_fp8_decode, pin_fp8_equals_bf16_layer,
             pin_fp8_scale, pin_fp8_float64, pin_moe_single_expert_is_dense,
-            pin_moe_slots_are_dense_rows, pin_moe_weight_linearity, pin_moe_float64]
+            pin_moe_slots_are_dense_rows, pin_moe_weight_linearity, pin_moe_merged_integer,
+            pin_moe_float64]
