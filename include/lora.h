@@ -305,6 +305,51 @@ lora_status_t lora_linear_profiled(const void *x, const void *W, const void *A, 
                                    const char **kernel_names, int32_t max_kernels,
                                    int32_t *n_kernels);
 
+/* MoE-LoRA ([P3], "MoE Models Raise the Bar": in a routed expert layer each adapted
+ * projection of each expert carries the request's adapter, and the adapter's shrink and
+ * expand are folded into the expert-routed kernel, with split-K for the skinny products).
+ * Token m is routed to top_k experts topk_ids[m][j] (-1: the slot has no expert) with
+ * routing weights topk_w[m][j]; it carries adapter ids[m] (-1: the bare base).  Per (token,
+ * slot), with e = topk_ids[m][j] and i = ids[m]:
+ *     y[m][j][:] = topk_w[m][j] * ( x[m] W[e] + scale_i (x[m] A[i][e]) B[i][e] )
+ * (the adapter term only when i >= 0) and y[m][j][:] = 0 for a slot with no expert.  Layouts,
+ * row-major, device memory, 16-byte aligned:
+ *   x         bf16 [M][d_in]                 W   bf16 [n_experts][d_in][d_out]
+ *   A         bf16 [n_adapters][n_experts][d_in][r_max]  (zero past each adapter's rank)
+ *   B         bf16 [n_adapters][n_experts][r_max][d_out] (zero past each adapter's rank)
+ *   scale     fp32 [n_adapters] = alpha_i / r_i;  ranks int32 [n_adapters] (NULL: all r_max)
+ *   ids       int32 [M];  topk_ids int32 [M][top_k];  topk_w fp32 [M][top_k] (NULL: weight 1)
+ *   y         bf16 or fp32 [M][top_k][d_out] (per slot; the caller sums slots if it wants)
+ * Limits: 1 <= top_k <= 64, 1 <= n_experts <= 4096, M * top_k <= LORA_MOE_MAX_PAIRS, d_in a
+ * multiple of 32 and at least 128, d_out a multiple of 8 (else LORA_ERR_SHAPE); r_max a
+ * multiple of 8 in [8, 64] (else LORA_ERR_RANK).  mode: LORA_MODE_AUTO or LORA_MODE_DECODE
+ * (else LORA_ERR_MODE), LORA_MODE_CHECKED may be OR-ed in: it also reports a topk_ids entry
+ * outside [-1, n_experts) as LORA_ERR_BAD_ID.  Without it, such a slot is a zero row and an
+ * id outside [-1, n_adapters) adds no adapter term.  ws: at least lora_moe_workspace_bytes()
+ * of the same sizes, 256-byte aligned, contents need not be initialised.  M = 0 is a no-op.
+ * Two launches on `stream`, no allocation, no host synchronisation (except checked mode). */
+#define LORA_MOE_MAX_PAIRS 8192
+size_t lora_moe_workspace_bytes(int32_t M, int32_t top_k, int32_t n_experts, int32_t d_in,
+                                int32_t d_out, int32_t r_max, int32_t n_adapters);
+lora_status_t lora_moe_linear(const void *x, const void *W, const void *A, const void *B,
+                              const float *scale, const int32_t *ranks, const int32_t *ids,
+                              const int32_t *topk_ids, const float *topk_w, int32_t M,
+                              int32_t top_k, int32_t n_experts, int32_t d_in, int32_t d_out,
+                              int32_t r_max, int32_t n_adapters, void *y, lora_dtype_t y_dtype,
+                              lora_mode_t mode, void *ws, size_t ws_bytes, void *stream);
+
+/* Measurement aid: lora_linear_profiled for lora_moe_linear's arguments. */
+lora_status_t lora_moe_linear_profiled(const void *x, const void *W, const void *A, const void *B,
+                                       const float *scale, const int32_t *ranks,
+                                       const int32_t *ids, const int32_t *topk_ids,
+                                       const float *topk_w, int32_t M, int32_t top_k,
+                                       int32_t n_experts, int32_t d_in, int32_t d_out,
+                                       int32_t r_max, int32_t n_adapters, void *y,
+                                       lora_dtype_t y_dtype, lora_mode_t mode, void *ws,
+                                       size_t ws_bytes, void *stream, float *kernel_ms,
+                                       const char **kernel_names, int32_t max_kernels,
+                                       int32_t *n_kernels);
+
 /* Measurement aid: lora_linear_profiled for lora_linear_compact's arguments. */
 lora_status_t lora_linear_compact_profiled(
     const void *x, const void *W, const void *A, const void *B, const float *scale,

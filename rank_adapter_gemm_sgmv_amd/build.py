@@ -22,7 +22,7 @@ OBJ_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "liblora_mi355x.so")
 ARCH = "gfx950"
 
-SOURCES = ["segments.hip", "shrink.hip", "expand.hip", "gemm.hip", "gemm_big.hip", "decode_gemm.hip", "noalloc.hip", "api.cpp"]
+SOURCES = ["segments.hip", "shrink.hip", "expand.hip", "gemm.hip", "gemm_big.hip", "decode_gemm.hip", "moe.hip", "noalloc.hip", "api.cpp"]
 
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall",

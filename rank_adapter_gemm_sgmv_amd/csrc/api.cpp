@@ -681,11 +681,166 @@ lora_status_t lora_linear_fp8w_profiled(const void *x, const void *W8, const flo
         kernel_ms, kernel_names, max_kernels, n_kernels);
 }
 
+}  // extern "C"
+
+namespace {
+
+// ---- MoE-LoRA ----------------------------------------------------------------------------
+
+lora_status_t check_moe_sizes(int32_t M, int32_t top_k, int32_t n_experts, int32_t d_in,
+                              int32_t d_out, int32_t r_max, int32_t n_adapters) {
+    if (M < 0 || top_k < 1 || top_k > 64 || n_experts < 1 || n_experts > 4096 ||
+        (int64_t)M * top_k > LORA_MOE_MAX_PAIRS || n_adapters < 1 ||
+        n_adapters > LORA_MAX_ADAPTERS)
+        return LORA_ERR_SHAPE;
+    if (!dim_ok(d_in) || !dim_ok(d_out) || d_in % 32 != 0 || d_in < 128) return LORA_ERR_SHAPE;
+    if (r_max < 8 || r_max > 64 || r_max % 8 != 0) return LORA_ERR_RANK;
+    return LORA_OK;
+}
+
+size_t moe_ws_bytes(int32_t M, int32_t top_k, int32_t n_experts, int32_t d_in, int32_t d_out,
+                    int32_t r_max, int32_t n_adapters) {
+    const MoePlan p = moe_plan(M, top_k, n_experts, d_in, d_out, r_max, n_adapters);
+    const int P = M * top_k;
+    return round_up(moe_partial_floats(p, P) * 4) + round_up(moe_tpart_floats(p, P) * 4);
+}
+
+lora_status_t check_moe(const void *x, const void *W, const void *A, const void *B,
+                        const float *scale, const int32_t *ranks, const int32_t *ids,
+                        const int32_t *topk_ids, const float *topk_w, int32_t M, int32_t top_k,
+                        int32_t n_experts, int32_t d_in, int32_t d_out, int32_t r_max,
+                        int32_t n_adapters, void *y, lora_dtype_t y_dtype, lora_mode_t mode,
+                        void *ws, size_t ws_bytes) {
+    lora_status_t st = check_moe_sizes(M, top_k, n_experts, d_in, d_out, r_max, n_adapters);
+    if (st != LORA_OK) return st;
+    if (y_dtype != LORA_BF16 && y_dtype != LORA_F32) return LORA_ERR_DTYPE;
+    const int bm = mode & ~LORA_MODE_CHECKED;
+    if (bm != LORA_MODE_AUTO && bm != LORA_MODE_DECODE) return LORA_ERR_MODE;
+    if (M == 0) return LORA_OK;
+    if (!x || !W || !A || !B || !scale || !ids || !topk_ids || !y || !ws) return LORA_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(W, 16) || !aligned(A, 16) || !aligned(B, 16) ||
+        !aligned(y, 16) || !aligned(ws, kAlign) || !aligned(scale, 4) || !aligned(ids, 4) ||
+        !aligned(topk_ids, 4) || (topk_w && !aligned(topk_w, 4)) || (ranks && !aligned(ranks, 4)))
+        return LORA_ERR_ALIGN;
+    if (ws_bytes < moe_ws_bytes(M, top_k, n_experts, d_in, d_out, r_max, n_adapters))
+        return LORA_ERR_WORKSPACE;
+    return LORA_OK;
+}
+
+// Checked mode of lora_moe_linear: ids and ranks as lora_linear's, and every topk_ids entry
+// in [-1, n_experts).
+lora_status_t check_moe_tables(const int32_t *ids, const int32_t *ranks, const int32_t *topk_ids,
+                               int32_t M, int32_t top_k, int32_t n_experts, int32_t r_max,
+                               int32_t n_adapters, hipStream_t s) {
+    lora_status_t st = check_tables(ids, M, ranks, nullptr, 0, r_max, n_adapters, s);
+    if (st != LORA_OK) return st;
+    std::vector<int32_t> h((size_t)M * top_k);
+    hipError_t e = hipMemcpy(h.data(), topk_ids, h.size() * 4, hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_status(e);
+    for (int32_t v : h)
+        if (v < -1 || v >= n_experts) return LORA_ERR_BAD_ID;
+    return LORA_OK;
+}
+
+// The launch sequence of lora_moe_linear (arguments validated, M > 0): the expert-routed
+// split-K GEMM with the adapters' A as extra column tiles, then the reduction with the expand
+// and the routing weight.
+hipError_t run_moe(const void *x, const void *W, const void *A, const void *B, const float *scale,
+                   const int32_t *ranks, const int32_t *ids, const int32_t *topk_ids,
+                   const float *topk_w, int32_t M, int32_t top_k, int32_t n_experts, int32_t d_in,
+                   int32_t d_out, int32_t r_max, int32_t n_adapters, void *y,
+                   lora_dtype_t y_dtype, void *ws, hipStream_t s, Marker *mk) {
+    const MoePlan p = moe_plan(M, top_k, n_experts, d_in, d_out, r_max, n_adapters);
+    const int P = M * top_k;
+    char *c = static_cast<char *>(ws);
+    float *partial = reinterpret_cast<float *>(c);
+    c += round_up(moe_partial_floats(p, P) * 4);
+    float *tpart = reinterpret_cast<float *>(c);
+    MoeGemmArgs g{};
+    g.x = static_cast<const uint16_t *>(x);
+    g.W = static_cast<const uint16_t *>(W);
+    g.A = static_cast<const uint16_t *>(A);
+    g.topk_ids = topk_ids;
+    g.ids = ids;
+    g.P = P; g.top_k = top_k; g.E = n_experts; g.K = d_in; g.N = d_out;
+    g.r_stride = r_max; g.n_adapters = n_adapters;
+    g.partial = partial;
+    g.tpart = tpart;
+    hipError_t e = launch_moe_gemm(p, g, s);
+    if (e != hipSuccess) return e;
+    mark(mk, "moe_gemm");
+    MoeReduceArgs r{};
+    r.partial = partial; r.tpart = tpart;
+    r.B = static_cast<const uint16_t *>(B);
+    r.scale = scale; r.ranks = ranks; r.topk_ids = topk_ids; r.ids = ids; r.topk_w = topk_w;
+    r.P = P; r.top_k = top_k; r.E = n_experts; r.N = d_out; r.r_stride = r_max;
+    r.n_adapters = n_adapters;
+    r.y = y;
+    if ((e = launch_moe_reduce(p, r, y_dtype == LORA_F32, s)) != hipSuccess) return e;
+    mark(mk, "moe_reduce");
+    return hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t lora_moe_workspace_bytes(int32_t M, int32_t top_k, int32_t n_experts, int32_t d_in,
+                                int32_t d_out, int32_t r_max, int32_t n_adapters) {
+    if (check_moe_sizes(M, top_k, n_experts, d_in, d_out, r_max, n_adapters) != LORA_OK || M == 0)
+        return 0;
+    return moe_ws_bytes(M, top_k, n_experts, d_in, d_out, r_max, n_adapters);
+}
+
+lora_status_t lora_moe_linear(const void *x, const void *W, const void *A, const void *B,
+                              const float *scale, const int32_t *ranks, const int32_t *ids,
+                              const int32_t *topk_ids, const float *topk_w, int32_t M,
+                              int32_t top_k, int32_t n_experts, int32_t d_in, int32_t d_out,
+                              int32_t r_max, int32_t n_adapters, void *y, lora_dtype_t y_dtype,
+                              lora_mode_t mode, void *ws, size_t ws_bytes, void *stream) {
+    lora_status_t st = check_moe(x, W, A, B, scale, ranks, ids, topk_ids, topk_w, M, top_k,
+                                 n_experts, d_in, d_out, r_max, n_adapters, y, y_dtype, mode, ws,
+                                 ws_bytes);
+    if (st != LORA_OK || M == 0) return st;
+    clear_stale_error();
+    if ((mode & LORA_MODE_CHECKED) &&
+        (st = check_moe_tables(ids, ranks, topk_ids, M, top_k, n_experts, r_max, n_adapters,
+                               (hipStream_t)stream)) != LORA_OK)
+        return st;
+    return hip_status(run_moe(x, W, A, B, scale, ranks, ids, topk_ids, topk_w, M, top_k, n_experts,
+                              d_in, d_out, r_max, n_adapters, y, y_dtype, ws, (hipStream_t)stream,
+                              nullptr));
+}
+
+lora_status_t lora_moe_linear_profiled(const void *x, const void *W, const void *A, const void *B,
+                                       const float *scale, const int32_t *ranks,
+                                       const int32_t *ids, const int32_t *topk_ids,
+                                       const float *topk_w, int32_t M, int32_t top_k,
+                                       int32_t n_experts, int32_t d_in, int32_t d_out,
+                                       int32_t r_max, int32_t n_adapters, void *y,
+                                       lora_dtype_t y_dtype, lora_mode_t mode, void *ws,
+                                       size_t ws_bytes, void *stream, float *kernel_ms,
+                                       const char **kernel_names, int32_t max_kernels,
+                                       int32_t *n_kernels) {
+    if (!kernel_ms || !kernel_names || !n_kernels || max_kernels < 0) return LORA_ERR_NULL;
+    *n_kernels = 0;
+    lora_status_t st = check_moe(x, W, A, B, scale, ranks, ids, topk_ids, topk_w, M, top_k,
+                                 n_experts, d_in, d_out, r_max, n_adapters, y, y_dtype, mode, ws,
+                                 ws_bytes);
+    if (st != LORA_OK || M == 0) return st;
+    return time_launches(
+        [&](Marker *mk) {
+            return run_moe(x, W, A, B, scale, ranks, ids, topk_ids, topk_w, M, top_k, n_experts,
+                           d_in, d_out, r_max, n_adapters, y, y_dtype, ws, (hipStream_t)stream, mk);
+        },
+        kernel_ms, kernel_names, max_kernels, n_kernels);
+}
+
 const char *lora_status_string(lora_status_t status) {
     switch (status) {
         case LORA_OK: return "LORA_OK";
         case LORA_ERR_NULL: return "LORA_ERR_NULL: a required pointer is NULL";
-        case LORA_ERR_SHAPE: return "LORA_ERR_SHAPE: M, d_in, d_out or n_adapters out of range";
+        case LORA_ERR_SHAPE: return "LORA_ERR_SHAPE: M, d_in, d_out, n_adapters (or top_k, n_experts) out of range";
         case LORA_ERR_RANK: return "LORA_ERR_RANK: r_max outside [1, 64], or (checked mode) a rank outside [1, r_max]";
         case LORA_ERR_ALIGN: return "LORA_ERR_ALIGN: a pointer is not aligned as required";
         case LORA_ERR_WORKSPACE:
@@ -693,7 +848,7 @@ const char *lora_status_string(lora_status_t status) {
                    "the call needs more than LORA_NOALLOC_SCRATCH_BYTES of scratch)";
         case LORA_ERR_DTYPE: return "LORA_ERR_DTYPE: unknown output dtype";
         case LORA_ERR_HIP: return "LORA_ERR_HIP: a kernel launch failed";
-        case LORA_ERR_BAD_ID: return "LORA_ERR_BAD_ID: adapter id out of range";
+        case LORA_ERR_BAD_ID: return "LORA_ERR_BAD_ID: (checked mode) adapter id or expert id out of range";
         case LORA_ERR_MODE: return "LORA_ERR_MODE: unknown mode";
         case LORA_ERR_POOL: return "LORA_ERR_POOL: (checked mode) an adapter's rank rows leave the compact pool";
     }

@@ -248,6 +248,42 @@ size_t gemm_partial_floats(int M, int K, int N);
 // Split-K plan of the shrink for d_in.
 void shrink_plan(int d_in, int r_max, int *kc, int *ksplit);
 
+// ---- MoE-LoRA (csrc/moe.hip) ---------------------------------------------------------------
+// Plan: tiles of 128 columns (n_tn of W[e], n_lt adapter tiles of 128 / rm adapters), K cut
+// into ks splits of k_per_split; pairs in blocks of bm rows; partial rows np floats apart.
+struct MoePlan {
+    int rm, bm, n_tn, n_lt, ks, k_per_split, np;
+};
+MoePlan moe_plan(int M, int top_k, int E, int K, int N, int r_max, int n_adapters);
+size_t moe_partial_floats(const MoePlan &p, int P);  // [ks][P][np]
+size_t moe_tpart_floats(const MoePlan &p, int P);    // [ks][P][rm]
+
+struct MoeGemmArgs {
+    const uint16_t *x;         // [M][K]
+    const uint16_t *W;         // [E][K][N]
+    const uint16_t *A;         // [n_adapters][E][K][r_stride]
+    const int32_t *topk_ids;   // [P] = [M][top_k]
+    const int32_t *ids;        // [M]
+    int P, top_k, E, K, N, r_stride, n_adapters;
+    int n_tn, n_lt, k_per_split, np;  // set from the plan by launch_moe_gemm
+    float *partial;            // [ks][P][np]
+    float *tpart;              // [ks][P][rm]
+};
+struct MoeReduceArgs {
+    const float *partial, *tpart;
+    const uint16_t *B;         // [n_adapters][E][r_stride][N]
+    const float *scale;        // [n_adapters]
+    const int32_t *ranks;      // [n_adapters] or nullptr (= r_stride)
+    const int32_t *topk_ids;   // [P]
+    const int32_t *ids;        // [M]
+    const float *topk_w;       // [P] or nullptr (= 1)
+    int P, top_k, E, N, r_stride, n_adapters;
+    int ks, np;                // set from the plan by launch_moe_reduce
+    void *y;                   // [P][N]
+};
+hipError_t launch_moe_gemm(const MoePlan &p, const MoeGemmArgs &a, hipStream_t s);
+hipError_t launch_moe_reduce(const MoePlan &p, const MoeReduceArgs &a, bool y_f32, hipStream_t s);
+
 // Records e as the error lora_last_hip_error() reports; LORA_ERR_HIP unless e is hipSuccess.
 lora_status_t hip_error_status(hipError_t e);
 

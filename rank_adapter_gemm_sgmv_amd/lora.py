@@ -21,6 +21,7 @@ LORA_MAX_ADAPTERS = 16384
 LORA_MAX_ROWS = 1 << 22
 LORA_PREFILL_MIN_ROWS = 768
 LORA_NOALLOC_SCRATCH_BYTES = 32 << 20
+LORA_MOE_MAX_PAIRS = 8192
 
 LORA_BF16, LORA_F32 = 0, 1
 LORA_MODE_AUTO, LORA_MODE_DECODE, LORA_MODE_PREFILL = 0, 1, 2
@@ -37,6 +38,7 @@ EXPORTS = ("lora_max_tiles", "lora_workspace_bytes", "lora_build_segments", "lor
            "lora_shrink_compact", "lora_expand", "lora_expand_compact", "lora_linear",
            "lora_linear_profiled", "lora_linear_compact", "lora_linear_compact_profiled",
            "lora_linear_noalloc", "lora_linear_fp8w", "lora_linear_fp8w_profiled",
+           "lora_moe_workspace_bytes", "lora_moe_linear", "lora_moe_linear_profiled",
            "lora_status_string", "lora_last_hip_error")
 
 
@@ -94,6 +96,14 @@ def _load():
     lib.lora_linear_fp8w_profiled.argtypes = lib.lora_linear_fp8w.argtypes + [
         ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_char_p), I, ctypes.POINTER(I)]
     lib.lora_linear_fp8w_profiled.restype = ctypes.c_int
+    lib.lora_moe_workspace_bytes.argtypes = [I, I, I, I, I, I, I]
+    lib.lora_moe_workspace_bytes.restype = S
+    lib.lora_moe_linear.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, P,
+                                    ctypes.c_int, ctypes.c_int, P, S, P]
+    lib.lora_moe_linear.restype = ctypes.c_int
+    lib.lora_moe_linear_profiled.argtypes = lib.lora_moe_linear.argtypes + [
+        ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_char_p), I, ctypes.POINTER(I)]
+    lib.lora_moe_linear_profiled.restype = ctypes.c_int
     lib.lora_linear_noalloc.argtypes = lib.lora_linear.argtypes[:16] + [P]
     lib.lora_linear_noalloc.restype = ctypes.c_int
     lib.lora_linear_profiled.argtypes = lib.lora_linear.argtypes + [
@@ -236,6 +246,47 @@ def lora_linear_fp8w_profiled(x, W8, w_scale, A, B, scale, ranks, ids, M: int, d
         d_in, d_out, r_max, n_adapters, seg_p, _ptr(y), y_dtype, mode, _ptr(ws), ws_bytes,
         _stream(stream), ms, names, max_kernels, ctypes.byref(n)), "lora_linear_fp8w_profiled")
     return [(names[i].decode(), float(ms[i])) for i in range(n.value)]
+
+
+def lora_moe_workspace_bytes(M: int, top_k: int, n_experts: int, d_in: int, d_out: int,
+                             r_max: int, n_adapters: int) -> int:
+    return int(_lib.lora_moe_workspace_bytes(M, top_k, n_experts, d_in, d_out, r_max, n_adapters))
+
+
+def lora_moe_linear(x, W, A, B, scale, ranks, ids, topk_ids, topk_w, M: int, top_k: int,
+                    n_experts: int, d_in: int, d_out: int, r_max: int, n_adapters: int, y,
+                    y_dtype: int, mode: int, ws, ws_bytes: int, stream=None) -> None:
+    """MoE-LoRA: y[M, top_k, d_out] per (token, slot); W[E, d_in, d_out], A[n, E, d_in, r_max],
+    B[n, E, r_max, d_out], topk_ids[M, top_k] (-1: empty slot), topk_w[M, top_k] or None."""
+    _check(_lib.lora_moe_linear(_ptr(x), _ptr(W), _ptr(A), _ptr(B), _ptr(scale), _ptr(ranks),
+                                _ptr(ids), _ptr(topk_ids), _ptr(topk_w), M, top_k, n_experts, d_in,
+                                d_out, r_max, n_adapters, _ptr(y), y_dtype, mode, _ptr(ws),
+                                ws_bytes, _stream(stream)), "lora_moe_linear")
+
+
+def lora_moe_linear_profiled(x, W, A, B, scale, ranks, ids, topk_ids, topk_w, M: int, top_k: int,
+                             n_experts: int, d_in: int, d_out: int, r_max: int, n_adapters: int,
+                             y, y_dtype: int, mode: int, ws, ws_bytes: int, stream=None,
+                             max_kernels: int = 16):
+    """lora_moe_linear with per-kernel HIP event timing; returns [(kernel name, ms), ...]."""
+    ms = (ctypes.c_float * max_kernels)()
+    names = (ctypes.c_char_p * max_kernels)()
+    n = ctypes.c_int32(0)
+    _check(_lib.lora_moe_linear_profiled(
+        _ptr(x), _ptr(W), _ptr(A), _ptr(B), _ptr(scale), _ptr(ranks), _ptr(ids), _ptr(topk_ids),
+        _ptr(topk_w), M, top_k, n_experts, d_in, d_out, r_max, n_adapters, _ptr(y), y_dtype, mode,
+        _ptr(ws), ws_bytes, _stream(stream), ms, names, max_kernels, ctypes.byref(n)),
+        "lora_moe_linear_profiled")
+    return [(names[i].decode(), float(ms[i])) for i in range(n.value)]
+
+
+def moe_workspace(M: int, top_k: int, n_experts: int, d_in: int, d_out: int, r_max: int,
+                  n_adapters: int, device="cuda"):
+    """A uint8 device tensor of lora_moe_workspace_bytes() bytes (256-byte aligned by torch)."""
+    import torch
+
+    nbytes = lora_moe_workspace_bytes(M, top_k, n_experts, d_in, d_out, r_max, n_adapters)
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device), nbytes
 
 
 def lora_linear_noalloc(x, W, A, B, scale, ranks, ids, M: int, d_in: int, d_out: int, r_max: int,

@@ -206,3 +206,39 @@ def test_linear_fp8w_rejects(over, code):
     with pytest.raises(L.LoraError) as e:
         L.lora_linear_fp8w(**args)
     assert e.value.status == code
+
+
+def test_moe_workspace_bytes():
+    b = L.lora_moe_workspace_bytes(64, 4, 32, 2880, 2880, 16, 8)
+    assert b > 0 and b % 256 == 0
+    assert L.lora_moe_workspace_bytes(0, 4, 32, 2880, 2880, 16, 8) == 0
+    assert L.lora_moe_workspace_bytes(64, 4, 32, 2880, 2880, 12, 8) == 0  # r_max % 8
+    assert L.lora_moe_workspace_bytes(2049, 4, 32, 2880, 2880, 16, 8) == 0  # pairs > max
+    assert L.lora_moe_workspace_bytes(2048, 4, 32, 2880, 2880, 16, 8) > b
+    assert L.lora_moe_workspace_bytes(64, 4, 32, 96, 2880, 16, 8) == 0  # d_in < 128
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(M=-1), 2), (dict(top_k=0), 2), (dict(top_k=65), 2), (dict(n_experts=0), 2),
+    (dict(n_experts=4097), 2), (dict(M=L.LORA_MOE_MAX_PAIRS // 4 + 1), 2), (dict(d_in=96), 2),
+    (dict(d_in=2888), 2), (dict(d_out=2884), 2), (dict(n_adapters=0), 2),
+    (dict(r_max=12), 3), (dict(r_max=4), 3), (dict(r_max=72), 3),
+    (dict(mode=L.LORA_MODE_PREFILL), 9), (dict(mode=6), 9), (dict(y_dtype=3), 6),
+    (dict(topk_ids=None), 1), (dict(W=None), 1), (dict(ids=None), 1),
+    (dict(topk_w=FAKE + 2), 4), (dict(W=FAKE + 8), 4), (dict(ws=FAKE + 64), 4),
+    (dict(ws_bytes=1024), 5),
+])
+def test_moe_linear_rejects(over, code):
+    args = dict(x=FAKE, W=FAKE, A=FAKE, B=FAKE, scale=FAKE, ranks=None, ids=FAKE, topk_ids=FAKE,
+                topk_w=FAKE, M=64, top_k=4, n_experts=32, d_in=2880, d_out=2880, r_max=16,
+                n_adapters=8, y=FAKE, y_dtype=L.LORA_BF16, mode=L.LORA_MODE_DECODE, ws=FAKE,
+                ws_bytes=L.lora_moe_workspace_bytes(64, 4, 32, 2880, 2880, 16, 8), stream=0)
+    args.update(over)
+    with pytest.raises(L.LoraError) as e:
+        L.lora_moe_linear(**args)
+    assert e.value.status == code
+
+
+def test_moe_empty_batch_is_noop():
+    L.lora_moe_linear(FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, None, 0, 4, 32, 2880, 2880,
+                      16, 8, None, L.LORA_BF16, L.LORA_MODE_DECODE, None, 0, stream=0)
