@@ -17,7 +17,9 @@ Also reported, outside that timed region: the spread of further replays of the s
 write evicts L2 and the Infinity Cache before each call; warm: the same call repeated), the
 roofline of the dominant kernel (HIP-event duration per launch, algorithmic bytes or flops
 per launch), the CPU oracle timed on the host on every workload, a per-kernel breakdown,
-the other decode and prefill workloads under "workloads", and three sweeps: step time
+the other decode and prefill workloads under "workloads", the MoE-LoRA decode workload
+(lora_moe_linear: 64 tokens routed top-4 over 32 experts of 2880 x 2880, 8 adapters of rank
+16) under "moe" with its own roofline and oracle time, and three sweeps: step time
 against the number of distinct adapters in a 64-row batch, against the adapters' rank, and
 decode against prefill sequence over the batch size (where LORA_MODE_AUTO switches).
 """
@@ -558,6 +560,155 @@ def run_workload(config, mode_name, steps, warmup, torch, profile_reps=20, compa
 
 
 # ---------------------------------------------------------------------------------------
+# MoE-LoRA
+# ---------------------------------------------------------------------------------------
+
+
+def moe_work(w, y_bytes: int = 2) -> dict:
+    """Algorithmic bytes / flops of one lora_moe_linear call (per kernel).  Counted once:
+    W[e] of every expert some slot is routed to, A[i][e] and B[i][e] of every (adapter,
+    expert) pair some token uses (at the adapter's true rank), x, y (every slot row).  Split
+    partial sums are not counted."""
+    E, M, K, N = w.n_experts, w.M, w.d_in, w.d_out
+    topk = w.topk_ids
+    routed = topk >= 0
+    active = np.unique(topk[routed])
+    pairs = set()
+    r_rows = 0
+    for m in range(M):
+        i = int(w.ids[m])
+        for e in topk[m][topk[m] >= 0]:
+            if i >= 0:
+                pairs.add((i, int(e)))
+                r_rows += int(w.ranks[i])
+    r_pairs = sum(int(w.ranks[i]) for i, _ in pairs)
+    n_routed = int(routed.sum())
+    w_bytes = len(active) * K * N * 2
+    a_bytes = r_pairs * K * 2
+    b_bytes = r_pairs * N * 2
+    x_bytes = M * K * 2
+    y_out = M * w.top_k * N * y_bytes
+    base_flops = 2.0 * n_routed * K * N
+    return {
+        "moe_gemm": {"bytes": w_bytes + a_bytes + x_bytes, "flops": base_flops + 2.0 * r_rows * K},
+        "moe_reduce": {"bytes": b_bytes + y_out, "flops": 2.0 * r_rows * N},
+        "call_bytes": w_bytes + a_bytes + b_bytes + x_bytes + y_out,
+        "active_experts": int(len(active)), "adapter_expert_pairs": len(pairs),
+        "routed_slots": n_routed,
+    }
+
+
+class MoeRunner:
+    """The MoE workload on the device: L copies of (W, A, B) cycled step by step (more bytes
+    than the Infinity Cache), shared routing and ids; `step(i)` = one lora_moe_linear call."""
+
+    def __init__(self, w, torch, L):
+        self.torch, self.w, self.L = torch, w, L
+        self.layers = [(_bf16(w.W, torch), _bf16(w.A, torch), _bf16(w.B, torch)) for _ in range(L)]
+        self.x = _bf16(w.x, torch)
+        self.ids = torch.from_numpy(w.ids.astype(np.int32)).cuda()
+        self.ranks = torch.from_numpy(w.ranks.astype(np.int32)).cuda()
+        self.scale = torch.from_numpy((w.alpha / w.ranks.astype(np.float32)).astype(np.float32)).cuda()
+        self.topk = torch.from_numpy(w.topk_ids.astype(np.int32)).cuda()
+        self.topk_w = torch.from_numpy(w.topk_w.astype(np.float32)).cuda()
+        self.ys = [torch.empty((w.M, w.top_k, w.d_out), dtype=torch.bfloat16, device="cuda")]
+        self.ws, self.ws_bytes = L_.moe_workspace(w.M, w.top_k, w.n_experts, w.d_in, w.d_out,
+                                                  w.r_max, w.n_adapters)
+
+    def _args(self, i):
+        W, A, B = self.layers[i % self.L]
+        w = self.w
+        return (self.x, W, A, B, self.scale, self.ranks, self.ids, self.topk, self.topk_w, w.M,
+                w.top_k, w.n_experts, w.d_in, w.d_out, w.r_max, w.n_adapters, self.ys[0],
+                L_.LORA_BF16, L_.LORA_MODE_DECODE, self.ws, self.ws_bytes)
+
+    def step(self, i):
+        L_.lora_moe_linear(*self._args(i))
+
+    def profile(self, i):
+        self.torch.cuda._sleep(2_000_000)
+        return [L_.lora_moe_linear_profiled(*self._args(i))]
+
+
+def moe_layers_needed(w) -> int:
+    per = w.W.nbytes + w.A.nbytes + w.B.nbytes
+    return max(2, -(-ROTATE_BYTES // per))
+
+
+def run_moe(steps, warmup, torch, profile_reps=20, call_reps=50):
+    """The MoE decode workload: graph of `steps` calls, spread, single calls, per-kernel
+    durations, the same calls with every id -1, the roofline of the routed GEMM."""
+    from synth import make_moe_workload
+
+    w = make_moe_workload()
+    L = moe_layers_needed(w)
+    runner = MoeRunner(w, torch, L)
+    log(f"bench: {w.name} layers={L} steps={steps}")
+    ms_total, wall, eager_ms, kernels, reps, calls = measure(runner, steps, warmup, torch,
+                                                             profile_reps, call_reps=call_reps)
+    ks = {name: ms for (_, name), ms in kernels.items()}
+    work = moe_work(w)
+    ms_step = ms_total / steps
+    keep = runner.ids
+    runner.ids = torch.full_like(keep, -1)
+    try:
+        g = capture(runner, steps, torch)
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        g.replay()
+        ev1.record()
+        torch.cuda.synchronize()
+        base_ms = ev0.elapsed_time(ev1) / steps
+        del g
+    finally:
+        runner.ids = keep
+    g_ms = ks.get("moe_gemm")
+    roof = None
+    if g_ms:
+        achieved = work["moe_gemm"]["bytes"] / (g_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "kernel": "moe_gemm", "us_per_launch": g_ms * 1e3,
+                "algorithmic_per_launch": work["moe_gemm"]["bytes"],
+                "traffic": committed_traffic(w.name, "moe_gemm")}
+    out = {
+        "workload": w.name, "M": w.M, "top_k": w.top_k, "n_experts": w.n_experts,
+        "d_in": w.d_in, "d_out": w.d_out, "n_adapters": w.n_adapters, "r_max": w.r_max,
+        "layers_rotated": L, "steps": steps,
+        "tokens_per_s": w.M * steps / (ms_total * 1e-3),
+        "ms_per_step": ms_step, "ms_per_step_eager": eager_ms,
+        "ms_per_step_replays": reps, "us_per_call": calls,
+        "kernels_us": {k: round(v * 1e3, 2) for k, v in ks.items()},
+        "base_only_ms_per_step": base_ms,
+        "lora_overhead_vs_base_only": ms_step / base_ms - 1.0,
+        "call_hbm_frac": work["call_bytes"] / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "algorithmic": {k: v for k, v in work.items() if not isinstance(v, dict)},
+        "roofline": roof,
+    }
+    del runner
+    torch.cuda.empty_cache()
+    return w, out
+
+
+def moe_cpu_baseline(w, threads: int, seconds: float = 3.0):
+    """The oracle's MoE layer on the host: full-batch calls for about `seconds` (inputs
+    widened to fp32 outside the timing)."""
+    import oracle
+    from synth import bf16_bits_to_f32
+
+    xf, Wf, Af, Bf = (bf16_bits_to_f32(v) for v in (w.x, w.W, w.A, w.B))
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.moe_lora_linear(xf, Wf, Af, Bf, w.alpha, w.ranks, w.ids, w.topk_ids, w.topk_w,
+                               n_threads=threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": w.M * reps / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"the full {w.M}-token batch of {w.name}, {reps} oracle calls in {el:.1f} s"}
+
+
+# ---------------------------------------------------------------------------------------
 # sweeps
 # ---------------------------------------------------------------------------------------
 
@@ -623,18 +774,23 @@ def sweeps(torch, steps=32):
 CALIB_BYTES = 256 << 20
 
 
-def pmc_pass(config, mode_name, steps, torch, compact=False):
+def pmc_pass(config, mode_name, steps, torch, compact=False, moe=False):
     """Eager steps of one workload, then the counter calibration kernel: torch.neg over
     CALIB_BYTES of bf16 (reads CALIB_BYTES, writes CALIB_BYTES), three times.  Meant to run
     under ``rocprofv3 --pmc``; no timing."""
-    from synth import make_workload
+    from synth import make_moe_workload, make_workload
 
-    w = make_workload(config).as_bf16()
-    prefill = mode_name == "prefill"
-    mode = L_.LORA_MODE_PREFILL if prefill else L_.LORA_MODE_DECODE
-    L = layers_needed(w, prefill, compact)
-    runner = Runner(w, mode, torch, L, rotate_x=prefill, prebuilt_segments=len(w.projections) > 1,
-                    compact=compact)
+    if moe:
+        w = make_moe_workload()
+        L = moe_layers_needed(w)
+        runner = MoeRunner(w, torch, L)
+    else:
+        w = make_workload(config).as_bf16()
+        prefill = mode_name == "prefill"
+        mode = L_.LORA_MODE_PREFILL if prefill else L_.LORA_MODE_DECODE
+        L = layers_needed(w, prefill, compact)
+        runner = Runner(w, mode, torch, L, rotate_x=prefill,
+                        prebuilt_segments=len(w.projections) > 1, compact=compact)
     for i in range(steps):
         runner.step(i)
     torch.cuda.synchronize()
@@ -665,6 +821,9 @@ def main():
     ap.add_argument("--compact", action="store_true",
                     help="serve the headline (or --pmc-pass) workload from its rank-compact pool "
                          "(lora_linear_compact)")
+    ap.add_argument("--moe", action="store_true",
+                    help="only the MoE-LoRA decode workload (its own JSON line; with --pmc-pass, "
+                         "its counter pass)")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="only eager steps of the chosen workload plus the counter calibration "
                          "kernel, for rocprofv3 --pmc runs (FETCH_SIZE / WRITE_SIZE)")
@@ -682,7 +841,12 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     if args.pmc_pass:
-        pmc_pass(args.workload, args.mode, args.steps, torch, args.compact)
+        pmc_pass(args.workload, args.mode, args.steps, torch, args.compact, args.moe)
+        return
+    if args.moe:
+        mw, moe = run_moe(args.steps, args.warmup, torch)
+        print(json.dumps({"moe": moe, "cpu_baseline": moe_cpu_baseline(mw, host_threads(), args.cpu_seconds)
+                          if args.cpu_seconds > 0 else None}), flush=True)
         return
 
     # headline: decode, q_proj geometry (unless another workload is asked for)
@@ -707,6 +871,16 @@ def main():
             except Exception as e:  # report, do not hide the headline
                 workloads[f"config{cfg}:{mode_name}"] = {"error": repr(e)}
             torch.cuda.empty_cache()
+
+    moe = None
+    if not args.headline_only:
+        try:
+            mw, moe = run_moe(64, 4, torch, profile_reps=8, call_reps=20)
+            if args.cpu_seconds > 0:
+                moe["cpu_baseline"] = moe_cpu_baseline(mw, host_threads(), min(args.cpu_seconds, 3.0))
+        except Exception as e:  # report, do not hide the headline
+            moe = {"error": repr(e)}
+        torch.cuda.empty_cache()
 
     sw = None
     if not args.headline_only and not args.no_sweeps:
@@ -745,6 +919,7 @@ def main():
                    "us_per_call": head["us_per_call"]},
         "headline_detail": head,
         "workloads": workloads,
+        "moe": moe,
         "sweeps": sw,
     }
     print(json.dumps(line), flush=True)

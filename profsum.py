@@ -44,6 +44,8 @@ _STEP_OF_KERNEL = [
     ("gemm_big_kernel", "gemm"),
     ("gemm_kernel", "gemm"),
     ("gemm_sk_kernel", "gemm"),
+    ("moe_gemm_kernel", "moe_gemm"),
+    ("moe_reduce_kernel", "moe_reduce"),
 ]
 _CALIB = "neg_kernel"
 
@@ -80,14 +82,34 @@ def step_of(kernel_name: str, mode: str, separate_shrink: bool = False):
     return None
 
 
+def dispatch_medians(trace_csv: str) -> dict:
+    """Median duration (ns) per kernel name over the dispatches of a kernel-trace CSV."""
+    by = {}
+    for r in csv.DictReader(open(trace_csv)):
+        by.setdefault(r["Kernel_Name"], []).append(
+            float(r["End_Timestamp"]) - float(r["Start_Timestamp"]))
+    out = {}
+    for k, v in by.items():
+        v = sorted(v)
+        n = len(v)
+        out[k] = v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
+    return out
+
+
 def trace_table(stats_csv: str, title: str, command: str) -> str:
+    """The stats CSV as a table; with the kernel-trace CSV beside it (same prefix), a median
+    column too (the average also counts the cold calls the benchmark makes on purpose)."""
     rows = list(csv.DictReader(open(stats_csv)))
+    trace = stats_csv.replace("_kernel_stats.csv", "_kernel_trace.csv")
+    med = dispatch_medians(trace) if trace != stats_csv and os.path.exists(trace) else {}
     out = [f"# {title}", "", "Command (from the repository root on the GPU host):", "", "```",
-           command, "```", "", "| kernel | calls | avg us | min us | max us | % of GPU time |",
-           "|---|---|---|---|---|---|"]
+           command, "```", "", "| kernel | calls | avg us | median us | min us | max us | % of GPU time |",
+           "|---|---|---|---|---|---|---|"]
     for r in rows:
+        m = med.get(r["Name"])
+        ms = f"{m / 1e3:.2f}" if m is not None else "-"
         out.append(f"| `{short_name(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
-                   f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                   f"{ms} | {float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                    f"{float(r['Percentage']):.2f} |")
     return "\n".join(out) + "\n"
 
