@@ -68,7 +68,17 @@ extern "C" {
 #define LORA_MAX_ADAPTERS 16384  /* pool slots one call can address */
 #define LORA_MAX_ROWS (1 << 22)  /* rows per call */
 
-typedef enum {
+/* The three enums below are passed as int.  Any int value may reach the library (an
+ * unknown status or dtype, a mode with LORA_MODE_CHECKED OR-ed in), so in C++ they are given
+ * int as their fixed underlying type, which makes every int value a valid value of the type
+ * and keeps the C representation. */
+#ifdef __cplusplus
+#define LORA_ENUM_INT : int
+#else
+#define LORA_ENUM_INT
+#endif
+
+typedef enum LORA_ENUM_INT {
     LORA_OK = 0,
     LORA_ERR_NULL = 1,      /* a required pointer is NULL */
     LORA_ERR_SHAPE = 2,     /* M, d_in, d_out or n_adapters out of range */
@@ -82,7 +92,7 @@ typedef enum {
     LORA_ERR_POOL = 10      /* (checked mode) a compact-pool adapter's rows leave the pool */
 } lora_status_t;
 
-typedef enum { LORA_BF16 = 0, LORA_F32 = 1 } lora_dtype_t;
+typedef enum LORA_ENUM_INT { LORA_BF16 = 0, LORA_F32 = 1 } lora_dtype_t;
 
 /* How lora_linear runs the layer ([P1], "How does one batch run 30 different adapters at
  * once?": decode is bound by the weight bytes read, prefill by the xW GEMM, which dilutes
@@ -98,7 +108,7 @@ typedef enum { LORA_BF16 = 0, LORA_F32 = 1 } lora_dtype_t;
  * them -- ids in [-1, n_adapters) (else LORA_ERR_BAD_ID), ranks in [1, r_max] (else
  * LORA_ERR_RANK), compact adapters inside the pool (else LORA_ERR_POOL) -- and enqueues
  * nothing when one fails.  For tests and debugging; not for graph capture. */
-typedef enum { LORA_MODE_AUTO = 0, LORA_MODE_DECODE = 1, LORA_MODE_PREFILL = 2 } lora_mode_t;
+typedef enum LORA_ENUM_INT { LORA_MODE_AUTO = 0, LORA_MODE_DECODE = 1, LORA_MODE_PREFILL = 2 } lora_mode_t;
 #define LORA_MODE_CHECKED 0x100
 #define LORA_PREFILL_MIN_ROWS 768 /* measured: decode and prefill sequences cost the same at 768 rows (4096 x 4096, r 16) */
 
