@@ -31,6 +31,8 @@
 //    as extra 32-deep MFMA steps (the K-extension [x | s t] [W ; B_a]) before the only store.
 //  * Tiles are handed to XCDs in compact blocks (workgroup b runs on XCD b % 8), so the
 //    x and W panels a tile group shares are read once into that XCD's L2.
+#include <type_traits>
+
 #include "common.h"
 
 namespace lora {
@@ -182,6 +184,36 @@ __device__ __forceinline__ void issue_stage(const DmaSrc<C> &src, uint4 *__restr
     }
 }
 
+// The same sources as 32-bit byte offsets from x and W (the prefill instances, when both
+// tensors fit in 4 GiB): the direct load's scalar-base form then takes one VGPR per address
+// instead of two, which frees the two registers the LoRA epilogue's kernel otherwise kept in
+// scratch memory across the K loop (prefill GEMM 118.1 -> 116.5 us).
+template <class C>
+struct DmaSrc32 {
+    const char *xb, *wb;
+    uint32_t xo[C::XINS];
+    uint32_t wo[C::WINS];
+};
+
+template <class C>
+__device__ __forceinline__ void issue_stage(const DmaSrc32<C> &src, uint4 *__restrict__ xslot,
+                                            uint4 *__restrict__ wslot,
+                                            int wave, int k0, int N) {
+#pragma unroll
+    for (int j = 0; j < C::XINS; ++j) {
+        const int q = wave * C::XINS + j;
+        __builtin_amdgcn_global_load_lds((const void *)(src.xb + (uint32_t)(src.xo[j] + 2u * (uint32_t)k0)),
+                                         (lds_void_t *)&xslot[q * 64], 16, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < C::WINS; ++j) {
+        const int q = wave * C::WINS + j;
+        __builtin_amdgcn_global_load_lds(
+            (const void *)(src.wb + (uint32_t)(src.wo[j] + 2u * (uint32_t)k0 * (uint32_t)N)),
+            (lds_void_t *)&wslot[q * 64], 16, 0, 0);
+    }
+}
+
 // Tile order: XCD-major (workgroup b runs on XCD b % 8), then groups of 4 tile rows, column-
 // major inside a group, so each XCD works on a compact block of tiles.
 __device__ __forceinline__ void tile_of(int b, int n_tm, int n_tn, int &tm, int &tn) {
@@ -223,7 +255,8 @@ __device__ __forceinline__ void fill_stage(uint4 *xs, uint4 *ws, const uint16_t 
     }
 }
 
-template <class C, bool SEGROWS, bool LORA, bool YF32>
+// O32: DMA sources as 32-bit byte offsets (x and W each below 4 GiB).
+template <class C, bool SEGROWS, bool LORA, bool YF32, bool O32>
 __global__ __launch_bounds__(C::NT) void gemm_big_kernel(const uint16_t *__restrict__ x,
                                                             const uint16_t *__restrict__ W,
                                                             int M, int K, int N,
@@ -246,7 +279,11 @@ __global__ __launch_bounds__(C::NT) void gemm_big_kernel(const uint16_t *__restr
 
     // DMA sources of this lane (rows beyond M and columns beyond N are clamped in bounds;
     // their results are never stored)
-    DmaSrc<C> src;
+    std::conditional_t<O32, DmaSrc32<C>, DmaSrc<C>> src;
+    if constexpr (O32) {
+        src.xb = reinterpret_cast<const char *>(x);
+        src.wb = reinterpret_cast<const char *>(W);
+    }
 #pragma unroll
     for (int j = 0; j < C::XINS; ++j) {
         const int q = wave * C::XINS + j;
@@ -254,7 +291,8 @@ __global__ __launch_bounds__(C::NT) void gemm_big_kernel(const uint16_t *__restr
         const int lc = (lane & 3) ^ ((lane >> 4) & 3);
         const int rr = min(row0 + row, M - 1);
         const int m = SEGROWS ? seg.perm[rr] : rr;
-        src.xp[j] = x + (size_t)m * K + lc * 8;
+        if constexpr (O32) src.xo[j] = (uint32_t)(((size_t)m * K + lc * 8) * 2);
+        else src.xp[j] = x + (size_t)m * K + lc * 8;
     }
 #pragma unroll
     for (int j = 0; j < C::WINS; ++j) {
@@ -262,7 +300,8 @@ __global__ __launch_bounds__(C::NT) void gemm_big_kernel(const uint16_t *__restr
         const int r = C::WROWS * q + lane / C::WCH;
         const int lc = (lane % C::WCH) ^ ((r & 3) << 2);
         const int n = min(n0 + lc * 8, N - 8);
-        src.wp[j] = W + (size_t)r * N + n;
+        if constexpr (O32) src.wo[j] = (uint32_t)(((size_t)r * N + n) * 2);
+        else src.wp[j] = W + (size_t)r * N + n;
     }
 
     f32x16_t acc[C::TM][C::TN];
@@ -692,12 +731,23 @@ hipError_t launch_big_cfg(const uint16_t *x, const uint16_t *W, int M, int K, in
     LoraEpilogue ep{};
     if (lora) ep = *lora;
     const dim3 grid(n_tm * n_tn);
-    if (y_f32)
-        launch((gemm_big_kernel<C, SEGROWS, LORA, true>), grid, dim3(C::NT), 0, s, x, W,
-                           M, K, N, y, n_tm, n_tn, seg, ep);
-    else
-        launch((gemm_big_kernel<C, SEGROWS, LORA, false>), grid, dim3(C::NT), 0, s, x, W,
-                           M, K, N, y, n_tm, n_tn, seg, ep);
+    // the LoRA instances take 32-bit load offsets when x and W each fit in 4 GiB
+    const bool o32 = LORA && (size_t)M * K * 2 <= 0xFFFFFFFFull && (size_t)K * N * 2 <= 0xFFFFFFFFull;
+    if (o32) {
+        if (y_f32)
+            launch((gemm_big_kernel<C, SEGROWS, LORA, true, LORA>), grid, dim3(C::NT), 0, s, x, W,
+                   M, K, N, y, n_tm, n_tn, seg, ep);
+        else
+            launch((gemm_big_kernel<C, SEGROWS, LORA, false, LORA>), grid, dim3(C::NT), 0, s, x, W,
+                   M, K, N, y, n_tm, n_tn, seg, ep);
+    } else {
+        if (y_f32)
+            launch((gemm_big_kernel<C, SEGROWS, LORA, true, false>), grid, dim3(C::NT), 0, s, x, W,
+                   M, K, N, y, n_tm, n_tn, seg, ep);
+        else
+            launch((gemm_big_kernel<C, SEGROWS, LORA, false, false>), grid, dim3(C::NT), 0, s, x, W,
+                   M, K, N, y, n_tm, n_tn, seg, ep);
+    }
     return hipGetLastError();
 }
 
