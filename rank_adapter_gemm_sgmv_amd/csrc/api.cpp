@@ -347,7 +347,7 @@ hipError_t run_linear(const void *x, const void *W, const void *A, const void *B
                                     true, gpart, nullptr, s)) != hipSuccess)
             return e;
         mark(mk, "decode_gemm_lora");
-        if ((e = launch_decode_reduce(gpart, M, d_in, d_out, y, yf, lo, true, s)) != hipSuccess) return e;
+        if ((e = launch_decode_reduce(gpart, M, d_in, d_out, y, yf, lo, true, nullptr, s)) != hipSuccess) return e;
         mark(mk, "decode_reduce_lora");
         return hipSuccess;
     }
@@ -367,7 +367,7 @@ hipError_t run_linear(const void *x, const void *W, const void *A, const void *B
                                d_in, rb, n_adapters, sg, spart, kc, ksplit, s)) != hipSuccess)
             return e;
         mark(mk, "shrink");
-        if ((e = launch_decode_reduce(gpart, M, d_in, d_out, y, yf, lo, false, s)) != hipSuccess) return e;
+        if ((e = launch_decode_reduce(gpart, M, d_in, d_out, y, yf, lo, false, &sg, s)) != hipSuccess) return e;
         mark(mk, "decode_reduce_lora");
         return hipSuccess;
     }
@@ -455,7 +455,7 @@ hipError_t run_fp8w(const void *x, const void *W8, const float *w_scale, const v
                            rb, n_adapters, sg, spart, kc, ksplit, s)) != hipSuccess)
         return e;
     mark(mk, "shrink");
-    if ((e = launch_decode_reduce(gpart, M, d_in, d_out, y, y_dtype == LORA_F32, lo, false, s)) !=
+    if ((e = launch_decode_reduce(gpart, M, d_in, d_out, y, y_dtype == LORA_F32, lo, false, &sg, s)) !=
         hipSuccess)
         return e;
     mark(mk, "decode_reduce_lora");

@@ -238,9 +238,12 @@ hipError_t launch_decode_gemm_fp8(const uint16_t *x, const uint8_t *W8, const fl
                                   hipStream_t s);
 
 // y = (split partials added in order) + scale_a * t B_a, t from the adapter tiles' splits
-// (`adapters`) or from the segment-path shrink's chunk sums; rounds once into y.
+// (`adapters`) or from the segment-path shrink's chunk sums; rounds once into y.  With the
+// chunk sums and `seg` (the segments of these ids, nullable) the rows of one adapter share
+// each load of B_a; the result is the same.
 hipError_t launch_decode_reduce(const float *partial, int M, int K, int N, void *y, bool y_f32,
-                                const DecodeLora &lo, bool adapters, hipStream_t s);
+                                const DecodeLora &lo, bool adapters, const Seg *seg,
+                                hipStream_t s);
 
 // Workspace floats the decode GEMM needs for split-K partials at these sizes.
 size_t gemm_partial_floats(int M, int K, int N);

@@ -33,6 +33,9 @@
 //    in split order, in fp32, rounded once into y's dtype; each touched B_a row slice is
 //    read once from HBM (rows of one adapter share it through L2).  No atomics: the result
 //    does not depend on scheduling.
+//  * Calls that come with segments (129-256 rows, rank-compact pools, the fp8 base) take
+//    reduce_seg_kernel instead: the same sums for items of four rows of one adapter, each
+//    B_a chunk loaded once per item.
 #include "batch_adapters.h"
 #include "decode_tiles.h"
 #include "segments_block.h"
@@ -491,6 +494,252 @@ __global__ __launch_bounds__(256) void reduce_lora_kernel(const float *__restric
     }
 }
 
+// The decode reduction for calls that carry segments (batches of 129-256 rows, rank-compact
+// pools, the fp8 base: t comes from the segment-path shrink's chunk sums).  Work item = up to
+// kSubRows consecutive positions of one adapter's segment (a quarter of a segment tile) x
+// kSegCols columns; base-only positions form items of their own.  Each 16-rank-row chunk of
+// the adapter's B slice is loaded once per item and applied to every row of it, so B is read
+// once per item instead of once per row, and unpacked once for all its rows.  Per row the
+// arithmetic is reduce_lora_kernel's: the split partials added in split order, t summed over
+// the chunks in chunk order, d the fmaf chain over rank rows in ascending order (chunks of
+// 16, zero terms past the rank), one fmaf with the scale, one rounding; so both kernels give
+// the same bits.  Two columns per thread keep a rank-64 item's FMA chain (4 rows x 2 columns
+// x 64 per lane) short.
+// Items are numbered densely: the tiles cover the LoRA positions in order, so tile t holds
+// (first position of tile t + 1, or the LoRA row count) - (its first position) rows and
+// ceil(rows / 4) items; every block reads all tiles at once and finds its own by a scan.
+// Block y takes item y; the grid is sized for the most items a batch of M rows and n
+// adapters can have, and blocks past the batch's count exit after that first round.
+constexpr int kSubRows = 4;
+constexpr int kSegCpt = 2;               // columns per thread
+constexpr int kSegCols = 256 * kSegCpt;  // columns per item
+constexpr int kSegMaxTiles = 512;        // tiles a block scans (lora_max_tiles at M <= 256)
+template <int RM, bool YF32, int MS, bool PADRM>
+__global__ __launch_bounds__(256) void reduce_seg_kernel(const float *__restrict__ partial,
+                                                         int M, int N, int n_tm, int n_tn,
+                                                         int bm_log2, int n_splits,
+                                                         int max_tiles, DecodeLora lo, Seg seg,
+                                                         void *__restrict__ y) {
+    constexpr int SUB = kSubRows;
+    constexpr int TPT = kSegMaxTiles / 256;  // tiles per thread in the scan
+    static_assert(SUB * RM <= 256, "one thread per (row, rank column) sums t");
+    static_assert(kSegCpt == 2, "two columns per thread");
+    __shared__ int s_p0[kSegMaxTiles + 1];
+    __shared__ int s_wave[4];
+    __shared__ int s_own[3];  // tile, first item of that tile, adapter
+    __shared__ __attribute__((aligned(16))) float s_t[SUB][RM];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+
+    // round 1: meta and every tile's (first position, adapter)
+    // (clamped: the counts index this block's LDS)
+    const int n_tiles = min(max(seg.meta[3], 0), max_tiles);
+    const int lora_rows = min(max(seg.meta[1], 0), M);
+    int2 te[TPT];
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) {
+        const int t = tid * TPT + u;
+        te[u] = t < max_tiles ? reinterpret_cast<const int2 *>(seg.tiles)[t] : make_int2(0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) {
+        const int t = tid * TPT + u;
+        if (t < n_tiles) s_p0[t] = te[u].x;
+    }
+    if (tid == 0) s_p0[n_tiles] = lora_rows;
+    __syncthreads();
+    int nsub[TPT], mine = 0;
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) {
+        const int t = tid * TPT + u;
+        nsub[u] = t < n_tiles ? (s_p0[t + 1] - te[u].x + SUB - 1) / SUB : 0;
+        mine += nsub[u];
+    }
+    // exclusive scan of the item counts over threads (tiles in order)
+    int incl = mine;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int v = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += v;
+    }
+    if (lane == 63) s_wave[wv] = incl;
+    __syncthreads();
+    int before = incl - mine, n_sub = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const int c = s_wave[w];
+        if (w < wv) before += c;
+        n_sub += c;
+    }
+    const int item = blockIdx.y;
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) {
+        if (item >= before && item < before + nsub[u]) {
+            s_own[0] = tid * TPT + u;
+            s_own[1] = before;
+            s_own[2] = te[u].y;
+        }
+        before += nsub[u];
+    }
+    const int n_items = n_sub + (M - lora_rows + SUB - 1) / SUB;
+    if (item >= n_items) return;  // uniform in the block
+    __syncthreads();
+    int p0, nr, a;
+    const bool has = item < n_sub;
+    if (has) {
+        const int t = s_own[0];
+        p0 = s_p0[t] + SUB * (item - s_own[1]);
+        nr = min(SUB, s_p0[t + 1] - p0);
+        a = s_own[2];
+    } else {
+        p0 = lora_rows + SUB * (item - n_sub);
+        nr = min(SUB, M - p0);
+        a = 0;
+    }
+    int m[SUB];
+#pragma unroll
+    for (int i = 0; i < SUB; ++i) m[i] = seg.perm[min(max(p0 + min(i, nr - 1), 0), M - 1)];
+
+    const int n = (blockIdx.x * 256 + tid) * kSegCpt;
+    const bool col_ok = n < N;  // N % 4 == 0: a thread's pair is all in or all out
+    const int nc = col_ok ? n : 0;
+    const int bm = 1 << bm_log2;
+    const size_t stride = (size_t)n_tm * n_tn * bm * kBN;  // one split of the partial tiles
+    const float *pp[SUB];
+#pragma unroll
+    for (int i = 0; i < SUB; ++i) {
+        const int tile = (m[i] >> bm_log2) + (nc / kBN) * n_tm;
+        pp[i] = partial + (size_t)tile * bm * kBN + (m[i] & (bm - 1)) * kBN + (nc % kBN);
+    }
+    const int width = PADRM || lo.roff ? RM : lo.pstride;
+    int r = !has ? 0 : lo.ranks ? min(max(lo.ranks[a], 1), width) : width;
+    const int row0 = PADRM ? a * RM : adapter_row0(lo.roff, lo.pool_rows, a, lo.pstride, r);
+    const uint16_t *bp = lo.B + (size_t)row0 * N + nc;
+
+    // Issued together: every row's split partials (up to four splits), the first TB chunk
+    // sums of t (thread (i, j) of the first SUB x RM reads column j of row i; columns at or
+    // beyond the rank are not read and stay zero) and the first two 16-row chunks of B.
+    constexpr bool EARLY = MS <= 4;
+    float2 pv[EARLY ? SUB : 1][EARLY ? MS : 1];
+    if constexpr (EARLY) {
+#pragma unroll
+        for (int i = 0; i < SUB; ++i)
+#pragma unroll
+            for (int sp = 0; sp < MS; ++sp)
+                if (sp < n_splits) pv[i][sp] = *reinterpret_cast<const float2 *>(pp[i] + sp * stride);
+    }
+    constexpr int TB = 32;
+    const int ti = tid / RM, tj = tid % RM;
+    const bool tmine = has && tid < SUB * RM && tj < r;
+    const float *ts = lo.tpart + (size_t)seg.perm[min(max(p0 + min(ti, nr - 1), 0), M - 1)] * RM + tj;
+    const size_t cs = (size_t)M * RM;
+    float tv[TB];
+#pragma unroll
+    for (int c = 0; c < TB; ++c) tv[c] = tmine && c < lo.n_chunks ? ts[c * cs] : 0.0f;
+
+    constexpr int BCH = RM <= 16 ? RM : 16;
+    constexpr int NCH = RM / BCH;
+    uint32_t bq[NCH][BCH];
+    // a padded pool at r_max <= 16 holds every row (the padding rows exist): loaded without
+    // waiting for the rank; otherwise rows at or beyond it are zeros, not loads
+#define SEG_LOAD_CHUNK(CI)                                                                        \
+    do {                                                                                          \
+        if (RM <= 16 && PADRM) {                                                                  \
+            _Pragma("unroll") for (int j = 0; j < BCH; ++j) bq[CI][j] =                           \
+                *reinterpret_cast<const uint32_t *>(bp + (size_t)((CI) * BCH + j) * N);           \
+        } else {                                                                                  \
+            _Pragma("unroll") for (int j = 0; j < BCH; ++j) bq[CI][j] =                           \
+                (CI) * BCH + j < r ? *reinterpret_cast<const uint32_t *>(bp + (size_t)((CI) * BCH + j) * N) \
+                                   : 0u;                                                          \
+        }                                                                                         \
+    } while (0)
+#pragma unroll
+    for (int c = 0; c < (NCH < 2 ? NCH : 2); ++c)
+        if (c * BCH < r) SEG_LOAD_CHUNK(c);
+
+    float2 acc[SUB];
+    if constexpr (EARLY) {
+#pragma unroll
+        for (int i = 0; i < SUB; ++i) {
+            acc[i] = pv[i][0];
+#pragma unroll
+            for (int sp = 1; sp < MS; ++sp) {
+                if (sp < n_splits) { acc[i].x += pv[i][sp].x; acc[i].y += pv[i][sp].y; }
+            }
+        }
+    }
+    // t[m_i, j] = sum over the shrink's chunks, in chunk order (zero at or beyond the rank)
+    if (has) {
+        float t = 0.0f;
+        if (tmine) {
+#pragma unroll
+            for (int c = 0; c < TB; ++c)
+                if (c < lo.n_chunks) t += tv[c];
+            for (int c0 = TB; c0 < lo.n_chunks; c0 += 8) {
+                float v[8];
+#pragma unroll
+                for (int c = 0; c < 8; ++c) v[c] = c0 + c < lo.n_chunks ? ts[(c0 + c) * cs] : 0.0f;
+#pragma unroll
+                for (int c = 0; c < 8; ++c)
+                    if (c0 + c < lo.n_chunks) t += v[c];
+            }
+        }
+        if (tid < SUB * RM) s_t[ti][tj] = t;
+        __syncthreads();
+    }
+
+    // d[i] = sum over rank rows j (ascending, in chunks of 16; zero terms past the rank) of
+    // t[m_i, j] B_a[j, cols]; chunk c + 2 is loaded while chunk c is multiplied
+    float d[SUB][2];
+#pragma unroll
+    for (int i = 0; i < SUB; ++i) d[i][0] = d[i][1] = 0.0f;
+    if (has) {
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            const int j0 = c * BCH;
+            if (j0 >= r) break;
+            if (c + 2 < NCH && j0 + 2 * BCH < r) SEG_LOAD_CHUNK(c + 2);
+#pragma unroll
+            for (int j = 0; j < BCH; ++j) {
+                const float b0 = bf16_lo(bq[c][j]), b1 = bf16_hi(bq[c][j]);
+#pragma unroll
+                for (int i = 0; i < SUB; ++i) {
+                    const float tt = s_t[i][j0 + j];
+                    d[i][0] = fmaf(tt, b0, d[i][0]);
+                    d[i][1] = fmaf(tt, b1, d[i][1]);
+                }
+            }
+        }
+    }
+#undef SEG_LOAD_CHUNK
+    const float sc = has ? lo.scale[a] : 0.0f;
+#pragma unroll
+    for (int i = 0; i < SUB; ++i) {
+        if constexpr (!EARLY) {
+            float2 pr[MS];
+#pragma unroll
+            for (int sp = 0; sp < MS; ++sp)
+                if (sp < n_splits) pr[sp] = *reinterpret_cast<const float2 *>(pp[i] + sp * stride);
+            acc[i] = pr[0];
+#pragma unroll
+            for (int sp = 1; sp < MS; ++sp) {
+                if (sp < n_splits) { acc[i].x += pr[sp].x; acc[i].y += pr[sp].y; }
+            }
+        }
+        float2 o = acc[i];
+        if (has) {
+            o.x = fmaf(sc, d[i][0], o.x);
+            o.y = fmaf(sc, d[i][1], o.y);
+        }
+        if (!col_ok || i >= nr) continue;
+        if constexpr (YF32) {
+            *reinterpret_cast<float2 *>(reinterpret_cast<float *>(y) + (size_t)m[i] * N + n) = o;
+        } else {
+            *reinterpret_cast<uint32_t *>(reinterpret_cast<uint16_t *>(y) + (size_t)m[i] * N + n) =
+                pack_bf16x2(o.x, o.y);
+        }
+    }
+}
+
 struct DecPlan {
     int bm, n_tm, n_tn, n_lt, ks, k_per_split;  // ks splits of K per tile
 };
@@ -620,15 +869,55 @@ hipError_t launch_decode_gemm_fp8(const uint16_t *x, const uint8_t *W8, const fl
 }
 
 hipError_t launch_decode_reduce(const float *partial, int M, int K, int N, void *y, bool y_f32,
-                                const DecodeLora &lo, bool adapters, hipStream_t s) {
+                                const DecodeLora &lo, bool adapters, const Seg *seg,
+                                hipStream_t s) {
     if (!decode_gemm_supported(M, K, N) || partial == nullptr || !rank_ok(lo.r_max) ||
         (adapters && lo.n_adapters > M && lo.slots == nullptr) ||
         (!adapters && (lo.tpart == nullptr || lo.n_chunks < 1)))
         return hipErrorInvalidValue;
     const int n_lt = adapters ? adapter_tiles(M, lo.r_max, lo.n_adapters) : 0;
     const DecPlan p = dec_plan(M, K, N, n_lt);
-    const dim3 rgrid((unsigned)((N + 1023) / 1024), (unsigned)M);
     const bool padrm = lo.roff == nullptr && lo.pstride == lo.r_max;
+    if (!adapters && seg != nullptr && lora_max_tiles(M, lo.n_adapters) <= kSegMaxTiles) {
+        // one block per (item, kSegCols columns), as many items as a batch of M rows and
+        // n adapters can have
+        const int max_tiles = lora_max_tiles(M, lo.n_adapters);
+        const int n_cc = (N + kSegCols - 1) / kSegCols;
+        const int n_seg = M < lo.n_adapters ? M : lo.n_adapters;
+        // sum over segments of ceil(rows / 4), plus ceil(base rows / 4), is at most
+        // (M + 3 (segments + 1)) / 4
+        const long max_items = ((long)M + 3L * n_seg + 6) / kSubRows;
+        const dim3 sgrid((unsigned)n_cc, (unsigned)max_items);
+        const int bl = p.bm == 32 ? 5 : 6;
+#define SEG_ONE(RMX, YF, MSX)                                                                   \
+    if (padrm)                                                                                  \
+        launch((reduce_seg_kernel<RMX, YF, MSX, true>), sgrid, dim3(256), 0, s, partial, M, N,  \
+               p.n_tm, p.n_tn, bl, p.ks, max_tiles, lo, *seg, y);                                \
+    else                                                                                        \
+        launch((reduce_seg_kernel<RMX, YF, MSX, false>), sgrid, dim3(256), 0, s, partial, M, N, \
+               p.n_tm, p.n_tn, bl, p.ks, max_tiles, lo, *seg, y)
+#define SEG_LAUNCH(RMX, YF)                                                                     \
+    if (p.ks <= 2) {                                                                            \
+        SEG_ONE(RMX, YF, 2);                                                                    \
+    } else if (p.ks <= 4) {                                                                     \
+        SEG_ONE(RMX, YF, 4);                                                                    \
+    } else {                                                                                    \
+        SEG_ONE(RMX, YF, 16);                                                                   \
+    }
+#define SEG_RANK(YF)                                                                            \
+    switch (lo.r_max) {                                                                         \
+        case 8: SEG_LAUNCH(8, YF); break;                                                       \
+        case 16: SEG_LAUNCH(16, YF); break;                                                     \
+        case 32: SEG_LAUNCH(32, YF); break;                                                     \
+        default: SEG_LAUNCH(64, YF); break;                                                     \
+    }
+        if (y_f32) { SEG_RANK(true) } else { SEG_RANK(false) }
+#undef SEG_RANK
+#undef SEG_LAUNCH
+#undef SEG_ONE
+        return hipGetLastError();
+    }
+    const dim3 rgrid((unsigned)((N + 1023) / 1024), (unsigned)M);
 #define RED_ONE(BM, RMX, YF, MSX)                                                           \
     if (padrm)                                                                              \
         launch((reduce_lora_kernel<BM, RMX, YF, MSX, true>), rgrid, dim3(256), 0, s, partial, M,\

@@ -6,25 +6,27 @@
 // Adapters Fit on One GPU" (dev.to), "How does one batch run 30 different adapters at
 // once?", memory-bound on the adapter weights.
 //
-// Work item = (tile, k-chunk), one wave each: a tile is up to LORA_TILE_ROWS (16) rows of one
-// adapter a (from the segment builder), a k-chunk is KC consecutive rows of A_a (one
-// contiguous block of the padded pool).  The product x[tile rows, chunk] A_a[chunk, :] runs
-// on v_mfma_f32_16x16x32_bf16: sixteen rows are exactly one MFMA row block, so a tile costs
-// one 16 x 16 accumulator per 16 rank columns, and the VALU does almost nothing (a VALU
-// version of this product is compute-bound at prefill sizes).  Each A_a byte is read once
-// per tile, each x byte once per chunk.
+// Work item = (tile, k-chunk), one workgroup each: a tile is up to LORA_TILE_ROWS (16) rows of
+// one adapter a (from the segment builder), a k-chunk is kc consecutive rows of A_a (one
+// contiguous block of the padded pool), and each of the four waves takes a quarter of it.
+// The product x[tile rows, quarter] A_a[quarter, :] runs on v_mfma_f32_16x16x32_bf16:
+// sixteen rows are exactly one MFMA row block, so a tile costs one 16 x 16 accumulator per
+// 16 rank columns, and the VALU does almost nothing (a VALU version of this product is
+// compute-bound at prefill sizes).  Each A_a byte is read once per tile, each x byte once per
+// chunk.
 //
-// The partial sums of each k-chunk go to partial[chunk][row][0:r_max] (zero beyond the
-// rank); shrink_finalize_kernel adds the chunks in ascending order, so the result does not
-// depend on scheduling.
+// Wave 0 adds the four quarters in wave order (through LDS) and writes the chunk's sums to
+// partial[chunk][row][0:r_max] (zero beyond the rank); the consumers add the chunks in
+// ascending order, so the result does not depend on scheduling.  Summing the quarters in
+// the workgroup leaves a quarter as many chunk sums to write and to read back.
 #include "common.h"
 
 namespace lora {
 
 namespace {
 
-constexpr int kKC = 256;           // k rows of A per work item (128 at r_max 64)
-constexpr int kWavesPerBlock = 4;  // independent waves per workgroup
+constexpr int kKC = 256;           // k rows of A per wave and chunk (128 at r_max 64)
+constexpr int kWavesPerBlock = 4;  // waves per workgroup, one quarter of the chunk each
 constexpr int kMaxGrid = 1 << 20;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -46,8 +48,8 @@ struct MfmaShrink {
     static_assert(KS * GR % 64 == 0, "whole loads per lane");
 };
 
-// One wave per (tile, k-chunk): t_part[rows of the tile, 0:RM] = x[rows, chunk] A_a[chunk, :]
-// on v_mfma_f32_16x16x32_bf16.  The A operand (16 rows x 32 k) is the tile's x rows, each
+// One workgroup per (tile, k-chunk), one wave per quarter of the chunk:
+// t_part[rows of the tile, 0:RM] = x[rows, quarter] A_a[quarter, :] on v_mfma_f32_16x16x32_bf16.  The A operand (16 rows x 32 k) is the tile's x rows, each
 // lane loading its 8 consecutive k straight from global memory; the B operand (32 k x 16
 // columns) is the adapter's chunk, staged in this wave's own LDS rows as it lies in HBM
 // ([k][columns], rows padded by 16 bytes) and read with the transposing LDS read, which
@@ -79,10 +81,13 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void shrink_mfma_kernel(
         for (int r = lane; r < C::KS; r += 64)
             *reinterpret_cast<uint4 *>(wg + r * C::LROW + 16) = make_uint4(0, 0, 0, 0);
     }
+    // the block's waves take the four quarters of the chunk's k range; waves 1-3 hand their
+    // sums to wave 0 through LDS, which adds them in wave order and writes the chunk's sums
+    __shared__ float red[kWavesPerBlock - 1][16 * C::RMP];
     const int total = seg.meta[3] * n_chunks;
-    const int nw = gridDim.x * kWavesPerBlock;
-    for (int w = blockIdx.x * kWavesPerBlock + wv; w < total; w += nw) {
-        const int tile = w / n_chunks, c = w % n_chunks;
+    const int kw = kc / kWavesPerBlock;
+    for (int it = blockIdx.x; it < total; it += gridDim.x) {
+        const int tile = it / n_chunks, c = it % n_chunks;
         const int p0 = seg.tiles[2 * tile], a = seg.tiles[2 * tile + 1];
         const int rows = min(p0 + kTileRows, seg.offsets[a + 1]) - p0;
         constexpr bool VARW = LAYOUT != kPadRM;
@@ -93,7 +98,8 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void shrink_mfma_kernel(
         // row stride of A_a: in a compact pool the groups at or beyond the rank are not
         // loaded (they are zero or belong to the next adapter)
         const int rs = !VARW ? RM : roff ? (r + 7) & ~7 : pstride;
-        const int k_lo = c * kc, k_hi = min(k_lo + kc, d_in);
+        const int k0 = c * kc + wv * kw;
+        const int k_lo = min(k0, d_in), k_hi = min(k0 + kw, d_in);
         // this lane's x row (rows beyond the tile repeat its last row; their sums are dropped)
         const int mrow = seg.perm[p0 + min(li, rows - 1)];
         const uint16_t *xr = x + (size_t)mrow * d_in;
@@ -185,19 +191,32 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void shrink_mfma_kernel(
             }
             __builtin_amdgcn_s_waitcnt(0xC07F);  // LDS reads done before the next fill overwrites
         }
-        // acc[b][i] = sum for tile row 4 g + i, column 16 b + li
+        // acc[b][i] = sum for tile row 4 g + i, column 16 b + li (this wave's quarter)
+        if (wv > 0) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int tr = 4 * g + i;
-            const int m = __shfl(mrow, tr, 64);
-            if (tr < rows) {
+            for (int b = 0; b < C::NB; ++b)
 #pragma unroll
-                for (int b = 0; b < C::NB; ++b) {
-                    const int col = 16 * b + li;
-                    if (col < RM) partial[((size_t)c * M + m) * RM + col] = acc[b][i];
+                for (int i = 0; i < 4; ++i) red[wv - 1][(4 * g + i) * C::RMP + 16 * b + li] = acc[b][i];
+        }
+        __syncthreads();
+        if (wv == 0) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int tr = 4 * g + i;
+                const int m = __shfl(mrow, tr, 64);
+                if (tr < rows) {
+#pragma unroll
+                    for (int b = 0; b < C::NB; ++b) {
+                        const int col = 16 * b + li;
+                        float v = acc[b][i];
+#pragma unroll
+                        for (int q = 0; q < kWavesPerBlock - 1; ++q) v += red[q][tr * C::RMP + col];
+                        if (col < RM) partial[((size_t)c * M + m) * RM + col] = v;
+                    }
                 }
             }
         }
+        __syncthreads();  // wave 0 has read red before the next chunk's sums go there
     }
 }
 
@@ -242,7 +261,7 @@ __global__ __launch_bounds__(256) void shrink_finalize_kernel(const float *__res
 }  // namespace
 
 void shrink_plan(int d_in, int r_max, int *kc, int *ksplit) {
-    *kc = r_max == 64 ? 128 : kKC;
+    *kc = (r_max == 64 ? 128 : kKC) * kWavesPerBlock;  // a workgroup's k range
     *ksplit = (d_in + *kc - 1) / *kc;
 }
 
@@ -251,9 +270,9 @@ hipError_t launch_shrink(const uint16_t *x, const uint16_t *A, const int32_t *ra
                          int r_max, int n_adapters, Seg seg, float *partial, int kc, int ksplit,
                          hipStream_t s) {
     if (roff == nullptr && (pstride < 1 || pstride > r_max)) return hipErrorInvalidValue;
-    const long items = (long)lora_max_tiles(M, n_adapters) * ksplit;
-    const long wblocks = (items + kWavesPerBlock - 1) / kWavesPerBlock;
-    const dim3 wgrid((unsigned)(wblocks < kMaxGrid ? wblocks : kMaxGrid));
+    if (kc % (8 * kWavesPerBlock) != 0) return hipErrorInvalidValue;
+    const long items = (long)lora_max_tiles(M, n_adapters) * ksplit;  // one per workgroup
+    const dim3 wgrid((unsigned)(items < kMaxGrid ? items : kMaxGrid));
     const dim3 wblock(64 * kWavesPerBlock);
     const int layout = roff != nullptr       ? kVarW
                        : pstride == r_max    ? kPadRM
