@@ -45,8 +45,34 @@ struct MfmaShrink {
     static constexpr int AL = KS * GR / 64;            // 16-byte A loads per lane per fill
     static constexpr int LROW = RMP * 2 + 16;          // LDS bytes per k row (padded)
     static constexpr int LDS = KS * LROW;              // LDS bytes per wave
+    static constexpr int KW = RM == 64 ? 128 : kKC;    // k rows per wave and chunk
+    static constexpr int FILLS = KW / KS;              // LDS fills per wave and chunk
     static_assert(KS * GR % 64 == 0, "whole loads per lane");
+    static_assert(KW % KS == 0 && FILLS >= 1 && FILLS <= 2, "whole fills per wave");
 };
+
+// The MFMA steps over one LDS fill: rows kb .. kb + KS of the chunk (x beyond k_hi masked),
+// v_mfma_f32_16x16x32_bf16 per 16 rank columns below the rank.
+template <class C, int RM>
+__device__ __forceinline__ void shrink_mfma_fill(f32x4_t (&acc)[C::NB], const uint4 (&xv)[C::STEPS],
+                                                 const lds_char_t *wl, int kb, int k_hi, int g,
+                                                 int li, int r) {
+#pragma unroll
+    for (int st = 0; st < C::STEPS; ++st) {
+        const uint4 xs = kb + 32 * st + 8 * g < k_hi ? xv[st] : make_uint4(0, 0, 0, 0);
+        const bf16x8_t xa = __builtin_bit_cast(bf16x8_t, xs);
+#pragma unroll
+        for (int b = 0; b < C::NB; ++b) {
+            if (16 * b < r) {
+                const lds_char_t *q = wl + (32 * st + 8 * g + (li >> 2)) * C::LROW + b * 32 + 8 * (li & 3);
+                const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)q);
+                const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)(q + 4 * C::LROW));
+                const bf16x8_t bb = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+                acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, bb, acc[b], 0, 0, 0);
+            }
+        }
+    }
+}
 
 // One workgroup per (tile, k-chunk), one wave per quarter of the chunk:
 // t_part[rows of the tile, 0:RM] = x[rows, quarter] A_a[quarter, :] on v_mfma_f32_16x16x32_bf16.  The A operand (16 rows x 32 k) is the tile's x rows, each
@@ -109,87 +135,79 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void shrink_mfma_kernel(
 #pragma unroll
         for (int b = 0; b < C::NB; ++b) acc[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-        for (int kb = k_lo; kb < k_hi; kb += C::KS) {
-            // (kFlat) rows of a width that is not a multiple of 8: the chunk's run of rs-wide
-            // rows, element by element
-            constexpr bool flat = LAYOUT == kFlat;
-            if constexpr (flat) {
-                // zero the wave's rows (columns at or beyond rs, rows at or beyond k_hi stay
-                // zero), wait for those writes, then place element e of the run at k row
-                // e / rs, column e % rs (rows kb .. k_hi - 1 of A_a: all inside it)
-                for (int v = lane; v < C::KS * C::LROW / 16; v += 64)
-                    *reinterpret_cast<uint4 *>(wg + v * 16) = make_uint4(0, 0, 0, 0);
-                __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-                const int n_el = min(C::KS, k_hi - kb) * rs;
-                const int step_k = 64 / rs, step_j = 64 - step_k * rs;
-                const uint16_t *src = Aa + (size_t)kb * rs;
+        constexpr bool flat = LAYOUT == kFlat;
+        if constexpr (!flat) {
+            // per LDS fill: A_a[kb .. kb+KS, 0:rank] and x; groups at or beyond the rank, and
+            // rows at or beyond the range's end, are zeros instead of loads (a padded pool's
+            // padding is not read).  Unit u = lane + 64 i is (row u / GR, group u % GR); the
+            // offsets are 32-bit bytes from the adapter's block (one VGPR per address).
+            const char *ab = reinterpret_cast<const char *>(Aa);
+#pragma unroll
+            for (int f = 0; f < C::FILLS; ++f) {
+                const int kb = k_lo + f * C::KS;
+                if (kb >= k_hi) break;  // uniform: the wave's range ends inside this chunk
+                uint4 av[C::AL];
+#pragma unroll
+                for (int i = 0; i < C::AL; ++i) {
+                    const int u = lane + 64 * i, kr = kb + u / C::GR, gr = u % C::GR;
+                    const uint32_t off = ((uint32_t)min(kr, d_in - 1) * (uint32_t)rs + (uint32_t)(gr * 8)) * 2u;
+                    av[i] = gr * 8 < r && kr < k_hi ? *reinterpret_cast<const uint4 *>(ab + off)
+                                                    : make_uint4(0, 0, 0, 0);
+                }
+                uint4 xv[C::STEPS];
+#pragma unroll
+                for (int st = 0; st < C::STEPS; ++st) xv[st] = ld16(xr + min(kb + 32 * st + 8 * g, d_in - 8));
+#pragma unroll
+                for (int i = 0; i < C::AL; ++i) {
+                    const int u = lane + 64 * i, kr = u / C::GR, gr = u % C::GR;
+                    *reinterpret_cast<uint4 *>(wg + kr * C::LROW + gr * 16) = av[i];
+                }
+                __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
+                shrink_mfma_fill<C, RM>(acc, xv, wl, kb, k_hi, g, li, r);
+                __builtin_amdgcn_s_waitcnt(0xC07F);  // LDS reads done before the next fill overwrites
+            }
+        } else {
+            for (int kb = k_lo; kb < k_hi; kb += C::KS) {
+                // (kFlat) rows of a width that is not a multiple of 8: the chunk's run of rs-wide
+                // rows, element by element
+                {
+                    // zero the wave's rows (columns at or beyond rs, rows at or beyond k_hi stay
+                    // zero), wait for those writes, then place element e of the run at k row
+                    // e / rs, column e % rs (rows kb .. k_hi - 1 of A_a: all inside it)
+                    for (int v = lane; v < C::KS * C::LROW / 16; v += 64)
+                        *reinterpret_cast<uint4 *>(wg + v * 16) = make_uint4(0, 0, 0, 0);
+                    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+                    const int n_el = min(C::KS, k_hi - kb) * rs;
+                    const int step_k = 64 / rs, step_j = 64 - step_k * rs;
+                    const uint16_t *src = Aa + (size_t)kb * rs;
 #pragma unroll 1
-                for (int e0 = 0; e0 < n_el; e0 += 64 * 8) {
-                    uint16_t h[8];
+                    for (int e0 = 0; e0 < n_el; e0 += 64 * 8) {
+                        uint16_t h[8];
 #pragma unroll
-                    for (int q = 0; q < 8; ++q) {
-                        const int e = e0 + lane + 64 * q;
-                        h[q] = e < n_el ? src[e] : (uint16_t)0;
-                    }
-                    // element e0 + lane + 64 q sits at k row kr, column j: one division per
-                    // batch, then steps of 64 elements
-                    int kr = (e0 + lane) / rs, j = (e0 + lane) - kr * rs;
+                        for (int q = 0; q < 8; ++q) {
+                            const int e = e0 + lane + 64 * q;
+                            h[q] = e < n_el ? src[e] : (uint16_t)0;
+                        }
+                        // element e0 + lane + 64 q sits at k row kr, column j: one division per
+                        // batch, then steps of 64 elements
+                        int kr = (e0 + lane) / rs, j = (e0 + lane) - kr * rs;
 #pragma unroll
-                    for (int q = 0; q < 8; ++q) {
-                        if (e0 + lane + 64 * q < n_el)
-                            *reinterpret_cast<uint16_t *>(wg + kr * C::LROW + j * 2) = h[q];
-                        j += step_j;
-                        kr += step_k;
-                        if (j >= rs) { j -= rs; ++kr; }
-                    }
-                }
-            }
-            // A_a[kb .. kb+KS, 0:RM]: unit f = lane + 64 i is (row f / GR, group f % GR)
-            uint4 av[C::AL];
-            if constexpr (!VARW) {
-                // padded pool: every group is loaded (the padding is zeros), so the loads do
-                // not wait for the rank
-#pragma unroll
-                for (int i = 0; i < C::AL; ++i) {
-                    const int f = lane + 64 * i, kr = kb + f / C::GR, gr = f % C::GR;
-                    av[i] = ld16(Aa + (size_t)min(kr, d_in - 1) * RM + gr * 8);
-                }
-            } else if (!flat) {
-#pragma unroll
-                for (int i = 0; i < C::AL; ++i) {
-                    const int f = lane + 64 * i, kr = kb + f / C::GR, gr = f % C::GR;
-                    av[i] = gr * 8 < r ? ld16(Aa + (size_t)min(kr, d_in - 1) * rs + gr * 8)
-                                       : make_uint4(0, 0, 0, 0);
-                }
-            }
-            uint4 xv[C::STEPS];
-#pragma unroll
-            for (int st = 0; st < C::STEPS; ++st) xv[st] = ld16(xr + min(kb + 32 * st + 8 * g, d_in - 8));
-            if (!flat) {
-#pragma unroll
-                for (int i = 0; i < C::AL; ++i) {
-                    const int f = lane + 64 * i, kr = f / C::GR, gr = f % C::GR;
-                    const bool ok = kb + kr < k_hi && gr * 8 < r;
-                    *reinterpret_cast<uint4 *>(wg + kr * C::LROW + gr * 16) = ok ? av[i] : make_uint4(0, 0, 0, 0);
-                }
-            }
-            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
-#pragma unroll
-            for (int st = 0; st < C::STEPS; ++st) {
-                const uint4 xs = kb + 32 * st + 8 * g < k_hi ? xv[st] : make_uint4(0, 0, 0, 0);
-                const bf16x8_t xa = __builtin_bit_cast(bf16x8_t, xs);
-#pragma unroll
-                for (int b = 0; b < C::NB; ++b) {
-                    if (16 * b < r) {
-                        const lds_char_t *q = wl + (32 * st + 8 * g + (li >> 2)) * C::LROW + b * 32 + 8 * (li & 3);
-                        const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)q);
-                        const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t *)(q + 4 * C::LROW));
-                        const bf16x8_t bb = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                        acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa, bb, acc[b], 0, 0, 0);
+                        for (int q = 0; q < 8; ++q) {
+                            if (e0 + lane + 64 * q < n_el)
+                                *reinterpret_cast<uint16_t *>(wg + kr * C::LROW + j * 2) = h[q];
+                            j += step_j;
+                            kr += step_k;
+                            if (j >= rs) { j -= rs; ++kr; }
+                        }
                     }
                 }
+                uint4 xv[C::STEPS];
+#pragma unroll
+                for (int st = 0; st < C::STEPS; ++st) xv[st] = ld16(xr + min(kb + 32 * st + 8 * g, d_in - 8));
+                __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes are done
+                shrink_mfma_fill<C, RM>(acc, xv, wl, kb, k_hi, g, li, r);
+                __builtin_amdgcn_s_waitcnt(0xC07F);  // LDS reads done before the next fill overwrites
             }
-            __builtin_amdgcn_s_waitcnt(0xC07F);  // LDS reads done before the next fill overwrites
         }
         // acc[b][i] = sum for tile row 4 g + i, column 16 b + li (this wave's quarter)
         if (wv > 0) {
@@ -261,7 +279,7 @@ __global__ __launch_bounds__(256) void shrink_finalize_kernel(const float *__res
 }  // namespace
 
 void shrink_plan(int d_in, int r_max, int *kc, int *ksplit) {
-    *kc = (r_max == 64 ? 128 : kKC) * kWavesPerBlock;  // a workgroup's k range
+    *kc = (r_max == 64 ? 128 : kKC) * kWavesPerBlock;  // a workgroup's k range (MfmaShrink::KW per wave)
     *ksplit = (d_in + *kc - 1) / *kc;
 }
 
