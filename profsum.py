@@ -34,6 +34,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 _STEP_OF_KERNEL = [
     ("decode_gemm_kernel", "decode_gemm_lora"),
     ("reduce_lora_kernel", "decode_reduce_lora"),
+    ("reduce_seg_kernel", "decode_reduce_lora"),
     ("build_segments_kernel", "build_segments"),
     ("build_segments_small_kernel", "build_segments"),
     ("shrink_finalize_kernel", "shrink_finalize"),

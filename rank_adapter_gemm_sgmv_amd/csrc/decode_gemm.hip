@@ -33,9 +33,8 @@
 //    in split order, in fp32, rounded once into y's dtype; each touched B_a row slice is
 //    read once from HBM (rows of one adapter share it through L2).  No atomics: the result
 //    does not depend on scheduling.
-//  * Calls that come with segments (129-256 rows, rank-compact pools, the fp8 base) take
-//    reduce_seg_kernel instead: the same sums for items of four rows of one adapter, each
-//    B_a chunk loaded once per item.
+//  * Batches of 129-256 rows (which come with segments) take reduce_seg_kernel instead: the
+//    same sums for items of four rows of one adapter, each B_a chunk loaded once per item.
 #include "batch_adapters.h"
 #include "decode_tiles.h"
 #include "segments_block.h"
@@ -494,8 +493,8 @@ __global__ __launch_bounds__(256) void reduce_lora_kernel(const float *__restric
     }
 }
 
-// The decode reduction for calls that carry segments (batches of 129-256 rows, rank-compact
-// pools, the fp8 base: t comes from the segment-path shrink's chunk sums).  Work item = up to
+// The decode reduction for batches of 129-256 rows (t comes from the segment-path shrink's
+// chunk sums; the rows arrive grouped by adapter).  Work item = up to
 // kSubRows consecutive positions of one adapter's segment (a quarter of a segment tile) x
 // kSegCols columns; base-only positions form items of their own.  Each 16-rank-row chunk of
 // the adapter's B slice is loaded once per item and applied to every row of it, so B is read
@@ -615,10 +614,10 @@ __global__ __launch_bounds__(256) void reduce_seg_kernel(const float *__restrict
     const int row0 = PADRM ? a * RM : adapter_row0(lo.roff, lo.pool_rows, a, lo.pstride, r);
     const uint16_t *bp = lo.B + (size_t)row0 * N + nc;
 
-    // Issued together: every row's split partials (up to four splits), the first TB chunk
+    // Issued together: every row's split partials (up to eight splits), the first TB chunk
     // sums of t (thread (i, j) of the first SUB x RM reads column j of row i; columns at or
     // beyond the rank are not read and stay zero) and the first two 16-row chunks of B.
-    constexpr bool EARLY = MS <= 4;
+    constexpr bool EARLY = MS <= 8;
     float2 pv[EARLY ? SUB : 1][EARLY ? MS : 1];
     if constexpr (EARLY) {
 #pragma unroll
@@ -712,19 +711,26 @@ __global__ __launch_bounds__(256) void reduce_seg_kernel(const float *__restrict
     }
 #undef SEG_LOAD_CHUNK
     const float sc = has ? lo.scale[a] : 0.0f;
+    if constexpr (!EARLY) {
+        // more than eight splits: every row's partials, issued together once B is no longer
+        // held, then added in split order
+        float2 pr[SUB][MS];
 #pragma unroll
-    for (int i = 0; i < SUB; ++i) {
-        if constexpr (!EARLY) {
-            float2 pr[MS];
+        for (int i = 0; i < SUB; ++i)
 #pragma unroll
             for (int sp = 0; sp < MS; ++sp)
-                if (sp < n_splits) pr[sp] = *reinterpret_cast<const float2 *>(pp[i] + sp * stride);
-            acc[i] = pr[0];
+                if (sp < n_splits) pr[i][sp] = *reinterpret_cast<const float2 *>(pp[i] + sp * stride);
+#pragma unroll
+        for (int i = 0; i < SUB; ++i) {
+            acc[i] = pr[i][0];
 #pragma unroll
             for (int sp = 1; sp < MS; ++sp) {
-                if (sp < n_splits) { acc[i].x += pr[sp].x; acc[i].y += pr[sp].y; }
+                if (sp < n_splits) { acc[i].x += pr[i][sp].x; acc[i].y += pr[i][sp].y; }
             }
         }
+    }
+#pragma unroll
+    for (int i = 0; i < SUB; ++i) {
         float2 o = acc[i];
         if (has) {
             o.x = fmaf(sc, d[i][0], o.x);
@@ -878,7 +884,10 @@ hipError_t launch_decode_reduce(const float *partial, int M, int K, int N, void 
     const int n_lt = adapters ? adapter_tiles(M, lo.r_max, lo.n_adapters) : 0;
     const DecPlan p = dec_plan(M, K, N, n_lt);
     const bool padrm = lo.roff == nullptr && lo.pstride == lo.r_max;
-    if (!adapters && seg != nullptr && lora_max_tiles(M, lo.n_adapters) <= kSegMaxTiles) {
+    // (at most kDecodeMaxRows rows the rows of an adapter are too few to share B; there the
+    // row kernel's shorter chain wins)
+    if (!adapters && seg != nullptr && M > kDecodeMaxRows &&
+        lora_max_tiles(M, lo.n_adapters) <= kSegMaxTiles) {
         // one block per (item, kSegCols columns), as many items as a batch of M rows and
         // n adapters can have
         const int max_tiles = lora_max_tiles(M, lo.n_adapters);
@@ -901,6 +910,8 @@ hipError_t launch_decode_reduce(const float *partial, int M, int K, int N, void 
         SEG_ONE(RMX, YF, 2);                                                                    \
     } else if (p.ks <= 4) {                                                                     \
         SEG_ONE(RMX, YF, 4);                                                                    \
+    } else if (p.ks <= 8) {                                                                     \
+        SEG_ONE(RMX, YF, 8);                                                                    \
     } else {                                                                                    \
         SEG_ONE(RMX, YF, 16);                                                                   \
     }

@@ -171,11 +171,12 @@ RANDOM = [
     (33, 1000, 2048, 2056, 400, 8, 0.0, DECODE),
     # the segment-tiled decode reduction (129-256 rows): one adapter on every row (full
     # 16-row tiles, 16 splits), 600 adapters in one-row segments over a single 8-column
-    # chunk, three 1024-column chunks, every row base-only
+    # chunk (8 splits), two and a half 1024-column chunks, every row base-only, four splits
     (34, 256, 2048, 136, 1, 64, 0.0, DECODE),
     (35, 250, 512, 8, 600, 16, 0.3, DECODE),
     (36, 231, 1024, 3072, 6, 32, 0.05, DECODE),
     (37, 256, 256, 1032, 40, 8, 1.0, DECODE),
+    (38, 200, 1024, 2048, 20, 16, 0.1, DECODE),   # four splits
 ]
 
 
