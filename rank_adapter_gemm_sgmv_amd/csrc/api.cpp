@@ -305,7 +305,8 @@ lora_status_t check_tables(const int32_t *ids, int32_t M, const int32_t *ranks,
 //            shrink (chunk sums), the stream-K GEMM, one pass adding its partial tiles, t
 //            and the expand
 //   decode otherwise: build_segments, shrink, shrink_finalize, gemm [, splitk_reduce], expand
-//   prefill: build_segments, shrink, shrink_finalize, gemm with the LoRA epilogue
+//   prefill: build_segments, shrink, gemm with the LoRA epilogue (which adds t from the
+//            shrink's chunk sums)
 // A rank-compact pool (roff != nullptr, lora_linear_compact), and a padded pool whose r_max is
 // not a rank bucket (8, 16, 32, 64), take the same sequences, except that decode batches of
 // at most 128 rows take the second one (the first lays adapters side by side at row stride
@@ -379,16 +380,17 @@ hipError_t run_linear(const void *x, const void *W, const void *A, const void *B
                            rb, n_adapters, sg, spart, kc, ksplit, s)) != hipSuccess)
         return e;
     mark(mk, "shrink");
-    // the stream-K reduction adds the shrink's chunk sums itself; the other consumers read t
+    // the stream-K reduction and the prefill GEMM's epilogue add the shrink's chunk sums
+    // themselves; the expand reads t
     const bool stream_k = !prefill && sk_plan(M, d_in, d_out).use;
-    if (!stream_k) {
+    if (!stream_k && !prefill) {
         if ((e = launch_shrink_finalize(spart, M, rb, ksplit, sg, t, rb, s)) != hipSuccess)
             return e;
         mark(mk, "shrink_finalize");
     }
     int gsplit = 1;
     if (prefill) {
-        LoraEpilogue ep{t, Bb, scale, ids, rb, n_adapters, ranks, roff, pool_rows, pstride};
+        LoraEpilogue ep{spart, ksplit, Bb, scale, ids, rb, n_adapters, ranks, roff, pool_rows, pstride};
         if ((e = launch_gemm(xb, Wb, M, d_in, d_out, y, yf, true, sg, &ep, nullptr, 0, &gsplit, s)) != hipSuccess)
             return e;
         mark(mk, "gemm_prefill_lora");

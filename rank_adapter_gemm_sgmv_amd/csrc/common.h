@@ -125,7 +125,8 @@ hipError_t launch_expand(const float *t, int t_stride, const uint16_t *B, const 
 
 // LoRA epilogue arguments of the prefill GEMM (rows are taken in segment order).
 struct LoraEpilogue {
-    const float *t;        // [M][r_max]
+    const float *tpart;    // [n_chunks][M][r_max]: the shrink's k-chunk sums of t
+    int n_chunks;
     const uint16_t *B;     // [n][r_max][d_out]
     const float *scale;    // [n]
     const int32_t *ids;    // [M]

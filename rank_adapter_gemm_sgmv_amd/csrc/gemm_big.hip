@@ -386,11 +386,31 @@ __global__ __launch_bounds__(C::NT) void gemm_big_kernel(const uint16_t *__restr
                     const int j = rc + (lc & 1) * 8;
                     uint4 v = make_uint4(0, 0, 0, 0);
                     if (pos >= p && pos < q_end && j < RM) {
-                        const float *tp = ep.t + (size_t)seg.perm[pos] * RM + j;
-                        const float4 t0 = *reinterpret_cast<const float4 *>(tp);
-                        const float4 t1 = *reinterpret_cast<const float4 *>(tp + 4);
-                        float f[8] = {s * t0.x, s * t0.y, s * t0.z, s * t0.w,
-                                      s * t1.x, s * t1.y, s * t1.z, s * t1.w};
+                        // t[m, j .. j+7]: the shrink's chunk sums added in chunk order, four
+                        // chunks' loads in flight at a time
+                        const float *tp = ep.tpart + (size_t)seg.perm[pos] * RM + j;
+                        const size_t cs = (size_t)M * RM;
+                        float t[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+                        for (int c0 = 0; c0 < ep.n_chunks; c0 += 4) {
+                            float4 v[4][2];
+#pragma unroll
+                            for (int c = 0; c < 4; ++c) {
+                                const bool in = c0 + c < ep.n_chunks;
+                                const float *q = tp + (size_t)(in ? c0 + c : 0) * cs;
+                                v[c][0] = in ? *reinterpret_cast<const float4 *>(q) : make_float4(0.f, 0.f, 0.f, 0.f);
+                                v[c][1] = in ? *reinterpret_cast<const float4 *>(q + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+                            }
+#pragma unroll
+                            for (int c = 0; c < 4; ++c) {
+                                if (c0 + c < ep.n_chunks) {
+                                    t[0] += v[c][0].x; t[1] += v[c][0].y; t[2] += v[c][0].z; t[3] += v[c][0].w;
+                                    t[4] += v[c][1].x; t[5] += v[c][1].y; t[6] += v[c][1].z; t[7] += v[c][1].w;
+                                }
+                            }
+                        }
+                        float f[8];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) f[e] = s * t[e];
                         if (lc >= 2) {  // the remainder after rounding to bf16
 #pragma unroll
                             for (int e = 0; e < 8; ++e) f[e] -= __uint_as_float(f32_to_bf16_rne(f[e]) << 16);
