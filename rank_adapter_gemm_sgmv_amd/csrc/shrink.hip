@@ -139,7 +139,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void shrink_mfma_kernel(
         if constexpr (!flat) {
             // per LDS fill: A_a[kb .. kb+KS, 0:rank] and x; groups at or beyond the rank, and
             // rows at or beyond the range's end, are zeros instead of loads (a padded pool's
-            // padding is not read).  Unit u = lane + 64 i is (row u / GR, group u % GR); the
+            // padding is not read above r_max 16).  Unit u = lane + 64 i is (row u / GR, group u % GR); the
             // offsets are 32-bit bytes from the adapter's block (one VGPR per address).
             const char *ab = reinterpret_cast<const char *>(Aa);
 #pragma unroll
@@ -151,8 +151,11 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void shrink_mfma_kernel(
                 for (int i = 0; i < C::AL; ++i) {
                     const int u = lane + 64 * i, kr = kb + u / C::GR, gr = u % C::GR;
                     const uint32_t off = ((uint32_t)min(kr, d_in - 1) * (uint32_t)rs + (uint32_t)(gr * 8)) * 2u;
-                    av[i] = gr * 8 < r && kr < k_hi ? *reinterpret_cast<const uint4 *>(ab + off)
-                                                    : make_uint4(0, 0, 0, 0);
+                    // (a padded pool at r_max <= 16 loads its padding too: its loads then need
+                    // not wait for the rank, and the saving would be at most half a row)
+                    const bool want = (LAYOUT == kPadRM && RM <= 16) || gr * 8 < r;
+                    av[i] = want && kr < k_hi ? *reinterpret_cast<const uint4 *>(ab + off)
+                                              : make_uint4(0, 0, 0, 0);
                 }
                 uint4 xv[C::STEPS];
 #pragma unroll
