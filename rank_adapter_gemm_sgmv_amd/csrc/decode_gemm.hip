@@ -583,12 +583,14 @@ __global__ __launch_bounds__(256) void reduce_seg_kernel(const float *__restrict
     if (item >= n_items) return;  // uniform in the block
     __syncthreads();
     int p0, nr, a;
-    const bool has = item < n_sub;
-    if (has) {
+    // (a tile naming no adapter of the pool, possible only in segments a caller built, adds
+    // nothing: its rows keep the base output)
+    const bool has = item < n_sub && s_own[2] >= 0 && s_own[2] < lo.n_adapters;
+    if (item < n_sub) {
         const int t = s_own[0];
         p0 = s_p0[t] + SUB * (item - s_own[1]);
-        nr = min(SUB, s_p0[t + 1] - p0);
-        a = s_own[2];
+        nr = max(min(SUB, s_p0[t + 1] - p0), 1);
+        a = has ? s_own[2] : 0;
     } else {
         p0 = lora_rows + SUB * (item - n_sub);
         nr = min(SUB, M - p0);

@@ -105,7 +105,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void expand_kernel(
     const float *__restrict__ t, int t_stride, const uint16_t *__restrict__ B,
     const float *__restrict__ scale, const int32_t *__restrict__ ranks,
     const int32_t *__restrict__ roff, int pool_rows, int pstride, int M, int d_out, int n_cc,
-    Seg seg, void *__restrict__ y) {
+    int n_adapters, Seg seg, void *__restrict__ y) {
     using L = ExpandLanes<RM>;
     constexpr int CPL = L::CPL;
     const int lane = threadIdx.x & 63;
@@ -114,6 +114,7 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void expand_kernel(
     for (int w = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6); w < total; w += nw) {
         const int tile = w / n_cc, cc = w % n_cc;
         const int p0 = seg.tiles[2 * tile], a = seg.tiles[2 * tile + 1];
+        if (a < 0 || a >= n_adapters) continue;  // only in segments a caller built: adds nothing
         const int p1 = min(p0 + kTileRows, seg.offsets[a + 1]);
         const int width = roff ? RM : pstride;
         int r = ranks ? min(max(ranks[a], 0), width) : width;
@@ -200,10 +201,10 @@ hipError_t launch_rm(const float *t, int t_stride, const uint16_t *B, const floa
     const dim3 block(64 * kWavesPerBlock);
     if (y_f32)
         launch((expand_kernel<RM, true>), grid, block, 0, s, t, t_stride, B, scale, ranks, roff,
-               pool_rows, pstride, M, d_out, n_cc, seg, y);
+               pool_rows, pstride, M, d_out, n_cc, n_adapters, seg, y);
     else
         launch((expand_kernel<RM, false>), grid, block, 0, s, t, t_stride, B, scale, ranks, roff,
-               pool_rows, pstride, M, d_out, n_cc, seg, y);
+               pool_rows, pstride, M, d_out, n_cc, n_adapters, seg, y);
     return hipGetLastError();
 }
 

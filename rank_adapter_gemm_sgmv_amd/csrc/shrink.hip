@@ -95,8 +95,8 @@ enum { kPadRM = 0, kVarW = 1, kFlat = 2 };
 template <int RM, int LAYOUT>
 __global__ __launch_bounds__(64 * kWavesPerBlock) void shrink_mfma_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ A, const int32_t *__restrict__ ranks,
-    const int32_t *__restrict__ roff, int pool_rows, int pstride, int M, int d_in, Seg seg,
-    float *__restrict__ partial, int n_chunks, int kc) {
+    const int32_t *__restrict__ roff, int pool_rows, int pstride, int M, int d_in, int n_adapters,
+    Seg seg, float *__restrict__ partial, int n_chunks, int kc) {
     using C = MfmaShrink<RM>;
     __shared__ __attribute__((aligned(16))) char lds[kWavesPerBlock][C::LDS];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -115,6 +115,9 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void shrink_mfma_kernel(
     for (int it = blockIdx.x; it < total; it += gridDim.x) {
         const int tile = it / n_chunks, c = it % n_chunks;
         const int p0 = seg.tiles[2 * tile], a = seg.tiles[2 * tile + 1];
+        // (a tile naming no adapter of the pool, possible only in segments a caller built, is
+        // skipped by the whole workgroup)
+        if (a < 0 || a >= n_adapters) continue;
         const int rows = min(p0 + kTileRows, seg.offsets[a + 1]) - p0;
         constexpr bool VARW = LAYOUT != kPadRM;
         // width of A_a's rows: RM, the padded stride, or (compact) the rank rounded up to 8
@@ -301,7 +304,7 @@ hipError_t launch_shrink(const uint16_t *x, const uint16_t *A, const int32_t *ra
                                              : kVarW;
 #define LORA_SHRINK_ONE(RMV, LAY)                                                                \
     launch(shrink_mfma_kernel<RMV, LAY>, wgrid, wblock, 0, s, x, A, ranks, roff, pool_rows,      \
-           pstride, M, d_in, seg, partial, ksplit, kc)
+           pstride, M, d_in, n_adapters, seg, partial, ksplit, kc)
 #define LORA_SHRINK_LAUNCH(RMV)                                                                  \
     if (layout == kPadRM) LORA_SHRINK_ONE(RMV, kPadRM);                                          \
     else if (layout == kVarW) LORA_SHRINK_ONE(RMV, kVarW);                                       \

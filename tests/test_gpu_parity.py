@@ -228,6 +228,37 @@ def test_prebuilt_segments_match():
         assert np.array_equal(a, b)
 
 
+def test_prebuilt_segments_bad_tile_adapter():
+    """Caller-built segments whose tile names an adapter outside the pool: the shrink skips the
+    tile and the 129-256-row reduction adds no delta to its rows (they equal a base-only call
+    bit for bit); every other row keeps its parity."""
+    import torch
+
+    from rank_adapter_gemm_sgmv_amd import lora as L
+
+    w = random_case(15, 200, 512, 264, 10, 16, base_frac=0.1)
+    dw = to_device(w)
+    seg = L.Segments(w.M, w.n_adapters)
+    L.lora_build_segments(dw.ids, w.M, w.n_adapters, seg)
+    torch.cuda.synchronize()
+    tiles = seg.tiles.cpu().numpy().reshape(-1, 2)
+    meta = seg.meta.cpu().numpy()
+    offsets = seg.offsets.cpu().numpy()
+    perm = seg.perm.cpu().numpy()
+    t_bad = 0
+    p0, a = int(tiles[t_bad, 0]), int(tiles[t_bad, 1])
+    rows = perm[p0:min(p0 + 16, int(offsets[a + 1]))]
+    tiles[t_bad, 1] = w.n_adapters + 5
+    seg.tiles.copy_(torch.from_numpy(tiles.reshape(-1)))
+    assert int(meta[3]) > 1
+    y = gpu_linear(dw, 0, DECODE, y_f32=True, segs=seg)
+    base = torch.full((w.M,), -1, dtype=torch.int32, device="cuda")
+    yb = gpu_linear(dw, 0, DECODE, y_f32=True, ids=base)
+    assert np.array_equal(y[rows], yb[rows])
+    keep = np.setdiff1d(np.arange(w.M), rows)
+    assert_parity(y[keep], oracle_y(w, 0)[keep], "bad tile adapter: other rows")
+
+
 @pytest.mark.parametrize("r_max", [8, 16, 32, 64])
 def test_shrink_matches_oracle(r_max):
     """lora_shrink alone: t vs the oracle's t (fp32 both; different summation order)."""
