@@ -39,7 +39,10 @@ template <int RM>
 struct MfmaShrink {
     static constexpr int NB = RM >= 16 ? RM / 16 : 1;  // 16-column MFMA blocks
     static constexpr int RMP = 16 * NB;                // columns held in LDS (RM 8 -> 16)
-    static constexpr int KS = 4096 / RMP;              // k rows of A per LDS fill
+    // k rows of A per LDS fill: at most 128, so that a workgroup's four staging areas stay small
+    // enough for five workgroups per CU at r_max <= 16 (with 256 rows three fit, and a batch's
+    // workgroups ran in two rounds)
+    static constexpr int KS = 4096 / RMP < 128 ? 4096 / RMP : 128;
     static constexpr int STEPS = KS / 32;              // 32-deep MFMA steps per fill
     static constexpr int GR = RM / 8;                  // 16-byte groups per row of A_a
     static constexpr int AL = KS * GR / 64;            // 16-byte A loads per lane per fill
