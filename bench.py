@@ -198,10 +198,12 @@ class Runner:
                            self.ws_bytes)
 
     def profile(self, i):
-        """Per-kernel HIP-event durations of one step (queued behind a GPU sleep)."""
-        torch = self.torch
+        """Per-kernel HIP-event durations of one step, queued behind two ordinary steps of other
+        layers: the GPU is then busy as in the timed replays when the step's kernels start (after
+        an idle GPU sleep the first kernel measured up to 15% longer than in the replays)."""
         li = i % self.L
-        torch.cuda._sleep(2_000_000)
+        self.step(i + 1)
+        self.step(i + 2)
         out = []
         if self.segs is not None:
             L_.lora_build_segments(self.ids, self.M, self.n, self.segs)
@@ -626,7 +628,9 @@ class MoeRunner:
         L_.lora_moe_linear(*self._args(i))
 
     def profile(self, i):
-        self.torch.cuda._sleep(2_000_000)
+        # queued behind two ordinary calls of other layers (see Runner.profile)
+        self.step(i + 1)
+        self.step(i + 2)
         return [L_.lora_moe_linear_profiled(*self._args(i))]
 
 
