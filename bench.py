@@ -103,6 +103,9 @@ def algorithmic_work(w, d_in: int, d_out: int, prefill: bool, y_bytes: int = 2) 
         # fp8 base: W8 (one byte per weight) + per-column scales + x
         out["decode_gemm_fp8"] = {"bytes": d_in * d_out + 4 * d_out + M * d_in * 2,
                                   "flops": base_flops}
+        # fp8 base with the shrink as adapter tiles of the same launch (batches of <= 128 rows)
+        out["decode_gemm_fp8_lora"] = {"bytes": d_in * d_out + 4 * d_out + M * d_in * 2 + a_bytes,
+                                       "flops": base_flops + 2.0 * r_rows * d_in}
         out["decode_reduce_lora"] = {"bytes": b_bytes + t_bytes + M * d_out * y_bytes,
                                      "flops": 2.0 * r_rows * d_out}
     return out
@@ -468,6 +471,7 @@ def summarize(w, runner, ms_total, steps, wall, eager_ms, kernels, prefill):
                  "kernels_us": {k: round(v * 1e3, 2) for k, v in ks.items()}}
         gname = "gemm_prefill_lora" if prefill else (
             "decode_gemm_lora" if "decode_gemm_lora" in ks else
+            "decode_gemm_fp8_lora" if "decode_gemm_fp8_lora" in ks else
             "decode_gemm_fp8" if "decode_gemm_fp8" in ks else
             "decode_gemm" if "decode_gemm" in ks else "gemm_decode")
         if gname in ks:

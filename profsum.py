@@ -33,6 +33,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 # kernel function name -> name of the step in lora_linear_profiled / bench.py
 _STEP_OF_KERNEL = [
     ("decode_gemm_kernel", "decode_gemm_lora"),
+    ("decode_gemm_fp8_kernel", "decode_gemm_fp8"),
+    ("decode_gemm_fp8_lora_kernel", "decode_gemm_fp8_lora"),
     ("reduce_lora_kernel", "decode_reduce_lora"),
     ("reduce_seg_kernel", "decode_reduce_lora"),
     ("build_segments_kernel", "build_segments"),

@@ -427,10 +427,12 @@ lora_status_t lora::hip_error_status(hipError_t e) { return hip_status(e); }
 
 namespace {
 
-// lora_linear_fp8w: the quantized-base decode sequence (arguments already validated, M > 0):
-// the fp8 decode GEMM (with the segment build in one extra workgroup unless segments are
-// given), the segment-path shrink (chunk sums), and the decode reduction that adds the GEMM's
-// scaled split partials and the expand.
+// lora_linear_fp8w: the quantized-base decode sequence (arguments already validated, M > 0).
+// Batches of at most 128 rows with r_max a rank bucket: the fp8 GEMM with the shrink as
+// adapter tiles of the same launch, then the decode reduction (two launches, no segments).
+// Otherwise: the fp8 decode GEMM (with the segment build in one extra workgroup unless
+// segments are given), the segment-path shrink (chunk sums), and the decode reduction that
+// adds the GEMM's scaled split partials and the expand.
 hipError_t run_fp8w(const void *x, const void *W8, const float *w_scale, const void *A,
                     const void *B, const float *scale, const int32_t *ranks, const int32_t *ids,
                     int32_t M, int32_t d_in, int32_t d_out, int32_t r_max, int32_t n_adapters,
@@ -438,19 +440,36 @@ hipError_t run_fp8w(const void *x, const void *W8, const float *w_scale, const v
                     hipStream_t s, Marker *mk) {
     char *p = static_cast<char *>(ws);
     lora_segments_t own = carve_segments(p, M, n_adapters);
-    p += t_bytes(M, r_max);
+    float *t = reinterpret_cast<float *>(p); p += t_bytes(M, r_max);
     float *spart = reinterpret_cast<float *>(p); p += shrink_partial_bytes(M, d_in, r_max);
     float *gpart = reinterpret_cast<float *>(p);
     const Seg sg = to_seg(segs ? *segs : own);
     const uint16_t *xb = static_cast<const uint16_t *>(x);
     const int rb = rank_bucket(r_max);
+    hipError_t e;
+    if (r_max == rb && decode_fused_supported(M, d_in, d_out)) {
+        // small batch, pool padded at a rank bucket: the shrink as adapter tiles of the fp8
+        // GEMM's launch (the row -> slot map, when needed, in the t region), then the reduction
+        const DecodeLora lo{nullptr, 0, reinterpret_cast<int32_t *>(t), static_cast<const uint16_t *>(B),
+                            scale, ids, ranks, rb, n_adapters, nullptr, 0, r_max};
+        if ((e = launch_decode_gemm_fp8_lora(xb, static_cast<const uint8_t *>(W8), w_scale,
+                                             static_cast<const uint16_t *>(A), M, d_in, d_out, lo,
+                                             gpart, s)) != hipSuccess)
+            return e;
+        mark(mk, "decode_gemm_fp8_lora");
+        if ((e = launch_decode_reduce(gpart, M, d_in, d_out, y, y_dtype == LORA_F32, lo, true,
+                                      nullptr, s)) != hipSuccess)
+            return e;
+        mark(mk, "decode_reduce_lora");
+        return hipSuccess;
+    }
     int kc, ksplit;
     shrink_plan(d_in, rb, &kc, &ksplit);
     const DecodeLora lo{spart, ksplit, nullptr, static_cast<const uint16_t *>(B), scale, ids, ranks,
                         rb, n_adapters, nullptr, 0, r_max};
     const SegBuild bld{ids, n_adapters, sg};
-    hipError_t e = launch_decode_gemm_fp8(xb, static_cast<const uint8_t *>(W8), w_scale, M, d_in,
-                                          d_out, gpart, segs ? nullptr : &bld, s);
+    e = launch_decode_gemm_fp8(xb, static_cast<const uint8_t *>(W8), w_scale, M, d_in, d_out, gpart,
+                               segs ? nullptr : &bld, s);
     if (e != hipSuccess) return e;
     mark(mk, "decode_gemm_fp8");
     if ((e = launch_shrink(xb, static_cast<const uint16_t *>(A), ranks, nullptr, 0, r_max, M, d_in,

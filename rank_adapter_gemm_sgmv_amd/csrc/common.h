@@ -238,6 +238,14 @@ hipError_t launch_decode_gemm_fp8(const uint16_t *x, const uint8_t *W8, const fl
                                   int M, int K, int N, float *partial, const SegBuild *build,
                                   hipStream_t s);
 
+// The same fp8 GEMM with the shrink x A_a as adapter tiles of the same launch (a batch of at
+// most kDecodeMaxRows rows, a pool padded at a rank bucket: lo.r_max 8, 16, 32 or 64; the row
+// -> slot map goes to lo.slots when the pool is larger than the batch): the partial tiles of
+// dec_plan with adapter tiles, what launch_decode_reduce (adapters = true) adds.
+hipError_t launch_decode_gemm_fp8_lora(const uint16_t *x, const uint8_t *W8, const float *w_scale,
+                                       const uint16_t *A, int M, int K, int N,
+                                       const DecodeLora &lo, float *partial, hipStream_t s);
+
 // y = (split partials added in order) + scale_a * t B_a, t from the adapter tiles' splits
 // (`adapters`) or from the segment-path shrink's chunk sums; rounds once into y.  With the
 // chunk sums and `seg` (the segments of these ids, nullable) the rows of one adapter share

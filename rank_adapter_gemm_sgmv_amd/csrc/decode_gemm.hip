@@ -43,6 +43,96 @@ namespace lora {
 
 namespace {
 
+// Sources of adapter tile lt of a fused call: the batch's adapters laid side by side, 128 / RM
+// per tile, numbered by id when the pool is no larger than the batch, else by first use (the
+// grouping found in LDS; leave_slots: this workgroup also leaves the row -> slot map for the
+// reduction).  Returns false -- for the whole workgroup -- when the tile holds no adapter of
+// the batch.  Every thread must call it (barriers).
+template <class C, int RM>
+__device__ __forceinline__ bool dec_adapter_src(DecSrc<C> &src, BatchAdapters &ba,
+                                                const DecodeLora &lo, const uint16_t *A, int M,
+                                                int K, int lt, bool leave_slots, int tid,
+                                                int lane) {
+    constexpr int APT = AdapterTiles<RM>::APT;
+    const bool by_id = lo.n_adapters <= M;
+    int T = lo.n_adapters;
+    if (!by_id) {
+        batch_adapters(ba, lo.ids, M, lo.n_adapters);  // every thread: barriers
+        T = ba.T;
+        if (leave_slots)
+            for (int m = tid; m < M; m += kThreads) lo.slots[m] = ba.slot[m];
+    }
+    if (lt * APT >= T) return false;  // no adapter of the batch in this tile
+    if (by_id) {
+        // numbered by id, a tile may hold only adapters no row of the batch uses
+        bool used = false;
+        for (int m = tid; m < M; m += kThreads) {
+            const int d = lo.ids[m] - lt * APT;
+            used |= d >= 0 && d < APT;
+        }
+        if (!__syncthreads_or(used)) return false;
+    }
+#pragma unroll
+    for (int q = 0; q < C::WINS; ++q) {
+        const int r = 4 * q + (lane >> 4);
+        const int col = ((lane & 15) ^ wsw(r)) * 8;
+        const int sl = lt * APT + col / RM;
+        // slots past the last read a valid adapter; their columns are never used
+        const int a = sl < T ? (by_id ? sl : ba.list[sl]) : (by_id ? 0 : ba.list[0]);
+        src.wp[q] = A + ((size_t)a * K + r) * RM + col % RM;
+    }
+    return true;
+}
+
+// x rows m0 .. m0 + BM of a tile: lane l fills position l % 8 of row 8 q + l / 8, chunk
+// (l % 8) ^ (l / 8); rows past the batch repeat its last.
+template <class C>
+__device__ __forceinline__ void dec_x_src(DecSrc<C> &src, const uint16_t *x, int M, int K,
+                                          int m0, int lane) {
+#pragma unroll
+    for (int q = 0; q < C::XINS; ++q) {
+        const int row = 8 * q + (lane >> 3);
+        const int lc = (lane & 7) ^ (lane >> 3);
+        const int m = min(m0 + row, M - 1);
+        src.xp[q] = x + (size_t)m * K + lc * 8;
+    }
+}
+
+// After a tile's K loop: wait for every load, add the four waves' partial tiles in wave order
+// through LDS and write the workgroup's partial tile to `mine`.  The reduction that follows
+// starts with dependent loads of the small tables (a row's adapter, then its rank and scale,
+// then B); left to it they come from HBM.  Touched here (loads from asm, results unused),
+// they are in every XCD's L2 by then; the registers they land in are handed to an empty asm
+// after the wait, so the compiler gives them to nothing else while the loads are in flight.
+// Every thread must call it (barriers).
+template <class C>
+__device__ __forceinline__ void dec_tile_out(const f32x16_t (&acc)[C::TM][C::TN], uint4 *lds,
+                                             const DecodeLora &lo, int M, float *mine, int tid,
+                                             int lane, int wave) {
+    uint32_t d0, d1, d2;
+    {
+        const int mm = min(tid, M - 1), aa = min(tid, lo.n_adapters - 1);
+        asm volatile("global_load_dword %0, %1, off" : "=v"(d0) : "v"(lo.ids + mm));
+        asm volatile("global_load_dword %0, %1, off" : "=v"(d1) : "v"(lo.scale + aa));
+        asm volatile("global_load_dword %0, %1, off" : "=v"(d2) : "v"(lo.ranks ? lo.ranks + aa : lo.ids + mm));
+    }
+    wait_vm<0>();
+    asm volatile("" ::"v"(d0), "v"(d1), "v"(d2));
+    __syncthreads();  // every wave is done with its stages
+
+    float4 *const red = reinterpret_cast<float4 *>(lds);
+    reduce_waves_put<C>(acc, red + wave * (C::TILE / 4), lane);
+    __syncthreads();
+    const int col = tid & 127;
+#pragma unroll
+    for (int q = 0; q < C::BM / 8; ++q) {
+        const int g = (tid >> 7) + 2 * q;  // rows 4 g .. 4 g + 3
+        const float4 s = reduce_waves_group<C>(red, g, col);
+        float *o = mine + (4 * g) * kBN + col;
+        o[0] = s.x; o[kBN] = s.y; o[2 * kBN] = s.z; o[3 * kBN] = s.w;
+    }
+}
+
 // Workgroup (tile, split), four waves.  Each wave streams its quarter of split `split` of K
 // (rows [split k_per_split, +k_per_split)) for one 128-column tile -- of W, or of the
 // adapters' A laid side by side -- and the workgroup writes its partial tile;
@@ -56,7 +146,6 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(
     // wave w's part: x stages 0, 1 then W stages 0 .. 3; after the K loop, its partial tile
     __shared__ __attribute__((aligned(1024))) uint4 lds[kWaves * C::WAVE];
     __shared__ BatchAdapters ba;
-    constexpr int APT = AdapterTiles<RM>::APT;
 
     if (BUILD && (int)blockIdx.x >= n_gemm_blocks) {
         // the extra workgroup: the segment build, in this kernel's LDS (the launch is a grid of
@@ -99,44 +188,12 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(
         }
     } else {
         const int lt = tn - n_tn;
-        const bool by_id = lo.n_adapters <= M;
-        int T = lo.n_adapters;
-        if (!by_id) {
-            batch_adapters(ba, lo.ids, M, lo.n_adapters);  // every thread: barriers
-            T = ba.T;
-            // one workgroup leaves the row -> slot map for the reduction
-            if (lt == 0 && split == 0 && tm == 0)
-                for (int m = tid; m < M; m += kThreads) lo.slots[m] = ba.slot[m];
-        }
-        if (lt * APT >= T) return;  // no adapter of the batch in this tile (whole workgroup)
-        if (by_id) {
-            // numbered by id, a tile may hold only adapters no row of the batch uses
-            bool used = false;
-            for (int m = tid; m < M; m += kThreads) {
-                const int d = lo.ids[m] - lt * APT;
-                used |= d >= 0 && d < APT;
-            }
-            if (!__syncthreads_or(used)) return;  // whole workgroup
-        }
-#pragma unroll
-        for (int q = 0; q < C::WINS; ++q) {
-            const int r = 4 * q + (lane >> 4);
-            const int col = ((lane & 15) ^ wsw(r)) * 8;
-            const int sl = lt * APT + col / RM;
-            // slots past the last read a valid adapter; their columns are never used
-            const int a = sl < T ? (by_id ? sl : ba.list[sl]) : (by_id ? 0 : ba.list[0]);
-            src.wp[q] = A + ((size_t)a * K + r) * RM + col % RM;
-        }
+        if (!dec_adapter_src<C, RM>(src, ba, lo, A, M, K, lt, lt == 0 && split == 0 && tm == 0,
+                                    tid, lane))
+            return;  // whole workgroup
         ldw = RM;
     }
-#pragma unroll
-    for (int q = 0; q < C::XINS; ++q) {
-        // lane l fills position l % 8 of row 8 q + l / 8: chunk (l % 8) ^ (l / 8)
-        const int row = 8 * q + (lane >> 3);
-        const int lc = (lane & 7) ^ (lane >> 3);
-        const int m = min(m0 + row, M - 1);  // rows past the batch repeat its last
-        src.xp[q] = x + (size_t)m * K + lc * 8;
-    }
+    dec_x_src<C>(src, x, M, K, m0, lane);
 
     f32x16_t acc[C::TM][C::TN];
 #pragma unroll
@@ -153,34 +210,8 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(
     const int kw1 = min(ks1, kw0 + per_wave);
     const int nst = (kw1 - kw0) / kBKW;
     dec_kloop<C>(acc, src, lds + wave * C::WAVE, kw0, nst, K, ldw, lane);
-    // The reduction that follows starts with dependent loads of these small tables (a row's
-    // adapter, then its rank and scale, then B); left to it they come from HBM.  Touched here
-    // (loads from asm, results unused), they are in every XCD's L2 by then.  The registers
-    // they land in are handed to an empty asm after the wait below, so that the compiler
-    // gives them to nothing else while the loads are in flight.
-    uint32_t d0, d1, d2;
-    {
-        const int mm = min(tid, M - 1), aa = min(tid, lo.n_adapters - 1);
-        asm volatile("global_load_dword %0, %1, off" : "=v"(d0) : "v"(lo.ids + mm));
-        asm volatile("global_load_dword %0, %1, off" : "=v"(d1) : "v"(lo.scale + aa));
-        asm volatile("global_load_dword %0, %1, off" : "=v"(d2) : "v"(lo.ranks ? lo.ranks + aa : lo.ids + mm));
-    }
-    wait_vm<0>();
-    asm volatile("" ::"v"(d0), "v"(d1), "v"(d2));
-    __syncthreads();  // every wave is done with its stages
-
-    float4 *const red = reinterpret_cast<float4 *>(lds);
-    reduce_waves_put<C>(acc, red + wave * (C::TILE / 4), lane);
-    __syncthreads();
-    float *mine = partial + ((size_t)split * n_tiles + tile) * C::TILE;
-    const int col = tid & 127;
-#pragma unroll
-    for (int q = 0; q < C::BM / 8; ++q) {
-        const int g = (tid >> 7) + 2 * q;  // rows 4 g .. 4 g + 3
-        const float4 s = reduce_waves_group<C>(red, g, col);
-        float *o = mine + (4 * g) * kBN + col;
-        o[0] = s.x; o[kBN] = s.y; o[2 * kBN] = s.z; o[3 * kBN] = s.w;
-    }
+    dec_tile_out<C>(acc, lds, lo, M, partial + ((size_t)split * n_tiles + tile) * C::TILE, tid,
+                    lane, wave);
 }
 
 // ---- the same split-K GEMM with an fp8 base weight -----------------------------------------
@@ -238,31 +269,16 @@ __device__ __forceinline__ bf16x8_t dec_fp8x8(uint32_t lo, uint32_t hi) {
     return bf16x8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-// Workgroup (tile, split): rows m0 .. m0 + BM of x, columns n0 .. n0 + 127 (wave w: 32 w ..),
-// k in the split.  BUILD: one more workgroup (the last) builds the segments instead.
-template <class C, bool BUILD>
-__global__ __launch_bounds__(kThreads) void decode_gemm_fp8_kernel(
-    const uint16_t *__restrict__ x, const uint8_t *__restrict__ W8, const float *__restrict__ w_scale,
-    int M, int K, int N, int n_tm, int n_tn, int k_per_split, float *__restrict__ partial,
-    int n_gemm_blocks, SegBuild build) {
-    __shared__ __attribute__((aligned(1024))) uint4 lds[C::LDS16];
-
-    if (BUILD && (int)blockIdx.x >= n_gemm_blocks) {
-        int32_t *cnt = reinterpret_cast<int32_t *>(lds);
-        int32_t(*wave_tot)[kWaves] =
-            reinterpret_cast<int32_t(*)[kWaves]>(cnt + ((build.n_adapters + 1 + 15) & ~15));
-        build_segments_block<kThreads>(build.ids, M, build.n_adapters, build.seg, cnt, wave_tot,
-                                       &wave_tot[3][0]);
-        return;
-    }
-
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int n_tiles = n_tm * n_tn;
-    int lin = blockIdx.x;
-    if (n_tm > 1 && (n_gemm_blocks & 7) == 0) lin = (blockIdx.x & 7) * (n_gemm_blocks >> 3) + (blockIdx.x >> 3);
-    const int tile = lin % n_tiles, split = lin / n_tiles;
-    const int tm = tile % n_tm, tn = tile / n_tm;
+// Workgroup (tile, split) of fp8 W tile tn: rows m0 .. m0 + BM of x, columns n0 .. n0 + 127
+// (wave w: 32 w ..), k in the split; writes partial tile `tile` of split `split` (n_tiles
+// tiles per split).  Every thread must call it (barriers).
+template <class C>
+__device__ __forceinline__ void f8_tile(uint4 *lds, const uint16_t *__restrict__ x,
+                                        const uint8_t *__restrict__ W8,
+                                        const float *__restrict__ w_scale, int M, int K, int N,
+                                        int n_tiles, int tile, int split, int tm, int tn,
+                                        int k_per_split, float *__restrict__ partial, int lane,
+                                        int wave) {
     const int m0 = tm * C::BM, n0 = tn * kBN;
     const int ks0 = split * k_per_split;
     const int ks1 = min(K, ks0 + k_per_split);
@@ -352,6 +368,85 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_fp8_kernel(
 #pragma unroll
         for (int v = 0; v < 16; ++v)
             P[(size_t)(32 * i + (v / 4) * 8 + g * 4 + v % 4) * kBN] = sc * (acc[i][0][v] + acc[i][1][v]);
+}
+
+// Workgroup (tile, split) of the fp8 GEMM.  BUILD: one more workgroup (the last) builds the
+// segments instead.
+template <class C, bool BUILD>
+__global__ __launch_bounds__(kThreads) void decode_gemm_fp8_kernel(
+    const uint16_t *__restrict__ x, const uint8_t *__restrict__ W8, const float *__restrict__ w_scale,
+    int M, int K, int N, int n_tm, int n_tn, int k_per_split, float *__restrict__ partial,
+    int n_gemm_blocks, SegBuild build) {
+    __shared__ __attribute__((aligned(1024))) uint4 lds[C::LDS16];
+
+    if (BUILD && (int)blockIdx.x >= n_gemm_blocks) {
+        int32_t *cnt = reinterpret_cast<int32_t *>(lds);
+        int32_t(*wave_tot)[kWaves] =
+            reinterpret_cast<int32_t(*)[kWaves]>(cnt + ((build.n_adapters + 1 + 15) & ~15));
+        build_segments_block<kThreads>(build.ids, M, build.n_adapters, build.seg, cnt, wave_tot,
+                                       &wave_tot[3][0]);
+        return;
+    }
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n_tiles = n_tm * n_tn;
+    int lin = blockIdx.x;
+    if (n_tm > 1 && (n_gemm_blocks & 7) == 0) lin = (blockIdx.x & 7) * (n_gemm_blocks >> 3) + (blockIdx.x >> 3);
+    const int tile = lin % n_tiles, split = lin / n_tiles;
+    f8_tile<C>(lds, x, W8, w_scale, M, K, N, n_tiles, tile, split, tile % n_tm, tile / n_tm,
+               k_per_split, partial, lane, wave);
+}
+
+// The fp8 GEMM with the shrink as adapter tiles, for batches of at most kDecodeMaxRows rows
+// and pools padded at a rank bucket: column tiles 0 .. n_tn - 1 are fp8 W tiles (f8_tile),
+// the next n_lt are adapter tiles streamed by the bf16 decode GEMM's core (decode_tiles.h),
+// all with one split plan (dec_plan with the adapter tiles) and one partial layout, so the
+// decode reduction adds W's scaled splits and sums t from the adapter tiles exactly as after
+// decode_gemm_kernel.  Both kinds of workgroup share one LDS array sized for the larger.
+template <class CF, class CB, int RM>
+__global__ __launch_bounds__(kThreads) void decode_gemm_fp8_lora_kernel(
+    const uint16_t *__restrict__ x, const uint8_t *__restrict__ W8, const float *__restrict__ w_scale,
+    const uint16_t *__restrict__ A, int M, int K, int N, int n_tm, int n_tn, int n_lt,
+    int k_per_split, float *__restrict__ partial, DecodeLora lo, int n_gemm_blocks) {
+    static_assert(CF::BM == CB::BM && CF::TILE == CB::TILE, "one tile shape");
+    constexpr int L16 = CF::LDS16 > kWaves * CB::WAVE ? CF::LDS16 : kWaves * CB::WAVE;
+    __shared__ __attribute__((aligned(1024))) uint4 lds[L16];
+    __shared__ BatchAdapters ba;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n_tiles = n_tm * (n_tn + n_lt);
+    int lin = blockIdx.x;
+    if (n_tm > 1 && (n_gemm_blocks & 7) == 0) lin = (blockIdx.x & 7) * (n_gemm_blocks >> 3) + (blockIdx.x >> 3);
+    const int tile = lin % n_tiles, split = lin / n_tiles;
+    const int tm = tile % n_tm, tn = tile / n_tm;
+    if (tn < n_tn) {
+        f8_tile<CF>(lds, x, W8, w_scale, M, K, N, n_tiles, tile, split, tm, tn, k_per_split,
+                    partial, lane, wave);
+        return;
+    }
+    const int lt = tn - n_tn;
+    DecSrc<CB> src;
+    if (!dec_adapter_src<CB, RM>(src, ba, lo, A, M, K, lt, lt == 0 && split == 0 && tm == 0, tid,
+                                 lane))
+        return;  // whole workgroup
+    dec_x_src<CB>(src, x, M, K, tm * CB::BM, lane);
+    f32x16_t acc[CB::TM][CB::TN];
+#pragma unroll
+    for (int i = 0; i < CB::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < CB::TN; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+    const int ks0 = split * k_per_split;
+    const int ks1 = min(K, ks0 + k_per_split);
+    const int per_wave = k_per_split / kWaves;  // multiple of 16
+    const int kw0 = min(ks1, ks0 + wave * per_wave);
+    const int kw1 = min(ks1, kw0 + per_wave);
+    dec_kloop<CB>(acc, src, lds + wave * CB::WAVE, kw0, (kw1 - kw0) / kBKW, K, RM, lane);
+    dec_tile_out<CB>(acc, lds, lo, M, partial + ((size_t)split * n_tiles + tile) * CB::TILE, tid,
+                     lane, wave);
 }
 
 // y[m, n .. n+3] = (sum over splits, in order, of the partial tiles)
@@ -873,6 +968,37 @@ hipError_t launch_decode_gemm_fp8(const uint16_t *x, const uint8_t *W8, const fl
         F8_LAUNCH(64);
     }
 #undef F8_LAUNCH
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_gemm_fp8_lora(const uint16_t *x, const uint8_t *W8, const float *w_scale,
+                                       const uint16_t *A, int M, int K, int N,
+                                       const DecodeLora &lo, float *partial, hipStream_t s) {
+    if (!decode_fused_supported(M, K, N) || N % 8 != 0 || partial == nullptr ||
+        w_scale == nullptr || A == nullptr || lo.ids == nullptr || !rank_ok(lo.r_max) ||
+        lo.n_adapters < 1 || (lo.n_adapters > M && lo.slots == nullptr))
+        return hipErrorInvalidValue;
+    const int n_lt = adapter_tiles(M, lo.r_max, lo.n_adapters);
+    const DecPlan p = dec_plan(M, K, N, n_lt);
+    const int n_gemm = p.n_tm * (p.n_tn + n_lt) * p.ks;
+#define F8L_ONE(BM, RMX)                                                                        \
+    launch((decode_gemm_fp8_lora_kernel<DecF8<BM>, Dec<BM>, RMX>), dim3(n_gemm), dim3(kThreads), \
+           0, s, x, W8, w_scale, A, M, K, N, p.n_tm, p.n_tn, n_lt, p.k_per_split, partial, lo,   \
+           n_gemm)
+#define F8L_RANK(BM)                                                                            \
+    switch (lo.r_max) {                                                                         \
+        case 8: F8L_ONE(BM, 8); break;                                                          \
+        case 16: F8L_ONE(BM, 16); break;                                                        \
+        case 32: F8L_ONE(BM, 32); break;                                                        \
+        default: F8L_ONE(BM, 64); break;                                                        \
+    }
+    if (p.bm == 32) {
+        F8L_RANK(32)
+    } else {
+        F8L_RANK(64)
+    }
+#undef F8L_RANK
+#undef F8L_ONE
     return hipGetLastError();
 }
 

@@ -78,6 +78,11 @@ CASES = [
     (406, 200, 512, 4104, 9, 64, 0.3),      # 129-256 rows
     (407, 256, 11008, 256, 70, 16, 0.1),    # long K
     (408, 33, 192, 8, 4, 5, 0.25),          # one ragged column tile, a short split
+    # up to 128 rows with r_max a rank bucket, the shrink runs as adapter tiles of the fp8
+    # GEMM's launch: r_max 64 with adapters numbered by id (64-row tiles) and by first use
+    # (32-row tiles)
+    (411, 48, 512, 264, 20, 64, 0.1),
+    (412, 20, 256, 136, 40, 64, 0.2),
 ]
 
 
