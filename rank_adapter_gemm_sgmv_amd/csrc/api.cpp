@@ -307,8 +307,8 @@ lora_status_t check_tables(const int32_t *ids, int32_t M, const int32_t *ranks,
 //   decode otherwise: build_segments, shrink, shrink_finalize, gemm [, splitk_reduce], expand
 //   prefill: build_segments, shrink, gemm with the LoRA epilogue (which adds t from the
 //            shrink's chunk sums)
-// A rank-compact pool (roff != nullptr, lora_linear_compact), and a padded pool whose r_max is
-// not a rank bucket (8, 16, 32, 64), take the same sequences, except that decode batches of
+// A rank-compact pool (roff != nullptr, lora_linear_compact) takes the same sequences; a padded
+// pool whose r_max is not a rank bucket (8, 16, 32, 64) too, except that its decode batches of
 // at most 128 rows take the second one (the first lays adapters side by side at row stride
 // r_max = the bucket).
 hipError_t run_linear(const void *x, const void *W, const void *A, const void *B,
@@ -336,14 +336,14 @@ hipError_t run_linear(const void *x, const void *W, const void *A, const void *B
     const int rb = rank_bucket(r_max), pstride = r_max;
     int kc, ksplit;
     shrink_plan(d_in, rb, &kc, &ksplit);
-    // (the fused path lays adapters side by side at row stride rb: padded pools whose stride
-    // is the bucket only)
-    if (!prefill && roff == nullptr && r_max == rb && decode_fused_supported(M, d_in, d_out)) {
+    // (the fused path lays adapters side by side at column stride rb: a padded pool whose row
+    // stride is the bucket, or a rank-compact pool, each adapter read at its own row width)
+    if (!prefill && (roff != nullptr || r_max == rb) && decode_fused_supported(M, d_in, d_out)) {
         // small decode batch: x W and the shrink x A_i as tiles of one split-K GEMM (the
         // row -> adapter slot map, when needed, goes to the t region), then one reduction
         // adds the splits and the expand
         const DecodeLora lo{nullptr, 0, reinterpret_cast<int32_t *>(t), Bb, scale, ids, ranks, rb,
-                            n_adapters, nullptr, 0, pstride};
+                            n_adapters, roff, pool_rows, pstride};
         if ((e = launch_decode_gemm(xb, Wb, static_cast<const uint16_t *>(A), M, d_in, d_out, lo,
                                     true, gpart, nullptr, s)) != hipSuccess)
             return e;

@@ -35,6 +35,8 @@
 //    does not depend on scheduling.
 //  * Batches of 129-256 rows (which come with segments) take reduce_seg_kernel instead: the
 //    same sums for items of four rows of one adapter, each B_a chunk loaded once per item.
+#include <type_traits>
+
 #include "batch_adapters.h"
 #include "decode_tiles.h"
 #include "segments_block.h"
@@ -48,12 +50,12 @@ namespace {
 // grouping found in LDS; leave_slots: this workgroup also leaves the row -> slot map for the
 // reduction).  Returns false -- for the whole workgroup -- when the tile holds no adapter of
 // the batch.  Every thread must call it (barriers).
-template <class C, int RM>
-__device__ __forceinline__ bool dec_adapter_src(DecSrc<C> &src, BatchAdapters &ba,
-                                                const DecodeLora &lo, const uint16_t *A, int M,
-                                                int K, int lt, bool leave_slots, int tid,
-                                                int lane) {
+template <class C, int RM, class S>
+__device__ __forceinline__ bool dec_adapter_src(S &src, BatchAdapters &ba, const DecodeLora &lo,
+                                                const uint16_t *A, int M, int K, int lt,
+                                                bool leave_slots, int tid, int lane) {
     constexpr int APT = AdapterTiles<RM>::APT;
+    constexpr bool COMPACT = !std::is_same<S, DecSrc<C>>::value;
     const bool by_id = lo.n_adapters <= M;
     int T = lo.n_adapters;
     if (!by_id) {
@@ -79,16 +81,33 @@ __device__ __forceinline__ bool dec_adapter_src(DecSrc<C> &src, BatchAdapters &b
         const int sl = lt * APT + col / RM;
         // slots past the last read a valid adapter; their columns are never used
         const int a = sl < T ? (by_id ? sl : ba.list[sl]) : (by_id ? 0 : ba.list[0]);
-        src.wp[q] = A + ((size_t)a * K + r) * RM + col % RM;
+        if constexpr (!COMPACT) {
+            src.wp[q] = A + ((size_t)a * K + r) * RM + col % RM;
+        } else {
+            // the adapter's own block: rows round8(rank) wide from its first rank row; groups
+            // past its width read its last group again (same lines, no HBM bytes; those t
+            // columns lie past the rank and are never read).  An adapter whose rows leave
+            // the pool (rank read as 0) reads element 0 at stride 0; it adds nothing.
+            int rk = lo.ranks ? min(max(lo.ranks[a], 1), RM) : RM;
+            const int row0 = adapter_row0(lo.roff, lo.pool_rows, a, 0, rk);
+            const int w = (rk + 7) & ~7;
+            if (rk > 0) {
+                src.wp[q] = A + (size_t)row0 * K + (size_t)r * w + min(col % RM, w - 8);
+                src.ws[q] = (uint32_t)w;
+            } else {
+                src.wp[q] = A;
+                src.ws[q] = 0;
+            }
+        }
     }
     return true;
 }
 
 // x rows m0 .. m0 + BM of a tile: lane l fills position l % 8 of row 8 q + l / 8, chunk
 // (l % 8) ^ (l / 8); rows past the batch repeat its last.
-template <class C>
-__device__ __forceinline__ void dec_x_src(DecSrc<C> &src, const uint16_t *x, int M, int K,
-                                          int m0, int lane) {
+template <class C, class S>
+__device__ __forceinline__ void dec_x_src(S &src, const uint16_t *x, int M, int K, int m0,
+                                          int lane) {
 #pragma unroll
     for (int q = 0; q < C::XINS; ++q) {
         const int row = 8 * q + (lane >> 3);
@@ -138,7 +157,7 @@ __device__ __forceinline__ void dec_tile_out(const f32x16_t (&acc)[C::TM][C::TN]
 // adapters' A laid side by side -- and the workgroup writes its partial tile;
 // reduce_lora_kernel adds the splits in order.
 // BUILD: one more workgroup (the last) builds the segments instead (see SegBuild).
-template <class C, int RM, bool BUILD>
+template <class C, int RM, bool BUILD, bool CPT>
 __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ W, const uint16_t *__restrict__ A,
     int M, int K, int N, int n_tm, int n_tn, int n_lt, int k_per_split, float *__restrict__ partial,
@@ -175,8 +194,9 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(
 
     // per-lane sources of the tile: W, or the adapters of this adapter tile.  Direct load q of
     // a W stage: lane l fills position l % 16 of row 4 q + l / 16, i.e. chunk
-    // (l % 16) ^ wsw(row) of the row's 16.
-    DecSrc<C> src;
+    // (l % 16) ^ wsw(row) of the row's 16.  CPT: the adapters come from a rank-compact pool,
+    // each load with its adapter's row stride.
+    std::conditional_t<CPT, DecSrcVS<C>, DecSrc<C>> src;
     size_t ldw = (size_t)N;
     if (tn < n_tn) {
         const int n0 = tn * kBN;
@@ -185,6 +205,7 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(
             const int r = 4 * q + (lane >> 4);
             const int lc = (lane & 15) ^ wsw(r);
             src.wp[q] = W + (size_t)r * N + min(n0 + lc * 8, N - 8);
+            if constexpr (CPT) src.ws[q] = (uint32_t)N;
         }
     } else {
         const int lt = tn - n_tn;
@@ -920,13 +941,18 @@ hipError_t launch_decode_gemm(const uint16_t *x, const uint16_t *W, const uint16
     const int n_gemm = p.n_tm * (p.n_tn + p.n_lt) * p.ks;
     const dim3 grid(n_gemm + (build ? 1 : 0));
     const SegBuild bld = build ? *build : SegBuild{nullptr, 1, Seg{}};
+    // adapter tiles from a rank-compact pool read each adapter at its own row stride
+    const bool cpt = adapters && lo.roff != nullptr;
 #define GEMM_LAUNCH(BM, RMX)                                                                  \
     if (build)                                                                                \
-        launch((decode_gemm_kernel<Dec<BM>, RMX, true>), grid, dim3(kThreads), 0, s, x, W, A, M, \
-               K, N, p.n_tm, p.n_tn, p.n_lt, p.k_per_split, partial, lo, n_gemm, bld);         \
+        launch((decode_gemm_kernel<Dec<BM>, RMX, true, false>), grid, dim3(kThreads), 0, s, x, W, \
+               A, M, K, N, p.n_tm, p.n_tn, p.n_lt, p.k_per_split, partial, lo, n_gemm, bld);   \
+    else if (cpt)                                                                             \
+        launch((decode_gemm_kernel<Dec<BM>, RMX, false, true>), grid, dim3(kThreads), 0, s, x, W, \
+               A, M, K, N, p.n_tm, p.n_tn, p.n_lt, p.k_per_split, partial, lo, n_gemm, bld);   \
     else                                                                                      \
-        launch((decode_gemm_kernel<Dec<BM>, RMX, false>), grid, dim3(kThreads), 0, s, x, W, A, M,\
-               K, N, p.n_tm, p.n_tn, p.n_lt, p.k_per_split, partial, lo, n_gemm, bld)
+        launch((decode_gemm_kernel<Dec<BM>, RMX, false, false>), grid, dim3(kThreads), 0, s, x,  \
+               W, A, M, K, N, p.n_tm, p.n_tn, p.n_lt, p.k_per_split, partial, lo, n_gemm, bld)
 #define GEMM_RANK(BM)                                                                         \
     switch (lo.r_max) {                                                                       \
         case 8: GEMM_LAUNCH(BM, 8); break;                                                    \

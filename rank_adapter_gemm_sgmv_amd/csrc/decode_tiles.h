@@ -92,6 +92,20 @@ struct DecSrc {
     const uint16_t *xp[C::XINS];
     const uint16_t *wp[C::WINS];
 };
+// The same with a row stride per W load: adapters of a rank-compact pool side by side in one
+// tile, each load reading its own adapter's block (rows round8(rank) wide).
+template <class C>
+struct DecSrcVS {
+    const uint16_t *xp[C::XINS];
+    const uint16_t *wp[C::WINS];
+    uint32_t ws[C::WINS];  // row stride of load q, elements
+};
+template <class C>
+__device__ __forceinline__ size_t dec_wstride(const DecSrc<C> &, int, size_t ldw) { return ldw; }
+template <class C>
+__device__ __forceinline__ size_t dec_wstride(const DecSrcVS<C> &src, int q, size_t) {
+    return src.ws[q];
+}
 
 // Direct global -> LDS load of 16 bytes per lane: lane i's bytes land at LDS address
 // m0 + 16 i.  Issued from asm so that the compiler adds no wait of its own for it: its
@@ -104,16 +118,17 @@ __device__ __forceinline__ void dma16(const void *g, const lds_void_t *l) {
                  : "memory", "m0");
 }
 
-// A W stage of this wave: rows k0 .. k0+15 of the tile (row stride ldw).
-template <class C>
-__device__ __forceinline__ void dec_issue_w(const DecSrc<C> &src, uint4 *__restrict__ wslot, int k0,
+// A W stage of this wave: rows k0 .. k0+15 of the tile (row stride ldw, or the load's own).
+template <class C, class S>
+__device__ __forceinline__ void dec_issue_w(const S &src, uint4 *__restrict__ wslot, int k0,
                                             size_t ldw) {
 #pragma unroll
-    for (int q = 0; q < C::WINS; ++q) dma16(src.wp[q] + (size_t)k0 * ldw, (const lds_void_t *)&wslot[q * 64]);
+    for (int q = 0; q < C::WINS; ++q)
+        dma16(src.wp[q] + (size_t)k0 * dec_wstride<C>(src, q, ldw), (const lds_void_t *)&wslot[q * 64]);
 }
 // An x stage of this wave: x[rows][k0 .. k0+63].
-template <class C>
-__device__ __forceinline__ void dec_issue_x(const DecSrc<C> &src, uint4 *__restrict__ xslot, int k0) {
+template <class C, class S>
+__device__ __forceinline__ void dec_issue_x(const S &src, uint4 *__restrict__ xslot, int k0) {
 #pragma unroll
     for (int q = 0; q < C::XINS; ++q) dma16(src.xp[q] + k0, (const lds_void_t *)&xslot[q * 64]);
 }
@@ -165,8 +180,8 @@ struct AdapterTiles {
 // through the wave's own part of the LDS (mine_lds, C::WAVE uint4) by direct loads; the
 // stages past the last reload it and are not computed.  Returns with loads of the ring still
 // in flight (the caller waits vmcnt(0) before the LDS is reused).
-template <class C>
-__device__ __forceinline__ void dec_kloop(f32x16_t (&acc)[C::TM][C::TN], const DecSrc<C> &src,
+template <class C, class S = DecSrc<C>>
+__device__ __forceinline__ void dec_kloop(f32x16_t (&acc)[C::TM][C::TN], const S &src,
                                           uint4 *const mine_lds, int kw0, int nst, int K,
                                           size_t ldw, int lane) {
     uint4 *const X0 = mine_lds, *const X1 = mine_lds + C::XSLOT;

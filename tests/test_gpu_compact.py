@@ -2,9 +2,10 @@
 oracle, through the C ABI, on every launch path of the layer.
 
 The compact pool is a storage layout of the same adapters: the oracle computes y from the
-padded pool it was cut from.  Where the compact call takes the same launches as lora_linear
-(every path but the small-batch fused one, which needs the padded row stride) the two
-outputs are also compared bit for bit.  The parity rule is that of test_gpu_parity.
+padded pool it was cut from.  The compact call takes the same launches as lora_linear on the
+padded pool (small decode batches included: the fused GEMM's adapter tiles read each compact
+adapter at its own row width), so the two outputs are also compared bit for bit.  The parity
+rule is that of test_gpu_parity.
 """
 
 import numpy as np
@@ -62,7 +63,8 @@ def ranks8(seed, n, r_max):
 
 CASES = [
     # seed, M, d_in, d_out, n, r_max, base_frac, mode, path
-    (41, 64, 1024, 520, 40, 64, 0.2, DECODE, "medium (small batches too)"),
+    (41, 64, 1024, 520, 40, 64, 0.2, DECODE, "small batch (fused)"),
+    (48, 33, 512, 264, 70, 16, 0.1, DECODE, "small batch (fused), pool larger than the batch"),
     (42, 200, 1024, 520, 40, 32, 0.1, DECODE, "medium"),
     (43, 300, 4096, 2056, 50, 64, 0.1, DECODE, "stream-K"),
     (44, 1500, 256, 512, 5, 16, 0.1, DECODE, "split-K GEMM + expand"),
@@ -82,9 +84,8 @@ def test_compact_matches_oracle(case, y_f32):
     dw = to_device(w)
     y = gpu_compact(dw, to_compact(w.as_bf16()), mode, y_f32=y_f32)
     assert_parity(y, oracle_y(w), f"compact {case}")
-    if M > 128 or mode == PREFILL:  # the same launches as lora_linear on the padded pool
-        y_pad = gpu_linear(dw, 0, mode, y_f32=y_f32)
-        assert np.array_equal(y, y_pad), f"compact {case}: differs from the padded pool's bits"
+    y_pad = gpu_linear(dw, 0, mode, y_f32=y_f32)  # the same launches on the padded pool
+    assert np.array_equal(y, y_pad), f"compact {case}: differs from the padded pool's bits"
 
 
 @pytest.mark.parametrize("mode", [DECODE, PREFILL])
