@@ -117,26 +117,33 @@ __device__ __forceinline__ void dec_x_src(S &src, const uint16_t *x, int M, int 
     }
 }
 
-// After a tile's K loop: wait for every load, add the four waves' partial tiles in wave order
-// through LDS and write the workgroup's partial tile to `mine`.  The reduction that follows
-// starts with dependent loads of the small tables (a row's adapter, then its rank and scale,
-// then B); left to it they come from HBM.  Touched here (loads from asm, results unused),
-// they are in every XCD's L2 by then; the registers they land in are handed to an empty asm
-// after the wait, so the compiler gives them to nothing else while the loads are in flight.
-// Every thread must call it (barriers).
+// The reduction that follows a decode GEMM starts with dependent loads of the small tables (a
+// row's adapter, then its rank and scale, then B); left to it they come from HBM.  Touched at
+// the end of the GEMM's tiles, they are in every XCD's L2 by then.  One asm block issues the
+// three loads and waits for every load of the wave (the K loop's included), so no load is in
+// flight when the block ends; its results are then handed to an empty asm.
+__device__ __forceinline__ void touch_tables(const DecodeLora &lo, int M, int tid) {
+    const int mm = min(tid, M - 1), aa = min(tid, lo.n_adapters - 1);
+    uint32_t d0, d1, d2;
+    asm volatile(
+        "global_load_dword %0, %3, off\n\t"
+        "global_load_dword %1, %4, off\n\t"
+        "global_load_dword %2, %5, off\n\t"
+        "s_waitcnt vmcnt(0)"
+        : "=&v"(d0), "=&v"(d1), "=&v"(d2)
+        : "v"(lo.ids + mm), "v"(lo.scale + aa), "v"(lo.ranks ? lo.ranks + aa : lo.ids + mm)
+        : "memory");
+    asm volatile("" ::"v"(d0), "v"(d1), "v"(d2));
+}
+
+// After a tile's K loop: wait for every load (touching the reduction's tables), add the four
+// waves' partial tiles in wave order through LDS and write the workgroup's partial tile to
+// `mine`.  Every thread must call it (barriers).
 template <class C>
 __device__ __forceinline__ void dec_tile_out(const f32x16_t (&acc)[C::TM][C::TN], uint4 *lds,
                                              const DecodeLora &lo, int M, float *mine, int tid,
                                              int lane, int wave) {
-    uint32_t d0, d1, d2;
-    {
-        const int mm = min(tid, M - 1), aa = min(tid, lo.n_adapters - 1);
-        asm volatile("global_load_dword %0, %1, off" : "=v"(d0) : "v"(lo.ids + mm));
-        asm volatile("global_load_dword %0, %1, off" : "=v"(d1) : "v"(lo.scale + aa));
-        asm volatile("global_load_dword %0, %1, off" : "=v"(d2) : "v"(lo.ranks ? lo.ranks + aa : lo.ids + mm));
-    }
-    wait_vm<0>();
-    asm volatile("" ::"v"(d0), "v"(d1), "v"(d2));
+    touch_tables(lo, M, tid);
     __syncthreads();  // every wave is done with its stages
 
     float4 *const red = reinterpret_cast<float4 *>(lds);

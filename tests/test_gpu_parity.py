@@ -176,7 +176,11 @@ RANDOM = [
     (35, 250, 512, 8, 600, 16, 0.3, DECODE),
     (36, 231, 1024, 3072, 6, 32, 0.05, DECODE),
     (37, 256, 256, 1032, 40, 8, 1.0, DECODE),
-    (38, 200, 1024, 2048, 20, 16, 0.1, DECODE),   # four splits
+    (38, 200, 1024, 2048, 20, 16, 0.1, DECODE),
+    # one row past the first 128 (a third 64-row tile of one row), K of 128; K of 4160
+    # (65 quanta of 64) cut into unequal splits
+    (39, 129, 128, 520, 10, 16, 0.2, DECODE),
+    (40, 256, 4160, 392, 30, 32, 0.1, DECODE),
 ]
 
 

@@ -52,6 +52,7 @@ CASES = [
     ("one row base", np.array([-1], np.int32), 8),
     ("all base", np.full(300, -1, np.int32), 5),
     ("all one adapter", np.full(1000, 7, np.int32), 8),
+    ("all one adapter, 313 tiles", np.full(5000, 3, np.int32), 8),
     ("single-slot pool", np.zeros(77, np.int32), 1),
     ("ragged 65", None, 3),
     ("ragged 1023", None, 40),
