@@ -62,32 +62,18 @@ __device__ void scan_buckets(int32_t *cnt, int32_t (*wave_tot)[NT / 64], int n, 
     int tli = wt + it - tiles;  // first tile slot
     __syncthreads();  // all reads of cnt[] as counts are done before it becomes a cursor
 
-    // Bucket b0 + k of every thread in step k (per is the same for all threads, so the
-    // wave's control flow is uniform).  A bucket's tiles are written by the whole wave: for
-    // each lane whose bucket has rows, its first position and first tile slot are broadcast
-    // and the 64 lanes write tiles j, j + 64, ... (a bucket of many rows no longer costs one
-    // lane a store per tile in turn).
-    for (int k = 0; k < per; ++k) {
-        const int b = b0 + k;
-        const int c = b < b1 ? cnt[b] : 0;
-        if (b < b1) {
-            seg.offsets[b] = pos;
-            cnt[b] = pos;
-            if (c > 0) seg.seg_adapter[sgi++] = b;
-        }
-        const int nt = (c + kTileRows - 1) / kTileRows;
-        uint64_t act = __ballot(nt > 0);
-        while (act) {
-            const int L = __ffsll((unsigned long long)act) - 1;
-            act &= act - 1;
-            const int bL = __shfl(b, L, 64), pL = __shfl(pos, L, 64);
-            const int tL = __shfl(tli, L, 64), nL = __shfl(nt, L, 64);
-            for (int j = lane; j < nL; j += 64) {
-                seg.tiles[2 * (tL + j)] = pL + j * kTileRows;
-                seg.tiles[2 * (tL + j) + 1] = bL;
+    for (int b = b0; b < b1; ++b) {
+        const int c = cnt[b];
+        seg.offsets[b] = pos;
+        cnt[b] = pos;
+        if (c > 0) {
+            seg.seg_adapter[sgi++] = b;
+            for (int j = 0; j < c; j += kTileRows) {
+                seg.tiles[2 * tli] = pos + j;
+                seg.tiles[2 * tli + 1] = b;
+                ++tli;
             }
         }
-        tli += nt;
         pos += c;
     }
     if (tid == 0) {
