@@ -51,6 +51,11 @@ __device__ __forceinline__ void unpack8(const uint4 v, float f[8]) {
 
 __device__ __forceinline__ uint4 ld16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
 __device__ __forceinline__ void st16(void *p, uint4 v) { *reinterpret_cast<uint4 *>(p) = v; }
+// A store that writes through the L2 to memory (sc0 sc1), for data only a later kernel reads:
+// the end-of-kernel write-back then finds no dirty lines of it.  A vector store; p is global.
+__device__ __forceinline__ void st_wt(float *p, float v) {
+    asm volatile("global_store_dword %0, %1, off sc0 sc1" ::"v"(p), "v"(v) : "memory");
+}
 
 // ---- where an adapter's rank rows are ----------------------------------------------------
 // A padded pool (roff == nullptr) holds adapter a at rank rows a * stride .. a * stride +

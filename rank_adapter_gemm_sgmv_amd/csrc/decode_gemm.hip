@@ -138,8 +138,12 @@ __device__ __forceinline__ void touch_tables(const DecodeLora &lo, int M, int ti
 
 // After a tile's K loop: wait for every load (touching the reduction's tables), add the four
 // waves' partial tiles in wave order through LDS and write the workgroup's partial tile to
-// `mine`.  Every thread must call it (barriers).
-template <class C>
+// `mine`.  WT: written through the L2 (the small-batch launches, whose end-of-kernel
+// write-back of the partial tiles was a visible part of a launch of ~13 us: 12.8-13.0 ->
+// 12.3-12.5 us at 64 x 4096 x 4096; the 256-row GEMM, whose stores overlap a longer W
+// stream, measured 0.5 us slower with them, so it keeps plain stores).  Every thread must call
+// it (barriers).
+template <class C, bool WT>
 __device__ __forceinline__ void dec_tile_out(const f32x16_t (&acc)[C::TM][C::TN], uint4 *lds,
                                              const DecodeLora &lo, int M, float *mine, int tid,
                                              int lane, int wave) {
@@ -155,7 +159,11 @@ __device__ __forceinline__ void dec_tile_out(const f32x16_t (&acc)[C::TM][C::TN]
         const int g = (tid >> 7) + 2 * q;  // rows 4 g .. 4 g + 3
         const float4 s = reduce_waves_group<C>(red, g, col);
         float *o = mine + (4 * g) * kBN + col;
-        o[0] = s.x; o[kBN] = s.y; o[2 * kBN] = s.z; o[3 * kBN] = s.w;
+        if constexpr (WT) {
+            st_wt(o, s.x); st_wt(o + kBN, s.y); st_wt(o + 2 * kBN, s.z); st_wt(o + 3 * kBN, s.w);
+        } else {
+            o[0] = s.x; o[kBN] = s.y; o[2 * kBN] = s.z; o[3 * kBN] = s.w;
+        }
     }
 }
 
@@ -238,8 +246,11 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(
     const int kw1 = min(ks1, kw0 + per_wave);
     const int nst = (kw1 - kw0) / kBKW;
     dec_kloop<C>(acc, src, lds + wave * C::WAVE, kw0, nst, K, ldw, lane);
-    dec_tile_out<C>(acc, lds, lo, M, partial + ((size_t)split * n_tiles + tile) * C::TILE, tid,
-                    lane, wave);
+    float *const mine = partial + ((size_t)split * n_tiles + tile) * C::TILE;
+    if (n_lt > 0)  // a small-batch launch (adapter tiles)
+        dec_tile_out<C, true>(acc, lds, lo, M, mine, tid, lane, wave);
+    else
+        dec_tile_out<C, false>(acc, lds, lo, M, mine, tid, lane, wave);
 }
 
 // ---- the same split-K GEMM with an fp8 base weight -----------------------------------------
@@ -299,8 +310,9 @@ __device__ __forceinline__ bf16x8_t dec_fp8x8(uint32_t lo, uint32_t hi) {
 
 // Workgroup (tile, split) of fp8 W tile tn: rows m0 .. m0 + BM of x, columns n0 .. n0 + 127
 // (wave w: 32 w ..), k in the split; writes partial tile `tile` of split `split` (n_tiles
-// tiles per split).  Every thread must call it (barriers).
-template <class C>
+// tiles per split), through the L2 with WT (small batches, as dec_tile_out).  Every thread
+// must call it (barriers).
+template <class C, bool WT>
 __device__ __forceinline__ void f8_tile(uint4 *lds, const uint16_t *__restrict__ x,
                                         const uint8_t *__restrict__ W8,
                                         const float *__restrict__ w_scale, int M, int K, int N,
@@ -394,8 +406,12 @@ __device__ __forceinline__ void f8_tile(uint4 *lds, const uint16_t *__restrict__
 #pragma unroll
     for (int i = 0; i < C::TM; ++i)
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
-            P[(size_t)(32 * i + (v / 4) * 8 + g * 4 + v % 4) * kBN] = sc * (acc[i][0][v] + acc[i][1][v]);
+        for (int v = 0; v < 16; ++v) {
+            float *const o = &P[(size_t)(32 * i + (v / 4) * 8 + g * 4 + v % 4) * kBN];
+            const float val = sc * (acc[i][0][v] + acc[i][1][v]);
+            if constexpr (WT) st_wt(o, val);
+            else *o = val;
+        }
 }
 
 // Workgroup (tile, split) of the fp8 GEMM.  BUILD: one more workgroup (the last) builds the
@@ -422,8 +438,12 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_fp8_kernel(
     int lin = blockIdx.x;
     if (n_tm > 1 && (n_gemm_blocks & 7) == 0) lin = (blockIdx.x & 7) * (n_gemm_blocks >> 3) + (blockIdx.x >> 3);
     const int tile = lin % n_tiles, split = lin / n_tiles;
-    f8_tile<C>(lds, x, W8, w_scale, M, K, N, n_tiles, tile, split, tile % n_tm, tile / n_tm,
-               k_per_split, partial, lane, wave);
+    if (M <= kDecodeMaxRows)
+        f8_tile<C, true>(lds, x, W8, w_scale, M, K, N, n_tiles, tile, split, tile % n_tm,
+                         tile / n_tm, k_per_split, partial, lane, wave);
+    else
+        f8_tile<C, false>(lds, x, W8, w_scale, M, K, N, n_tiles, tile, split, tile % n_tm,
+                          tile / n_tm, k_per_split, partial, lane, wave);
 }
 
 // The fp8 GEMM with the shrink as adapter tiles, for batches of at most kDecodeMaxRows rows
@@ -450,8 +470,8 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_fp8_lora_kernel(
     const int tile = lin % n_tiles, split = lin / n_tiles;
     const int tm = tile % n_tm, tn = tile / n_tm;
     if (tn < n_tn) {
-        f8_tile<CF>(lds, x, W8, w_scale, M, K, N, n_tiles, tile, split, tm, tn, k_per_split,
-                    partial, lane, wave);
+        f8_tile<CF, true>(lds, x, W8, w_scale, M, K, N, n_tiles, tile, split, tm, tn,
+                          k_per_split, partial, lane, wave);
         return;
     }
     const int lt = tn - n_tn;
@@ -473,7 +493,7 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_fp8_lora_kernel(
     const int kw0 = min(ks1, ks0 + wave * per_wave);
     const int kw1 = min(ks1, kw0 + per_wave);
     dec_kloop<CB>(acc, src, lds + wave * CB::WAVE, kw0, (kw1 - kw0) / kBKW, K, RM, lane);
-    dec_tile_out<CB>(acc, lds, lo, M, partial + ((size_t)split * n_tiles + tile) * CB::TILE, tid,
+    dec_tile_out<CB, true>(acc, lds, lo, M, partial + ((size_t)split * n_tiles + tile) * CB::TILE, tid,
                      lane, wave);
 }
 
