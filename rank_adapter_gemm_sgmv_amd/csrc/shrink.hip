@@ -148,11 +148,8 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void shrink_mfma_kernel(
             // padding is not read above r_max 16).  Unit u = lane + 64 i is (row u / GR, group u % GR); the
             // offsets are 32-bit bytes from the adapter's block (one VGPR per address).
             const char *ab = reinterpret_cast<const char *>(Aa);
-#pragma unroll
-            for (int f = 0; f < C::FILLS; ++f) {
-                const int kb = k_lo + f * C::KS;
-                if (kb >= k_hi) break;  // uniform: the wave's range ends inside this chunk
-                uint4 av[C::AL];
+            // fill f's loads: A_a rows kb .. kb + KS (zeros past k_hi) and this lane's x
+            auto load_fill = [&](int kb, uint4(&av)[C::AL], uint4(&xv)[C::STEPS]) {
 #pragma unroll
                 for (int i = 0; i < C::AL; ++i) {
                     const int u = lane + 64 * i, kr = kb + u / C::GR, gr = u % C::GR;
@@ -163,9 +160,33 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void shrink_mfma_kernel(
                     av[i] = want && kr < k_hi ? *reinterpret_cast<const uint4 *>(ab + off)
                                               : make_uint4(0, 0, 0, 0);
                 }
-                uint4 xv[C::STEPS];
 #pragma unroll
                 for (int st = 0; st < C::STEPS; ++st) xv[st] = ld16(xr + min(kb + 32 * st + 8 * g, d_in - 8));
+            };
+            // At r_max <= 16 every fill's loads are issued before the first fill is used (one
+            // round trip per chunk instead of one per fill; at r_max 16, 30 more VGPRs and four
+            // workgroups per CU instead of five): prefill shrink 9.9 -> 9.4 us, the MLP's
+            // 11008-deep shrink 16.0 -> 15.7 us.  Above r_max 16 the registers would cost a
+            // wave per SIMD.
+            constexpr bool UPFRONT = RM <= 16;
+            uint4 pav[UPFRONT ? C::FILLS : 1][C::AL], pxv[UPFRONT ? C::FILLS : 1][C::STEPS];
+            if constexpr (UPFRONT) {
+#pragma unroll
+                for (int f = 0; f < C::FILLS; ++f) load_fill(k_lo + f * C::KS, pav[f], pxv[f]);
+            }
+#pragma unroll
+            for (int f = 0; f < C::FILLS; ++f) {
+                const int kb = k_lo + f * C::KS;
+                if (kb >= k_hi) break;  // uniform: the wave's range ends inside this chunk
+                uint4 av[C::AL], xv[C::STEPS];
+                if constexpr (UPFRONT) {
+#pragma unroll
+                    for (int i = 0; i < C::AL; ++i) av[i] = pav[f][i];
+#pragma unroll
+                    for (int st = 0; st < C::STEPS; ++st) xv[st] = pxv[f][st];
+                } else {
+                    load_fill(kb, av, xv);
+                }
 #pragma unroll
                 for (int i = 0; i < C::AL; ++i) {
                     const int u = lane + 64 * i, kr = u / C::GR, gr = u % C::GR;
