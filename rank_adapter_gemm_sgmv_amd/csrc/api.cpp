@@ -336,14 +336,15 @@ hipError_t run_linear(const void *x, const void *W, const void *A, const void *B
     const int rb = rank_bucket(r_max), pstride = r_max;
     int kc, ksplit;
     shrink_plan(d_in, rb, &kc, &ksplit);
-    // (the fused path lays adapters side by side at column stride rb: a padded pool whose row
-    // stride is the bucket, or a rank-compact pool, each adapter read at its own row width)
-    if (!prefill && (roff != nullptr || r_max == rb) && decode_fused_supported(M, d_in, d_out)) {
+    // (the fused path lays adapters side by side in slots fused_tile_rank(rb) columns wide,
+    // each adapter's rows read at its own width: a padded pool's stride when that is a
+    // multiple of 8 (16-byte loads), or a rank-compact adapter's round8(rank))
+    if (!prefill && (roff != nullptr || r_max % 8 == 0) && decode_fused_supported(M, d_in, d_out)) {
         // small decode batch: x W and the shrink x A_i as tiles of one split-K GEMM (the
         // row -> adapter slot map, when needed, goes to the t region), then one reduction
         // adds the splits and the expand
-        const DecodeLora lo{nullptr, 0, reinterpret_cast<int32_t *>(t), Bb, scale, ids, ranks, rb,
-                            n_adapters, roff, pool_rows, pstride};
+        const DecodeLora lo{nullptr, 0, reinterpret_cast<int32_t *>(t), Bb, scale, ids, ranks,
+                            fused_tile_rank(rb), n_adapters, roff, pool_rows, pstride};
         if ((e = launch_decode_gemm(xb, Wb, static_cast<const uint16_t *>(A), M, d_in, d_out, lo,
                                     true, gpart, nullptr, s)) != hipSuccess)
             return e;

@@ -79,6 +79,12 @@ __device__ __forceinline__ int adapter_row0(const int32_t *roff, int pool_rows, 
 // Kernel rank bucket of a pool whose widest adapter has r_max rank rows: t, the shrink's
 // partial sums and every other internal buffer use the bucket as their row width.
 constexpr int rank_bucket(int r_max) { return r_max <= 8 ? 8 : r_max <= 16 ? 16 : r_max <= 32 ? 32 : 64; }
+// Width of an adapter's slot in the small-batch GEMM's adapter tiles for rank bucket rb (the
+// bf16 base; t there has this row width).  Rank-8 pools take 16-wide slots: an 8-wide slot
+// gave each load of an adapter tile 16 bytes of 16 adapters, half a cache line each, twice
+// the lines per byte of the wider slots (64 x 4096 x 4096 with 28 rank-8 adapters: 20.5 us per
+// step against 18.3 at rank 16); in a 16-wide slot the second group re-reads the first.
+constexpr int fused_tile_rank(int rb) { return rb < 16 ? 16 : rb; }
 
 // ---- kernel launches -------------------------------------------------------------------
 // Every kernel of the library is launched through launch().  Normally it is a plain launch;
@@ -191,7 +197,8 @@ struct DecodeLora {
     const float *scale;    // [n]
     const int32_t *ids;    // [M]
     const int32_t *ranks;  // [n] true ranks, or nullptr (= pstride)
-    int r_max;             // the kernel rank bucket
+    int r_max;             // the kernel rank bucket (with adapter tiles: the slot width,
+                           // fused_tile_rank of the bucket for the bf16 base)
     int n_adapters;
     const int32_t *roff;   // [n] first rank row of each adapter (rank-compact pool), or nullptr
     int pool_rows;

@@ -84,14 +84,21 @@ __device__ __forceinline__ bool dec_adapter_src(S &src, BatchAdapters &ba, const
         if constexpr (!COMPACT) {
             src.wp[q] = A + ((size_t)a * K + r) * RM + col % RM;
         } else {
-            // the adapter's own block: rows round8(rank) wide from its first rank row; groups
-            // past its width read its last group again (same lines, no HBM bytes; those t
-            // columns lie past the rank and are never read).  An adapter whose rows leave
-            // the pool (rank read as 0) reads element 0 at stride 0; it adds nothing.
-            int rk = lo.ranks ? min(max(lo.ranks[a], 1), RM) : RM;
-            const int row0 = adapter_row0(lo.roff, lo.pool_rows, a, 0, rk);
-            const int w = (rk + 7) & ~7;
-            if (rk > 0) {
+            // the adapter's own block, w rows wide from its first rank row: a padded pool's
+            // stride, or a rank-compact adapter's round8(rank); groups past w read the last
+            // group again (same lines, no HBM bytes; those t columns lie past the rank and are
+            // never read).  A compact adapter whose rows leave the pool (rank read as 0) reads
+            // element 0 at stride 0; it adds nothing.
+            int row0, w;
+            if (lo.roff != nullptr) {
+                int rk = lo.ranks ? min(max(lo.ranks[a], 1), RM) : RM;
+                row0 = adapter_row0(lo.roff, lo.pool_rows, a, 0, rk);
+                w = rk > 0 ? (rk + 7) & ~7 : 0;
+            } else {
+                row0 = a * lo.pstride;
+                w = lo.pstride;
+            }
+            if (w > 0) {
                 src.wp[q] = A + (size_t)row0 * K + (size_t)r * w + min(col % RM, w - 8);
                 src.ws[q] = (uint32_t)w;
             } else {
@@ -946,10 +953,13 @@ size_t decode_gemm_partial_floats(int M, int K, int N, int r_max, int n_adapters
     // them (the fused small-batch path); the latter has more tiles but may have fewer splits
     const DecPlan p0 = dec_plan(M, K, N, 0);
     size_t f = (size_t)p0.ks * p0.n_tm * p0.n_tn * p0.bm * kBN;
+    // (adapter slots r_max wide, the fp8 base's, or fused_tile_rank(r_max) wide, the bf16's)
     if (rank_ok(r_max) && decode_fused_supported(M, K, N)) {
-        const DecPlan p = dec_plan(M, K, N, adapter_tiles(M, r_max, n_adapters));
-        const size_t fa = (size_t)p.ks * p.n_tm * (p.n_tn + p.n_lt) * p.bm * kBN;
-        if (fa > f) f = fa;
+        for (const int rs : {r_max, fused_tile_rank(r_max)}) {
+            const DecPlan p = dec_plan(M, K, N, adapter_tiles(M, rs, n_adapters));
+            const size_t fa = (size_t)p.ks * p.n_tm * (p.n_tn + p.n_lt) * p.bm * kBN;
+            if (fa > f) f = fa;
+        }
     }
     return f;
 }
@@ -959,7 +969,9 @@ hipError_t launch_decode_gemm(const uint16_t *x, const uint16_t *W, const uint16
                               const SegBuild *build, hipStream_t s) {
     if (!decode_gemm_supported(M, K, N) || partial == nullptr || !rank_ok(lo.r_max) ||
         (adapters && (M > kDecodeMaxRows || A == nullptr || lo.ids == nullptr ||
-                      (lo.n_adapters > M && lo.slots == nullptr))))
+                      (lo.n_adapters > M && lo.slots == nullptr) ||
+                      (lo.roff == nullptr && (lo.pstride % 8 != 0 || lo.pstride < 8 ||
+                                              lo.pstride > lo.r_max)))))
         return hipErrorInvalidValue;
     const int n_lt = adapters ? adapter_tiles(M, lo.r_max, lo.n_adapters) : 0;
     const DecPlan p = dec_plan(M, K, N, n_lt);
@@ -968,8 +980,9 @@ hipError_t launch_decode_gemm(const uint16_t *x, const uint16_t *W, const uint16
     const int n_gemm = p.n_tm * (p.n_tn + p.n_lt) * p.ks;
     const dim3 grid(n_gemm + (build ? 1 : 0));
     const SegBuild bld = build ? *build : SegBuild{nullptr, 1, Seg{}};
-    // adapter tiles from a rank-compact pool read each adapter at its own row stride
-    const bool cpt = adapters && lo.roff != nullptr;
+    // adapter tiles whose adapters' rows are not r_max wide (a rank-compact pool, or a padded
+    // pool of another stride) read each adapter at its own row stride
+    const bool cpt = adapters && (lo.roff != nullptr || lo.pstride != lo.r_max);
 #define GEMM_LAUNCH(BM, RMX)                                                                  \
     if (build)                                                                                \
         launch((decode_gemm_kernel<Dec<BM>, RMX, true, false>), grid, dim3(kThreads), 0, s, x, W, \

@@ -1,7 +1,9 @@
 """The C ABI at the edges of its contract, on the GPU, against the CPU oracle:
 
 - r_max anywhere in [1, 64] (the kernels run at the rank bucket 8/16/32/64; a padded pool of
-  any r_max is stored at that stride), on every launch path of lora_linear;
+  any r_max is stored at that stride), on every launch path of lora_linear: small decode
+  batches take the fused GEMM when r_max is a multiple of 8 (each adapter's rows read at the
+  pool's stride; rank-8 pools in 16-wide slots), the medium sequence otherwise;
 - rank-compact pools whose ranks are any value in [1, r_max] (not only multiples of 8);
 - lora_shrink / lora_expand with such an r_max (t is [M, r_max]) and their compact variants;
 - LORA_MODE_CHECKED: a bad id, rank or compact offset is reported and nothing is enqueued;
@@ -37,7 +39,10 @@ ANY_RANK = [
     (205, 640, 2048, 256, 200, 3, 0.0, PREFILL, "prefill epilogue"),
     (206, 100, 264, 1032, 60, 1, 0.1, DECODE, "segment path, rank 1"),
     (207, 17, 136, 264, 3, 63, 0.2, PREFILL, "prefill, ragged"),
-    (208, 96, 2048, 768, 12, 48, 0.1, DECODE, "small batch -> medium, r 48"),
+    (208, 96, 2048, 768, 12, 48, 0.1, DECODE, "small batch (fused), stride 48"),
+    (209, 64, 1024, 520, 30, 8, 0.1, DECODE, "small batch (fused), rank 8 in 16-wide slots"),
+    (210, 40, 512, 264, 90, 40, 0.2, DECODE, "small batch (fused), stride 40, pool > batch"),
+    (218, 128, 4096, 1032, 33, 24, 0.0, DECODE, "small batch (fused), stride 24, 128 rows"),
 ]
 
 
@@ -105,9 +110,10 @@ def test_compact_any_rank(case):
 
 def same_launches(M, d_in, r_max, mode):
     """A compact call takes the padded pool's launches, except for decode batches of at most
-    128 rows (d_in % 32 == 0) whose padded r_max is no rank bucket: the padded pool then
-    takes the medium path, the compact one the fused path."""
-    return not (mode == DECODE and M <= 128 and d_in % 32 == 0 and r_max not in (8, 16, 32, 64))
+    128 rows (d_in % 32 == 0) whose padded r_max is not a multiple of 8: the padded pool then
+    takes the medium path (its adapters' rows cannot be read in 16-byte groups), the compact
+    one the fused path."""
+    return not (mode == DECODE and M <= 128 and d_in % 32 == 0 and r_max % 8 != 0)
 
 
 @pytest.mark.parametrize("M", [300, 96], ids=["M300", "M96-fused"])
