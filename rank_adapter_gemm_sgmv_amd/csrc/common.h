@@ -228,22 +228,17 @@ bool decode_fused_supported(int M, int K, int N);  // and M <= kDecodeMaxRows
 size_t decode_gemm_partial_floats(int M, int K, int N, int r_max, int n_adapters);
 // Split-K partial tiles of x W for a decode batch; with `adapters` (M <= kDecodeMaxRows)
 // the same launch also streams the batch's adapters' A as extra tiles (the LoRA shrink).
-// build (nullable): also build the segments of these ids, in one more workgroup.
+// Tiles of bm (32 or 64) rows x 128 columns, the n_tn column tiles of W then the adapter
+// tiles; K cut into ks splits (the last may be shorter); partial tiles laid out
+// [split][tm + tn * n_tm][bm][128] (fp32), what launch_decode_reduce adds.  build
+// (nullable): also build the segments of these ids, in one more workgroup.
 hipError_t launch_decode_gemm(const uint16_t *x, const uint16_t *W, const uint16_t *A, int M,
                               int K, int N, const DecodeLora &lo, bool adapters, float *partial,
                               const SegBuild *build, hipStream_t s);
 
-// The split plan of the decode GEMM without adapter tiles: tiles of bm rows x 128 columns
-// (n_tm x n_tn of them), K cut into ks splits of k_per_split (a multiple of 256; the last
-// split may be shorter).  Its partial tiles are laid out [split][tm + tn * n_tm][bm][128]
-// (fp32), what launch_decode_reduce (adapters = false) adds.
-struct DecodeSplits {
-    int bm, n_tm, n_tn, ks, k_per_split;
-};
-DecodeSplits decode_splits(int M, int K, int N);
-
 // x W_eff for a decode batch whose base weight is fp8 E4M3 codes W8[N][K] with per-column
-// scales w_scale[N] (csrc/decode_gemm.hip): the scaled partial tiles of decode_splits(M, K, N).
+// scales w_scale[N] (csrc/decode_gemm.hip): the scaled partial tiles of the decode plan without
+// adapter tiles, laid out [split][tm + tn * n_tm][bm][128] (fp32) as launch_decode_gemm's.
 // As decode_gemm_supported, and N % 8 == 0.  build (nullable): also build the segments of
 // these ids in one more workgroup.
 hipError_t launch_decode_gemm_fp8(const uint16_t *x, const uint8_t *W8, const float *w_scale,

@@ -941,11 +941,6 @@ bool decode_fused_supported(int M, int K, int N) {
     return decode_gemm_supported(M, K, N) && M <= kDecodeMaxRows;
 }
 
-DecodeSplits decode_splits(int M, int K, int N) {
-    const DecPlan p = dec_plan(M, K, N, 0);
-    return DecodeSplits{p.bm, p.n_tm, p.n_tn, p.ks, p.k_per_split};
-}
-
 size_t decode_gemm_partial_floats(int M, int K, int N, int r_max, int n_adapters) {
     if (!decode_gemm_supported(M, K, N)) return 0;
     // every plan a call of these sizes may run: without adapter tiles (batches of 129-256
