@@ -340,10 +340,9 @@ hipError_t run_linear(const void *x, const void *W, const void *A, const void *B
     // each adapter's rows read at its own width: a padded pool's stride when that is a
     // multiple of 8 (16-byte loads), or a rank-compact adapter's round8(rank))
     if (!prefill && (roff != nullptr || r_max % 8 == 0) && decode_fused_supported(M, d_in, d_out)) {
-        // small decode batch: x W and the shrink x A_i as tiles of one split-K GEMM (the
-        // row -> adapter slot map, when needed, goes to the t region), then one reduction
-        // adds the splits and the expand
-        const DecodeLora lo{nullptr, 0, reinterpret_cast<int32_t *>(t), Bb, scale, ids, ranks,
+        // small decode batch: x W and the shrink x A_i as tiles of one split-K GEMM, then one
+        // reduction adds the splits and the expand
+        const DecodeLora lo{nullptr, 0, Bb, scale, ids, ranks,
                             fused_tile_rank(rb), n_adapters, roff, pool_rows, pstride};
         if ((e = launch_decode_gemm(xb, Wb, static_cast<const uint16_t *>(A), M, d_in, d_out, lo,
                                     true, gpart, nullptr, s)) != hipSuccess)
@@ -358,7 +357,7 @@ hipError_t run_linear(const void *x, const void *W, const void *A, const void *B
         // workgroup of the same launch (unless the caller passed segments); then the
         // segment-path shrink, whose per-chunk partial sums have the layout the decode
         // reduction reads; the reduction with the expand
-        const DecodeLora lo{spart, ksplit, nullptr, Bb, scale, ids, ranks, rb, n_adapters, roff,
+        const DecodeLora lo{spart, ksplit, Bb, scale, ids, ranks, rb, n_adapters, roff,
                             pool_rows, pstride};
         const SegBuild bld{ids, n_adapters, sg};
         if ((e = launch_decode_gemm(xb, Wb, nullptr, M, d_in, d_out, lo, false, gpart,
@@ -450,8 +449,8 @@ hipError_t run_fp8w(const void *x, const void *W8, const float *w_scale, const v
     hipError_t e;
     if (r_max == rb && decode_fused_supported(M, d_in, d_out)) {
         // small batch, pool padded at a rank bucket: the shrink as adapter tiles of the fp8
-        // GEMM's launch (the row -> slot map, when needed, in the t region), then the reduction
-        const DecodeLora lo{nullptr, 0, reinterpret_cast<int32_t *>(t), static_cast<const uint16_t *>(B),
+        // GEMM's launch, then the reduction
+        const DecodeLora lo{nullptr, 0, static_cast<const uint16_t *>(B),
                             scale, ids, ranks, rb, n_adapters, nullptr, 0, r_max};
         if ((e = launch_decode_gemm_fp8_lora(xb, static_cast<const uint8_t *>(W8), w_scale,
                                              static_cast<const uint16_t *>(A), M, d_in, d_out, lo,
@@ -466,7 +465,7 @@ hipError_t run_fp8w(const void *x, const void *W8, const float *w_scale, const v
     }
     int kc, ksplit;
     shrink_plan(d_in, rb, &kc, &ksplit);
-    const DecodeLora lo{spart, ksplit, nullptr, static_cast<const uint16_t *>(B), scale, ids, ranks,
+    const DecodeLora lo{spart, ksplit, static_cast<const uint16_t *>(B), scale, ids, ranks,
                         rb, n_adapters, nullptr, 0, r_max};
     const SegBuild bld{ids, n_adapters, sg};
     e = launch_decode_gemm_fp8(xb, static_cast<const uint8_t *>(W8), w_scale, M, d_in, d_out, gpart,

@@ -191,8 +191,6 @@ struct DecodeLora {
     const float *tpart;    // [n_chunks][M][r_max]: the segment-path shrink's chunk sums of t
                            // (calls without adapter tiles)
     int n_chunks;
-    int32_t *slots;        // [M]: row -> adapter slot, written by the GEMM when the pool is
-                           // larger than the batch (calls with adapter tiles)
     const uint16_t *B;     // [n][r_max][d_out]
     const float *scale;    // [n]
     const int32_t *ids;    // [M]
@@ -214,9 +212,8 @@ struct SegBuild {
 };
 
 // Decode batches up to this many rows take the fused path (x W and x A_i as tiles of one
-// split-K launch) when d_in % 32 == 0: the slot tables of batch_adapters.h hold this many
-// rows, and beyond it one adapter tile per distinct adapter costs more than the
-// segment-path shrink.
+// split-K launch) when d_in % 32 == 0: beyond it the adapter tiles (up to one slot per row)
+// cost more than the segment-path shrink.
 constexpr int kDecodeMaxRows = 128;
 // The split-K decode GEMM + LoRA reduction serve batches up to this many rows (beyond
 // kDecodeMaxRows with the segment-path shrink writing the chunk sums).
@@ -246,9 +243,9 @@ hipError_t launch_decode_gemm_fp8(const uint16_t *x, const uint8_t *W8, const fl
                                   hipStream_t s);
 
 // The same fp8 GEMM with the shrink x A_a as adapter tiles of the same launch (a batch of at
-// most kDecodeMaxRows rows, a pool padded at a rank bucket: lo.r_max 8, 16, 32 or 64; the row
-// -> slot map goes to lo.slots when the pool is larger than the batch): the partial tiles of
-// dec_plan with adapter tiles, what launch_decode_reduce (adapters = true) adds.
+// most kDecodeMaxRows rows, a pool padded at a rank bucket: lo.r_max 8, 16, 32 or 64): the
+// partial tiles of dec_plan with adapter tiles, what launch_decode_reduce (adapters = true)
+// adds.
 hipError_t launch_decode_gemm_fp8_lora(const uint16_t *x, const uint8_t *W8, const float *w_scale,
                                        const uint16_t *A, int M, int K, int N,
                                        const DecodeLora &lo, float *partial, hipStream_t s);

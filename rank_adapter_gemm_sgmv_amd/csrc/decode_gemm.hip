@@ -37,7 +37,6 @@
 //    same sums for items of four rows of one adapter, each B_a chunk loaded once per item.
 #include <type_traits>
 
-#include "batch_adapters.h"
 #include "decode_tiles.h"
 #include "segments_block.h"
 
@@ -45,26 +44,23 @@ namespace lora {
 
 namespace {
 
-// Sources of adapter tile lt of a fused call: the batch's adapters laid side by side, 128 / RM
-// per tile, numbered by id when the pool is no larger than the batch, else by first use (the
-// grouping found in LDS; leave_slots: this workgroup also leaves the row -> slot map for the
-// reduction).  Returns false -- for the whole workgroup -- when the tile holds no adapter of
-// the batch.  Every thread must call it (barriers).
+// Sources of adapter tile lt of a fused call: adapters laid side by side, 128 / RM slots per
+// tile.  With a pool no larger than the batch, slot = adapter id; otherwise slot = row: slot m
+// holds row m's adapter (rows sharing an adapter read the same A lines, from L2), so the tile
+// needs only its rows' ids, and the reduction finds row m's t at slot m.  (Grouping the
+// batch's distinct adapters first -- an ids load, then a scan and three barriers in LDS --
+// held the adapter tiles 2.8 us before their first load against 0.6 us for W tiles, and with 8
+// distinct adapters in 64 rows they ended last: 19.0-19.6 us per step at 64 x 4096 x 4096
+// against 17.6 with the adapters numbered by id.)  Returns false -- for the whole workgroup --
+// when the tile has nothing to compute.  Every thread must call it (barriers).
 template <class C, int RM, class S>
-__device__ __forceinline__ bool dec_adapter_src(S &src, BatchAdapters &ba, const DecodeLora &lo,
-                                                const uint16_t *A, int M, int K, int lt,
-                                                bool leave_slots, int tid, int lane) {
+__device__ __forceinline__ bool dec_adapter_src(S &src, const DecodeLora &lo, const uint16_t *A,
+                                                int M, int K, int lt, int tid, int lane) {
     constexpr int APT = AdapterTiles<RM>::APT;
     constexpr bool COMPACT = !std::is_same<S, DecSrc<C>>::value;
     const bool by_id = lo.n_adapters <= M;
-    int T = lo.n_adapters;
-    if (!by_id) {
-        batch_adapters(ba, lo.ids, M, lo.n_adapters);  // every thread: barriers
-        T = ba.T;
-        if (leave_slots)
-            for (int m = tid; m < M; m += kThreads) lo.slots[m] = ba.slot[m];
-    }
-    if (lt * APT >= T) return false;  // no adapter of the batch in this tile
+    const int T = by_id ? lo.n_adapters : M;  // slots
+    if (lt * APT >= T) return false;  // no slot in this tile
     if (by_id) {
         // numbered by id, a tile may hold only adapters no row of the batch uses
         bool used = false;
@@ -79,8 +75,15 @@ __device__ __forceinline__ bool dec_adapter_src(S &src, BatchAdapters &ba, const
         const int r = 4 * q + (lane >> 4);
         const int col = ((lane & 15) ^ wsw(r)) * 8;
         const int sl = lt * APT + col / RM;
-        // slots past the last read a valid adapter; their columns are never used
-        const int a = sl < T ? (by_id ? sl : ba.list[sl]) : (by_id ? 0 : ba.list[0]);
+        // slots past the last, and rows without a valid adapter, read adapter 0; their columns
+        // are never used
+        int a = 0;
+        if (by_id) {
+            a = sl < T ? sl : 0;
+        } else if (sl < T) {
+            const int id = lo.ids[sl];
+            a = id >= 0 && id < lo.n_adapters ? id : 0;
+        }
         if constexpr (!COMPACT) {
             src.wp[q] = A + ((size_t)a * K + r) * RM + col % RM;
         } else {
@@ -186,7 +189,6 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(
     DecodeLora lo, int n_gemm_blocks, SegBuild build) {
     // wave w's part: x stages 0, 1 then W stages 0 .. 3; after the K loop, its partial tile
     __shared__ __attribute__((aligned(1024))) uint4 lds[kWaves * C::WAVE];
-    __shared__ BatchAdapters ba;
 
     if (BUILD && (int)blockIdx.x >= n_gemm_blocks) {
         // the extra workgroup: the segment build, in this kernel's LDS (the launch is a grid of
@@ -231,9 +233,7 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_kernel(
         }
     } else {
         const int lt = tn - n_tn;
-        if (!dec_adapter_src<C, RM>(src, ba, lo, A, M, K, lt, lt == 0 && split == 0 && tm == 0,
-                                    tid, lane))
-            return;  // whole workgroup
+        if (!dec_adapter_src<C, RM>(src, lo, A, M, K, lt, tid, lane)) return;  // whole workgroup
         ldw = RM;
     }
     dec_x_src<C>(src, x, M, K, m0, lane);
@@ -467,7 +467,6 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_fp8_lora_kernel(
     static_assert(CF::BM == CB::BM && CF::TILE == CB::TILE, "one tile shape");
     constexpr int L16 = CF::LDS16 > kWaves * CB::WAVE ? CF::LDS16 : kWaves * CB::WAVE;
     __shared__ __attribute__((aligned(1024))) uint4 lds[L16];
-    __shared__ BatchAdapters ba;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -483,9 +482,7 @@ __global__ __launch_bounds__(kThreads) void decode_gemm_fp8_lora_kernel(
     }
     const int lt = tn - n_tn;
     DecSrc<CB> src;
-    if (!dec_adapter_src<CB, RM>(src, ba, lo, A, M, K, lt, lt == 0 && split == 0 && tm == 0, tid,
-                                 lane))
-        return;  // whole workgroup
+    if (!dec_adapter_src<CB, RM>(src, lo, A, M, K, lt, tid, lane)) return;  // whole workgroup
     dec_x_src<CB>(src, x, M, K, tm * CB::BM, lane);
     f32x16_t acc[CB::TM][CB::TN];
 #pragma unroll
@@ -565,7 +562,7 @@ __global__ __launch_bounds__(256) void reduce_lora_kernel(const float *__restric
     size_t t_stride;
     int n_t;
     if (n_lt > 0) {
-        const int sl = !has ? 0 : lo.n_adapters <= M ? id : lo.slots[m];
+        const int sl = !has ? 0 : lo.n_adapters <= M ? id : m;  // slot: id, or row
         const int ttile = (m / BM) + (n_tn + sl / APT) * n_tm;
         tsrc = partial + (size_t)ttile * BM * kBN + (m % BM) * kBN + (sl % APT) * RM;
         t_stride = stride;
@@ -964,7 +961,6 @@ hipError_t launch_decode_gemm(const uint16_t *x, const uint16_t *W, const uint16
                               const SegBuild *build, hipStream_t s) {
     if (!decode_gemm_supported(M, K, N) || partial == nullptr || !rank_ok(lo.r_max) ||
         (adapters && (M > kDecodeMaxRows || A == nullptr || lo.ids == nullptr ||
-                      (lo.n_adapters > M && lo.slots == nullptr) ||
                       (lo.roff == nullptr && (lo.pstride % 8 != 0 || lo.pstride < 8 ||
                                               lo.pstride > lo.r_max)))))
         return hipErrorInvalidValue;
@@ -1037,7 +1033,7 @@ hipError_t launch_decode_gemm_fp8_lora(const uint16_t *x, const uint8_t *W8, con
                                        const DecodeLora &lo, float *partial, hipStream_t s) {
     if (!decode_fused_supported(M, K, N) || N % 8 != 0 || partial == nullptr ||
         w_scale == nullptr || A == nullptr || lo.ids == nullptr || !rank_ok(lo.r_max) ||
-        lo.n_adapters < 1 || (lo.n_adapters > M && lo.slots == nullptr))
+        lo.n_adapters < 1)
         return hipErrorInvalidValue;
     const int n_lt = adapter_tiles(M, lo.r_max, lo.n_adapters);
     const DecPlan p = dec_plan(M, K, N, n_lt);
@@ -1067,7 +1063,6 @@ hipError_t launch_decode_reduce(const float *partial, int M, int K, int N, void 
                                 const DecodeLora &lo, bool adapters, const Seg *seg,
                                 hipStream_t s) {
     if (!decode_gemm_supported(M, K, N) || partial == nullptr || !rank_ok(lo.r_max) ||
-        (adapters && lo.n_adapters > M && lo.slots == nullptr) ||
         (!adapters && (lo.tpart == nullptr || lo.n_chunks < 1)))
         return hipErrorInvalidValue;
     const int n_lt = adapters ? adapter_tiles(M, lo.r_max, lo.n_adapters) : 0;

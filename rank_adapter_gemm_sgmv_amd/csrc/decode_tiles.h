@@ -168,8 +168,8 @@ __device__ __forceinline__ float4 reduce_waves_group(const float4 *red, int g, i
 
 // Column tiles: n_tn tiles of W, then n_lt adapter tiles.  Adapter "slots" are numbered
 // 0 .. T-1: with a pool no larger than the batch, slot = adapter id (T = n_adapters), else
-// the batch's distinct adapters in order of first use (batch_adapters.h).  Adapter tile lt
-// holds slots lt * APT .. lt * APT + APT - 1, each r_max columns wide.
+// slot = row (T = M; slot m holds row m's adapter).  Adapter tile lt holds slots lt * APT ..
+// lt * APT + APT - 1, each r_max columns wide.
 template <int RM>
 struct AdapterTiles {
     static_assert(RM == 8 || RM == 16 || RM == 32 || RM == 64, "rank bucket");
