@@ -23,6 +23,9 @@ GRAPH_CASES = [
     (94, 300, 4096, 2056, 50, 64, 1, False),  # stream-K decode path
     (95, 300, 4096, 2056, 50, 64, 1, True),   # stream-K, compact pool
     (96, 200, 1024, 520, 40, 32, 2, True),    # prefill, compact pool
+    (97, 48, 1024, 520, 300, 16, 1, False),   # small batch, pool larger than the batch (slot per row)
+    (98, 40, 512, 264, 90, 24, 1, True),      # small batch, compact pool larger than the batch
+    (99, 64, 1024, 392, 30, 8, 1, False),     # small batch, rank 8 in 16-wide slots
 ]
 
 
