@@ -2,7 +2,8 @@
 adapters in one call, in both modes, with the smallest dimensions (d_in = d_out = r_max = 8)
 so that the oracle still checks every output element.  Every adapter is touched about 230
 times, so prefill tiles hold hundreds of short adapter runs; the segments are checked bit for
-bit at that size too."""
+bit at that size too.  Small decode batches (1 and 128 rows) with LORA_MAX_ADAPTERS adapters
+take the fused path."""
 
 import numpy as np
 import pytest
@@ -46,3 +47,18 @@ def test_max_rows_segments():
     ref = oracle.build_segments(w.ids, w.n_adapters, 16)
     for key in ("perm", "offsets", "seg_adapter", "tiles", "meta"):
         assert np.array_equal(got[key], ref[key]), key
+
+
+@pytest.mark.parametrize("M,r_max", [(1, 8), (128, 24)], ids=["M1-r8", "M128-r24"])
+def test_small_batch_largest_pool(M, r_max):
+    """The small-batch fused path with a pool of LORA_MAX_ADAPTERS adapters: one adapter slot
+    per row, any row's adapter anywhere in the pool (rank 8 in 16-wide slots; stride 24)."""
+    from rank_adapter_gemm_sgmv_amd import lora as L
+
+    w = random_case(78 + M, M, 128, 136, L.LORA_MAX_ADAPTERS, r_max, base_frac=0.1)
+    log(f"limits: small batch M={M} n={w.n_adapters} r_max={r_max}")
+    p = w.projections[0]
+    ref = oracle.lora_linear(p.x, p.W, p.A, p.B, w.alpha, w.ranks, w.ids)
+    for y_f32 in (False, True):
+        y = gpu_linear(to_device(w), 0, 1, y_f32=y_f32)
+        assert_parity(y, ref, f"small batch, largest pool, M={M} r_max={r_max} y_f32={y_f32}")
