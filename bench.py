@@ -151,6 +151,25 @@ class DeviceLayers:
             self.layers.append((x, W, A, B))
 
 
+def split_group_kernels(ks, n):
+    """Per-projection kernel lists of one lora_linear_multi call over n projections: a kernel
+    name launched n times (each projection's own shrink, or every launch when the call ran
+    projection by projection) goes to the projections in order; a launch shared by the group
+    (the merged GEMM and reduction, the segment build) is split evenly between them."""
+    out = [[] for _ in range(n)]
+    names = [name for name, _ in ks]
+    seen = {}
+    for name, ms in ks:
+        if names.count(name) == n:
+            k = seen.get(name, 0)
+            seen[name] = k + 1
+            out[k].append((name, ms))
+        else:
+            for q in range(n):
+                out[q].append((name, ms / n))
+    return out
+
+
 def layers_needed(w, rotate_x: bool, compact: bool = False, fp8: bool = False) -> int:
     per = 0
     for p in w.projections:
@@ -164,7 +183,7 @@ class Runner:
     projection, workspace; `step(i)` enqueues one step (all projections) for layer i % L."""
 
     def __init__(self, w, mode, torch, L, rotate_x=False, prebuilt_segments=False, compact=False,
-                 fp8=False):
+                 fp8=False, merge=True):
         self.torch, self.w, self.mode, self.L = torch, w, mode, L
         self.compact, self.fp8 = compact, fp8
         self.M, self.n, self.r_max = w.M, w.n_adapters, w.r_max
@@ -174,16 +193,44 @@ class Runner:
         self.projs = [DeviceLayers(w, pi, L, rotate_x, torch, compact, fp8)
                       for pi in range(len(w.projections))]
         self.ys = [torch.empty((w.M, pr.d_out), dtype=torch.bfloat16, device="cuda") for pr in self.projs]
+        # projections that read the same x with the same shape (an MLP's gate and up) run as one
+        # lora_linear_multi call
+        self.groups = []
+        for pi, p in enumerate(w.projections):
+            g = self.groups[-1] if self.groups else None
+            q = w.projections[g[0]] if g else None
+            if (merge and not (compact or fp8) and g and len(g) < L_.LORA_MAX_PROJ and p.x is q.x
+                    and (p.d_in, p.d_out) == (q.d_in, q.d_out)):
+                g.append(pi)
+            else:
+                self.groups.append([pi])
         nb = max(L_.lora_workspace_bytes(w.M, pr.d_in, pr.d_out, w.r_max, w.n_adapters) for pr in self.projs)
+        for g in self.groups:
+            if len(g) > 1:
+                pr = self.projs[g[0]]
+                nb = max(nb, L_.lora_workspace_bytes_multi(w.M, pr.d_in, pr.d_out, w.r_max,
+                                                           w.n_adapters, len(g)))
         self.ws = torch.empty(max(nb, 256), dtype=torch.uint8, device="cuda")
         self.ws_bytes = nb
         self.segs = L_.Segments(w.M, w.n_adapters) if prebuilt_segments else None
+
+    def _multi_args(self, g, li):
+        pr = self.projs[g[0]]
+        x = pr.layers[li][0]
+        return (x, [self.projs[q].layers[li][1] for q in g], [self.projs[q].layers[li][2] for q in g],
+                [self.projs[q].layers[li][3] for q in g], self.scale, self.ranks, self.ids, self.M,
+                pr.d_in, pr.d_out, self.r_max, self.n, self.segs, [self.ys[q] for q in g],
+                L_.LORA_BF16, self.mode, self.ws, self.ws_bytes)
 
     def step(self, i):
         li = i % self.L
         if self.segs is not None:
             L_.lora_build_segments(self.ids, self.M, self.n, self.segs)
-        for pr, y in zip(self.projs, self.ys):
+        for g in self.groups:
+            if len(g) > 1:
+                L_.lora_linear_multi(*self._multi_args(g, li))
+                continue
+            pr, y = self.projs[g[0]], self.ys[g[0]]
             x, W, A, B = pr.layers[li]
             if self.fp8:
                 L_.lora_linear_fp8w(x, W, pr.w_scale, A, B, self.scale, self.ranks, self.ids, self.M,
@@ -210,7 +257,12 @@ class Runner:
         out = []
         if self.segs is not None:
             L_.lora_build_segments(self.ids, self.M, self.n, self.segs)
-        for pr, y in zip(self.projs, self.ys):
+        for g in self.groups:
+            if len(g) > 1:
+                out.extend(split_group_kernels(L_.lora_linear_multi_profiled(*self._multi_args(g, li)),
+                                               len(g)))
+                continue
+            pr, y = self.projs[g[0]], self.ys[g[0]]
             x, W, A, B = pr.layers[li]
             if self.fp8:
                 ks = L_.lora_linear_fp8w_profiled(
@@ -542,14 +594,14 @@ def workload(config):
 
 
 def run_workload(config, mode_name, steps, warmup, torch, profile_reps=20, compact=False,
-                 call_reps=100, fp8=False):
+                 call_reps=100, fp8=False, merge=True):
     w = workload(config)
     prefill = mode_name == "prefill"
     mode = L_.LORA_MODE_PREFILL if prefill else L_.LORA_MODE_DECODE
     rotate_x = prefill
     L = layers_needed(w, rotate_x, compact, fp8)
     runner = Runner(w, mode, torch, L, rotate_x=rotate_x, prebuilt_segments=len(w.projections) > 1,
-                    compact=compact, fp8=fp8)
+                    compact=compact, fp8=fp8, merge=merge)
     log(f"bench: {w.name} mode={mode_name} layers={L} steps={steps} compact={compact} fp8={fp8}")
     ms_total, wall, eager_ms, kernels, reps, calls = measure(runner, steps, warmup, torch,
                                                              profile_reps, call_reps=call_reps)
@@ -557,7 +609,9 @@ def run_workload(config, mode_name, steps, warmup, torch, profile_reps=20, compa
     s.update({"workload": w.name, "mode": mode_name, "layers_rotated": L, "steps": steps,
               "pool": "rank-compact (lora_linear_compact)" if compact else "padded to r_max",
               "base": "fp8 E4M3 W8[d_out, d_in] + column scales (lora_linear_fp8w)" if fp8 else "bf16 W",
-              "ms_per_step_replays": reps, "us_per_call": calls})
+              "ms_per_step_replays": reps, "us_per_call": calls,
+              "merged_projections": [[w.projections[q].name for q in g] for g in runner.groups
+                                     if len(g) > 1]})
     base_ms = base_only_ms(w, runner, steps, torch)
     s["base_only_ms_per_step"] = base_ms
     s["lora_overhead_vs_base_only"] = s["ms_per_step"] / base_ms - 1.0
@@ -832,6 +886,9 @@ def main():
     ap.add_argument("--moe", action="store_true",
                     help="only the MoE-LoRA decode workload (its own JSON line; with --pmc-pass, "
                          "its counter pass)")
+    ap.add_argument("--separate-projections", action="store_true",
+                    help="call lora_linear per projection also where projections share x (the "
+                         "MLP's gate and up), instead of one lora_linear_multi call")
     ap.add_argument("--pmc-pass", action="store_true",
                     help="only eager steps of the chosen workload plus the counter calibration "
                          "kernel, for rocprofv3 --pmc runs (FETCH_SIZE / WRITE_SIZE)")
@@ -859,7 +916,8 @@ def main():
 
     # headline: decode, q_proj geometry (unless another workload is asked for)
     w, head, kernels, steps, ms_total = run_workload(args.workload, args.mode, args.steps,
-                                                     args.warmup, torch, compact=args.compact)
+                                                     args.warmup, torch, compact=args.compact,
+                                                     merge=not args.separate_projections)
     p0 = w.projections[0]
     work = algorithmic_work(w, p0.d_in, p0.d_out, args.mode == "prefill")
     kmain = {name: ms for (pi, name), ms in kernels.items() if pi == 0}
@@ -870,11 +928,13 @@ def main():
     if not args.headline_only:
         for cfg, mode_name, st, var in ((3, "decode", 128, ""), (3, "decode", 128, "compact"),
                                         (4, "prefill", 40, ""), (5, "decode", 64, ""),
+                                        (5, "decode", 64, "separate-projections"),
                                         (4, "decode", 20, ""), (2, "prefill", 64, ""),
                                         (2, "decode", 128, "fp8base")):
             try:
                 _, s, _, _, _ = run_workload(cfg, mode_name, st, 4, torch, profile_reps=8,
-                                             compact=var == "compact", fp8=var == "fp8base")
+                                             compact=var == "compact", fp8=var == "fp8base",
+                                             merge=var != "separate-projections")
                 workloads[f"{s['workload']}:{mode_name}{'-' + var if var else ''}"] = s
             except Exception as e:  # report, do not hide the headline
                 workloads[f"config{cfg}:{mode_name}"] = {"error": repr(e)}

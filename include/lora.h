@@ -67,6 +67,7 @@ extern "C" {
 #define LORA_TILE_ROWS 16        /* rows per work tile of a segment */
 #define LORA_MAX_ADAPTERS 16384  /* pool slots one call can address */
 #define LORA_MAX_ROWS (1 << 22)  /* rows per call */
+#define LORA_MAX_PROJ 4          /* projections per lora_linear_multi call */
 
 /* The three enums below are passed as int.  Any int value may reach the library (an
  * unknown status or dtype, a mode with LORA_MODE_CHECKED OR-ed in), so in C++ they are given
@@ -247,6 +248,38 @@ lora_status_t lora_linear_compact(const void *x, const void *W, const void *A, c
                                   int32_t r_max, int32_t n_adapters, const lora_segments_t *segs,
                                   void *y, lora_dtype_t y_dtype, lora_mode_t mode, void *ws,
                                   size_t ws_bytes, void *stream);
+
+/* Several projections of one layer that read the same input rows, each with its own adapter
+ * pool: [P1], "How much memory does one LoRA adapter actually cost?", names the MLP's
+ * gate_proj, up_proj and down_proj as adapted modules; gate and up both read the layer's
+ * hidden state.  For p < n_proj:
+ *     y[p] = x W[p] + scale_i (x A[p]_i) B[p]_i   (i = ids[m] per row, as lora_linear)
+ * W, A, B and y are HOST arrays of n_proj device pointers (1 <= n_proj <= LORA_MAX_PROJ, else
+ * LORA_ERR_SHAPE; a NULL array gives LORA_ERR_NULL), each laid out and aligned as the
+ * lora_linear argument of the same name; the projections share x, d_in, d_out, r_max, the
+ * adapter tables (scale, ranks, ids: one adapter owns a pair A[p]_i, B[p]_i in every
+ * projection) and segs.  ws: lora_workspace_bytes_multi() bytes (else LORA_ERR_WORKSPACE).
+ * Decode batches of 257-1024 rows that take lora_linear's stream-K sequence build the
+ * segments once and run the projections' GEMMs as one launch (their column panels end to
+ * end on one K line) and their reductions as one; the K sums are then split at other points
+ * than in separate calls, so the bits may differ from lora_linear's by the order of fp32
+ * additions.  Every other batch runs lora_linear's launches per projection (same bits).
+ * Errors as lora_linear, for the first projection whose arguments fail. */
+size_t lora_workspace_bytes_multi(int32_t M, int32_t d_in, int32_t d_out, int32_t r_max,
+                                  int32_t n_adapters, int32_t n_proj);
+lora_status_t lora_linear_multi(const void *x, int32_t n_proj, const void *const *W,
+                                const void *const *A, const void *const *B, const float *scale,
+                                const int32_t *ranks, const int32_t *ids, int32_t M, int32_t d_in,
+                                int32_t d_out, int32_t r_max, int32_t n_adapters,
+                                const lora_segments_t *segs, void *const *y, lora_dtype_t y_dtype,
+                                lora_mode_t mode, void *ws, size_t ws_bytes, void *stream);
+/* Measurement aid: lora_linear_profiled for lora_linear_multi's arguments. */
+lora_status_t lora_linear_multi_profiled(
+    const void *x, int32_t n_proj, const void *const *W, const void *const *A,
+    const void *const *B, const float *scale, const int32_t *ranks, const int32_t *ids, int32_t M,
+    int32_t d_in, int32_t d_out, int32_t r_max, int32_t n_adapters, const lora_segments_t *segs,
+    void *const *y, lora_dtype_t y_dtype, lora_mode_t mode, void *ws, size_t ws_bytes, void *stream,
+    float *kernel_ms, const char **kernel_names, int32_t max_kernels, int32_t *n_kernels);
 
 /* The whole layer with a quantized base ([P1], "Where does multi-LoRA serving actually
  * break?", item 4: a base stored at low precision served beside higher-precision adapters,

@@ -403,9 +403,13 @@ hipError_t run_linear(const void *x, const void *W, const void *A, const void *B
     if (gsplit < 0) {
         // stream-K partial tiles: one pass adds them, t from the chunk sums, and the expand,
         // rows in segment order
-        if ((e = launch_sk_reduce_lora(gpart, M, d_in, d_out, sk_plan(M, d_in, d_out), sg, spart,
-                                       ksplit, Bb, scale, ids, ranks, roff, pool_rows, pstride, rb,
-                                       n_adapters, y, yf, s)) != hipSuccess)
+        SkProj pj{};
+        pj.B[0] = Bb;
+        pj.tpart[0] = spart;
+        pj.y[0] = y;
+        if ((e = launch_sk_reduce_lora(gpart, M, d_in, d_out, sk_plan(M, d_in, d_out), sg, pj,
+                                       ksplit, scale, ids, ranks, roff, pool_rows, pstride, rb,
+                                       n_adapters, yf, s)) != hipSuccess)
             return e;
         mark(mk, "decode_reduce_lora");
         return hipSuccess;
@@ -585,6 +589,149 @@ lora_status_t lora_linear_fp8w(const void *x, const void *W8, const float *w_sca
 
 namespace {
 
+// lora_linear_multi: the most projections one merged stream-K launch takes (the largest g <=
+// n_proj whose g x n_tn panels still leave the data-parallel tiling short of the chip), or 0
+// when the batch does not take the stream-K path at all.
+static_assert(kMaxProj == LORA_MAX_PROJ, "projection arrays");
+
+int multi_group(int32_t M, int32_t d_in, int32_t d_out, int32_t n_proj) {
+    if (!sk_plan(M, d_in, d_out).use) return 0;
+    int g = n_proj;
+    while (g > 1 && !sk_plan(M, d_in, d_out, g).use) --g;
+    return g;
+}
+
+// Workspace of the merged stream-K sequence: segments, one shrink chunk-sum area per
+// projection, the partial tiles of one group of g projections.
+size_t multi_sk_bytes(int32_t M, int32_t d_in, int32_t d_out, int32_t r_max, int32_t n_adapters,
+                      int32_t n_proj) {
+    const int g = multi_group(M, d_in, d_out, n_proj);
+    if (g < 2) return 0;
+    return segments_bytes(M, n_adapters) + (size_t)n_proj * shrink_partial_bytes(M, d_in, r_max) +
+           round_up(sk_partial_floats(sk_plan(M, d_in, d_out, g)) * sizeof(float));
+}
+
+// The launch sequence of lora_linear_multi (arguments already validated, M > 0).  Batches
+// that take lora_linear's stream-K sequence (decode, 257-1024 rows) build the segments once,
+// run each projection's shrink, then one stream-K GEMM and one reduction per group of up to g
+// projections, whose column panels are laid end to end on one K line (longer lanes: fewer
+// partial tiles per panel).  Every other batch runs lora_linear's sequence per projection.
+hipError_t run_linear_multi(const void *x, int32_t n_proj, const void *const *W,
+                            const void *const *A, const void *const *B, const float *scale,
+                            const int32_t *ranks, const int32_t *ids, int32_t M, int32_t d_in,
+                            int32_t d_out, int32_t r_max, int32_t n_adapters,
+                            const lora_segments_t *segs, void *const *y, lora_dtype_t y_dtype,
+                            lora_mode_t mode, void *ws, hipStream_t s, Marker *mk) {
+    const bool prefill = mode == LORA_MODE_PREFILL || (mode == LORA_MODE_AUTO && M >= LORA_PREFILL_MIN_ROWS);
+    const int g = prefill ? 0 : multi_group(M, d_in, d_out, n_proj);
+    hipError_t e;
+    if (g < 2) {
+        for (int i = 0; i < n_proj; ++i)
+            if ((e = run_linear(x, W[i], A[i], B[i], scale, ranks, nullptr, 0, ids, M, d_in, d_out,
+                                r_max, n_adapters, segs, y[i], y_dtype, mode, ws, s, mk)) != hipSuccess)
+                return e;
+        return hipSuccess;
+    }
+    char *p = static_cast<char *>(ws);
+    lora_segments_t own = carve_segments(p, M, n_adapters);
+    float *spart[kMaxProj] = {};
+    for (int i = 0; i < n_proj; ++i) {
+        spart[i] = reinterpret_cast<float *>(p);
+        p += shrink_partial_bytes(M, d_in, r_max);
+    }
+    float *gpart = reinterpret_cast<float *>(p);
+    const Seg sg = to_seg(segs ? *segs : own);
+    const uint16_t *xb = static_cast<const uint16_t *>(x);
+    const int rb = rank_bucket(r_max), pstride = r_max;
+    int kc, ksplit;
+    shrink_plan(d_in, rb, &kc, &ksplit);
+    if (!segs) {
+        if ((e = launch_build_segments(ids, M, n_adapters, sg, s)) != hipSuccess) return e;
+        mark(mk, "build_segments");
+    }
+    for (int i = 0; i < n_proj; ++i) {
+        if ((e = launch_shrink(xb, static_cast<const uint16_t *>(A[i]), ranks, nullptr, 0, pstride, M,
+                               d_in, rb, n_adapters, sg, spart[i], kc, ksplit, s)) != hipSuccess)
+            return e;
+        mark(mk, "shrink");
+    }
+    for (int i0 = 0; i0 < n_proj; i0 += g) {
+        const int gn = n_proj - i0 < g ? n_proj - i0 : g;
+        const SkPlan sp = sk_plan(M, d_in, d_out, gn);
+        if (!sp.use) return hipErrorInvalidValue;
+        SkProj pj{};
+        for (int j = 0; j < gn; ++j) {
+            pj.W[j] = static_cast<const uint16_t *>(W[i0 + j]);
+            pj.B[j] = static_cast<const uint16_t *>(B[i0 + j]);
+            pj.tpart[j] = spart[i0 + j];
+            pj.y[j] = y[i0 + j];
+        }
+        if ((e = launch_gemm_sk(xb, pj, M, d_in, d_out, sp, gpart, s)) != hipSuccess) return e;
+        mark(mk, "gemm_decode");
+        if ((e = launch_sk_reduce_lora(gpart, M, d_in, d_out, sp, sg, pj, ksplit, scale, ids, ranks,
+                                       nullptr, 0, pstride, rb, n_adapters, y_dtype == LORA_F32,
+                                       s)) != hipSuccess)
+            return e;
+        mark(mk, "decode_reduce_lora");
+    }
+    return hipSuccess;
+}
+
+lora_status_t check_multi(const void *x, int32_t n_proj, const void *const *W,
+                          const void *const *A, const void *const *B, const float *scale,
+                          const int32_t *ranks, const int32_t *ids, int32_t M, int32_t d_in,
+                          int32_t d_out, int32_t r_max, int32_t n_adapters,
+                          const lora_segments_t *segs, void *const *y, lora_dtype_t y_dtype,
+                          lora_mode_t mode, void *ws, size_t ws_bytes) {
+    if (n_proj < 1 || n_proj > LORA_MAX_PROJ) return LORA_ERR_SHAPE;
+    if (!W || !A || !B || !y) return LORA_ERR_NULL;
+    for (int i = 0; i < n_proj; ++i) {
+        const lora_status_t st = check_linear(x, W[i], A[i], B[i], scale, ranks, ids, M, d_in, d_out,
+                                              r_max, n_adapters, segs, y[i], y_dtype, mode, ws,
+                                              ws_bytes);
+        if (st != LORA_OK) return st;
+    }
+    if (ws_bytes < lora_workspace_bytes_multi(M, d_in, d_out, r_max, n_adapters, n_proj))
+        return LORA_ERR_WORKSPACE;
+    return LORA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t lora_workspace_bytes_multi(int32_t M, int32_t d_in, int32_t d_out, int32_t r_max,
+                                  int32_t n_adapters, int32_t n_proj) {
+    if (n_proj < 1 || n_proj > LORA_MAX_PROJ) return 0;
+    const size_t one = lora_workspace_bytes(M, d_in, d_out, r_max, n_adapters);
+    if (one == 0) return 0;
+    const size_t merged = multi_sk_bytes(M, d_in, d_out, r_max, n_adapters, n_proj);
+    return merged > one ? merged : one;
+}
+
+lora_status_t lora_linear_multi(const void *x, int32_t n_proj, const void *const *W,
+                                const void *const *A, const void *const *B, const float *scale,
+                                const int32_t *ranks, const int32_t *ids, int32_t M, int32_t d_in,
+                                int32_t d_out, int32_t r_max, int32_t n_adapters,
+                                const lora_segments_t *segs, void *const *y, lora_dtype_t y_dtype,
+                                lora_mode_t mode, void *ws, size_t ws_bytes, void *stream) {
+    lora_status_t st = check_multi(x, n_proj, W, A, B, scale, ranks, ids, M, d_in, d_out, r_max,
+                                   n_adapters, segs, y, y_dtype, mode, ws, ws_bytes);
+    if (st != LORA_OK || M == 0) return st;
+    clear_stale_error();
+    if ((mode & LORA_MODE_CHECKED) &&
+        (st = check_tables(ids, M, ranks, nullptr, 0, r_max, n_adapters, (hipStream_t)stream)) != LORA_OK)
+        return st;
+    return hip_status(run_linear_multi(x, n_proj, W, A, B, scale, ranks, ids, M, d_in, d_out, r_max,
+                                       n_adapters, segs, y, y_dtype,
+                                       (lora_mode_t)(mode & ~LORA_MODE_CHECKED), ws,
+                                       (hipStream_t)stream, nullptr));
+}
+
+}  // extern "C"
+
+namespace {
+
 // lora_linear / lora_linear_compact with each launch timed by start / stop events taken
 // from its own dispatch packet (arguments already validated, M > 0).
 // `run(marker)` enqueues a call's launches; each is timed by start / stop events taken from its
@@ -660,6 +807,27 @@ lora_status_t lora_linear_profiled(const void *x, const void *W, const void *A, 
     return run_profiled(x, W, A, B, scale, ranks, nullptr, 0, ids, M, d_in, d_out, r_max,
                         n_adapters, segs, y, y_dtype, mode, ws, stream, kernel_ms, kernel_names,
                         max_kernels, n_kernels);
+}
+
+lora_status_t lora_linear_multi_profiled(
+    const void *x, int32_t n_proj, const void *const *W, const void *const *A,
+    const void *const *B, const float *scale, const int32_t *ranks, const int32_t *ids, int32_t M,
+    int32_t d_in, int32_t d_out, int32_t r_max, int32_t n_adapters, const lora_segments_t *segs,
+    void *const *y, lora_dtype_t y_dtype, lora_mode_t mode, void *ws, size_t ws_bytes, void *stream,
+    float *kernel_ms, const char **kernel_names, int32_t max_kernels, int32_t *n_kernels) {
+    if (!kernel_ms || !kernel_names || !n_kernels || max_kernels < 0) return LORA_ERR_NULL;
+    *n_kernels = 0;
+    lora_status_t st = check_multi(x, n_proj, W, A, B, scale, ranks, ids, M, d_in, d_out, r_max,
+                                   n_adapters, segs, y, y_dtype, mode, ws, ws_bytes);
+    if (st != LORA_OK || M == 0) return st;
+    return time_launches(
+        [&](Marker *mk) {
+            return run_linear_multi(x, n_proj, W, A, B, scale, ranks, ids, M, d_in, d_out, r_max,
+                                    n_adapters, segs, y, y_dtype,
+                                    (lora_mode_t)(mode & ~LORA_MODE_CHECKED), ws,
+                                    (hipStream_t)stream, mk);
+        },
+        kernel_ms, kernel_names, max_kernels, n_kernels);
 }
 
 lora_status_t lora_linear_compact_profiled(

@@ -92,7 +92,7 @@ constexpr int fused_tile_rank(int rb) { return rb < 16 ? 16 : rb; }
 // launch carries a start and a stop event that the GPU stamps from the kernel's own dispatch
 // packet, so the elapsed time is the kernel's duration with no extra packet in the stream.
 struct KernelTimer {
-    static constexpr int kMax = 16;
+    static constexpr int kMax = 24;
     hipEvent_t start[kMax] = {};
     hipEvent_t stop[kMax] = {};
     int n = 0;
@@ -165,22 +165,34 @@ hipError_t launch_gemm_big(const uint16_t *x, const uint16_t *W, int M, int K, i
 
 // Stream-K decode GEMM (csrc/gemm_big.hip) for batches of 257-1024 rows whose 256 x 256
 // tiles are too few to fill the chip: L lanes of equal K length, n_tm workgroups per lane.
+// Several projections of one layer that read the same x (lora_linear_multi) share one
+// launch: their column panels are laid end to end, projection after projection (n_proj
+// projections of n_tn1 panels each, n_tn = n_proj * n_tn1).
 struct SkPlan {
     bool use;
     int n_tm, n_tn, L;
+    int n_proj, n_tn1;
 };
-SkPlan sk_plan(int M, int K, int N);
+SkPlan sk_plan(int M, int K, int N, int n_proj = 1);
 size_t sk_partial_floats(const SkPlan &p);
-hipError_t launch_gemm_sk(const uint16_t *x, const uint16_t *W, int M, int K, int N,
+// Per-projection operands of the stream-K launches (entries past p.n_proj unused).
+constexpr int kMaxProj = 4;
+struct SkProj {
+    const uint16_t *W[kMaxProj];   // [K][N]
+    const uint16_t *B[kMaxProj];   // adapter pool B of each projection
+    const float *tpart[kMaxProj];  // its shrink's chunk sums [n_chunks][M][r_max]
+    void *y[kMaxProj];             // [M][N]
+};
+hipError_t launch_gemm_sk(const uint16_t *x, const SkProj &pj, int M, int K, int N,
                           const SkPlan &p, float *partial, hipStream_t s);
 // y = (the stream-K partial tiles added in lane order) + scale_a t B_a on rows with an
 // adapter, rows in segment order; t summed from the shrink's n_chunks chunk sums; rounds
-// once into y.
+// once into y (each projection's own B, t and y).
 hipError_t launch_sk_reduce_lora(const float *partial, int M, int K, int N, const SkPlan &p,
-                                 Seg seg, const float *tpart, int n_chunks, const uint16_t *B,
-                                 const float *scale, const int32_t *ids, const int32_t *ranks,
-                                 const int32_t *roff, int pool_rows, int pstride, int r_max,
-                                 int n_adapters, void *y, bool y_f32, hipStream_t s);
+                                 Seg seg, const SkProj &pj, int n_chunks, const float *scale,
+                                 const int32_t *ids, const int32_t *ranks, const int32_t *roff,
+                                 int pool_rows, int pstride, int r_max, int n_adapters,
+                                 bool y_f32, hipStream_t s);
 
 // Adds the split-K decode GEMM's ksplit > 1 partial slices into y, in order.
 hipError_t launch_splitk_reduce(const float *partial, int M, int N, int ksplit, void *y,

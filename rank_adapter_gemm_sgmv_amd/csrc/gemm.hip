@@ -311,7 +311,9 @@ hipError_t launch_gemm(const uint16_t *x, const uint16_t *W, int M, int K, int N
         if (sk_partial_floats(sp) > ws_partial_floats || ws_partial == nullptr)
             return hipErrorInvalidValue;
         *ksplit_out = -1;
-        return launch_gemm_sk(x, W, M, K, N, sp, ws_partial, s);
+        SkProj pj{};
+        pj.W[0] = W;
+        return launch_gemm_sk(x, pj, M, K, N, sp, ws_partial, s);
     }
     if (use_big(M, N)) return launch_gemm_big(x, W, M, K, N, y, y_f32, seg, nullptr, s);
 

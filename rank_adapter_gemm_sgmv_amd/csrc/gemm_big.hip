@@ -503,6 +503,14 @@ __global__ __launch_bounds__(C::NT) void gemm_big_kernel(const uint16_t *__restr
 // both advance along the one K line.  sk_reduce_kernel adds a panel's slots in lane order,
 // so the sum does not depend on scheduling.
 
+// Entry i of a per-projection pointer array held in kernel arguments, by selects (a
+// runtime index into the argument array would copy it to scratch memory).
+template <class T>
+__device__ __forceinline__ T pick_proj(int i, T const (&v)[kMaxProj]) {
+    static_assert(kMaxProj == 4, "selects below");
+    return i == 0 ? v[0] : i == 1 ? v[1] : i == 2 ? v[2] : v[3];
+}
+
 // Lane run by the workgroups of each rank: lanes sorted by the K offset at which they
 // start inside their panel, so the ranks an XCD gets (16 when L = 128) read neighbouring
 // K slices of x and share them through that XCD's L2.
@@ -519,10 +527,9 @@ __device__ __forceinline__ int sk_start(int l, int total, int L) {
 
 template <class C>
 __global__ __launch_bounds__(C::NT) void gemm_sk_kernel(const uint16_t *__restrict__ x,
-                                                        const uint16_t *__restrict__ W,
-                                                        int M, int K, int N,
+                                                        SkProj pj, int M, int K, int N,
                                                         float *__restrict__ partial, int n_tm,
-                                                        int n_tn, int L, SkLanes lanes) {
+                                                        int n_tn, int n_tn1, int L, SkLanes lanes) {
     __shared__ __attribute__((aligned(1024))) uint4 X0[C::XSLOT];
     __shared__ __attribute__((aligned(1024))) uint4 X1[C::XSLOT];
     __shared__ __attribute__((aligned(1024))) uint4 X2[C::XSLOT];
@@ -556,7 +563,10 @@ __global__ __launch_bounds__(C::NT) void gemm_sk_kernel(const uint16_t *__restri
     for (int p = s0 / KI; p * KI < s1; ++p) {
         const int kb = max(s0, p * KI) - p * KI;
         const int n = min(s1, (p + 1) * KI) - p * KI - kb;  // steps of this panel, 4 | n
-        const int n0 = p * C::BN;
+        // panel p is panel pl of projection pr
+        const int pr = p / n_tn1, pl = p - pr * n_tn1;
+        const uint16_t *__restrict__ W = pick_proj(pr, pj.W);
+        const int n0 = pl * C::BN;
 #pragma unroll
         for (int j = 0; j < C::WINS; ++j) {
             const int q = wave * C::WINS + j;
@@ -628,11 +638,10 @@ __global__ __launch_bounds__(C::NT) void gemm_sk_kernel(const uint16_t *__restri
 // on XCD b % 8), panel-major, so one XCD reads a panel's partial slots and B columns.
 template <class C, bool YF32>
 __global__ __launch_bounds__(256) void sk_reduce_lora_kernel(
-    const float *__restrict__ partial, int M, int K, int N, int n_tm, int n_tn, int L, Seg seg,
-    const float *__restrict__ tpart, int n_chunks, const uint16_t *__restrict__ B,
-    const float *__restrict__ scale, const int32_t *__restrict__ ids,
-    const int32_t *__restrict__ ranks, const int32_t *__restrict__ roff, int pool_rows, int pstride,
-    int r_max, int n_adapters, void *__restrict__ y) {
+    const float *__restrict__ partial, int M, int K, int N, int n_tm, int n_tn, int n_tn1, int L,
+    Seg seg, SkProj pj, int n_chunks, const float *__restrict__ scale,
+    const int32_t *__restrict__ ids, const int32_t *__restrict__ ranks,
+    const int32_t *__restrict__ roff, int pool_rows, int pstride, int r_max, int n_adapters) {
     static_assert(C::BN == 256, "one panel per block");
     __shared__ float4 s_part[256];
     __shared__ float s_t[8][64];
@@ -641,9 +650,14 @@ __global__ __launch_bounds__(256) void sk_reduce_lora_kernel(
     int lin = blockIdx.x;
     if ((nblk & 7) == 0) lin = (lin & 7) * (nblk >> 3) + (lin >> 3);
     const int p = lin / G, g = lin % G;
+    // panel p of the stream-K line is panel p - pr * n_tn1 of projection pr
+    const int pr = p / n_tn1;
+    const float *__restrict__ tpart = pick_proj(pr, pj.tpart);
+    const uint16_t *__restrict__ B = pick_proj(pr, pj.B);
+    void *__restrict__ y = pick_proj(pr, pj.y);
     const int pl = threadIdx.x >> 5;
     const int pos = g * 8 + pl;
-    const int n = p * C::BN + (threadIdx.x & 31) * 8;
+    const int n = (p - pr * n_tn1) * C::BN + (threadIdx.x & 31) * 8;
     const bool live = pos < M && n < N;
     // this thread's partial tiles first, so their loads overlap the t sums below
     int m = 0, a = -1;
@@ -791,11 +805,14 @@ hipError_t launch_gemm_big(const uint16_t *x, const uint16_t *W, int M, int K, i
 }
 
 
-SkPlan sk_plan(int M, int K, int N) {
+SkPlan sk_plan(int M, int K, int N, int n_proj) {
     SkPlan p{};
     if (M <= kDecodeGemmMaxRows || M > 1024 || K % (4 * kBK) != 0 || N % 8 != 0) return p;
+    if (n_proj < 1 || n_proj > kMaxProj) return p;
     p.n_tm = (M + CfgSk::BM - 1) / CfgSk::BM;
-    p.n_tn = (N + CfgSk::BN - 1) / CfgSk::BN;
+    p.n_proj = n_proj;
+    p.n_tn1 = (N + CfgSk::BN - 1) / CfgSk::BN;
+    p.n_tn = n_proj * p.n_tn1;
     if ((long)p.n_tm * p.n_tn >= 192) return p;  // the data-parallel tiling fills the chip
     p.L = (256 / p.n_tm) / 8 * 8;
     if ((long)p.n_tn * (K / kBK) < 8L * p.L) return p;  // at least 8 K steps per lane
@@ -807,7 +824,7 @@ size_t sk_partial_floats(const SkPlan &p) {
     return p.use ? (size_t)(p.L + p.n_tn - 1) * p.n_tm * CfgSk::BM * CfgSk::BN : 0;
 }
 
-hipError_t launch_gemm_sk(const uint16_t *x, const uint16_t *W, int M, int K, int N,
+hipError_t launch_gemm_sk(const uint16_t *x, const SkProj &pj, int M, int K, int N,
                           const SkPlan &p, float *partial, hipStream_t s) {
     // lanes in order of (K offset of their first step inside its panel, lane)
     const int KI = K / kBK, total = p.n_tn * KI;
@@ -822,27 +839,27 @@ hipError_t launch_gemm_sk(const uint16_t *x, const uint16_t *W, int M, int K, in
         }
         lanes.lane[r] = (uint8_t)l;
     }
-    launch(gemm_sk_kernel<CfgSk>, dim3(p.L * p.n_tm), dim3(CfgSk::NT), 0, s, x, W, M, K, N,
-           partial, p.n_tm, p.n_tn, p.L, lanes);
+    launch(gemm_sk_kernel<CfgSk>, dim3(p.L * p.n_tm), dim3(CfgSk::NT), 0, s, x, pj, M, K, N,
+           partial, p.n_tm, p.n_tn, p.n_tn1, p.L, lanes);
     return hipGetLastError();
 }
 
 hipError_t launch_sk_reduce_lora(const float *partial, int M, int K, int N, const SkPlan &p,
-                                 Seg seg, const float *tpart, int n_chunks, const uint16_t *B,
-                                 const float *scale, const int32_t *ids, const int32_t *ranks,
-                                 const int32_t *roff, int pool_rows, int pstride, int r_max,
-                                 int n_adapters, void *y, bool y_f32, hipStream_t s) {
+                                 Seg seg, const SkProj &pj, int n_chunks, const float *scale,
+                                 const int32_t *ids, const int32_t *ranks, const int32_t *roff,
+                                 int pool_rows, int pstride, int r_max, int n_adapters,
+                                 bool y_f32, hipStream_t s) {
     if (r_max < 8 || r_max > 64 || (r_max & (r_max - 1)) != 0) return hipErrorInvalidValue;
     if (roff == nullptr && (pstride < 1 || pstride > r_max)) return hipErrorInvalidValue;
     const dim3 grid((unsigned)(((M + 7) / 8) * p.n_tn));
     if (y_f32)
         launch(sk_reduce_lora_kernel<CfgSk, true>, grid, dim3(256), 0, s, partial, M, K, N, p.n_tm,
-               p.n_tn, p.L, seg, tpart, n_chunks, B, scale, ids, ranks, roff, pool_rows, pstride,
-               r_max, n_adapters, y);
+               p.n_tn, p.n_tn1, p.L, seg, pj, n_chunks, scale, ids, ranks, roff, pool_rows, pstride,
+               r_max, n_adapters);
     else
         launch(sk_reduce_lora_kernel<CfgSk, false>, grid, dim3(256), 0, s, partial, M, K, N, p.n_tm,
-               p.n_tn, p.L, seg, tpart, n_chunks, B, scale, ids, ranks, roff, pool_rows, pstride,
-               r_max, n_adapters, y);
+               p.n_tn, p.n_tn1, p.L, seg, pj, n_chunks, scale, ids, ranks, roff, pool_rows, pstride,
+               r_max, n_adapters);
     return hipGetLastError();
 }
 

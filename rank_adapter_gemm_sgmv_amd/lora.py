@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(PKG, "liblora_mi355x.so")
 LORA_TILE_ROWS = 16
 LORA_MAX_ADAPTERS = 16384
 LORA_MAX_ROWS = 1 << 22
+LORA_MAX_PROJ = 4
 LORA_PREFILL_MIN_ROWS = 768
 LORA_NOALLOC_SCRATCH_BYTES = 32 << 20
 LORA_MOE_MAX_PAIRS = 8192
@@ -39,6 +40,7 @@ EXPORTS = ("lora_max_tiles", "lora_workspace_bytes", "lora_build_segments", "lor
            "lora_linear_profiled", "lora_linear_compact", "lora_linear_compact_profiled",
            "lora_linear_noalloc", "lora_linear_fp8w", "lora_linear_fp8w_profiled",
            "lora_moe_workspace_bytes", "lora_moe_linear", "lora_moe_linear_profiled",
+           "lora_workspace_bytes_multi", "lora_linear_multi", "lora_linear_multi_profiled",
            "lora_status_string", "lora_last_hip_error")
 
 
@@ -116,6 +118,15 @@ def _load():
     lib.lora_linear_compact_profiled.argtypes = lib.lora_linear_compact.argtypes + [
         ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_char_p), I, ctypes.POINTER(I)]
     lib.lora_linear_compact_profiled.restype = ctypes.c_int
+    lib.lora_workspace_bytes_multi.argtypes = [I, I, I, I, I, I]
+    lib.lora_workspace_bytes_multi.restype = S
+    lib.lora_linear_multi.argtypes = [P, I, P, P, P, P, P, P, I, I, I, I, I,
+                                      ctypes.POINTER(lora_segments_t), P, ctypes.c_int,
+                                      ctypes.c_int, P, S, P]
+    lib.lora_linear_multi.restype = ctypes.c_int
+    lib.lora_linear_multi_profiled.argtypes = lib.lora_linear_multi.argtypes + [
+        ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_char_p), I, ctypes.POINTER(I)]
+    lib.lora_linear_multi_profiled.restype = ctypes.c_int
     lib.lora_status_string.argtypes = [ctypes.c_int]
     lib.lora_status_string.restype = ctypes.c_char_p
     lib.lora_last_hip_error.argtypes = []
@@ -310,6 +321,49 @@ def lora_linear_profiled(x, W, A, B, scale, ranks, ids, M: int, d_in: int, d_out
                                      _ptr(ids), M, d_in, d_out, r_max, n_adapters, seg_p, _ptr(y),
                                      y_dtype, mode, _ptr(ws), ws_bytes, _stream(stream), ms, names,
                                      max_kernels, ctypes.byref(n)), "lora_linear_profiled")
+    return [(names[i].decode(), float(ms[i])) for i in range(n.value)]
+
+
+def lora_workspace_bytes_multi(M: int, d_in: int, d_out: int, r_max: int, n_adapters: int,
+                               n_proj: int) -> int:
+    return int(_lib.lora_workspace_bytes_multi(M, d_in, d_out, r_max, n_adapters, n_proj))
+
+
+def _ptr_array(ts):
+    """Host array of device addresses (None for a missing list)."""
+    if ts is None:
+        return None
+    return (ctypes.c_void_p * len(ts))(*[_ptr(t) for t in ts])
+
+
+def lora_linear_multi(x, Ws, As, Bs, scale, ranks, ids, M: int, d_in: int, d_out: int,
+                      r_max: int, n_adapters: int, segs, ys, y_dtype: int, mode: int, ws,
+                      ws_bytes: int, stream=None, n_proj: Optional[int] = None) -> None:
+    """lora_linear for len(Ws) projections that share x and the adapter tables (Ws, As, Bs,
+    ys: lists of device tensors, one per projection)."""
+    seg_p = None if segs is None else ctypes.byref(_seg_struct(segs))
+    if n_proj is None:  # the length of the lists (a missing list is passed as NULL)
+        n_proj = next((len(v) for v in (Ws, As, Bs, ys) if v is not None), 0)
+    n = n_proj
+    _check(_lib.lora_linear_multi(_ptr(x), n, _ptr_array(Ws), _ptr_array(As), _ptr_array(Bs),
+                                  _ptr(scale), _ptr(ranks), _ptr(ids), M, d_in, d_out, r_max,
+                                  n_adapters, seg_p, _ptr_array(ys), y_dtype, mode, _ptr(ws),
+                                  ws_bytes, _stream(stream)), "lora_linear_multi")
+
+
+def lora_linear_multi_profiled(x, Ws, As, Bs, scale, ranks, ids, M: int, d_in: int, d_out: int,
+                               r_max: int, n_adapters: int, segs, ys, y_dtype: int, mode: int,
+                               ws, ws_bytes: int, stream=None, max_kernels: int = 24):
+    """lora_linear_multi with per-kernel HIP event timing; returns [(kernel name, ms), ...]."""
+    seg_p = None if segs is None else ctypes.byref(_seg_struct(segs))
+    ms = (ctypes.c_float * max_kernels)()
+    names = (ctypes.c_char_p * max_kernels)()
+    n = ctypes.c_int32(0)
+    _check(_lib.lora_linear_multi_profiled(
+        _ptr(x), len(Ws), _ptr_array(Ws), _ptr_array(As), _ptr_array(Bs), _ptr(scale), _ptr(ranks),
+        _ptr(ids), M, d_in, d_out, r_max, n_adapters, seg_p, _ptr_array(ys), y_dtype, mode,
+        _ptr(ws), ws_bytes, _stream(stream), ms, names, max_kernels, ctypes.byref(n)),
+        "lora_linear_multi_profiled")
     return [(names[i].decode(), float(ms[i])) for i in range(n.value)]
 
 

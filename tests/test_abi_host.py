@@ -242,3 +242,45 @@ def test_moe_linear_rejects(over, code):
 def test_moe_empty_batch_is_noop():
     L.lora_moe_linear(FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, None, 0, 4, 32, 2880, 2880,
                       16, 8, None, L.LORA_BF16, L.LORA_MODE_DECODE, None, 0, stream=0)
+
+
+def test_workspace_bytes_multi():
+    one = L.lora_workspace_bytes(512, 4096, 11008, 16, 1024)
+    assert L.lora_workspace_bytes_multi(512, 4096, 11008, 16, 1024, 0) == 0
+    assert L.lora_workspace_bytes_multi(512, 4096, 11008, 16, 1024, L.LORA_MAX_PROJ + 1) == 0
+    assert L.lora_workspace_bytes_multi(512, 4096, 11008, 16, 1024, 1) == one
+    # the stream-K batch: one shrink area per projection and the merged launch's partial tiles
+    two = L.lora_workspace_bytes_multi(512, 4096, 11008, 16, 1024, 2)
+    assert two > one and two % 256 == 0
+    # batches outside the stream-K range run projection by projection on one workspace
+    for M in (64, 200, 2048):
+        assert (L.lora_workspace_bytes_multi(M, 4096, 4096, 16, 32, 3) ==
+                L.lora_workspace_bytes(M, 4096, 4096, 16, 32))
+    assert L.lora_workspace_bytes_multi(64, 4096, 4096, 65, 32, 2) == 0
+
+
+def _multi(n_proj=2, **over):
+    args = dict(x=FAKE, Ws=[FAKE] * n_proj, As=[FAKE] * n_proj, Bs=[FAKE] * n_proj, scale=FAKE,
+                ranks=None, ids=FAKE, M=512, d_in=4096, d_out=11008, r_max=16, n_adapters=1024,
+                segs=None, ys=[FAKE] * n_proj, y_dtype=L.LORA_BF16, mode=L.LORA_MODE_DECODE,
+                ws=FAKE, ws_bytes=L.lora_workspace_bytes(512, 4096, 11008, 16, 1024), stream=0)
+    args.update(over)
+    return L.lora_linear_multi(**args)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(n_proj=0), 2), (dict(n_proj=L.LORA_MAX_PROJ + 1), 2),
+    (dict(Ws=None), 1), (dict(ys=None), 1), (dict(As=[FAKE, None]), 1), (dict(ys=[FAKE, FAKE + 8]), 4),
+    (dict(r_max=65), 3), (dict(M=-1), 2),
+    # enough for one projection's sequence, not for the merged stream-K launch of two
+    (dict(), 5),
+])
+def test_linear_multi_rejects(over, code):
+    n_proj = over.pop("n_proj", 2)
+    with pytest.raises(L.LoraError) as e:
+        _multi(n_proj=n_proj, **over)
+    assert e.value.status == code
+
+
+def test_linear_multi_empty_batch_is_noop():
+    _multi(M=0, x=None, ys=[None, None], ws=None)
