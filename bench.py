@@ -153,9 +153,9 @@ class DeviceLayers:
 
 def split_group_kernels(ks, n):
     """Per-projection kernel lists of one lora_linear_multi call over n projections: a kernel
-    name launched n times (each projection's own shrink, or every launch when the call ran
-    projection by projection) goes to the projections in order; a launch shared by the group
-    (the merged GEMM and reduction, the segment build) is split evenly between them."""
+    name launched n times (every launch when the call ran projection by projection) goes to
+    the projections in order; a launch shared by the group (the merged shrink, GEMM and
+    reduction, the segment build) is split evenly between them."""
     out = [[] for _ in range(n)]
     names = [name for name, _ in ks]
     seen = {}

@@ -613,7 +613,8 @@ size_t multi_sk_bytes(int32_t M, int32_t d_in, int32_t d_out, int32_t r_max, int
 
 // The launch sequence of lora_linear_multi (arguments already validated, M > 0).  Batches
 // that take lora_linear's stream-K sequence (decode, 257-1024 rows) build the segments once,
-// run each projection's shrink, then one stream-K GEMM and one reduction per group of up to g
+// run every projection's shrink in one launch, then one stream-K GEMM and one reduction per
+// group of up to g
 // projections, whose column panels are laid end to end on one K line (longer lanes: fewer
 // partial tiles per panel).  Every other batch runs lora_linear's sequence per projection.
 hipError_t run_linear_multi(const void *x, int32_t n_proj, const void *const *W,
@@ -649,12 +650,13 @@ hipError_t run_linear_multi(const void *x, int32_t n_proj, const void *const *W,
         if ((e = launch_build_segments(ids, M, n_adapters, sg, s)) != hipSuccess) return e;
         mark(mk, "build_segments");
     }
-    for (int i = 0; i < n_proj; ++i) {
-        if ((e = launch_shrink(xb, static_cast<const uint16_t *>(A[i]), ranks, nullptr, 0, pstride, M,
-                               d_in, rb, n_adapters, sg, spart[i], kc, ksplit, s)) != hipSuccess)
-            return e;
-        mark(mk, "shrink");
-    }
+    // every projection's shrink in one launch
+    const uint16_t *Ab[kMaxProj] = {};
+    for (int i = 0; i < n_proj; ++i) Ab[i] = static_cast<const uint16_t *>(A[i]);
+    if ((e = launch_shrink_multi(xb, n_proj, Ab, spart, ranks, pstride, M, d_in, rb, n_adapters, sg,
+                                 kc, ksplit, s)) != hipSuccess)
+        return e;
+    mark(mk, "shrink");
     for (int i0 = 0; i0 < n_proj; i0 += g) {
         const int gn = n_proj - i0 < g ? n_proj - i0 : g;
         const SkPlan sp = sk_plan(M, d_in, d_out, gn);

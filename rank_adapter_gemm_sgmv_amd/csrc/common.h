@@ -78,6 +78,16 @@ __device__ __forceinline__ int adapter_row0(const int32_t *roff, int pool_rows, 
 
 // Kernel rank bucket of a pool whose widest adapter has r_max rank rows: t, the shrink's
 // partial sums and every other internal buffer use the bucket as their row width.
+// Projections one lora_linear_multi launch takes, and entry i of a per-projection pointer
+// array held in kernel arguments, by selects (a runtime index into the argument array would
+// copy it to scratch memory).
+constexpr int kMaxProj = 4;
+template <class T>
+__device__ __forceinline__ T pick_proj(int i, T const (&v)[kMaxProj]) {
+    static_assert(kMaxProj == 4, "selects below");
+    return i == 0 ? v[0] : i == 1 ? v[1] : i == 2 ? v[2] : v[3];
+}
+
 constexpr int rank_bucket(int r_max) { return r_max <= 8 ? 8 : r_max <= 16 ? 16 : r_max <= 32 ? 32 : 64; }
 // Width of an adapter's slot in the small-batch GEMM's adapter tiles for rank bucket rb (the
 // bf16 base; t there has this row width).  Rank-8 pools take 16-wide slots: an 8-wide slot
@@ -124,6 +134,12 @@ hipError_t launch_shrink(const uint16_t *x, const uint16_t *A, const int32_t *ra
                          const int32_t *roff, int pool_rows, int pstride, int M, int d_in,
                          int r_max, int n_adapters, Seg seg, float *partial, int kc, int ksplit,
                          hipStream_t s);
+// The same over n_proj <= kMaxProj pools that share x, the tables and the segments
+// (lora_linear_multi) in one launch: pool p reads A[p] and writes partial[p].
+hipError_t launch_shrink_multi(const uint16_t *x, int n_proj, const uint16_t *const *A,
+                               float *const *partial, const int32_t *ranks, int pstride, int M,
+                               int d_in, int r_max, int n_adapters, Seg seg, int kc, int ksplit,
+                               hipStream_t s);
 // t[m][0 : t_stride) from the partial sums (t_stride <= r_max, the bucket).
 hipError_t launch_shrink_finalize(const float *partial, int M, int r_max, int ksplit, Seg seg,
                                   float *t, int t_stride, hipStream_t s);
@@ -176,7 +192,6 @@ struct SkPlan {
 SkPlan sk_plan(int M, int K, int N, int n_proj = 1);
 size_t sk_partial_floats(const SkPlan &p);
 // Per-projection operands of the stream-K launches (entries past p.n_proj unused).
-constexpr int kMaxProj = 4;
 struct SkProj {
     const uint16_t *W[kMaxProj];   // [K][N]
     const uint16_t *B[kMaxProj];   // adapter pool B of each projection

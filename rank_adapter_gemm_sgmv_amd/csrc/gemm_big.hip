@@ -503,14 +503,6 @@ __global__ __launch_bounds__(C::NT) void gemm_big_kernel(const uint16_t *__restr
 // both advance along the one K line.  sk_reduce_kernel adds a panel's slots in lane order,
 // so the sum does not depend on scheduling.
 
-// Entry i of a per-projection pointer array held in kernel arguments, by selects (a
-// runtime index into the argument array would copy it to scratch memory).
-template <class T>
-__device__ __forceinline__ T pick_proj(int i, T const (&v)[kMaxProj]) {
-    static_assert(kMaxProj == 4, "selects below");
-    return i == 0 ? v[0] : i == 1 ? v[1] : i == 2 ? v[2] : v[3];
-}
-
 // Lane run by the workgroups of each rank: lanes sorted by the K offset at which they
 // start inside their panel, so the ranks an XCD gets (16 when L = 128) read neighbouring
 // K slices of x and share them through that XCD's L2.

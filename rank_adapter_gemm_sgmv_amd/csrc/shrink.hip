@@ -95,11 +95,19 @@ __device__ __forceinline__ void shrink_mfma_fill(f32x4_t (&acc)[C::NB], const ui
 //            loads in flight per lane) and scattered into the zeroed LDS rows.  A separate
 //            instantiation, so that the other layouts keep their registers and occupancy.
 enum { kPadRM = 0, kVarW = 1, kFlat = 2 };
+// Several pools of one x (lora_linear_multi): item it belongs to pool it / (tiles x chunks),
+// which reads A.p[pool] and writes partial.p[pool].
+struct ShrinkPools {
+    const uint16_t *A[kMaxProj];
+    float *partial[kMaxProj];
+    int n;
+};
+
 template <int RM, int LAYOUT>
 __global__ __launch_bounds__(64 * kWavesPerBlock) void shrink_mfma_kernel(
-    const uint16_t *__restrict__ x, const uint16_t *__restrict__ A, const int32_t *__restrict__ ranks,
+    const uint16_t *__restrict__ x, ShrinkPools pools, const int32_t *__restrict__ ranks,
     const int32_t *__restrict__ roff, int pool_rows, int pstride, int M, int d_in, int n_adapters,
-    Seg seg, float *__restrict__ partial, int n_chunks, int kc) {
+    Seg seg, int n_chunks, int kc) {
     using C = MfmaShrink<RM>;
     __shared__ __attribute__((aligned(16))) char lds[kWavesPerBlock][C::LDS];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -113,10 +121,14 @@ __global__ __launch_bounds__(64 * kWavesPerBlock) void shrink_mfma_kernel(
     // the block's waves take the four quarters of the chunk's k range; waves 1-3 hand their
     // sums to wave 0 through LDS, which adds them in wave order and writes the chunk's sums
     __shared__ float red[kWavesPerBlock - 1][16 * C::RMP];
-    const int total = seg.meta[3] * n_chunks;
+    const int per_pool = seg.meta[3] * n_chunks;
+    const int total = per_pool * pools.n;
     const int kw = kc / kWavesPerBlock;
     for (int it = blockIdx.x; it < total; it += gridDim.x) {
-        const int tile = it / n_chunks, c = it % n_chunks;
+        const int pi = it / per_pool, ip = it - pi * per_pool;
+        const uint16_t *__restrict__ A = pick_proj(pi, pools.A);
+        float *__restrict__ partial = pick_proj(pi, pools.partial);
+        const int tile = ip / n_chunks, c = ip % n_chunks;
         const int p0 = seg.tiles[2 * tile], a = seg.tiles[2 * tile + 1];
         // (a tile naming no adapter of the pool, possible only in segments a caller built, is
         // skipped by the whole workgroup)
@@ -313,13 +325,17 @@ void shrink_plan(int d_in, int r_max, int *kc, int *ksplit) {
     *ksplit = (d_in + *kc - 1) / *kc;
 }
 
-hipError_t launch_shrink(const uint16_t *x, const uint16_t *A, const int32_t *ranks,
-                         const int32_t *roff, int pool_rows, int pstride, int M, int d_in,
-                         int r_max, int n_adapters, Seg seg, float *partial, int kc, int ksplit,
-                         hipStream_t s) {
+namespace {
+
+hipError_t launch_shrink_pools(const uint16_t *x, const ShrinkPools &pools, const int32_t *ranks,
+                               const int32_t *roff, int pool_rows, int pstride, int M, int d_in,
+                               int r_max, int n_adapters, Seg seg, int kc, int ksplit,
+                               hipStream_t s) {
     if (roff == nullptr && (pstride < 1 || pstride > r_max)) return hipErrorInvalidValue;
     if (kc % (8 * kWavesPerBlock) != 0) return hipErrorInvalidValue;
-    const long items = (long)lora_max_tiles(M, n_adapters) * ksplit;  // one per workgroup
+    if (pools.n < 1 || pools.n > kMaxProj) return hipErrorInvalidValue;
+    // one workgroup per item
+    const long items = (long)lora_max_tiles(M, n_adapters) * ksplit * pools.n;
     const dim3 wgrid((unsigned)(items < kMaxGrid ? items : kMaxGrid));
     const dim3 wblock(64 * kWavesPerBlock);
     const int layout = roff != nullptr       ? kVarW
@@ -327,8 +343,8 @@ hipError_t launch_shrink(const uint16_t *x, const uint16_t *A, const int32_t *ra
                        : (pstride & 7) != 0  ? kFlat
                                              : kVarW;
 #define LORA_SHRINK_ONE(RMV, LAY)                                                                \
-    launch(shrink_mfma_kernel<RMV, LAY>, wgrid, wblock, 0, s, x, A, ranks, roff, pool_rows,      \
-           pstride, M, d_in, n_adapters, seg, partial, ksplit, kc)
+    launch(shrink_mfma_kernel<RMV, LAY>, wgrid, wblock, 0, s, x, pools, ranks, roff, pool_rows,  \
+           pstride, M, d_in, n_adapters, seg, ksplit, kc)
 #define LORA_SHRINK_LAUNCH(RMV)                                                                  \
     if (layout == kPadRM) LORA_SHRINK_ONE(RMV, kPadRM);                                          \
     else if (layout == kVarW) LORA_SHRINK_ONE(RMV, kVarW);                                       \
@@ -343,6 +359,35 @@ hipError_t launch_shrink(const uint16_t *x, const uint16_t *A, const int32_t *ra
 #undef LORA_SHRINK_LAUNCH
 #undef LORA_SHRINK_ONE
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_shrink(const uint16_t *x, const uint16_t *A, const int32_t *ranks,
+                         const int32_t *roff, int pool_rows, int pstride, int M, int d_in,
+                         int r_max, int n_adapters, Seg seg, float *partial, int kc, int ksplit,
+                         hipStream_t s) {
+    ShrinkPools pools{};
+    pools.A[0] = A;
+    pools.partial[0] = partial;
+    pools.n = 1;
+    return launch_shrink_pools(x, pools, ranks, roff, pool_rows, pstride, M, d_in, r_max,
+                               n_adapters, seg, kc, ksplit, s);
+}
+
+hipError_t launch_shrink_multi(const uint16_t *x, int n_proj, const uint16_t *const *A,
+                               float *const *partial, const int32_t *ranks, int pstride, int M,
+                               int d_in, int r_max, int n_adapters, Seg seg, int kc, int ksplit,
+                               hipStream_t s) {
+    if (n_proj < 1 || n_proj > kMaxProj) return hipErrorInvalidValue;
+    ShrinkPools pools{};
+    for (int p = 0; p < n_proj; ++p) {
+        pools.A[p] = A[p];
+        pools.partial[p] = partial[p];
+    }
+    pools.n = n_proj;
+    return launch_shrink_pools(x, pools, ranks, nullptr, 0, pstride, M, d_in, r_max, n_adapters,
+                               seg, kc, ksplit, s);
 }
 
 hipError_t launch_shrink_finalize(const float *partial, int M, int r_max, int ksplit, Seg seg,
