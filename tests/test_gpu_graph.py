@@ -84,3 +84,51 @@ def test_graph_replays_match_eager(case):
         call()  # eager work between replays
         torch.cuda.synchronize()
         assert torch.equal(y.view(torch.int16), eager.view(torch.int16))
+
+
+def test_graph_replays_match_eager_multi():
+    """lora_linear_multi (two projections of one x, merged stream-K launches) in a graph."""
+    import torch
+
+    from rank_adapter_gemm_sgmv_amd import lora as L
+
+    M, d_in, d_out, n, r_max = 300, 4096, 2048, 24, 16
+    log(f"graph: lora_linear_multi M={M} {d_in}x{d_out} two projections")
+    w0 = random_case(101, M, d_in, d_out, n, r_max, base_frac=0.2)
+    w1 = random_case(102, M, d_in, d_out, n, r_max, ids=w0.ids, ranks=w0.ranks)
+    d0, d1 = to_device(w0), to_device(w1)
+    p0, p1 = d0.projs[0], d1.projs[0]
+    ys = [torch.empty((M, d_out), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    nb = L.lora_workspace_bytes_multi(M, d_in, d_out, r_max, n, 2)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+
+    def call():
+        L.lora_linear_multi(p0.x, [p0.W, p1.W], [p0.A, p1.A], [p0.B, p1.B], d0.scale, d0.ranks,
+                            d0.ids, M, d_in, d_out, r_max, n, None, ys, L.LORA_BF16,
+                            L.LORA_MODE_DECODE, ws, nb)
+
+    call()
+    torch.cuda.synchronize()
+    eager = [y.clone() for y in ys]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for rep in range(4):
+        for y in ys:
+            y.fill_(0)
+        ws.fill_(0xAB)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for y, e in zip(ys, eager):
+            assert torch.equal(y.view(torch.int16), e.view(torch.int16)), f"replay {rep}"
+        call()
+        torch.cuda.synchronize()
+        for y, e in zip(ys, eager):
+            assert torch.equal(y.view(torch.int16), e.view(torch.int16))
