@@ -494,13 +494,14 @@ __global__ __launch_bounds__(C::NT) void gemm_big_kernel(const uint16_t *__restr
 // ---- stream-K decode GEMM -----------------------------------------------------------------
 // Decode batches of a few hundred rows have too few 256 x 256 output tiles to fill the chip
 // (512 x 11008: 86 tiles on 256 CUs), and smaller tiles lose the large tile's MFMA rate.
-// Instead the K steps of all column panels, laid end to end panel after panel, are cut into
-// L equal lanes.  Each lane is run by n_tm workgroups, one per 256-row tile, placed on the
-// same XCD (workgroup b runs on XCD b % 8), so the W panel they share is read once into that
-// XCD's L2.  A lane's range may start inside one panel and end inside the next: for every
-// panel it meets, the lane writes its fp32 partial tile to slot (lane + panel) * n_tm + tm.
-// lane + panel differs for every (lane, panel) pair that meets, because panels and lanes
-// both advance along the one K line.  sk_reduce_kernel adds a panel's slots in lane order,
+// Instead the K steps of all column panels, laid end to end panel after panel (projection
+// after projection when several that share x run in one launch), are cut into L equal lanes.
+// Each lane is run by n_tm workgroups, one per 256-row tile, placed on the same XCD
+// (workgroup b runs on XCD b % 8), so the W panel they share is read once into that XCD's L2.
+// A lane's range may start inside one panel and end inside the next: for every panel it
+// meets, the lane writes its fp32 partial tile to slot (lane + panel) * n_tm + tm. lane +
+// panel differs for every (lane, panel) pair that meets, because panels and lanes both
+// advance along the one K line. sk_reduce_lora_kernel adds a panel's slots in lane order,
 // so the sum does not depend on scheduling.
 
 // Lane run by the workgroups of each rank: lanes sorted by the K offset at which they
