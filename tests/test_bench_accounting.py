@@ -46,3 +46,20 @@ def test_heterogeneous_adapters_count_at_true_rank():
     r_rows = int(w.ranks[w.ids[w.ids >= 0]].sum())
     assert work["shrink"]["bytes"] == a_true + lora_rows * 4096 * 2 + r_rows * 4
     assert a_true < len(used) * 64 * 4096 * 2  # below the padded bytes
+
+
+def test_merged_call_kernels_split_between_projections():
+    """A lora_linear_multi call over two projections: launches shared by the group (the merged
+    shrink, GEMM and reduction) are charged half to each projection; launches made once per
+    projection (the call ran projection by projection) go to the projections in order."""
+    merged = [("shrink", 16.0), ("gemm_decode", 100.0), ("decode_reduce_lora", 50.0)]
+    a, b = bench.split_group_kernels(merged, 2)
+    assert a == b == [("shrink", 8.0), ("gemm_decode", 50.0), ("decode_reduce_lora", 25.0)]
+    looped = [("shrink", 9.0), ("gemm_decode", 60.0), ("shrink", 10.0), ("gemm_decode", 61.0)]
+    a, b = bench.split_group_kernels(looped, 2)
+    assert a == [("shrink", 9.0), ("gemm_decode", 60.0)]
+    assert b == [("shrink", 10.0), ("gemm_decode", 61.0)]
+    # the per-projection lists add back to the call's total
+    for ks in (merged, looped):
+        a, b = bench.split_group_kernels(ks, 2)
+        assert abs(sum(ms for _, ms in a + b) - sum(ms for _, ms in ks)) < 1e-9
