@@ -259,13 +259,14 @@ lora_status_t lora_linear_compact(const void *x, const void *W, const void *A, c
  * lora_linear argument of the same name; the projections share x, d_in, d_out, r_max, the
  * adapter tables (scale, ranks, ids: one adapter owns a pair A[p]_i, B[p]_i in every
  * projection) and segs.  ws: lora_workspace_bytes_multi() bytes (else LORA_ERR_WORKSPACE).
+ * The pointer arrays are read during the call only; the caller owns every buffer.
  * Decode batches of 257-1024 rows that take lora_linear's stream-K sequence build the
- * segments once and run the projections' shrinks as one launch, their GEMMs as one (their
- * column panels end to end on one K line) and their reductions as one; the K sums are then
- * split at other points
- * than in separate calls, so the bits may differ from lora_linear's by the order of fp32
- * additions.  Every other batch runs lora_linear's launches per projection (same bits).
- * Errors as lora_linear, for the first projection whose arguments fail. */
+ * segments once (unless segs is given) and run the projections' shrinks as one launch, their
+ * GEMMs as one (their column panels end to end on one K line) and their reductions as one;
+ * the K sums are then split at other points than in separate calls, so the bits may differ
+ * from lora_linear's by the order of fp32 additions.  Every other batch runs lora_linear's
+ * launches per projection (same bits).  Errors as lora_linear, for the first projection
+ * whose arguments fail. */
 size_t lora_workspace_bytes_multi(int32_t M, int32_t d_in, int32_t d_out, int32_t r_max,
                                   int32_t n_adapters, int32_t n_proj);
 lora_status_t lora_linear_multi(const void *x, int32_t n_proj, const void *const *W,
