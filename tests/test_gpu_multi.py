@@ -127,3 +127,52 @@ def test_multi_separate_paths(case):
     for p, (y, y1, ref) in enumerate(zip(out, singles, refs(base, projs))):
         assert np.array_equal(y, y1), f"projection {p}: bits differ from lora_linear"
         assert_parity(y, ref, f"projection {p}")
+
+
+def test_multi_caller_segments_and_checked_mode():
+    """The merged stream-K sequence on segments the caller built (no build launch) gives the
+    bits of the call that builds them; LORA_MODE_CHECKED passes valid tables through
+    unchanged and reports an id outside [-1, n) before enqueueing anything."""
+    import torch
+
+    from rank_adapter_gemm_sgmv_amd import lora as L
+
+    M, d_in, d_out, n, r_max = 320, 4096, 2048, 20, 16
+    log(f"multi: caller segments and checked mode, M={M}")
+    base, projs = multi_case(531, M, d_in, d_out, n, r_max, 2)
+    x = bf16_dev(projs[0].x)
+    Ws = [bf16_dev(p.W) for p in projs]
+    As = [bf16_dev(p.A) for p in projs]
+    Bs = [bf16_dev(p.B) for p in projs]
+    ids = torch.from_numpy(base.ids.astype(np.int32)).cuda()
+    ranks = torch.from_numpy(base.ranks.astype(np.int32)).cuda()
+    scale = torch.from_numpy(scale_of(base)).cuda()
+    nb = L.lora_workspace_bytes_multi(M, d_in, d_out, r_max, n, 2)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+
+    def call(segs=None, mode=L.LORA_MODE_DECODE, ids_t=ids):
+        ys = [torch.full((M, d_out), 3.0, dtype=torch.float32, device="cuda") for _ in range(2)]
+        L.lora_linear_multi(x, Ws, As, Bs, scale, ranks, ids_t, M, d_in, d_out, r_max, n, segs,
+                            ys, L.LORA_F32, mode, ws, nb)
+        torch.cuda.synchronize()
+        return ys
+
+    own = call()
+    segs = L.Segments(M, n)
+    L.lora_build_segments(ids, M, n, segs)
+    for y, y0 in zip(call(segs=segs), own):
+        assert torch.equal(y, y0)
+    for y, y0 in zip(call(mode=L.LORA_MODE_DECODE | L.LORA_MODE_CHECKED), own):
+        assert torch.equal(y, y0)
+    for y, ref in zip(own, refs(base, projs)):
+        assert_parity(y.cpu().numpy(), ref, "caller segments")
+    bad = base.ids.copy()
+    bad[M // 3] = n
+    ys = [torch.full((M, d_out), 3.0, dtype=torch.float32, device="cuda") for _ in range(2)]
+    with pytest.raises(L.LoraError) as e:
+        L.lora_linear_multi(x, Ws, As, Bs, scale, ranks, torch.from_numpy(bad).cuda(), M, d_in,
+                            d_out, r_max, n, None, ys, L.LORA_F32,
+                            L.LORA_MODE_DECODE | L.LORA_MODE_CHECKED, ws, nb)
+    assert e.value.status == 8  # LORA_ERR_BAD_ID
+    torch.cuda.synchronize()
+    assert all(bool((y == 3.0).all()) for y in ys)  # nothing was enqueued
