@@ -176,3 +176,44 @@ def test_multi_caller_segments_and_checked_mode():
     assert e.value.status == 8  # LORA_ERR_BAD_ID
     torch.cuda.synchronize()
     assert all(bool((y == 3.0).all()) for y in ys)  # nothing was enqueued
+
+
+def _sk_group(M, K, N, n_proj):
+    """Projections per merged stream-K launch (0: the batch does not take stream-K): the rule
+    the library states, restated here to name what each seeded case exercises."""
+    def use(g):
+        if M <= 256 or M > 1024 or K % 128 or N % 8:
+            return False
+        n_tm, n_tn = (M + 255) // 256, g * ((N + 255) // 256)
+        if n_tm * n_tn >= 192:
+            return False
+        return n_tn * (K // 32) >= 8 * ((256 // n_tm) // 8 * 8)
+    if not use(1):
+        return 0
+    g = n_proj
+    while g > 1 and not use(g):
+        g -= 1
+    return g
+
+
+RANDOM_MULTI = list(range(8))
+
+
+@pytest.mark.parametrize("i", RANDOM_MULTI)
+def test_multi_random_shapes(i):
+    """Seeded shapes across the stream-K range: 257-1024 rows, d_out any multiple of 8 from
+    1800 to 3072 (ragged last panels), 2-4 projections, r_max 1-64, pools of 4-300 adapters."""
+    from rank_adapter_gemm_sgmv_amd import lora as L
+
+    rng = np.random.default_rng(600 + i)
+    M = int(rng.integers(257, 1025))
+    d_out = int(rng.integers(225, 385)) * 8
+    n_proj = int(rng.integers(2, 5))
+    r_max = int(rng.integers(1, 65))
+    n = int(rng.integers(4, 301))
+    g = _sk_group(M, 4096, d_out, n_proj)
+    log(f"multi random {i}: M={M} d_out={d_out} projections {n_proj} r_max={r_max} n={n} group {g}")
+    base, projs = multi_case(610 + i, M, 4096, d_out, n, r_max, n_proj)
+    out, singles = run_multi(base, projs, L.LORA_MODE_DECODE)
+    for p, (y, ref) in enumerate(zip(out, refs(base, projs))):
+        assert_parity(y, ref, f"case {i} projection {p} (group {g})")
